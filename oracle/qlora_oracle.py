@@ -1,0 +1,346 @@
+"""Plain CPU oracle: NF4 codebook, blockwise absmax quantization, double quantization of
+the block constants, dequantization, and the LoRA-augmented forward/backward.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).  FP64 math unless a step is
+defined in FP32; FP32 steps use NumPy float32 scalars/arrays, whose +, -, *, / are
+IEEE round-to-nearest-even and never fused.
+
+Sources (cited by page title and section):
+  [4-Bit]  "QLoRA: Quantize Base Weights to 4-Bit" -- Section 2 ("1. 4-bit NormalFloat",
+           "2. Double Quantization"), Section 3 (the dequantize-compute loop).
+  [65B]    "QLoRA -- Fine-Tuning a 65B Model on One GPU" -- "Prerequisite: LoRA's low-rank
+           update", "Quantization in one paragraph", "NF4: sixteen levels shaped like the
+           weights", "Double quantization: the constants are not free", "Where the
+           gradients actually go".
+  [Consumer] "QLoRA fine-tuning on consumer GPUs" -- FAQ on double quantization.
+"""
+
+from __future__ import annotations
+
+import math
+
+import mpmath
+import numpy as np
+
+BLOCK1 = 64  # weights per first-level absmax block ([4-Bit] Sec. 2 "2. Double Quantization")
+BLOCK2 = 256  # first-level constants per second-level group (same passage)
+E4M3_MAX = 448.0  # largest finite OCP FP8 E4M3 value (S.1111.110 = 1.75 * 2^8)
+
+# --------------------------------------------------------------------------------------
+# NF4 codebook
+# --------------------------------------------------------------------------------------
+
+
+def _q_normal(num: int, den: int) -> mpmath.mpf:
+    """Standard-normal quantile Q(num/den) at 60 significant digits.
+
+    Evaluated on the lower half only and mirrored, so Q(1-p) == -Q(p) holds exactly
+    (reading R(1)): the interior of the table is then exactly antisymmetric."""
+    with mpmath.workdps(60):
+        if 2 * num > den:
+            return -_q_normal(den - num, den)
+        p = mpmath.mpf(num) / den
+        return mpmath.sqrt(2) * mpmath.erfinv(2 * p - 1)
+
+
+def nf4_codebook_exact() -> list:
+    """The 16 NF4 levels as 60-digit mpmath numbers, before FP32 rounding.
+
+    [4-Bit] Sec. 2 "1. 4-bit NormalFloat": q_i = 1/2 (Q(i/(2^k+1)) + Q((i+1)/(2^k+1))),
+    k = 4, Q the standard-normal quantile function; 0 is represented exactly and q_15 is
+    finite.  [65B] "NF4": 8 negative and 8 non-negative levels including a true 0, and the
+    endpoints are exactly -1 and +1 so a block's absmax survives.
+
+    Reading R (the printed formula gives q_0 = -inf, since Q(0) = -inf):
+      (1) levels 1..15 follow the formula literally (q_8 = 0 exactly);
+      (2) the tail level q_0, whose bin [0, 1/17] has one infinite edge, takes the
+          quantile at the bin's probability midpoint, Q(1/34);
+      (3) each side is scaled by its own extreme: negatives by |q_0|, non-negatives by
+          q_15, so the endpoints are exactly -1 and +1 and 0 stays 0.
+    """
+    den = 2**4 + 1  # 17
+    raw = [None] * 16
+    with mpmath.workdps(60):
+        raw[0] = _q_normal(1, 2 * den)  # Q(1/34)
+        for i in range(1, 16):
+            raw[i] = (_q_normal(i, den) + _q_normal(i + 1, den)) / 2
+        neg_scale = -raw[0]
+        pos_scale = raw[15]
+        out = []
+        for i in range(16):
+            if i < 8:
+                out.append(raw[i] / neg_scale)
+            elif i == 8:
+                out.append(mpmath.mpf(0))
+            else:
+                out.append(raw[i] / pos_scale)
+    return out
+
+
+def nf4_codebook() -> np.ndarray:
+    """The NF4 table rounded to FP32 (RNE), as float32[16] (reading R(4))."""
+    vals = []
+    for v in nf4_codebook_exact():
+        d = float(v)  # correctly rounded to binary64 by mpmath
+        f = np.float32(d)  # RNE binary64 -> binary32
+        # Guard against double rounding: the binary64 value must not sit on a binary32 tie.
+        assert abs(float(f) - d) != 0.5 * float(np.spacing(np.abs(f))) or d == 0.0
+        vals.append(f)
+    return np.array(vals, dtype=np.float32)
+
+
+# --------------------------------------------------------------------------------------
+# First level: blockwise absmax + nearest NF4 level
+# --------------------------------------------------------------------------------------
+
+
+def nearest_level(rho: np.ndarray, table: np.ndarray) -> np.ndarray:
+    """Index of the NF4 level nearest to each rho ([65B] "Quantization in one paragraph":
+    store the index of the level nearest to x/c).  Brute force over all 16 levels, FP64
+    distances; ties go to the lower index (reading: the pages do not say)."""
+    rho = np.asarray(rho, dtype=np.float32).astype(np.float64)
+    t = table.astype(np.float64)
+    out = np.empty(rho.shape, dtype=np.uint8)
+    flat_in = rho.reshape(-1)
+    flat_out = out.reshape(-1)
+    chunk = 1 << 20
+    for s in range(0, flat_in.size, chunk):
+        r = flat_in[s : s + chunk]
+        dist = np.abs(r[:, None] - t[None, :])
+        flat_out[s : s + chunk] = np.argmin(dist, axis=1)  # first minimum = lowest index
+    return out
+
+
+def pack_codes(codes: np.ndarray) -> np.ndarray:
+    """Pack 4-bit codes, row-major order, two per byte.
+
+    Layout (a format choice; the pages fix none): each aligned run of 8 consecutive
+    weights e0..e7 occupies 4 bytes, byte i = e_i | e_{i+4} << 4 (i = 0..3)."""
+    c = np.asarray(codes, dtype=np.uint8).reshape(-1)
+    assert c.size % 8 == 0
+    g = c.reshape(-1, 8).astype(np.uint16)
+    packed = (g[:, 0:4] | (g[:, 4:8] << 4)).astype(np.uint8)
+    return packed.reshape(-1)
+
+
+def unpack_codes(packed: np.ndarray) -> np.ndarray:
+    """Inverse of :func:`pack_codes`."""
+    p = np.asarray(packed, dtype=np.uint8).reshape(-1, 4)
+    lo = p & 0x0F
+    hi = p >> 4
+    return np.concatenate([lo, hi], axis=1).reshape(-1).astype(np.uint8)
+
+
+# --------------------------------------------------------------------------------------
+# OCP FP8 E4M3 (the 8-bit float used for the double-quantized constants)
+# --------------------------------------------------------------------------------------
+
+
+def e4m3_value(code) -> np.ndarray:
+    """Value of an OCP E4M3 ("E4M3FN") bit pattern as float64: sign bit, 4 exponent bits
+    (bias 7), 3 mantissa bits; exponent 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN."""
+    b = np.asarray(code, dtype=np.int64)
+    sign = np.where((b >> 7) & 1, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = b & 0x7
+    mag = np.where(e == 0, (m / 8.0) * 2.0**-6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7))
+    val = sign * mag
+    return np.where((e == 15) & (m == 7), np.nan, val)
+
+
+_E4M3_POS_CODES = np.arange(0x00, 0x7F, dtype=np.int64)  # 0x00..0x7E: all finite non-negative
+_E4M3_POS_VALS = e4m3_value(_E4M3_POS_CODES)
+
+
+def e4m3_encode(s: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest finite E4M3 value, ties to the even code.
+
+    Reading: the 8-bit format of the double-quantized constants is OCP FP8 E4M3 (the
+    pages say "8-bit FP8" / "8-bit floats"; [Consumer] says "8-bit integers").  Brute force
+    over the 127 finite magnitudes; the sign bit is the sign of s (so tiny negatives give
+    0x80).  Values beyond 448 go to 448 (nearest finite)."""
+    s = np.asarray(s, dtype=np.float32)
+    flat = s.reshape(-1).astype(np.float64)
+    neg = np.signbit(s.reshape(-1))
+    mag = np.abs(flat)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    chunk = 1 << 16
+    for st in range(0, flat.size, chunk):
+        a = mag[st : st + chunk]
+        dist = np.abs(a[:, None] - _E4M3_POS_VALS[None, :])
+        first = np.argmin(dist, axis=1)
+        dmin = dist[np.arange(a.size), first]
+        nxt = np.minimum(first + 1, _E4M3_POS_VALS.size - 1)
+        tie = (nxt != first) & (dist[np.arange(a.size), nxt] == dmin)
+        pick = np.where(tie & (first % 2 == 1), nxt, first)
+        out[st : st + chunk] = pick.astype(np.uint8)
+    out = np.where(neg, out | 0x80, out).astype(np.uint8)
+    return out.reshape(s.shape)
+
+
+# --------------------------------------------------------------------------------------
+# BF16 rounding
+# --------------------------------------------------------------------------------------
+
+
+def bf16_round_bits(x) -> np.ndarray:
+    """bfloat16 bit patterns of float32 values, round-to-nearest-even (finite inputs)."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = (u + 0x7FFF + lsb) >> 16
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# --------------------------------------------------------------------------------------
+# Quantize: absmax NF4 + double quantization
+# --------------------------------------------------------------------------------------
+
+
+def quantize(W: np.ndarray) -> dict:
+    """Quantize an FP32 weight matrix W[d_out, d_in] (d_in % 64 == 0).
+
+    Steps, in the pages' order:
+      1. Blocks of 64 consecutive row-major weights; c1 = max |w| per block
+         ([65B] "Quantization in one paragraph").
+      2. rho = fl32(w / c1); code = index of the nearest NF4 level (ties to the lower
+         index).  An all-zero block (c1 = 0) gets code 8, the exact-zero level (reading).
+      3. Double quantization ([4-Bit] Sec. 2 "2. Double Quantization"; [65B] "Double
+         quantization"): subtract the mean of the constants first.  Reading: one mean per
+         tensor over all its c1, mu = fl32(fl64(exact sum) / n_blocks).
+      4. d = fl32(c1 - mu); groups of 256 consecutive constants (flattened block order);
+         per group c2s = fl32(max|d| / 448) is the FP32 second-level constant, and
+         code8 = E4M3_RNE(fl32(d / c2s)) (code8 = 0 when c2s == 0).
+    Returns a dict of the stored buffers plus the transient c1 and the unpacked codes.
+    """
+    W = np.asarray(W, dtype=np.float32)
+    assert W.ndim == 2 and W.shape[1] % BLOCK1 == 0
+    if not np.all(np.isfinite(W)):
+        raise ValueError("non-finite weight")
+    d_out, d_in = W.shape
+    table = nf4_codebook()
+
+    blocks = W.reshape(-1, BLOCK1)
+    c1 = np.max(np.abs(blocks), axis=1).astype(np.float32)
+    n_blocks = c1.size
+
+    codes = np.full(blocks.shape, 8, dtype=np.uint8)
+    nz = c1 > 0
+    rho = np.zeros(blocks.shape, dtype=np.float32)
+    rho[nz] = blocks[nz] / c1[nz][:, None]  # float32 / float32: one IEEE rounding
+    codes[nz] = nearest_level(rho[nz], table)
+
+    mu = np.float32(math.fsum(c1.astype(np.float64).tolist()) / n_blocks)
+
+    d = (c1 - mu).astype(np.float32)
+    n_groups = -(-n_blocks // BLOCK2)
+    c2s = np.zeros(n_groups, dtype=np.float32)
+    code8 = np.zeros(n_blocks, dtype=np.uint8)
+    for g in range(n_groups):
+        seg = d[g * BLOCK2 : (g + 1) * BLOCK2]
+        m = np.max(np.abs(seg))
+        c2 = np.float32(m / np.float32(E4M3_MAX))
+        c2s[g] = c2
+        if c2 > 0:
+            code8[g * BLOCK2 : (g + 1) * BLOCK2] = e4m3_encode((seg / c2).astype(np.float32))
+    return {
+        "d_out": d_out,
+        "d_in": d_in,
+        "codes": codes.reshape(d_out, d_in),
+        "packed": pack_codes(codes).reshape(d_out, d_in // 2),
+        "c1": c1,
+        "mu": mu,
+        "code8": code8,
+        "c2s": c2s,
+    }
+
+
+def decode_scales(code8: np.ndarray, c2s: np.ndarray, mu) -> np.ndarray:
+    """Recovered first-level constants: c1_hat = fl32(fl32(E4M3(code8) * c2s) + mu).
+
+    Two separate FP32 roundings, undoing the mean shift and the second-level scaling of
+    [4-Bit] Sec. 2 "2. Double Quantization" / [65B] "Double quantization"."""
+    code8 = np.asarray(code8, dtype=np.uint8)
+    n = code8.size
+    grp = np.arange(n) // BLOCK2
+    v = e4m3_value(code8).astype(np.float32)  # every finite E4M3 value is exact in FP32
+    prod = (v * np.asarray(c2s, dtype=np.float32)[grp]).astype(np.float32)
+    return (prod + np.float32(mu)).astype(np.float32)
+
+
+def dequantize_bf16_bits(q: dict) -> np.ndarray:
+    """Dequantized weights as BF16 bit patterns [d_out, d_in]:
+    w_hat = bf16(fl32(q[code] * c1_hat)) -- a lookup and a multiply ([65B] "Quantization
+    in one paragraph"), rounded to the BF16 compute type ([4-Bit] Sec. 3)."""
+    table = nf4_codebook()
+    c1h = decode_scales(q["code8"], q["c2s"], q["mu"])
+    codes = q["codes"].reshape(-1, BLOCK1)
+    vals = (table[codes] * c1h[:, None]).astype(np.float32)
+    return bf16_round_bits(vals).reshape(q["d_out"], q["d_in"])
+
+
+def dequantize_f64(q: dict) -> np.ndarray:
+    return bf16_bits_to_f32(dequantize_bf16_bits(q)).astype(np.float64)
+
+
+# --------------------------------------------------------------------------------------
+# LoRA-augmented linear: forward and backward (FP64 over the exact BF16 inputs)
+# --------------------------------------------------------------------------------------
+
+
+def lora_fwd(W_hat: np.ndarray, X: np.ndarray, A: np.ndarray, B: np.ndarray, alpha: float, r: int):
+    """Forward of the frozen quantized linear with its adapter.
+
+    [65B] "Prerequisite: LoRA" and "Where the gradients actually go": h = deq(W) x + B A x;
+    [4-Bit] Sec. 3 scales the adapter branch by alpha/r.  Row-major batch form:
+      T = X A^T  [M, r],   Y = X W_hat^T + (alpha/r) T B^T  [M, d_out].
+    W_hat [d_out, d_in], X [M, d_in], A [r, d_in], B [d_out, r]; all float64.
+    Returns (Y, T)."""
+    s = float(alpha) / float(r)
+    T = X @ A.T
+    Y = X @ W_hat.T + s * (T @ B.T)
+    return Y, T
+
+
+def lora_bwd(W_hat: np.ndarray, X: np.ndarray, dY: np.ndarray, A: np.ndarray, B: np.ndarray, alpha: float, r: int):
+    """Backward ([65B] "Where the gradients actually go"): the input gradient runs through
+    the dequantized frozen weights, and only the adapters receive parameter gradients.
+      G  = dY B                    [M, r]
+      dX = dY W_hat + (alpha/r) G A   [M, d_in]   (chain rule through both branches)
+      dA = (alpha/r) G^T X         [r, d_in]
+      dB = (alpha/r) dY^T T, T = X A^T   [d_out, r]
+    No gradient for W is formed."""
+    s = float(alpha) / float(r)
+    T = X @ A.T
+    G = dY @ B
+    dX = dY @ W_hat + s * (G @ A)
+    dA = s * (G.T @ X)
+    dB = s * (dY.T @ T)
+    return dX, dA, dB
+
+
+# --------------------------------------------------------------------------------------
+# Storage sizes
+# --------------------------------------------------------------------------------------
+
+
+def quant_sizes(d_out: int, d_in: int) -> dict:
+    """Bytes of each stored buffer: 4-bit codes, one 8-bit constant per 64 weights, one
+    FP32 second-level constant per 256 constants, and one FP32 mean per tensor."""
+    n = d_out * d_in
+    n_blocks = n // BLOCK1
+    n_groups = -(-n_blocks // BLOCK2)
+    return {"codes": n // 2, "code8": n_blocks, "c2s": 4 * n_groups, "mu": 4}
+
+
+def bits_per_param(d_out: int, d_in: int, double_quant: bool = True) -> float:
+    """Storage bits per weight.  Without double quantization the constants are FP32 per
+    64 weights ([65B] "Double quantization": 4 + 32/64 = 4.5)."""
+    n = d_out * d_in
+    sz = quant_sizes(d_out, d_in)
+    if not double_quant:
+        return 8.0 * (sz["codes"] + 4 * (n // BLOCK1)) / n
+    return 8.0 * sum(sz.values()) / n

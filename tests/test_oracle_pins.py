@@ -1,0 +1,366 @@
+"""Pins for the CPU oracle: each test checks the oracle against something other than
+itself -- the pages' printed figures, closed forms, other libraries' routines, brute force
+by a different formulation, or invariants the pages state.  CPU only."""
+
+import json
+import math
+import os
+import statistics
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+GIB = float(2**30)
+
+
+# ------------------------------------------------------------------ codebook
+
+def test_codebook_shape_and_endpoints():
+    q = O.nf4_codebook()
+    assert q.dtype == np.float32 and q.shape == (16,)
+    assert np.all(np.diff(q.astype(np.float64)) > 0), "levels strictly increasing"
+    # exact zero with positive sign, exact endpoints (65B page, "NF4")
+    assert q[8] == 0.0 and not np.signbit(q[8])
+    assert q[0] == -1.0 and q[15] == 1.0
+    assert np.sum(q < 0) == 8 and np.sum(q >= 0) == 8
+
+
+def test_codebook_interior_antisymmetry():
+    # q_i / q_{16-i} is one constant for i = 1..7 (literal formula, per-side scaling)
+    ex = O.nf4_codebook_exact()
+    ratios = [float(ex[i] / ex[16 - i]) for i in range(1, 8)]
+    assert max(ratios) - min(ratios) < 1e-40
+    raw15 = 0.5 * (statistics.NormalDist().inv_cdf(15 / 17) + statistics.NormalDist().inv_cdf(16 / 17))
+    raw0 = statistics.NormalDist().inv_cdf(1 / 34)
+    assert ratios[0] == pytest.approx(-raw15 / abs(raw0), rel=1e-12)
+
+
+def _table_from(inv):
+    raw = [inv(1 / 34)] + [0.5 * (inv(i / 17) + inv((i + 1) / 17)) for i in range(1, 16)]
+    raw[8] = 0.0
+    out = [raw[i] / -raw[0] for i in range(8)] + [0.0] + [raw[i] / raw[15] for i in range(9, 16)]
+    return np.array(out, dtype=np.float64)
+
+
+@pytest.mark.parametrize("which", ["statistics", "scipy"])
+def test_codebook_matches_other_quantile_routines(which):
+    """Two other inverse-normal routines (Wichura AS241 in `statistics`, cephes ndtri in
+    SciPy) give the same FP32 table bit for bit."""
+    inv = statistics.NormalDist().inv_cdf if which == "statistics" else (lambda p: float(scipy.special.ndtri(p)))
+    t64 = _table_from(inv)
+    q = O.nf4_codebook()
+    assert np.max(np.abs(t64 - q.astype(np.float64))) < 2e-7
+    assert np.array_equal(t64.astype(np.float32).view(np.uint32), q.view(np.uint32))
+
+
+def test_codebook_levels_sit_in_their_quantile_bins():
+    """Closed-form check through the CDF (math.erfc, not the oracle's erfinv): the
+    un-normalised level i lies between Q(i/17) and Q((i+1)/17), and Phi(Q(j/17)) = j/17."""
+    phi = lambda x: 0.5 * math.erfc(-x / math.sqrt(2.0))
+    for j in range(1, 17):
+        x = float(O.qlora_oracle._q_normal(j, 17))
+        assert phi(x) == pytest.approx(j / 17, abs=1e-15)
+    ex = O.nf4_codebook_exact()
+    scale_pos = float(0.5 * (O.qlora_oracle._q_normal(15, 17) + O.qlora_oracle._q_normal(16, 17)))
+    for i in range(9, 16):
+        raw = float(ex[i]) * scale_pos
+        assert phi(raw) > i / 17 and phi(raw) < (i + 1) / 17
+
+
+# ------------------------------------------------------------------ nearest level
+
+def test_nearest_level_equals_searchsorted_on_midpoints():
+    """Independent formulation: count of exact FP64 midpoints strictly below rho."""
+    q = O.nf4_codebook().astype(np.float64)
+    mids = 0.5 * (q[:-1] + q[1:])
+    rng = np.random.default_rng(0)
+    rho = rng.uniform(-1, 1, 200000).astype(np.float32)
+    # adversarial: the FP32 neighbours of every midpoint, and the midpoints themselves when exact
+    adv = []
+    for m in mids:
+        f = np.float32(m)
+        adv += [f, np.nextafter(f, np.float32(-2)), np.nextafter(f, np.float32(2))]
+    rho = np.concatenate([rho, np.array(adv, dtype=np.float32), O.nf4_codebook()])
+    ours = O.nearest_level(rho, O.nf4_codebook())
+    theirs = np.searchsorted(mids, rho.astype(np.float64), side="left")  # ties -> lower index
+    assert np.array_equal(ours, theirs.astype(np.uint8))
+
+
+def test_nearest_level_tie_goes_low():
+    q = O.nf4_codebook().astype(np.float64)
+    for k in range(15):
+        m = 0.5 * (q[k] + q[k + 1])
+        if np.float64(np.float32(m)) == m:  # exact FP32 midpoint -> a true tie
+            assert O.nearest_level(np.array([m], np.float32), O.nf4_codebook())[0] == k
+
+
+# ------------------------------------------------------------------ packing
+
+def test_pack_roundtrip_and_layout():
+    codes = np.arange(16, dtype=np.uint8).repeat(2)[:32]
+    p = O.pack_codes(codes)
+    assert p.size == 16
+    # group of 8: byte i = e_i | e_{i+4} << 4
+    e = codes[:8]
+    assert list(p[:4]) == [int(e[i]) | (int(e[i + 4]) << 4) for i in range(4)]
+    assert np.array_equal(O.unpack_codes(p), codes)
+
+
+# ------------------------------------------------------------------ E4M3 and BF16
+
+def test_e4m3_decode_matches_torch():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    ours = O.e4m3_value(codes)
+    t = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(ours, t)
+    assert O.e4m3_value(0x7E) == 448.0 and O.e4m3_value(0x01) == 2.0**-9 and O.e4m3_value(0x38) == 1.0
+
+
+def test_e4m3_encode_matches_torch_everywhere_that_matters():
+    vals = O.e4m3_value(np.arange(0, 0x7F)).astype(np.float64)
+    mids = 0.5 * (vals[:-1] + vals[1:])
+    pts = []
+    for m in np.concatenate([vals, mids]):
+        f = np.float32(m)
+        pts += [f, np.nextafter(f, np.float32(0)), np.nextafter(f, np.float32(1e9))]
+    rng = np.random.default_rng(1)
+    pts = np.array(pts, dtype=np.float32)
+    pts = np.concatenate([pts, -pts, rng.uniform(-448, 448, 100000).astype(np.float32),
+                          (rng.standard_normal(20000) * 1e-3).astype(np.float32)])
+    pts = pts[np.abs(pts) <= 448]
+    ours = O.e4m3_encode(pts)
+    theirs = torch.from_numpy(pts.copy()).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, theirs)
+
+
+def test_e4m3_signed_zero():
+    assert O.e4m3_encode(np.array([-1e-30], np.float32))[0] == 0x80
+    assert O.e4m3_encode(np.array([1e-30], np.float32))[0] == 0x00
+
+
+def test_bf16_round_matches_torch():
+    rng = np.random.default_rng(2)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 3,
+                        np.array([1 + 2**-8, 1 + 3 * 2**-8, -(1 + 2**-8), 0.0, -0.0, 1e-40], np.float32)])
+    ours = O.bf16_round_bits(x)
+    theirs = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, theirs)
+
+
+# ------------------------------------------------------------------ quantize / DQ
+
+def _randW(n, k, seed=0, std=0.02):
+    return (np.random.default_rng(seed).standard_normal((n, k)) * std).astype(np.float32)
+
+
+def test_absmax_element_is_an_endpoint_and_decodes_to_scale():
+    W = _randW(32, 256)
+    q = O.quantize(W)
+    blocks = W.reshape(-1, 64)
+    idx = np.argmax(np.abs(blocks), axis=1)
+    codes = q["codes"].reshape(-1, 64)
+    picked = codes[np.arange(codes.shape[0]), idx]
+    sgn = blocks[np.arange(blocks.shape[0]), idx] > 0
+    assert np.all(picked == np.where(sgn, 15, 0))
+    c1h = O.decode_scales(q["code8"], q["c2s"], q["mu"])
+    what = O.bf16_bits_to_f32(O.dequantize_bf16_bits(q)).reshape(-1, 64)
+    got = what[np.arange(what.shape[0]), idx]
+    exp = O.bf16_bits_to_f32(O.bf16_round_bits(np.where(sgn, c1h, -c1h)))
+    assert np.array_equal(got, exp)
+
+
+def test_zero_stays_zero():
+    W = _randW(8, 128, seed=3)
+    W[0, 5] = 0.0
+    W[3, 64:128] = 0.0  # an all-zero block
+    q = O.quantize(W)
+    assert q["codes"][0, 5] == 8 and np.all(q["codes"][3, 64:128] == 8)
+    what = O.bf16_bits_to_f32(O.dequantize_bf16_bits(q))
+    assert what[0, 5] == 0.0 and np.all(what[3, 64:128] == 0.0)
+    assert q["c1"][3 * 2 + 1] == 0.0
+
+
+def test_outlier_only_damages_its_own_block():
+    W = _randW(16, 256, seed=4)
+    a = O.quantize(W)
+    W2 = W.copy()
+    W2[5, 70] = 3.0  # block (5, 1)
+    b = O.quantize(W2)
+    ca, cb = a["codes"].reshape(-1, 64), b["codes"].reshape(-1, 64)
+    changed = np.nonzero(np.any(ca != cb, axis=1))[0]
+    assert list(changed) == [5 * 4 + 1]
+
+
+def test_roundtrip_special_case_is_exact():
+    """Every block holds +-c plus entries c*q_k (c a power of two): rho = q_k exactly,
+    every c1 = c so mu = c, d = 0, c2s = 0, code8 = 0, c1_hat = c, and w_hat = bf16(W)."""
+    q = O.nf4_codebook()
+    rng = np.random.default_rng(5)
+    c = np.float32(2.0**-6)
+    k = rng.integers(0, 16, size=(64, 512)).astype(np.int64)
+    k[:, ::64] = 15
+    W = (q[k] * c).astype(np.float32)
+    qq = O.quantize(W)
+    assert np.array_equal(qq["codes"], k.astype(np.uint8))
+    assert qq["mu"] == c and np.all(qq["c2s"] == 0) and np.all(qq["code8"] == 0)
+    expected = torch.from_numpy(W).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.dequantize_bf16_bits(qq), expected)
+
+
+def test_mean_is_exact_closed_form():
+    """Block absmaxes j * 2^-10 for j = 1..n: the exact mean is (n+1)/2 * 2^-10."""
+    n = 1024
+    W = np.zeros((n, 64), np.float32)
+    W[:, 0] = np.arange(1, n + 1, dtype=np.float32) * np.float32(2.0**-10)
+    W[:, 1] = -0.5 * W[:, 0]
+    q = O.quantize(W)
+    assert q["mu"] == np.float32((n + 1) / 2 * 2.0**-10)
+
+
+def test_double_quant_error_bound():
+    W = _randW(256, 1024, seed=6)
+    q = O.quantize(W)
+    c1, mu = q["c1"].astype(np.float64), float(q["mu"])
+    c1h = O.decode_scales(q["code8"], q["c2s"], q["mu"]).astype(np.float64)
+    d = c1 - mu
+    c2s = q["c2s"].astype(np.float64)[np.arange(c1.size) // 256]
+    bound = np.abs(d) * 2.0**-4 + c2s * 2.0**-10 + 2.0**-23 * (np.abs(c1) + np.abs(d) + 1e-30)
+    assert np.all(np.abs(c1h - c1) <= bound)
+    # a group's largest |d| maps to +-448 exactly
+    for g in range(q["c2s"].size):
+        seg = np.abs(d[g * 256:(g + 1) * 256])
+        j = g * 256 + int(np.argmax(seg))
+        assert (q["code8"][j] & 0x7F) == 0x7E
+
+
+def test_quantize_rejects_non_finite():
+    W = _randW(4, 64)
+    W[1, 3] = np.inf
+    with pytest.raises(ValueError):
+        O.quantize(W)
+
+
+def test_brute_force_tiny_tensor_by_hand():
+    """Recompute a tiny quantization with plain Python loops and floats."""
+    W = _randW(2, 64, seed=7)
+    q = O.quantize(W)
+    table = [float(v) for v in O.nf4_codebook()]
+    for r in range(2):
+        c = max(abs(float(w)) for w in W[r])
+        for j in range(64):
+            rho = float(np.float32(W[r, j]) / np.float32(c))
+            best = min(range(16), key=lambda k: (abs(rho - table[k]), k))
+            assert q["codes"][r, j] == best
+
+
+# ------------------------------------------------------------------ the pages' figures
+
+def _page(fig_id):
+    with open(os.path.join(GOLDEN, "page_figures.json")) as f:
+        figs = {d["id"]: d for d in json.load(f)["figures"]}
+    return figs[fig_id]
+
+
+def _check(fig_id, value):
+    d = _page(fig_id)
+    assert round(value, d["digits"]) == pytest.approx(d["value"]), (fig_id, value, d)
+
+
+def test_page_figures_bits_per_param():
+    bpp = O.bits_per_param(4096, 4096)
+    _check("bits_dq", bpp)
+    _check("overhead_dq", bpp - 4.0)
+    _check("overhead_first_level", O.bits_per_param(4096, 4096, double_quant=False) - 4.0)
+    _check("bits_no_dq", O.bits_per_param(4096, 4096, double_quant=False))
+    _check("saved_dq", O.bits_per_param(4096, 4096, double_quant=False) - bpp)
+
+
+def test_page_figures_memory():
+    bytes_per_param = O.bits_per_param(4096, 4096) / 8.0
+    _check("base_8b_nf4dq_gb", 8.03e9 * bytes_per_param / GIB)
+    _check("base_8b_bf16_gb", 8.03e9 * 2 / GIB)
+    _check("base_14b_gb", 14e9 * 0.516 / GIB)
+    shapes = [(4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096), (14336, 4096), (14336, 4096), (4096, 14336)]
+    n_adapter = 32 * sum(16 * (a + b) for a, b in shapes)
+    _check("lora_8b_params", n_adapter)
+    _check("lora_8b_w_grad_gb", n_adapter * 4 / GIB)
+    _check("lora_8b_adamw_gb", n_adapter * 12 / GIB)
+    _check("lora_4096_r16_params", 16 * (4096 + 4096))
+    _check("lora_4096_r16_factor", 4096 * 4096 / (16 * 8192))
+    _check("constants_65b_gb", (O.bits_per_param(4096, 4096, double_quant=False) - 4) * 65e9 / 8 / 1e9)
+    _check("weights_65b_4bit_gb", 65e9 * 4 / 8 / 1e9)
+
+
+# ------------------------------------------------------------------ forward / backward
+
+def _case(M=6, N=24, K=128, r=4, seed=8):
+    rng = np.random.default_rng(seed)
+    What = rng.standard_normal((N, K))
+    X = rng.standard_normal((M, K))
+    A = rng.standard_normal((r, K)) / math.sqrt(K)
+    B = rng.standard_normal((N, r)) * 0.1
+    dY = rng.standard_normal((M, N))
+    return What, X, A, B, dY
+
+
+def test_fwd_bwd_match_torch_autograd():
+    What, X, A, B, dY = _case()
+    alpha, r = 8.0, 4
+    Y, T = O.lora_fwd(What, X, A, B, alpha, r)
+    dX, dA, dB = O.lora_bwd(What, X, dY, A, B, alpha, r)
+    tW = torch.tensor(What)
+    tX = torch.tensor(X, requires_grad=True)
+    tA = torch.tensor(A, requires_grad=True)
+    tB = torch.tensor(B, requires_grad=True)
+    h = torch.nn.functional.linear(tX, tW) + (alpha / r) * torch.nn.functional.linear(torch.nn.functional.linear(tX, tA), tB)
+    h.backward(torch.tensor(dY))
+    assert np.allclose(Y, h.detach().numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(dX, tX.grad.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(dA, tA.grad.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(dB, tB.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_bwd_matches_finite_differences():
+    What, X, A, B, dY = _case(M=3, N=8, K=64, r=2, seed=9)
+    alpha, r = 4.0, 2
+    L = lambda X_, A_, B_: float(np.sum(O.lora_fwd(What, X_, A_, B_, alpha, r)[0] * dY))
+    dX, dA, dB = O.lora_bwd(What, X, dY, A, B, alpha, r)
+    eps = 1e-6
+    for arr, g in ((X, dX), (A, dA), (B, dB)):
+        for idx in [(0, 0), (1, 1), (arr.shape[0] - 1, arr.shape[1] - 1)]:
+            p, m = arr.copy(), arr.copy()
+            p[idx] += eps
+            m[idx] -= eps
+            args_p = [p if arr is a else a for a in (X, A, B)]
+            args_m = [m if arr is a else a for a in (X, A, B)]
+            fd = (L(*args_p) - L(*args_m)) / (2 * eps)
+            assert fd == pytest.approx(g[idx], rel=1e-6, abs=1e-8)
+
+
+def test_fwd_one_hot_inputs_pick_columns():
+    """X = e_j rows pick column j of W_hat; with W_hat = 0 and one-hot adapters the LoRA
+    term is alpha/r * B[n, a] * A[a, j]: catches a transposed operand or a wrong scale."""
+    N, K, r = 5, 64, 3
+    rng = np.random.default_rng(10)
+    What = rng.standard_normal((N, K))
+    X = np.zeros((2, K)); X[0, 7] = 1; X[1, 40] = 1
+    A = np.zeros((r, K)); B = np.zeros((N, r))
+    Y, _ = O.lora_fwd(What, X, A, B, 6.0, r)
+    assert np.array_equal(Y[0], What[:, 7]) and np.array_equal(Y[1], What[:, 40])
+    A[1, 40] = 1.0; B[3, 1] = 1.0
+    Y, _ = O.lora_fwd(np.zeros((N, K)), X, A, B, 6.0, r)
+    exp = np.zeros((2, N)); exp[1, 3] = 2.0
+    assert np.array_equal(Y, exp)
+
+
+def test_special_cases_alpha_zero_and_B_zero():
+    What, X, A, B, dY = _case(seed=11)
+    Y0, _ = O.lora_fwd(What, X, A, B, 0.0, 4)
+    assert np.allclose(Y0, X @ What.T)
+    dX, dA, dB = O.lora_bwd(What, X, dY, A, np.zeros_like(B), 8.0, 4)
+    assert np.all(dA == 0) and np.allclose(dX, dY @ What)
