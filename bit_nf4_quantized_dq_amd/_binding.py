@@ -1,0 +1,266 @@
+"""ctypes binding of include/qlora.h.  Argument marshalling only: torch tensors provide
+device memory (``data_ptr``) and the stream (``cuda_stream``); every step of the method runs
+in the HIP library."""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libqlora_nf4.so")
+
+OP_QUANTIZE, OP_FWD, OP_BWD = 0, 1, 2
+KERNEL_IDS = {
+    "quant_pass1": 0,
+    "quant_pass2": 1,
+    "dequant": 2,
+    "gemv_fwd": 3,
+    "gemm_fwd": 4,
+    "gemm_dx": 5,
+    "lora_down": 6,
+    "lora_grad": 7,
+}
+
+
+class QLoRAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {_strerror(status)} (status {status})")
+        self.status = status
+
+
+class _Nf4dq(ctypes.Structure):
+    _fields_ = [
+        ("codes", ctypes.c_void_p),
+        ("code8", ctypes.c_void_p),
+        ("c2s", ctypes.c_void_p),
+        ("mu", ctypes.c_void_p),
+        ("d_out", ctypes.c_int64),
+        ("d_in", ctypes.c_int64),
+        ("block1", ctypes.c_int32),
+        ("block2", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = path or _LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"HIP library not built: {p} (run python -m bit_nf4_quantized_dq_amd.build)")
+    L = ctypes.CDLL(p)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    P = ctypes.POINTER
+    sig = {
+        "qlora_quant_sizes": (i64, i64, P(sz), P(sz), P(sz)),
+        "qlora_workspace_size": (ctypes.c_int, i64, i64, i64, i32, P(sz)),
+        "qlora_nf4_codebook": (P(ctypes.c_float),),
+        "qlora_quantize": (vp, P(_Nf4dq), P(ctypes.c_float), vp, sz, vp),
+        "qlora_dequantize": (P(_Nf4dq), vp, vp),
+        "qlora_linear_fwd": (P(_Nf4dq), vp, i64, vp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp),
+        "qlora_linear_bwd": (P(_Nf4dq), vp, vp, i64, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp),
+        "qlora_e4m3_encode": (vp, vp, i64, vp),
+        "qlora_timing_enable": (ctypes.c_int,),
+        "qlora_timing_read": (ctypes.c_int, P(ctypes.c_double), P(i64)),
+        "qlora_strerror": (ctypes.c_int,),
+    }
+    for name, args in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = list(args)
+        fn.restype = ctypes.c_int
+    L.qlora_strerror.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+class _LazyLib:
+    def __getattr__(self, name):
+        return getattr(load_library(), name)
+
+
+lib = _LazyLib()
+
+
+def _strerror(status: int) -> str:
+    try:
+        return load_library().qlora_strerror(status).decode()
+    except Exception:  # noqa: BLE001
+        return "?"
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise QLoRAError(status, what)
+
+
+def _stream(t: torch.Tensor | None = None) -> int:
+    dev = t.device if t is not None else torch.device("cuda")
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, dtype, name: str) -> None:
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name}: need a contiguous {dtype} CUDA tensor, got {t.dtype} on {t.device}")
+
+
+def quant_sizes(d_out: int, d_in: int) -> tuple[int, int, int]:
+    a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load_library().qlora_quant_sizes(d_out, d_in, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)), "quant_sizes")
+    return a.value, b.value, c.value
+
+
+def workspace_size(op: int, M: int, d_out: int, d_in: int, r: int) -> int:
+    n = ctypes.c_size_t()
+    _check(load_library().qlora_workspace_size(op, M, d_out, d_in, r, ctypes.byref(n)), "workspace_size")
+    return n.value
+
+
+def nf4_codebook() -> list[float]:
+    arr = (ctypes.c_float * 16)()
+    _check(load_library().qlora_nf4_codebook(arr), "nf4_codebook")
+    return list(arr)
+
+
+@dataclasses.dataclass
+class QuantizedWeight:
+    """Device buffers of one NF4 + DQ tensor (owned by these torch tensors)."""
+
+    codes: torch.Tensor  # uint8 [d_out * d_in / 2]
+    code8: torch.Tensor  # uint8 [d_out * d_in / 64]
+    c2s: torch.Tensor  # float32 [ceil(n_blocks / 256)]
+    mu: torch.Tensor  # float32 [1]
+    d_out: int
+    d_in: int
+
+    @classmethod
+    def empty(cls, d_out: int, d_in: int, device="cuda") -> "QuantizedWeight":
+        nc, n8, n2 = quant_sizes(d_out, d_in)
+        return cls(
+            codes=torch.empty(nc, dtype=torch.uint8, device=device),
+            code8=torch.empty(n8, dtype=torch.uint8, device=device),
+            c2s=torch.empty(n2 // 4, dtype=torch.float32, device=device),
+            mu=torch.empty(1, dtype=torch.float32, device=device),
+            d_out=d_out,
+            d_in=d_in,
+        )
+
+    def struct(self) -> _Nf4dq:
+        return _Nf4dq(self.codes.data_ptr(), self.code8.data_ptr(), self.c2s.data_ptr(), self.mu.data_ptr(),
+                      self.d_out, self.d_in, 64, 256)
+
+    def nbytes(self) -> int:
+        return self.codes.numel() + self.code8.numel() + 4 * self.c2s.numel() + 4
+
+
+class _Workspace:
+    """Per-device scratch buffers grown on demand (allocated through torch)."""
+
+    def __init__(self):
+        self._bufs: dict = {}
+
+    def get(self, nbytes: int, device: torch.device, key: str = "ws") -> torch.Tensor:
+        k = (device.index if device.index is not None else torch.cuda.current_device(), key)
+        buf = self._bufs.get(k)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+            self._bufs[k] = buf
+        return buf
+
+
+_WS = _Workspace()
+
+
+def quantize(W: torch.Tensor, out: QuantizedWeight | None = None, ws: torch.Tensor | None = None) -> QuantizedWeight:
+    """Quantize an FP32 [d_out, d_in] CUDA tensor (synchronizes the current stream once)."""
+    _dev(W, torch.float32, "W")
+    d_out, d_in = W.shape
+    q = out if out is not None else QuantizedWeight.empty(d_out, d_in, W.device)
+    need = workspace_size(OP_QUANTIZE, 1, d_out, d_in, 1)
+    ws = ws if ws is not None else _WS.get(need, W.device, "quant")
+    mu = ctypes.c_float()
+    s = q.struct()
+    _check(load_library().qlora_quantize(W.data_ptr(), ctypes.byref(s), ctypes.byref(mu), ws.data_ptr(), ws.numel(),
+                                         _stream(W)), "quantize")
+    return q
+
+
+def dequantize(q: QuantizedWeight, out: torch.Tensor | None = None) -> torch.Tensor:
+    """BF16 [d_out, d_in] w_hat, bit-exact."""
+    out = out if out is not None else torch.empty(q.d_out, q.d_in, dtype=torch.bfloat16, device=q.codes.device)
+    _dev(out, torch.bfloat16, "out")
+    s = q.struct()
+    _check(load_library().qlora_dequantize(ctypes.byref(s), out.data_ptr(), _stream(out)), "dequantize")
+    return out
+
+
+def linear_fwd(q: QuantizedWeight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor, alpha: float,
+               Y: torch.Tensor | None = None, T_save: torch.Tensor | None = None,
+               ws: torch.Tensor | None = None) -> torch.Tensor:
+    """Y = X w_hat^T + (alpha/r) (X A^T) B^T.  X [M, d_in], A [r, d_in], B [d_out, r] BF16."""
+    for t, n in ((X, "X"), (A, "A"), (B, "B")):
+        _dev(t, torch.bfloat16, n)
+    M, r = X.shape[0], A.shape[0]
+    Y = Y if Y is not None else torch.empty(M, q.d_out, dtype=torch.bfloat16, device=X.device)
+    _dev(Y, torch.bfloat16, "Y")
+    if T_save is not None:
+        _dev(T_save, torch.bfloat16, "T_save")
+    need = workspace_size(OP_FWD, M, q.d_out, q.d_in, r)
+    ws = ws if ws is not None else _WS.get(need, X.device, "fwd")
+    s = q.struct()
+    _check(load_library().qlora_linear_fwd(ctypes.byref(s), X.data_ptr(), M, A.data_ptr(), B.data_ptr(), r,
+                                           float(alpha), Y.data_ptr(), _ptr(T_save), ws.data_ptr(), ws.numel(),
+                                           _stream(X)), "linear_fwd")
+    return Y
+
+
+def linear_bwd(q: QuantizedWeight, X: torch.Tensor, dY: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+               alpha: float, T_saved: torch.Tensor | None = None, need_dX: bool = True,
+               dX: torch.Tensor | None = None, dA: torch.Tensor | None = None, dB: torch.Tensor | None = None,
+               ws: torch.Tensor | None = None):
+    """Returns (dX or None, dA, dB), all BF16."""
+    for t, n in ((X, "X"), (dY, "dY"), (A, "A"), (B, "B")):
+        _dev(t, torch.bfloat16, n)
+    M, r = X.shape[0], A.shape[0]
+    dev = X.device
+    if need_dX and dX is None:
+        dX = torch.empty(M, q.d_in, dtype=torch.bfloat16, device=dev)
+    dA = dA if dA is not None else torch.empty(r, q.d_in, dtype=torch.bfloat16, device=dev)
+    dB = dB if dB is not None else torch.empty(q.d_out, r, dtype=torch.bfloat16, device=dev)
+    need = workspace_size(OP_BWD, M, q.d_out, q.d_in, r)
+    ws = ws if ws is not None else _WS.get(need, dev, "bwd")
+    s = q.struct()
+    _check(load_library().qlora_linear_bwd(ctypes.byref(s), X.data_ptr(), dY.data_ptr(), M, A.data_ptr(),
+                                           B.data_ptr(), r, float(alpha), _ptr(T_saved),
+                                           _ptr(dX if need_dX else None), dA.data_ptr(), dB.data_ptr(),
+                                           ws.data_ptr(), ws.numel(), _stream(X)), "linear_bwd")
+    return (dX if need_dX else None), dA, dB
+
+
+def e4m3_encode(x: torch.Tensor) -> torch.Tensor:
+    _dev(x, torch.float32, "x")
+    out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _check(load_library().qlora_e4m3_encode(x.data_ptr(), out.data_ptr(), x.numel(), _stream(x)), "e4m3_encode")
+    return out
+
+
+def timing_enable(on: bool) -> None:
+    _check(load_library().qlora_timing_enable(1 if on else 0), "timing_enable")
+
+
+def timing_read(kernel: str) -> tuple[float, int]:
+    """(total ms, launches) of one kernel since the last read; waits for its events."""
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    _check(load_library().qlora_timing_read(KERNEL_IDS[kernel], ctypes.byref(ms), ctypes.byref(n)), "timing_read")
+    return ms.value, n.value

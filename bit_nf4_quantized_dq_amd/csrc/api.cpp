@@ -1,0 +1,403 @@
+// C ABI of the NF4 + double-quantized LoRA linear (declared in include/qlora.h).
+// Validates arguments, carves the caller's workspace, picks launch shapes and enqueues the
+// kernels.  The only host-side arithmetic of the method is the exact mean of the block
+// constants for double quantization, folded from the per-exponent integer sums that the
+// first quantize pass gathers.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/qlora.h"
+#include "qlora_host.h"
+
+using namespace qlora;
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP; }
+
+int check_wq(const qlora_nf4dq_t* Wq) {
+  if (!Wq || !Wq->codes || !Wq->code8 || !Wq->c2s || !Wq->mu) return QLORA_ERR_INVALID_ARG;
+  if (Wq->block1 != 64 || Wq->block2 != 256) return QLORA_ERR_UNSUPPORTED;
+  if (Wq->d_out < 16 || Wq->d_in < 64 || Wq->d_in % 64 != 0 || Wq->d_out % 16 != 0) return QLORA_ERR_BAD_SHAPE;
+  if (Wq->d_out > kMaxElems / Wq->d_in) return QLORA_ERR_BAD_SHAPE;
+  if (!aligned16(Wq->codes)) return QLORA_ERR_INVALID_ARG;
+  return QLORA_OK;
+}
+
+int check_lora(int64_t M, int32_t r, float alpha) {
+  if (M < 1 || M > (int64_t(1) << 24)) return QLORA_ERR_INVALID_ARG;
+  if (r < 1 || r > 128) return QLORA_ERR_INVALID_ARG;
+  if (!std::isfinite(alpha)) return QLORA_ERR_INVALID_ARG;
+  return QLORA_OK;
+}
+
+// ---- launch shapes of the skinny LoRA kernels
+struct RowdotShape {
+  int32_t ksplit;
+  int64_t kps;
+};
+RowdotShape rowdot_shape(int64_t M, int64_t Kd) {
+  const int64_t gm = (M + 15) / 16;
+  int64_t ks = std::max<int64_t>(1, std::min<int64_t>((512 + gm - 1) / gm, Kd / 128));
+  int64_t kps = align_up((size_t)((Kd + ks - 1) / ks), 128);
+  ks = (Kd + kps - 1) / kps;
+  return {(int32_t)ks, kps};
+}
+
+struct ColdotShape {
+  int32_t msplit;
+  int64_t mps;
+};
+ColdotShape coldot_shape(int64_t M, int32_t R, int64_t C) {
+  const int64_t gc = ((C + 511) / 512) * ((R + 15) / 16);
+  int64_t ms = std::max<int64_t>(1, std::min<int64_t>((512 + gc - 1) / gc, (M + 63) / 64));
+  const int64_t mps = (M + ms - 1) / ms;
+  ms = (M + mps - 1) / mps;
+  return {(int32_t)ms, mps};
+}
+
+int32_t gemv_ksplit(int64_t N, int64_t K) {
+  const int64_t tiles = (N + 15) / 16;
+  const int64_t nb = K / 64;
+  return (int32_t)std::max<int64_t>(1, std::min<int64_t>((512 + tiles - 1) / tiles, nb / 4));
+}
+
+constexpr int64_t kGemvMaxM = 16;
+
+// ---- workspace layouts
+struct FwdWs {
+  size_t tpart, ypart, ls, total;
+};
+FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
+  FwdWs w{};
+  const RowdotShape rs = rowdot_shape(M, K);
+  size_t off = 0;
+  w.tpart = off;
+  off = align_up(off + sizeof(float) * rs.ksplit * M * r, 256);
+  w.ypart = off;
+  if (M <= kGemvMaxM) {
+    const int32_t ks = gemv_ksplit(N, K);
+    if (ks > 1) off = align_up(off + sizeof(float) * ks * M * N, 256);
+  }
+  w.ls = off;
+  if (M > kGemvMaxM) off = align_up(off + 2 * M * r, 256);
+  w.total = std::max<size_t>(off, 256);
+  return w;
+}
+
+struct BwdWs {
+  size_t tpart, t, g, lg, bt, cpart, total;
+};
+BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
+  BwdWs w{};
+  const RowdotShape rt = rowdot_shape(M, K), rg = rowdot_shape(M, N);
+  const ColdotShape ca = coldot_shape(M, r, K), cb = coldot_shape(M, r, N);
+  size_t off = 0;
+  w.tpart = off;
+  off = align_up(off + sizeof(float) * std::max<int64_t>(rt.ksplit, rg.ksplit) * M * r, 256);
+  w.t = off;
+  off = align_up(off + 2 * M * r, 256);
+  w.g = off;
+  off = align_up(off + 2 * M * r, 256);
+  w.lg = off;
+  off = align_up(off + 2 * M * r, 256);
+  w.bt = off;
+  off = align_up(off + 2 * (size_t)r * N, 256);
+  w.cpart = off;
+  off = align_up(off + sizeof(float) * std::max<int64_t>((int64_t)ca.msplit * r * K, (int64_t)cb.msplit * r * N), 256);
+  w.total = off;
+  return w;
+}
+
+size_t quant_ws(int64_t d_out, int64_t d_in) {
+  const int64_t nb = d_out * d_in / 64;
+  return align_up(sizeof(float) * nb, 256) + 256 * sizeof(unsigned long long) + 256;
+}
+
+// ---- exact mean: value = sum_e S_e * 2^(e-150) (e >= 1), folded in a big integer and
+// rounded once to double (nearest, ties to even).
+double exact_sum_to_double(const unsigned long long hist[256]) {
+  // bit i of the integer has weight 2^(i - 149); bin e contributes S_e << (e - 1)
+  constexpr int kWords = 12;  // 384 bits > 253 + 64 + margin
+  uint64_t big[kWords] = {0};
+  for (int e = 1; e < 256; ++e) {
+    const uint64_t s = hist[e];
+    if (!s) continue;
+    const int sh = e - 1, w = sh / 64, b = sh % 64;
+    unsigned __int128 add = (unsigned __int128)s << b;
+    for (int i = w; i < kWords && add; ++i) {
+      const unsigned __int128 cur = (unsigned __int128)big[i] + (uint64_t)add;
+      big[i] = (uint64_t)cur;
+      add = (add >> 64) + (cur >> 64);
+    }
+  }
+  int top = -1;
+  for (int i = kWords - 1; i >= 0 && top < 0; --i)
+    if (big[i]) top = i * 64 + 63 - __builtin_clzll(big[i]);
+  if (top < 0) return 0.0;
+  auto bit = [&](int i) -> uint64_t { return i < 0 ? 0 : (big[i / 64] >> (i % 64)) & 1u; };
+  if (top < 53) {
+    uint64_t v = 0;
+    for (int i = top; i >= 0; --i) v = (v << 1) | bit(i);
+    return std::ldexp((double)v, -149);
+  }
+  uint64_t mant = 0;
+  for (int i = top; i > top - 53; --i) mant = (mant << 1) | bit(i);
+  const int lsb_pos = top - 52;
+  const uint64_t guard = bit(lsb_pos - 1);
+  bool sticky = false;
+  for (int i = lsb_pos - 2; i >= 0 && !sticky; --i) sticky = bit(i) != 0;
+  if (guard && (sticky || (mant & 1))) mant += 1;  // may carry to 2^53: still exact in double
+  return std::ldexp((double)mant, lsb_pos - 149);
+}
+
+// ---- kernel timing
+struct TimingState {
+  std::mutex mu;
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[QLORA_K_COUNT];
+  size_t used[QLORA_K_COUNT] = {0};
+};
+TimingState& timing() {
+  static TimingState t;
+  return t;
+}
+
+}  // namespace
+
+namespace qlora {
+
+LaunchTimer::LaunchTimer(int kernel_id, hipStream_t s) : id(kernel_id), stream(s), slot(nullptr) {
+  TimingState& T = timing();
+  std::lock_guard<std::mutex> lk(T.mu);
+  if (!T.on || id < 0 || id >= QLORA_K_COUNT) return;
+  auto& v = T.ev[id];
+  if (T.used[id] == v.size()) {
+    hipEvent_t a, b;
+    if (hipEventCreate(&a) != hipSuccess) return;
+    if (hipEventCreate(&b) != hipSuccess) { hipEventDestroy(a); return; }
+    v.emplace_back(a, b);
+  }
+  const size_t idx = T.used[id]++;
+  hipEventRecord(v[idx].first, stream);
+  slot = reinterpret_cast<void*>(idx + 1);
+}
+
+LaunchTimer::~LaunchTimer() {
+  if (!slot) return;
+  TimingState& T = timing();
+  std::lock_guard<std::mutex> lk(T.mu);
+  const size_t idx = reinterpret_cast<size_t>(slot) - 1;
+  hipEventRecord(T.ev[id][idx].second, stream);
+}
+
+}  // namespace qlora
+
+extern "C" {
+
+const char* qlora_strerror(int status) {
+  switch (status) {
+    case QLORA_OK: return "ok";
+    case QLORA_ERR_INVALID_ARG: return "invalid argument";
+    case QLORA_ERR_BAD_SHAPE: return "bad shape (need d_in % 64 == 0, d_out % 16 == 0)";
+    case QLORA_ERR_UNSUPPORTED: return "unsupported block sizes (need 64, 256)";
+    case QLORA_ERR_NONFINITE: return "non-finite weight";
+    case QLORA_ERR_WORKSPACE: return "workspace too small";
+    case QLORA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int qlora_quant_sizes(int64_t d_out, int64_t d_in, size_t* codes_bytes, size_t* code8_bytes, size_t* c2s_bytes) {
+  if (!codes_bytes || !code8_bytes || !c2s_bytes) return QLORA_ERR_INVALID_ARG;
+  if (d_out < 16 || d_in < 64 || d_in % 64 || d_out % 16 || d_out > kMaxElems / d_in) return QLORA_ERR_BAD_SHAPE;
+  const int64_t n = d_out * d_in, nb = n / 64;
+  *codes_bytes = (size_t)(n / 2);
+  *code8_bytes = (size_t)nb;
+  *c2s_bytes = sizeof(float) * (size_t)((nb + 255) / 256);
+  return QLORA_OK;
+}
+
+int qlora_workspace_size(int op, int64_t M, int64_t d_out, int64_t d_in, int32_t r, size_t* ws_bytes) {
+  if (!ws_bytes) return QLORA_ERR_INVALID_ARG;
+  if (d_out < 16 || d_in < 64 || d_in % 64 || d_out % 16 || d_out > kMaxElems / d_in) return QLORA_ERR_BAD_SHAPE;
+  if (op == QLORA_OP_QUANTIZE) {
+    *ws_bytes = quant_ws(d_out, d_in);
+    return QLORA_OK;
+  }
+  int st = check_lora(M, r, 1.0f);
+  if (st) return st;
+  if (op == QLORA_OP_FWD) *ws_bytes = fwd_ws(M, d_out, d_in, r).total;
+  else if (op == QLORA_OP_BWD) *ws_bytes = bwd_ws(M, d_out, d_in, r).total;
+  else return QLORA_ERR_INVALID_ARG;
+  return QLORA_OK;
+}
+
+int qlora_nf4_codebook(float out16[16]) {
+  if (!out16) return QLORA_ERR_INVALID_ARG;
+  std::memcpy(out16, nf4_tables().q, sizeof(float) * 16);
+  return QLORA_OK;
+}
+
+int qlora_quantize(const float* W, const qlora_nf4dq_t* Wq, float* host_mu, void* ws, size_t ws_bytes,
+                   hipStream_t stream) {
+  int st = check_wq(Wq);
+  if (st) return st;
+  if (!W || !aligned16(W)) return QLORA_ERR_INVALID_ARG;
+  const int64_t n = Wq->d_out * Wq->d_in, nb = n / 64;
+  if (!ws || ws_bytes < quant_ws(Wq->d_out, Wq->d_in)) return QLORA_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  float* c1 = reinterpret_cast<float*>(base);
+  auto* hist = reinterpret_cast<unsigned long long*>(base + align_up(sizeof(float) * nb, 256));
+  int* flag = reinterpret_cast<int*>(hist + 256);
+  hipError_t e = hipMemsetAsync(hist, 0, 256 * sizeof(unsigned long long) + 256, stream);
+  if (e != hipSuccess) return QLORA_ERR_HIP;
+  e = launch_quant_pass1(W, reinterpret_cast<uint32_t*>(Wq->codes), c1, hist, flag, n / 8, nf4_tables(), stream);
+  if (e != hipSuccess) return QLORA_ERR_HIP;
+  unsigned long long h_hist[256];
+  int h_flag = 0;
+  if (hipMemcpyAsync(h_hist, hist, sizeof(h_hist), hipMemcpyDeviceToHost, stream) != hipSuccess) return QLORA_ERR_HIP;
+  if (hipMemcpyAsync(&h_flag, flag, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess) return QLORA_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return QLORA_ERR_HIP;
+  if (h_flag) return QLORA_ERR_NONFINITE;
+  const double mean = exact_sum_to_double(h_hist) / (double)nb;
+  const float mu = (float)mean;
+  if (host_mu) *host_mu = mu;
+  e = launch_quant_pass2(c1, mu, Wq->code8, Wq->c2s, Wq->mu, nb, stream);
+  return hip_status(e);
+}
+
+int qlora_dequantize(const qlora_nf4dq_t* Wq, uint16_t* W_bf16, hipStream_t stream) {
+  int st = check_wq(Wq);
+  if (st) return st;
+  if (!W_bf16 || !aligned16(W_bf16)) return QLORA_ERR_INVALID_ARG;
+  const int64_t n = Wq->d_out * Wq->d_in;
+  return hip_status(launch_dequant(reinterpret_cast<const uint32_t*>(Wq->codes), Wq->code8, Wq->c2s, Wq->mu,
+                                   W_bf16, n / 8, nf4_tables(), stream));
+}
+
+int qlora_linear_fwd(const qlora_nf4dq_t* Wq, const uint16_t* X, int64_t M, const uint16_t* A, const uint16_t* B,
+                     int32_t r, float alpha, uint16_t* Y, uint16_t* T_save, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  int st = check_wq(Wq);
+  if (st) return st;
+  if ((st = check_lora(M, r, alpha))) return st;
+  if (!X || !A || !B || !Y || !aligned16(X) || !aligned16(A) || !aligned16(Y)) return QLORA_ERR_INVALID_ARG;
+  const int64_t N = Wq->d_out, K = Wq->d_in;
+  const FwdWs L = fwd_ws(M, N, K, r);
+  if (!ws || ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  const float s = alpha / (float)r;
+  const uint32_t* codes = reinterpret_cast<const uint32_t*>(Wq->codes);
+  float* tpart = reinterpret_cast<float*>(base + L.tpart);
+  const RowdotShape rs = rowdot_shape(M, K);
+  hipError_t e = launch_rowdot(X, A, M, r, K, rs.ksplit, rs.kps, tpart, stream);
+  if (e != hipSuccess) return QLORA_ERR_HIP;
+  if (M <= kGemvMaxM) {
+    const int32_t ks = gemv_ksplit(N, K);
+    float* ypart = reinterpret_cast<float*>(base + L.ypart);
+    e = launch_gemv_fwd(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, X, M, tpart, rs.ksplit, B, r, s, Y, T_save, ypart,
+                        ks, nf4_tables(), stream);
+    if (e != hipSuccess) return QLORA_ERR_HIP;
+    if (ks > 1) e = launch_gemv_finish(ypart, ks, M, N, tpart, rs.ksplit, B, r, s, Y, T_save, stream);
+    return hip_status(e);
+  }
+  uint16_t* ls = reinterpret_cast<uint16_t*>(base + L.ls);
+  e = launch_rowdot_finish(tpart, rs.ksplit, M, r, s, ls, T_save, stream);
+  if (e != hipSuccess) return QLORA_ERR_HIP;
+  e = launch_gemm_fwd(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, X, M, ls, B, r, Y, nf4_tables(), stream);
+  return hip_status(e);
+}
+
+int qlora_linear_bwd(const qlora_nf4dq_t* Wq, const uint16_t* X, const uint16_t* dY, int64_t M, const uint16_t* A,
+                     const uint16_t* B, int32_t r, float alpha, const uint16_t* T_saved, uint16_t* dX, uint16_t* dA,
+                     uint16_t* dB, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_wq(Wq);
+  if (st) return st;
+  if ((st = check_lora(M, r, alpha))) return st;
+  if (!X || !dY || !A || !B || !dA || !dB) return QLORA_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(dY) || !aligned16(A) || (dX && !aligned16(dX))) return QLORA_ERR_INVALID_ARG;
+  const int64_t N = Wq->d_out, K = Wq->d_in;
+  const BwdWs L = bwd_ws(M, N, K, r);
+  if (!ws || ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  const float s = alpha / (float)r;
+  float* part = reinterpret_cast<float*>(base + L.tpart);
+  uint16_t* t = reinterpret_cast<uint16_t*>(base + L.t);
+  uint16_t* g = reinterpret_cast<uint16_t*>(base + L.g);
+  uint16_t* lg = reinterpret_cast<uint16_t*>(base + L.lg);
+  uint16_t* bt = reinterpret_cast<uint16_t*>(base + L.bt);
+  float* cpart = reinterpret_cast<float*>(base + L.cpart);
+  hipError_t e;
+  const uint16_t* T = T_saved;
+  if (!T) {  // recompute T = X A^T
+    const RowdotShape rt = rowdot_shape(M, K);
+    if ((e = launch_rowdot(X, A, M, r, K, rt.ksplit, rt.kps, part, stream)) != hipSuccess) return QLORA_ERR_HIP;
+    if ((e = launch_rowdot_finish(part, rt.ksplit, M, r, 1.0f, t, nullptr, stream)) != hipSuccess) return QLORA_ERR_HIP;
+    T = t;
+  }
+  // G = dY B  (B^T staged so the reduction index is contiguous)
+  if ((e = launch_transpose_bf16(B, N, r, bt, stream)) != hipSuccess) return QLORA_ERR_HIP;
+  const RowdotShape rg = rowdot_shape(M, N);
+  if ((e = launch_rowdot(dY, bt, M, r, N, rg.ksplit, rg.kps, part, stream)) != hipSuccess) return QLORA_ERR_HIP;
+  if ((e = launch_rowdot_finish(part, rg.ksplit, M, r, s, lg, g, stream)) != hipSuccess) return QLORA_ERR_HIP;
+  // dX = dY w_hat + (s G) A
+  if (dX) {
+    if ((e = launch_gemm_dx(reinterpret_cast<const uint32_t*>(Wq->codes), Wq->code8, Wq->c2s, Wq->mu, N, K, dY, M, lg,
+                            A, r, dX, nf4_tables(), stream)) != hipSuccess)
+      return QLORA_ERR_HIP;
+  }
+  // dA = s G^T X
+  const ColdotShape ca = coldot_shape(M, r, K);
+  if ((e = launch_coldot(g, X, M, r, K, ca.msplit, ca.mps, cpart, stream)) != hipSuccess) return QLORA_ERR_HIP;
+  if ((e = launch_coldot_finish(cpart, ca.msplit, r, K, s, 0, dA, stream)) != hipSuccess) return QLORA_ERR_HIP;
+  // dB = s dY^T T
+  const ColdotShape cb = coldot_shape(M, r, N);
+  if ((e = launch_coldot(T, dY, M, r, N, cb.msplit, cb.mps, cpart, stream)) != hipSuccess) return QLORA_ERR_HIP;
+  if ((e = launch_coldot_finish(cpart, cb.msplit, r, N, s, 1, dB, stream)) != hipSuccess) return QLORA_ERR_HIP;
+  return QLORA_OK;
+}
+
+int qlora_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream) {
+  if (!in || !out || n < 0) return QLORA_ERR_INVALID_ARG;
+  if (n == 0) return QLORA_OK;
+  return hip_status(launch_e4m3_encode(in, out, n, stream));
+}
+
+int qlora_timing_enable(int on) {
+  TimingState& T = timing();
+  std::lock_guard<std::mutex> lk(T.mu);
+  T.on = on != 0;
+  if (T.on)
+    for (auto& u : T.used) u = 0;
+  return QLORA_OK;
+}
+
+int qlora_timing_read(int kernel_id, double* total_ms, int64_t* launches) {
+  if (kernel_id < 0 || kernel_id >= QLORA_K_COUNT || !total_ms || !launches) return QLORA_ERR_INVALID_ARG;
+  TimingState& T = timing();
+  std::lock_guard<std::mutex> lk(T.mu);
+  double sum = 0.0;
+  const size_t n = T.used[kernel_id];
+  for (size_t i = 0; i < n; ++i) {
+    auto& p = T.ev[kernel_id][i];
+    if (hipEventSynchronize(p.second) != hipSuccess) return QLORA_ERR_HIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, p.first, p.second) != hipSuccess) return QLORA_ERR_HIP;
+    sum += ms;
+  }
+  T.used[kernel_id] = 0;
+  *total_ms = sum;
+  *launches = (int64_t)n;
+  return QLORA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Internal host-side declarations of the HIP library: the NF4 tables, kernel launchers
+// (defined next to their kernels) and the launch-timing hook.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "qlora_tables.h"
+
+namespace qlora {
+
+void build_nf4_tables(Nf4Tables* t);
+const Nf4Tables& nf4_tables();
+
+// Brackets one kernel launch with hipEvents when timing is enabled (see qlora_timing_*).
+struct LaunchTimer {
+  LaunchTimer(int kernel_id, hipStream_t s);
+  ~LaunchTimer();
+  int id;
+  hipStream_t stream;
+  void* slot;
+};
+
+// ---- quantize / dequantize (quantize.hip, dequant.hip)
+hipError_t launch_quant_pass1(const float* W, uint32_t* codes, float* c1, unsigned long long* hist,
+                              int* flag, int64_t n_words, const Nf4Tables& T, hipStream_t s);
+hipError_t launch_quant_pass2(const float* c1, float mu, uint8_t* code8, float* c2s, float* mu_out,
+                              int64_t n_blocks, hipStream_t s);
+hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t s);
+hipError_t launch_dequant(const uint32_t* codes, const uint8_t* code8, const float* c2s,
+                          const float* mu, uint16_t* out, int64_t n_words, const Nf4Tables& T,
+                          hipStream_t s);
+
+// ---- LoRA skinny kernels (lora.hip)
+// part[ks][m][j] = sum over k in split ks of P[m,k] * Q[j,k]; P [M,Kd], Q [R,Kd] BF16.
+hipError_t launch_rowdot(const uint16_t* P, const uint16_t* Q, int64_t M, int32_t R, int64_t Kd,
+                         int32_t ksplit, int64_t k_per_split, float* part, hipStream_t s);
+// Fixed-order sum of the partials: out_s = bf16(scale * sum), out_u = bf16(sum); BF16 [M,R],
+// either may be null.
+hipError_t launch_rowdot_finish(const float* part, int32_t ksplit, int64_t M, int32_t R, float scale,
+                                uint16_t* out_s, uint16_t* out_u, hipStream_t s);
+// out[j][c] partials over m-splits of U[m,j] * V[m,c]; U BF16 [M,R], V BF16 [M,C].
+hipError_t launch_coldot(const uint16_t* U, const uint16_t* V, int64_t M, int32_t R, int64_t C,
+                         int32_t msplit, int64_t m_per_split, float* part, hipStream_t s);
+// res = scale * sum over splits; transposed == 0: res[j][c] -> out [R, C]; else out [C, R].
+hipError_t launch_coldot_finish(const float* part, int32_t msplit, int32_t R, int64_t C, float scale,
+                                int transposed, uint16_t* out, hipStream_t s);
+// BF16 transpose [rows, cols] -> [cols, rows].
+hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out,
+                                 hipStream_t s);
+
+// ---- weight-streaming forward, M <= 16 (gemv.hip)
+hipError_t launch_gemv_fwd(const uint32_t* codes, const uint8_t* code8, const float* c2s,
+                           const float* mu, int64_t N, int64_t K, const uint16_t* X, int64_t M,
+                           const float* Tpart, int32_t t_splits, const uint16_t* B, int32_t r,
+                           float s, uint16_t* Y, uint16_t* T_save, float* Ypart, int32_t ksplit,
+                           const Nf4Tables& T, hipStream_t st);
+hipError_t launch_gemv_finish(const float* Ypart, int32_t ksplit, int64_t M, int64_t N,
+                              const float* Tpart, int32_t t_splits, const uint16_t* B, int32_t r,
+                              float s, uint16_t* Y, uint16_t* T_save, hipStream_t st);
+
+// ---- fused dequant MFMA GEMMs (gemm.hip)
+// Y[M,N] = X[M,K] w_hat^T + L[M,r] B[N,r]^T, L = s*T (BF16, prescaled)
+hipError_t launch_gemm_fwd(const uint32_t* codes, const uint8_t* code8, const float* c2s,
+                           const float* mu, int64_t N, int64_t K, const uint16_t* X, int64_t M,
+                           const uint16_t* L, const uint16_t* B, int32_t r, uint16_t* Y,
+                           const Nf4Tables& T, hipStream_t st);
+// dX[M,K] = dY[M,N] w_hat + Lg[M,r] A[r,K], Lg = s*G (BF16, prescaled)
+hipError_t launch_gemm_dx(const uint32_t* codes, const uint8_t* code8, const float* c2s,
+                          const float* mu, int64_t N, int64_t K, const uint16_t* dY, int64_t M,
+                          const uint16_t* Lg, const uint16_t* A, int32_t r, uint16_t* dX,
+                          const Nf4Tables& T, hipStream_t st);
+
+}  // namespace qlora

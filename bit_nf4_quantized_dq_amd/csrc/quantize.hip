@@ -1,0 +1,157 @@
+// Quantize kernels: absmax NF4 with double-quantized block constants.
+//
+// Pass 1 ("QLoRA -- Fine-Tuning a 65B Model on One GPU", "Quantization in one paragraph"):
+//   per block of 64 consecutive row-major weights, c1 = max |w|; each weight becomes the
+//   index of the NF4 level nearest to fl32(w / c1) (ties to the lower level; all-zero
+//   blocks take the zero level).  The exact sum of all c1 is gathered for the mean as
+//   integer mantissa sums per FP32 exponent (commutative, so bit-reproducible).
+// Pass 2 ("QLoRA: Quantize Base Weights to 4-Bit", Section 2 "2. Double Quantization";
+//   "QLoRA -- Fine-Tuning a 65B Model on One GPU", "Double quantization"): the constants
+//   are centred on their mean mu and quantized to 8-bit floats in groups of 256 with one
+//   FP32 constant per group: c2s = fl32(max|c1 - mu| / 448), code8 = E4M3(fl32(d / c2s)).
+//
+// Memory layout: W FP32 [d_out*d_in] is read as 8-float words (one packed code word each);
+// a wavefront covers 8 blocks = 2 KB of W with 16-byte lane loads.
+#include "qlora_device.h"
+#include "qlora_host.h"
+
+namespace qlora {
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void k_quant_pass1(const float4* __restrict__ W,
+                                                          uint32_t* __restrict__ codes,
+                                                          float* __restrict__ c1_out,
+                                                          unsigned long long* __restrict__ hist,
+                                                          int* __restrict__ flag, int64_t n_words,
+                                                          Nf4Tables T) {
+  __shared__ unsigned long long sh_hist[256];
+  sh_hist[threadIdx.x] = 0ull;
+  __syncthreads();
+
+  const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // one code word = 8 weights
+  const bool active = g < n_words;  // n_words is a multiple of 8, so whole blocks are active
+  float v[8];
+  if (active) {
+    const float4 a = W[2 * g];
+    const float4 b = W[2 * g + 1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.f;
+  }
+  bool bad = false;
+  float mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    bad |= !__builtin_isfinite(v[i]);
+    mx = fmaxf(mx, fabsf(v[i]));
+  }
+  // absmax over the 8 lanes of one 64-weight block (lanes 8j..8j+7)
+  mx = fmaxf(mx, __shfl_xor(mx, 1));
+  mx = fmaxf(mx, __shfl_xor(mx, 2));
+  mx = fmaxf(mx, __shfl_xor(mx, 4));
+
+  uint32_t c[8];
+  if (mx > 0.f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = nf4_code(__fdiv_rn(v[i], mx), T);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = 8u;
+  }
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) word |= (c[i] | (c[i + 4] << 4)) << (8 * i);
+
+  if (active) {
+    codes[g] = word;
+    if ((threadIdx.x & 7) == 0 && !bad) {
+      c1_out[g >> 3] = mx;
+      const uint32_t bits = __float_as_uint(mx);
+      const uint32_t e = bits >> 23;  // mx >= 0
+      const uint32_t bin = e ? e : 1u;
+      const unsigned long long m = (unsigned long long)((bits & 0x7FFFFFu) | (e ? 0x800000u : 0u));
+      if (m) atomicAdd(&sh_hist[bin], m);
+    }
+  }
+  if (__any(bad && active)) {
+    if ((threadIdx.x & 63) == 0) atomicOr(flag, 1);
+  }
+  __syncthreads();
+  const unsigned long long h = sh_hist[threadIdx.x];
+  if (h) atomicAdd(&hist[threadIdx.x], h);
+}
+
+// One wavefront per group of 256 constants; lane l owns constants 4l..4l+3 of the group.
+__global__ __launch_bounds__(kThreads) void k_quant_pass2(const float* __restrict__ c1, float mu,
+                                                          uint8_t* __restrict__ code8,
+                                                          float* __restrict__ c2s,
+                                                          float* __restrict__ mu_out,
+                                                          int64_t n_blocks) {
+  const int lane = threadIdx.x & 63;
+  const int64_t grp = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int64_t n_groups = (n_blocks + kBlock2 - 1) / kBlock2;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *mu_out = mu;
+  if (grp >= n_groups) return;  // whole wavefront leaves together
+  const int64_t base = grp * kBlock2 + 4 * lane;
+  float d[4];
+  float m = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bool ok = base + j < n_blocks;
+    d[j] = ok ? __fsub_rn(c1[base + j], mu) : 0.f;
+    m = fmaxf(m, fabsf(d[j]));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  const float c2 = __fdiv_rn(m, 448.0f);
+  uint32_t q[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) q[j] = (c2 > 0.f) ? f32_to_e4m3(__fdiv_rn(d[j], c2)) : 0u;
+  if (base + 3 < n_blocks && (base & 3) == 0) {
+    *reinterpret_cast<uint32_t*>(code8 + base) = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (base + j < n_blocks) code8[base + j] = (uint8_t)q[j];
+  }
+  if (lane == 0) c2s[grp] = c2;
+}
+
+__global__ __launch_bounds__(kThreads) void k_e4m3_encode(const float* __restrict__ in,
+                                                          uint8_t* __restrict__ out, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) out[i] = (uint8_t)f32_to_e4m3(in[i]);
+}
+
+}  // namespace
+
+hipError_t launch_quant_pass1(const float* W, uint32_t* codes, float* c1, unsigned long long* hist,
+                              int* flag, int64_t n_words, const Nf4Tables& T, hipStream_t s) {
+  const int64_t grid = (n_words + kThreads - 1) / kThreads;
+  LaunchTimer t(0, s);
+  hipLaunchKernelGGL(k_quant_pass1, dim3((unsigned)grid), dim3(kThreads), 0, s,
+                     reinterpret_cast<const float4*>(W), codes, c1, hist, flag, n_words, T);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_pass2(const float* c1, float mu, uint8_t* code8, float* c2s, float* mu_out,
+                              int64_t n_blocks, hipStream_t s) {
+  const int64_t n_groups = (n_blocks + kBlock2 - 1) / kBlock2;
+  const int64_t grid = (n_groups + 3) / 4;
+  LaunchTimer t(1, s);
+  hipLaunchKernelGGL(k_quant_pass2, dim3((unsigned)grid), dim3(kThreads), 0, s, c1, mu, code8, c2s,
+                     mu_out, n_blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t s) {
+  const int64_t grid = (n + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(k_e4m3_encode, dim3((unsigned)grid), dim3(kThreads), 0, s, in, out, n);
+  return hipGetLastError();
+}
+
+}  // namespace qlora

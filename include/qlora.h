@@ -1,0 +1,170 @@
+/*
+ * qlora.h -- C ABI of the MI355X (gfx950) NF4 + double-quantized frozen linear with a
+ * 16-bit LoRA side path.
+ *
+ * The method (pages cited by title and section):
+ *   - "QLoRA -- Fine-Tuning a 65B Model on One GPU", "Quantization in one paragraph":
+ *     absmax blocks of 64 weights, each weight stored as the index of the nearest of 16
+ *     levels; dequantization is a lookup times the block constant.
+ *   - "QLoRA: Quantize Base Weights to 4-Bit", Section 2 "1. 4-bit NormalFloat": the 16
+ *     levels come from standard-normal quantiles; "2. Double Quantization": the FP32 block
+ *     constants are re-quantized to 8-bit floats in groups of 256 with one FP32 constant
+ *     per group, after subtracting their mean ("QLoRA -- Fine-Tuning a 65B Model on One
+ *     GPU", "Double quantization: the constants are not free").
+ *   - "QLoRA: Quantize Base Weights to 4-Bit", Section 3: weights are dequantized to BF16
+ *     on chip for every matmul, and the adapter branch (alpha/r) B (A x) is added.
+ *   - "QLoRA -- Fine-Tuning a 65B Model on One GPU", "Where the gradients actually go":
+ *     the input gradient runs through the dequantized weights; only A and B get gradients;
+ *     the 4-bit tensor is never written.
+ *
+ * Conventions for every entry point:
+ *   - Row-major.  W is [d_out, d_in] (h = W x), X is [M, d_in], Y is [M, d_out],
+ *     A is [r, d_in], B is [d_out, r].  BF16 tensors are passed as uint16_t bit patterns.
+ *   - "device" pointers are HIP device memory on the current device; "host" pointers are
+ *     ordinary host memory.  The caller owns every buffer; the library never allocates
+ *     device memory in fwd/bwd and never frees anything it was given.
+ *   - Every call returns a status (0 = QLORA_OK, negative = error, see qlora_strerror).
+ *     Arguments are validated before any launch; on an error nothing is launched.
+ *     Work is enqueued on the caller's stream `stream` (0 = null stream).  Except where
+ *     stated, calls do not synchronize, so device-side faults surface on the stream.
+ *   - Calls that share a workspace must not overlap in time.
+ */
+#ifndef QLORA_NF4_H
+#define QLORA_NF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum qlora_status {
+  QLORA_OK = 0,
+  QLORA_ERR_INVALID_ARG = -1, /* null pointer, M < 1, r outside [1, 128], alpha not finite */
+  QLORA_ERR_BAD_SHAPE = -2,   /* d_in % 64 != 0, d_out < 1, sizes that overflow */
+  QLORA_ERR_UNSUPPORTED = -3, /* block sizes other than (64, 256) */
+  QLORA_ERR_NONFINITE = -4,   /* NaN or Inf in the weights given to qlora_quantize */
+  QLORA_ERR_WORKSPACE = -5,   /* workspace pointer null or smaller than required */
+  QLORA_ERR_HIP = -6          /* a HIP runtime call or kernel launch failed */
+};
+
+/* A quantized weight tensor.  The struct and the buffers it points to belong to the
+ * caller.  Sizes come from qlora_quant_sizes.  After qlora_quantize fills it, it is
+ * read-only to every other entry point.
+ *
+ *   codes : device uint8[d_out * d_in / 2].  4-bit level indices, row-major; each aligned
+ *           run of 8 weights e0..e7 is 4 bytes, byte i = e_i | (e_{i+4} << 4).
+ *   code8 : device uint8[d_out * d_in / 64].  One OCP FP8 E4M3 bit pattern per block of
+ *           64 consecutive weights (the double-quantized, mean-shifted block constant).
+ *   c2s   : device float[ceil(n_blocks / 256)].  The FP32 second-level constant of each
+ *           group of 256 consecutive blocks (flattened order).
+ *   mu    : device float[1].  The mean of all first-level constants of the tensor.
+ *   block1, block2 : must be 64 and 256. */
+typedef struct qlora_nf4dq {
+  uint8_t *codes;
+  uint8_t *code8;
+  float *c2s;
+  float *mu;
+  int64_t d_out;
+  int64_t d_in;
+  int32_t block1;
+  int32_t block2;
+} qlora_nf4dq_t;
+
+/* Bytes of the three buffers of a [d_out, d_in] tensor (mu is always 4 bytes).
+ * Host only.  Errors: INVALID_ARG (null outputs), BAD_SHAPE. */
+int qlora_quant_sizes(int64_t d_out, int64_t d_in, size_t *codes_bytes, size_t *code8_bytes,
+                      size_t *c2s_bytes);
+
+/* Workspace bytes needed by one call of `op` (QLORA_OP_*) at these sizes.  Host only. */
+enum qlora_op { QLORA_OP_QUANTIZE = 0, QLORA_OP_FWD = 1, QLORA_OP_BWD = 2 };
+int qlora_workspace_size(int op, int64_t M, int64_t d_out, int64_t d_in, int32_t r,
+                         size_t *ws_bytes);
+
+/* The FP32 NF4 table the library uses (host memory, 16 floats), built from the
+ * normal-quantile formula of "QLoRA: Quantize Base Weights to 4-Bit", Section 2
+ * "1. 4-bit NormalFloat", with the tail level at Q(1/34) and each side scaled to its
+ * extreme so the endpoints are exactly -1 and +1 ("QLoRA -- Fine-Tuning a 65B Model on
+ * One GPU", "NF4"). */
+int qlora_nf4_codebook(float out16[16]);
+
+/* Quantize FP32 weights W (device, [d_out, d_in], d_in % 64 == 0) into *Wq, whose
+ * buffers the caller allocated.  First level: c1 = max|w| per 64-block, code = nearest
+ * level to fl32(w / c1), ties to the lower level, an all-zero block gets the zero level.
+ * Double quantization: mu = FP32 of the exact mean of all c1; d = fl32(c1 - mu); per group
+ * of 256 blocks c2s = fl32(max|d| / 448) and code8 = E4M3(fl32(d / c2s)) rounded to
+ * nearest, ties to even (0 when c2s == 0).
+ * ws: device, qlora_workspace_size(QLORA_OP_QUANTIZE) bytes.  host_mu: host float, may be
+ * NULL.  SYNCHRONIZES `stream` once (to fold the exact mean on the host).
+ * Errors: INVALID_ARG, BAD_SHAPE, UNSUPPORTED, NONFINITE (then Wq's contents are
+ * unspecified), WORKSPACE, HIP. */
+int qlora_quantize(const float *W, const qlora_nf4dq_t *Wq, float *host_mu, void *ws,
+                   size_t ws_bytes, hipStream_t stream);
+
+/* Dequantize to BF16 (device uint16[d_out, d_in]), bit-exact:
+ *   c1_hat = fl32(fl32(E4M3(code8) * c2s) + mu),  w_hat = bf16_rne(fl32(q[code] * c1_hat)).
+ * For export and tests; the linear entry points decode on chip instead.
+ * Errors: INVALID_ARG, BAD_SHAPE, UNSUPPORTED, HIP. */
+int qlora_dequantize(const qlora_nf4dq_t *Wq, uint16_t *W_bf16, hipStream_t stream);
+
+/* Forward: Y = X w_hat^T + (alpha / r) T B^T with T = X A^T, FP32 accumulation, BF16 out
+ * ("QLoRA: Quantize Base Weights to 4-Bit", Section 3; "QLoRA -- Fine-Tuning a 65B Model
+ * on One GPU", "Where the gradients actually go").
+ *   X [M, d_in], A [r, d_in], B [d_out, r]: device BF16 inputs.
+ *   Y [M, d_out]: device BF16 output (overwritten).
+ *   T_save [M, r]: device BF16, receives bf16(T) for the backward; may be NULL.
+ *   ws: device workspace of qlora_workspace_size(QLORA_OP_FWD) bytes.
+ * M <= 16 runs a weight-streaming kernel; larger M runs the fused dequant MFMA GEMM.
+ * Errors: INVALID_ARG, BAD_SHAPE, UNSUPPORTED, WORKSPACE, HIP. */
+int qlora_linear_fwd(const qlora_nf4dq_t *Wq, const uint16_t *X, int64_t M, const uint16_t *A,
+                     const uint16_t *B, int32_t r, float alpha, uint16_t *Y, uint16_t *T_save,
+                     void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Backward of qlora_linear_fwd.  With G = dY B:
+ *   dX = dY w_hat + (alpha/r) G A      [M, d_in]   (may be NULL: not computed)
+ *   dA = (alpha/r) G^T X               [r, d_in]
+ *   dB = (alpha/r) dY^T T, T = X A^T   [d_out, r]
+ * dY [M, d_out], X, A, B: device BF16 inputs.  T_saved: device BF16 [M, r] from the
+ * forward, or NULL to recompute it.  Outputs are device BF16 and overwritten (not
+ * accumulated).  The quantized weights are only read.
+ * Errors: INVALID_ARG, BAD_SHAPE, UNSUPPORTED, WORKSPACE, HIP. */
+int qlora_linear_bwd(const qlora_nf4dq_t *Wq, const uint16_t *X, const uint16_t *dY, int64_t M,
+                     const uint16_t *A, const uint16_t *B, int32_t r, float alpha,
+                     const uint16_t *T_saved, uint16_t *dX, uint16_t *dA, uint16_t *dB, void *ws,
+                     size_t ws_bytes, hipStream_t stream);
+
+/* Diagnostic: the device E4M3 encoder used by qlora_quantize, applied elementwise to n
+ * floats (device in, device out), so it can be checked exhaustively.  |in| <= 448 is
+ * rounded to nearest, ties to even; larger magnitudes go to 448.  Errors: INVALID_ARG, HIP. */
+int qlora_e4m3_encode(const float *in, uint8_t *out, int64_t n, hipStream_t stream);
+
+/* Diagnostic kernel timing.  While enabled, the library brackets every launch of the
+ * kernels below with a pair of hipEvents recorded on the launch stream.
+ * qlora_timing_read waits for those events and returns the summed duration (ms) and
+ * the launch count of one kernel id since the last reset, then resets that id.
+ * Host only; events are created by the library and reused. */
+enum qlora_kernel_id {
+  QLORA_K_QUANT_PASS1 = 0,
+  QLORA_K_QUANT_PASS2 = 1,
+  QLORA_K_DEQUANT = 2,
+  QLORA_K_GEMV_FWD = 3,
+  QLORA_K_GEMM_FWD = 4,
+  QLORA_K_GEMM_DX = 5,
+  QLORA_K_LORA_DOWN = 6,
+  QLORA_K_LORA_GRAD = 7,
+  QLORA_K_COUNT = 8
+};
+int qlora_timing_enable(int on);
+int qlora_timing_read(int kernel_id, double *total_ms, int64_t *launches);
+
+/* Human-readable text of a status code (static storage). */
+const char *qlora_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_NF4_H */

@@ -200,8 +200,12 @@ def bf16_bits_to_f32(b) -> np.ndarray:
 # --------------------------------------------------------------------------------------
 
 
-def quantize(W: np.ndarray) -> dict:
+def quantize(W: np.ndarray, blocks: np.ndarray | None = None) -> dict:
     """Quantize an FP32 weight matrix W[d_out, d_in] (d_in % 64 == 0).
+
+    `blocks` (optional boolean mask over the flattened 64-blocks) restricts which blocks
+    get their 4-bit codes computed (others hold 255); the constants c1, mu, c2s and code8
+    always cover the whole tensor, since the mean and the 256-groups span it.
 
     Steps, in the pages' order:
       1. Blocks of 64 consecutive row-major weights; c1 = max |w| per block
@@ -222,6 +226,7 @@ def quantize(W: np.ndarray) -> dict:
         raise ValueError("non-finite weight")
     d_out, d_in = W.shape
     table = nf4_codebook()
+    sel = None if blocks is None else np.asarray(blocks, dtype=bool).reshape(-1)
 
     blocks = W.reshape(-1, BLOCK1)
     c1 = np.max(np.abs(blocks), axis=1).astype(np.float32)
@@ -229,9 +234,11 @@ def quantize(W: np.ndarray) -> dict:
 
     codes = np.full(blocks.shape, 8, dtype=np.uint8)
     nz = c1 > 0
-    rho = np.zeros(blocks.shape, dtype=np.float32)
-    rho[nz] = blocks[nz] / c1[nz][:, None]  # float32 / float32: one IEEE rounding
-    codes[nz] = nearest_level(rho[nz], table)
+    if sel is not None:
+        codes[~sel] = 255
+        nz = nz & sel
+    rho = blocks[nz] / c1[nz][:, None]  # float32 / float32: one IEEE rounding
+    codes[nz] = nearest_level(rho, table)
 
     mu = np.float32(math.fsum(c1.astype(np.float64).tolist()) / n_blocks)
 
@@ -250,7 +257,7 @@ def quantize(W: np.ndarray) -> dict:
         "d_out": d_out,
         "d_in": d_in,
         "codes": codes.reshape(d_out, d_in),
-        "packed": pack_codes(codes).reshape(d_out, d_in // 2),
+        "packed": pack_codes(codes).reshape(d_out, d_in // 2) if sel is None else None,
         "c1": c1,
         "mu": mu,
         "code8": code8,
@@ -274,12 +281,15 @@ def decode_scales(code8: np.ndarray, c2s: np.ndarray, mu) -> np.ndarray:
 def dequantize_bf16_bits(q: dict) -> np.ndarray:
     """Dequantized weights as BF16 bit patterns [d_out, d_in]:
     w_hat = bf16(fl32(q[code] * c1_hat)) -- a lookup and a multiply ([65B] "Quantization
-    in one paragraph"), rounded to the BF16 compute type ([4-Bit] Sec. 3)."""
-    table = nf4_codebook()
+    in one paragraph"), rounded to the BF16 compute type ([4-Bit] Sec. 3).
+    Blocks whose codes were not computed (code 255) decode to NaN."""
+    table = np.concatenate([nf4_codebook(), np.full(240, np.nan, np.float32)])
     c1h = decode_scales(q["code8"], q["c2s"], q["mu"])
     codes = q["codes"].reshape(-1, BLOCK1)
     vals = (table[codes] * c1h[:, None]).astype(np.float32)
-    return bf16_round_bits(vals).reshape(q["d_out"], q["d_in"])
+    bits = bf16_round_bits(np.where(np.isnan(vals), 0, vals))
+    bits = np.where(np.isnan(vals), np.uint16(0x7FC0), bits)
+    return bits.reshape(q["d_out"], q["d_in"])
 
 
 def dequantize_f64(q: dict) -> np.ndarray:

@@ -1,0 +1,292 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on identical seeded
+inputs.  Encode/decode outputs must match bit for bit; forward/backward outputs must be
+within a normwise relative error of 1e-2: max|got - ref| / max|ref| <= 1e-2 per tensor."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from bit_nf4_quantized_dq_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-2
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _f64(t_bf16):
+    return t_bf16.detach().float().cpu().numpy().astype(np.float64)
+
+
+def normwise(got, ref):
+    den = np.max(np.abs(ref))
+    return float(np.max(np.abs(got - ref)) / (den if den > 0 else 1.0))
+
+
+def _assert_quant_equal(q, oq):
+    assert np.array_equal(_np(q.codes), oq["packed"].reshape(-1)), "packed codes"
+    assert np.array_equal(_np(q.code8), oq["code8"]), "code8"
+    assert np.array_equal(_np(q.c2s).view(np.uint32), oq["c2s"].view(np.uint32)), "c2s"
+    assert _np(q.mu).view(np.uint32)[0] == np.float32(oq["mu"]).view(np.uint32), "mu"
+
+
+def _case(cfg, d_out, d_in, M, r, std, idx=0):
+    c = I.linear_case(cfg, idx, d_out, d_in, M, r, std)
+    return c
+
+
+# ---------------------------------------------------------------- encoders
+
+def test_e4m3_encoder_matches_oracle(gpu_lib):
+    from bit_nf4_quantized_dq_amd import e4m3_encode
+
+    vals = O.e4m3_value(np.arange(0, 0x7F)).astype(np.float64)
+    mids = 0.5 * (vals[:-1] + vals[1:])
+    pts = []
+    for m in np.concatenate([vals, mids]):
+        f = np.float32(m)
+        pts += [f, np.nextafter(f, np.float32(0)), np.nextafter(f, np.float32(1e9))]
+    rng = np.random.default_rng(0)
+    pts = np.array(pts, dtype=np.float32)
+    pts = np.concatenate([pts, -pts, rng.uniform(-449, 449, 200000).astype(np.float32),
+                          np.array([0.0, -0.0, 1e-30, -1e-30, 448.0, -448.0], np.float32)])
+    got = _np(e4m3_encode(torch.from_numpy(pts).cuda()))
+    assert np.array_equal(got, O.e4m3_encode(pts))
+
+
+# ---------------------------------------------------------------- quantize / dequantize
+
+QSHAPES = [(1, 256, 256, 0.02), (2, 4096, 4096, 0.02), (9, 272, 320, 0.02), (9, 16, 64, 0.02), (4, 1024, 4096, 0.02)]
+
+
+@pytest.mark.parametrize("cfg,d_out,d_in,std", QSHAPES)
+def test_quantize_and_dequantize_bit_exact(gpu_lib, cfg, d_out, d_in, std):
+    from bit_nf4_quantized_dq_amd import dequantize, quantize
+
+    W = I.weight(cfg, 0, d_out, d_in, std)
+    oq = O.quantize(W.numpy())
+    q = quantize(W.cuda())
+    torch.cuda.synchronize()
+    _assert_quant_equal(q, oq)
+    w = dequantize(q)
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(w.view(torch.int16)).view(np.uint16), O.dequantize_bf16_bits(oq))
+
+
+def test_quantize_special_values(gpu_lib):
+    """Zero blocks, exact zeros, a lone outlier, FP32 subnormals, a huge block and exact
+    NF4 multiples in one tensor."""
+    from bit_nf4_quantized_dq_amd import dequantize, quantize
+
+    rng = np.random.default_rng(3)
+    W = (rng.standard_normal((64, 512)) * 0.02).astype(np.float32)
+    W[0, :64] = 0.0
+    W[1, 5] = 0.0
+    W[2, 100] = 40.0
+    W[3, :64] = (rng.standard_normal(64) * 1e-40).astype(np.float32)  # subnormal block
+    W[4, 64:128] = np.float32(1e30) * rng.standard_normal(64).astype(np.float32)
+    W[5, :64] = O.nf4_codebook()[rng.integers(0, 16, 64)] * np.float32(0.25)
+    W[6, 0:64] = -W[6, 0:64]
+    oq = O.quantize(W)
+    q = quantize(torch.from_numpy(W).cuda())
+    torch.cuda.synchronize()
+    _assert_quant_equal(q, oq)
+    w = dequantize(q)
+    assert np.array_equal(_np(w.view(torch.int16)).view(np.uint16), O.dequantize_bf16_bits(oq))
+
+
+def test_roundtrip_special_case_gpu(gpu_lib):
+    from bit_nf4_quantized_dq_amd import dequantize, quantize
+
+    q_tab = O.nf4_codebook()
+    rng = np.random.default_rng(5)
+    k = rng.integers(0, 16, size=(128, 1024))
+    k[:, ::64] = 0
+    W = (q_tab[k] * np.float32(2.0**-5)).astype(np.float32)
+    q = quantize(torch.from_numpy(W).cuda())
+    w = dequantize(q)
+    exp = torch.from_numpy(W).to(torch.bfloat16)
+    assert torch.equal(w.cpu().view(torch.int16), exp.view(torch.int16))
+
+
+def test_quantize_rejects_nonfinite(gpu_lib):
+    from bit_nf4_quantized_dq_amd import QLoRAError, quantize
+
+    W = torch.randn(64, 256)
+    W[7, 9] = float("nan")
+    with pytest.raises(QLoRAError) as e:
+        quantize(W.cuda())
+    assert e.value.status == -4
+    W[7, 9] = float("inf")
+    with pytest.raises(QLoRAError):
+        quantize(W.cuda())
+
+
+# ---------------------------------------------------------------- forward / backward
+
+
+def _run(c, alpha, r, zero_w=False, t_saved=True, need_dx=True):
+    from bit_nf4_quantized_dq_amd import linear_bwd, linear_fwd, quantize
+
+    W = torch.zeros_like(c["W"]) if zero_w else c["W"]
+    oq = O.quantize(W.numpy())
+    what = O.dequantize_f64(oq)
+    X, A, Bm, dY = (c[k] for k in ("X", "A", "B", "dY"))
+    Xd, Ad, Bd, dYd = (t.cuda() for t in (X, A, Bm, dY))
+    q = quantize(W.cuda())
+    M = X.shape[0]
+    T = torch.empty(M, r, dtype=torch.bfloat16, device="cuda")
+    Y = linear_fwd(q, Xd, Ad, Bd, alpha, T_save=T)
+    dX, dA, dB = linear_bwd(q, Xd, dYd, Ad, Bd, alpha, T_saved=T if t_saved else None, need_dX=need_dx)
+    torch.cuda.synchronize()
+    Yr, Tr = O.lora_fwd(what, _f64(X), _f64(A), _f64(Bm), alpha, r)
+    dXr, dAr, dBr = O.lora_bwd(what, _f64(X), _f64(dY), _f64(A), _f64(Bm), alpha, r)
+    return dict(Y=(_f64(Y), Yr), T=(_f64(T), Tr), dA=(_f64(dA), dAr), dB=(_f64(dB), dBr),
+                dX=(_f64(dX) if need_dx else None, dXr))
+
+
+FB_CASES = [
+    # cfg, d_out, d_in, M, r, alpha
+    (1, 256, 256, 4, 8, 16.0),
+    (9, 272, 320, 1, 8, 16.0),
+    (9, 272, 320, 16, 16, 32.0),
+    (9, 272, 320, 17, 16, 32.0),
+    (9, 272, 320, 300, 16, 32.0),
+    (9, 512, 1024, 777, 24, 48.0),
+    (9, 1040, 192, 513, 8, 16.0),
+    (9, 64, 2048, 100, 128, 256.0),
+    (9, 2048, 64, 40, 3, 6.0),
+]
+
+
+@pytest.mark.parametrize("cfg,d_out,d_in,M,r,alpha", FB_CASES)
+def test_fwd_bwd_parity(gpu_lib, cfg, d_out, d_in, M, r, alpha):
+    c = _case(cfg, d_out, d_in, M, r, 0.02)
+    res = _run(c, alpha, r)
+    for k, (got, ref) in res.items():
+        e = normwise(got, ref)
+        assert e <= TOL, (k, e)
+
+
+@pytest.mark.parametrize("M", [1, 16, 300])
+def test_lora_path_in_isolation(gpu_lib, M):
+    """W = 0: Y = s T B^T and dX = s G A exactly as the adapter branch alone."""
+    c = _case(9, 272, 320, M, 16, 0.02)
+    res = _run(c, 32.0, 16, zero_w=True, t_saved=False)
+    for k in ("Y", "dX", "dA", "dB"):
+        got, ref = res[k]
+        assert np.max(np.abs(ref)) > 0
+        assert normwise(got, ref) <= TOL, k
+
+
+def test_alpha_zero_is_base_only(gpu_lib):
+    c = _case(9, 272, 320, 33, 8, 0.02)
+    res = _run(c, 0.0, 8, need_dx=True)
+    for k in ("Y", "dX"):
+        got, ref = res[k]
+        assert normwise(got, ref) <= TOL
+    assert np.all(res["dA"][0] == 0) and np.all(res["dB"][0] == 0)
+
+
+def test_no_dx_requested(gpu_lib):
+    c = _case(9, 272, 320, 64, 8, 0.02)
+    res = _run(c, 16.0, 8, need_dx=False)
+    assert res["dX"][0] is None
+    for k in ("dA", "dB"):
+        assert normwise(*res[k]) <= TOL
+
+
+def test_weights_read_only_and_deterministic(gpu_lib):
+    from bit_nf4_quantized_dq_amd import linear_bwd, linear_fwd, quantize
+
+    c = _case(9, 512, 512, 300, 16, 0.02)
+    q = quantize(c["W"].cuda())
+    before = [t.clone() for t in (q.codes, q.code8, q.c2s, q.mu)]
+    X, A, Bm, dY = (c[k].cuda() for k in ("X", "A", "B", "dY"))
+    outs = []
+    for _ in range(2):
+        Y = linear_fwd(q, X, A, Bm, 32.0)
+        dX, dA, dB = linear_bwd(q, X, dY, A, Bm, 32.0)
+        Ys = linear_fwd(q, X[:8].contiguous(), A, Bm, 32.0)
+        outs.append([t.clone() for t in (Y, dX, dA, dB, Ys)])
+    torch.cuda.synchronize()
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    for a, b in zip(before, (q.codes, q.code8, q.c2s, q.mu)):
+        assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------- the named workloads
+
+
+def test_config2_weight_stream_4096(gpu_lib):
+    """4096x4096 at M=1 and M=16, forward only."""
+    for M in (1, 16):
+        c = _case(2, 4096, 4096, M, 16, 0.02)
+        from bit_nf4_quantized_dq_amd import linear_fwd, quantize
+
+        q = quantize(c["W"].cuda())
+        oq = O.quantize(c["W"].numpy())
+        _assert_quant_equal(q, oq)
+        Y = linear_fwd(q, c["X"].cuda(), c["A"].cuda(), c["B"].cuda(), 32.0)
+        Yr, _ = O.lora_fwd(O.dequantize_f64(oq), _f64(c["X"]), _f64(c["A"]), _f64(c["B"]), 32.0, 16)
+        assert normwise(_f64(Y), Yr) <= TOL
+
+
+def test_config3_train_step_4096(gpu_lib):
+    """4096x4096 at M=4096: forward and backward against the full FP64 oracle."""
+    c = _case(3, 4096, 4096, 4096, 16, 0.02)
+    res = _run(c, 32.0, 16)
+    for k, (got, ref) in res.items():
+        assert normwise(got, ref) <= TOL, k
+
+
+@pytest.mark.parametrize("idx", range(7))
+def test_config4_llama3_8b_layer_sampled(gpu_lib, idx):
+    """Llama-3-8B layer linears at M=8192: encode/decode checked on sampled blocks;
+    outputs checked on sampled tokens and features; dA/dB in full."""
+    from bit_nf4_quantized_dq_amd import dequantize, linear_bwd, linear_fwd, quantize
+
+    shp = I.LLAMA3_8B_LAYER[idx]
+    N, K, M, r, alpha = shp.d_out, shp.d_in, 8192, 16, 32.0
+    c = I.linear_case(4, idx, N, K, M, r, 0.02)
+    rng = np.random.default_rng(idx)
+    n_s = np.sort(rng.choice(N, 48, replace=False))
+    kb_s = int(rng.integers(0, K // 64))
+    m_s = np.sort(rng.choice(M, 48, replace=False))
+    mask = np.zeros((N, K // 64), bool)
+    mask[n_s, :] = True
+    mask[:, kb_s] = True
+    oq = O.quantize(c["W"].numpy(), blocks=mask)
+    what = O.dequantize_f64(oq)  # NaN outside the sampled blocks
+    q = quantize(c["W"].cuda())
+    X, A, Bm, dY = (c[k].cuda() for k in ("X", "A", "B", "dY"))
+    T = torch.empty(M, r, dtype=torch.bfloat16, device="cuda")
+    Y = linear_fwd(q, X, A, Bm, alpha, T_save=T)
+    dX, dA, dB = linear_bwd(q, X, dY, A, Bm, alpha, T_saved=T)
+    wq = dequantize(q)
+    torch.cuda.synchronize()
+    # encode/decode on the sampled blocks
+    assert np.array_equal(_np(q.code8), oq["code8"]) and np.array_equal(_np(q.c2s), oq["c2s"])
+    assert _np(q.mu)[0] == oq["mu"]
+    gw = _np(wq.view(torch.int16)).view(np.uint16)
+    ow = O.dequantize_bf16_bits(oq)
+    sel = np.repeat(mask, 64, axis=1)
+    assert np.array_equal(gw[sel], ow[sel])
+    s = alpha / r
+    Xf, Af, Bf, dYf = _f64(c["X"]), _f64(c["A"]), _f64(c["B"]), _f64(c["dY"])
+    T_ref = Xf @ Af.T
+    G_ref = dYf @ Bf
+    # forward on sampled (token, feature) pairs
+    Y_ref = Xf[m_s] @ what[n_s].T + s * T_ref[m_s] @ Bf[n_s].T
+    assert normwise(_f64(Y)[np.ix_(m_s, n_s)], Y_ref) <= TOL
+    # dX on sampled tokens, one column block
+    cols = slice(64 * kb_s, 64 * kb_s + 64)
+    dX_ref = dYf[m_s] @ what[:, cols] + s * G_ref[m_s] @ Af[:, cols]
+    assert normwise(_f64(dX)[m_s][:, cols], dX_ref) <= TOL
+    assert normwise(_f64(dA), s * G_ref.T @ Xf) <= TOL
+    assert normwise(_f64(dB), s * dYf.T @ T_ref) <= TOL
+    assert normwise(_f64(T), T_ref) <= TOL

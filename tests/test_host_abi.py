@@ -1,0 +1,86 @@
+"""CPU-side checks of the C-ABI library: it loads, exports every symbol the header declares,
+and its host-only entry points (sizes, codebook, argument validation) behave.  No GPU
+compute is called: every error path tested here returns before any launch."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from bit_nf4_quantized_dq_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlora.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    return B.load_library()
+
+
+def test_every_declared_symbol_is_exported(L):
+    text = open(HEADER).read()
+    names = sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text)))
+    assert len(names) == 11
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_codebook_equals_oracle_bit_for_bit():
+    lib_q = np.array(B.nf4_codebook(), dtype=np.float32)
+    assert np.array_equal(lib_q.view(np.uint32), O.nf4_codebook().view(np.uint32))
+
+
+@pytest.mark.parametrize("shape", [(256, 256), (4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336), (272, 320)])
+def test_quant_sizes_match_oracle(shape):
+    a, b, c = B.quant_sizes(*shape)
+    sz = O.quant_sizes(*shape)
+    assert (a, b, c) == (sz["codes"], sz["code8"], sz["c2s"])
+
+
+def test_bits_per_param_from_library_sizes():
+    a, b, c = B.quant_sizes(4096, 4096)
+    bpp = 8.0 * (a + b + c + 4) / (4096 * 4096)
+    assert round(bpp, 3) == 4.127
+
+
+def _wq(d_out=256, d_in=256, b1=64, b2=256):
+    dummy = ctypes.c_void_p(4096)  # never dereferenced: validation fails first
+    return B._Nf4dq(dummy, dummy, dummy, dummy, d_out, d_in, b1, b2)
+
+
+def test_shape_and_argument_errors_before_launch(L):
+    dummy = ctypes.c_void_p(4096)
+    ws = ctypes.c_void_p(8192)
+    assert L.qlora_linear_fwd(ctypes.byref(_wq(d_in=100)), dummy, 4, dummy, dummy, 8, 16.0, dummy, None, ws, 1 << 20, None) == -2
+    assert L.qlora_linear_fwd(ctypes.byref(_wq(d_out=250)), dummy, 4, dummy, dummy, 8, 16.0, dummy, None, ws, 1 << 20, None) == -2
+    assert L.qlora_linear_fwd(ctypes.byref(_wq(b1=32)), dummy, 4, dummy, dummy, 8, 16.0, dummy, None, ws, 1 << 20, None) == -3
+    assert L.qlora_linear_fwd(ctypes.byref(_wq()), dummy, 0, dummy, dummy, 8, 16.0, dummy, None, ws, 1 << 20, None) == -1
+    assert L.qlora_linear_fwd(ctypes.byref(_wq()), dummy, 4, dummy, dummy, 0, 16.0, dummy, None, ws, 1 << 20, None) == -1
+    assert L.qlora_linear_fwd(ctypes.byref(_wq()), dummy, 4, dummy, dummy, 129, 16.0, dummy, None, ws, 1 << 20, None) == -1
+    assert L.qlora_linear_fwd(ctypes.byref(_wq()), dummy, 4, dummy, dummy, 8, float("nan"), dummy, None, ws, 1 << 20, None) == -1
+    assert L.qlora_linear_fwd(ctypes.byref(_wq()), None, 4, dummy, dummy, 8, 16.0, dummy, None, ws, 1 << 20, None) == -1
+    assert L.qlora_linear_fwd(ctypes.byref(_wq()), dummy, 4, dummy, dummy, 8, 16.0, dummy, None, ws, 16, None) == -5
+    assert L.qlora_linear_fwd(ctypes.byref(_wq()), dummy, 4, dummy, dummy, 8, 16.0, dummy, None, None, 1 << 20, None) == -5
+    assert L.qlora_linear_bwd(ctypes.byref(_wq()), dummy, dummy, 4, dummy, dummy, 8, 16.0, None, dummy, dummy, None, ws, 1 << 20, None) == -1
+    assert L.qlora_linear_bwd(ctypes.byref(_wq()), dummy, dummy, 4, dummy, dummy, 8, 16.0, None, dummy, dummy, dummy, ws, 8, None) == -5
+    assert L.qlora_quantize(dummy, ctypes.byref(_wq()), None, ws, 8, None) == -5
+    assert L.qlora_quantize(None, ctypes.byref(_wq()), None, ws, 1 << 20, None) == -1
+    assert L.qlora_quantize(ctypes.c_void_p(4100), ctypes.byref(_wq()), None, ws, 1 << 20, None) == -1  # misaligned
+    assert L.qlora_dequantize(None, dummy, None) == -1
+
+
+def test_workspace_sizes_are_sane():
+    for M in (1, 16, 17, 4096):
+        for op in (B.OP_FWD, B.OP_BWD):
+            n = B.workspace_size(op, M, 4096, 4096, 16)
+            assert 256 <= n < (64 << 20) + 64 * M * 16 * 4
+    assert B.workspace_size(B.OP_QUANTIZE, 1, 4096, 4096, 1) >= 4096 * 4096 // 64 * 4
+
+
+def test_strerror_covers_every_status(L):
+    for s in range(0, -7, -1):
+        assert B._strerror(s) not in ("?", "unknown status")
