@@ -1,0 +1,253 @@
+"""Benchmark of the NF4 + double-quantized LoRA linear on one MI355X.
+
+A step is one training pass of the hot path over one batch: forward (LoRA down-projection,
+fused dequant->MFMA GEMM with the adapter slice) and backward (G, fused transposed-tile
+dX GEMM, dA, dB) of the 4096x4096 linear at M = 4096 tokens, r = 16, alpha = 32, inputs
+resident in HBM.  value = algorithmic TFLOP/s of that step (4MNK + 6Mr(N+K) per step).
+
+Also reported in the same JSON line: the M = 1 weight-stream rate of the same linear
+(128 distinct quantized copies rotated so every call reads HBM), the quantize rate, the
+roofline of the dominant kernel from per-launch HIP events, and the CPU oracle timed on a
+bounded sample of the same workload.
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "NF4+DQ linear fwd+bwd TFLOP/s at M=4096; weight-stream GB/s at M=1"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def step_flops(M, N, K, r):
+    return 4 * M * N * K + 6 * M * r * (N + K)
+
+
+def stream_bytes(M, N, K, r):
+    # 0.515869 B/weight of NF4+DQ (codes, code8, c2s, mu) + adapters + activations
+    return N * K // 2 + N * K // 64 + 4 * ((N * K // 64 + 255) // 256) + 4 + 2 * r * (N + K) + 2 * M * K + 2 * M * N
+
+
+def cpu_baseline(N, K, r, alpha, target_s=15.0):
+    """The oracle as it stands, on the host cores: dequantize + fwd + bwd on a token sample."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+    from bit_nf4_quantized_dq_amd import inputs as I
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    c = I.linear_case(3, 0, N, K, 4096, r, 0.02)
+    oq = O.quantize(c["W"].numpy())
+    Ms = 256
+    X = c["X"][:Ms].float().numpy().astype(np.float64)
+    dY = c["dY"][:Ms].float().numpy().astype(np.float64)
+    A = c["A"].float().numpy().astype(np.float64)
+    B = c["B"].float().numpy().astype(np.float64)
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        what = O.dequantize_f64(oq)
+        O.lora_fwd(what, X, A, B, alpha, r)
+        O.lora_bwd(what, X, dY, A, B, alpha, r)
+        n += 1
+        if time.perf_counter() - t0 > target_s / 2 or n >= 8:
+            break
+    dt = (time.perf_counter() - t0) / n
+    del torch
+    return {
+        "value": step_flops(Ms, N, K, r) / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{n} oracle step(s) (dequantize + FP64 fwd + bwd) at M={Ms} tokens of the {N}x{K} r={r} linear; "
+                  f"{dt:.2f} s per step",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "this build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_nf4_quantized_dq_amd as Q
+    from bit_nf4_quantized_dq_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    N = K = 4096
+    M, r, alpha = 4096, 16, 32.0
+
+    # ---- training step workload (inputs resident in HBM)
+    c = I.linear_case(3, 0, N, K, M, r, 0.02, device="cpu")
+    W = c["W"].to(dev)
+    X, A, B, dY = (c[k].to(dev) for k in ("X", "A", "B", "dY"))
+    q = Q.quantize(W)
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    T = torch.empty(M, r, dtype=torch.bfloat16, device=dev)
+    dX = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+    dA = torch.empty(r, K, dtype=torch.bfloat16, device=dev)
+    dB = torch.empty(N, r, dtype=torch.bfloat16, device=dev)
+    ws_f = torch.empty(Q.workspace_size(Q.OP_FWD, M, N, K, r), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(Q.workspace_size(Q.OP_BWD, M, N, K, r), dtype=torch.uint8, device=dev)
+
+    def step():
+        Q.linear_fwd(q, X, A, B, alpha, Y=Y, T_save=T, ws=ws_f)
+        Q.linear_bwd(q, X, dY, A, B, alpha, T_saved=T, dX=dX, dA=dA, dB=dB, ws=ws_b)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, per-kernel HIP events on the launch stream
+    Q.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    per_kernel = {}
+    for name in Q.KERNEL_IDS:
+        ms, n = Q.timing_read(name)
+        if n:
+            per_kernel[name] = {"avg_us": 1e3 * ms / n, "launches_per_step": n / args.steps}
+    Q.timing_enable(False)
+    ms_per_step = 1e3 * (t1 - t0) / args.steps
+    flops = step_flops(M, N, K, r)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+
+    # un-instrumented repeat, for the event overhead
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_plain = 1e3 * (time.perf_counter() - t2) / args.steps
+
+    # dominant kernel roofline (algorithmic FLOPs per launch / avg launch time)
+    kflops = {"gemm_fwd": 2 * M * N * K + 2 * M * N * r, "gemm_dx": 2 * M * N * K + 2 * M * K * r}
+    dom = max(kflops, key=lambda k: per_kernel.get(k, {}).get("avg_us", 0.0))
+    ach = kflops[dom] / (per_kernel[dom]["avg_us"] * 1e-6) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "algorithmic_flops_per_launch": kflops[dom]}
+
+    # ---- M = 1 weight stream over 128 distinct copies (>= 1.1 GB, beyond the 256 MB cache)
+    ncopy = 128
+    Ws = [Q.quantize(W) for _ in range(1)]
+    base = Ws[0]
+    copies = []
+    for _ in range(ncopy):
+        copies.append(Q.QuantizedWeight(base.codes.clone(), base.code8.clone(), base.c2s.clone(), base.mu.clone(), N, K))
+    del Ws
+    X1 = c["X"][:1].to(dev).contiguous()
+    Y1 = torch.empty(1, N, dtype=torch.bfloat16, device=dev)
+    ws1 = torch.empty(Q.workspace_size(Q.OP_FWD, 1, N, K, r), dtype=torch.uint8, device=dev)
+    for cp in copies[:8]:
+        Q.linear_fwd(cp, X1, A, B, alpha, Y=Y1, ws=ws1)
+    torch.cuda.synchronize()
+    # (a) kernel durations from HIP events, eager launches
+    Q.timing_enable(True)
+    for cp in copies:
+        Q.linear_fwd(cp, X1, A, B, alpha, Y=Y1, ws=ws1)
+    torch.cuda.synchronize()
+    gv_ms, gv_n = Q.timing_read("gemv_fwd")
+    Q.timing_enable(False)
+    # (b) whole calls back to back, captured once in a HIP graph and replayed
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for cp in copies:
+                Q.linear_fwd(cp, X1, A, B, alpha, Y=Y1, ws=ws1)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    rounds = 8
+    t0 = time.perf_counter()
+    for _ in range(rounds):
+        graph.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    calls = rounds * ncopy
+    us_call = 1e6 * (t1 - t0) / calls
+    # (c) eager Python calls, for reference
+    t0 = time.perf_counter()
+    for cp in copies:
+        Q.linear_fwd(cp, X1, A, B, alpha, Y=Y1, ws=ws1)
+    torch.cuda.synchronize()
+    us_eager = 1e6 * (time.perf_counter() - t0) / ncopy
+    sb = stream_bytes(1, N, K, r)
+    gemv_us = 1e3 * gv_ms / max(gv_n, 1)
+    stream = {
+        "metric": "weight-stream GB/s at M=1 (4096x4096, r=16, 128 rotated copies, HIP-graph replay)",
+        "value": round(sb / (us_call * 1e-6) / 1e9, 1), "unit": "GB/s", "us_per_call": round(us_call, 2),
+        "us_per_call_eager_python": round(us_eager, 2),
+        "bytes_per_call": sb,
+        "gemv_kernel": {"avg_us": round(gemv_us, 2), "achieved_GBs": round(sb / (gemv_us * 1e-6) / 1e9, 1),
+                        "peak_GBs": PEAK_HBM_GBS, "frac": round(sb / (gemv_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
+    }
+    del graph
+    del copies
+
+    # ---- quantize (load time) of the same FP32 weight
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    nq = 5
+    for _ in range(nq):
+        Q.quantize(W, out=q)
+    torch.cuda.synchronize()
+    q_ms = 1e3 * (time.perf_counter() - t0) / nq
+    quant = {"ms": round(q_ms, 3), "input_GBs": round(4 * N * K / (q_ms * 1e-3) / 1e9, 1)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian W ~ N(0, 0.02^2), X ~ N(0,1), dY ~ N(0, 1e-2))",
+        "config": {"workload": "llama7b-qproj-4096x4096-M4096-train (fwd+bwd dX,dA,dB)", "M": M, "d_out": N,
+                   "d_in": K, "r": r, "alpha": alpha, "step_flops": flops},
+        "roofline": roofline,
+        "kernels": {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in per_kernel.items()},
+        "ms_per_step_without_kernel_events": round(ms_plain, 4),
+        "weight_stream_M1": stream,
+        "quantize_4096x4096": quant,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(N, K, r, alpha)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

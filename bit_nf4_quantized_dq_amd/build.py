@@ -50,6 +50,8 @@ def _compile(src: str, verbose: bool) -> str:
     cmd = [_hipcc(), *COMMON]
     if src.endswith(".hip"):
         cmd += ["-x", "hip", *DEVICE]
+    else:
+        cmd += ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include"]  # host-only units
     cmd += ["-c", path, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -9,7 +9,7 @@
 #include <mutex>
 #include <vector>
 
-#include "../../include/qlora.h"
+#include "qlora.h"
 #include "qlora_host.h"
 
 using namespace qlora;
@@ -64,12 +64,6 @@ ColdotShape coldot_shape(int64_t M, int32_t R, int64_t C) {
   return {(int32_t)ms, mps};
 }
 
-int32_t gemv_ksplit(int64_t N, int64_t K) {
-  const int64_t tiles = (N + 15) / 16;
-  const int64_t nb = K / 64;
-  return (int32_t)std::max<int64_t>(1, std::min<int64_t>((512 + tiles - 1) / tiles, nb / 4));
-}
-
 constexpr int64_t kGemvMaxM = 16;
 
 // ---- workspace layouts
@@ -78,17 +72,21 @@ struct FwdWs {
 };
 FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   FwdWs w{};
-  const RowdotShape rs = rowdot_shape(M, K);
   size_t off = 0;
   w.tpart = off;
-  off = align_up(off + sizeof(float) * rs.ksplit * M * r, 256);
-  w.ypart = off;
   if (M <= kGemvMaxM) {
     const int32_t ks = gemv_ksplit(N, K);
-    if (ks > 1) off = align_up(off + sizeof(float) * ks * M * N, 256);
+    off = align_up(off + sizeof(float) * ks * M * r, 256);
+    w.ypart = off;
+    off = align_up(off + sizeof(float) * ks * M * N, 256);
+    w.ls = off;
+  } else {
+    const RowdotShape rs = rowdot_shape(M, K);
+    off = align_up(off + sizeof(float) * rs.ksplit * M * r, 256);
+    w.ypart = off;
+    w.ls = off;
+    off = align_up(off + 2 * M * r, 256);
   }
-  w.ls = off;
-  if (M > kGemvMaxM) off = align_up(off + 2 * M * r, 256);
   w.total = std::max<size_t>(off, 256);
   return w;
 }
@@ -298,18 +296,15 @@ int qlora_linear_fwd(const qlora_nf4dq_t* Wq, const uint16_t* X, int64_t M, cons
   const float s = alpha / (float)r;
   const uint32_t* codes = reinterpret_cast<const uint32_t*>(Wq->codes);
   float* tpart = reinterpret_cast<float*>(base + L.tpart);
+  if (M <= kGemvMaxM) {
+    if (N / 256 >= 4096) return QLORA_ERR_BAD_SHAPE;
+    float* ypart = reinterpret_cast<float*>(base + L.ypart);
+    return hip_status(launch_gemv_fwd(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, X, M, A, B, r, s, Y, T_save, ypart,
+                                      tpart, nf4_tables(), stream));
+  }
   const RowdotShape rs = rowdot_shape(M, K);
   hipError_t e = launch_rowdot(X, A, M, r, K, rs.ksplit, rs.kps, tpart, stream);
   if (e != hipSuccess) return QLORA_ERR_HIP;
-  if (M <= kGemvMaxM) {
-    const int32_t ks = gemv_ksplit(N, K);
-    float* ypart = reinterpret_cast<float*>(base + L.ypart);
-    e = launch_gemv_fwd(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, X, M, tpart, rs.ksplit, B, r, s, Y, T_save, ypart,
-                        ks, nf4_tables(), stream);
-    if (e != hipSuccess) return QLORA_ERR_HIP;
-    if (ks > 1) e = launch_gemv_finish(ypart, ks, M, N, tpart, rs.ksplit, B, r, s, Y, T_save, stream);
-    return hip_status(e);
-  }
   uint16_t* ls = reinterpret_cast<uint16_t*>(base + L.ls);
   e = launch_rowdot_finish(tpart, rs.ksplit, M, r, s, ls, T_save, stream);
   if (e != hipSuccess) return QLORA_ERR_HIP;

@@ -1,199 +1,378 @@
-// Weight-streaming forward for few tokens (M <= 16): Y = X w_hat^T + s T B^T.
+// Weight-streaming forward for few tokens (M <= 16): Y = X w_hat^T + s (X A^T) B^T, one launch.
 //
 // At small batch the layer is bound by reading the 4-bit weights from HBM ("QLoRA --
 // Fine-Tuning a 65B Model on One GPU", "Pitfalls": small-batch generation is memory-bound
 // and 4 bits leave less to read).  Each weight is decoded once, on chip, from its 4-bit code
 // ("QLoRA: Quantize Base Weights to 4-Bit", Section 3) and multiplied on the MFMA units.
 //
-// Work split: a workgroup owns 16 weight rows and a range of 64-weight blocks; its four
-// wavefronts take interleaved blocks.  Lane l handles row n0 + (l & 15) and the 16 weights
-// [16g, 16g+16) of each block, g = l >> 4 (an 8-byte code load).  Two MFMA 16x16x32 steps
-// cover one block; since all 32 reduction indices of each step lie in that block, its
-// constant c1_hat multiplies the 16x16 partial product once, in FP32, before it joins the
-// accumulator.  The 16 levels are looked up unscaled (BF16) with byte permutes.
+// Work split.  A workgroup owns 128 weight rows (4 wavefronts x 2 MFMA column tiles of 16
+// rows) and one of `ksplit` ranges of 64-weight blocks, walked in chunks of kChunk blocks.
+// Per chunk, every thread first issues all of its global loads (part of one weight row's
+// codes and block constants, a slice of X) into registers, then writes them to LDS; the MFMA
+// loop then reads LDS, while the next chunk's loads are in flight.  Lane l handles rows 16t + (l & 15) and, in each block, the 16 weights
+// [16g, 16g+16), g = l >> 4.  Two MFMA 16x16x32 steps cover a block; all 32 reduction
+// indices of each step lie in that block, so its constant c1_hat multiplies the 16x16
+// partial product once, in FP32, before it joins the accumulator.  The 16 levels are looked
+// up unscaled (BF16) with byte permutes.  Loops stay rolled: each workgroup runs the code
+// once, so a compact instruction stream matters as much as the memory stream.
+//
+// Adapter.  T = X A^T is linear in the reduction range, so each workgroup forms the part of
+// T over its own k-range (its wavefronts take interleaved blocks), applies B to it for its
+// 128 rows, and adds that to its partial output.
+//
+// Split-K reduction.  With ksplit > 1 each workgroup writes an FP32 partial; the last
+// workgroup of a row group to finish (a device-scope counter that each workgroup advances by
+// 65536/ksplit, so it is always a multiple of 65536 between calls) sums the partials in a
+// fixed order and writes BF16 Y (and T for the backward).  The counters live in this file as
+// zero-initialized device data; calls with M <= 16 on one device must therefore not overlap.
+// The partials travel through memory with system-scope (cache-bypassing) stores and loads:
+// the writer waits for its stores to complete before advancing the counter, so the reader
+// needs no cache write-back fence.
 #include "qlora_device.h"
 #include "qlora_host.h"
 
 namespace qlora {
+
+__device__ unsigned int g_gemv_counters[4096];
+
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kTiles = 2;               // column tiles (16 rows) per wavefront
+constexpr int kRows = 4 * 16 * kTiles;  // rows per workgroup
+constexpr int kChunk = 4;               // blocks staged per pass
+constexpr int kStageBlocks = kChunk * kRows / kThreads;  // blocks of one row staged per thread
+constexpr uint32_t kCounterPeriod = 65536;
+constexpr int kSumU = 16;               // partials loaded together in the split-K sum
 
-struct BlockIn {
-  uint2 code;      // 16 codes of this lane
-  uint4 x0, x1;    // X[m, 64b + 16g .. +16]
-  uint32_t c8;
-  float c2;
+struct GemvArgs {
+  const uint8_t* codes;
+  const uint8_t* code8;
+  const float* c2s;
+  const float* mu;
+  int64_t N, K;
+  const uint16_t* X;
+  int64_t M;
+  const uint16_t* A;
+  const uint16_t* B;
+  int32_t r;
+  float s;
+  uint16_t* Y;
+  uint16_t* T_save;
+  float* part;   // [ksplit][M][N]
+  float* tpart;  // [ksplit][M][r]
+  int32_t ksplit;
+  int32_t nbs;   // blocks per split
 };
 
-__device__ __forceinline__ void load_block(const uint8_t* codes_b, const uint8_t* code8,
-                                           const float* c2s, const uint16_t* X, int64_t K,
-                                           int64_t nrow, bool nok, int64_t mrow, bool mok, int g,
-                                           int64_t b, BlockIn& in) {
+__device__ __forceinline__ void publish(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ float sum_published(const float* p, int32_t n, int64_t stride) {
+  float s = 0.f;
+  for (int32_t k0 = 0; k0 < n; k0 += kSumU) {
+    float v[kSumU];
+#pragma unroll
+    for (int u = 0; u < kSumU; ++u)
+      v[u] = (k0 + u < n) ? __hip_atomic_load(p + (int64_t)(k0 + u) * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) : 0.f;
+#pragma unroll
+    for (int u = 0; u < kSumU; ++u) s += v[u];
+  }
+  return s;
+}
+
+// Rows are padded so the 16 lanes that read 16 consecutive rows hit distinct LDS banks.
+struct Stage {
+  uint2 codes[kRows][kChunk * 4 + 1];  // row, (block, 8-byte part g) at 4 * block + g
+  float scale[kRows][kChunk + 1];
+  uint4 x[16][kChunk * 8 + 1];         // X[m][64 b + 8 c .. +8] at 8 * b + c
+};
+constexpr int kRStage = 32;       // adapter ranks whose B rows are prefetched into LDS
+
+// Registers holding one chunk's global loads between issue and the LDS write.
+struct ChunkRegs {
+  uint4 cv[kStageBlocks][2];
+  uint32_t c8[kStageBlocks], c2[kStageBlocks];
+  uint4 xv[kChunk / 2];
+};
+
+template <int RT>  // 16-wide tiles of the adapter rank: r <= 16 * RT
+__global__ __launch_bounds__(kThreads) void k_gemv_fused(GemvArgs a, Nf4Tables T) {
+  __shared__ Stage S;
+  __shared__ f32x4_t sred[4][RT][64];
+  __shared__ float sT[16][16 * RT + 1];
+  __shared__ unsigned int s_last;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int64_t N = a.N, K = a.K, M = a.M;
   const int64_t nb_row = K / kBlock1;
-  if (nok) {
-    in.code = *reinterpret_cast<const uint2*>(codes_b + nrow * (K / 2) + b * 32 + 8 * g);
-    const int64_t blk = nrow * nb_row + b;
-    in.c8 = code8[blk];
-    in.c2 = c2s[blk >> 8];
-  } else {
-    in.code = make_uint2(0x88888888u, 0x88888888u);  // the zero level
-    in.c8 = 0;
-    in.c2 = 0.f;
-  }
-  if (mok) {
-    const uint4* xp = reinterpret_cast<const uint4*>(X + mrow * K + b * 64 + 16 * g);
-    in.x0 = xp[0];
-    in.x1 = xp[1];
-  } else {
-    in.x0 = make_uint4(0, 0, 0, 0);
-    in.x1 = in.x0;
-  }
-}
+  const int64_t grp = blockIdx.x;
+  const int ks = blockIdx.y;
+  const int64_t b0 = (int64_t)ks * a.nbs;
+  const int64_t b1 = (b0 + a.nbs < nb_row) ? b0 + a.nbs : nb_row;
+  const float mu = a.mu[0];
+  const int64_t row0 = grp * kRows;
 
-__device__ __forceinline__ void mma_block(const BlockIn& in, const Lut& L, float mu, f32x4_t& acc) {
-  uint32_t w0[4], w1[4];
-  decode8(in.code.x, L, w0);
-  decode8(in.code.y, L, w1);
-  const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-  f32x4_t t = mfma16x16x32(as_bf16x8(in.x0), as_bf16x8(w0), z);
-  t = mfma16x16x32(as_bf16x8(in.x1), as_bf16x8(w1), t);
-  const float c = block_scale(in.c8, in.c2, mu);
-  acc[0] = fmaf(c, t[0], acc[0]);
-  acc[1] = fmaf(c, t[1], acc[1]);
-  acc[2] = fmaf(c, t[2], acc[2]);
-  acc[3] = fmaf(c, t[3], acc[3]);
-}
-
-// Sum the LoRA-down partials into LDS: sT[m][j] = sum_s Tpart[s][m][j].
-__device__ void gather_T(const float* Tpart, int32_t t_splits, int64_t M, int32_t r, float* sT) {
-  for (int i = threadIdx.x; i < M * r; i += kThreads) {
-    float s = 0.f;
-    for (int32_t k = 0; k < t_splits; ++k) s += Tpart[(int64_t)k * M * r + i];
-    sT[i] = s;
-  }
-}
-
-// grid (ceil(N/16), ksplit)
-__global__ __launch_bounds__(kThreads) void k_gemv_fwd(
-    const uint8_t* __restrict__ codes_b, const uint8_t* __restrict__ code8,
-    const float* __restrict__ c2s, const float* __restrict__ mu_p, int64_t N, int64_t K,
-    const uint16_t* __restrict__ X, int64_t M, const float* __restrict__ Tpart, int32_t t_splits,
-    const uint16_t* __restrict__ B, int32_t r, float s, uint16_t* __restrict__ Y,
-    uint16_t* __restrict__ T_save, float* __restrict__ Ypart, int32_t ksplit, Nf4Tables T) {
-  __shared__ f32x4_t red[4][64];
-  __shared__ float sT[16 * 128];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int64_t nrow = n0 + (lane & 15);
-  const int64_t mrow = lane & 15;
-  const bool nok = nrow < N, mok = mrow < M;
-  const float mu = mu_p[0];
+  const rsrc_t rc = make_rsrc(a.codes, N * (K / 2));
+  const rsrc_t r8 = make_rsrc(a.code8, N * nb_row);
+  const rsrc_t r2 = make_rsrc(a.c2s, ((N * nb_row + 255) / 256) * 4);
+  const rsrc_t rx = make_rsrc(a.X, M * K * 2);
+  const rsrc_t ra = make_rsrc(a.A, (int64_t)a.r * K * 2);
   Lut L;
   load_unscaled_lut(T, L);
 
-  const int64_t nb_row = K / kBlock1;
-  const int64_t bps = (nb_row + ksplit - 1) / ksplit;
-  const int64_t bbeg = (int64_t)blockIdx.y * bps;
-  const int64_t bend = (bbeg + bps < nb_row) ? bbeg + bps : nb_row;
+  f32x4_t acc[kTiles];
+  f32x4_t tacc[RT];
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < RT; ++j) tacc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
 
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  int64_t b = bbeg + wave;
-  for (; b + 4 * (kUnroll - 1) < bend; b += 4 * kUnroll) {
-    BlockIn in[kUnroll];
+  // staging roles: thread tid stages blocks [sb0, sb0 + kStageBlocks) of the chunk for weight
+  // row row0 + srow and, for X, row tid >> 4 at the 16-byte column tid & 15 of each pair of
+  // blocks
+  const int srow = tid % kRows, sb0 = (tid / kRows) * kStageBlocks;
+  const uint32_t my_code_off = (uint32_t)((row0 + srow) * (K / 2));
+  const uint32_t my_blk = (uint32_t)((row0 + srow) * nb_row);
+  const int xm = tid >> 4, xc = tid & 15;
+
+  // B rows of this workgroup for the adapter up-projection, prefetched with the first chunk
+  __shared__ uint4 sB[kRows][kRStage / 8];
+  uint4 bpre[kRStage / 8];
+  {
+    const rsrc_t rb = make_rsrc(a.B, N * a.r * 2);
+    const bool pre = (a.r % 8) == 0 && a.r <= kRStage;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) load_block(codes_b, code8, c2s, X, K, nrow, nok, mrow, mok, g, b + 4 * u, in[u]);
+    for (int q = 0; q < kRStage / 8; ++q)
+      bpre[q] = bload16(rb, (pre && 8 * q < a.r && tid < kRows) ? (uint32_t)(((row0 + tid) * a.r + 8 * q) * 2) : kOOB);
+  }
+
+  auto issue = [&](int64_t c0, ChunkRegs& R) {
+    const int nb = (b1 - c0 < kChunk) ? (int)(b1 - c0) : kChunk;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) mma_block(in[u], L, mu, acc);
-  }
-  for (; b < bend; b += 4) {
-    BlockIn in;
-    load_block(codes_b, code8, c2s, X, K, nrow, nok, mrow, mok, g, b, in);
-    mma_block(in, L, mu, acc);
-  }
-  red[wave][lane] = acc;
-  const bool writes_T = T_save && blockIdx.x == 0 && blockIdx.y == 0 && ksplit == 1;
-  if (ksplit == 1) gather_T(Tpart, t_splits, M, r, sT);
-  __syncthreads();
-  if (writes_T) {
-    for (int i = threadIdx.x; i < M * r; i += kThreads) T_save[i] = (uint16_t)(pack_bf16x2(sT[i], 0.f) & 0xFFFFu);
-  }
-  if (wave != 0) return;
-  f32x4_t y = red[0][lane];
+    for (int v = 0; v < kStageBlocks; ++v) {
+      const int u = sb0 + v;
+      const bool ok = u < nb;
+      const uint32_t off = my_code_off + (uint32_t)((c0 + u) * 32);
+      R.cv[v][0] = bload16(rc, ok ? off : kOOB);
+      R.cv[v][1] = bload16(rc, ok ? off + 16 : kOOB);
+      const uint32_t bi = my_blk + (uint32_t)(c0 + u);
+      R.c8[v] = bload1(r8, ok ? bi : kOOB);
+      R.c2[v] = bload4(r2, ok ? (bi >> 8) * 4 : kOOB);
+    }
 #pragma unroll
-  for (int w = 1; w < 4; ++w) {
-    const f32x4_t t = red[w][lane];
-    y[0] += t[0]; y[1] += t[1]; y[2] += t[2]; y[3] += t[3];
-  }
-  // D[m][n]: lane holds rows m = 4g + v, column n = nrow
-  if (!nok) return;
-  if (ksplit == 1) {
+    for (int p = 0; p < kChunk / 2; ++p) {  // X[xm][64 (c0 + 2p) + 8 xc .. +8]
+      const int64_t k = 64 * (c0 + 2 * p) + 8 * xc;
+      const bool ok = (c0 + 2 * p + (xc >> 3)) < b1;
+      R.xv[p] = bload16(rx, ok ? (uint32_t)((xm * K + k) * 2) : kOOB);
+    }
+  };
+  auto stage = [&](const ChunkRegs& R) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t m = 4 * g + v;
-      if (m < M) {
-        float lo = 0.f;
-        for (int32_t j = 0; j < r; ++j) lo = fmaf(sT[m * r + j], bf16lo_to_f32(B[nrow * r + j]), lo);
-        const float out = fmaf(s, lo, y[v]);
-        Y[m * N + nrow] = (uint16_t)(pack_bf16x2(out, 0.f) & 0xFFFFu);
+    for (int v = 0; v < kStageBlocks; ++v) {
+      const int u = sb0 + v;
+      S.codes[srow][4 * u + 0] = make_uint2(R.cv[v][0].x, R.cv[v][0].y);
+      S.codes[srow][4 * u + 1] = make_uint2(R.cv[v][0].z, R.cv[v][0].w);
+      S.codes[srow][4 * u + 2] = make_uint2(R.cv[v][1].x, R.cv[v][1].y);
+      S.codes[srow][4 * u + 3] = make_uint2(R.cv[v][1].z, R.cv[v][1].w);
+      S.scale[srow][u] = block_scale(R.c8[v], __uint_as_float(R.c2[v]), mu);
+    }
+#pragma unroll
+    for (int p = 0; p < kChunk / 2; ++p) S.x[xm][8 * (2 * p + (xc >> 3)) + (xc & 7)] = R.xv[p];
+  };
+
+  ChunkRegs R;
+  issue(b0, R);
+  if (tid < kRows) {
+#pragma unroll
+    for (int q = 0; q < kRStage / 8; ++q) sB[tid][q] = bpre[q];
+  }
+  for (int64_t c0 = b0; c0 < b1; c0 += kChunk) {
+    const int nb = (b1 - c0 < kChunk) ? (int)(b1 - c0) : kChunk;
+    // adapter down-projection inputs of this chunk (this wavefront's share), issued early
+    const int64_t bt = c0 + ((wave - (c0 - b0)) & 3);  // block with ((b - b0) & 3) == wave
+    const bool tshare = bt < c0 + nb;
+    uint4 av[RT][2];
+#pragma unroll
+    for (int j = 0; j < RT; ++j) {
+      const bool ok = tshare && 16 * j + l16 < a.r;
+      const uint32_t ao = (uint32_t)((((int64_t)(16 * j + l16)) * K + 64 * bt + 16 * g) * 2);
+      av[j][0] = bload16(ra, ok ? ao : kOOB);
+      av[j][1] = bload16(ra, ok ? ao + 16 : kOOB);
+    }
+    __syncthreads();  // the previous chunk's LDS reads are done
+    stage(R);
+    __syncthreads();
+    if (c0 + kChunk < b1) issue(c0 + kChunk, R);  // next chunk in flight during this one's math
+
+    // ---- MFMA over the staged chunk
+    for (int u = 0; u < nb; ++u) {
+      const bf16x8_t xa = as_bf16x8(S.x[l16][8 * u + 2 * g]);
+      const bf16x8_t xb = as_bf16x8(S.x[l16][8 * u + 2 * g + 1]);
+      if (c0 + u == bt) {
+#pragma unroll
+        for (int j = 0; j < RT; ++j) {
+          tacc[j] = mfma16x16x32(xa, as_bf16x8(av[j][0]), tacc[j]);
+          tacc[j] = mfma16x16x32(xb, as_bf16x8(av[j][1]), tacc[j]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t) {
+        const int row = wave * 16 * kTiles + 16 * t + l16;
+        const uint2 cw = S.codes[row][4 * u + g];
+        uint32_t w0[4], w1[4];
+        decode8(cw.x, L, w0);
+        decode8(cw.y, L, w1);
+        f32x4_t p = mfma16x16x32(xa, as_bf16x8(w0), z);
+        p = mfma16x16x32(xb, as_bf16x8(w1), p);
+        const float c = S.scale[row][u];
+        acc[t][0] = fmaf(c, p[0], acc[t][0]);
+        acc[t][1] = fmaf(c, p[1], acc[t][1]);
+        acc[t][2] = fmaf(c, p[2], acc[t][2]);
+        acc[t][3] = fmaf(c, p[3], acc[t][3]);
       }
     }
-  } else {
+  }
+
+  // ---- T over this k-range: sum the four wavefronts' shares -> sT[m][j]
+#pragma unroll
+  for (int j = 0; j < RT; ++j) sred[wave][j][lane] = tacc[j];
+  __syncthreads();
+  for (int i = tid; i < 16 * 16 * RT; i += kThreads) {
+    const int j16 = i / 256, rem = i % 256, ln = rem / 4, v = rem % 4;  // D[m = 4*(ln>>4)+v][j = ln & 15]
+    const float s = sred[0][j16][ln][v] + sred[1][j16][ln][v] + sred[2][j16][ln][v] + sred[3][j16][ln][v];
+    sT[4 * (ln >> 4) + v][16 * j16 + (ln & 15)] = s;
+  }
+  __syncthreads();
+
+  // ---- adapter up-projection of this partial T: acc[t][m][n] += s * sum_j T[m][j] B[n][j]
+  const bool b_staged = (a.r % 8) == 0 && a.r <= kRStage;
+  const rsrc_t rb = make_rsrc(a.B, N * a.r * 2);
+  for (int32_t j0 = 0; j0 < a.r; j0 += 32) {
+    const int32_t jj = j0 + 8 * g;
+    uint32_t tv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float lo = (jj + 2 * q < a.r) ? a.s * sT[l16][jj + 2 * q] : 0.f;
+      const float hi = (jj + 2 * q + 1 < a.r) ? a.s * sT[l16][jj + 2 * q + 1] : 0.f;
+      tv[q] = pack_bf16x2(lo, hi);
+    }
+    const bf16x8_t ta = as_bf16x8(tv);
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+      const int rl = wave * 16 * kTiles + 16 * t + l16;
+      uint4 bw;
+      if (b_staged) {
+        bw = (jj < a.r) ? sB[rl][jj / 8] : make_uint4(0, 0, 0, 0);
+      } else {
+        const int64_t n = row0 + rl;
+        uint32_t e[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          e[q] = __builtin_amdgcn_raw_buffer_load_b16(rb, (jj + q < a.r) ? (int)((n * a.r + jj + q) * 2) : (int)kOOB, 0, 0);
+        bw = make_uint4((e[0] & 0xFFFFu) | (e[1] << 16), (e[2] & 0xFFFFu) | (e[3] << 16),
+                        (e[4] & 0xFFFFu) | (e[5] << 16), (e[6] & 0xFFFFu) | (e[7] << 16));
+      }
+      acc[t] = mfma16x16x32(ta, as_bf16x8(bw), acc[t]);
+    }
+  }
+
+  // ---- output: D[m][n] -- lane holds rows m = 4g + v of column n
+  if (a.ksplit == 1) {
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+      const int64_t n = row0 + wave * 16 * kTiles + 16 * t + l16;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t m = 4 * g + v;
+        if (m < M && n < N) a.Y[m * N + n] = (uint16_t)(pack_bf16x2(acc[t][v], 0.f) & 0xFFFFu);
+      }
+    }
+    if (a.T_save && grp == 0) {
+      for (int i = tid; i < M * a.r; i += kThreads)
+        a.T_save[i] = (uint16_t)(pack_bf16x2(sT[i / a.r][i % a.r], 0.f) & 0xFFFFu);
+    }
+    return;
+  }
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) {
+    const int64_t n = row0 + wave * 16 * kTiles + 16 * t + l16;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int64_t m = 4 * g + v;
-      if (m < M) Ypart[((int64_t)blockIdx.y * M + m) * N + nrow] = y[v];
+      if (m < M && n < N) publish(a.part + ((int64_t)ks * M + m) * N + n, acc[t][v]);
     }
   }
-}
-
-// Y[m][n] = sum_s Ypart[s][m][n] + s * sum_j T[m][j] B[n][j]
-__global__ __launch_bounds__(kThreads) void k_gemv_finish(const float* __restrict__ Ypart,
-                                                          int32_t ksplit, int64_t M, int64_t N,
-                                                          const float* __restrict__ Tpart,
-                                                          int32_t t_splits,
-                                                          const uint16_t* __restrict__ B, int32_t r,
-                                                          float s, uint16_t* __restrict__ Y,
-                                                          uint16_t* __restrict__ T_save) {
-  __shared__ float sT[16 * 128];
-  gather_T(Tpart, t_splits, M, r, sT);
-  __syncthreads();
-  if (T_save && blockIdx.x == 0) {
-    for (int i = threadIdx.x; i < M * r; i += kThreads) T_save[i] = (uint16_t)(pack_bf16x2(sT[i], 0.f) & 0xFFFFu);
+  if (grp == 0) {
+    for (int i = tid; i < M * a.r; i += kThreads) publish(a.tpart + (int64_t)ks * M * a.r + i, sT[i / a.r][i % a.r]);
   }
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= M * N) return;
-  const int64_t m = i / N, n = i % N;
-  float y = 0.f;
-  for (int32_t k = 0; k < ksplit; ++k) y += Ypart[(int64_t)k * M * N + i];
-  float lo = 0.f;
-  for (int32_t j = 0; j < r; ++j) lo = fmaf(sT[m * r + j], bf16lo_to_f32(B[n * r + j]), lo);
-  Y[i] = (uint16_t)(pack_bf16x2(fmaf(s, lo, y), 0.f) & 0xFFFFu);
+  // every partial store of this workgroup has completed before its counter increment
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned int inc = kCounterPeriod / (unsigned int)a.ksplit;
+    const unsigned int old = __hip_atomic_fetch_add(&g_gemv_counters[grp], inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = ((old + inc) % kCounterPeriod) == 0u;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // last workgroup of this row group: fixed-order sum of the partials
+  const int64_t nrows = (row0 + kRows <= N) ? kRows : N - row0;
+  for (int64_t i = tid; i < M * nrows; i += kThreads) {
+    const int64_t m = i / nrows, n = row0 + i % nrows;
+    a.Y[m * N + n] = (uint16_t)(pack_bf16x2(sum_published(a.part + m * N + n, a.ksplit, M * N), 0.f) & 0xFFFFu);
+  }
+  if (a.T_save && grp == 0) {
+    for (int i = tid; i < M * a.r; i += kThreads)
+      a.T_save[i] = (uint16_t)(pack_bf16x2(sum_published(a.tpart + i, a.ksplit, M * a.r), 0.f) & 0xFFFFu);
+  }
 }
 
 }  // namespace
 
-hipError_t launch_gemv_fwd(const uint32_t* codes, const uint8_t* code8, const float* c2s,
-                           const float* mu, int64_t N, int64_t K, const uint16_t* X, int64_t M,
-                           const float* Tpart, int32_t t_splits, const uint16_t* B, int32_t r,
-                           float s, uint16_t* Y, uint16_t* T_save, float* Ypart, int32_t ksplit,
-                           const Nf4Tables& T, hipStream_t st) {
-  dim3 grid((unsigned)((N + 15) / 16), (unsigned)ksplit);
-  LaunchTimer t(3, st);
-  hipLaunchKernelGGL(k_gemv_fwd, grid, dim3(kThreads), 0, st,
-                     reinterpret_cast<const uint8_t*>(codes), code8, c2s, mu, N, K, X, M, Tpart,
-                     t_splits, B, r, s, Y, T_save, Ypart, ksplit, T);
-  return hipGetLastError();
+int32_t gemv_ksplit(int64_t N, int64_t K) {
+  const int64_t groups = (N + kRows - 1) / kRows;
+  const int64_t nb_row = K / kBlock1;
+  const int64_t want = (256 + groups - 1) / groups;
+  int32_t ks = 1;
+  while (ks < want && ks * 2 <= nb_row && ks < (int32_t)kCounterPeriod) ks *= 2;
+  return ks;
 }
 
-hipError_t launch_gemv_finish(const float* Ypart, int32_t ksplit, int64_t M, int64_t N,
-                              const float* Tpart, int32_t t_splits, const uint16_t* B, int32_t r,
-                              float s, uint16_t* Y, uint16_t* T_save, hipStream_t st) {
-  const int64_t n = M * N;
-  hipLaunchKernelGGL(k_gemv_finish, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads),
-                     0, st, Ypart, ksplit, M, N, Tpart, t_splits, B, r, s, Y, T_save);
+int64_t gemv_groups(int64_t N) { return (N + kRows - 1) / kRows; }
+
+hipError_t launch_gemv_fwd(const uint32_t* codes, const uint8_t* code8, const float* c2s,
+                           const float* mu, int64_t N, int64_t K, const uint16_t* X, int64_t M,
+                           const uint16_t* A, const uint16_t* B, int32_t r, float s, uint16_t* Y,
+                           uint16_t* T_save, float* part, float* tpart, const Nf4Tables& T,
+                           hipStream_t st) {
+  GemvArgs a;
+  a.codes = reinterpret_cast<const uint8_t*>(codes);
+  a.code8 = code8;
+  a.c2s = c2s;
+  a.mu = mu;
+  a.N = N;
+  a.K = K;
+  a.X = X;
+  a.M = M;
+  a.A = A;
+  a.B = B;
+  a.r = r;
+  a.s = s;
+  a.Y = Y;
+  a.T_save = T_save;
+  a.part = part;
+  a.tpart = tpart;
+  a.ksplit = gemv_ksplit(N, K);
+  const int64_t nb_row = K / kBlock1;
+  a.nbs = (int32_t)((nb_row + a.ksplit - 1) / a.ksplit);
+  dim3 grid((unsigned)gemv_groups(N), (unsigned)a.ksplit);
+  LaunchTimer t(3, st);
+  if (r <= 16) hipLaunchKernelGGL(k_gemv_fused<1>, grid, dim3(kThreads), 0, st, a, T);
+  else if (r <= 32) hipLaunchKernelGGL(k_gemv_fused<2>, grid, dim3(kThreads), 0, st, a, T);
+  else if (r <= 64) hipLaunchKernelGGL(k_gemv_fused<4>, grid, dim3(kThreads), 0, st, a, T);
+  else hipLaunchKernelGGL(k_gemv_fused<8>, grid, dim3(kThreads), 0, st, a, T);
   return hipGetLastError();
 }
 

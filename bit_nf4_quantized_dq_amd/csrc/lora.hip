@@ -15,6 +15,21 @@ namespace qlora {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kSumU = 16;  // partials loaded together before they are added
+
+// Fixed-order sum of n partials p[0], p[stride], ...; loads of kSumU partials are issued
+// before their adds so the sum costs a few memory latencies, not n.
+__device__ __forceinline__ float sum_partials(const float* __restrict__ p, int32_t n, int64_t stride) {
+  float s = 0.f;
+  for (int32_t k0 = 0; k0 < n; k0 += kSumU) {
+    float v[kSumU];
+#pragma unroll
+    for (int u = 0; u < kSumU; ++u) v[u] = (k0 + u < n) ? p[(int64_t)(k0 + u) * stride] : 0.f;
+#pragma unroll
+    for (int u = 0; u < kSumU; ++u) s += v[u];
+  }
+  return s;
+}
 
 __device__ __forceinline__ uint4 ld16_or_zero(const uint16_t* p, bool ok) {
   return ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
@@ -83,8 +98,7 @@ __global__ __launch_bounds__(kThreads) void k_rowdot_finish(const float* __restr
                                                             uint16_t* __restrict__ out_u) {
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (i >= M * R) return;
-  float s = 0.f;
-  for (int32_t ks = 0; ks < ksplit; ++ks) s += part[(int64_t)ks * M * R + i];
+  const float s = sum_partials(part + i, ksplit, M * R);
   if (out_s) out_s[i] = (uint16_t)(pack_bf16x2(s * scale, 0.f) & 0xFFFFu);
   if (out_u) out_u[i] = (uint16_t)(pack_bf16x2(s, 0.f) & 0xFFFFu);
 }
@@ -160,8 +174,7 @@ __global__ __launch_bounds__(kThreads) void k_coldot_finish(const float* __restr
                                                             uint16_t* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // i = j*C + c
   if (i >= (int64_t)R * C) return;
-  float s = 0.f;
-  for (int32_t ms = 0; ms < msplit; ++ms) s += part[(int64_t)ms * R * C + i];
+  const float s = sum_partials(part + i, msplit, (int64_t)R * C);
   const uint16_t b = (uint16_t)(pack_bf16x2(s * scale, 0.f) & 0xFFFFu);
   if (!transposed) {
     out[i] = b;

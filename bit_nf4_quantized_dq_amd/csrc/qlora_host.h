@@ -50,15 +50,14 @@ hipError_t launch_coldot_finish(const float* part, int32_t msplit, int32_t R, in
 hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out,
                                  hipStream_t s);
 
-// ---- weight-streaming forward, M <= 16 (gemv.hip)
+// ---- weight-streaming forward, M <= 16 (gemv.hip): one launch, split-K with FP32
+// partials part [ksplit][M][N] and tpart [ksplit][M][r] in the workspace.
+int32_t gemv_ksplit(int64_t N, int64_t K);
 hipError_t launch_gemv_fwd(const uint32_t* codes, const uint8_t* code8, const float* c2s,
                            const float* mu, int64_t N, int64_t K, const uint16_t* X, int64_t M,
-                           const float* Tpart, int32_t t_splits, const uint16_t* B, int32_t r,
-                           float s, uint16_t* Y, uint16_t* T_save, float* Ypart, int32_t ksplit,
-                           const Nf4Tables& T, hipStream_t st);
-hipError_t launch_gemv_finish(const float* Ypart, int32_t ksplit, int64_t M, int64_t N,
-                              const float* Tpart, int32_t t_splits, const uint16_t* B, int32_t r,
-                              float s, uint16_t* Y, uint16_t* T_save, hipStream_t st);
+                           const uint16_t* A, const uint16_t* B, int32_t r, float s, uint16_t* Y,
+                           uint16_t* T_save, float* part, float* tpart, const Nf4Tables& T,
+                           hipStream_t st);
 
 // ---- fused dequant MFMA GEMMs (gemm.hip)
 // Y[M,N] = X[M,K] w_hat^T + L[M,r] B[N,r]^T, L = s*T (BF16, prescaled)
