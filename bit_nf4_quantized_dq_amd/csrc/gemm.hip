@@ -16,26 +16,33 @@
 //             the output dimension, so a thread decodes 8 rows x 8 columns with the unscaled
 //             table, applies each row's constant in FP32, and writes the 8x8 tile transposed
 //             (8 n-values per feature k) -- the transposed tile.
-// Adapter term: after the main loop, ceil(r/32) extra reduction steps of width 32 multiply
-// the prescaled BF16 side input (s T for forward, s G for dX) by B (forward) or A^T (dX).
+// Adapter term: ceil(r/32) extra reduction steps of width 32 multiply the prescaled BF16
+// side input (s T for forward, s G for dX) by B (forward) or A^T (dX); they run first,
+// through the second LDS stage buffer, so the accumulators start from the adapter term.
 //
-// Tiling: 256 (features) x 256 (tokens) per workgroup, reduction step 64, 4 wavefronts in a
-// 2 x 2 grid of 128 x 128 wavefront tiles (8 x 8 MFMA tiles, FP32 accumulators).  LDS holds
-// two stages of a BF16 weight tile and a BF16 activation tile (4 x 32 KB); 16-byte chunks
-// are XOR-swizzled by row so both the staging writes and the MFMA operand reads are free of
-// bank conflicts.  Global loads are raw buffer loads (zero outside the tensor), so the
-// steady-state loop has no branches; the last stage is peeled.
+// Tiling: 256 (features) x 256 (tokens) per workgroup, reduction step 64, 8 wavefronts
+// (two per SIMD) in a 2 x 4 grid of 128 x 64 wavefront tiles (8 x 4 MFMA tiles, 128 FP32
+// accumulators per lane).  Wavefronts 0-3 stage (decode) the weight tile, 4-7 stage the
+// activation tile, through one shared prefetch register buffer; every wavefront then runs
+// its share of the MFMAs, so the decode VALU work of one wavefront overlaps the matrix work
+// of the other wavefront on its SIMD.  LDS holds two stages of both tiles (4 x 32 KB);
+// 16-byte chunks are XOR-swizzled by row so the staging writes and the operand reads are
+// free of bank conflicts.  Global loads are raw buffer loads (zero outside the tensor), so
+// the steady-state loop has no data-dependent branches; the last stage is peeled.
 #include "qlora_device.h"
 #include "qlora_host.h"
 
 namespace qlora {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int BF = 256;   // features per tile
-constexpr int BMT = 256;  // tokens per tile
-constexpr int BK = 64;    // reduction step
+constexpr int kThreads = 512;
+constexpr int kStage = 256;      // threads of each staging role
+constexpr int BF = 256;          // features per tile
+constexpr int BMT = 256;         // tokens per tile
+constexpr int BK = 64;           // reduction step
 constexpr int kChunks = BK / 8;  // 16-byte chunks per LDS row
+constexpr int TI = 8, TJ = 4;    // 16x16 MFMA tiles per wavefront: 128 features x 64 tokens
+typedef f32x4_t Acc[TI][TJ];
 
 __device__ __forceinline__ int swz(int row, int chunk) {
   return row * kChunks + (chunk ^ ((row ^ (row >> 3)) & 7));
@@ -46,185 +53,188 @@ struct Smem {
   uint4 x[2][BMT * kChunks];
 };
 
-// ---- activation tile: rows = tokens (from m0), columns = reduction index (Kr in total)
-struct ActRegs {
+// One staging thread's global loads between issue and the LDS write (either role).
+struct Pre {
   uint4 v[8];
 };
 
-__device__ __forceinline__ void act_load(rsrc_t rp, int64_t Kr, int64_t k0, ActRegs& R) {
+// ---- activation tile: rows = tokens (from m0), columns = reduction index (Kr in total)
+__device__ __forceinline__ void act_load(rsrc_t rp, uint32_t Kr, uint32_t k0, int t, Pre& R) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int c = threadIdx.x + kThreads * i;
-    const int row = c >> 3, ch = c & 7;
-    const int64_t k = k0 + 8 * ch;
-    const uint32_t off = (k < Kr) ? (uint32_t)((row * Kr + k) * 2) : kOOB;
-    R.v[i] = bload16(rp, off);
+    const int c = t + kStage * i;
+    const uint32_t row = c >> 3, k = k0 + 8 * (c & 7);
+    R.v[i] = bload16(rp, (k < Kr) ? (row * Kr + k) * 2 : kOOB);
   }
 }
 
-__device__ __forceinline__ void act_store(uint4* __restrict__ s, const ActRegs& R) {
+__device__ __forceinline__ void act_store(uint4* __restrict__ s, int t, const Pre& R) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int c = threadIdx.x + kThreads * i;
+    const int c = t + kStage * i;
     s[swz(c >> 3, c & 7)] = R.v[i];
   }
 }
 
 // ---- forward weight tile: thread t decodes row f0 + t, block kb (64 weights)
-struct FwdRegs {
-  uint4 c0, c1;
-  uint32_t c8;
-  float c2;
-};
-
 struct FwdSrc {
   rsrc_t codes;  // from row f0
-  rsrc_t code8;  // whole tensor
+  rsrc_t code8;  // from block f0 * nb_row
   rsrc_t c2s;    // whole tensor
-  int64_t row_bytes;  // K / 2
-  int64_t nb_row;     // K / 64
-  int64_t f0;
+  uint32_t row_bytes;  // K / 2
+  uint32_t nb_row;     // K / 64
+  uint32_t blk0;       // f0 * nb_row
 };
 
-__device__ __forceinline__ void fwd_w_load(const FwdSrc& S, int64_t kb, FwdRegs& R) {
-  const int t = threadIdx.x;
-  const uint32_t off = (uint32_t)(t * S.row_bytes + kb * 32);
-  R.c0 = bload16(S.codes, off);
-  R.c1 = bload16(S.codes, off + 16);
-  const int64_t blk = (S.f0 + t) * S.nb_row + kb;
-  R.c8 = bload1(S.code8, (uint32_t)blk);
-  R.c2 = __uint_as_float(bload4(S.c2s, (uint32_t)((blk >> 8) * 4)));
+__device__ __forceinline__ void fwd_w_load(const FwdSrc& S, uint32_t kb, int t, Pre& R) {
+  const uint32_t off = t * S.row_bytes + kb * 32;
+  R.v[0] = bload16(S.codes, off);
+  R.v[1] = bload16(S.codes, off + 16);
+  const uint32_t lb = t * S.nb_row + kb;
+  R.v[2].x = bload1(S.code8, lb);
+  R.v[2].y = bload4(S.c2s, ((S.blk0 + lb) >> 8) * 4);
 }
 
-__device__ __forceinline__ void fwd_w_store(uint4* __restrict__ s, const FwdRegs& R, float mu,
+__device__ __forceinline__ void fwd_w_store(uint4* __restrict__ s, int t, const Pre& R, float mu,
                                             const Nf4Tables& T) {
   Lut L;
-  build_scaled_lut(T, block_scale(R.c8, R.c2, mu), L);
-  const uint32_t words[8] = {R.c0.x, R.c0.y, R.c0.z, R.c0.w, R.c1.x, R.c1.y, R.c1.z, R.c1.w};
-  const int row = threadIdx.x;
+  build_scaled_lut(T, block_scale(R.v[2].x, __uint_as_float(R.v[2].y), mu), L);
+  const uint32_t words[8] = {R.v[0].x, R.v[0].y, R.v[0].z, R.v[0].w, R.v[1].x, R.v[1].y, R.v[1].z, R.v[1].w};
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     uint32_t o[4];
     decode8(words[c], L, o);
-    s[swz(row, c)] = make_uint4(o[0], o[1], o[2], o[3]);
+    s[swz(t, c)] = make_uint4(o[0], o[1], o[2], o[3]);
   }
 }
 
 // ---- dX weight tile: thread t decodes rows n0 + 8*(t>>5) + i (i < 8), columns k0 + 8*(t&31) + e
-struct DxRegs {
-  uint32_t w[8];
-  uint32_t c8[8];
-  float c2[8];
-};
-
 struct DxSrc {
   rsrc_t codes;  // whole tensor
   rsrc_t code8;
   rsrc_t c2s;
-  int64_t K;
-  int64_t k0;
+  uint32_t row_bytes;  // K / 2
+  uint32_t nb_row;     // K / 64
+  uint32_t code_off;   // this thread's offset of row 8*rg, column k0 + 8*kc (kOOB when past K)
+  uint32_t blk_off;    // this thread's block index of row 8*rg
 };
 
-__device__ __forceinline__ void dx_w_load(const DxSrc& S, int64_t n0, DxRegs& R) {
-  const int rg = threadIdx.x >> 5, kc = threadIdx.x & 31;
-  const int64_t k = S.k0 + 8 * kc;
-  const bool kok = k < S.K;
+__device__ __forceinline__ void dx_w_load(const DxSrc& S, uint32_t n0, Pre& R) {
+  uint32_t* w = reinterpret_cast<uint32_t*>(&R.v[0]);   // 8 code words
+  uint32_t* c8 = reinterpret_cast<uint32_t*>(&R.v[2]);  // 8 code8
+  uint32_t* c2 = reinterpret_cast<uint32_t*>(&R.v[4]);  // 8 c2s bits
+  const bool kok = S.code_off != kOOB;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int64_t n = n0 + 8 * rg + i;
-    R.w[i] = bload4(S.codes, kok ? (uint32_t)((n * S.K + k) / 2) : kOOB);
-    const int64_t blk = n * (S.K / kBlock1) + (k >> 6);
-    R.c8[i] = bload1(S.code8, kok ? (uint32_t)blk : kOOB);
-    R.c2[i] = __uint_as_float(bload4(S.c2s, kok ? (uint32_t)((blk >> 8) * 4) : kOOB));
+    const uint32_t n = n0 + i;
+    w[i] = bload4(S.codes, kok ? S.code_off + n * S.row_bytes : kOOB);
+    const uint32_t blk = S.blk_off + n * S.nb_row;
+    c8[i] = bload1(S.code8, kok ? blk : kOOB);
+    c2[i] = bload4(S.c2s, kok ? (blk >> 8) * 4 : kOOB);
   }
 }
 
-__device__ __forceinline__ void dx_w_store(uint4* __restrict__ s, const DxRegs& R, float mu, const Lut& L) {
-  const int rg = threadIdx.x >> 5, kc = threadIdx.x & 31;
-  float sc[8];
-  uint32_t d[8][4];
+__device__ __forceinline__ void dx_w_store(uint4* __restrict__ s, int t, const Pre& R, float mu, const Lut& L) {
+  const int rg = t >> 5, kc = t & 31;
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(&R.v[0]);
+  const uint32_t* c8 = reinterpret_cast<const uint32_t*>(&R.v[2]);
+  const uint32_t* c2 = reinterpret_cast<const uint32_t*>(&R.v[4]);
+  uint32_t o[8][4];  // o[e][p]: BF16 pair (rows 2p, 2p+1) of column e
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    sc[i] = block_scale(R.c8[i], R.c2[i], mu);
-    decode8(R.w[i], L, d[i]);
-  }
+  for (int p = 0; p < 4; ++p) {
+    const float sa = block_scale(c8[2 * p], __uint_as_float(c2[2 * p]), mu);
+    const float sb = block_scale(c8[2 * p + 1], __uint_as_float(c2[2 * p + 1]), mu);
+    uint32_t da[4], db[4];
+    decode8(w[2 * p], L, da);
+    decode8(w[2 * p + 1], L, db);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    uint32_t o[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t a = d[2 * p][e >> 1], b = d[2 * p + 1][e >> 1];
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t a = da[e >> 1], b = db[e >> 1];
       const float fa = (e & 1) ? bf16hi_to_f32(a) : bf16lo_to_f32(a);
       const float fb = (e & 1) ? bf16hi_to_f32(b) : bf16lo_to_f32(b);
-      o[p] = pack_bf16x2(fa * sc[2 * p], fb * sc[2 * p + 1]);
+      o[e][p] = pack_bf16x2(fa * sa, fb * sb);
     }
-    s[swz(8 * kc + e, rg)] = make_uint4(o[0], o[1], o[2], o[3]);
   }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s[swz(8 * kc + e, rg)] = make_uint4(o[e][0], o[e][1], o[e][2], o[e][3]);
 }
 
-// ---- MFMA on one LDS stage: two 32-wide reduction halves, 8 x 8 tiles per wavefront
+// ---- MFMA on one LDS stage: two 32-wide reduction halves
 __device__ __forceinline__ void mma_stage(const uint4* __restrict__ sw, const uint4* __restrict__ sx,
-                                          int wf, int wmt, int lr, int lg, f32x4_t (&acc)[8][8]) {
+                                          int wf, int wmt, int lr, int lg, Acc& acc) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    bf16x8_t a[8];
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8_t a[TI], b[TJ];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = as_bf16x8(sw[swz(wf + 16 * i + lr, 4 * h + lg)]);
+    for (int i = 0; i < TI; ++i) a[i] = as_bf16x8(sw[swz(wf + 16 * i + lr, 4 * h + lg)]);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bf16x8_t b = as_bf16x8(sx[swz(wmt + 16 * j + lr, 4 * h + lg)]);
+    for (int j = 0; j < TJ; ++j) b[j] = as_bf16x8(sx[swz(wmt + 16 * j + lr, 4 * h + lg)]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i][j] = mfma16x16x32(a[i], b, acc[i][j]);
-    }
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
   }
 }
 
-// Gather 8 BF16 values p[0], p[stride], ... (predicated) into one MFMA operand.
-__device__ __forceinline__ bf16x8_t gather8(const uint16_t* __restrict__ p, int64_t stride, int valid) {
-  uint32_t v[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t lo = (2 * q < valid) ? p[(2 * q) * stride] : 0u;
-    const uint32_t hi = (2 * q + 1 < valid) ? p[(2 * q + 1) * stride] : 0u;
-    v[q] = lo | (hi << 16);
-  }
-  return as_bf16x8(v);
-}
-
-// Adapter K-slices: acc[f][m] += sum_j Wl[f][j] * Lm[m][j], j < r.  Wl element (f, j) is at
-// wl[f * wl_fs + j * wl_js]; Lm is [M, r] row-major.
+// Adapter K-slices: acc[f][m] += sum_j Wl[f][j] * Lm[m][j], j < r, in slices of 32 j.
+// Each slice is staged through an LDS stage buffer (weights side by wavefronts 0-3, token
+// side by 4-7; one row of 32 values per thread, element loads with out-of-range zeros) and
+// multiplied like one 32-wide half of a main-loop stage.  Wl element (f, j) is at
+// f * wl_fs + j * wl_js (elements); Lm is [M, r] row-major.
 __device__ __forceinline__ void lora_slices(const uint16_t* __restrict__ wl, int64_t wl_fs, int64_t wl_js,
                                             int64_t F, const uint16_t* __restrict__ Lm, int64_t M,
-                                            int32_t r, int64_t f0, int64_t m0, int lr, int lg,
-                                            f32x4_t (&acc)[8][8]) {
+                                            int32_t r, int64_t f0, int64_t m0, bool wrole, int st,
+                                            uint4* __restrict__ sw, uint4* __restrict__ sx, int wf,
+                                            int wmt, int lr, int lg, Acc& acc) {
+  const rsrc_t rw = make_rsrc(wl, (F - 1) * wl_fs * 2 + (int64_t)r * wl_js * 2);
+  const rsrc_t rm = make_rsrc(Lm, M * (int64_t)r * 2);
   for (int32_t j0 = 0; j0 < r; j0 += 32) {
-    const int32_t jj = j0 + 8 * lg;
-    const int valid = (r - jj) > 8 ? 8 : (r - jj > 0 ? r - jj : 0);
-    bf16x8_t a[8];
+    uint32_t e[32];
+    if (wrole) {
+      const int64_t f = f0 + st;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t f = f0 + 16 * i + lr;
-      a[i] = gather8(wl + (f < F ? f : 0) * wl_fs + (int64_t)jj * wl_js, wl_js, f < F ? valid : 0);
+      for (int q = 0; q < 32; ++q) {
+        const bool ok = f < F && j0 + q < r;
+        e[q] = __builtin_amdgcn_raw_buffer_load_b16(rw, ok ? (int)((f * wl_fs + (int64_t)(j0 + q) * wl_js) * 2) : (int)kOOB, 0, 0);
+      }
+    } else {
+      const int64_t m = m0 + st;
+#pragma unroll
+      for (int q = 0; q < 32; ++q) {
+        const bool ok = m < M && j0 + q < r;
+        e[q] = __builtin_amdgcn_raw_buffer_load_b16(rm, ok ? (int)((m * r + j0 + q) * 2) : (int)kOOB, 0, 0);
+      }
     }
+    __syncthreads();  // previous slice's reads are done
+    uint4* dst = wrole ? sw : sx;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t m = m0 + 16 * j + lr;
-      const bf16x8_t b = gather8(Lm + (m < M ? m : 0) * r + jj, 1, m < M ? valid : 0);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i][j] = mfma16x16x32(a[i], b, acc[i][j]);
+    for (int c = 0; c < 4; ++c) {
+      dst[swz(st, c)] = make_uint4((e[8 * c + 0] & 0xFFFFu) | (e[8 * c + 1] << 16), (e[8 * c + 2] & 0xFFFFu) | (e[8 * c + 3] << 16),
+                                   (e[8 * c + 4] & 0xFFFFu) | (e[8 * c + 5] << 16), (e[8 * c + 6] & 0xFFFFu) | (e[8 * c + 7] << 16));
     }
+    __syncthreads();
+    bf16x8_t a[TI], b[TJ];
+#pragma unroll
+    for (int i = 0; i < TI; ++i) a[i] = as_bf16x8(sw[swz(wf + 16 * i + lr, lg)]);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) b[j] = as_bf16x8(sx[swz(wmt + 16 * j + lr, lg)]);
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
   }
 }
 
 // Store D[f][m] tile: lane holds features f = f0 + 16 i + 4 lg + v (v < 4) of token m.
 __device__ __forceinline__ void store_tile(uint16_t* __restrict__ Y, int64_t M, int64_t F, int64_t f0,
-                                           int64_t m0, int lr, int lg, const f32x4_t (&acc)[8][8]) {
+                                           int64_t m0, int lr, int lg, const Acc& acc) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < TJ; ++j) {
     const int64_t m = m0 + 16 * j + lr;
     if (m >= M) continue;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < TI; ++i) {
       const int64_t f = f0 + 16 * i + 4 * lg;
       if (f < F) {
         const uint32_t lo = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
@@ -235,6 +245,13 @@ __device__ __forceinline__ void store_tile(uint16_t* __restrict__ Y, int64_t M, 
   }
 }
 
+__device__ __forceinline__ void zero_acc(Acc& acc) {
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+}
+
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_fwd(
     const uint32_t* __restrict__ codes, const uint8_t* __restrict__ code8,
     const float* __restrict__ c2s, const float* __restrict__ mu_p, int64_t N, int64_t K,
@@ -242,49 +259,48 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_fwd(
     const uint16_t* __restrict__ Bl, int32_t r, uint16_t* __restrict__ Y, Nf4Tables T) {
   extern __shared__ uint4 smem_raw[];
   Smem& S = *reinterpret_cast<Smem*>(smem_raw);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const int wf = (wave >> 1) * 128, wmt = (wave & 1) * 128;
+  const int wf = (wave & 1) * 128, wmt = (wave >> 1) * 64;
+  const bool wrole = tid < kStage;  // wavefronts 0-3 stage weights, 4-7 activations
+  const int st = wrole ? tid : tid - kStage;
   const int64_t f0 = (int64_t)blockIdx.x * BF;
   const int64_t m0 = (int64_t)blockIdx.y * BMT;
   const float mu = mu_p[0];
-  const int64_t nkb = K / BK;
+  const uint32_t nkb = (uint32_t)(K / BK);
 
   const rsrc_t xr = make_rsrc(X + m0 * K, (M - m0) * K * 2);
   FwdSrc ws;
   ws.codes = make_rsrc(reinterpret_cast<const uint8_t*>(codes) + f0 * (K / 2), (N - f0) * (K / 2));
-  ws.code8 = make_rsrc(code8, N * (K / kBlock1));
+  ws.code8 = make_rsrc(code8 + f0 * (K / kBlock1), (N - f0) * (K / kBlock1));
   ws.c2s = make_rsrc(c2s, ((N * (K / kBlock1) + 255) / 256) * 4);
-  ws.row_bytes = K / 2;
-  ws.nb_row = K / kBlock1;
-  ws.f0 = f0;
+  ws.row_bytes = (uint32_t)(K / 2);
+  ws.nb_row = (uint32_t)(K / kBlock1);
+  ws.blk0 = (uint32_t)(f0 * (K / kBlock1));
 
-  f32x4_t acc[8][8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  Pre pre;
+  if (wrole) fwd_w_load(ws, 0, st, pre);
+  else act_load(xr, (uint32_t)K, 0, st, pre);
 
-  ActRegs ar;
-  FwdRegs wr;
-  act_load(xr, K, 0, ar);
-  fwd_w_load(ws, 0, wr);
-  act_store(S.x[0], ar);
-  fwd_w_store(S.w[0], wr, mu, T);
+  Acc acc;
+  zero_acc(acc);
+  // adapter: Y += (s T) B^T, B [N, r] row-major -> element (f, j) at f*r + j
+  lora_slices(Bl, r, 1, N, Lm, M, r, f0, m0, wrole, st, S.w[1], S.x[1], wf, wmt, lr, lg, acc);
+
+  if (wrole) fwd_w_store(S.w[0], st, pre, mu, T);
+  else act_store(S.x[0], st, pre);
   __syncthreads();
 
-  for (int64_t kb = 0; kb + 1 < nkb; ++kb) {
+  for (uint32_t kb = 0; kb + 1 < nkb; ++kb) {
     const int buf = kb & 1;
-    act_load(xr, K, (kb + 1) * BK, ar);
-    fwd_w_load(ws, kb + 1, wr);
+    if (wrole) fwd_w_load(ws, kb + 1, st, pre);
+    else act_load(xr, (uint32_t)K, (kb + 1) * BK, st, pre);
     mma_stage(S.w[buf], S.x[buf], wf, wmt, lr, lg, acc);
-    act_store(S.x[buf ^ 1], ar);
-    fwd_w_store(S.w[buf ^ 1], wr, mu, T);
+    if (wrole) fwd_w_store(S.w[buf ^ 1], st, pre, mu, T);
+    else act_store(S.x[buf ^ 1], st, pre);
     __syncthreads();
   }
   mma_stage(S.w[(nkb - 1) & 1], S.x[(nkb - 1) & 1], wf, wmt, lr, lg, acc);
-  // adapter: Y += (s T) B^T, B [N, r] row-major -> element (f, j) at f*r + j
-  lora_slices(Bl, r, 1, N, Lm, M, r, f0 + wf, m0 + wmt, lr, lg, acc);
   store_tile(Y, M, N, f0 + wf, m0 + wmt, lr, lg, acc);
 }
 
@@ -295,13 +311,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_dx(
     const uint16_t* __restrict__ Al, int32_t r, uint16_t* __restrict__ dX, Nf4Tables T) {
   extern __shared__ uint4 smem_raw[];
   Smem& S = *reinterpret_cast<Smem*>(smem_raw);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const int wf = (wave >> 1) * 128, wmt = (wave & 1) * 128;
+  const int wf = (wave & 1) * 128, wmt = (wave >> 1) * 64;
+  const bool wrole = tid < kStage;
+  const int st = wrole ? tid : tid - kStage;
   const int64_t k0 = (int64_t)blockIdx.x * BF;  // output features = columns of W
   const int64_t m0 = (int64_t)blockIdx.y * BMT;
   const float mu = mu_p[0];
-  const int64_t nnb = (N + BK - 1) / BK;
+  const uint32_t nnb = (uint32_t)((N + BK - 1) / BK);
   Lut L;
   load_unscaled_lut(T, L);
 
@@ -310,35 +328,38 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_dx(
   ws.codes = make_rsrc(codes, N * (K / 2));
   ws.code8 = make_rsrc(code8, N * (K / kBlock1));
   ws.c2s = make_rsrc(c2s, ((N * (K / kBlock1) + 255) / 256) * 4);
-  ws.K = K;
-  ws.k0 = k0;
+  ws.row_bytes = (uint32_t)(K / 2);
+  ws.nb_row = (uint32_t)(K / kBlock1);
+  {
+    const int rg = st >> 5, kc = st & 31;
+    const int64_t k = k0 + 8 * kc;
+    ws.code_off = (k < K) ? (uint32_t)((8 * rg) * (K / 2) + k / 2) : kOOB;
+    ws.blk_off = (uint32_t)((8 * rg) * (K / kBlock1) + k / kBlock1);
+  }
 
-  f32x4_t acc[8][8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  Pre pre;
+  if (wrole) dx_w_load(ws, 0, pre);
+  else act_load(yr, (uint32_t)N, 0, st, pre);
 
-  ActRegs ar;
-  DxRegs wr;
-  act_load(yr, N, 0, ar);
-  dx_w_load(ws, 0, wr);
-  act_store(S.x[0], ar);
-  dx_w_store(S.w[0], wr, mu, L);
+  Acc acc;
+  zero_acc(acc);
+  // adapter: dX += (s G) A, A [r, K] -> element (f = k, j) at j*K + k
+  lora_slices(Al, 1, K, K, Lg, M, r, k0, m0, wrole, st, S.w[1], S.x[1], wf, wmt, lr, lg, acc);
+
+  if (wrole) dx_w_store(S.w[0], st, pre, mu, L);
+  else act_store(S.x[0], st, pre);
   __syncthreads();
 
-  for (int64_t nb = 0; nb + 1 < nnb; ++nb) {
+  for (uint32_t nb = 0; nb + 1 < nnb; ++nb) {
     const int buf = nb & 1;
-    act_load(yr, N, (nb + 1) * BK, ar);
-    dx_w_load(ws, (nb + 1) * BK, wr);
+    if (wrole) dx_w_load(ws, (nb + 1) * BK, pre);
+    else act_load(yr, (uint32_t)N, (nb + 1) * BK, st, pre);
     mma_stage(S.w[buf], S.x[buf], wf, wmt, lr, lg, acc);
-    act_store(S.x[buf ^ 1], ar);
-    dx_w_store(S.w[buf ^ 1], wr, mu, L);
+    if (wrole) dx_w_store(S.w[buf ^ 1], st, pre, mu, L);
+    else act_store(S.x[buf ^ 1], st, pre);
     __syncthreads();
   }
   mma_stage(S.w[(nnb - 1) & 1], S.x[(nnb - 1) & 1], wf, wmt, lr, lg, acc);
-  // adapter: dX += (s G) A, A [r, K] -> element (f = k, j) at j*K + k
-  lora_slices(Al, 1, K, K, Lg, M, r, k0 + wf, m0 + wmt, lr, lg, acc);
   store_tile(dX, M, K, k0 + wf, m0 + wmt, lr, lg, acc);
 }
 
