@@ -23,6 +23,7 @@ KERNEL_IDS = {
     "gemm_dx": 5,
     "lora_down": 6,
     "lora_grad": 7,
+    "dequant_t": 8,
 }
 
 

@@ -16,7 +16,15 @@ using namespace qlora;
 
 namespace {
 
-constexpr int64_t kMaxElems = int64_t(1) << 40;
+// Buffer descriptors address at most 4 GiB from their base: a 256-row operand tile of
+// width d must stay below 2^32 bytes, and the codes of one weight below 2^31 bytes.
+constexpr int64_t kMaxDim = int64_t(1) << 22;
+constexpr int64_t kMaxElems = int64_t(1) << 32;
+
+inline bool shape_ok(int64_t d_out, int64_t d_in) {
+  return d_out >= 16 && d_in >= 64 && d_in % 64 == 0 && d_out % 16 == 0 && d_out <= kMaxDim && d_in <= kMaxDim &&
+         d_out * d_in <= kMaxElems;
+}
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -26,8 +34,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP
 int check_wq(const qlora_nf4dq_t* Wq) {
   if (!Wq || !Wq->codes || !Wq->code8 || !Wq->c2s || !Wq->mu) return QLORA_ERR_INVALID_ARG;
   if (Wq->block1 != 64 || Wq->block2 != 256) return QLORA_ERR_UNSUPPORTED;
-  if (Wq->d_out < 16 || Wq->d_in < 64 || Wq->d_in % 64 != 0 || Wq->d_out % 16 != 0) return QLORA_ERR_BAD_SHAPE;
-  if (Wq->d_out > kMaxElems / Wq->d_in) return QLORA_ERR_BAD_SHAPE;
+  if (!shape_ok(Wq->d_out, Wq->d_in)) return QLORA_ERR_BAD_SHAPE;
   if (!aligned16(Wq->codes)) return QLORA_ERR_INVALID_ARG;
   return QLORA_OK;
 }
@@ -65,10 +72,13 @@ ColdotShape coldot_shape(int64_t M, int32_t R, int64_t C) {
 }
 
 constexpr int64_t kGemvMaxM = 16;
+// From this many tokens on, the weight is decoded once into a BF16 copy in the workspace
+// and multiplied by the plain BF16 GEMM; below it the fused kernels decode per tile.
+constexpr int64_t kNtMinM = 1024;
 
 // ---- workspace layouts
 struct FwdWs {
-  size_t tpart, ypart, ls, total;
+  size_t tpart, ypart, ls, wcopy, total;
 };
 FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   FwdWs w{};
@@ -86,13 +96,17 @@ FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
     w.ypart = off;
     w.ls = off;
     off = align_up(off + 2 * M * r, 256);
+    if (M >= kNtMinM) {
+      w.wcopy = off;
+      off = align_up(off + 2 * (size_t)N * K, 256);
+    }
   }
   w.total = std::max<size_t>(off, 256);
   return w;
 }
 
 struct BwdWs {
-  size_t tpart, t, g, lg, bt, cpart, total;
+  size_t tpart, t, g, lg, bt, cpart, wcopy, total;
 };
 BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   BwdWs w{};
@@ -111,6 +125,10 @@ BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   off = align_up(off + 2 * (size_t)r * N, 256);
   w.cpart = off;
   off = align_up(off + sizeof(float) * std::max<int64_t>((int64_t)ca.msplit * r * K, (int64_t)cb.msplit * r * N), 256);
+  if (M >= kNtMinM) {
+    w.wcopy = off;
+    off = align_up(off + 2 * (size_t)N * K, 256);
+  }
   w.total = off;
   return w;
 }
@@ -216,7 +234,7 @@ const char* qlora_strerror(int status) {
 
 int qlora_quant_sizes(int64_t d_out, int64_t d_in, size_t* codes_bytes, size_t* code8_bytes, size_t* c2s_bytes) {
   if (!codes_bytes || !code8_bytes || !c2s_bytes) return QLORA_ERR_INVALID_ARG;
-  if (d_out < 16 || d_in < 64 || d_in % 64 || d_out % 16 || d_out > kMaxElems / d_in) return QLORA_ERR_BAD_SHAPE;
+  if (!shape_ok(d_out, d_in)) return QLORA_ERR_BAD_SHAPE;
   const int64_t n = d_out * d_in, nb = n / 64;
   *codes_bytes = (size_t)(n / 2);
   *code8_bytes = (size_t)nb;
@@ -226,7 +244,7 @@ int qlora_quant_sizes(int64_t d_out, int64_t d_in, size_t* codes_bytes, size_t* 
 
 int qlora_workspace_size(int op, int64_t M, int64_t d_out, int64_t d_in, int32_t r, size_t* ws_bytes) {
   if (!ws_bytes) return QLORA_ERR_INVALID_ARG;
-  if (d_out < 16 || d_in < 64 || d_in % 64 || d_out % 16 || d_out > kMaxElems / d_in) return QLORA_ERR_BAD_SHAPE;
+  if (!shape_ok(d_out, d_in)) return QLORA_ERR_BAD_SHAPE;
   if (op == QLORA_OP_QUANTIZE) {
     *ws_bytes = quant_ws(d_out, d_in);
     return QLORA_OK;
@@ -308,6 +326,14 @@ int qlora_linear_fwd(const qlora_nf4dq_t* Wq, const uint16_t* X, int64_t M, cons
   uint16_t* ls = reinterpret_cast<uint16_t*>(base + L.ls);
   e = launch_rowdot_finish(tpart, rs.ksplit, M, r, s, ls, T_save, stream);
   if (e != hipSuccess) return QLORA_ERR_HIP;
+  if (M >= kNtMinM) {
+    uint16_t* wcopy = reinterpret_cast<uint16_t*>(base + L.wcopy);
+    if ((e = launch_dequant(codes, Wq->code8, Wq->c2s, Wq->mu, wcopy, N * K / 8, nf4_tables(), stream)) != hipSuccess)
+      return QLORA_ERR_HIP;
+    // Y = X w_hat^T + (s T) B^T: A = w_hat [N, K], Wl = B [N, r] (f*r + j)
+    e = launch_gemm_nt(wcopy, N, X, M, K, B, r, 1, ls, r, Y, QLORA_K_GEMM_FWD, stream);
+    return hip_status(e);
+  }
   e = launch_gemm_fwd(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, X, M, ls, B, r, Y, nf4_tables(), stream);
   return hip_status(e);
 }
@@ -345,7 +371,15 @@ int qlora_linear_bwd(const qlora_nf4dq_t* Wq, const uint16_t* X, const uint16_t*
   if ((e = launch_rowdot(dY, bt, M, r, N, rg.ksplit, rg.kps, part, stream)) != hipSuccess) return QLORA_ERR_HIP;
   if ((e = launch_rowdot_finish(part, rg.ksplit, M, r, s, lg, g, stream)) != hipSuccess) return QLORA_ERR_HIP;
   // dX = dY w_hat + (s G) A
-  if (dX) {
+  if (dX && M >= kNtMinM) {
+    uint16_t* wcopy = reinterpret_cast<uint16_t*>(base + L.wcopy);
+    if ((e = launch_dequant_t(reinterpret_cast<const uint32_t*>(Wq->codes), Wq->code8, Wq->c2s, Wq->mu, N, K, wcopy,
+                              nf4_tables(), stream)) != hipSuccess)
+      return QLORA_ERR_HIP;
+    // dX = dY w_hat + (s G) A: A = w_hat^T [K, N], Wl = A^T, element (k, j) at j*K + k
+    if ((e = launch_gemm_nt(wcopy, K, dY, M, N, A, 1, K, lg, r, dX, QLORA_K_GEMM_DX, stream)) != hipSuccess)
+      return QLORA_ERR_HIP;
+  } else if (dX) {
     if ((e = launch_gemm_dx(reinterpret_cast<const uint32_t*>(Wq->codes), Wq->code8, Wq->c2s, Wq->mu, N, K, dY, M, lg,
                             A, r, dX, nf4_tables(), stream)) != hipSuccess)
       return QLORA_ERR_HIP;

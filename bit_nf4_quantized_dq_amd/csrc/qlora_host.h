@@ -32,6 +32,11 @@ hipError_t launch_dequant(const uint32_t* codes, const uint8_t* code8, const flo
                           const float* mu, uint16_t* out, int64_t n_words, const Nf4Tables& T,
                           hipStream_t s);
 
+// w_hat^T [K, N] BF16 (transposed decode; the dX operand).
+hipError_t launch_dequant_t(const uint32_t* codes, const uint8_t* code8, const float* c2s,
+                            const float* mu, int64_t N, int64_t K, uint16_t* out, const Nf4Tables& T,
+                            hipStream_t s);
+
 // ---- LoRA skinny kernels (lora.hip)
 // part[ks][m][j] = sum over k in split ks of P[m,k] * Q[j,k]; P [M,Kd], Q [R,Kd] BF16.
 hipError_t launch_rowdot(const uint16_t* P, const uint16_t* Q, int64_t M, int32_t R, int64_t Kd,
@@ -70,5 +75,11 @@ hipError_t launch_gemm_dx(const uint32_t* codes, const uint8_t* code8, const flo
                           const float* mu, int64_t N, int64_t K, const uint16_t* dY, int64_t M,
                           const uint16_t* Lg, const uint16_t* A, int32_t r, uint16_t* dX,
                           const Nf4Tables& T, hipStream_t st);
+
+// ---- BF16 GEMM over a decoded weight copy (gemm_nt.hip):
+// C [M, F] = (A [F, Kr] B [M, Kr]^T)^T + L [M, r] Wl^T, Wl(f, j) at f*wl_fs + j*wl_js.
+hipError_t launch_gemm_nt(const uint16_t* A, int64_t F, const uint16_t* B, int64_t M, int64_t Kr,
+                          const uint16_t* wl, int64_t wl_fs, int64_t wl_js, const uint16_t* L, int32_t r,
+                          uint16_t* C, int kernel_id, hipStream_t st);
 
 }  // namespace qlora

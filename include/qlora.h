@@ -155,7 +155,8 @@ enum qlora_kernel_id {
   QLORA_K_GEMM_DX = 5,
   QLORA_K_LORA_DOWN = 6,
   QLORA_K_LORA_GRAD = 7,
-  QLORA_K_COUNT = 8
+  QLORA_K_DEQUANT_T = 8,
+  QLORA_K_COUNT = 9
 };
 int qlora_timing_enable(int on);
 int qlora_timing_read(int kernel_id, double *total_ms, int64_t *launches);

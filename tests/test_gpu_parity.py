@@ -159,6 +159,10 @@ FB_CASES = [
     (9, 1040, 192, 513, 8, 16.0),
     (9, 64, 2048, 100, 128, 256.0),
     (9, 2048, 64, 40, 3, 6.0),
+    # M >= 1024: decoded weight copy + plain BF16 GEMM
+    (9, 272, 320, 1100, 16, 32.0),  # ragged M and N; the dX reduction (over N) ends mid-step
+    (9, 528, 192, 1025, 40, 80.0),  # two adapter slices, r not a multiple of 8
+    (9, 64, 2048, 1024, 128, 256.0),  # four adapter slices, one feature tile
 ]
 
 
@@ -171,7 +175,7 @@ def test_fwd_bwd_parity(gpu_lib, cfg, d_out, d_in, M, r, alpha):
         assert e <= TOL, (k, e)
 
 
-@pytest.mark.parametrize("M", [1, 16, 300])
+@pytest.mark.parametrize("M", [1, 16, 300, 1100])
 def test_lora_path_in_isolation(gpu_lib, M):
     """W = 0: Y = s T B^T and dX = s G A exactly as the adapter branch alone."""
     c = _case(9, 272, 320, M, 16, 0.02)
@@ -182,8 +186,9 @@ def test_lora_path_in_isolation(gpu_lib, M):
         assert normwise(got, ref) <= TOL, k
 
 
-def test_alpha_zero_is_base_only(gpu_lib):
-    c = _case(9, 272, 320, 33, 8, 0.02)
+@pytest.mark.parametrize("M", [33, 1030])
+def test_alpha_zero_is_base_only(gpu_lib, M):
+    c = _case(9, 272, 320, M, 8, 0.02)
     res = _run(c, 0.0, 8, need_dx=True)
     for k in ("Y", "dX"):
         got, ref = res[k]
