@@ -256,8 +256,18 @@ def e4m3_encode(x: torch.Tensor) -> torch.Tensor:
     return out
 
 
-def timing_enable(on: bool) -> None:
-    _check(load_library().qlora_timing_enable(1 if on else 0), "timing_enable")
+def timing_enable(on, kernels=None) -> None:
+    """Per-launch HIP events for the named kernels (all of them when `kernels` is None);
+    on=False turns timing off."""
+    if not on:
+        mask = 0
+    elif kernels is None:
+        mask = (1 << len(KERNEL_IDS)) - 1
+    else:
+        mask = 0
+        for k in kernels:
+            mask |= 1 << KERNEL_IDS[k]
+    _check(load_library().qlora_timing_enable(mask), "timing_enable")
 
 
 def timing_read(kernel: str) -> tuple[float, int]:

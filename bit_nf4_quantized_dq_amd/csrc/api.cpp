@@ -178,7 +178,7 @@ double exact_sum_to_double(const unsigned long long hist[256]) {
 // ---- kernel timing
 struct TimingState {
   std::mutex mu;
-  bool on = false;
+  unsigned mask = 0;  // bit i: kernel id i is timed
   std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[QLORA_K_COUNT];
   size_t used[QLORA_K_COUNT] = {0};
 };
@@ -191,28 +191,23 @@ TimingState& timing() {
 
 namespace qlora {
 
-LaunchTimer::LaunchTimer(int kernel_id, hipStream_t s) : id(kernel_id), stream(s), slot(nullptr) {
+LaunchTimer::LaunchTimer(int kernel_id, hipStream_t) {
   TimingState& T = timing();
   std::lock_guard<std::mutex> lk(T.mu);
-  if (!T.on || id < 0 || id >= QLORA_K_COUNT) return;
-  auto& v = T.ev[id];
-  if (T.used[id] == v.size()) {
+  if (kernel_id < 0 || kernel_id >= QLORA_K_COUNT || !((T.mask >> kernel_id) & 1)) return;
+  auto& v = T.ev[kernel_id];
+  if (T.used[kernel_id] == v.size()) {
     hipEvent_t a, b;
     if (hipEventCreate(&a) != hipSuccess) return;
-    if (hipEventCreate(&b) != hipSuccess) { hipEventDestroy(a); return; }
+    if (hipEventCreate(&b) != hipSuccess) {
+      (void)hipEventDestroy(a);
+      return;
+    }
     v.emplace_back(a, b);
   }
-  const size_t idx = T.used[id]++;
-  hipEventRecord(v[idx].first, stream);
-  slot = reinterpret_cast<void*>(idx + 1);
-}
-
-LaunchTimer::~LaunchTimer() {
-  if (!slot) return;
-  TimingState& T = timing();
-  std::lock_guard<std::mutex> lk(T.mu);
-  const size_t idx = reinterpret_cast<size_t>(slot) - 1;
-  hipEventRecord(T.ev[id][idx].second, stream);
+  const size_t idx = T.used[kernel_id]++;
+  start = v[idx].first;
+  stop = v[idx].second;
 }
 
 }  // namespace qlora
@@ -401,12 +396,12 @@ int qlora_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stre
   return hip_status(launch_e4m3_encode(in, out, n, stream));
 }
 
-int qlora_timing_enable(int on) {
+int qlora_timing_enable(int kernel_mask) {
   TimingState& T = timing();
   std::lock_guard<std::mutex> lk(T.mu);
-  T.on = on != 0;
-  if (T.on)
-    for (auto& u : T.used) u = 0;
+  T.mask = (unsigned)kernel_mask & ((1u << QLORA_K_COUNT) - 1u);
+  for (int i = 0; i < QLORA_K_COUNT; ++i)
+    if ((T.mask >> i) & 1) T.used[i] = 0;
   return QLORA_OK;
 }
 

@@ -92,7 +92,7 @@ hipError_t launch_dequant_t(const uint32_t* codes, const uint8_t* code8, const f
                             hipStream_t s) {
   dim3 grid((unsigned)((K + kTK - 1) / kTK), (unsigned)((N + kTN - 1) / kTN));
   LaunchTimer t(8, s);
-  hipLaunchKernelGGL(k_dequant_t, grid, dim3(kThreads), 0, s, codes, code8, c2s, mu, out, N, K, T);
+  hipExtLaunchKernelGGL(k_dequant_t, grid, dim3(kThreads), 0, s, t.start, t.stop, 0, codes, code8, c2s, mu, out, N, K, T);
   return hipGetLastError();
 }
 
@@ -101,7 +101,7 @@ hipError_t launch_dequant(const uint32_t* codes, const uint8_t* code8, const flo
                           hipStream_t s) {
   const int64_t grid = (n_words + kThreads - 1) / kThreads;
   LaunchTimer t(2, s);
-  hipLaunchKernelGGL(k_dequant, dim3((unsigned)grid), dim3(kThreads), 0, s, codes, code8, c2s, mu,
+  hipExtLaunchKernelGGL(k_dequant, dim3((unsigned)grid), dim3(kThreads), 0, s, t.start, t.stop, 0, codes, code8, c2s, mu,
                      reinterpret_cast<uint4*>(out), n_words, T);
   return hipGetLastError();
 }

@@ -507,7 +507,7 @@ hipError_t launch_gemm_fwd(const uint32_t* codes, const uint8_t* code8, const fl
                            const Nf4Tables& T, hipStream_t st) {
   dim3 grid((unsigned)((N + BF - 1) / BF), (unsigned)((M + BMT - 1) / BMT));
   LaunchTimer t(4, st);
-  hipLaunchKernelGGL(k_gemm_fwd, grid, dim3(kThreads), 0, st, codes, code8, c2s, mu, N, K, X, M,
+  hipExtLaunchKernelGGL(k_gemm_fwd, grid, dim3(kThreads), 0, st, t.start, t.stop, 0, codes, code8, c2s, mu, N, K, X, M,
                      L, B, r, Y, T);
   return hipGetLastError();
 }
@@ -518,7 +518,7 @@ hipError_t launch_gemm_dx(const uint32_t* codes, const uint8_t* code8, const flo
                           const Nf4Tables& T, hipStream_t st) {
   dim3 grid((unsigned)((K + BF - 1) / BF), (unsigned)((M + BMT - 1) / BMT));
   LaunchTimer t(5, st);
-  hipLaunchKernelGGL(k_gemm_dx, grid, dim3(kThreads), 0, st, codes, code8, c2s, mu, N, K, dY, M,
+  hipExtLaunchKernelGGL(k_gemm_dx, grid, dim3(kThreads), 0, st, t.start, t.stop, 0, codes, code8, c2s, mu, N, K, dY, M,
                      Lg, A, r, dX, T);
   return hipGetLastError();
 }

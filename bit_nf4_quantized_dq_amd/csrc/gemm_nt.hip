@@ -288,7 +288,7 @@ hipError_t launch_gemm_nt(const uint16_t* A, int64_t F, const uint16_t* B, int64
                           uint16_t* C, int kernel_id, hipStream_t st) {
   dim3 grid((unsigned)((F + BF - 1) / BF), (unsigned)((M + BMT - 1) / BMT));
   LaunchTimer t(kernel_id, st);
-  hipLaunchKernelGGL(k_gemm_nt, grid, dim3(kThreads), 0, st, A, F, B, M, Kr, wl, wl_fs, wl_js, L, r, C);
+  hipExtLaunchKernelGGL(k_gemm_nt, grid, dim3(kThreads), 0, st, t.start, t.stop, 0, A, F, B, M, Kr, wl, wl_fs, wl_js, L, r, C);
   return hipGetLastError();
 }
 

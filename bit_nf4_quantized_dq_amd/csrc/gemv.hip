@@ -369,10 +369,10 @@ hipError_t launch_gemv_fwd(const uint32_t* codes, const uint8_t* code8, const fl
   a.nbs = (int32_t)((nb_row + a.ksplit - 1) / a.ksplit);
   dim3 grid((unsigned)gemv_groups(N), (unsigned)a.ksplit);
   LaunchTimer t(3, st);
-  if (r <= 16) hipLaunchKernelGGL(k_gemv_fused<1>, grid, dim3(kThreads), 0, st, a, T);
-  else if (r <= 32) hipLaunchKernelGGL(k_gemv_fused<2>, grid, dim3(kThreads), 0, st, a, T);
-  else if (r <= 64) hipLaunchKernelGGL(k_gemv_fused<4>, grid, dim3(kThreads), 0, st, a, T);
-  else hipLaunchKernelGGL(k_gemv_fused<8>, grid, dim3(kThreads), 0, st, a, T);
+  if (r <= 16) hipExtLaunchKernelGGL(k_gemv_fused<1>, grid, dim3(kThreads), 0, st, t.start, t.stop, 0, a, T);
+  else if (r <= 32) hipExtLaunchKernelGGL(k_gemv_fused<2>, grid, dim3(kThreads), 0, st, t.start, t.stop, 0, a, T);
+  else if (r <= 64) hipExtLaunchKernelGGL(k_gemv_fused<4>, grid, dim3(kThreads), 0, st, t.start, t.stop, 0, a, T);
+  else hipExtLaunchKernelGGL(k_gemv_fused<8>, grid, dim3(kThreads), 0, st, t.start, t.stop, 0, a, T);
   return hipGetLastError();
 }
 

@@ -207,7 +207,7 @@ hipError_t launch_rowdot(const uint16_t* P, const uint16_t* Q, int64_t M, int32_
                          int32_t ksplit, int64_t k_per_split, float* part, hipStream_t s) {
   dim3 grid((unsigned)((M + 15) / 16), (unsigned)ksplit, (unsigned)((R + 15) / 16));
   LaunchTimer t(6, s);
-  hipLaunchKernelGGL(k_rowdot, grid, dim3(kThreads), 0, s, P, Q, M, R, Kd, k_per_split, part);
+  hipExtLaunchKernelGGL(k_rowdot, grid, dim3(kThreads), 0, s, t.start, t.stop, 0, P, Q, M, R, Kd, k_per_split, part);
   return hipGetLastError();
 }
 
@@ -223,7 +223,7 @@ hipError_t launch_coldot(const uint16_t* U, const uint16_t* V, int64_t M, int32_
                          int32_t msplit, int64_t m_per_split, float* part, hipStream_t s) {
   dim3 grid((unsigned)((C + 511) / 512), (unsigned)msplit, (unsigned)((R + 15) / 16));
   LaunchTimer t(7, s);
-  hipLaunchKernelGGL(k_coldot, grid, dim3(kThreads), 0, s, U, V, M, R, C, m_per_split, part);
+  hipExtLaunchKernelGGL(k_coldot, grid, dim3(kThreads), 0, s, t.start, t.stop, 0, U, V, M, R, C, m_per_split, part);
   return hipGetLastError();
 }
 

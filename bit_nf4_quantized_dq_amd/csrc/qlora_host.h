@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime_api.h>
+#include <hip/hip_ext.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -13,13 +14,13 @@ namespace qlora {
 void build_nf4_tables(Nf4Tables* t);
 const Nf4Tables& nf4_tables();
 
-// Brackets one kernel launch with hipEvents when timing is enabled (see qlora_timing_*).
+// Start/stop events for one kernel launch when timing is enabled for its id (see
+// qlora_timing_*), else null.  Launch with hipExtLaunchKernelGGL(..., t.start, t.stop, 0,
+// ...): the runtime then stamps the kernel's own execution window into the events.
 struct LaunchTimer {
   LaunchTimer(int kernel_id, hipStream_t s);
-  ~LaunchTimer();
-  int id;
-  hipStream_t stream;
-  void* slot;
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
 };
 
 // ---- quantize / dequantize (quantize.hip, dequant.hip)

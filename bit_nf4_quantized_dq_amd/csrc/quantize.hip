@@ -133,7 +133,7 @@ hipError_t launch_quant_pass1(const float* W, uint32_t* codes, float* c1, unsign
                               int* flag, int64_t n_words, const Nf4Tables& T, hipStream_t s) {
   const int64_t grid = (n_words + kThreads - 1) / kThreads;
   LaunchTimer t(0, s);
-  hipLaunchKernelGGL(k_quant_pass1, dim3((unsigned)grid), dim3(kThreads), 0, s,
+  hipExtLaunchKernelGGL(k_quant_pass1, dim3((unsigned)grid), dim3(kThreads), 0, s, t.start, t.stop, 0,
                      reinterpret_cast<const float4*>(W), codes, c1, hist, flag, n_words, T);
   return hipGetLastError();
 }
@@ -143,7 +143,7 @@ hipError_t launch_quant_pass2(const float* c1, float mu, uint8_t* code8, float* 
   const int64_t n_groups = (n_blocks + kBlock2 - 1) / kBlock2;
   const int64_t grid = (n_groups + 3) / 4;
   LaunchTimer t(1, s);
-  hipLaunchKernelGGL(k_quant_pass2, dim3((unsigned)grid), dim3(kThreads), 0, s, c1, mu, code8, c2s,
+  hipExtLaunchKernelGGL(k_quant_pass2, dim3((unsigned)grid), dim3(kThreads), 0, s, t.start, t.stop, 0, c1, mu, code8, c2s,
                      mu_out, n_blocks);
   return hipGetLastError();
 }

@@ -44,7 +44,8 @@ extern "C" {
 enum qlora_status {
   QLORA_OK = 0,
   QLORA_ERR_INVALID_ARG = -1, /* null pointer, M < 1, r outside [1, 128], alpha not finite */
-  QLORA_ERR_BAD_SHAPE = -2,   /* d_in % 64 != 0, d_out < 1, sizes that overflow */
+  QLORA_ERR_BAD_SHAPE = -2,   /* d_in % 64 != 0, d_out % 16 != 0, d_in or d_out > 2^22,
+                                 d_out * d_in > 2^32 (32-bit buffer offsets) */
   QLORA_ERR_UNSUPPORTED = -3, /* block sizes other than (64, 256) */
   QLORA_ERR_NONFINITE = -4,   /* NaN or Inf in the weights given to qlora_quantize */
   QLORA_ERR_WORKSPACE = -5,   /* workspace pointer null or smaller than required */
@@ -142,23 +143,25 @@ int qlora_linear_bwd(const qlora_nf4dq_t *Wq, const uint16_t *X, const uint16_t 
 int qlora_e4m3_encode(const float *in, uint8_t *out, int64_t n, hipStream_t stream);
 
 /* Diagnostic kernel timing.  While enabled, the library brackets every launch of the
- * kernels below with a pair of hipEvents recorded on the launch stream.
- * qlora_timing_read waits for those events and returns the summed duration (ms) and
- * the launch count of one kernel id since the last reset, then resets that id.
- * Host only; events are created by the library and reused. */
+ * selected kernels below with a pair of hipEvents recorded on the launch stream.
+ * qlora_timing_enable takes a bit mask over the kernel ids (bit i selects id i; 0 turns
+ * timing off); launches of unselected kernels carry no events.  qlora_timing_read waits
+ * for the events of one kernel id and returns their summed duration (ms) and the launch
+ * count since the last read, then resets that id.  Host only; events are created by the
+ * library and reused.  Errors: INVALID_ARG (bad id or null output), HIP. */
 enum qlora_kernel_id {
-  QLORA_K_QUANT_PASS1 = 0,
-  QLORA_K_QUANT_PASS2 = 1,
-  QLORA_K_DEQUANT = 2,
-  QLORA_K_GEMV_FWD = 3,
-  QLORA_K_GEMM_FWD = 4,
-  QLORA_K_GEMM_DX = 5,
-  QLORA_K_LORA_DOWN = 6,
-  QLORA_K_LORA_GRAD = 7,
-  QLORA_K_DEQUANT_T = 8,
+  QLORA_K_QUANT_PASS1 = 0, /* quantize: codes, first-level constants, exponent sums */
+  QLORA_K_QUANT_PASS2 = 1, /* quantize: 8-bit constant codes and their scales */
+  QLORA_K_DEQUANT = 2,     /* BF16 w_hat (standalone, and the forward copy for M >= 1024) */
+  QLORA_K_GEMV_FWD = 3,    /* forward, M <= 16 */
+  QLORA_K_GEMM_FWD = 4,    /* forward GEMM, M > 16 */
+  QLORA_K_GEMM_DX = 5,     /* dX GEMM */
+  QLORA_K_LORA_DOWN = 6,   /* T = X A^T and G = dY B */
+  QLORA_K_LORA_GRAD = 7,   /* dA and dB */
+  QLORA_K_DEQUANT_T = 8,   /* BF16 w_hat^T, the dX copy for M >= 1024 */
   QLORA_K_COUNT = 9
 };
-int qlora_timing_enable(int on);
+int qlora_timing_enable(int kernel_mask);
 int qlora_timing_read(int kernel_id, double *total_ms, int64_t *launches);
 
 /* Human-readable text of a status code (static storage). */
