@@ -106,7 +106,7 @@ FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
 }
 
 struct BwdWs {
-  size_t tpart, t, g, lg, bt, cpart, wcopy, total;
+  size_t tpart, t, g, lg, bt, at, cpart, wcopy, total;
 };
 BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   BwdWs w{};
@@ -123,6 +123,8 @@ BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   off = align_up(off + 2 * M * r, 256);
   w.bt = off;
   off = align_up(off + 2 * (size_t)r * N, 256);
+  w.at = off;
+  off = align_up(off + 2 * (size_t)r * K, 256);
   w.cpart = off;
   off = align_up(off + sizeof(float) * std::max<int64_t>((int64_t)ca.msplit * r * K, (int64_t)cb.msplit * r * N), 256);
   if (M >= kNtMinM) {
@@ -371,8 +373,10 @@ int qlora_linear_bwd(const qlora_nf4dq_t* Wq, const uint16_t* X, const uint16_t*
     if ((e = launch_dequant_t(reinterpret_cast<const uint32_t*>(Wq->codes), Wq->code8, Wq->c2s, Wq->mu, N, K, wcopy,
                               nf4_tables(), stream)) != hipSuccess)
       return QLORA_ERR_HIP;
-    // dX = dY w_hat + (s G) A: A = w_hat^T [K, N], Wl = A^T, element (k, j) at j*K + k
-    if ((e = launch_gemm_nt(wcopy, K, dY, M, N, A, 1, K, lg, r, dX, QLORA_K_GEMM_DX, stream)) != hipSuccess)
+    // dX = dY w_hat + (s G) A: A = w_hat^T [K, N], Wl = A^T [K, r] (staged row-contiguous)
+    uint16_t* at = reinterpret_cast<uint16_t*>(base + L.at);
+    if ((e = launch_transpose_bf16(A, r, K, at, stream)) != hipSuccess) return QLORA_ERR_HIP;
+    if ((e = launch_gemm_nt(wcopy, K, dY, M, N, at, r, 1, lg, r, dX, QLORA_K_GEMM_DX, stream)) != hipSuccess)
       return QLORA_ERR_HIP;
   } else if (dX) {
     if ((e = launch_gemm_dx(reinterpret_cast<const uint32_t*>(Wq->codes), Wq->code8, Wq->c2s, Wq->mu, N, K, dY, M, lg,

@@ -14,13 +14,11 @@
 //
 // Tiling: 256 (f) x 256 (m) per workgroup, 8 wavefronts in a 2 x 4 grid of 128 x 64
 // wavefront tiles (4 x 2 MFMA 32x32x16 tiles, 128 FP32 accumulators per lane), reduction
-// step 32.  Both operand tiles stream through four-slot LDS rings filled by direct
-// buffer->LDS loads issued three steps ahead; each step is: read the first half of the
-// step's operands, issue the loads of step kb+3, run the deferred second-half MFMAs of step
-// kb-1, read the second half, run the first-half MFMAs, wait for this wavefront's loads of
-// step kb+1, one barrier.  The step loop is
-// unrolled four times so that each ring slot is a distinct LDS array known at compile time,
-// which lets the compiler wait only for the slot an access touches.  Rows are 4 chunks of
+// step 32.  Both operand tiles stream through five-slot LDS rings (all 160 KB of LDS)
+// filled by direct buffer->LDS loads issued three steps ahead, with one barrier per pair of
+// steps (details at nt_step).  The step loop is unrolled ten times so that each ring slot
+// is a distinct LDS array known at compile time, which lets the compiler wait only for the
+// slot an access touches.  Rows are 4 chunks of
 // 16 bytes, XOR-swizzled by (row >> 2) & 3: the LDS serves 16 lanes x 16 bytes per clock
 // from 64 banks, and the 16 rows x one chunk of an MFMA operand read then cover all 256
 // bytes exactly once; the ring writes (1 KB contiguous per load) are conflict-free anyway.  Out-of-range rows or
@@ -42,15 +40,16 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef f32x16_t Acc[TI][TJ];
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Two rings of four 16 KB slots (128 KB).
-__shared__ uint4 s_a0[kSlot], s_a1[kSlot], s_a2[kSlot], s_a3[kSlot];
-__shared__ uint4 s_b0[kSlot], s_b1[kSlot], s_b2[kSlot], s_b3[kSlot];
+// Two rings of five 16 KB slots (160 KB, all of a CU's LDS).
+constexpr int kRing = 5;
+__shared__ uint4 s_a0[kSlot], s_a1[kSlot], s_a2[kSlot], s_a3[kSlot], s_a4[kSlot];
+__shared__ uint4 s_b0[kSlot], s_b1[kSlot], s_b2[kSlot], s_b3[kSlot], s_b4[kSlot];
 
 template <int I> __device__ __forceinline__ uint4* abuf() {
-  return I == 0 ? s_a0 : (I == 1 ? s_a1 : (I == 2 ? s_a2 : s_a3));
+  return I == 0 ? s_a0 : (I == 1 ? s_a1 : (I == 2 ? s_a2 : (I == 3 ? s_a3 : s_a4)));
 }
 template <int I> __device__ __forceinline__ uint4* bbuf() {
-  return I == 0 ? s_b0 : (I == 1 ? s_b1 : (I == 2 ? s_b2 : s_b3));
+  return I == 0 ? s_b0 : (I == 1 ? s_b1 : (I == 2 ? s_b2 : (I == 3 ? s_b3 : s_b4)));
 }
 
 __device__ __forceinline__ f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
@@ -96,13 +95,14 @@ struct Ring {
       base[j] = row < rows ? (uint32_t)(row * Kr_ * 2 + 16 * lc) : kOOB;
     }
   }
-  __device__ __forceinline__ void issue(uint4* slot, uint32_t kb) const {
+  __device__ __forceinline__ void issue1(uint4* slot, uint32_t kb, int j) const {
     const uint32_t k0 = kb * BK;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t off = (base[j] != kOOB && k0 + col[j] < Kr) ? base[j] + 2 * k0 : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(slot + (2 * wave + j) * 64), 16, off, 0, 0, 0);
-    }
+    const uint32_t off = (base[j] != kOOB && k0 + col[j] < Kr) ? base[j] + 2 * k0 : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(slot + (2 * wave + j) * 64), 16, off, 0, 0, 0);
+  }
+  __device__ __forceinline__ void issue(uint4* slot, uint32_t kb) const {
+    issue1(slot, kb, 0);
+    issue1(slot, kb, 1);
   }
 };
 
@@ -124,6 +124,13 @@ __device__ __forceinline__ void mma(const Ops& o, Acc& acc) {
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = mfma32(o.a[i], o.b[j], acc[i][j]);
 }
+// Half of mma(): tiles i = 2h, 2h + 1 (4 MFMAs).
+__device__ __forceinline__ void mma_half(const Ops& o, int h, Acc& acc) {
+#pragma unroll
+  for (int i = 2 * h; i < 2 * h + 2; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = mfma32(o.a[i], o.b[j], acc[i][j]);
+}
 __device__ __forceinline__ void mma_step(const uint4* __restrict__ sa, const uint4* __restrict__ sb, int wf,
                                          int wmt, int l32, int h32, Acc& acc) {
   Ops o0, o1;
@@ -133,9 +140,11 @@ __device__ __forceinline__ void mma_step(const uint4* __restrict__ sa, const uin
   mma(o1, acc);
 }
 
-// Adapter slices of 32: acc[f][m] += sum_j Wl(f, j) * L[m][j], Wl(f, j) at f*wl_fs + j*wl_js
-// (elements), L [M, r] row-major; element loads (any r, any stride), staged through slot 3.
-// Threads 0-255 load feature row f0 + t, threads 256-511 token row m0 + t - 256.
+// Adapter slices of 32: acc[f][m] += sum_j Wl(f, j) * L[m][j] for j < r, Wl(f, j) at
+// f*wl_fs + j*wl_js (elements), L [M, r] row-major, staged through slot 4.  Threads 0-255
+// load feature row f0 + t, threads 256-511 token row m0 + t - 256.  When both are
+// row-contiguous with r % 8 == 0 a thread moves whole 16-byte chunks; otherwise element by
+// element (any r, any stride).
 __device__ __forceinline__ void adapter(const uint16_t* __restrict__ wl, int64_t wl_fs, int64_t wl_js, int64_t F,
                                         const uint16_t* __restrict__ Lm, int64_t M, int32_t r, int64_t f0, int64_t m0,
                                         int tid, int wf, int wmt, int l32, int h32, Acc& acc) {
@@ -143,54 +152,92 @@ __device__ __forceinline__ void adapter(const uint16_t* __restrict__ wl, int64_t
   const int row = wside ? tid : tid - 256;
   const rsrc_t rw = make_rsrc(wl, (F - 1) * wl_fs * 2 + (int64_t)r * wl_js * 2);
   const rsrc_t rm = make_rsrc(Lm, M * (int64_t)r * 2);
+  const bool vec = wl_js == 1 && wl_fs == r && (r & 7) == 0;
+  const int64_t f = f0 + row, m = m0 + row;
+  const bool rok = wside ? f < F : m < M;
+  const rsrc_t rr = wside ? rw : rm;
+  const int64_t rowoff = (wside ? f : m) * (int64_t)r;  // vec: both sides are [rows, r]
   for (int32_t j0 = 0; j0 < r; j0 += BK) {
-    uint32_t e[BK];
-    if (wside) {
-      const int64_t f = f0 + row;
+    uint4 c4[kChunks];
+    if (vec) {
 #pragma unroll
-      for (int q = 0; q < BK; ++q) {
-        const bool ok = f < F && j0 + q < r;
-        e[q] = __builtin_amdgcn_raw_buffer_load_b16(rw, ok ? (int)((f * wl_fs + (int64_t)(j0 + q) * wl_js) * 2) : (int)kOOB, 0, 0);
+      for (int c = 0; c < kChunks; ++c) {
+        const bool ok = rok && j0 + 8 * c < r;
+        c4[c] = bload16(rr, ok ? (uint32_t)((rowoff + j0 + 8 * c) * 2) : kOOB);
       }
     } else {
-      const int64_t m = m0 + row;
+      uint32_t e[BK];
+      if (wside) {
 #pragma unroll
-      for (int q = 0; q < BK; ++q) {
-        const bool ok = m < M && j0 + q < r;
-        e[q] = __builtin_amdgcn_raw_buffer_load_b16(rm, ok ? (int)((m * r + j0 + q) * 2) : (int)kOOB, 0, 0);
+        for (int q = 0; q < BK; ++q) {
+          const bool ok = rok && j0 + q < r;
+          e[q] = __builtin_amdgcn_raw_buffer_load_b16(rw, ok ? (int)((f * wl_fs + (int64_t)(j0 + q) * wl_js) * 2) : (int)kOOB, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < BK; ++q) {
+          const bool ok = rok && j0 + q < r;
+          e[q] = __builtin_amdgcn_raw_buffer_load_b16(rm, ok ? (int)((m * r + j0 + q) * 2) : (int)kOOB, 0, 0);
+        }
       }
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c)
+        c4[c] = make_uint4((e[8 * c + 0] & 0xFFFFu) | (e[8 * c + 1] << 16), (e[8 * c + 2] & 0xFFFFu) | (e[8 * c + 3] << 16),
+                           (e[8 * c + 4] & 0xFFFFu) | (e[8 * c + 5] << 16), (e[8 * c + 6] & 0xFFFFu) | (e[8 * c + 7] << 16));
     }
-    uint4* dst = wside ? abuf<3>() : bbuf<3>();
+    uint4* dst = wside ? abuf<4>() : bbuf<4>();
     if (j0 > 0) lds_barrier();  // the previous slice's MFMA reads are done
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c)
-      dst[swz(row, c)] = make_uint4((e[8 * c + 0] & 0xFFFFu) | (e[8 * c + 1] << 16), (e[8 * c + 2] & 0xFFFFu) | (e[8 * c + 3] << 16),
-                                    (e[8 * c + 4] & 0xFFFFu) | (e[8 * c + 5] << 16), (e[8 * c + 6] & 0xFFFFu) | (e[8 * c + 7] << 16));
+    for (int c = 0; c < kChunks; ++c) dst[swz(row, c)] = c4[c];
     lds_barrier();
-    mma_step(abuf<3>(), bbuf<3>(), wf, wmt, l32, h32, acc);
+    mma_step(abuf<4>(), bbuf<4>(), wf, wmt, l32, h32, acc);
   }
 }
 
-// Store C (32x32 layout): register 4q + v of tile (i, j) holds feature
-// f = f0 + 32 i + 8 q + 4 h32 + v of token m = m0 + 32 j + l32; output is [M, F] BF16.
-__device__ __forceinline__ void store_tile(uint16_t* __restrict__ Y, int64_t M, int64_t F, int64_t f0, int64_t m0,
-                                           int l32, int h32, const Acc& acc) {
+// Epilogue.  C is [M, F] BF16 (token-major).  Register 4q + v of tile (i, j) holds feature
+// 32 i + 8 q + 4 h32 + v of token 32 j + l32 within the wavefront's 128 x 64 tile.  The tile
+// is staged in 16 KB of LDS as 64 token rows of 256 bytes (32 units of 8 bytes; unit u of
+// row m at position u ^ (m & 31), so the 8-byte writes of 32 rows hit distinct banks), then
+// read back 16 bytes per lane, 16 lanes per row, so every global store writes contiguous
+// 256-byte row segments.  An odd row swizzle swaps the two 8-byte halves of a 16-byte read.
+__device__ __forceinline__ uint4* epi_region(int wave) {
+  switch (wave) {
+    case 0: return s_a0;
+    case 1: return s_a1;
+    case 2: return s_a2;
+    case 3: return s_a3;
+    case 4: return s_a4;
+    case 5: return s_b0;
+    case 6: return s_b1;
+    default: return s_b2;
+  }
+}
+__device__ __forceinline__ void store_tile(uint16_t* __restrict__ C, int64_t M, int64_t F, int64_t f0, int64_t m0,
+                                           int wave, int lane, int l32, int h32, const Acc& acc) {
+  uint4* reg = epi_region(wave);
+  uint2* reg2 = reinterpret_cast<uint2*>(reg);
 #pragma unroll
   for (int j = 0; j < TJ; ++j) {
-    const int64_t m = m0 + 32 * j + l32;
-    if (m >= M) continue;
+    const int m = 32 * j + l32;
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t f = f0 + 32 * i + 8 * q + 4 * h32;
-        if (f < F) {
-          const uint32_t lo = pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
-          const uint32_t hi = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-          *reinterpret_cast<uint2*>(Y + m * F + f) = make_uint2(lo, hi);
-        }
+        const int u = 8 * i + 2 * q + h32;
+        reg2[m * 32 + (u ^ (m & 31))] = make_uint2(pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]),
+                                                   pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
       }
-    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // this wavefront's LDS writes are done (it reads only its own region)
+  const int c = lane & 15;
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    const int m = 4 * it + (lane >> 4);
+    const int s = m & 31;
+    uint4 v = reg[m * 16 + (c ^ (s >> 1))];
+    if (s & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+    const int64_t gm = m0 + m, gf = f0 + 8 * c;
+    if (gm < M && gf < F) *reinterpret_cast<uint4*>(C + gm * F + gf) = v;
   }
 }
 
@@ -204,27 +251,47 @@ __device__ __forceinline__ void tile_xy(int64_t& tx, int64_t& ty) {
   ty = L / gx;
 }
 
-// Ring step kb (slot S), entered right after the barrier that published it.  The second
-// half (ks = 1) of the previous step's MFMAs was deferred: its operands are in `o1`, so
-// those MFMAs run while this step's operand reads are in flight, and the wavefronts never
-// sit on an LDS read directly after a barrier.
-template <int S>
+// Ring step kb in slot S = kb % 5.  Steps run in pairs (2t, 2t+1) between barriers: the
+// barrier after step 2t+1 publishes the slots of steps 2t+2 and 2t+3 and retires those of
+// steps up to 2t+1, so within a pair the wavefronts of a SIMD may drift apart and fill each
+// other's gaps on the matrix pipe.  Step kb issues the loads of step kb+3 into the slot of
+// step kb-2, which every wavefront finished reading before the last barrier.
+//
+// The second half (ks = 1) of the previous step's MFMAs is deferred: its operands are in
+// `o1`, so those MFMAs run while this step's operand reads are in flight.  The four ring
+// loads are issued one at a time between groups of four MFMAs: a CU's address unit takes
+// one 1 KB load per ~16 clocks, and a burst at the top of the step would stall every
+// wavefront's (in-order) issue behind it.
+template <int S, bool ODD>
 __device__ __forceinline__ void nt_step(const Ring& ra, const Ring& rb, uint32_t kb, uint32_t nk, int wf, int wmt,
                                         int l32, int h32, Ops& o1, Acc& acc) {
+  const bool ld = kb + 3 < nk;
+  uint4* const na = abuf<(S + 3) % kRing>();
+  uint4* const nb = bbuf<(S + 3) % kRing>();
   Ops o0;
   read_ops(abuf<S>(), bbuf<S>(), 0, wf, wmt, l32, h32, o0);
-  if (kb + 3 < nk) {
-    ra.issue(abuf<(S + 3) % 4>(), kb + 3);
-    rb.issue(bbuf<(S + 3) % 4>(), kb + 3);
-  }
-  mma(o1, acc);  // ks = 1 of step kb - 1
+  mma_half(o1, 0, acc);  // ks = 1 of step kb - 1
+  __builtin_amdgcn_sched_barrier(0);
+  if (ld) ra.issue1(na, kb + 3, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_half(o1, 1, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  if (ld) ra.issue1(na, kb + 3, 1);
+  __builtin_amdgcn_sched_barrier(0);
   read_ops(abuf<S>(), bbuf<S>(), 1, wf, wmt, l32, h32, o1);
-  mma(o0, acc);
-  // this wavefront's loads of step kb+1 are complete (steps kb+2, kb+3 may be pending)
-  if (kb + 3 < nk) wait_vm<8>();
-  else if (kb + 2 < nk) wait_vm<4>();
-  else wait_vm<0>();
-  lds_barrier();
+  mma_half(o0, 0, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  if (ld) rb.issue1(nb, kb + 3, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_half(o0, 1, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  if (ld) rb.issue1(nb, kb + 3, 1);
+  if (ODD) {
+    // this wavefront's loads of steps kb+1 and kb+2 are complete (only kb+3's may be pending)
+    if (ld) wait_vm<4>();
+    else wait_vm<0>();
+    lds_barrier();
+  }
 }
 
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(const uint16_t* __restrict__ A, int64_t F,
@@ -243,7 +310,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(const uint16_t* __restr
   Ring ra, rb;
   ra.init(A, F, f0, Kr, wave, lane);
   rb.init(B, M, m0, Kr, wave, lane);
-  // steps 0..2 in flight while the adapter slices run through slot 3
+  // steps 0..2 in flight while the adapter slices run through slot 4
   ra.issue(abuf<0>(), 0);
   rb.issue(bbuf<0>(), 0);
   if (nk > 1) {
@@ -261,24 +328,37 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(const uint16_t* __restr
     for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16_t{};
   adapter(wl, wl_fs, wl_js, F, Lm, M, r, f0, m0, tid, wf, wmt, l32, h32, acc);
   wait_vm<0>();
-  lds_barrier();  // step 0 landed everywhere; the adapter's reads of slot 3 are done
+  lds_barrier();  // steps 0, 1 landed everywhere; the adapter's reads of slot 4 are done
 
   Ops o1;  // deferred second half of the previous step: none before step 0
 #pragma unroll
   for (int i = 0; i < TI; ++i) o1.a[i] = bf16x8_t{};
 #pragma unroll
   for (int j = 0; j < TJ; ++j) o1.b[j] = bf16x8_t{};
-  for (uint32_t kb = 0; kb < nk; kb += 4) {
-    nt_step<0>(ra, rb, kb + 0, nk, wf, wmt, l32, h32, o1, acc);
+  for (uint32_t kb = 0; kb < nk; kb += 10) {
+    nt_step<0, false>(ra, rb, kb + 0, nk, wf, wmt, l32, h32, o1, acc);
     if (kb + 1 >= nk) break;
-    nt_step<1>(ra, rb, kb + 1, nk, wf, wmt, l32, h32, o1, acc);
+    nt_step<1, true>(ra, rb, kb + 1, nk, wf, wmt, l32, h32, o1, acc);
     if (kb + 2 >= nk) break;
-    nt_step<2>(ra, rb, kb + 2, nk, wf, wmt, l32, h32, o1, acc);
+    nt_step<2, false>(ra, rb, kb + 2, nk, wf, wmt, l32, h32, o1, acc);
     if (kb + 3 >= nk) break;
-    nt_step<3>(ra, rb, kb + 3, nk, wf, wmt, l32, h32, o1, acc);
+    nt_step<3, true>(ra, rb, kb + 3, nk, wf, wmt, l32, h32, o1, acc);
+    if (kb + 4 >= nk) break;
+    nt_step<4, false>(ra, rb, kb + 4, nk, wf, wmt, l32, h32, o1, acc);
+    if (kb + 5 >= nk) break;
+    nt_step<0, true>(ra, rb, kb + 5, nk, wf, wmt, l32, h32, o1, acc);
+    if (kb + 6 >= nk) break;
+    nt_step<1, false>(ra, rb, kb + 6, nk, wf, wmt, l32, h32, o1, acc);
+    if (kb + 7 >= nk) break;
+    nt_step<2, true>(ra, rb, kb + 7, nk, wf, wmt, l32, h32, o1, acc);
+    if (kb + 8 >= nk) break;
+    nt_step<3, false>(ra, rb, kb + 8, nk, wf, wmt, l32, h32, o1, acc);
+    if (kb + 9 >= nk) break;
+    nt_step<4, true>(ra, rb, kb + 9, nk, wf, wmt, l32, h32, o1, acc);
   }
   mma(o1, acc);  // ks = 1 of the last step
-  store_tile(C, M, F, f0 + wf, m0 + wmt, l32, h32, acc);
+  lds_barrier();  // every wavefront is done with the ring slots, which now stage the epilogue
+  store_tile(C, M, F, f0 + wf, m0 + wmt, wave, lane, l32, h32, acc);
 }
 
 }  // namespace
