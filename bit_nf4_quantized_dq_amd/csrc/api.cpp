@@ -46,31 +46,6 @@ int check_lora(int64_t M, int32_t r, float alpha) {
   return QLORA_OK;
 }
 
-// ---- launch shapes of the skinny LoRA kernels
-struct RowdotShape {
-  int32_t ksplit;
-  int64_t kps;
-};
-RowdotShape rowdot_shape(int64_t M, int64_t Kd) {
-  const int64_t gm = (M + 15) / 16;
-  int64_t ks = std::max<int64_t>(1, std::min<int64_t>((512 + gm - 1) / gm, Kd / 128));
-  int64_t kps = align_up((size_t)((Kd + ks - 1) / ks), 128);
-  ks = (Kd + kps - 1) / kps;
-  return {(int32_t)ks, kps};
-}
-
-struct ColdotShape {
-  int32_t msplit;
-  int64_t mps;
-};
-ColdotShape coldot_shape(int64_t M, int32_t R, int64_t C) {
-  const int64_t gc = ((C + 511) / 512) * ((R + 15) / 16);
-  int64_t ms = std::max<int64_t>(1, std::min<int64_t>((512 + gc - 1) / gc, (M + 63) / 64));
-  const int64_t mps = (M + ms - 1) / ms;
-  ms = (M + mps - 1) / mps;
-  return {(int32_t)ms, mps};
-}
-
 constexpr int64_t kGemvMaxM = 16;
 // From this many tokens on, the weight is decoded once into a BF16 copy in the workspace
 // and multiplied by the plain BF16 GEMM; below it the fused kernels decode per tile.
@@ -91,8 +66,6 @@ FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
     off = align_up(off + sizeof(float) * ks * M * N, 256);
     w.ls = off;
   } else {
-    const RowdotShape rs = rowdot_shape(M, K);
-    off = align_up(off + sizeof(float) * rs.ksplit * M * r, 256);
     w.ypart = off;
     w.ls = off;
     off = align_up(off + 2 * M * r, 256);
@@ -106,27 +79,22 @@ FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
 }
 
 struct BwdWs {
-  size_t tpart, t, g, lg, bt, at, cpart, wcopy, total;
+  size_t t, g, lg, at, cpart, wcopy, total;
 };
 BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   BwdWs w{};
-  const RowdotShape rt = rowdot_shape(M, K), rg = rowdot_shape(M, N);
-  const ColdotShape ca = coldot_shape(M, r, K), cb = coldot_shape(M, r, N);
   size_t off = 0;
-  w.tpart = off;
-  off = align_up(off + sizeof(float) * std::max<int64_t>(rt.ksplit, rg.ksplit) * M * r, 256);
   w.t = off;
   off = align_up(off + 2 * M * r, 256);
   w.g = off;
   off = align_up(off + 2 * M * r, 256);
   w.lg = off;
   off = align_up(off + 2 * M * r, 256);
-  w.bt = off;
-  off = align_up(off + 2 * (size_t)r * N, 256);
   w.at = off;
   off = align_up(off + 2 * (size_t)r * K, 256);
   w.cpart = off;
-  off = align_up(off + sizeof(float) * std::max<int64_t>((int64_t)ca.msplit * r * K, (int64_t)cb.msplit * r * N), 256);
+  const int64_t ca = (int64_t)lora_grad_msplit(M, K) * r * K, cb = (int64_t)lora_grad_msplit(M, N) * r * N;
+  off = align_up(off + sizeof(float) * std::max<int64_t>(ca, cb), 256);
   if (M >= kNtMinM) {
     w.wcopy = off;
     off = align_up(off + 2 * (size_t)N * K, 256);
@@ -317,11 +285,9 @@ int qlora_linear_fwd(const qlora_nf4dq_t* Wq, const uint16_t* X, int64_t M, cons
     return hip_status(launch_gemv_fwd(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, X, M, A, B, r, s, Y, T_save, ypart,
                                       tpart, nf4_tables(), stream));
   }
-  const RowdotShape rs = rowdot_shape(M, K);
-  hipError_t e = launch_rowdot(X, A, M, r, K, rs.ksplit, rs.kps, tpart, stream);
-  if (e != hipSuccess) return QLORA_ERR_HIP;
+  // T = X A^T: s T (BF16) feeds the adapter slices of the GEMM; T itself is saved if asked
   uint16_t* ls = reinterpret_cast<uint16_t*>(base + L.ls);
-  e = launch_rowdot_finish(tpart, rs.ksplit, M, r, s, ls, T_save, stream);
+  hipError_t e = launch_lora_down(X, A, 0, M, r, K, s, ls, T_save, stream);
   if (e != hipSuccess) return QLORA_ERR_HIP;
   if (M >= kNtMinM) {
     uint16_t* wcopy = reinterpret_cast<uint16_t*>(base + L.wcopy);
@@ -348,25 +314,18 @@ int qlora_linear_bwd(const qlora_nf4dq_t* Wq, const uint16_t* X, const uint16_t*
   if (!ws || ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
   char* base = static_cast<char*>(ws);
   const float s = alpha / (float)r;
-  float* part = reinterpret_cast<float*>(base + L.tpart);
   uint16_t* t = reinterpret_cast<uint16_t*>(base + L.t);
   uint16_t* g = reinterpret_cast<uint16_t*>(base + L.g);
   uint16_t* lg = reinterpret_cast<uint16_t*>(base + L.lg);
-  uint16_t* bt = reinterpret_cast<uint16_t*>(base + L.bt);
   float* cpart = reinterpret_cast<float*>(base + L.cpart);
   hipError_t e;
   const uint16_t* T = T_saved;
   if (!T) {  // recompute T = X A^T
-    const RowdotShape rt = rowdot_shape(M, K);
-    if ((e = launch_rowdot(X, A, M, r, K, rt.ksplit, rt.kps, part, stream)) != hipSuccess) return QLORA_ERR_HIP;
-    if ((e = launch_rowdot_finish(part, rt.ksplit, M, r, 1.0f, t, nullptr, stream)) != hipSuccess) return QLORA_ERR_HIP;
+    if ((e = launch_lora_down(X, A, 0, M, r, K, 1.0f, t, nullptr, stream)) != hipSuccess) return QLORA_ERR_HIP;
     T = t;
   }
-  // G = dY B  (B^T staged so the reduction index is contiguous)
-  if ((e = launch_transpose_bf16(B, N, r, bt, stream)) != hipSuccess) return QLORA_ERR_HIP;
-  const RowdotShape rg = rowdot_shape(M, N);
-  if ((e = launch_rowdot(dY, bt, M, r, N, rg.ksplit, rg.kps, part, stream)) != hipSuccess) return QLORA_ERR_HIP;
-  if ((e = launch_rowdot_finish(part, rg.ksplit, M, r, s, lg, g, stream)) != hipSuccess) return QLORA_ERR_HIP;
+  // G = dY B (B [N, r] is read as the transposed operand); s G and G in BF16
+  if ((e = launch_lora_down(dY, B, 1, M, r, N, s, lg, g, stream)) != hipSuccess) return QLORA_ERR_HIP;
   // dX = dY w_hat + (s G) A
   if (dX && M >= kNtMinM) {
     uint16_t* wcopy = reinterpret_cast<uint16_t*>(base + L.wcopy);
@@ -383,14 +342,9 @@ int qlora_linear_bwd(const qlora_nf4dq_t* Wq, const uint16_t* X, const uint16_t*
                             A, r, dX, nf4_tables(), stream)) != hipSuccess)
       return QLORA_ERR_HIP;
   }
-  // dA = s G^T X
-  const ColdotShape ca = coldot_shape(M, r, K);
-  if ((e = launch_coldot(g, X, M, r, K, ca.msplit, ca.mps, cpart, stream)) != hipSuccess) return QLORA_ERR_HIP;
-  if ((e = launch_coldot_finish(cpart, ca.msplit, r, K, s, 0, dA, stream)) != hipSuccess) return QLORA_ERR_HIP;
-  // dB = s dY^T T
-  const ColdotShape cb = coldot_shape(M, r, N);
-  if ((e = launch_coldot(T, dY, M, r, N, cb.msplit, cb.mps, cpart, stream)) != hipSuccess) return QLORA_ERR_HIP;
-  if ((e = launch_coldot_finish(cpart, cb.msplit, r, N, s, 1, dB, stream)) != hipSuccess) return QLORA_ERR_HIP;
+  // dA = s G^T X [r, K]; dB = s dY^T T, stored [N, r]
+  if ((e = launch_lora_grad(g, X, M, r, K, s, 0, cpart, dA, stream)) != hipSuccess) return QLORA_ERR_HIP;
+  if ((e = launch_lora_grad(T, dY, M, r, N, s, 1, cpart, dB, stream)) != hipSuccess) return QLORA_ERR_HIP;
   return QLORA_OK;
 }
 

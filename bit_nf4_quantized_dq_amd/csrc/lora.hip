@@ -3,190 +3,294 @@
 // "Where the gradients actually go": only A and B receive gradients.  "QLoRA: Quantize
 // Base Weights to 4-Bit", Section 3: the branch is scaled by alpha/r.
 //
-// rowdot : part[ks][m][j] = sum_{k in split ks} P[m,k] Q[j,k]    (T = X A^T, G = dY B)
-//          MFMA 16x16x32 BF16; Q rows are the MFMA A operand, P rows the B operand.
-// coldot : part[ms][j][c] = sum_{m in split ms} U[m,j] V[m,c]    (dA = G^T X, dB^T = T^T dY)
-//          FP32 FMA over columns c (reduction over tokens m, which are strided in V).
-// finish : fixed-order sum of the partials, times the scale, rounded to BF16.
+// down : out[m][j] = sum_k P[m][k] Q(j, k)                    (T = X A^T, G = dY B)
+//        Q is [R, Kd] (A) or [Kd, R] (B).  One workgroup owns 16*MT tokens and all R
+//        outputs over the whole reduction (no partials); 8 wavefronts take interleaved
+//        32-wide slabs and their sums meet in LDS in a fixed order.
+// grad : out(j, c) = scale * sum_m U[m][j] V[m][c]            (dA = s G^T X, dB = s dY^T T)
+//        One workgroup owns 64 columns c and a slice of the tokens; the slices' FP32 sums
+//        are combined in a fixed order by the last workgroup of the column tile to finish.
+//
+// Both use MFMA 16x16x32 BF16.  Operands whose reduction index is strided in memory (Q as
+// [Kd, R], U and V) are staged in LDS row-major and read with ds_read_b64_tr_b16: within
+// each 16-lane group, lane i receives element (i % 4) of the 8 bytes addressed by lanes
+// i/4, i/4 + 4, i/4 + 8, i/4 + 12.  If lane j addresses row k0 + j/4, columns 4 (j % 4) .. +3
+// of a tile with 16 columns, lane i therefore receives rows k0 .. k0+3 of column i, and two
+// such reads give the 8 consecutive reduction indices of an MFMA operand.
 #include "qlora_device.h"
 #include "qlora_host.h"
 
 namespace qlora {
+
+__device__ unsigned int g_lora_counters[65536];
+
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kSumU = 16;  // partials loaded together before they are added
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-// Fixed-order sum of n partials p[0], p[stride], ...; loads of kSumU partials are issued
-// before their adds so the sum costs a few memory latencies, not n.
-__device__ __forceinline__ float sum_partials(const float* __restrict__ p, int32_t n, int64_t stride) {
-  float s = 0.f;
-  for (int32_t k0 = 0; k0 < n; k0 += kSumU) {
-    float v[kSumU];
-#pragma unroll
-    for (int u = 0; u < kSumU; ++u) v[u] = (k0 + u < n) ? p[(int64_t)(k0 + u) * stride] : 0.f;
-#pragma unroll
-    for (int u = 0; u < kSumU; ++u) s += v[u];
-  }
-  return s;
+constexpr int kSumU = 16;                 // partials loaded together before they are added
+constexpr uint32_t kCounterPeriod = 65536;
+
+// 8 consecutive rows k0 + 8 (lane >> 4) .. +7 of column (lane & 15) of an LDS tile with 16
+// columns and a row pitch of `pitch` bytes (rows k0 .. k0 + 31).
+__device__ __forceinline__ bf16x8_t tr_operand(const char* tile, int pitch, int lane) {
+  const int j = lane & 15, g = lane >> 4;
+  const char* p0 = tile + (8 * g + (j >> 2)) * pitch + 8 * (j & 3);
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0 + 4 * pitch));
+  bf16x8_t r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
 }
 
-__device__ __forceinline__ uint4 ld16_or_zero(const uint16_t* p, bool ok) {
-  return ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
-}
+__device__ __forceinline__ uint16_t to_bf16(float v) { return (uint16_t)(pack_bf16x2(v, 0.f) & 0xFFFFu); }
 
-// grid (ceil(M/16), ksplit, ceil(R/16)); 4 wavefronts split the WG's k-range in steps of 32.
-__global__ __launch_bounds__(kThreads) void k_rowdot(const uint16_t* __restrict__ P,
-                                                     const uint16_t* __restrict__ Q, int64_t M,
-                                                     int32_t R, int64_t Kd, int64_t kps,
-                                                     float* __restrict__ part) {
-  __shared__ f32x4_t red[4][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t m0 = (int64_t)blockIdx.x * 16;
-  const int32_t j0 = blockIdx.z * 16;
-  const int64_t kbeg = (int64_t)blockIdx.y * kps;
-  const int64_t kend = (kbeg + kps < Kd) ? kbeg + kps : Kd;
-  const int64_t mrow = m0 + (lane & 15);
-  const int32_t jrow = j0 + (lane & 15);
-  const int kk = 8 * (lane >> 4);
-  const bool mok = mrow < M, jok = jrow < R;
-  const uint16_t* pp = P + (mok ? mrow : 0) * Kd + kk;
-  const uint16_t* qp = Q + (int64_t)(jok ? jrow : 0) * Kd + kk;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  int64_t k = kbeg + 32 * wave;
-  for (; k + 3 * 128 < kend; k += 4 * 128) {
-    uint4 pv[4], qv[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const bool ok = k + 128 * u + kk < kend;
-      pv[u] = ld16_or_zero(pp + k + 128 * u, mok && ok);
-      qv[u] = ld16_or_zero(qp + k + 128 * u, jok && ok);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) acc = mfma16x16x32(as_bf16x8(qv[u]), as_bf16x8(pv[u]), acc);
-  }
-  for (; k < kend; k += 128) {
-    const bool ok = k + kk < kend;
-    const uint4 pv = ld16_or_zero(pp + k, mok && ok);
-    const uint4 qv = ld16_or_zero(qp + k, jok && ok);
-    acc = mfma16x16x32(as_bf16x8(qv), as_bf16x8(pv), acc);
-  }
-  red[wave][lane] = acc;
-  __syncthreads();
-  if (wave == 0) {
-    f32x4_t s = red[0][lane];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) {
-      const f32x4_t t = red[w][lane];
-      s[0] += t[0]; s[1] += t[1]; s[2] += t[2]; s[3] += t[3];
-    }
-    // D[j][m]: lane holds rows j = 4*(lane>>4) + v, column m = lane & 15
-    const int64_t m = m0 + (lane & 15);
-    if (m < M) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int32_t j = j0 + 4 * (lane >> 4) + v;
-        if (j < R) part[((int64_t)blockIdx.y * M + m) * R + j] = s[v];
-      }
-    }
-  }
-}
+// ---------------------------------------------------------------- down-projection
+constexpr int kDownThreads = 512;
+constexpr int kDownWaves = kDownThreads / 64;
 
-__global__ __launch_bounds__(kThreads) void k_rowdot_finish(const float* __restrict__ part,
-                                                            int32_t ksplit, int64_t M, int32_t R,
-                                                            float scale, uint16_t* __restrict__ out_s,
+// grid: ceil(M / (16 MT)).  JT = ceil(R / 16) tiles of outputs, all held by every wavefront.
+template <int JT, int MT, bool QT>
+__global__ __launch_bounds__(kDownThreads) void k_lora_down(const uint16_t* __restrict__ P,
+                                                            const uint16_t* __restrict__ Q, int64_t M,
+                                                            int32_t R, int64_t Kd, float scale,
+                                                            uint16_t* __restrict__ out_s,
                                                             uint16_t* __restrict__ out_u) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= M * R) return;
-  const float s = sum_partials(part + i, ksplit, M * R);
-  if (out_s) out_s[i] = (uint16_t)(pack_bf16x2(s * scale, 0.f) & 0xFFFFu);
-  if (out_u) out_u[i] = (uint16_t)(pack_bf16x2(s, 0.f) & 0xFFFFu);
+  // per wavefront: QT staging of one slab (JT tiles of 32 rows x 16 columns); reused below
+  // for the cross-wavefront sums
+  __shared__ __attribute__((aligned(16))) char smem[kDownWaves * JT * MT * 64 * 16 > kDownWaves * JT * 1024
+                                                       ? kDownWaves * JT * MT * 64 * 16
+                                                       : kDownWaves * JT * 1024];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t m0 = (int64_t)blockIdx.x * 16 * MT;
+  const int kk = 8 * (lane >> 4);
+  const rsrc_t rp = make_rsrc(P + m0 * Kd, (M - m0) * Kd * 2);
+  const rsrc_t rq = make_rsrc(Q, (int64_t)R * Kd * 2);
+  f32x4_t acc[JT][MT];
+#pragma unroll
+  for (int t = 0; t < JT; ++t)
+#pragma unroll
+    for (int u = 0; u < MT; ++u) acc[t][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  char* qs = smem + wave * JT * 1024;  // QT: this wavefront's slab, JT tiles of [32][16] BF16
+  const int64_t nslab = (Kd + 31) / 32;
+  for (int64_t s = wave; s < nslab; s += kDownWaves) {
+    const int64_t k = 32 * s + kk;
+    const bool kok = k < Kd;
+    uint4 pv[MT];
+#pragma unroll
+    for (int u = 0; u < MT; ++u) {
+      const int64_t row = 16 * u + (lane & 15);
+      pv[u] = bload16(rp, (kok && m0 + row < M) ? (uint32_t)((row * Kd + k) * 2) : kOOB);
+    }
+    bf16x8_t qa[JT];
+    if (!QT) {
+#pragma unroll
+      for (int t = 0; t < JT; ++t) {
+        const int j = 16 * t + (lane & 15);
+        qa[t] = as_bf16x8(bload16(rq, (kok && j < R) ? (uint32_t)(((int64_t)j * Kd + k) * 2) : kOOB));
+      }
+    } else {
+      // rows k = 32 s + (lane >> 1), columns 8 (lane & 1) .. +7 of every tile
+      const int64_t kr = 32 * s + (lane >> 1);
+#pragma unroll
+      for (int t = 0; t < JT; ++t) {
+        const int j = 16 * t + 8 * (lane & 1);
+        uint4 v;
+        if ((R & 7) == 0) {  // 16-byte rows pieces
+          v = bload16(rq, (kr < Kd && j < R) ? (uint32_t)((kr * R + j) * 2) : kOOB);
+        } else {
+          uint32_t e[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            e[q] = __builtin_amdgcn_raw_buffer_load_b16(rq, (kr < Kd && j + q < R) ? (int)((kr * R + j + q) * 2) : (int)kOOB, 0, 0);
+          v = make_uint4((e[0] & 0xFFFFu) | (e[1] << 16), (e[2] & 0xFFFFu) | (e[3] << 16), (e[4] & 0xFFFFu) | (e[5] << 16),
+                         (e[6] & 0xFFFFu) | (e[7] << 16));
+        }
+        *reinterpret_cast<uint4*>(qs + t * 1024 + (lane >> 1) * 32 + 16 * (lane & 1)) = v;
+      }
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int t = 0; t < JT; ++t) qa[t] = tr_operand(qs + t * 1024, 32, lane);
+      asm volatile("" ::: "memory");
+    }
+#pragma unroll
+    for (int t = 0; t < JT; ++t)
+#pragma unroll
+      for (int u = 0; u < MT; ++u) acc[t][u] = mfma16x16x32(qa[t], as_bf16x8(pv[u]), acc[t][u]);
+  }
+  // fixed-order sum over the wavefronts
+  __syncthreads();
+  f32x4_t* red = reinterpret_cast<f32x4_t*>(smem);
+#pragma unroll
+  for (int t = 0; t < JT; ++t)
+#pragma unroll
+    for (int u = 0; u < MT; ++u) red[((wave * JT + t) * MT + u) * 64 + lane] = acc[t][u];
+  __syncthreads();
+  for (int i = threadIdx.x; i < JT * MT * 64; i += kDownThreads) {
+    const int l = i & 63, u = (i >> 6) % MT, t = (i >> 6) / MT;
+    f32x4_t sum = red[(t * MT + u) * 64 + l];
+    for (int w = 1; w < kDownWaves; ++w) {
+      const f32x4_t v = red[((w * JT + t) * MT + u) * 64 + l];
+      sum[0] += v[0]; sum[1] += v[1]; sum[2] += v[2]; sum[3] += v[3];
+    }
+    // D[j][m]: lane l holds rows j = 4 (l >> 4) + v of column m = l & 15
+    const int64_t m = m0 + 16 * u + (l & 15);
+    if (m >= M) continue;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int j = 16 * t + 4 * (l >> 4) + v;
+      if (j >= R) continue;
+      if (out_s) out_s[m * R + j] = to_bf16(sum[v] * scale);
+      if (out_u) out_u[m * R + j] = to_bf16(sum[v]);
+    }
+  }
 }
 
-// grid (ceil(C/512), msplit, ceil(R/16)); each thread owns two adjacent columns.
-__global__ __launch_bounds__(kThreads) void k_coldot(const uint16_t* __restrict__ U,
-                                                     const uint16_t* __restrict__ V, int64_t M,
-                                                     int32_t R, int64_t C, int64_t mps,
-                                                     float* __restrict__ part) {
-  constexpr int kMC = 128;  // token rows staged per pass
-  __shared__ float su[kMC][16];
-  const int64_t c = (int64_t)blockIdx.x * 512 + 2 * threadIdx.x;
-  const int32_t j0 = blockIdx.z * 16;
+// ---------------------------------------------------------------- gradients of A and B
+constexpr int kGradThreads = 256;
+constexpr int kGradWaves = kGradThreads / 64;
+constexpr int kGradCols = 64;      // columns per workgroup (4 tiles of 16)
+constexpr int kVTile = 32 * 32 + 64;  // bytes per staged [32][16] BF16 tile, padded (bank offset)
+
+// grid (ceil(C / 64), msplit).  JT = ceil(R / 16).  part: [msplit][R][C] FP32 (msplit > 1).
+template <int JT>
+__global__ __launch_bounds__(kGradThreads) void k_lora_grad(const uint16_t* __restrict__ U,
+                                                            const uint16_t* __restrict__ V, int64_t M,
+                                                            int32_t R, int64_t C, int64_t mps, float scale,
+                                                            int transposed, float* __restrict__ part,
+                                                            uint16_t* __restrict__ out) {
+  // per wavefront: 4 V tiles + JT U tiles of [32][16] BF16; reused for the cross-wave sums
+  constexpr int kWaveBytes = (4 + JT) * kVTile;
+  constexpr int kRedBytes = kGradWaves * JT * 4 * 64 * 16;
+  __shared__ __attribute__((aligned(16))) char smem[kGradWaves * kWaveBytes > kRedBytes ? kGradWaves * kWaveBytes : kRedBytes];
+  __shared__ bool s_last;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t c0 = (int64_t)blockIdx.x * kGradCols;
   const int64_t mbeg = (int64_t)blockIdx.y * mps;
   const int64_t mend = (mbeg + mps < M) ? mbeg + mps : M;
-  const bool cok = c < C;
-  float a0[16], a1[16];
+  const rsrc_t rv = make_rsrc(V, M * C * 2);
+  const rsrc_t ru = make_rsrc(U, M * (int64_t)R * 2);
+  char* vt = smem + wave * kWaveBytes;  // 4 V tiles, then JT U tiles
+  char* ut = vt + 4 * kVTile;
+  f32x4_t acc[JT][4];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) a0[j] = a1[j] = 0.f;
-  for (int64_t mc = mbeg; mc < mend; mc += kMC) {
-    const int64_t mlen = (mend - mc < kMC) ? mend - mc : kMC;
-    __syncthreads();
-    for (int t = threadIdx.x; t < kMC * 16; t += kThreads) {
-      const int mm = t >> 4, j = t & 15;
-      float v = 0.f;
-      if (mm < mlen && j0 + j < R) v = bf16lo_to_f32(U[(mc + mm) * R + j0 + j]);
-      su[mm][j] = v;
+  for (int t = 0; t < JT; ++t)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[t][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // wavefront w takes chunks of 32 tokens mbeg + 32 (w + 4 i)
+  for (int64_t mc = mbeg + 32 * wave; mc < mend; mc += 32 * kGradWaves) {
+    // V chunk [32][64]: 4 loads; lane -> row 8 i + (lane >> 3), columns 8 (lane & 7) .. +7
+    uint4 vv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = mc + 8 * i + (lane >> 3);
+      const int64_t c = c0 + 8 * (lane & 7);
+      vv[i] = bload16(rv, (m < mend && c < C) ? (uint32_t)((m * C + c) * 2) : kOOB);
     }
-    __syncthreads();
-    if (cok) {
-      const uint32_t* vp = reinterpret_cast<const uint32_t*>(V + mc * C + c);
-      int64_t mm = 0;
-      for (; mm + 4 <= mlen; mm += 4) {
-        uint32_t w[4];
+    // U chunk [32][16 JT]: element loads (any R)
+    uint32_t uu[JT][8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) w[u] = vp[(mm + u) * (C / 2)];
+    for (int t = 0; t < JT; ++t) {
+      const int64_t m = mc + (lane >> 1);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float v0 = bf16lo_to_f32(w[u]), v1 = bf16hi_to_f32(w[u]);
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const float uu = su[mm + u][j];
-            a0[j] = fmaf(uu, v0, a0[j]);
-            a1[j] = fmaf(uu, v1, a1[j]);
-          }
-        }
+      for (int e = 0; e < 8; ++e) {
+        const int j = 16 * t + 8 * (lane & 1) + e;
+        uu[t][e] = __builtin_amdgcn_raw_buffer_load_b16(ru, (m < mend && j < R) ? (int)((m * R + j) * 2) : (int)kOOB, 0, 0);
       }
-      for (; mm < mlen; ++mm) {
-        const uint32_t w = vp[mm * (C / 2)];
-        const float v0 = bf16lo_to_f32(w), v1 = bf16hi_to_f32(w);
+    }
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          a0[j] = fmaf(su[mm][j], v0, a0[j]);
-          a1[j] = fmaf(su[mm][j], v1, a1[j]);
-        }
+    for (int i = 0; i < 4; ++i) {
+      const int row = 8 * i + (lane >> 3), ct = (lane & 7) >> 1, half = lane & 1;
+      *reinterpret_cast<uint4*>(vt + ct * kVTile + row * 32 + 16 * half) = vv[i];
+    }
+#pragma unroll
+    for (int t = 0; t < JT; ++t) {
+      const uint4 w = make_uint4((uu[t][0] & 0xFFFFu) | (uu[t][1] << 16), (uu[t][2] & 0xFFFFu) | (uu[t][3] << 16),
+                                 (uu[t][4] & 0xFFFFu) | (uu[t][5] << 16), (uu[t][6] & 0xFFFFu) | (uu[t][7] << 16));
+      *reinterpret_cast<uint4*>(ut + t * kVTile + (lane >> 1) * 32 + 16 * (lane & 1)) = w;
+    }
+    asm volatile("" ::: "memory");
+    bf16x8_t a[JT], b[4];
+#pragma unroll
+    for (int t = 0; t < JT; ++t) a[t] = tr_operand(ut + t * kVTile, 32, lane);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) b[q] = tr_operand(vt + q * kVTile, 32, lane);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int t = 0; t < JT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[t][q] = mfma16x16x32(a[t], b[q], acc[t][q]);
+  }
+  // fixed-order sum over the wavefronts: D[j][c], lane l holds j = 4 (l >> 4) + v, c = l & 15
+  __syncthreads();
+  f32x4_t* red = reinterpret_cast<f32x4_t*>(smem);
+#pragma unroll
+  for (int t = 0; t < JT; ++t)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) red[((wave * JT + t) * 4 + q) * 64 + lane] = acc[t][q];
+  __syncthreads();
+  const int32_t msplit = gridDim.y;
+  // one (t, q, lane) item per thread pass: JT * 4 * 64 items
+  for (int i = threadIdx.x; i < JT * 4 * 64; i += kGradThreads) {
+    const int l = i & 63, q = (i >> 6) & 3, t = i >> 8;
+    f32x4_t sum = red[(t * 4 + q) * 64 + l];
+    for (int w = 1; w < kGradWaves; ++w) {
+      const f32x4_t v = red[((w * JT + t) * 4 + q) * 64 + l];
+      sum[0] += v[0]; sum[1] += v[1]; sum[2] += v[2]; sum[3] += v[3];
+    }
+    const int64_t c = c0 + 16 * q + (l & 15);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int j = 16 * t + 4 * (l >> 4) + v;
+      if (j >= R || c >= C) continue;
+      if (msplit == 1) {
+        const uint16_t b16 = to_bf16(sum[v] * scale);
+        if (transposed) out[c * R + j] = b16;
+        else out[(int64_t)j * C + c] = b16;
+      } else {
+        __hip_atomic_store(part + ((int64_t)blockIdx.y * R + j) * C + c, sum[v], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_SYSTEM);
       }
     }
   }
-  if (cok) {
+  if (msplit == 1) return;
+  // every partial store of this workgroup has completed before its counter increment
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned int inc = kCounterPeriod / (unsigned int)msplit;
+    const unsigned int old = __hip_atomic_fetch_add(&g_lora_counters[blockIdx.x], inc, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+    s_last = ((old + inc) % kCounterPeriod) == 0u;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // last workgroup of this column tile: fixed-order sum of the slices
+  const int64_t ncol = (c0 + kGradCols <= C) ? kGradCols : C - c0;
+  for (int64_t i = threadIdx.x; i < (int64_t)R * ncol; i += kGradThreads) {
+    const int32_t j = (int32_t)(i / ncol);
+    const int64_t c = c0 + i % ncol;
+    const float* p = part + (int64_t)j * C + c;
+    float s = 0.f;
+    for (int32_t k0 = 0; k0 < msplit; k0 += kSumU) {
+      float v[kSumU];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (j0 + j < R) {
-        float* dst = part + ((int64_t)blockIdx.y * R + j0 + j) * C + c;
-        *reinterpret_cast<float2*>(dst) = make_float2(a0[j], a1[j]);
-      }
+      for (int u = 0; u < kSumU; ++u)
+        v[u] = (k0 + u < msplit) ? __hip_atomic_load(p + (int64_t)(k0 + u) * R * C, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)
+                                 : 0.f;
+#pragma unroll
+      for (int u = 0; u < kSumU; ++u) s += v[u];
     }
+    const uint16_t b16 = to_bf16(s * scale);
+    if (transposed) out[c * R + j] = b16;
+    else out[(int64_t)j * C + c] = b16;
   }
 }
 
-__global__ __launch_bounds__(kThreads) void k_coldot_finish(const float* __restrict__ part,
-                                                            int32_t msplit, int32_t R, int64_t C,
-                                                            float scale, int transposed,
-                                                            uint16_t* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // i = j*C + c
-  if (i >= (int64_t)R * C) return;
-  const float s = sum_partials(part + i, msplit, (int64_t)R * C);
-  const uint16_t b = (uint16_t)(pack_bf16x2(s * scale, 0.f) & 0xFFFFu);
-  if (!transposed) {
-    out[i] = b;
-  } else {
-    const int64_t j = i / C, c = i % C;
-    out[c * R + j] = b;
-  }
-}
-
-__global__ __launch_bounds__(kThreads) void k_transpose_bf16(const uint16_t* __restrict__ in,
-                                                             int64_t rows, int64_t cols,
-                                                             uint16_t* __restrict__ out) {
+__global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restrict__ in, int64_t rows, int64_t cols,
+                                                        uint16_t* __restrict__ out) {
   __shared__ uint16_t tile[32][33];
   const int64_t r0 = (int64_t)blockIdx.y * 32, c0 = (int64_t)blockIdx.x * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
@@ -201,44 +305,63 @@ __global__ __launch_bounds__(kThreads) void k_transpose_bf16(const uint16_t* __r
   }
 }
 
+template <int JT, int MT, bool QT>
+hipError_t down_launch(const uint16_t* P, const uint16_t* Q, int64_t M, int32_t R, int64_t Kd, float scale,
+                       uint16_t* out_s, uint16_t* out_u, hipStream_t s) {
+  const int64_t grid = (M + 16 * MT - 1) / (16 * MT);
+  LaunchTimer t(6, s);
+  hipExtLaunchKernelGGL((k_lora_down<JT, MT, QT>), dim3((unsigned)grid), dim3(kDownThreads), 0, s, t.start, t.stop, 0,
+                        P, Q, M, R, Kd, scale, out_s, out_u);
+  return hipGetLastError();
+}
+
+template <int JT>
+hipError_t grad_launch(const uint16_t* U, const uint16_t* V, int64_t M, int32_t R, int64_t C, int32_t msplit,
+                       int64_t mps, float scale, int transposed, float* part, uint16_t* out, hipStream_t s) {
+  dim3 grid((unsigned)((C + kGradCols - 1) / kGradCols), (unsigned)msplit);
+  LaunchTimer t(7, s);
+  hipExtLaunchKernelGGL(k_lora_grad<JT>, grid, dim3(kGradThreads), 0, s, t.start, t.stop, 0, U, V, M, R, C, mps, scale,
+                        transposed, part, out);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_rowdot(const uint16_t* P, const uint16_t* Q, int64_t M, int32_t R, int64_t Kd,
-                         int32_t ksplit, int64_t k_per_split, float* part, hipStream_t s) {
-  dim3 grid((unsigned)((M + 15) / 16), (unsigned)ksplit, (unsigned)((R + 15) / 16));
-  LaunchTimer t(6, s);
-  hipExtLaunchKernelGGL(k_rowdot, grid, dim3(kThreads), 0, s, t.start, t.stop, 0, P, Q, M, R, Kd, k_per_split, part);
-  return hipGetLastError();
+hipError_t launch_lora_down(const uint16_t* P, const uint16_t* Q, int q_transposed, int64_t M, int32_t R, int64_t Kd,
+                            float scale, uint16_t* out_s, uint16_t* out_u, hipStream_t s) {
+  // tokens per workgroup grow with R so that Q (re-read by every workgroup) stays amortized
+  if (q_transposed) {
+    if (R <= 16) return down_launch<1, 1, true>(P, Q, M, R, Kd, scale, out_s, out_u, s);
+    if (R <= 32) return down_launch<2, 1, true>(P, Q, M, R, Kd, scale, out_s, out_u, s);
+    if (R <= 64) return down_launch<4, 2, true>(P, Q, M, R, Kd, scale, out_s, out_u, s);
+    return down_launch<8, 2, true>(P, Q, M, R, Kd, scale, out_s, out_u, s);
+  }
+  if (R <= 16) return down_launch<1, 1, false>(P, Q, M, R, Kd, scale, out_s, out_u, s);
+  if (R <= 32) return down_launch<2, 1, false>(P, Q, M, R, Kd, scale, out_s, out_u, s);
+  if (R <= 64) return down_launch<4, 2, false>(P, Q, M, R, Kd, scale, out_s, out_u, s);
+  return down_launch<8, 2, false>(P, Q, M, R, Kd, scale, out_s, out_u, s);
 }
 
-hipError_t launch_rowdot_finish(const float* part, int32_t ksplit, int64_t M, int32_t R, float scale,
-                                uint16_t* out_s, uint16_t* out_u, hipStream_t s) {
-  const int64_t n = M * R;
-  hipLaunchKernelGGL(k_rowdot_finish, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads),
-                     0, s, part, ksplit, M, R, scale, out_s, out_u);
-  return hipGetLastError();
+int32_t lora_grad_msplit(int64_t M, int64_t C) {
+  const int64_t tiles = (C + kGradCols - 1) / kGradCols;
+  int32_t ms = 1;
+  while (tiles * ms < 256 && (int64_t)ms * 2 * 128 <= M && ms < 64) ms *= 2;
+  return ms;
 }
 
-hipError_t launch_coldot(const uint16_t* U, const uint16_t* V, int64_t M, int32_t R, int64_t C,
-                         int32_t msplit, int64_t m_per_split, float* part, hipStream_t s) {
-  dim3 grid((unsigned)((C + 511) / 512), (unsigned)msplit, (unsigned)((R + 15) / 16));
-  LaunchTimer t(7, s);
-  hipExtLaunchKernelGGL(k_coldot, grid, dim3(kThreads), 0, s, t.start, t.stop, 0, U, V, M, R, C, m_per_split, part);
-  return hipGetLastError();
+hipError_t launch_lora_grad(const uint16_t* U, const uint16_t* V, int64_t M, int32_t R, int64_t C, float scale,
+                            int transposed, float* part, uint16_t* out, hipStream_t s) {
+  const int32_t ms = lora_grad_msplit(M, C);
+  const int64_t mps = ((M + ms - 1) / ms + 31) / 32 * 32;
+  if (R <= 16) return grad_launch<1>(U, V, M, R, C, ms, mps, scale, transposed, part, out, s);
+  if (R <= 32) return grad_launch<2>(U, V, M, R, C, ms, mps, scale, transposed, part, out, s);
+  if (R <= 64) return grad_launch<4>(U, V, M, R, C, ms, mps, scale, transposed, part, out, s);
+  return grad_launch<8>(U, V, M, R, C, ms, mps, scale, transposed, part, out, s);
 }
 
-hipError_t launch_coldot_finish(const float* part, int32_t msplit, int32_t R, int64_t C, float scale,
-                                int transposed, uint16_t* out, hipStream_t s) {
-  const int64_t n = (int64_t)R * C;
-  hipLaunchKernelGGL(k_coldot_finish, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads),
-                     0, s, part, msplit, R, C, scale, transposed, out);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out,
-                                 hipStream_t s) {
+hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out, hipStream_t s) {
   dim3 grid((unsigned)((cols + 31) / 32), (unsigned)((rows + 31) / 32));
-  hipLaunchKernelGGL(k_transpose_bf16, grid, dim3(kThreads), 0, s, in, rows, cols, out);
+  hipLaunchKernelGGL(k_transpose_bf16, grid, dim3(256), 0, s, in, rows, cols, out);
   return hipGetLastError();
 }
 

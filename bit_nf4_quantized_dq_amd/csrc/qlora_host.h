@@ -39,19 +39,15 @@ hipError_t launch_dequant_t(const uint32_t* codes, const uint8_t* code8, const f
                             hipStream_t s);
 
 // ---- LoRA skinny kernels (lora.hip)
-// part[ks][m][j] = sum over k in split ks of P[m,k] * Q[j,k]; P [M,Kd], Q [R,Kd] BF16.
-hipError_t launch_rowdot(const uint16_t* P, const uint16_t* Q, int64_t M, int32_t R, int64_t Kd,
-                         int32_t ksplit, int64_t k_per_split, float* part, hipStream_t s);
-// Fixed-order sum of the partials: out_s = bf16(scale * sum), out_u = bf16(sum); BF16 [M,R],
-// either may be null.
-hipError_t launch_rowdot_finish(const float* part, int32_t ksplit, int64_t M, int32_t R, float scale,
-                                uint16_t* out_s, uint16_t* out_u, hipStream_t s);
-// out[j][c] partials over m-splits of U[m,j] * V[m,c]; U BF16 [M,R], V BF16 [M,C].
-hipError_t launch_coldot(const uint16_t* U, const uint16_t* V, int64_t M, int32_t R, int64_t C,
-                         int32_t msplit, int64_t m_per_split, float* part, hipStream_t s);
-// res = scale * sum over splits; transposed == 0: res[j][c] -> out [R, C]; else out [C, R].
-hipError_t launch_coldot_finish(const float* part, int32_t msplit, int32_t R, int64_t C, float scale,
-                                int transposed, uint16_t* out, hipStream_t s);
+// out[m][j] = sum_k P[m][k] Q(j, k) for j < R, Q [R, Kd] (q_transposed = 0) or [Kd, R] (1);
+// out_s = bf16(scale * sum), out_u = bf16(sum), BF16 [M, R], either may be null.
+hipError_t launch_lora_down(const uint16_t* P, const uint16_t* Q, int q_transposed, int64_t M, int32_t R, int64_t Kd,
+                            float scale, uint16_t* out_s, uint16_t* out_u, hipStream_t s);
+// out(j, c) = bf16(scale * sum_m U[m][j] V[m][c]); U [M, R], V [M, C]; out [R, C], or
+// [C, R] when transposed.  part: FP32 [lora_grad_msplit(M, C)][R][C] scratch.
+int32_t lora_grad_msplit(int64_t M, int64_t C);
+hipError_t launch_lora_grad(const uint16_t* U, const uint16_t* V, int64_t M, int32_t R, int64_t C, float scale,
+                            int transposed, float* part, uint16_t* out, hipStream_t s);
 // BF16 transpose [rows, cols] -> [cols, rows].
 hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out,
                                  hipStream_t s);
