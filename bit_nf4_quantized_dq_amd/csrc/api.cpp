@@ -280,7 +280,7 @@ int qlora_linear_fwd(const qlora_nf4dq_t* Wq, const uint16_t* X, int64_t M, cons
   const uint32_t* codes = reinterpret_cast<const uint32_t*>(Wq->codes);
   float* tpart = reinterpret_cast<float*>(base + L.tpart);
   if (M <= kGemvMaxM) {
-    if (N / 256 >= 4096) return QLORA_ERR_BAD_SHAPE;
+    if ((N + 63) / 64 > 65536) return QLORA_ERR_BAD_SHAPE;  // one arrival counter per 64 rows
     float* ypart = reinterpret_cast<float*>(base + L.ypart);
     return hip_status(launch_gemv_fwd(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, X, M, A, B, r, s, Y, T_save, ypart,
                                       tpart, nf4_tables(), stream));

@@ -33,14 +33,16 @@
 
 namespace qlora {
 
-__device__ unsigned int g_gemv_counters[4096];
+__device__ unsigned int g_gemv_counters[65536];
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kTiles = 2;               // column tiles (16 rows) per wavefront
-constexpr int kRows = 4 * 16 * kTiles;  // rows per workgroup
-constexpr int kChunk = 4;               // blocks staged per pass
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int kTiles = 1;               // column tiles (16 rows) per wavefront
+constexpr int kRows = kWaves * 16 * kTiles;  // rows per workgroup
+constexpr int kChunk = 8;               // blocks staged per pass (all loads of a pass in flight at once)
+constexpr int kXItems = 16 * kChunk * 8 / kThreads;  // 16-byte pieces of X staged per thread per pass
 constexpr int kStageBlocks = kChunk * kRows / kThreads;  // blocks of one row staged per thread
 constexpr uint32_t kCounterPeriod = 65536;
 constexpr int kSumU = 16;               // partials loaded together in the split-K sum
@@ -93,13 +95,13 @@ constexpr int kRStage = 32;       // adapter ranks whose B rows are prefetched i
 struct ChunkRegs {
   uint4 cv[kStageBlocks][2];
   uint32_t c8[kStageBlocks], c2[kStageBlocks];
-  uint4 xv[kChunk / 2];
+  uint4 xv[kXItems];
 };
 
 template <int RT>  // 16-wide tiles of the adapter rank: r <= 16 * RT
 __global__ __launch_bounds__(kThreads) void k_gemv_fused(GemvArgs a, Nf4Tables T) {
   __shared__ Stage S;
-  __shared__ f32x4_t sred[4][RT][64];
+  __shared__ f32x4_t sred[kWaves][RT][64];
   __shared__ float sT[16][16 * RT + 1];
   __shared__ unsigned int s_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -135,7 +137,6 @@ __global__ __launch_bounds__(kThreads) void k_gemv_fused(GemvArgs a, Nf4Tables T
   const int srow = tid % kRows, sb0 = (tid / kRows) * kStageBlocks;
   const uint32_t my_code_off = (uint32_t)((row0 + srow) * (K / 2));
   const uint32_t my_blk = (uint32_t)((row0 + srow) * nb_row);
-  const int xm = tid >> 4, xc = tid & 15;
 
   // B rows of this workgroup for the adapter up-projection, prefetched with the first chunk
   __shared__ uint4 sB[kRows][kRStage / 8];
@@ -162,9 +163,10 @@ __global__ __launch_bounds__(kThreads) void k_gemv_fused(GemvArgs a, Nf4Tables T
       R.c2[v] = bload4(r2, ok ? (bi >> 8) * 4 : kOOB);
     }
 #pragma unroll
-    for (int p = 0; p < kChunk / 2; ++p) {  // X[xm][64 (c0 + 2p) + 8 xc .. +8]
-      const int64_t k = 64 * (c0 + 2 * p) + 8 * xc;
-      const bool ok = (c0 + 2 * p + (xc >> 3)) < b1;
+    for (int p = 0; p < kXItems; ++p) {  // item i: X row i / (8 kChunk), 16-byte piece i % (8 kChunk)
+      const int i = tid + kThreads * p, xm = i / (8 * kChunk), col = i % (8 * kChunk);
+      const int64_t k = 64 * (c0 + col / 8) + 8 * (col % 8);
+      const bool ok = c0 + col / 8 < b1;
       R.xv[p] = bload16(rx, ok ? (uint32_t)((xm * K + k) * 2) : kOOB);
     }
   };
@@ -179,7 +181,10 @@ __global__ __launch_bounds__(kThreads) void k_gemv_fused(GemvArgs a, Nf4Tables T
       S.scale[srow][u] = block_scale(R.c8[v], __uint_as_float(R.c2[v]), mu);
     }
 #pragma unroll
-    for (int p = 0; p < kChunk / 2; ++p) S.x[xm][8 * (2 * p + (xc >> 3)) + (xc & 7)] = R.xv[p];
+    for (int p = 0; p < kXItems; ++p) {
+      const int i = tid + kThreads * p;
+      S.x[i / (8 * kChunk)][i % (8 * kChunk)] = R.xv[p];
+    }
   };
 
   ChunkRegs R;
@@ -190,33 +195,61 @@ __global__ __launch_bounds__(kThreads) void k_gemv_fused(GemvArgs a, Nf4Tables T
   }
   for (int64_t c0 = b0; c0 < b1; c0 += kChunk) {
     const int nb = (b1 - c0 < kChunk) ? (int)(b1 - c0) : kChunk;
-    // adapter down-projection inputs of this chunk (this wavefront's share), issued early
-    const int64_t bt = c0 + ((wave - (c0 - b0)) & 3);  // block with ((b - b0) & 3) == wave
-    const bool tshare = bt < c0 + nb;
-    uint4 av[RT][2];
+    // adapter down-projection inputs of this chunk: wavefront w takes blocks u = w (mod kWaves);
+    // for r <= 32 they are issued here, with the chunk, for larger r when the block comes up
+    constexpr int kTA = RT <= 2 ? (kChunk + kWaves - 1) / kWaves : 1;
+    uint4 av[kTA][RT][2];
+    auto load_a = [&](int u, uint4 (&dst)[RT][2]) {
 #pragma unroll
-    for (int j = 0; j < RT; ++j) {
-      const bool ok = tshare && 16 * j + l16 < a.r;
-      const uint32_t ao = (uint32_t)((((int64_t)(16 * j + l16)) * K + 64 * bt + 16 * g) * 2);
-      av[j][0] = bload16(ra, ok ? ao : kOOB);
-      av[j][1] = bload16(ra, ok ? ao + 16 : kOOB);
+      for (int j = 0; j < RT; ++j) {
+        const bool ok = u < nb && 16 * j + l16 < a.r;
+        const uint32_t ao = (uint32_t)((((int64_t)(16 * j + l16)) * K + 64 * (c0 + u) + 16 * g) * 2);
+        dst[j][0] = bload16(ra, ok ? ao : kOOB);
+        dst[j][1] = bload16(ra, ok ? ao + 16 : kOOB);
+      }
+    };
+    if (RT <= 2) {
+#pragma unroll
+      for (int q = 0; q < kTA; ++q) load_a(kWaves * q + wave, av[q]);
     }
     __syncthreads();  // the previous chunk's LDS reads are done
     stage(R);
     __syncthreads();
     if (c0 + kChunk < b1) issue(c0 + kChunk, R);  // next chunk in flight during this one's math
 
-    // ---- MFMA over the staged chunk
-    for (int u = 0; u < nb; ++u) {
-      const bf16x8_t xa = as_bf16x8(S.x[l16][8 * u + 2 * g]);
-      const bf16x8_t xb = as_bf16x8(S.x[l16][8 * u + 2 * g + 1]);
-      if (c0 + u == bt) {
+    // ---- adapter down-projection share of this wavefront: blocks u = wave (mod kWaves)
+    if (RT <= 2) {
 #pragma unroll
-        for (int j = 0; j < RT; ++j) {
-          tacc[j] = mfma16x16x32(xa, as_bf16x8(av[j][0]), tacc[j]);
-          tacc[j] = mfma16x16x32(xb, as_bf16x8(av[j][1]), tacc[j]);
+      for (int q = 0; q < kTA; ++q) {
+        const int u = kWaves * q + wave;
+        if (u < nb) {
+          const bf16x8_t xa = as_bf16x8(S.x[l16][8 * u + 2 * g]);
+          const bf16x8_t xb = as_bf16x8(S.x[l16][8 * u + 2 * g + 1]);
+#pragma unroll
+          for (int j = 0; j < RT; ++j) {
+            tacc[j] = mfma16x16x32(xa, as_bf16x8(av[q][j][0]), tacc[j]);
+            tacc[j] = mfma16x16x32(xb, as_bf16x8(av[q][j][1]), tacc[j]);
+          }
         }
       }
+    } else {
+      for (int u = wave; u < nb; u += kWaves) {
+        load_a(u, av[0]);
+        const bf16x8_t xa = as_bf16x8(S.x[l16][8 * u + 2 * g]);
+        const bf16x8_t xb = as_bf16x8(S.x[l16][8 * u + 2 * g + 1]);
+#pragma unroll
+        for (int j = 0; j < RT; ++j) {
+          tacc[j] = mfma16x16x32(xa, as_bf16x8(av[0][j][0]), tacc[j]);
+          tacc[j] = mfma16x16x32(xb, as_bf16x8(av[0][j][1]), tacc[j]);
+        }
+      }
+    }
+    // ---- MFMA over the staged chunk
+    // blocks past the slice (u >= nb) hold zero activations, so they add exact zeros
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const bf16x8_t xa = as_bf16x8(S.x[l16][8 * u + 2 * g]);
+      const bf16x8_t xb = as_bf16x8(S.x[l16][8 * u + 2 * g + 1]);
 #pragma unroll
       for (int t = 0; t < kTiles; ++t) {
         const int row = wave * 16 * kTiles + 16 * t + l16;
@@ -235,13 +268,14 @@ __global__ __launch_bounds__(kThreads) void k_gemv_fused(GemvArgs a, Nf4Tables T
     }
   }
 
-  // ---- T over this k-range: sum the four wavefronts' shares -> sT[m][j]
+  // ---- T over this k-range: sum the wavefronts' shares -> sT[m][j]
 #pragma unroll
   for (int j = 0; j < RT; ++j) sred[wave][j][lane] = tacc[j];
   __syncthreads();
   for (int i = tid; i < 16 * 16 * RT; i += kThreads) {
     const int j16 = i / 256, rem = i % 256, ln = rem / 4, v = rem % 4;  // D[m = 4*(ln>>4)+v][j = ln & 15]
-    const float s = sred[0][j16][ln][v] + sred[1][j16][ln][v] + sred[2][j16][ln][v] + sred[3][j16][ln][v];
+    float s = sred[0][j16][ln][v];
+    for (int w = 1; w < kWaves; ++w) s += sred[w][j16][ln][v];
     sT[4 * (ln >> 4) + v][16 * j16 + (ln & 15)] = s;
   }
   __syncthreads();
