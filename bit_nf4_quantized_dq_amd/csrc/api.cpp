@@ -79,7 +79,7 @@ FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
 }
 
 struct BwdWs {
-  size_t t, g, lg, at, cpart, wcopy, total;
+  size_t t, g, lg, at, cpa, cpb, wcopy, total;
 };
 BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   BwdWs w{};
@@ -92,9 +92,10 @@ BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   off = align_up(off + 2 * M * r, 256);
   w.at = off;
   off = align_up(off + 2 * (size_t)r * K, 256);
-  w.cpart = off;
-  const int64_t ca = (int64_t)lora_grad_msplit(M, K) * r * K, cb = (int64_t)lora_grad_msplit(M, N) * r * N;
-  off = align_up(off + sizeof(float) * std::max<int64_t>(ca, cb), 256);
+  w.cpa = off;  // dA and dB run concurrently: separate partials
+  off = align_up(off + sizeof(float) * (int64_t)lora_grad_msplit(M, K) * r * K, 256);
+  w.cpb = off;
+  off = align_up(off + sizeof(float) * (int64_t)lora_grad_msplit(M, N) * r * N, 256);
   if (M >= kNtMinM) {
     w.wcopy = off;
     off = align_up(off + 2 * (size_t)N * K, 256);
@@ -287,8 +288,8 @@ int qlora_linear_fwd(const qlora_nf4dq_t* Wq, const uint16_t* X, int64_t M, cons
   }
   // T = X A^T: s T (BF16) feeds the adapter slices of the GEMM; T itself is saved if asked
   uint16_t* ls = reinterpret_cast<uint16_t*>(base + L.ls);
-  hipError_t e = launch_lora_down(X, A, 0, M, r, K, s, ls, T_save, stream);
-  if (e != hipSuccess) return QLORA_ERR_HIP;
+  hipError_t e;
+  if ((e = launch_lora_down(X, A, 0, M, r, K, s, ls, T_save, stream)) != hipSuccess) return QLORA_ERR_HIP;
   if (M >= kNtMinM) {
     uint16_t* wcopy = reinterpret_cast<uint16_t*>(base + L.wcopy);
     if ((e = launch_dequant(codes, Wq->code8, Wq->c2s, Wq->mu, wcopy, N * K / 8, nf4_tables(), stream)) != hipSuccess)
@@ -317,7 +318,9 @@ int qlora_linear_bwd(const qlora_nf4dq_t* Wq, const uint16_t* X, const uint16_t*
   uint16_t* t = reinterpret_cast<uint16_t*>(base + L.t);
   uint16_t* g = reinterpret_cast<uint16_t*>(base + L.g);
   uint16_t* lg = reinterpret_cast<uint16_t*>(base + L.lg);
-  float* cpart = reinterpret_cast<float*>(base + L.cpart);
+  float* cpa = reinterpret_cast<float*>(base + L.cpa);
+  float* cpb = reinterpret_cast<float*>(base + L.cpb);
+  const uint32_t* codes = reinterpret_cast<const uint32_t*>(Wq->codes);
   hipError_t e;
   const uint16_t* T = T_saved;
   if (!T) {  // recompute T = X A^T
@@ -329,22 +332,21 @@ int qlora_linear_bwd(const qlora_nf4dq_t* Wq, const uint16_t* X, const uint16_t*
   // dX = dY w_hat + (s G) A
   if (dX && M >= kNtMinM) {
     uint16_t* wcopy = reinterpret_cast<uint16_t*>(base + L.wcopy);
-    if ((e = launch_dequant_t(reinterpret_cast<const uint32_t*>(Wq->codes), Wq->code8, Wq->c2s, Wq->mu, N, K, wcopy,
-                              nf4_tables(), stream)) != hipSuccess)
-      return QLORA_ERR_HIP;
-    // dX = dY w_hat + (s G) A: A = w_hat^T [K, N], Wl = A^T [K, r] (staged row-contiguous)
     uint16_t* at = reinterpret_cast<uint16_t*>(base + L.at);
+    if ((e = launch_dequant_t(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, wcopy, nf4_tables(), stream)) != hipSuccess)
+      return QLORA_ERR_HIP;
     if ((e = launch_transpose_bf16(A, r, K, at, stream)) != hipSuccess) return QLORA_ERR_HIP;
+    // A = w_hat^T [K, N], Wl = A^T [K, r] (staged row-contiguous)
     if ((e = launch_gemm_nt(wcopy, K, dY, M, N, at, r, 1, lg, r, dX, QLORA_K_GEMM_DX, stream)) != hipSuccess)
       return QLORA_ERR_HIP;
   } else if (dX) {
-    if ((e = launch_gemm_dx(reinterpret_cast<const uint32_t*>(Wq->codes), Wq->code8, Wq->c2s, Wq->mu, N, K, dY, M, lg,
-                            A, r, dX, nf4_tables(), stream)) != hipSuccess)
+    if ((e = launch_gemm_dx(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, dY, M, lg, A, r, dX, nf4_tables(), stream)) !=
+        hipSuccess)
       return QLORA_ERR_HIP;
   }
-  // dA = s G^T X [r, K]; dB = s dY^T T, stored [N, r]
-  if ((e = launch_lora_grad(g, X, M, r, K, s, 0, cpart, dA, stream)) != hipSuccess) return QLORA_ERR_HIP;
-  if ((e = launch_lora_grad(T, dY, M, r, N, s, 1, cpart, dB, stream)) != hipSuccess) return QLORA_ERR_HIP;
+  // dA = s G^T X [r, K]; dB = s dY^T T, stored [N, r] (own partials and arrival counters each)
+  if ((e = launch_lora_grad(g, X, M, r, K, s, 0, cpa, 0, dA, stream)) != hipSuccess) return QLORA_ERR_HIP;
+  if ((e = launch_lora_grad(T, dY, M, r, N, s, 1, cpb, 1, dB, stream)) != hipSuccess) return QLORA_ERR_HIP;
   return QLORA_OK;
 }
 

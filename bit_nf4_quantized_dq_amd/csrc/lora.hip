@@ -9,7 +9,8 @@
 //        32-wide slabs and their sums meet in LDS in a fixed order.
 // grad : out(j, c) = scale * sum_m U[m][j] V[m][c]            (dA = s G^T X, dB = s dY^T T)
 //        One workgroup owns 64 columns c and a slice of the tokens; the slices' FP32 sums
-//        are combined in a fixed order by the last workgroup of the column tile to finish.
+//        are combined in a fixed order by the last workgroup of the column tile to finish
+//        (arrival counters in one of two sets, so two launches may run concurrently).
 //
 // Both use MFMA 16x16x32 BF16.  Operands whose reduction index is strided in memory (Q as
 // [Kd, R], U and V) are staged in LDS row-major and read with ds_read_b64_tr_b16: within
@@ -22,7 +23,7 @@
 
 namespace qlora {
 
-__device__ unsigned int g_lora_counters[65536];
+__device__ unsigned int g_lora_counters[2 * 65536];
 
 namespace {
 
@@ -160,6 +161,7 @@ __global__ __launch_bounds__(kGradThreads) void k_lora_grad(const uint16_t* __re
                                                             const uint16_t* __restrict__ V, int64_t M,
                                                             int32_t R, int64_t C, int64_t mps, float scale,
                                                             int transposed, float* __restrict__ part,
+                                                            unsigned int* __restrict__ counters,
                                                             uint16_t* __restrict__ out) {
   // per wavefront: 4 V tiles + JT U tiles of [32][16] BF16; reused for the cross-wave sums
   constexpr int kWaveBytes = (4 + JT) * kVTile;
@@ -261,7 +263,7 @@ __global__ __launch_bounds__(kGradThreads) void k_lora_grad(const uint16_t* __re
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned int inc = kCounterPeriod / (unsigned int)msplit;
-    const unsigned int old = __hip_atomic_fetch_add(&g_lora_counters[blockIdx.x], inc, __ATOMIC_RELAXED,
+    const unsigned int old = __hip_atomic_fetch_add(&counters[blockIdx.x], inc, __ATOMIC_RELAXED,
                                                     __HIP_MEMORY_SCOPE_AGENT);
     s_last = ((old + inc) % kCounterPeriod) == 0u;
   }
@@ -305,6 +307,19 @@ __global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restri
   }
 }
 
+// Device address of the arrival counters on the current device (looked up once per device).
+unsigned int* lora_counters() {
+  static unsigned int* addr[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_lora_counters)) != hipSuccess) return nullptr;
+    addr[dev] = static_cast<unsigned int*>(p);
+  }
+  return addr[dev];
+}
+
 template <int JT, int MT, bool QT>
 hipError_t down_launch(const uint16_t* P, const uint16_t* Q, int64_t M, int32_t R, int64_t Kd, float scale,
                        uint16_t* out_s, uint16_t* out_u, hipStream_t s) {
@@ -317,11 +332,15 @@ hipError_t down_launch(const uint16_t* P, const uint16_t* Q, int64_t M, int32_t 
 
 template <int JT>
 hipError_t grad_launch(const uint16_t* U, const uint16_t* V, int64_t M, int32_t R, int64_t C, int32_t msplit,
-                       int64_t mps, float scale, int transposed, float* part, uint16_t* out, hipStream_t s) {
+                       int64_t mps, float scale, int transposed, float* part, int counter_set, uint16_t* out,
+                       hipStream_t s) {
   dim3 grid((unsigned)((C + kGradCols - 1) / kGradCols), (unsigned)msplit);
+  unsigned int* counters = lora_counters();
+  if (!counters) return hipErrorInvalidSymbol;
+  counters += 65536 * counter_set;
   LaunchTimer t(7, s);
   hipExtLaunchKernelGGL(k_lora_grad<JT>, grid, dim3(kGradThreads), 0, s, t.start, t.stop, 0, U, V, M, R, C, mps, scale,
-                        transposed, part, out);
+                        transposed, part, counters, out);
   return hipGetLastError();
 }
 
@@ -350,13 +369,13 @@ int32_t lora_grad_msplit(int64_t M, int64_t C) {
 }
 
 hipError_t launch_lora_grad(const uint16_t* U, const uint16_t* V, int64_t M, int32_t R, int64_t C, float scale,
-                            int transposed, float* part, uint16_t* out, hipStream_t s) {
+                            int transposed, float* part, int counter_set, uint16_t* out, hipStream_t s) {
   const int32_t ms = lora_grad_msplit(M, C);
   const int64_t mps = ((M + ms - 1) / ms + 31) / 32 * 32;
-  if (R <= 16) return grad_launch<1>(U, V, M, R, C, ms, mps, scale, transposed, part, out, s);
-  if (R <= 32) return grad_launch<2>(U, V, M, R, C, ms, mps, scale, transposed, part, out, s);
-  if (R <= 64) return grad_launch<4>(U, V, M, R, C, ms, mps, scale, transposed, part, out, s);
-  return grad_launch<8>(U, V, M, R, C, ms, mps, scale, transposed, part, out, s);
+  if (R <= 16) return grad_launch<1>(U, V, M, R, C, ms, mps, scale, transposed, part, counter_set, out, s);
+  if (R <= 32) return grad_launch<2>(U, V, M, R, C, ms, mps, scale, transposed, part, counter_set, out, s);
+  if (R <= 64) return grad_launch<4>(U, V, M, R, C, ms, mps, scale, transposed, part, counter_set, out, s);
+  return grad_launch<8>(U, V, M, R, C, ms, mps, scale, transposed, part, counter_set, out, s);
 }
 
 hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out, hipStream_t s) {

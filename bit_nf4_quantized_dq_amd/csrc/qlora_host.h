@@ -44,10 +44,11 @@ hipError_t launch_dequant_t(const uint32_t* codes, const uint8_t* code8, const f
 hipError_t launch_lora_down(const uint16_t* P, const uint16_t* Q, int q_transposed, int64_t M, int32_t R, int64_t Kd,
                             float scale, uint16_t* out_s, uint16_t* out_u, hipStream_t s);
 // out(j, c) = bf16(scale * sum_m U[m][j] V[m][c]); U [M, R], V [M, C]; out [R, C], or
-// [C, R] when transposed.  part: FP32 [lora_grad_msplit(M, C)][R][C] scratch.
+// [C, R] when transposed.  part: FP32 [lora_grad_msplit(M, C)][R][C] scratch; counter_set
+// (0 or 1) selects the arrival counters, so two launches with different sets may overlap.
 int32_t lora_grad_msplit(int64_t M, int64_t C);
 hipError_t launch_lora_grad(const uint16_t* U, const uint16_t* V, int64_t M, int32_t R, int64_t C, float scale,
-                            int transposed, float* part, uint16_t* out, hipStream_t s);
+                            int transposed, float* part, int counter_set, uint16_t* out, hipStream_t s);
 // BF16 transpose [rows, cols] -> [cols, rows].
 hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out,
                                  hipStream_t s);
