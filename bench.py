@@ -12,7 +12,8 @@ FLOPs per launch over its average duration from HIP events recorded on the launc
 inside the timed region -- only the two GEMM launches carry events there), a per-kernel
 breakdown from a separate fully instrumented pass, the M = 1 weight-stream rate of the
 same linear (128 distinct quantized copies rotated so every call reads HBM), the quantize
-rate, and the CPU oracle timed on a bounded sample of the same workload.
+rate, the merged-export rate (w_hat + s B A to BF16 over the same rotated copies), and the
+CPU oracle timed on a bounded sample of the same workload.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
   python bench.py --pmc-pass    # 2 steps + a 256 MiB device copy, for counter runs
@@ -38,6 +39,11 @@ def step_flops(M, N, K, r):
 def stream_bytes(M, N, K, r):
     # 0.515869 B/weight of NF4+DQ (codes, code8, c2s, mu) + adapters + activations
     return N * K // 2 + N * K // 64 + 4 * ((N * K // 64 + 255) // 256) + 4 + 2 * r * (N + K) + 2 * M * K + 2 * M * N
+
+
+def merge_bytes(N, K, r):
+    # NF4+DQ weight read + both adapters read + the BF16 merged weight written
+    return N * K // 2 + N * K // 64 + 4 * ((N * K // 64 + 255) // 256) + 4 + 2 * r * (N + K) + 2 * N * K
 
 
 def cpu_baseline(N, K, r, alpha, target_s=15.0):
@@ -234,6 +240,28 @@ def main():
                         "peak_GBs": PEAK_HBM_GBS, "frac": round(sb / (gemv_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
     }
     del graph
+
+    # ---- merged export bf16(w_hat + s B A): the same rotated copies, 8 rotated outputs
+    # (8 x 32 MiB, beyond the 256 MB cache), kernel time from HIP events
+    outs = [torch.empty(N, K, dtype=torch.bfloat16, device=dev) for _ in range(8)]
+    for i in range(8):
+        Q.merge(copies[i], A, B, alpha, out=outs[i])
+    torch.cuda.synchronize()
+    Q.timing_enable(True, kernels=("merge",))
+    t0 = time.perf_counter()
+    for i, cp in enumerate(copies):
+        Q.merge(cp, A, B, alpha, out=outs[i % 8])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    mg_ms, mg_n = Q.timing_read("merge")
+    Q.timing_enable(False)
+    mb = merge_bytes(N, K, r)
+    mg_us = 1e3 * mg_ms / max(mg_n, 1)
+    merge = {"bytes_per_call": mb, "kernel_avg_us": round(mg_us, 2),
+             "achieved_GBs": round(mb / (mg_us * 1e-6) / 1e9, 1), "peak_GBs": PEAK_HBM_GBS,
+             "frac": round(mb / (mg_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+             "us_per_call_eager_python": round(1e6 * (t1 - t0) / len(copies), 2)}
+    del outs
     del copies
 
     # ---- quantize (load time) of the same FP32 weight
@@ -265,6 +293,7 @@ def main():
         "kernels_instrumented_pass": {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in per_kernel.items()},
         "weight_stream_M1": stream,
         "quantize_4096x4096": quant,
+        "merge_4096x4096": merge,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(N, K, r, alpha)

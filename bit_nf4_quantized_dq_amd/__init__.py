@@ -12,6 +12,8 @@ from ._binding import (  # noqa: F401
     load_library,
     nf4_codebook,
     quantize,
+    quantize_bf16,
+    merge,
     dequantize,
     linear_fwd,
     linear_bwd,

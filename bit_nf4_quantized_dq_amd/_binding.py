@@ -24,6 +24,7 @@ KERNEL_IDS = {
     "lora_down": 6,
     "lora_grad": 7,
     "dequant_t": 8,
+    "merge": 9,
 }
 
 
@@ -65,7 +66,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         "qlora_workspace_size": (ctypes.c_int, i64, i64, i64, i32, P(sz)),
         "qlora_nf4_codebook": (P(ctypes.c_float),),
         "qlora_quantize": (vp, P(_Nf4dq), P(ctypes.c_float), vp, sz, vp),
+        "qlora_quantize_bf16": (vp, P(_Nf4dq), P(ctypes.c_float), vp, sz, vp),
         "qlora_dequantize": (P(_Nf4dq), vp, vp),
+        "qlora_merge": (P(_Nf4dq), vp, vp, i32, ctypes.c_float, vp, vp),
         "qlora_linear_fwd": (P(_Nf4dq), vp, i64, vp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp),
         "qlora_linear_bwd": (P(_Nf4dq), vp, vp, i64, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp),
         "qlora_e4m3_encode": (vp, vp, i64, vp),
@@ -195,6 +198,35 @@ def quantize(W: torch.Tensor, out: QuantizedWeight | None = None, ws: torch.Tens
     _check(load_library().qlora_quantize(W.data_ptr(), ctypes.byref(s), ctypes.byref(mu), ws.data_ptr(), ws.numel(),
                                          _stream(W)), "quantize")
     return q
+
+
+def quantize_bf16(W: torch.Tensor, out: QuantizedWeight | None = None,
+                  ws: torch.Tensor | None = None) -> QuantizedWeight:
+    """Quantize a BF16 [d_out, d_in] CUDA tensor (its exact FP32 values; synchronizes once)."""
+    _dev(W, torch.bfloat16, "W")
+    d_out, d_in = W.shape
+    q = out if out is not None else QuantizedWeight.empty(d_out, d_in, W.device)
+    need = workspace_size(OP_QUANTIZE, 1, d_out, d_in, 1)
+    ws = ws if ws is not None else _WS.get(need, W.device, "quant")
+    mu = ctypes.c_float()
+    s = q.struct()
+    _check(load_library().qlora_quantize_bf16(W.data_ptr(), ctypes.byref(s), ctypes.byref(mu), ws.data_ptr(),
+                                              ws.numel(), _stream(W)), "quantize_bf16")
+    return q
+
+
+def merge(q: QuantizedWeight, A: torch.Tensor, B: torch.Tensor, alpha: float,
+          out: torch.Tensor | None = None) -> torch.Tensor:
+    """Merged BF16 [d_out, d_in] weight bf16(w_hat + (alpha/r) B A) for export."""
+    for t, n in ((A, "A"), (B, "B")):
+        _dev(t, torch.bfloat16, n)
+    r = A.shape[0]
+    out = out if out is not None else torch.empty(q.d_out, q.d_in, dtype=torch.bfloat16, device=A.device)
+    _dev(out, torch.bfloat16, "out")
+    s = q.struct()
+    _check(load_library().qlora_merge(ctypes.byref(s), A.data_ptr(), B.data_ptr(), r, float(alpha), out.data_ptr(),
+                                      _stream(out)), "merge")
+    return out
 
 
 def dequantize(q: QuantizedWeight, out: torch.Tensor | None = None) -> torch.Tensor:

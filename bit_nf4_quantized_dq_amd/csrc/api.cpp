@@ -229,8 +229,13 @@ int qlora_nf4_codebook(float out16[16]) {
   return QLORA_OK;
 }
 
-int qlora_quantize(const float* W, const qlora_nf4dq_t* Wq, float* host_mu, void* ws, size_t ws_bytes,
-                   hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Both quantize entry points: W is FP32 or BF16 (widened exactly on load).
+int quantize_impl(const void* W, bool w_bf16, const qlora_nf4dq_t* Wq, float* host_mu, void* ws, size_t ws_bytes,
+                  hipStream_t stream) {
   int st = check_wq(Wq);
   if (st) return st;
   if (!W || !aligned16(W)) return QLORA_ERR_INVALID_ARG;
@@ -242,7 +247,8 @@ int qlora_quantize(const float* W, const qlora_nf4dq_t* Wq, float* host_mu, void
   int* flag = reinterpret_cast<int*>(hist + 256);
   hipError_t e = hipMemsetAsync(hist, 0, 256 * sizeof(unsigned long long) + 256, stream);
   if (e != hipSuccess) return QLORA_ERR_HIP;
-  e = launch_quant_pass1(W, reinterpret_cast<uint32_t*>(Wq->codes), c1, hist, flag, n / 8, nf4_tables(), stream);
+  e = launch_quant_pass1(W, w_bf16, reinterpret_cast<uint32_t*>(Wq->codes), c1, hist, flag, n / 8, nf4_tables(),
+                         stream);
   if (e != hipSuccess) return QLORA_ERR_HIP;
   unsigned long long h_hist[256];
   int h_flag = 0;
@@ -257,6 +263,20 @@ int qlora_quantize(const float* W, const qlora_nf4dq_t* Wq, float* host_mu, void
   return hip_status(e);
 }
 
+}  // namespace
+
+extern "C" {
+
+int qlora_quantize(const float* W, const qlora_nf4dq_t* Wq, float* host_mu, void* ws, size_t ws_bytes,
+                   hipStream_t stream) {
+  return quantize_impl(W, false, Wq, host_mu, ws, ws_bytes, stream);
+}
+
+int qlora_quantize_bf16(const uint16_t* W, const qlora_nf4dq_t* Wq, float* host_mu, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  return quantize_impl(W, true, Wq, host_mu, ws, ws_bytes, stream);
+}
+
 int qlora_dequantize(const qlora_nf4dq_t* Wq, uint16_t* W_bf16, hipStream_t stream) {
   int st = check_wq(Wq);
   if (st) return st;
@@ -264,6 +284,19 @@ int qlora_dequantize(const qlora_nf4dq_t* Wq, uint16_t* W_bf16, hipStream_t stre
   const int64_t n = Wq->d_out * Wq->d_in;
   return hip_status(launch_dequant(reinterpret_cast<const uint32_t*>(Wq->codes), Wq->code8, Wq->c2s, Wq->mu,
                                    W_bf16, n / 8, nf4_tables(), stream));
+}
+
+int qlora_merge(const qlora_nf4dq_t* Wq, const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                uint16_t* W_out, hipStream_t stream) {
+  int st = check_wq(Wq);
+  if (st) return st;
+  if ((st = check_lora(1, r, alpha))) return st;
+  if (!A || !B || !W_out || !aligned16(A) || !aligned16(W_out)) return QLORA_ERR_INVALID_ARG;
+  if ((r & 7) == 0 && !aligned16(B)) return QLORA_ERR_INVALID_ARG;
+  const int64_t N = Wq->d_out, K = Wq->d_in;
+  if ((N + 127) / 128 > 65535) return QLORA_ERR_BAD_SHAPE;  // grid rows of 128 weights
+  return hip_status(launch_merge(reinterpret_cast<const uint32_t*>(Wq->codes), Wq->code8, Wq->c2s, Wq->mu, A, B, N, K,
+                                 r, alpha / (float)r, W_out, nf4_tables(), stream));
 }
 
 int qlora_linear_fwd(const qlora_nf4dq_t* Wq, const uint16_t* X, int64_t M, const uint16_t* A, const uint16_t* B,

@@ -24,7 +24,7 @@ struct LaunchTimer {
 };
 
 // ---- quantize / dequantize (quantize.hip, dequant.hip)
-hipError_t launch_quant_pass1(const float* W, uint32_t* codes, float* c1, unsigned long long* hist,
+hipError_t launch_quant_pass1(const void* W, bool w_bf16, uint32_t* codes, float* c1, unsigned long long* hist,
                               int* flag, int64_t n_words, const Nf4Tables& T, hipStream_t s);
 hipError_t launch_quant_pass2(const float* c1, float mu, uint8_t* code8, float* c2s, float* mu_out,
                               int64_t n_blocks, hipStream_t s);
@@ -37,6 +37,11 @@ hipError_t launch_dequant(const uint32_t* codes, const uint8_t* code8, const flo
 hipError_t launch_dequant_t(const uint32_t* codes, const uint8_t* code8, const float* c2s,
                             const float* mu, int64_t N, int64_t K, uint16_t* out, const Nf4Tables& T,
                             hipStream_t s);
+
+// ---- merged export (merge.hip): out [N, K] BF16 = bf16(w_hat + s B A), B [N, r], A [r, K]
+hipError_t launch_merge(const uint32_t* codes, const uint8_t* code8, const float* c2s, const float* mu,
+                        const uint16_t* A, const uint16_t* B, int64_t N, int64_t K, int32_t r, float s,
+                        uint16_t* out, const Nf4Tables& T, hipStream_t st);
 
 // ---- LoRA skinny kernels (lora.hip)
 // out[m][j] = sum_k P[m][k] Q(j, k) for j < R, Q [R, Kd] (q_transposed = 0) or [Kd, R] (1);

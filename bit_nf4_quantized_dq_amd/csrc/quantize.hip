@@ -10,8 +10,9 @@
 //   are centred on their mean mu and quantized to 8-bit floats in groups of 256 with one
 //   FP32 constant per group: c2s = fl32(max|c1 - mu| / 448), code8 = E4M3(fl32(d / c2s)).
 //
-// Memory layout: W FP32 [d_out*d_in] is read as 8-float words (one packed code word each);
-// a wavefront covers 8 blocks = 2 KB of W with 16-byte lane loads.
+// Memory layout: W FP32 or BF16 [d_out*d_in] is read as 8-value words (one packed code word
+// each); a wavefront covers 8 blocks of W with 16-byte lane loads.  A BF16 checkpoint (the
+// 16-bit form a model ships in, and the merged export) is quantized as its exact FP32 values.
 #include "qlora_device.h"
 #include "qlora_host.h"
 
@@ -20,7 +21,10 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__global__ __launch_bounds__(kThreads) void k_quant_pass1(const float4* __restrict__ W,
+// W is FP32 (BF = false: two 16-byte loads per word) or BF16 (BF = true: one 16-byte load
+// per word, each value widened exactly to FP32).
+template <bool BF>
+__global__ __launch_bounds__(kThreads) void k_quant_pass1(const void* __restrict__ W,
                                                           uint32_t* __restrict__ codes,
                                                           float* __restrict__ c1_out,
                                                           unsigned long long* __restrict__ hist,
@@ -33,9 +37,17 @@ __global__ __launch_bounds__(kThreads) void k_quant_pass1(const float4* __restri
   const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // one code word = 8 weights
   const bool active = g < n_words;  // n_words is a multiple of 8, so whole blocks are active
   float v[8];
-  if (active) {
-    const float4 a = W[2 * g];
-    const float4 b = W[2 * g + 1];
+  if (active && BF) {
+    const uint4 a = static_cast<const uint4*>(W)[g];
+    const uint32_t p[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16lo_to_f32(p[i]);
+      v[2 * i + 1] = bf16hi_to_f32(p[i]);
+    }
+  } else if (active) {
+    const float4 a = static_cast<const float4*>(W)[2 * g];
+    const float4 b = static_cast<const float4*>(W)[2 * g + 1];
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
   } else {
@@ -129,12 +141,16 @@ __global__ __launch_bounds__(kThreads) void k_e4m3_encode(const float* __restric
 
 }  // namespace
 
-hipError_t launch_quant_pass1(const float* W, uint32_t* codes, float* c1, unsigned long long* hist,
+hipError_t launch_quant_pass1(const void* W, bool w_bf16, uint32_t* codes, float* c1, unsigned long long* hist,
                               int* flag, int64_t n_words, const Nf4Tables& T, hipStream_t s) {
   const int64_t grid = (n_words + kThreads - 1) / kThreads;
   LaunchTimer t(0, s);
-  hipExtLaunchKernelGGL(k_quant_pass1, dim3((unsigned)grid), dim3(kThreads), 0, s, t.start, t.stop, 0,
-                     reinterpret_cast<const float4*>(W), codes, c1, hist, flag, n_words, T);
+  if (w_bf16)
+    hipExtLaunchKernelGGL(k_quant_pass1<true>, dim3((unsigned)grid), dim3(kThreads), 0, s, t.start, t.stop, 0, W, codes,
+                          c1, hist, flag, n_words, T);
+  else
+    hipExtLaunchKernelGGL(k_quant_pass1<false>, dim3((unsigned)grid), dim3(kThreads), 0, s, t.start, t.stop, 0, W,
+                          codes, c1, hist, flag, n_words, T);
   return hipGetLastError();
 }
 

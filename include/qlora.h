@@ -105,11 +105,35 @@ int qlora_nf4_codebook(float out16[16]);
 int qlora_quantize(const float *W, const qlora_nf4dq_t *Wq, float *host_mu, void *ws,
                    size_t ws_bytes, hipStream_t stream);
 
+/* Quantize BF16 weights (device uint16 bit patterns [d_out, d_in]): the same steps as
+ * qlora_quantize applied to their exact FP32 values.  A 16-bit checkpoint is quantized as
+ * it stands ("QLoRA: Quantize Base Weights to 4-Bit", Section 1: the frozen base otherwise
+ * sits in memory in 16-bit precision), and so is a merged export from qlora_merge when a
+ * 4-bit copy of it is wanted ("QLoRA -- Fine-Tuning a 65B Model on One GPU", "Pitfalls":
+ * merge in 16 bits, then quantize the merged result).  Same buffers, workspace, single
+ * synchronization and errors as qlora_quantize; W must be 16-byte aligned. */
+int qlora_quantize_bf16(const uint16_t *W, const qlora_nf4dq_t *Wq, float *host_mu, void *ws,
+                        size_t ws_bytes, hipStream_t stream);
+
 /* Dequantize to BF16 (device uint16[d_out, d_in]), bit-exact:
  *   c1_hat = fl32(fl32(E4M3(code8) * c2s) + mu),  w_hat = bf16_rne(fl32(q[code] * c1_hat)).
  * For export and tests; the linear entry points decode on chip instead.
  * Errors: INVALID_ARG, BAD_SHAPE, UNSUPPORTED, HIP. */
 int qlora_dequantize(const qlora_nf4dq_t *Wq, uint16_t *W_bf16, hipStream_t stream);
+
+/* Merged export: W_out = bf16_rne(fl32(w_hat + s * (B A))), s = fl32(alpha / r), with
+ * w_hat the bit-exact dequantized base (as qlora_dequantize) and B A summed in FP32 from
+ * the BF16 adapters ("QLoRA: Quantize Base Weights to 4-Bit", "Interview questions": the
+ * base is dequantized to 16 bits and the adapter folded in, W = W_dequant + (alpha/r) B A,
+ * for a 16-bit checkpoint with no adapter left at inference; "QLoRA -- Fine-Tuning a 65B
+ * Model on One GPU", "Pitfalls": the fold is done in 16 bits, not inside the 4-bit format).
+ *   A [r, d_in], B [d_out, r]: device BF16 adapters (A 16-byte aligned; B too when r % 8 == 0).
+ *   W_out [d_out, d_in]: device BF16, overwritten; 16-byte aligned.
+ * The quantized weight is only read; to re-quantize, pass W_out to qlora_quantize_bf16.
+ * No workspace, no synchronization.  Errors: INVALID_ARG (null or misaligned pointer, r
+ * outside [1, 128], alpha not finite), BAD_SHAPE, UNSUPPORTED, HIP. */
+int qlora_merge(const qlora_nf4dq_t *Wq, const uint16_t *A, const uint16_t *B, int32_t r,
+                float alpha, uint16_t *W_out, hipStream_t stream);
 
 /* Forward: Y = X w_hat^T + (alpha / r) T B^T with T = X A^T, FP32 accumulation, BF16 out
  * ("QLoRA: Quantize Base Weights to 4-Bit", Section 3; "QLoRA -- Fine-Tuning a 65B Model
@@ -159,7 +183,8 @@ enum qlora_kernel_id {
   QLORA_K_LORA_DOWN = 6,   /* T = X A^T and G = dY B */
   QLORA_K_LORA_GRAD = 7,   /* dA and dB */
   QLORA_K_DEQUANT_T = 8,   /* BF16 w_hat^T, the dX copy for M >= 1024 */
-  QLORA_K_COUNT = 9
+  QLORA_K_MERGE = 9,       /* merged export w_hat + s B A */
+  QLORA_K_COUNT = 10
 };
 int qlora_timing_enable(int kernel_mask);
 int qlora_timing_read(int kernel_id, double *total_ms, int64_t *launches);

@@ -36,4 +36,7 @@ from .qlora_oracle import (  # noqa: F401
     lora_bwd,
     quant_sizes,
     bits_per_param,
+    bf16_round_f64_bits,
+    merge,
+    quantize_bf16,
 )

@@ -354,3 +354,48 @@ def bits_per_param(d_out: int, d_in: int, double_quant: bool = True) -> float:
     if not double_quant:
         return 8.0 * (sz["codes"] + 4 * (n // BLOCK1)) / n
     return 8.0 * sum(sz.values()) / n
+
+
+# --------------------------------------------------------------------------------------
+# Merge / export: fold the adapter into the dequantized base, optionally re-quantize
+# --------------------------------------------------------------------------------------
+
+
+def bf16_round_f64_bits(x) -> np.ndarray:
+    """bfloat16 bit patterns of float64 values, one round-to-nearest-even (finite inputs).
+
+    Rounding float64 -> float32 -> bfloat16 by RNE twice can differ from one rounding.  The
+    first step is therefore done by rounding to odd (truncate, then set the last bit when
+    the truncation was inexact); a float32 carries 24 >= 2 * 8 + 2 significant bits, so
+    the following RNE to bfloat16 equals the direct RNE of x (Boldo and Melquiond,
+    "Emulation of FMA and correctly rounded sums: proved algorithms using rounding to odd",
+    IEEE Trans. Computers, 2008)."""
+    x = np.asarray(x, dtype=np.float64)
+    f = x.astype(np.float32)  # RNE
+    away = np.abs(f.astype(np.float64)) > np.abs(x)
+    f = np.where(away, np.nextafter(f, np.float32(0)), f).astype(np.float32)  # truncation
+    inexact = (f.astype(np.float64) != x).astype(np.uint32)
+    f = (f.view(np.uint32) | inexact).view(np.float32)
+    return bf16_round_bits(f)
+
+
+def merge(q: dict, A: np.ndarray, B: np.ndarray, alpha: float, r: int):
+    """Merged 16-bit weight W' = bf16(w_hat + (alpha/r) B A), d_out x d_in.
+
+    [4-Bit] "Interview questions" (deployment): the base is dequantized back to 16 bits
+    and the trained adapter is added, W = W_dequant + (alpha/r) B A, giving an ordinary
+    16-bit checkpoint.  [65B] "Pitfalls" and "How it's used in practice": the merge happens
+    in 16 bits, never inside the 4-bit format; the merged result may then be quantized
+    again (:func:`quantize_bf16`).  The sum is exact in float64 over the BF16 w_hat and the
+    BF16 adapters, rounded once to BF16.
+    Returns (BF16 bit patterns [d_out, d_in], the float64 values before rounding)."""
+    s = float(alpha) / float(r)
+    exact = dequantize_f64(q) + s * (np.asarray(B, np.float64) @ np.asarray(A, np.float64))
+    return bf16_round_f64_bits(exact), exact
+
+
+def quantize_bf16(W_bits: np.ndarray, blocks: np.ndarray | None = None) -> dict:
+    """Quantize a BF16 weight matrix (bit patterns).  Every BF16 value is exact in FP32,
+    so this is :func:`quantize` of the widened values: the 16-bit checkpoint a model ships
+    in is quantized as it stands ([4-Bit] Sec. 1: the frozen base lives in 16 bits)."""
+    return quantize(bf16_bits_to_f32(W_bits), blocks)

@@ -24,7 +24,7 @@ def L():
 def test_every_declared_symbol_is_exported(L):
     text = open(HEADER).read()
     names = sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text)))
-    assert len(names) == 11
+    assert len(names) == 13
     for n in names:
         assert hasattr(L, n), n
 
@@ -71,6 +71,17 @@ def test_shape_and_argument_errors_before_launch(L):
     assert L.qlora_quantize(None, ctypes.byref(_wq()), None, ws, 1 << 20, None) == -1
     assert L.qlora_quantize(ctypes.c_void_p(4100), ctypes.byref(_wq()), None, ws, 1 << 20, None) == -1  # misaligned
     assert L.qlora_dequantize(None, dummy, None) == -1
+    assert L.qlora_quantize_bf16(dummy, ctypes.byref(_wq()), None, ws, 8, None) == -5
+    assert L.qlora_quantize_bf16(ctypes.c_void_p(4098), ctypes.byref(_wq()), None, ws, 1 << 20, None) == -1
+    assert L.qlora_quantize_bf16(dummy, ctypes.byref(_wq(d_in=96)), None, ws, 1 << 20, None) == -2
+    assert L.qlora_merge(ctypes.byref(_wq()), dummy, dummy, 0, 16.0, dummy, None) == -1
+    assert L.qlora_merge(ctypes.byref(_wq()), dummy, dummy, 129, 16.0, dummy, None) == -1
+    assert L.qlora_merge(ctypes.byref(_wq()), dummy, dummy, 8, float("inf"), dummy, None) == -1
+    assert L.qlora_merge(ctypes.byref(_wq()), dummy, None, 8, 16.0, dummy, None) == -1
+    assert L.qlora_merge(ctypes.byref(_wq()), dummy, ctypes.c_void_p(4098), 8, 16.0, dummy, None) == -1  # B misaligned
+    assert L.qlora_merge(ctypes.byref(_wq()), dummy, dummy, 8, 16.0, ctypes.c_void_p(4098), None) == -1
+    assert L.qlora_merge(ctypes.byref(_wq(d_out=250)), dummy, dummy, 8, 16.0, dummy, None) == -2
+    assert L.qlora_merge(ctypes.byref(_wq(b1=32)), dummy, dummy, 8, 16.0, dummy, None) == -3
 
 
 def test_workspace_sizes_are_sane():

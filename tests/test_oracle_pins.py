@@ -364,3 +364,87 @@ def test_special_cases_alpha_zero_and_B_zero():
     assert np.allclose(Y0, X @ What.T)
     dX, dA, dB = O.lora_bwd(What, X, dY, A, np.zeros_like(B), 8.0, 4)
     assert np.all(dA == 0) and np.allclose(dX, dY @ What)
+
+
+# ------------------------------------------------------------------ merge / export
+
+from fractions import Fraction
+
+
+def _bf16_nearest_by_enumeration(x: float) -> int:
+    """BF16 bit pattern nearest to the float64 x (ties to the even pattern), by exact
+    rational distances to the neighbouring patterns -- no rounding mode involved."""
+    sign = 0x8000 if math.copysign(1.0, x) < 0 else 0
+    a = abs(x)
+    t = int(np.array(a, np.float32).view(np.uint32)) >> 16  # near a (within a few patterns)
+    best, best_d = None, None
+    for cand in range(max(t - 2, 0), t + 3):
+        v = Fraction(float(np.array(cand << 16, np.uint32).view(np.float32)))
+        d = abs(Fraction(a) - v)
+        if best is None or d < best_d or (d == best_d and cand % 2 == 0):
+            best, best_d = cand, d
+    return best | sign
+
+
+def test_bf16_round_f64_is_one_correct_rounding():
+    rng = np.random.default_rng(20)
+    vals = list(rng.standard_normal(400) * 10.0 ** rng.integers(-6, 4, 400))
+    # exact BF16 midpoints and points a hair off them (where a double rounding goes wrong)
+    for b in rng.integers(0x3000, 0x4800, 100):
+        lo = float(np.array(int(b) << 16, np.uint32).view(np.float32))
+        hi = float(np.array((int(b) + 1) << 16, np.uint32).view(np.float32))
+        mid = (lo + hi) / 2
+        vals += [mid, -mid, mid + abs(mid) * 2.0**-40, mid - abs(mid) * 2.0**-40, mid * (1 + 2.0**-30)]
+    vals += [0.0, 3.0e-40, -7.1e-39, 1.0 + 2.0**-8 + 2.0**-40]
+    x = np.array(vals, np.float64)
+    got = O.bf16_round_f64_bits(x)
+    exp = np.array([_bf16_nearest_by_enumeration(v) for v in vals], np.uint16)
+    assert np.array_equal(got, exp)
+
+
+def test_merge_is_the_forward_through_one_matrix():
+    """X W'^T equals the adapted forward of X for every X (before W' is rounded): a
+    transposed, unscaled or sign-flipped adapter fails.  Non-square, r > 1."""
+    W = _randW(48, 192, seed=21)
+    q = O.quantize(W)
+    rng = np.random.default_rng(22)
+    r, alpha = 5, 11.0
+    A = rng.standard_normal((r, 192))
+    B = rng.standard_normal((48, r))
+    X = rng.standard_normal((7, 192))
+    _, exact = O.merge(q, A, B, alpha, r)
+    Y, _ = O.lora_fwd(O.dequantize_f64(q), X, A, B, alpha, r)
+    assert np.allclose(X @ exact.T, Y, rtol=1e-12, atol=1e-12)
+
+
+def test_merge_special_cases():
+    W = _randW(32, 128, seed=23)
+    q = O.quantize(W)
+    A = np.zeros((3, 128))
+    B = np.zeros((32, 3))
+    bits, _ = O.merge(q, A, B, 6.0, 3)
+    assert np.array_equal(bits, O.dequantize_bf16_bits(q))  # B = 0: the dequantized base
+    A[2, 70] = 1.0
+    B[9, 2] = 1.0
+    bits, _ = O.merge(q, A, B, 6.0, 3)  # one-hot adapter: only (9, 70) moves, by alpha/r
+    base = O.dequantize_bf16_bits(q)
+    diff = np.argwhere(bits != base)
+    assert [tuple(d) for d in diff] == [(9, 70)]
+    w = float(O.bf16_bits_to_f32(base[9, 70]))
+    assert int(bits[9, 70]) == _bf16_nearest_by_enumeration(w + 2.0)
+
+
+def test_requantize_unchanged_special_weight_restores_codes():
+    """NF4 codes -> BF16 merge with B = 0 -> quantize again: with block absmaxes +-c exact,
+    the re-quantized codes and constants equal the originals."""
+    qt = O.nf4_codebook()
+    rng = np.random.default_rng(24)
+    c = np.float32(2.0**-5)
+    k = rng.integers(0, 16, size=(32, 256)).astype(np.int64)
+    k[:, ::64] = 0
+    W = (qt[k] * c).astype(np.float32)
+    q = O.quantize(W)
+    bits, _ = O.merge(q, np.zeros((2, 256)), np.zeros((32, 2)), 4.0, 2)
+    q2 = O.quantize_bf16(bits)
+    assert np.array_equal(q2["codes"], q["codes"]) and np.array_equal(q2["codes"], k.astype(np.uint8))
+    assert q2["mu"] == c and np.array_equal(q2["code8"], q["code8"]) and np.array_equal(q2["c2s"], q["c2s"])
