@@ -261,7 +261,19 @@ def main():
              "achieved_GBs": round(mb / (mg_us * 1e-6) / 1e9, 1), "peak_GBs": PEAK_HBM_GBS,
              "frac": round(mb / (mg_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
              "us_per_call_eager_python": round(1e6 * (t1 - t0) / len(copies), 2)}
-    del outs
+    # context: a plain device copy moving the same kind of mixed read + write traffic
+    src32 = torch.empty(32 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    cps = [torch.empty_like(src32) for _ in range(8)]
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(64):
+        cps[i % 8].copy_(src32)
+    e1.record()
+    torch.cuda.synchronize()
+    cp_us = 1e3 * e0.elapsed_time(e1) / 64
+    merge["reference_device_copy_32MiB"] = {"us": round(cp_us, 2), "GBs_read_plus_write": round(2 * (32 << 20) / (cp_us * 1e-6) / 1e9, 1)}
+    del outs, cps, src32
     del copies
 
     # ---- quantize (load time) of the same FP32 weight

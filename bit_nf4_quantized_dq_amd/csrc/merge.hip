@@ -12,8 +12,11 @@
 //   D[i][j] = sum_rho A[rho][k0 + i] B[n0 + j][rho]      (i: weight column, j: weight row)
 // Register 4q + v of lane l holds column 8q + 4(l >> 5) + v of row (l & 31): the nibbles
 // 4(l >> 5) .. +3 of code word q of that row, so each lane reads one 16-byte run of codes
-// per 32x32 tile, and writes 8 bytes per word.  Then v = fl32(w_hat + s * acc) (one fused
-// rounding) and W' = bf16_rne(v).
+// per 32x32 tile.  Then v = fl32(w_hat + s * acc) (one fused rounding) and W' = bf16_rne(v).
+// A wavefront's 32 x 64 results pass through LDS so they leave as full 128-byte row
+// segments with non-temporal stores; the loads are issued in the order they are consumed,
+// so the stores of one block overlap the loads of the next.  The kernel moves 2.52 bytes
+// per weight (0.52 read, 2 written) and is bound by HBM.
 //
 // The A operand (reduction index rho strided in memory) is staged per workgroup in LDS,
 // rows rho x 256 columns, and read with ds_read_b64_tr_b16: in each 16-lane group, lane i
@@ -33,6 +36,7 @@ constexpr int kColsWG = 256;                 // weight columns per workgroup: 8 
 constexpr int kTilesK = kColsWG / 32;
 constexpr int kPitch = 2 * kColsWG + 64;     // LDS row pitch (bytes): 4 consecutive rows hit
                                              // disjoint bank quarters for the transposing reads
+constexpr int kStagePitch = 144;             // output staging: 32 rows x 64 columns per wave
 
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -77,6 +81,7 @@ __global__ __launch_bounds__(kThreads) void k_merge(const uint32_t* __restrict__
                                                     int32_t r, float s, uint16_t* __restrict__ out,
                                                     Nf4Tables T) {
   __shared__ __attribute__((aligned(16))) char sa[16 * RC * kPitch];
+  __shared__ __attribute__((aligned(16))) char so[kWaves * 32 * kStagePitch];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, h32 = lane >> 5;
   const int64_t k0 = (int64_t)blockIdx.x * kColsWG;
@@ -84,26 +89,20 @@ __global__ __launch_bounds__(kThreads) void k_merge(const uint32_t* __restrict__
   const bool row_ok = n < N;
   const int64_t nb_row = K / kBlock1, nb = N * nb_row;
 
-  // this lane's code words: tile i holds columns k0 + 32 i .. +31 (16 bytes of codes)
-  const rsrc_t rc = make_rsrc(codes, N * K / 2);
-  uint4 cw[kTilesK];
+  // Loads are issued in the order they are consumed -- A (staged before the barrier), B,
+  // the block constants, then the code words tile by tile -- so each wait below covers only
+  // what its step needs and the stores of one block overlap the loads of the next.
+  constexpr int kStage = 16 * RC * (kColsWG / 8);  // 16-byte pieces of the A tile
+  constexpr int kStageIt = (kStage + kThreads - 1) / kThreads;
+  const rsrc_t ra = make_rsrc(A, (int64_t)r * K * 2);
+  uint4 av[kStageIt];
 #pragma unroll
-  for (int i = 0; i < kTilesK; ++i)
-    cw[i] = bload16(rc, (row_ok && k0 + 32 * i < K) ? (uint32_t)((n * K + k0 + 32 * i) / 2) : kOOB);
-
-  // block constants of the 4 blocks of 64 columns
-  const rsrc_t r8 = make_rsrc(code8, nb);
-  const rsrc_t r2 = make_rsrc(c2s, 4 * ((nb + kBlock2 - 1) / kBlock2));
-  uint32_t c8[kTilesK / 2];
-  float g2[kTilesK / 2];
-#pragma unroll
-  for (int b = 0; b < kTilesK / 2; ++b) {
-    const bool ok = row_ok && k0 + 64 * b < K;
-    const int64_t blk = n * nb_row + k0 / kBlock1 + b;
-    c8[b] = bload1(r8, ok ? (uint32_t)blk : kOOB);
-    g2[b] = __uint_as_float(bload4(r2, ok ? (uint32_t)(4 * (blk / kBlock2)) : kOOB));
+  for (int it = 0; it < kStageIt; ++it) {
+    const int idx = threadIdx.x + kThreads * it;
+    const int row = idx / (kColsWG / 8), ch = idx % (kColsWG / 8);
+    const int64_t k = k0 + 8 * ch;
+    av[it] = bload16(ra, (idx < kStage && row < r && k < K) ? (uint32_t)(((int64_t)row * K + k) * 2) : kOOB);
   }
-  const float mu0 = mu[0];
 
   // B operand: row n, rank indices 16 c + 8 h32 .. +7
   const rsrc_t rb = make_rsrc(B, N * r * 2);
@@ -125,18 +124,38 @@ __global__ __launch_bounds__(kThreads) void k_merge(const uint32_t* __restrict__
     }
   }
 
-  // stage A[0 .. 16 RC)[k0 .. k0 + 256) (zeros beyond r and K)
-  const rsrc_t ra = make_rsrc(A, (int64_t)r * K * 2);
+  // block constants of the blocks of 64 columns
+  const rsrc_t r8 = make_rsrc(code8, nb);
+  const rsrc_t r2 = make_rsrc(c2s, 4 * ((nb + kBlock2 - 1) / kBlock2));
+  uint32_t c8[kTilesK / 2];
+  float g2[kTilesK / 2];
 #pragma unroll
-  for (int it = 0; it < 16 * RC * (kColsWG / 8) / kThreads; ++it) {
-    const int idx = threadIdx.x + kThreads * it;
-    const int row = idx / (kColsWG / 8), ch = idx % (kColsWG / 8);
-    const int64_t k = k0 + 8 * ch;
-    const uint4 v = bload16(ra, (row < r && k < K) ? (uint32_t)(((int64_t)row * K + k) * 2) : kOOB);
-    *reinterpret_cast<uint4*>(sa + row * kPitch + 16 * ch) = v;
+  for (int b = 0; b < kTilesK / 2; ++b) {
+    const bool ok = row_ok && k0 + 64 * b < K;
+    const int64_t blk = n * nb_row + k0 / kBlock1 + b;
+    c8[b] = bload1(r8, ok ? (uint32_t)blk : kOOB);
+    g2[b] = __uint_as_float(bload4(r2, ok ? (uint32_t)(4 * ((uint64_t)blk >> 8)) : kOOB));
   }
-  __syncthreads();
+  const float mu0 = mu[0];
 
+  // this lane's code words: tile i holds columns k0 + 32 i .. +31 (16 bytes of codes)
+  const rsrc_t rc = make_rsrc(codes, N * K / 2);
+  uint4 cw[kTilesK];
+#pragma unroll
+  for (int i = 0; i < kTilesK; ++i)
+    cw[i] = bload16(rc, (row_ok && k0 + 32 * i < K) ? (uint32_t)((uint64_t)(n * K + k0 + 32 * i) >> 1) : kOOB);
+
+  // A[0 .. 16 RC)[k0 .. k0 + kColsWG) into LDS (zeros beyond r and K); the barrier waits for
+  // LDS traffic only, not for the loads still in flight
+#pragma unroll
+  for (int it = 0; it < kStageIt; ++it) {
+    const int idx = threadIdx.x + kThreads * it;
+    if (idx < kStage) *reinterpret_cast<uint4*>(sa + (idx / (kColsWG / 8)) * kPitch + 16 * (idx % (kColsWG / 8))) = av[it];
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+
+  char* stg = so + wave * 32 * kStagePitch;
 #pragma unroll
   for (int bb = 0; bb < kTilesK / 2; ++bb) {
     // uniform per workgroup (K is a multiple of 64); rows past N still run the MFMAs and the
@@ -153,8 +172,6 @@ __global__ __launch_bounds__(kThreads) void k_merge(const uint32_t* __restrict__
 #pragma unroll
       for (int c = 0; c < RC; ++c) acc = mfma32(tr32_operand(sa + 16 * c * kPitch + 64 * i, lane), bop[c], acc);
       const uint32_t words[4] = {cw[i].x, cw[i].y, cw[i].z, cw[i].w};
-      uint16_t* dst = out + n * K + k0 + 32 * i + 4 * h32;
-      if (!row_ok) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         uint32_t p01, p23;
@@ -163,9 +180,25 @@ __global__ __launch_bounds__(kThreads) void k_merge(const uint32_t* __restrict__
         const float v1 = fmaf(s, acc[4 * q + 1], bf16hi_to_f32(p01));
         const float v2 = fmaf(s, acc[4 * q + 2], bf16lo_to_f32(p23));
         const float v3 = fmaf(s, acc[4 * q + 3], bf16hi_to_f32(p23));
-        *reinterpret_cast<uint2*>(dst + 8 * q) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+        *reinterpret_cast<uint2*>(stg + l32 * kStagePitch + 2 * (32 * half + 8 * q + 4 * h32)) =
+            make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
       }
     }
+    // the wavefront's 32 x 64 block goes out as 8 full 128-byte row segments per store,
+    // bypassing the caches on the way (the export is not read back here)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int row = 8 * t + (lane >> 3), ch = lane & 7;
+      const uint4 v = *reinterpret_cast<const uint4*>(stg + row * kStagePitch + 16 * ch);
+      const int64_t nr = (int64_t)blockIdx.y * kRowsWG + 32 * wave + row;
+      if (nr < N)
+        __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w},
+                                    reinterpret_cast<u32x4_t*>(out + nr * K + k0 + 64 * bb + 8 * ch));
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
