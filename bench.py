@@ -12,8 +12,9 @@ FLOPs per launch over its average duration from HIP events recorded on the launc
 inside the timed region -- only the two GEMM launches carry events there), a per-kernel
 breakdown from a separate fully instrumented pass, the M = 1 weight-stream rate of the
 same linear (128 distinct quantized copies rotated so every call reads HBM), the quantize
-rate, the merged-export rate (w_hat + s B A to BF16 over the same rotated copies), and the
-CPU oracle timed on a bounded sample of the same workload.
+rate, the merged-export rate (w_hat + s B A to BF16 over the same rotated copies), the
+AdamW step over the 41.9M adapter parameters of a Llama-3-8B-shaped model, and the CPU
+oracle timed on a bounded sample of the same workload.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
   python bench.py --pmc-pass    # 2 steps + a 256 MiB device copy, for counter runs
@@ -276,6 +277,29 @@ def main():
     del outs, cps, src32
     del copies
 
+    # ---- adapter optimizer step over the pages' 41.9M-parameter adapter set (one flat call)
+    na = I.LLAMA3_8B_ADAPTER_PARAMS
+    st_master, st_m, st_v, st_g = (t.to(dev) for t in I.optimizer_state(1, na))
+    st_p = torch.empty(na, dtype=torch.bfloat16, device=dev)
+    for t in range(1, 3):
+        Q.adamw_step(st_master, st_m, st_v, st_g, t, 2e-4, weight_decay=0.01, param=st_p)
+    torch.cuda.synchronize()
+    Q.timing_enable(True, kernels=("adamw",))
+    t0 = time.perf_counter()
+    for t in range(3, 13):
+        Q.adamw_step(st_master, st_m, st_v, st_g, t, 2e-4, weight_decay=0.01, param=st_p)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    aw_ms, aw_n = Q.timing_read("adamw")
+    Q.timing_enable(False)
+    aw_us = 1e3 * aw_ms / max(aw_n, 1)
+    ab = 28 * na  # FP32 master, m, v read and written (24 B), BF16 grad read, BF16 weight written
+    adamw = {"params": na, "bytes_per_call": ab, "kernel_avg_us": round(aw_us, 2),
+             "achieved_GBs": round(ab / (aw_us * 1e-6) / 1e9, 1), "peak_GBs": PEAK_HBM_GBS,
+             "frac": round(ab / (aw_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+             "us_per_call_eager_python": round(1e6 * (t1 - t0) / 10, 2)}
+    del st_master, st_m, st_v, st_g, st_p
+
     # ---- quantize (load time) of the same FP32 weight
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -306,6 +330,7 @@ def main():
         "weight_stream_M1": stream,
         "quantize_4096x4096": quant,
         "merge_4096x4096": merge,
+        "adamw_llama3_8b_adapters": adamw,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(N, K, r, alpha)

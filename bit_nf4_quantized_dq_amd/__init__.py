@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     quantize,
     quantize_bf16,
     merge,
+    adamw_step,
     dequantize,
     linear_fwd,
     linear_bwd,

@@ -25,6 +25,7 @@ KERNEL_IDS = {
     "lora_grad": 7,
     "dequant_t": 8,
     "merge": 9,
+    "adamw": 10,
 }
 
 
@@ -71,6 +72,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         "qlora_merge": (P(_Nf4dq), vp, vp, i32, ctypes.c_float, vp, vp),
         "qlora_linear_fwd": (P(_Nf4dq), vp, i64, vp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp),
         "qlora_linear_bwd": (P(_Nf4dq), vp, vp, i64, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp),
+        "qlora_adamw_step": (vp, vp, vp, vp, vp, i64, i64, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                             ctypes.c_float, ctypes.c_float, vp),
         "qlora_e4m3_encode": (vp, vp, i64, vp),
         "qlora_timing_enable": (ctypes.c_int,),
         "qlora_timing_read": (ctypes.c_int, P(ctypes.c_double), P(i64)),
@@ -279,6 +282,24 @@ def linear_bwd(q: QuantizedWeight, X: torch.Tensor, dY: torch.Tensor, A: torch.T
                                            _ptr(dX if need_dX else None), dA.data_ptr(), dB.data_ptr(),
                                            ws.data_ptr(), ws.numel(), _stream(X)), "linear_bwd")
     return (dX if need_dX else None), dA, dB
+
+
+def adamw_step(master: torch.Tensor, m: torch.Tensor, v: torch.Tensor, grad: torch.Tensor, step: int, lr: float,
+               beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8, weight_decay: float = 0.0,
+               param: torch.Tensor | None = None) -> None:
+    """One AdamW step, in place, over flat FP32 master/m/v with a BF16 gradient; writes the
+    BF16 working copy into `param` when given."""
+    for t, n in ((master, "master"), (m, "m"), (v, "v")):
+        _dev(t, torch.float32, n)
+    _dev(grad, torch.bfloat16, "grad")
+    if param is not None:
+        _dev(param, torch.bfloat16, "param")
+    n = master.numel()
+    if any(t.numel() != n for t in (m, v, grad)) or (param is not None and param.numel() != n):
+        raise ValueError("adamw_step: all buffers need the same number of elements")
+    _check(load_library().qlora_adamw_step(master.data_ptr(), m.data_ptr(), v.data_ptr(), grad.data_ptr(),
+                                           _ptr(param), n, int(step), float(lr), float(beta1), float(beta2),
+                                           float(eps), float(weight_decay), _stream(master)), "adamw_step")
 
 
 def e4m3_encode(x: torch.Tensor) -> torch.Tensor:

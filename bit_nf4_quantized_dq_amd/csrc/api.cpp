@@ -383,6 +383,31 @@ int qlora_linear_bwd(const qlora_nf4dq_t* Wq, const uint16_t* X, const uint16_t*
   return QLORA_OK;
 }
 
+int qlora_adamw_step(float* master, float* m, float* v, const uint16_t* grad, uint16_t* param, int64_t n,
+                     int64_t step, float lr, float beta1, float beta2, float eps, float weight_decay,
+                     hipStream_t stream) {
+  if (n < 0 || step < 1) return QLORA_ERR_INVALID_ARG;
+  if (!(std::isfinite(lr) && lr >= 0.f && beta1 >= 0.f && beta1 < 1.f && beta2 >= 0.f && beta2 < 1.f &&
+        std::isfinite(eps) && eps > 0.f && std::isfinite(weight_decay) && weight_decay >= 0.f))
+    return QLORA_ERR_INVALID_ARG;
+  if (n == 0) return QLORA_OK;
+  if (!master || !m || !v || !grad) return QLORA_ERR_INVALID_ARG;
+  if (!aligned16(master) || !aligned16(m) || !aligned16(v) || (reinterpret_cast<uintptr_t>(grad) & 7u) ||
+      (param && (reinterpret_cast<uintptr_t>(param) & 7u)))
+    return QLORA_ERR_INVALID_ARG;
+  const double t = (double)step, b1 = beta1, b2 = beta2;
+  AdamWScalars a;
+  a.decay = (float)(1.0 - (double)lr * (double)weight_decay);
+  a.b1 = beta1;
+  a.omb1 = (float)(1.0 - b1);
+  a.b2 = beta2;
+  a.omb2 = (float)(1.0 - b2);
+  a.step_size = (float)((double)lr / (1.0 - std::pow(b1, t)));
+  a.inv_bc2_sqrt = (float)(1.0 / std::sqrt(1.0 - std::pow(b2, t)));
+  a.eps = eps;
+  return hip_status(launch_adamw(master, m, v, grad, param, n, a, stream));
+}
+
 int qlora_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream) {
   if (!in || !out || n < 0) return QLORA_ERR_INVALID_ARG;
   if (n == 0) return QLORA_OK;

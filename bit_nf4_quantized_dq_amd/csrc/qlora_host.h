@@ -43,6 +43,18 @@ hipError_t launch_merge(const uint32_t* codes, const uint8_t* code8, const float
                         const uint16_t* A, const uint16_t* B, int64_t N, int64_t K, int32_t r, float s,
                         uint16_t* out, const Nf4Tables& T, hipStream_t st);
 
+// ---- adapter optimizer step (adamw.hip): scalars formed on the host in FP64, rounded once
+struct AdamWScalars {
+  float decay;         // 1 - lr * weight_decay
+  float b1, omb1;      // beta1, 1 - beta1
+  float b2, omb2;      // beta2, 1 - beta2
+  float step_size;     // lr / (1 - beta1^t)
+  float inv_bc2_sqrt;  // 1 / sqrt(1 - beta2^t)
+  float eps;
+};
+hipError_t launch_adamw(float* master, float* m, float* v, const uint16_t* grad, uint16_t* param, int64_t n,
+                        const AdamWScalars& a, hipStream_t s);
+
 // ---- LoRA skinny kernels (lora.hip)
 // out[m][j] = sum_k P[m][k] Q(j, k) for j < R, Q [R, Kd] (q_transposed = 0) or [Kd, R] (1);
 // out_s = bf16(scale * sum), out_u = bf16(sum), BF16 [M, R], either may be null.

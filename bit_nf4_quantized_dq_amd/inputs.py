@@ -99,3 +99,20 @@ def linear_case(cfg: int, linear_idx: int, d_out: int, d_in: int, M: int, r: int
         B=lora_B(cfg, linear_idx, d_out, r, layer, device),
         dY=grad_out(cfg, linear_idx, M, d_out, layer, device),
     )
+
+
+# Trainable adapter parameters of the Llama-3-8B layer shapes above with r = 16 on all seven
+# linears, over 32 layers: 32 * 16 * sum(d_out + d_in) = 41,943,040 (the pages' 41.9M).
+LLAMA3_8B_ADAPTER_PARAMS = 32 * 16 * sum(s.d_out + s.d_in for s in LLAMA3_8B_LAYER)
+
+
+def optimizer_state(seed: int, n: int, device="cpu"):
+    """Flat AdamW inputs for n adapter parameters: FP32 master ~ N(0, 0.02^2), FP32 first
+    moment ~ N(0, (1e-3)^2), FP32 second moment ~ U(0, 1e-6), BF16 gradient ~ N(0, (1e-3)^2)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    master = torch.randn(n, generator=g, device=device) * 0.02
+    m = torch.randn(n, generator=g, device=device) * 1e-3
+    v = torch.rand(n, generator=g, device=device) * 1e-6
+    grad = (torch.randn(n, generator=g, device=device) * 1e-3).to(torch.bfloat16)
+    return master, m, v, grad

@@ -161,6 +161,26 @@ int qlora_linear_bwd(const qlora_nf4dq_t *Wq, const uint16_t *X, const uint16_t 
                      const uint16_t *T_saved, uint16_t *dX, uint16_t *dA, uint16_t *dB, void *ws,
                      size_t ws_bytes, hipStream_t stream);
 
+/* One AdamW step over a flat array of n trainable adapter parameters (all of a model's A
+ * and B laid end to end, so one call updates them all).  The pages keep, per trainable
+ * parameter, an FP32 master weight and FP32 first and second moments (12 bytes) beside the
+ * 16-bit weight and 16-bit gradient ("QLoRA: Quantize Base Weights to 4-Bit", Section 1 and
+ * Section 4's optimizer term; "QLoRA -- Fine-Tuning a 65B Model on One GPU", "Paged
+ * optimizers"); the update is the published AdamW with decoupled, lr-scaled decay:
+ *   theta *= 1 - lr*wd;  m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;
+ *   theta -= lr/(1-b1^step) * m / (sqrt(v)/sqrt(1-b2^step) + eps);  param = bf16_rne(theta)
+ *   master, m, v : device float[n], updated in place, 16-byte aligned.
+ *   grad         : device BF16[n] (e.g. the dA / dB written by qlora_linear_bwd into slices
+ *                  of one flat buffer), 8-byte aligned.
+ *   param        : device BF16[n] working copy, overwritten; may be NULL; 8-byte aligned.
+ *   step         : 1 for the first step (bias correction).
+ * Paging of the states to host memory is not done.  n == 0 is a no-op.
+ * Errors: INVALID_ARG (n < 0, step < 1, null or misaligned pointer, lr < 0, beta outside
+ * [0, 1), eps <= 0, weight_decay < 0, a non-finite scalar), HIP. */
+int qlora_adamw_step(float *master, float *m, float *v, const uint16_t *grad, uint16_t *param,
+                     int64_t n, int64_t step, float lr, float beta1, float beta2, float eps,
+                     float weight_decay, hipStream_t stream);
+
 /* Diagnostic: the device E4M3 encoder used by qlora_quantize, applied elementwise to n
  * floats (device in, device out), so it can be checked exhaustively.  |in| <= 448 is
  * rounded to nearest, ties to even; larger magnitudes go to 448.  Errors: INVALID_ARG, HIP. */
@@ -184,7 +204,8 @@ enum qlora_kernel_id {
   QLORA_K_LORA_GRAD = 7,   /* dA and dB */
   QLORA_K_DEQUANT_T = 8,   /* BF16 w_hat^T, the dX copy for M >= 1024 */
   QLORA_K_MERGE = 9,       /* merged export w_hat + s B A */
-  QLORA_K_COUNT = 10
+  QLORA_K_ADAMW = 10,      /* adapter optimizer step */
+  QLORA_K_COUNT = 11
 };
 int qlora_timing_enable(int kernel_mask);
 int qlora_timing_read(int kernel_id, double *total_ms, int64_t *launches);

@@ -39,4 +39,5 @@ from .qlora_oracle import (  # noqa: F401
     bf16_round_f64_bits,
     merge,
     quantize_bf16,
+    adamw_step,
 )

@@ -399,3 +399,42 @@ def quantize_bf16(W_bits: np.ndarray, blocks: np.ndarray | None = None) -> dict:
     so this is :func:`quantize` of the widened values: the 16-bit checkpoint a model ships
     in is quantized as it stands ([4-Bit] Sec. 1: the frozen base lives in 16 bits)."""
     return quantize(bf16_bits_to_f32(W_bits), blocks)
+
+
+# --------------------------------------------------------------------------------------
+# Adapter optimizer step: AdamW with FP32 master weights and moments
+# --------------------------------------------------------------------------------------
+
+
+def adamw_step(master: np.ndarray, m: np.ndarray, v: np.ndarray, grad_bits: np.ndarray, step: int,
+               lr: float, beta1: float, beta2: float, eps: float, weight_decay: float):
+    """One AdamW step over flat adapter parameters.
+
+    State layout from the pages: every trainable parameter keeps an FP32 master copy, an
+    FP32 first moment and an FP32 second moment (12 bytes), next to the 16-bit weight and
+    16-bit gradient ("QLoRA: Quantize Base Weights to 4-Bit", Section 1 and Section 4's
+    optimizer term; "QLoRA -- Fine-Tuning a 65B Model on One GPU", "Paged optimizers").
+    The pages name AdamW but do not print it; the update is the published one
+    (Loshchilov and Hutter, "Decoupled Weight Decay Regularization", ICLR 2019, with the
+    bias correction of Kingma and Ba, "Adam", ICLR 2015), with the decay scaled by lr:
+      theta <- theta (1 - lr wd)
+      m <- b1 m + (1 - b1) g,   v <- b2 v + (1 - b2) g^2
+      theta <- theta - lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps)
+    g is the BF16 gradient widened exactly.  Arithmetic in FP64 from the FP32 inputs; the
+    three states are returned rounded to FP32 (their storage type) and the working weight
+    as BF16 bits of the new FP32 master.
+    Returns (master, m, v as float32; param BF16 bits; the FP64 master before rounding)."""
+    t = int(step)
+    assert t >= 1
+    th = np.asarray(master, np.float32).astype(np.float64)
+    m0 = np.asarray(m, np.float32).astype(np.float64)
+    v0 = np.asarray(v, np.float32).astype(np.float64)
+    g = bf16_bits_to_f32(grad_bits).astype(np.float64)
+    th = th * (1.0 - lr * weight_decay)
+    m1 = beta1 * m0 + (1.0 - beta1) * g
+    v1 = beta2 * v0 + (1.0 - beta2) * g * g
+    mhat = m1 / (1.0 - beta1**t)
+    vhat = v1 / (1.0 - beta2**t)
+    th = th - lr * mhat / (np.sqrt(vhat) + eps)
+    th32 = th.astype(np.float32)
+    return th32, m1.astype(np.float32), v1.astype(np.float32), bf16_round_bits(th32), th

@@ -24,7 +24,7 @@ def L():
 def test_every_declared_symbol_is_exported(L):
     text = open(HEADER).read()
     names = sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text)))
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(L, n), n
 
@@ -82,6 +82,18 @@ def test_shape_and_argument_errors_before_launch(L):
     assert L.qlora_merge(ctypes.byref(_wq()), dummy, dummy, 8, 16.0, ctypes.c_void_p(4098), None) == -1
     assert L.qlora_merge(ctypes.byref(_wq(d_out=250)), dummy, dummy, 8, 16.0, dummy, None) == -2
     assert L.qlora_merge(ctypes.byref(_wq(b1=32)), dummy, dummy, 8, 16.0, dummy, None) == -3
+    f = ctypes.c_float
+    ok = dict(lr=f(1e-3), b1=f(0.9), b2=f(0.999), eps=f(1e-8), wd=f(0.0))
+    def adamw(master=dummy, g=dummy, p=dummy, n=16, step=1, **kw):
+        a = dict(ok, **{k: f(x) for k, x in kw.items()})
+        return L.qlora_adamw_step(master, dummy, dummy, g, p, n, step, a["lr"], a["b1"], a["b2"], a["eps"], a["wd"], None)
+    assert adamw(n=0) == 0 and adamw(master=None, n=0) == 0  # no-op
+    assert adamw(n=-1) == -1 and adamw(step=0) == -1
+    assert adamw(master=None) == -1 and adamw(g=None) == -1
+    assert adamw(master=ctypes.c_void_p(4100)) == -1 and adamw(g=ctypes.c_void_p(4098)) == -1
+    assert adamw(p=ctypes.c_void_p(4098)) == -1
+    assert adamw(lr=-1.0) == -1 and adamw(lr=float("nan")) == -1 and adamw(b1=1.0) == -1 and adamw(b2=-0.1) == -1
+    assert adamw(eps=0.0) == -1 and adamw(wd=-0.5) == -1 and adamw(wd=float("inf")) == -1
 
 
 def test_workspace_sizes_are_sane():

@@ -448,3 +448,61 @@ def test_requantize_unchanged_special_weight_restores_codes():
     q2 = O.quantize_bf16(bits)
     assert np.array_equal(q2["codes"], q["codes"]) and np.array_equal(q2["codes"], k.astype(np.uint8))
     assert q2["mu"] == c and np.array_equal(q2["code8"], q["code8"]) and np.array_equal(q2["c2s"], q["c2s"])
+
+
+# ------------------------------------------------------------------ adapter optimizer step
+
+def _bf16_bits(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("step,wd", [(1, 0.0), (7, 0.01), (1000, 0.1)])
+def test_adamw_matches_torch_adamw(step, wd):
+    """One step from a given state equals torch.optim.AdamW in float64 (a separate
+    implementation of the same published update)."""
+    rng = np.random.default_rng(30 + step)
+    n = 999
+    master = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    v = (rng.random(n) * 1e-6).astype(np.float32)
+    g = _bf16_bits(rng.standard_normal(n) * 1e-3)
+    lr, b1, b2, eps = 2e-4, 0.9, 0.999, 1e-8
+    th32, m32, v32, pbits, th = O.adamw_step(master, m, v, g, step, lr, b1, b2, eps, wd)
+    p = torch.tensor(master.astype(np.float64), requires_grad=True)
+    opt = torch.optim.AdamW([p], lr=lr, betas=(b1, b2), eps=eps, weight_decay=wd, foreach=False)
+    opt.state[p] = {"step": torch.tensor(float(step - 1), dtype=torch.float64),
+                    "exp_avg": torch.tensor(m.astype(np.float64)), "exp_avg_sq": torch.tensor(v.astype(np.float64))}
+    p.grad = torch.tensor(O.bf16_bits_to_f32(g).astype(np.float64))
+    opt.step()
+    assert np.allclose(th, p.detach().numpy(), rtol=1e-12, atol=1e-18)
+    assert np.allclose(m32, opt.state[p]["exp_avg"].numpy(), rtol=1e-6, atol=0)
+    assert np.allclose(v32, opt.state[p]["exp_avg_sq"].numpy(), rtol=1e-6, atol=0)
+    assert np.array_equal(pbits, _bf16_bits(th32))
+
+
+def test_adamw_constant_gradient_closed_form():
+    """With a constant gradient c, no decay and zero initial moments, the bias-corrected
+    moments are exactly c and c^2, so every step moves theta by lr |c| / (|c| + eps)
+    against the sign of c."""
+    n = 64
+    rng = np.random.default_rng(40)
+    c = rng.choice([-1.0, 1.0], n) * 2.0 ** rng.integers(-12, -4, n)
+    g = _bf16_bits(c)
+    th0 = (rng.standard_normal(n) * 0.05).astype(np.float32)
+    th, m, v = th0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    lr, eps = 1e-3, 1e-8
+    for t in range(1, 6):
+        th, m, v, _, _ = O.adamw_step(th, m, v, g, t, lr, 0.9, 0.999, eps, 0.0)
+    exp = th0.astype(np.float64) - 5 * lr * np.sign(c) * np.abs(c) / (np.abs(c) + eps)
+    assert np.allclose(th, exp, rtol=0, atol=2e-7 * 5 * lr + 5 * 2.0**-24 * np.abs(exp))
+
+
+def test_adamw_pure_decay():
+    n = 32
+    th0 = np.linspace(-1, 1, n).astype(np.float32)
+    th, m, v = th0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    g = np.zeros(n, np.uint16)
+    for t in range(1, 4):
+        th, m, v, _, _ = O.adamw_step(th, m, v, g, t, 0.01, 0.9, 0.999, 1e-8, 0.5)
+    assert np.all(m == 0) and np.all(v == 0)
+    assert np.allclose(th, th0.astype(np.float64) * (1 - 0.005) ** 3, rtol=1e-6)
