@@ -17,7 +17,8 @@ AdamW step over the 41.9M adapter parameters of a Llama-3-8B-shaped model, and t
 oracle timed on a bounded sample of the same workload.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
-  python bench.py --pmc-pass    # 2 steps + a 256 MiB device copy, for counter runs
+  python bench.py --pmc-pass    # 2 steps, one merge, one AdamW step and a 256 MiB device
+                                # copy (the counter calibration), for counter runs
 """
 
 from __future__ import annotations
@@ -31,6 +32,37 @@ import time
 METRIC = "NF4+DQ linear fwd+bwd TFLOP/s at M=4096; weight-stream GB/s at M=1"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+
+
+# HBM bytes per launch from two rocprofv3 counter passes of `bench.py --pmc-pass`
+# (FETCH_SIZE scaled by 2.0 and WRITE_SIZE by 1.0, the factors that make a plain 256 MiB
+# device copy read and write 256 MiB).  A figure holds only for the kernel source it was
+# taken on: when that file's SHA-1 differs, the traffic is reported as null.
+COUNTER_TRAFFIC = {
+    "gemm_nt": {"source": "bit_nf4_quantized_dq_amd/csrc/gemm_nt.hip",
+                "sha1": "55a5847c5dd297270656fa3947bbba1b45dd78ec",
+                "read_bytes": 303_434_547, "write_bytes": 33_554_432},
+    "merge": {"source": "bit_nf4_quantized_dq_amd/csrc/merge.hip",
+              "sha1": "ed2a116b67d462d7e3501d8ca7652e1d8ca9ec4b",
+              "read_bytes": 11_907_993, "write_bytes": 33_554_688},
+    "adamw": {"source": "bit_nf4_quantized_dq_amd/csrc/adamw.hip",
+              "sha1": "513130524f3da5219d61f8dcabd1c76bb0828e6f",
+              "read_bytes": 587_279_872, "write_bytes": 587_202_560},
+}
+
+
+def counter_traffic(kernel):
+    import hashlib
+
+    rec = COUNTER_TRAFFIC[kernel]
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), rec["source"])
+    try:
+        with open(path, "rb") as f:
+            if hashlib.sha1(f.read()).hexdigest() != rec["sha1"]:
+                return None
+    except OSError:
+        return None
+    return rec["read_bytes"] + rec["write_bytes"]
 
 
 def step_flops(M, N, K, r):
@@ -96,7 +128,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-pass", action="store_true",
-                    help="run 2 steps and a plain 256 MiB device copy (the counter calibration), print nothing")
+                    help="run 2 steps, one merge, one AdamW step and a plain 256 MiB device copy (the counter "
+                         "calibration), print nothing")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
@@ -133,6 +166,14 @@ def main():
     if args.pmc_pass:
         step()
         step()
+        wm = torch.empty(N, K, dtype=torch.bfloat16, device=dev)
+        Q.merge(q, A, B, alpha, out=wm)
+        del wm
+        na = I.LLAMA3_8B_ADAPTER_PARAMS
+        st = [t.to(dev) for t in I.optimizer_state(1, na)]
+        Q.adamw_step(st[0], st[1], st[2], st[3], 1, 2e-4, weight_decay=0.01,
+                     param=torch.empty(na, dtype=torch.bfloat16, device=dev))
+        del st
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         src.fill_(1)
@@ -180,7 +221,8 @@ def main():
     dom = max(kflops, key=lambda k: gemm_us[k])
     ach = kflops[dom] / (gemm_us[dom] * 1e-6) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": counter_traffic("gemm_nt"),
+                "traffic_algorithmic_bytes": 2 * (N * K + M * K + M * r + N * r) + 2 * M * N,
                 "algorithmic_flops_per_launch": kflops[dom], "avg_us": round(gemm_us[dom], 2),
                 "other_gemm_avg_us": {k: round(v, 2) for k, v in gemm_us.items() if k != dom}}
 
@@ -258,7 +300,7 @@ def main():
     Q.timing_enable(False)
     mb = merge_bytes(N, K, r)
     mg_us = 1e3 * mg_ms / max(mg_n, 1)
-    merge = {"bytes_per_call": mb, "kernel_avg_us": round(mg_us, 2),
+    merge = {"bytes_per_call": mb, "traffic": counter_traffic("merge"), "kernel_avg_us": round(mg_us, 2),
              "achieved_GBs": round(mb / (mg_us * 1e-6) / 1e9, 1), "peak_GBs": PEAK_HBM_GBS,
              "frac": round(mb / (mg_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
              "us_per_call_eager_python": round(1e6 * (t1 - t0) / len(copies), 2)}
@@ -294,7 +336,7 @@ def main():
     Q.timing_enable(False)
     aw_us = 1e3 * aw_ms / max(aw_n, 1)
     ab = 28 * na  # FP32 master, m, v read and written (24 B), BF16 grad read, BF16 weight written
-    adamw = {"params": na, "bytes_per_call": ab, "kernel_avg_us": round(aw_us, 2),
+    adamw = {"params": na, "bytes_per_call": ab, "traffic": counter_traffic("adamw"), "kernel_avg_us": round(aw_us, 2),
              "achieved_GBs": round(ab / (aw_us * 1e-6) / 1e9, 1), "peak_GBs": PEAK_HBM_GBS,
              "frac": round(ab / (aw_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
              "us_per_call_eager_python": round(1e6 * (t1 - t0) / 10, 2)}

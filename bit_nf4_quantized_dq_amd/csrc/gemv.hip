@@ -13,8 +13,9 @@
 // [16g, 16g+16), g = l >> 4.  Two MFMA 16x16x32 steps cover a block; all 32 reduction
 // indices of each step lie in that block, so its constant c1_hat multiplies the 16x16
 // partial product once, in FP32, before it joins the accumulator.  The 16 levels are looked
-// up unscaled (BF16) with byte permutes.  Loops stay rolled: each workgroup runs the code
-// once, so a compact instruction stream matters as much as the memory stream.
+// up unscaled (BF16) with byte permutes.  The block loop over a staged chunk is unrolled
+// without bounds tests: blocks past the end of the slice hold zero activations (and finite
+// decoded weights), so they add exact zeros.
 //
 // Adapter.  T = X A^T is linear in the reduction range, so each workgroup forms the part of
 // T over its own k-range (its wavefronts take interleaved blocks), applies B to it for its
