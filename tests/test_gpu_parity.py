@@ -159,6 +159,11 @@ FB_CASES = [
     (9, 1040, 192, 513, 8, 16.0),
     (9, 64, 2048, 100, 128, 256.0),
     (9, 2048, 64, 40, 3, 6.0),
+    # M <= 16: more adapter ranks and reduction splits
+    (9, 528, 192, 3, 40, 80.0),     # r not a multiple of 8
+    (9, 64, 2048, 2, 128, 256.0),   # the largest rank
+    (9, 1040, 4096, 1, 5, 10.0),    # ragged rank tile, a deep reduction split
+    (9, 16, 64, 16, 16, 32.0),      # a single row group, a single block per row
     # M >= 1024: decoded weight copy + plain BF16 GEMM
     (9, 272, 320, 1100, 16, 32.0),  # ragged M and N; the dX reduction (over N) ends mid-step
     (9, 528, 192, 1025, 40, 80.0),  # two adapter slices, r not a multiple of 8
@@ -295,3 +300,46 @@ def test_config4_llama3_8b_layer_sampled(gpu_lib, idx):
     assert normwise(_f64(dA), s * G_ref.T @ Xf) <= TOL
     assert normwise(_f64(dB), s * dYf.T @ T_ref) <= TOL
     assert normwise(_f64(T), T_ref) <= TOL
+
+
+def test_weight_stream_graph_replay(gpu_lib):
+    """The M <= 16 path captured in a HIP graph and replayed with new inputs in between:
+    every replay equals an eager call on the same inputs (the split-K arrival counters
+    carry no per-call host state)."""
+    from bit_nf4_quantized_dq_amd import QuantizedWeight, linear_fwd, quantize, workspace_size, OP_FWD
+
+    dev = torch.device("cuda")
+    shapes = [(1040, 4096, 1, 16), (272, 320, 16, 16), (4096, 4096, 16, 16)]
+    cases = []
+    for i, (N, K, M, r) in enumerate(shapes):
+        c = _case(9, N, K, M, r, 0.02, idx=10 + i)
+        q = quantize(c["W"].to(dev))
+        X = c["X"].to(dev)
+        A, B = c["A"].to(dev), c["B"].to(dev)
+        Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(workspace_size(OP_FWD, M, N, K, r), dtype=torch.uint8, device=dev)
+        cases.append((q, X, A, B, Y, ws))
+    for q, X, A, B, Y, ws in cases:  # warm-up outside the capture
+        linear_fwd(q, X, A, B, 32.0, Y=Y, ws=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            for q, X, A, B, Y, ws in cases:
+                linear_fwd(q, X, A, B, 32.0, Y=Y, ws=ws)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cpu").manual_seed(77)
+    for rep in range(4):
+        for q, X, A, B, Y, ws in cases:
+            X.copy_(torch.randn(X.shape, generator=gen).to(torch.bfloat16))
+            A.copy_((torch.randn(A.shape, generator=gen) * 0.02).to(torch.bfloat16))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [Y.clone() for *_, Y, _ in cases]
+        for (q, X, A, B, Y, ws), yg in zip(cases, got):
+            ye = linear_fwd(q, X, A, B, 32.0)
+            torch.cuda.synchronize()
+            assert torch.equal(ye.view(torch.int16), yg.view(torch.int16)), f"replay {rep}"
