@@ -79,7 +79,7 @@ FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
 }
 
 struct BwdWs {
-  size_t t, g, lg, at, cpa, cpb, wcopy, total;
+  size_t t, g, lg, cpa, cpb, wcopy, total;
 };
 BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   BwdWs w{};
@@ -90,8 +90,6 @@ BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   off = align_up(off + 2 * M * r, 256);
   w.lg = off;
   off = align_up(off + 2 * M * r, 256);
-  w.at = off;
-  off = align_up(off + 2 * (size_t)r * K, 256);
   w.cpa = off;  // dA and dB run concurrently: separate partials
   off = align_up(off + sizeof(float) * (int64_t)lora_grad_msplit(M, K) * r * K, 256);
   w.cpb = off;
@@ -365,12 +363,10 @@ int qlora_linear_bwd(const qlora_nf4dq_t* Wq, const uint16_t* X, const uint16_t*
   // dX = dY w_hat + (s G) A
   if (dX && M >= kNtMinM) {
     uint16_t* wcopy = reinterpret_cast<uint16_t*>(base + L.wcopy);
-    uint16_t* at = reinterpret_cast<uint16_t*>(base + L.at);
     if ((e = launch_dequant_t(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, wcopy, nf4_tables(), stream)) != hipSuccess)
       return QLORA_ERR_HIP;
-    if ((e = launch_transpose_bf16(A, r, K, at, stream)) != hipSuccess) return QLORA_ERR_HIP;
-    // A = w_hat^T [K, N], Wl = A^T [K, r] (staged row-contiguous)
-    if ((e = launch_gemm_nt(wcopy, K, dY, M, N, at, r, 1, lg, r, dX, QLORA_K_GEMM_DX, stream)) != hipSuccess)
+    // A = w_hat^T [K, N], Wl(f, j) = A[j][f]: read in place from A [r, K] (f*1 + j*K)
+    if ((e = launch_gemm_nt(wcopy, K, dY, M, N, A, 1, K, lg, r, dX, QLORA_K_GEMM_DX, stream)) != hipSuccess)
       return QLORA_ERR_HIP;
   } else if (dX) {
     if ((e = launch_gemm_dx(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, dY, M, lg, A, r, dX, nf4_tables(), stream)) !=

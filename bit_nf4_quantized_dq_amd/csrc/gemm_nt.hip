@@ -142,9 +142,10 @@ __device__ __forceinline__ void mma_step(const uint4* __restrict__ sa, const uin
 
 // Adapter slices of 32: acc[f][m] += sum_j Wl(f, j) * L[m][j] for j < r, Wl(f, j) at
 // f*wl_fs + j*wl_js (elements), L [M, r] row-major, staged through slot 4.  Threads 0-255
-// load feature row f0 + t, threads 256-511 token row m0 + t - 256.  When both are
-// row-contiguous with r % 8 == 0 a thread moves whole 16-byte chunks; otherwise element by
-// element (any r, any stride).
+// load feature row f0 + t, threads 256-511 token row m0 + t - 256.  A side whose rows are
+// contiguous with r % 8 == 0 moves whole 16-byte chunks; otherwise element by element (any
+// r, any stride: a transposed Wl such as A^T read straight from A [r, F] costs no extra
+// launch, and its element loads are coalesced across the 256 feature threads).
 __device__ __forceinline__ void adapter(const uint16_t* __restrict__ wl, int64_t wl_fs, int64_t wl_js, int64_t F,
                                         const uint16_t* __restrict__ Lm, int64_t M, int32_t r, int64_t f0, int64_t m0,
                                         int tid, int wf, int wmt, int l32, int h32, Acc& acc) {
@@ -152,7 +153,7 @@ __device__ __forceinline__ void adapter(const uint16_t* __restrict__ wl, int64_t
   const int row = wside ? tid : tid - 256;
   const rsrc_t rw = make_rsrc(wl, (F - 1) * wl_fs * 2 + (int64_t)r * wl_js * 2);
   const rsrc_t rm = make_rsrc(Lm, M * (int64_t)r * 2);
-  const bool vec = wl_js == 1 && wl_fs == r && (r & 7) == 0;
+  const bool vec = wside ? (wl_js == 1 && wl_fs == r && (r & 7) == 0) : ((r & 7) == 0);
   const int64_t f = f0 + row, m = m0 + row;
   const bool rok = wside ? f < F : m < M;
   const rsrc_t rr = wside ? rw : rm;

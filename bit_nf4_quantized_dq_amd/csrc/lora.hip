@@ -53,7 +53,7 @@ constexpr int kDownThreads = 512;
 constexpr int kDownWaves = kDownThreads / 64;
 
 // grid: ceil(M / (16 MT)).  JT = ceil(R / 16) tiles of outputs, all held by every wavefront.
-template <int JT, int MT, bool QT>
+template <int JT, int MT, bool QT, int D>
 __global__ __launch_bounds__(kDownThreads) void k_lora_down(const uint16_t* __restrict__ P,
                                                             const uint16_t* __restrict__ Q, int64_t M,
                                                             int32_t R, int64_t Kd, float scale,
@@ -76,50 +76,70 @@ __global__ __launch_bounds__(kDownThreads) void k_lora_down(const uint16_t* __re
     for (int u = 0; u < MT; ++u) acc[t][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   char* qs = smem + wave * JT * 1024;  // QT: this wavefront's slab, JT tiles of [32][16] BF16
   const int64_t nslab = (Kd + 31) / 32;
-  for (int64_t s = wave; s < nslab; s += kDownWaves) {
-    const int64_t k = 32 * s + kk;
-    const bool kok = k < Kd;
-    uint4 pv[MT];
+  // D slabs per pass (chosen at launch from the slabs per wavefront): all their global loads
+  // are issued before the first is used, and no register buffer is carried across passes
+  for (int64_t s0 = wave; s0 < nslab; s0 += (int64_t)kDownWaves * D) {
+    uint4 pv[D][MT];
+    uint4 qv[D][JT];
 #pragma unroll
-    for (int u = 0; u < MT; ++u) {
-      const int64_t row = 16 * u + (lane & 15);
-      pv[u] = bload16(rp, (kok && m0 + row < M) ? (uint32_t)((row * Kd + k) * 2) : kOOB);
-    }
-    bf16x8_t qa[JT];
-    if (!QT) {
+    for (int d = 0; d < D; ++d) {
+      const int64_t s = s0 + (int64_t)kDownWaves * d;
+      const int64_t k = 32 * s + kk;
+      const bool kok = s < nslab && k < Kd;
 #pragma unroll
-      for (int t = 0; t < JT; ++t) {
-        const int j = 16 * t + (lane & 15);
-        qa[t] = as_bf16x8(bload16(rq, (kok && j < R) ? (uint32_t)(((int64_t)j * Kd + k) * 2) : kOOB));
+      for (int u = 0; u < MT; ++u) {
+        const int64_t row = 16 * u + (lane & 15);
+        pv[d][u] = bload16(rp, (kok && m0 + row < M) ? (uint32_t)((row * Kd + k) * 2) : kOOB);
       }
-    } else {
-      // rows k = 32 s + (lane >> 1), columns 8 (lane & 1) .. +7 of every tile
-      const int64_t kr = 32 * s + (lane >> 1);
+      if (!QT) {
 #pragma unroll
-      for (int t = 0; t < JT; ++t) {
-        const int j = 16 * t + 8 * (lane & 1);
-        uint4 v;
-        if ((R & 7) == 0) {  // 16-byte rows pieces
-          v = bload16(rq, (kr < Kd && j < R) ? (uint32_t)((kr * R + j) * 2) : kOOB);
-        } else {
-          uint32_t e[8];
-#pragma unroll
-          for (int q = 0; q < 8; ++q)
-            e[q] = __builtin_amdgcn_raw_buffer_load_b16(rq, (kr < Kd && j + q < R) ? (int)((kr * R + j + q) * 2) : (int)kOOB, 0, 0);
-          v = make_uint4((e[0] & 0xFFFFu) | (e[1] << 16), (e[2] & 0xFFFFu) | (e[3] << 16), (e[4] & 0xFFFFu) | (e[5] << 16),
-                         (e[6] & 0xFFFFu) | (e[7] << 16));
+        for (int t = 0; t < JT; ++t) {
+          const int j = 16 * t + (lane & 15);
+          qv[d][t] = bload16(rq, (kok && j < R) ? (uint32_t)(((int64_t)j * Kd + k) * 2) : kOOB);
         }
-        *reinterpret_cast<uint4*>(qs + t * 1024 + (lane >> 1) * 32 + 16 * (lane & 1)) = v;
+      } else {
+        // rows k = 32 s + (lane >> 1), columns 8 (lane & 1) .. +7 of every tile
+        const int64_t kr = 32 * s + (lane >> 1);
+        const bool rok = s < nslab && kr < Kd;
+#pragma unroll
+        for (int t = 0; t < JT; ++t) {
+          const int j = 16 * t + 8 * (lane & 1);
+          if ((R & 7) == 0) {  // 16-byte row pieces
+            qv[d][t] = bload16(rq, (rok && j < R) ? (uint32_t)((kr * R + j) * 2) : kOOB);
+          } else {
+            uint32_t e[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+              e[q] = __builtin_amdgcn_raw_buffer_load_b16(rq, (rok && j + q < R) ? (int)((kr * R + j + q) * 2) : (int)kOOB, 0, 0);
+            qv[d][t] = make_uint4((e[0] & 0xFFFFu) | (e[1] << 16), (e[2] & 0xFFFFu) | (e[3] << 16),
+                                  (e[4] & 0xFFFFu) | (e[5] << 16), (e[6] & 0xFFFFu) | (e[7] << 16));
+          }
+        }
       }
-      asm volatile("" ::: "memory");
-#pragma unroll
-      for (int t = 0; t < JT; ++t) qa[t] = tr_operand(qs + t * 1024, 32, lane);
-      asm volatile("" ::: "memory");
     }
+    // Every slab of the pass is used, also those past the end (their loads read as zero), so
+    // no load sits behind a branch that the compiler could sink it into.
 #pragma unroll
-    for (int t = 0; t < JT; ++t)
+    for (int d = 0; d < D; ++d) {
+      bf16x8_t qa[JT];
+      if (!QT) {
 #pragma unroll
-      for (int u = 0; u < MT; ++u) acc[t][u] = mfma16x16x32(qa[t], as_bf16x8(pv[u]), acc[t][u]);
+        for (int t = 0; t < JT; ++t) qa[t] = as_bf16x8(qv[d][t]);
+      } else {
+        // the wavefront's LDS tiles are reused slab after slab; its LDS accesses run in order
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int t = 0; t < JT; ++t) *reinterpret_cast<uint4*>(qs + t * 1024 + (lane >> 1) * 32 + 16 * (lane & 1)) = qv[d][t];
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int t = 0; t < JT; ++t) qa[t] = tr_operand(qs + t * 1024, 32, lane);
+        asm volatile("" ::: "memory");
+      }
+#pragma unroll
+      for (int t = 0; t < JT; ++t)
+#pragma unroll
+        for (int u = 0; u < MT; ++u) acc[t][u] = mfma16x16x32(qa[t], as_bf16x8(pv[d][u]), acc[t][u]);
+    }
   }
   // fixed-order sum over the wavefronts
   __syncthreads();
@@ -156,7 +176,7 @@ constexpr int kGradCols = 64;      // columns per workgroup (4 tiles of 16)
 constexpr int kVTile = 32 * 32 + 64;  // bytes per staged [32][16] BF16 tile, padded (bank offset)
 
 // grid (ceil(C / 64), msplit).  JT = ceil(R / 16).  part: [msplit][R][C] FP32 (msplit > 1).
-template <int JT>
+template <int JT, int D>
 __global__ __launch_bounds__(kGradThreads) void k_lora_grad(const uint16_t* __restrict__ U,
                                                             const uint16_t* __restrict__ V, int64_t M,
                                                             int32_t R, int64_t C, int64_t mps, float scale,
@@ -181,49 +201,63 @@ __global__ __launch_bounds__(kGradThreads) void k_lora_grad(const uint16_t* __re
   for (int t = 0; t < JT; ++t)
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[t][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // wavefront w takes chunks of 32 tokens mbeg + 32 (w + 4 i)
-  for (int64_t mc = mbeg + 32 * wave; mc < mend; mc += 32 * kGradWaves) {
-    // V chunk [32][64]: 4 loads; lane -> row 8 i + (lane >> 3), columns 8 (lane & 7) .. +7
-    uint4 vv[4];
+  // wavefront w takes chunks of 32 tokens mbeg + 32 (w + 4 i), D chunks per pass (chosen at
+  // launch from the chunks per wavefront): all their global loads are issued before the
+  // first chunk is staged, so D chunks stay in flight
+  const bool uvec = (R & 7) == 0;
+  for (int64_t mc0 = mbeg + 32 * wave; mc0 < mend; mc0 += (int64_t)32 * kGradWaves * D) {
+    uint4 vv[D][4];     // V chunk [32][64]: lane -> row 8 i + (lane >> 3), columns 8 (lane & 7) .. +7
+    uint4 uw[D][JT];    // U chunk [32][16 JT]: lane -> row lane >> 1, columns 16 t + 8 (lane & 1) .. +7
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t m = mc + 8 * i + (lane >> 3);
-      const int64_t c = c0 + 8 * (lane & 7);
-      vv[i] = bload16(rv, (m < mend && c < C) ? (uint32_t)((m * C + c) * 2) : kOOB);
-    }
-    // U chunk [32][16 JT]: element loads (any R)
-    uint32_t uu[JT][8];
+    for (int d = 0; d < D; ++d) {
+      const int64_t mc = mc0 + (int64_t)32 * kGradWaves * d;
 #pragma unroll
-    for (int t = 0; t < JT; ++t) {
+      for (int i = 0; i < 4; ++i) {
+        const int64_t m = mc + 8 * i + (lane >> 3);
+        const int64_t c = c0 + 8 * (lane & 7);
+        vv[d][i] = bload16(rv, (m < mend && c < C) ? (uint32_t)((m * C + c) * 2) : kOOB);
+      }
       const int64_t m = mc + (lane >> 1);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = 16 * t + 8 * (lane & 1) + e;
-        uu[t][e] = __builtin_amdgcn_raw_buffer_load_b16(ru, (m < mend && j < R) ? (int)((m * R + j) * 2) : (int)kOOB, 0, 0);
+      for (int t = 0; t < JT; ++t) {
+        const int j = 16 * t + 8 * (lane & 1);
+        if (uvec) {
+          uw[d][t] = bload16(ru, (m < mend && j < R) ? (uint32_t)((m * R + j) * 2) : kOOB);
+        } else {
+          uint32_t e[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            e[q] = __builtin_amdgcn_raw_buffer_load_b16(ru, (m < mend && j + q < R) ? (int)((m * R + j + q) * 2) : (int)kOOB, 0, 0);
+          uw[d][t] = make_uint4((e[0] & 0xFFFFu) | (e[1] << 16), (e[2] & 0xFFFFu) | (e[3] << 16),
+                                (e[4] & 0xFFFFu) | (e[5] << 16), (e[6] & 0xFFFFu) | (e[7] << 16));
+        }
       }
     }
+    // Every chunk of the pass is used, also those past the end (their loads read as zero),
+    // so no load sits behind a branch that the compiler could sink it into.
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 8 * i + (lane >> 3), ct = (lane & 7) >> 1, half = lane & 1;
-      *reinterpret_cast<uint4*>(vt + ct * kVTile + row * 32 + 16 * half) = vv[i];
+    for (int d = 0; d < D; ++d) {
+      // the wavefront's LDS tiles are reused chunk after chunk; its LDS accesses run in order
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 8 * i + (lane >> 3), ct = (lane & 7) >> 1, half = lane & 1;
+        *reinterpret_cast<uint4*>(vt + ct * kVTile + row * 32 + 16 * half) = vv[d][i];
+      }
+#pragma unroll
+      for (int t = 0; t < JT; ++t) *reinterpret_cast<uint4*>(ut + t * kVTile + (lane >> 1) * 32 + 16 * (lane & 1)) = uw[d][t];
+      asm volatile("" ::: "memory");
+      bf16x8_t a[JT], b[4];
+#pragma unroll
+      for (int t = 0; t < JT; ++t) a[t] = tr_operand(ut + t * kVTile, 32, lane);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) b[q] = tr_operand(vt + q * kVTile, 32, lane);
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int t = 0; t < JT; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[t][q] = mfma16x16x32(a[t], b[q], acc[t][q]);
     }
-#pragma unroll
-    for (int t = 0; t < JT; ++t) {
-      const uint4 w = make_uint4((uu[t][0] & 0xFFFFu) | (uu[t][1] << 16), (uu[t][2] & 0xFFFFu) | (uu[t][3] << 16),
-                                 (uu[t][4] & 0xFFFFu) | (uu[t][5] << 16), (uu[t][6] & 0xFFFFu) | (uu[t][7] << 16));
-      *reinterpret_cast<uint4*>(ut + t * kVTile + (lane >> 1) * 32 + 16 * (lane & 1)) = w;
-    }
-    asm volatile("" ::: "memory");
-    bf16x8_t a[JT], b[4];
-#pragma unroll
-    for (int t = 0; t < JT; ++t) a[t] = tr_operand(ut + t * kVTile, 32, lane);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) b[q] = tr_operand(vt + q * kVTile, 32, lane);
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int t = 0; t < JT; ++t)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) acc[t][q] = mfma16x16x32(a[t], b[q], acc[t][q]);
   }
   // fixed-order sum over the wavefronts: D[j][c], lane l holds j = 4 (l >> 4) + v, c = l & 15
   __syncthreads();
@@ -291,22 +325,6 @@ __global__ __launch_bounds__(kGradThreads) void k_lora_grad(const uint16_t* __re
   }
 }
 
-__global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restrict__ in, int64_t rows, int64_t cols,
-                                                        uint16_t* __restrict__ out) {
-  __shared__ uint16_t tile[32][33];
-  const int64_t r0 = (int64_t)blockIdx.y * 32, c0 = (int64_t)blockIdx.x * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
-  for (int y = ty; y < 32; y += 8) {
-    const int64_t r = r0 + y, c = c0 + tx;
-    tile[y][tx] = (r < rows && c < cols) ? in[r * cols + c] : (uint16_t)0;
-  }
-  __syncthreads();
-  for (int y = ty; y < 32; y += 8) {
-    const int64_t c = c0 + y, r = r0 + tx;  // out[c][r]
-    if (c < cols && r < rows) out[c * rows + r] = tile[tx][y];
-  }
-}
-
 // Device address of the arrival counters on the current device (looked up once per device).
 unsigned int* lora_counters() {
   static unsigned int* addr[64] = {nullptr};
@@ -320,13 +338,30 @@ unsigned int* lora_counters() {
   return addr[dev];
 }
 
+// Batch depth: slabs (or token chunks) per pass, at most the wavefront's share and at most
+// kMaxD (the register budget of the loads held at once).
+inline int batch_depth(int64_t per_wave, int max_d) {
+  int d = 1;
+  while (d < max_d && d < per_wave) d *= 2;
+  return d;
+}
+
 template <int JT, int MT, bool QT>
 hipError_t down_launch(const uint16_t* P, const uint16_t* Q, int64_t M, int32_t R, int64_t Kd, float scale,
                        uint16_t* out_s, uint16_t* out_u, hipStream_t s) {
   const int64_t grid = (M + 16 * MT - 1) / (16 * MT);
+  constexpr int kMaxD = (JT + MT <= 2) ? 16 : (JT + MT <= 3 ? 8 : (JT + MT <= 6 ? 4 : 2));  // <= 128 VGPRs
+  const int d = batch_depth(((Kd + 31) / 32 + kDownWaves - 1) / kDownWaves, kMaxD);
   LaunchTimer t(6, s);
-  hipExtLaunchKernelGGL((k_lora_down<JT, MT, QT>), dim3((unsigned)grid), dim3(kDownThreads), 0, s, t.start, t.stop, 0,
-                        P, Q, M, R, Kd, scale, out_s, out_u);
+  auto go = [&](auto kern) {
+    hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kDownThreads), 0, s, t.start, t.stop, 0, P, Q, M, R, Kd, scale,
+                          out_s, out_u);
+  };
+  if (d >= 16 && kMaxD >= 16) go(k_lora_down<JT, MT, QT, (kMaxD >= 16 ? 16 : 1)>);
+  else if (d >= 8 && kMaxD >= 8) go(k_lora_down<JT, MT, QT, (kMaxD >= 8 ? 8 : 1)>);
+  else if (d >= 4 && kMaxD >= 4) go(k_lora_down<JT, MT, QT, (kMaxD >= 4 ? 4 : 1)>);
+  else if (d >= 2) go(k_lora_down<JT, MT, QT, 2>);
+  else go(k_lora_down<JT, MT, QT, 1>);
   return hipGetLastError();
 }
 
@@ -338,9 +373,17 @@ hipError_t grad_launch(const uint16_t* U, const uint16_t* V, int64_t M, int32_t 
   unsigned int* counters = lora_counters();
   if (!counters) return hipErrorInvalidSymbol;
   counters += 65536 * counter_set;
+  constexpr int kMaxD = JT <= 2 ? 8 : (JT <= 4 ? 4 : 2);  // <= 192 VGPRs of loads
+  const int d = batch_depth((mps / 32 + kGradWaves - 1) / kGradWaves, kMaxD);
   LaunchTimer t(7, s);
-  hipExtLaunchKernelGGL(k_lora_grad<JT>, grid, dim3(kGradThreads), 0, s, t.start, t.stop, 0, U, V, M, R, C, mps, scale,
-                        transposed, part, counters, out);
+  auto go = [&](auto kern) {
+    hipExtLaunchKernelGGL(kern, grid, dim3(kGradThreads), 0, s, t.start, t.stop, 0, U, V, M, R, C, mps, scale, transposed,
+                          part, counters, out);
+  };
+  if (d >= 8 && kMaxD >= 8) go(k_lora_grad<JT, (kMaxD >= 8 ? 8 : 1)>);
+  else if (d >= 4 && kMaxD >= 4) go(k_lora_grad<JT, (kMaxD >= 4 ? 4 : 1)>);
+  else if (d >= 2) go(k_lora_grad<JT, 2>);
+  else go(k_lora_grad<JT, 1>);
   return hipGetLastError();
 }
 
@@ -376,12 +419,6 @@ hipError_t launch_lora_grad(const uint16_t* U, const uint16_t* V, int64_t M, int
   if (R <= 32) return grad_launch<2>(U, V, M, R, C, ms, mps, scale, transposed, part, counter_set, out, s);
   if (R <= 64) return grad_launch<4>(U, V, M, R, C, ms, mps, scale, transposed, part, counter_set, out, s);
   return grad_launch<8>(U, V, M, R, C, ms, mps, scale, transposed, part, counter_set, out, s);
-}
-
-hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out, hipStream_t s) {
-  dim3 grid((unsigned)((cols + 31) / 32), (unsigned)((rows + 31) / 32));
-  hipLaunchKernelGGL(k_transpose_bf16, grid, dim3(256), 0, s, in, rows, cols, out);
-  return hipGetLastError();
 }
 
 }  // namespace qlora

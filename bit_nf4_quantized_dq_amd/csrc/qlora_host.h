@@ -66,9 +66,6 @@ hipError_t launch_lora_down(const uint16_t* P, const uint16_t* Q, int q_transpos
 int32_t lora_grad_msplit(int64_t M, int64_t C);
 hipError_t launch_lora_grad(const uint16_t* U, const uint16_t* V, int64_t M, int32_t R, int64_t C, float scale,
                             int transposed, float* part, int counter_set, uint16_t* out, hipStream_t s);
-// BF16 transpose [rows, cols] -> [cols, rows].
-hipError_t launch_transpose_bf16(const uint16_t* in, int64_t rows, int64_t cols, uint16_t* out,
-                                 hipStream_t s);
 
 // ---- weight-streaming forward, M <= 16 (gemv.hip): one launch, split-K with FP32
 // partials part [ksplit][M][N] and tpart [ksplit][M][r] in the workspace.
