@@ -13,8 +13,9 @@ inside the timed region -- only the two GEMM launches carry events there), a per
 breakdown from a separate fully instrumented pass, the M = 1 weight-stream rate of the
 same linear (128 distinct quantized copies rotated so every call reads HBM), the quantize
 rate, the merged-export rate (w_hat + s B A to BF16 over the same rotated copies), the
-AdamW step over the 41.9M adapter parameters of a Llama-3-8B-shaped model, and the CPU
-oracle timed on a bounded sample of the same workload.
+AdamW step over the 41.9M adapter parameters of a Llama-3-8B-shaped model, an error study of
+the format variants (codebook x second-level format: bits/weight, reconstruction error,
+decode time), and the CPU oracle timed on a bounded sample of the same workload.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
   python bench.py --pmc-pass    # 2 steps, one merge, one AdamW step and a 256 MiB device
@@ -342,6 +343,27 @@ def main():
              "us_per_call_eager_python": round(1e6 * (t1 - t0) / 10, 2)}
     del st_master, st_m, st_v, st_g, st_p
 
+    # ---- format study: every codebook x second-level format on the same Gaussian weight:
+    # storage bits per weight, relative reconstruction MSE of the GPU's dequantized weight,
+    # and the decode kernel's time (cache-warm, HIP events)
+    study = {}
+    w_ms = float(torch.mean(W.double() ** 2))
+    for cb in Q.CODEBOOKS:
+        for dqf in Q.DQ_FORMATS:
+            qf = Q.quantize(W, codebook=cb, dq=dqf)
+            wd = Q.dequantize(qf)
+            Q.timing_enable(True, kernels=("dequant",))
+            for _ in range(5):
+                Q.dequantize(qf, out=wd)
+            torch.cuda.synchronize()
+            dms, dn = Q.timing_read("dequant")
+            Q.timing_enable(False)
+            nb = sum(Q.quant_sizes(N, K, dqf)) + (0 if dqf == "none" else 4)
+            study[f"{cb}/{dqf}"] = {"bits_per_weight": round(8.0 * nb / (N * K), 4),
+                                    "rel_mse": round(float(torch.mean((wd.double() - W.double()) ** 2)) / w_ms, 6),
+                                    "dequant_us": round(1e3 * dms / max(dn, 1), 2)}
+            del qf, wd
+
     # ---- quantize (load time) of the same FP32 weight
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -373,6 +395,7 @@ def main():
         "quantize_4096x4096": quant,
         "merge_4096x4096": merge,
         "adamw_llama3_8b_adapters": adamw,
+        "format_study_4096x4096": study,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(N, K, r, alpha)

@@ -11,6 +11,9 @@ from ._binding import (  # noqa: F401
     lib,
     load_library,
     nf4_codebook,
+    codebook,
+    CODEBOOKS,
+    DQ_FORMATS,
     quantize,
     quantize_bf16,
     merge,

@@ -14,6 +14,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libqlora_nf4.so")
 
 OP_QUANTIZE, OP_FWD, OP_BWD = 0, 1, 2
+CODEBOOKS = {"nf4": 0, "int4": 1, "fp4": 2}
+DQ_FORMATS = {"e4m3": 0, "e5m2": 1, "int8": 2, "none": 3}
 KERNEL_IDS = {
     "quant_pass1": 0,
     "quant_pass2": 1,
@@ -45,6 +47,8 @@ class _Nf4dq(ctypes.Structure):
         ("d_in", ctypes.c_int64),
         ("block1", ctypes.c_int32),
         ("block2", ctypes.c_int32),
+        ("codebook", ctypes.c_int32),
+        ("dq_format", ctypes.c_int32),
     ]
 
 
@@ -65,7 +69,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     sig = {
         "qlora_quant_sizes": (i64, i64, P(sz), P(sz), P(sz)),
         "qlora_workspace_size": (ctypes.c_int, i64, i64, i64, i32, P(sz)),
+        "qlora_workspace_size_fmt": (ctypes.c_int, i64, i64, i64, i32, ctypes.c_int, P(sz)),
+        "qlora_format_sizes": (i64, i64, ctypes.c_int, P(sz), P(sz), P(sz)),
         "qlora_nf4_codebook": (P(ctypes.c_float),),
+        "qlora_codebook": (ctypes.c_int, P(ctypes.c_float)),
         "qlora_quantize": (vp, P(_Nf4dq), P(ctypes.c_float), vp, sz, vp),
         "qlora_quantize_bf16": (vp, P(_Nf4dq), P(ctypes.c_float), vp, sz, vp),
         "qlora_dequantize": (P(_Nf4dq), vp, vp),
@@ -122,15 +129,17 @@ def _dev(t: torch.Tensor, dtype, name: str) -> None:
         raise ValueError(f"{name}: need a contiguous {dtype} CUDA tensor, got {t.dtype} on {t.device}")
 
 
-def quant_sizes(d_out: int, d_in: int) -> tuple[int, int, int]:
+def quant_sizes(d_out: int, d_in: int, dq: str = "e4m3") -> tuple[int, int, int]:
     a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
-    _check(load_library().qlora_quant_sizes(d_out, d_in, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)), "quant_sizes")
+    _check(load_library().qlora_format_sizes(d_out, d_in, DQ_FORMATS[dq], ctypes.byref(a), ctypes.byref(b),
+                                             ctypes.byref(c)), "quant_sizes")
     return a.value, b.value, c.value
 
 
-def workspace_size(op: int, M: int, d_out: int, d_in: int, r: int) -> int:
+def workspace_size(op: int, M: int, d_out: int, d_in: int, r: int, dq: str = "e4m3") -> int:
     n = ctypes.c_size_t()
-    _check(load_library().qlora_workspace_size(op, M, d_out, d_in, r, ctypes.byref(n)), "workspace_size")
+    _check(load_library().qlora_workspace_size_fmt(op, M, d_out, d_in, r, DQ_FORMATS[dq], ctypes.byref(n)),
+           "workspace_size")
     return n.value
 
 
@@ -140,35 +149,50 @@ def nf4_codebook() -> list[float]:
     return list(arr)
 
 
+def codebook(name: str = "nf4") -> list[float]:
+    arr = (ctypes.c_float * 16)()
+    _check(load_library().qlora_codebook(CODEBOOKS[name], arr), "codebook")
+    return list(arr)
+
+
 @dataclasses.dataclass
 class QuantizedWeight:
     """Device buffers of one NF4 + DQ tensor (owned by these torch tensors)."""
 
     codes: torch.Tensor  # uint8 [d_out * d_in / 2]
-    code8: torch.Tensor  # uint8 [d_out * d_in / 64]
-    c2s: torch.Tensor  # float32 [ceil(n_blocks / 256)]
+    code8: torch.Tensor  # uint8 [d_out * d_in / 64] (uint8 [4 * ...] holding FP32 when dq == "none")
+    c2s: torch.Tensor  # float32 [ceil(n_blocks / 256)] (empty when dq == "none")
     mu: torch.Tensor  # float32 [1]
     d_out: int
     d_in: int
+    codebook: str = "nf4"
+    dq: str = "e4m3"
 
     @classmethod
-    def empty(cls, d_out: int, d_in: int, device="cuda") -> "QuantizedWeight":
-        nc, n8, n2 = quant_sizes(d_out, d_in)
+    def empty(cls, d_out: int, d_in: int, device="cuda", codebook: str = "nf4", dq: str = "e4m3") -> "QuantizedWeight":
+        nc, n8, n2 = quant_sizes(d_out, d_in, dq)
         return cls(
             codes=torch.empty(nc, dtype=torch.uint8, device=device),
             code8=torch.empty(n8, dtype=torch.uint8, device=device),
-            c2s=torch.empty(n2 // 4, dtype=torch.float32, device=device),
+            c2s=torch.empty(max(n2 // 4, 1), dtype=torch.float32, device=device),
             mu=torch.empty(1, dtype=torch.float32, device=device),
             d_out=d_out,
             d_in=d_in,
+            codebook=codebook,
+            dq=dq,
         )
 
     def struct(self) -> _Nf4dq:
         return _Nf4dq(self.codes.data_ptr(), self.code8.data_ptr(), self.c2s.data_ptr(), self.mu.data_ptr(),
-                      self.d_out, self.d_in, 64, 256)
+                      self.d_out, self.d_in, 64, 256, CODEBOOKS[self.codebook], DQ_FORMATS[self.dq])
+
+    def stored_constants(self) -> torch.Tensor:
+        """The per-block constants as stored: E4M3/E5M2/INT8 bytes, or FP32 without DQ."""
+        return self.code8.view(torch.float32) if self.dq == "none" else self.code8
 
     def nbytes(self) -> int:
-        return self.codes.numel() + self.code8.numel() + 4 * self.c2s.numel() + 4
+        extra = 0 if self.dq == "none" else 4 * self.c2s.numel() + 4
+        return self.codes.numel() + self.code8.numel() + extra
 
 
 class _Workspace:
@@ -189,11 +213,13 @@ class _Workspace:
 _WS = _Workspace()
 
 
-def quantize(W: torch.Tensor, out: QuantizedWeight | None = None, ws: torch.Tensor | None = None) -> QuantizedWeight:
-    """Quantize an FP32 [d_out, d_in] CUDA tensor (synchronizes the current stream once)."""
+def quantize(W: torch.Tensor, out: QuantizedWeight | None = None, ws: torch.Tensor | None = None,
+             codebook: str = "nf4", dq: str = "e4m3") -> QuantizedWeight:
+    """Quantize an FP32 [d_out, d_in] CUDA tensor (synchronizes the current stream once).
+    The format comes from `out` when given, else from `codebook` and `dq`."""
     _dev(W, torch.float32, "W")
     d_out, d_in = W.shape
-    q = out if out is not None else QuantizedWeight.empty(d_out, d_in, W.device)
+    q = out if out is not None else QuantizedWeight.empty(d_out, d_in, W.device, codebook, dq)
     need = workspace_size(OP_QUANTIZE, 1, d_out, d_in, 1)
     ws = ws if ws is not None else _WS.get(need, W.device, "quant")
     mu = ctypes.c_float()
@@ -203,12 +229,12 @@ def quantize(W: torch.Tensor, out: QuantizedWeight | None = None, ws: torch.Tens
     return q
 
 
-def quantize_bf16(W: torch.Tensor, out: QuantizedWeight | None = None,
-                  ws: torch.Tensor | None = None) -> QuantizedWeight:
+def quantize_bf16(W: torch.Tensor, out: QuantizedWeight | None = None, ws: torch.Tensor | None = None,
+                  codebook: str = "nf4", dq: str = "e4m3") -> QuantizedWeight:
     """Quantize a BF16 [d_out, d_in] CUDA tensor (its exact FP32 values; synchronizes once)."""
     _dev(W, torch.bfloat16, "W")
     d_out, d_in = W.shape
-    q = out if out is not None else QuantizedWeight.empty(d_out, d_in, W.device)
+    q = out if out is not None else QuantizedWeight.empty(d_out, d_in, W.device, codebook, dq)
     need = workspace_size(OP_QUANTIZE, 1, d_out, d_in, 1)
     ws = ws if ws is not None else _WS.get(need, W.device, "quant")
     mu = ctypes.c_float()
@@ -252,7 +278,7 @@ def linear_fwd(q: QuantizedWeight, X: torch.Tensor, A: torch.Tensor, B: torch.Te
     _dev(Y, torch.bfloat16, "Y")
     if T_save is not None:
         _dev(T_save, torch.bfloat16, "T_save")
-    need = workspace_size(OP_FWD, M, q.d_out, q.d_in, r)
+    need = workspace_size(OP_FWD, M, q.d_out, q.d_in, r, q.dq)
     ws = ws if ws is not None else _WS.get(need, X.device, "fwd")
     s = q.struct()
     _check(load_library().qlora_linear_fwd(ctypes.byref(s), X.data_ptr(), M, A.data_ptr(), B.data_ptr(), r,
@@ -274,7 +300,7 @@ def linear_bwd(q: QuantizedWeight, X: torch.Tensor, dY: torch.Tensor, A: torch.T
         dX = torch.empty(M, q.d_in, dtype=torch.bfloat16, device=dev)
     dA = dA if dA is not None else torch.empty(r, q.d_in, dtype=torch.bfloat16, device=dev)
     dB = dB if dB is not None else torch.empty(q.d_out, r, dtype=torch.bfloat16, device=dev)
-    need = workspace_size(OP_BWD, M, q.d_out, q.d_in, r)
+    need = workspace_size(OP_BWD, M, q.d_out, q.d_in, r, q.dq)
     ws = ws if ws is not None else _WS.get(need, dev, "bwd")
     s = q.struct()
     _check(load_library().qlora_linear_bwd(ctypes.byref(s), X.data_ptr(), dY.data_ptr(), M, A.data_ptr(),

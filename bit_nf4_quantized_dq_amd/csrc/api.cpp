@@ -32,8 +32,13 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 int hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP; }
 
 int check_wq(const qlora_nf4dq_t* Wq) {
-  if (!Wq || !Wq->codes || !Wq->code8 || !Wq->c2s || !Wq->mu) return QLORA_ERR_INVALID_ARG;
+  if (!Wq || !Wq->codes || !Wq->code8) return QLORA_ERR_INVALID_ARG;
   if (Wq->block1 != 64 || Wq->block2 != 256) return QLORA_ERR_UNSUPPORTED;
+  if (Wq->codebook < QLORA_CB_NF4 || Wq->codebook > QLORA_CB_FP4 || Wq->dq_format < QLORA_DQ_E4M3 ||
+      Wq->dq_format > QLORA_DQ_NONE)
+    return QLORA_ERR_UNSUPPORTED;
+  if (Wq->dq_format != QLORA_DQ_NONE && (!Wq->c2s || !Wq->mu)) return QLORA_ERR_INVALID_ARG;
+  if ((Wq->dq_format == QLORA_DQ_NONE) && (reinterpret_cast<uintptr_t>(Wq->code8) & 3u)) return QLORA_ERR_INVALID_ARG;
   if (!shape_ok(Wq->d_out, Wq->d_in)) return QLORA_ERR_BAD_SHAPE;
   if (!aligned16(Wq->codes)) return QLORA_ERR_INVALID_ARG;
   return QLORA_OK;
@@ -46,20 +51,28 @@ int check_lora(int64_t M, int32_t r, float alpha) {
   return QLORA_OK;
 }
 
+// The first-level table of a weight's codebook.
+inline const Nf4Tables& tables_of(const qlora_nf4dq_t* Wq) { return codebook_tables(Wq->codebook); }
+
+// Only E4M3 constants are decoded inside the fused GEMV / GEMM kernels; the other formats
+// decode once per call into a BF16 copy (k_dequant, k_dequant_t) at every token count.
+inline bool decode_once(int64_t M, int dq);
+
 constexpr int64_t kGemvMaxM = 16;
 // From this many tokens on, the weight is decoded once into a BF16 copy in the workspace
 // and multiplied by the plain BF16 GEMM; below it the fused kernels decode per tile.
 constexpr int64_t kNtMinM = 1024;
+inline bool decode_once(int64_t M, int dq) { return M >= kNtMinM || dq != QLORA_DQ_E4M3; }
 
 // ---- workspace layouts
 struct FwdWs {
   size_t tpart, ypart, ls, wcopy, total;
 };
-FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
+FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r, int dq) {
   FwdWs w{};
   size_t off = 0;
   w.tpart = off;
-  if (M <= kGemvMaxM) {
+  if (M <= kGemvMaxM && !decode_once(M, dq)) {
     const int32_t ks = gemv_ksplit(N, K);
     off = align_up(off + sizeof(float) * ks * M * r, 256);
     w.ypart = off;
@@ -69,7 +82,7 @@ FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
     w.ypart = off;
     w.ls = off;
     off = align_up(off + 2 * M * r, 256);
-    if (M >= kNtMinM) {
+    if (decode_once(M, dq)) {
       w.wcopy = off;
       off = align_up(off + 2 * (size_t)N * K, 256);
     }
@@ -81,7 +94,7 @@ FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
 struct BwdWs {
   size_t t, g, lg, cpa, cpb, wcopy, total;
 };
-BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
+BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r, int dq) {
   BwdWs w{};
   size_t off = 0;
   w.t = off;
@@ -94,7 +107,7 @@ BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   off = align_up(off + sizeof(float) * (int64_t)lora_grad_msplit(M, K) * r * K, 256);
   w.cpb = off;
   off = align_up(off + sizeof(float) * (int64_t)lora_grad_msplit(M, N) * r * N, 256);
-  if (M >= kNtMinM) {
+  if (decode_once(M, dq)) {
     w.wcopy = off;
     off = align_up(off + 2 * (size_t)N * K, 256);
   }
@@ -188,7 +201,7 @@ const char* qlora_strerror(int status) {
     case QLORA_OK: return "ok";
     case QLORA_ERR_INVALID_ARG: return "invalid argument";
     case QLORA_ERR_BAD_SHAPE: return "bad shape (need d_in % 64 == 0, d_out % 16 == 0)";
-    case QLORA_ERR_UNSUPPORTED: return "unsupported block sizes (need 64, 256)";
+    case QLORA_ERR_UNSUPPORTED: return "unsupported block sizes (need 64, 256), codebook or format";
     case QLORA_ERR_NONFINITE: return "non-finite weight";
     case QLORA_ERR_WORKSPACE: return "workspace too small";
     case QLORA_ERR_HIP: return "HIP runtime error";
@@ -207,17 +220,39 @@ int qlora_quant_sizes(int64_t d_out, int64_t d_in, size_t* codes_bytes, size_t* 
 }
 
 int qlora_workspace_size(int op, int64_t M, int64_t d_out, int64_t d_in, int32_t r, size_t* ws_bytes) {
+  return qlora_workspace_size_fmt(op, M, d_out, d_in, r, QLORA_DQ_E4M3, ws_bytes);
+}
+
+int qlora_workspace_size_fmt(int op, int64_t M, int64_t d_out, int64_t d_in, int32_t r, int dq_format,
+                             size_t* ws_bytes) {
   if (!ws_bytes) return QLORA_ERR_INVALID_ARG;
   if (!shape_ok(d_out, d_in)) return QLORA_ERR_BAD_SHAPE;
+  if (dq_format < QLORA_DQ_E4M3 || dq_format > QLORA_DQ_NONE) return QLORA_ERR_UNSUPPORTED;
   if (op == QLORA_OP_QUANTIZE) {
     *ws_bytes = quant_ws(d_out, d_in);
     return QLORA_OK;
   }
   int st = check_lora(M, r, 1.0f);
   if (st) return st;
-  if (op == QLORA_OP_FWD) *ws_bytes = fwd_ws(M, d_out, d_in, r).total;
-  else if (op == QLORA_OP_BWD) *ws_bytes = bwd_ws(M, d_out, d_in, r).total;
+  if (op == QLORA_OP_FWD) *ws_bytes = fwd_ws(M, d_out, d_in, r, dq_format).total;
+  else if (op == QLORA_OP_BWD) *ws_bytes = bwd_ws(M, d_out, d_in, r, dq_format).total;
   else return QLORA_ERR_INVALID_ARG;
+  return QLORA_OK;
+}
+
+int qlora_format_sizes(int64_t d_out, int64_t d_in, int dq_format, size_t* codes_bytes, size_t* code8_bytes,
+                       size_t* c2s_bytes) {
+  if (dq_format < QLORA_DQ_E4M3 || dq_format > QLORA_DQ_NONE) return QLORA_ERR_UNSUPPORTED;
+  int st = qlora_quant_sizes(d_out, d_in, codes_bytes, code8_bytes, c2s_bytes);
+  if (st || dq_format != QLORA_DQ_NONE) return st;
+  *code8_bytes *= 4;  // one FP32 constant per block
+  *c2s_bytes = 0;
+  return QLORA_OK;
+}
+
+int qlora_codebook(int codebook, float out16[16]) {
+  if (!out16 || codebook < QLORA_CB_NF4 || codebook > QLORA_CB_FP4) return QLORA_ERR_INVALID_ARG;
+  std::memcpy(out16, codebook_tables(codebook).q, sizeof(float) * 16);
   return QLORA_OK;
 }
 
@@ -245,8 +280,9 @@ int quantize_impl(const void* W, bool w_bf16, const qlora_nf4dq_t* Wq, float* ho
   int* flag = reinterpret_cast<int*>(hist + 256);
   hipError_t e = hipMemsetAsync(hist, 0, 256 * sizeof(unsigned long long) + 256, stream);
   if (e != hipSuccess) return QLORA_ERR_HIP;
-  e = launch_quant_pass1(W, w_bf16, reinterpret_cast<uint32_t*>(Wq->codes), c1, hist, flag, n / 8, nf4_tables(),
-                         stream);
+  const bool no_dq = Wq->dq_format == QLORA_DQ_NONE;  // then c1 itself is the stored constant
+  e = launch_quant_pass1(W, w_bf16, reinterpret_cast<uint32_t*>(Wq->codes), no_dq ? reinterpret_cast<float*>(Wq->code8) : c1,
+                         hist, flag, n / 8, tables_of(Wq), stream);
   if (e != hipSuccess) return QLORA_ERR_HIP;
   unsigned long long h_hist[256];
   int h_flag = 0;
@@ -254,10 +290,14 @@ int quantize_impl(const void* W, bool w_bf16, const qlora_nf4dq_t* Wq, float* ho
   if (hipMemcpyAsync(&h_flag, flag, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess) return QLORA_ERR_HIP;
   if (hipStreamSynchronize(stream) != hipSuccess) return QLORA_ERR_HIP;
   if (h_flag) return QLORA_ERR_NONFINITE;
+  if (no_dq) {
+    if (host_mu) *host_mu = 0.f;
+    return QLORA_OK;
+  }
   const double mean = exact_sum_to_double(h_hist) / (double)nb;
   const float mu = (float)mean;
   if (host_mu) *host_mu = mu;
-  e = launch_quant_pass2(c1, mu, Wq->code8, Wq->c2s, Wq->mu, nb, stream);
+  e = launch_quant_pass2(c1, mu, Wq->code8, Wq->c2s, Wq->mu, nb, Wq->dq_format, stream);
   return hip_status(e);
 }
 
@@ -281,7 +321,7 @@ int qlora_dequantize(const qlora_nf4dq_t* Wq, uint16_t* W_bf16, hipStream_t stre
   if (!W_bf16 || !aligned16(W_bf16)) return QLORA_ERR_INVALID_ARG;
   const int64_t n = Wq->d_out * Wq->d_in;
   return hip_status(launch_dequant(reinterpret_cast<const uint32_t*>(Wq->codes), Wq->code8, Wq->c2s, Wq->mu,
-                                   W_bf16, n / 8, nf4_tables(), stream));
+                                   W_bf16, n / 8, tables_of(Wq), Wq->dq_format, stream));
 }
 
 int qlora_merge(const qlora_nf4dq_t* Wq, const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
@@ -294,7 +334,7 @@ int qlora_merge(const qlora_nf4dq_t* Wq, const uint16_t* A, const uint16_t* B, i
   const int64_t N = Wq->d_out, K = Wq->d_in;
   if ((N + 127) / 128 > 65535) return QLORA_ERR_BAD_SHAPE;  // grid rows of 128 weights
   return hip_status(launch_merge(reinterpret_cast<const uint32_t*>(Wq->codes), Wq->code8, Wq->c2s, Wq->mu, A, B, N, K,
-                                 r, alpha / (float)r, W_out, nf4_tables(), stream));
+                                 r, alpha / (float)r, W_out, tables_of(Wq), Wq->dq_format, stream));
 }
 
 int qlora_linear_fwd(const qlora_nf4dq_t* Wq, const uint16_t* X, int64_t M, const uint16_t* A, const uint16_t* B,
@@ -305,31 +345,33 @@ int qlora_linear_fwd(const qlora_nf4dq_t* Wq, const uint16_t* X, int64_t M, cons
   if ((st = check_lora(M, r, alpha))) return st;
   if (!X || !A || !B || !Y || !aligned16(X) || !aligned16(A) || !aligned16(Y)) return QLORA_ERR_INVALID_ARG;
   const int64_t N = Wq->d_out, K = Wq->d_in;
-  const FwdWs L = fwd_ws(M, N, K, r);
+  const int dq = Wq->dq_format;
+  const FwdWs L = fwd_ws(M, N, K, r, dq);
   if (!ws || ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
   char* base = static_cast<char*>(ws);
   const float s = alpha / (float)r;
   const uint32_t* codes = reinterpret_cast<const uint32_t*>(Wq->codes);
   float* tpart = reinterpret_cast<float*>(base + L.tpart);
-  if (M <= kGemvMaxM) {
+  if (M <= kGemvMaxM && !decode_once(M, dq)) {
     if ((N + 63) / 64 > 65536) return QLORA_ERR_BAD_SHAPE;  // one arrival counter per 64 rows
     float* ypart = reinterpret_cast<float*>(base + L.ypart);
     return hip_status(launch_gemv_fwd(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, X, M, A, B, r, s, Y, T_save, ypart,
-                                      tpart, nf4_tables(), stream));
+                                      tpart, tables_of(Wq), stream));
   }
   // T = X A^T: s T (BF16) feeds the adapter slices of the GEMM; T itself is saved if asked
   uint16_t* ls = reinterpret_cast<uint16_t*>(base + L.ls);
   hipError_t e;
   if ((e = launch_lora_down(X, A, 0, M, r, K, s, ls, T_save, stream)) != hipSuccess) return QLORA_ERR_HIP;
-  if (M >= kNtMinM) {
+  if (decode_once(M, dq)) {
     uint16_t* wcopy = reinterpret_cast<uint16_t*>(base + L.wcopy);
-    if ((e = launch_dequant(codes, Wq->code8, Wq->c2s, Wq->mu, wcopy, N * K / 8, nf4_tables(), stream)) != hipSuccess)
+    if ((e = launch_dequant(codes, Wq->code8, Wq->c2s, Wq->mu, wcopy, N * K / 8, tables_of(Wq), dq, stream)) !=
+        hipSuccess)
       return QLORA_ERR_HIP;
     // Y = X w_hat^T + (s T) B^T: A = w_hat [N, K], Wl = B [N, r] (f*r + j)
     e = launch_gemm_nt(wcopy, N, X, M, K, B, r, 1, ls, r, Y, QLORA_K_GEMM_FWD, stream);
     return hip_status(e);
   }
-  e = launch_gemm_fwd(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, X, M, ls, B, r, Y, nf4_tables(), stream);
+  e = launch_gemm_fwd(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, X, M, ls, B, r, Y, tables_of(Wq), stream);
   return hip_status(e);
 }
 
@@ -342,7 +384,8 @@ int qlora_linear_bwd(const qlora_nf4dq_t* Wq, const uint16_t* X, const uint16_t*
   if (!X || !dY || !A || !B || !dA || !dB) return QLORA_ERR_INVALID_ARG;
   if (!aligned16(X) || !aligned16(dY) || !aligned16(A) || (dX && !aligned16(dX))) return QLORA_ERR_INVALID_ARG;
   const int64_t N = Wq->d_out, K = Wq->d_in;
-  const BwdWs L = bwd_ws(M, N, K, r);
+  const int dq = Wq->dq_format;
+  const BwdWs L = bwd_ws(M, N, K, r, dq);
   if (!ws || ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
   char* base = static_cast<char*>(ws);
   const float s = alpha / (float)r;
@@ -361,15 +404,15 @@ int qlora_linear_bwd(const qlora_nf4dq_t* Wq, const uint16_t* X, const uint16_t*
   // G = dY B (B [N, r] is read as the transposed operand); s G and G in BF16
   if ((e = launch_lora_down(dY, B, 1, M, r, N, s, lg, g, stream)) != hipSuccess) return QLORA_ERR_HIP;
   // dX = dY w_hat + (s G) A
-  if (dX && M >= kNtMinM) {
+  if (dX && decode_once(M, dq)) {
     uint16_t* wcopy = reinterpret_cast<uint16_t*>(base + L.wcopy);
-    if ((e = launch_dequant_t(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, wcopy, nf4_tables(), stream)) != hipSuccess)
+    if ((e = launch_dequant_t(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, wcopy, tables_of(Wq), dq, stream)) != hipSuccess)
       return QLORA_ERR_HIP;
     // A = w_hat^T [K, N], Wl(f, j) = A[j][f]: read in place from A [r, K] (f*1 + j*K)
     if ((e = launch_gemm_nt(wcopy, K, dY, M, N, A, 1, K, lg, r, dX, QLORA_K_GEMM_DX, stream)) != hipSuccess)
       return QLORA_ERR_HIP;
   } else if (dX) {
-    if ((e = launch_gemm_dx(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, dY, M, lg, A, r, dX, nf4_tables(), stream)) !=
+    if ((e = launch_gemm_dx(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, dY, M, lg, A, r, dX, tables_of(Wq), stream)) !=
         hipSuccess)
       return QLORA_ERR_HIP;
   }

@@ -50,6 +50,9 @@ uint16_t bf16_rne_host(float f) {
   return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
 }
 
+// Thresholds and byte tables of a table whose 16 FP32 levels are already in t->q.
+void finish_tables(Nf4Tables* t);
+
 }  // namespace
 
 void build_nf4_tables(Nf4Tables* t) {
@@ -66,6 +69,34 @@ void build_nf4_tables(Nf4Tables* t) {
   t->q[0] = -1.0f;
   t->q[8] = 0.0f;
   t->q[15] = 1.0f;
+  finish_tables(t);
+}
+
+// Other first-level codebooks, for comparison with NF4 ("QLoRA: Quantize Base Weights to
+// 4-Bit", Section 2 "1. 4-bit NormalFloat", against standard INT4 and FP4):
+//   INT4 : 16 evenly spaced levels -1 + 2 i / 15 (both ends exact, no zero level);
+//   FP4  : the E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 with both signs, over 6, so the ends
+//          are +-1; +0 and -0 are one level and the 16th entry repeats +1 (never nearest first).
+// Each level is its double value rounded once to FP32.
+void build_codebook_tables(int codebook, Nf4Tables* t) {
+  if (codebook == 1) {
+    for (int i = 0; i < 16; ++i) t->q[i] = (float)((2.0 * i - 15.0) / 15.0);
+  } else if (codebook == 2) {
+    const double mags[7] = {6.0, 4.0, 3.0, 2.0, 1.5, 1.0, 0.5};
+    for (int i = 0; i < 7; ++i) t->q[i] = (float)(-mags[i] / 6.0);
+    t->q[7] = 0.0f;
+    for (int i = 0; i < 7; ++i) t->q[8 + i] = (float)(mags[6 - i] / 6.0);
+    t->q[15] = 1.0f;
+  } else {
+    build_nf4_tables(t);
+    return;
+  }
+  finish_tables(t);
+}
+
+namespace {
+
+void finish_tables(Nf4Tables* t) {
   // Decision thresholds: the exact midpoint of two FP32 levels is exact in double;
   // round it down to FP32 so that "rho > thr" equals "rho is nearer the upper level"
   // with ties going to the lower level.
@@ -88,13 +119,20 @@ void build_nf4_tables(Nf4Tables* t) {
   }
 }
 
-const Nf4Tables& nf4_tables() {
-  static Nf4Tables t = [] {
-    Nf4Tables x;
-    build_nf4_tables(&x);
-    return x;
-  }();
-  return t;
+struct AllTables {
+  Nf4Tables t[3];
+  AllTables() {
+    for (int c = 0; c < 3; ++c) build_codebook_tables(c, &t[c]);
+  }
+};
+
+}  // namespace
+
+const Nf4Tables& codebook_tables(int codebook) {
+  static const AllTables all;
+  return all.t[(codebook >= 0 && codebook < 3) ? codebook : 0];
 }
+
+const Nf4Tables& nf4_tables() { return codebook_tables(0); }
 
 }  // namespace qlora

@@ -1,6 +1,7 @@
 // Standalone dequantization to BF16, bit-exact:
 //   c1_hat = fl32(fl32(E4M3(code8) * c2s) + mu)      (undo DQ: "QLoRA: Quantize Base
-//            Weights to 4-Bit", Section 2 "2. Double Quantization")
+//            Weights to 4-Bit", Section 2 "2. Double Quantization"; the comparison formats
+//            read E5M2 or a signed byte instead, or the FP32 constant itself)
 //   w_hat  = bf16(fl32(q[code] * c1_hat))             (lookup times constant: "QLoRA --
 //            Fine-Tuning a 65B Model on One GPU", "Quantization in one paragraph")
 // It runs the same per-block scaled byte-permute decoder as the fused forward GEMM, so
@@ -13,6 +14,15 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// The stored constant of block blk and the block's recovered c1 (DQ: second-level format).
+template <int DQ>
+__device__ __forceinline__ float load_scale(const uint8_t* __restrict__ code8, const float* __restrict__ c2s,
+                                            const float* __restrict__ mu, int64_t blk) {
+  if (DQ == kDqNone) return reinterpret_cast<const float*>(code8)[blk];
+  return block_scale_fmt<DQ>(code8[blk], c2s[blk >> 8], mu[0]);
+}
+
+template <int DQ>
 __global__ __launch_bounds__(kThreads) void k_dequant(const uint32_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ code8,
                                                       const float* __restrict__ c2s,
@@ -22,7 +32,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint32_t* __restrict
   const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (g >= n_words) return;
   const int64_t blk = g >> 3;
-  const float c = block_scale(code8[blk], c2s[blk >> 8], mu[0]);
+  const float c = load_scale<DQ>(code8, c2s, mu, blk);
   Lut L;
   build_scaled_lut(T, c, L);
   uint32_t w[4];
@@ -39,6 +49,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint32_t* __restrict
 // spread over distinct banks.
 constexpr int kTN = 64, kTK = 256, kTPitch = kTK / 2 + 1;
 
+template <int DQ>
 __global__ __launch_bounds__(kThreads) void k_dequant_t(const uint32_t* __restrict__ codes,
                                                         const uint8_t* __restrict__ code8,
                                                         const float* __restrict__ c2s,
@@ -54,7 +65,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant_t(const uint32_t* __restri
   if (n < N && kb < nb_row) {
     const int64_t blk = n * nb_row + kb;
     Lut L;
-    build_scaled_lut(T, block_scale(code8[blk], c2s[blk >> 8], mu[0]), L);
+    build_scaled_lut(T, load_scale<DQ>(code8, c2s, mu, blk), L);
     const uint4* wp = reinterpret_cast<const uint4*>(codes + blk * 8);
     const uint4 w0 = wp[0], w1 = wp[1];
     const uint32_t words[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
@@ -88,21 +99,33 @@ __global__ __launch_bounds__(kThreads) void k_dequant_t(const uint32_t* __restri
 }  // namespace
 
 hipError_t launch_dequant_t(const uint32_t* codes, const uint8_t* code8, const float* c2s,
-                            const float* mu, int64_t N, int64_t K, uint16_t* out, const Nf4Tables& T,
+                            const float* mu, int64_t N, int64_t K, uint16_t* out, const Nf4Tables& T, int dq,
                             hipStream_t s) {
   dim3 grid((unsigned)((K + kTK - 1) / kTK), (unsigned)((N + kTN - 1) / kTN));
   LaunchTimer t(8, s);
-  hipExtLaunchKernelGGL(k_dequant_t, grid, dim3(kThreads), 0, s, t.start, t.stop, 0, codes, code8, c2s, mu, out, N, K, T);
+  auto go = [&](auto kern) {
+    hipExtLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, t.start, t.stop, 0, codes, code8, c2s, mu, out, N, K, T);
+  };
+  if (dq == kDqE5M2) go(k_dequant_t<kDqE5M2>);
+  else if (dq == kDqInt8) go(k_dequant_t<kDqInt8>);
+  else if (dq == kDqNone) go(k_dequant_t<kDqNone>);
+  else go(k_dequant_t<kDqE4M3>);
   return hipGetLastError();
 }
 
 hipError_t launch_dequant(const uint32_t* codes, const uint8_t* code8, const float* c2s,
-                          const float* mu, uint16_t* out, int64_t n_words, const Nf4Tables& T,
+                          const float* mu, uint16_t* out, int64_t n_words, const Nf4Tables& T, int dq,
                           hipStream_t s) {
   const int64_t grid = (n_words + kThreads - 1) / kThreads;
   LaunchTimer t(2, s);
-  hipExtLaunchKernelGGL(k_dequant, dim3((unsigned)grid), dim3(kThreads), 0, s, t.start, t.stop, 0, codes, code8, c2s, mu,
-                     reinterpret_cast<uint4*>(out), n_words, T);
+  auto go = [&](auto kern) {
+    hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, s, t.start, t.stop, 0, codes, code8, c2s, mu,
+                          reinterpret_cast<uint4*>(out), n_words, T);
+  };
+  if (dq == kDqE5M2) go(k_dequant<kDqE5M2>);
+  else if (dq == kDqInt8) go(k_dequant<kDqInt8>);
+  else if (dq == kDqNone) go(k_dequant<kDqNone>);
+  else go(k_dequant<kDqE4M3>);
   return hipGetLastError();
 }
 

@@ -71,7 +71,7 @@ __device__ __forceinline__ void decode4(uint32_t u, int h, const Lut& L, uint32_
 }
 
 // grid: (ceil(K / 256), ceil(N / 128)).  RC = ceil(r / 16) rank chunks.
-template <int RC>
+template <int RC, int DQ>
 __global__ __launch_bounds__(kThreads) void k_merge(const uint32_t* __restrict__ codes,
                                                     const uint8_t* __restrict__ code8,
                                                     const float* __restrict__ c2s,
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void k_merge(const uint32_t* __restrict__
   }
 
   // block constants of the blocks of 64 columns
-  const rsrc_t r8 = make_rsrc(code8, nb);
+  const rsrc_t r8 = make_rsrc(code8, DQ == kDqNone ? 4 * nb : nb);
   const rsrc_t r2 = make_rsrc(c2s, 4 * ((nb + kBlock2 - 1) / kBlock2));
   uint32_t c8[kTilesK / 2];
   float g2[kTilesK / 2];
@@ -133,10 +133,15 @@ __global__ __launch_bounds__(kThreads) void k_merge(const uint32_t* __restrict__
   for (int b = 0; b < kTilesK / 2; ++b) {
     const bool ok = row_ok && k0 + 64 * b < K;
     const int64_t blk = n * nb_row + k0 / kBlock1 + b;
-    c8[b] = bload1(r8, ok ? (uint32_t)blk : kOOB);
-    g2[b] = __uint_as_float(bload4(r2, ok ? (uint32_t)(4 * ((uint64_t)blk >> 8)) : kOOB));
+    if (DQ == kDqNone) {  // the FP32 constant itself
+      c8[b] = bload4(r8, ok ? (uint32_t)(4 * blk) : kOOB);
+      g2[b] = 0.f;
+    } else {
+      c8[b] = bload1(r8, ok ? (uint32_t)blk : kOOB);
+      g2[b] = __uint_as_float(bload4(r2, ok ? (uint32_t)(4 * ((uint64_t)blk >> 8)) : kOOB));
+    }
   }
-  const float mu0 = mu[0];
+  const float mu0 = DQ == kDqNone ? 0.f : mu[0];
 
   // this lane's code words: tile i holds columns k0 + 32 i .. +31 (16 bytes of codes)
   const rsrc_t rc = make_rsrc(codes, N * K / 2);
@@ -162,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void k_merge(const uint32_t* __restrict__
     // transposing reads, which gather across lanes, and only skip the stores
     if (k0 + 64 * bb >= K) break;
     Lut L;
-    build_scaled_lut(T, block_scale(c8[bb], g2[bb], mu0), L);
+    build_scaled_lut(T, block_scale_fmt<DQ>(c8[bb], g2[bb], mu0), L);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int i = 2 * bb + half;
@@ -205,9 +210,15 @@ __global__ __launch_bounds__(kThreads) void k_merge(const uint32_t* __restrict__
 template <int RC>
 hipError_t launch_rc(dim3 grid, const LaunchTimer& t, hipStream_t st, const uint32_t* codes, const uint8_t* code8,
                      const float* c2s, const float* mu, const uint16_t* A, const uint16_t* B, int64_t N, int64_t K,
-                     int32_t r, float s, uint16_t* out, const Nf4Tables& T) {
-  hipExtLaunchKernelGGL(k_merge<RC>, grid, dim3(kThreads), 0, st, t.start, t.stop, 0, codes, code8, c2s, mu, A, B, N,
-                        K, r, s, out, T);
+                     int32_t r, float s, uint16_t* out, const Nf4Tables& T, int dq) {
+  auto go = [&](auto kern) {
+    hipExtLaunchKernelGGL(kern, grid, dim3(kThreads), 0, st, t.start, t.stop, 0, codes, code8, c2s, mu, A, B, N, K, r, s,
+                          out, T);
+  };
+  if (dq == kDqE5M2) go(k_merge<RC, kDqE5M2>);
+  else if (dq == kDqInt8) go(k_merge<RC, kDqInt8>);
+  else if (dq == kDqNone) go(k_merge<RC, kDqNone>);
+  else go(k_merge<RC, kDqE4M3>);
   return hipGetLastError();
 }
 
@@ -215,18 +226,18 @@ hipError_t launch_rc(dim3 grid, const LaunchTimer& t, hipStream_t st, const uint
 
 hipError_t launch_merge(const uint32_t* codes, const uint8_t* code8, const float* c2s, const float* mu,
                         const uint16_t* A, const uint16_t* B, int64_t N, int64_t K, int32_t r, float s,
-                        uint16_t* out, const Nf4Tables& T, hipStream_t st) {
+                        uint16_t* out, const Nf4Tables& T, int dq, hipStream_t st) {
   const dim3 grid((unsigned)((K + kColsWG - 1) / kColsWG), (unsigned)((N + kRowsWG - 1) / kRowsWG));
   LaunchTimer t(9, st);
   switch ((r + 15) / 16) {
-    case 1: return launch_rc<1>(grid, t, st, codes, code8, c2s, mu, A, B, N, K, r, s, out, T);
-    case 2: return launch_rc<2>(grid, t, st, codes, code8, c2s, mu, A, B, N, K, r, s, out, T);
-    case 3: return launch_rc<3>(grid, t, st, codes, code8, c2s, mu, A, B, N, K, r, s, out, T);
-    case 4: return launch_rc<4>(grid, t, st, codes, code8, c2s, mu, A, B, N, K, r, s, out, T);
-    case 5: return launch_rc<5>(grid, t, st, codes, code8, c2s, mu, A, B, N, K, r, s, out, T);
-    case 6: return launch_rc<6>(grid, t, st, codes, code8, c2s, mu, A, B, N, K, r, s, out, T);
-    case 7: return launch_rc<7>(grid, t, st, codes, code8, c2s, mu, A, B, N, K, r, s, out, T);
-    case 8: return launch_rc<8>(grid, t, st, codes, code8, c2s, mu, A, B, N, K, r, s, out, T);
+    case 1: return launch_rc<1>(grid, t, st, codes, code8, c2s, mu, A, B, N, K, r, s, out, T, dq);
+    case 2: return launch_rc<2>(grid, t, st, codes, code8, c2s, mu, A, B, N, K, r, s, out, T, dq);
+    case 3: return launch_rc<3>(grid, t, st, codes, code8, c2s, mu, A, B, N, K, r, s, out, T, dq);
+    case 4: return launch_rc<4>(grid, t, st, codes, code8, c2s, mu, A, B, N, K, r, s, out, T, dq);
+    case 5: return launch_rc<5>(grid, t, st, codes, code8, c2s, mu, A, B, N, K, r, s, out, T, dq);
+    case 6: return launch_rc<6>(grid, t, st, codes, code8, c2s, mu, A, B, N, K, r, s, out, T, dq);
+    case 7: return launch_rc<7>(grid, t, st, codes, code8, c2s, mu, A, B, N, K, r, s, out, T, dq);
+    case 8: return launch_rc<8>(grid, t, st, codes, code8, c2s, mu, A, B, N, K, r, s, out, T, dq);
     default: return hipErrorInvalidValue;
   }
 }

@@ -78,6 +78,57 @@ __device__ __forceinline__ float block_scale(uint32_t code8, float c2s, float mu
   return __fadd_rn(__fmul_rn(e4m3_to_f32(code8), c2s), mu);
 }
 
+// ---------------------------------------------------------------- second-level format variants
+// The format of the stored block constants (the comparison formats of "QLoRA: Quantize Base
+// Weights to 4-Bit", Section 2 "2. Double Quantization", whose 8-bit format the pages call
+// both a float and an integer, and FP32 constants without double quantization).
+enum DqFormat : int { kDqE4M3 = 0, kDqE5M2 = 1, kDqInt8 = 2, kDqNone = 3 };
+
+// OCP FP8 E5M2 -> FP32, exact: bias 15, 2 mantissa bits, exponent field 0 subnormal
+// (m/4 * 2^-14).  Inf and NaN codes never occur in stored constants.
+__device__ __forceinline__ float e5m2_to_f32(uint32_t b) {
+  const uint32_t e = (b >> 2) & 0x1Fu;
+  const uint32_t m = b & 0x3u;
+  const float v = (e == 0) ? (float)m * 1.52587890625e-05f  // m * 2^-16, exact
+                           : __uint_as_float(((e + 112u) << 23) | (m << 21));
+  return (b & 0x80u) ? -v : v;
+}
+
+// FP32 -> OCP E5M2, round to nearest, ties to even; beyond 57344 to 57344; the sign of zero
+// follows s.  Written from the OCP OFP8 definition, like the E4M3 encoder above.
+__device__ __forceinline__ uint32_t f32_to_e5m2(float s) {
+  const uint32_t u = __float_as_uint(s);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t E = (u >> 23) & 0xFFu;
+  uint32_t code;
+  if (E < 113u) {
+    // below the smallest normal 2^-14: grid m * 2^-16, m = RNE(|s| * 2^16) in 0..4
+    code = (uint32_t)__builtin_rintf(__uint_as_float(u & 0x7FFFFFFFu) * 65536.0f);
+  } else {
+    const uint32_t mant = u & 0x7FFFFFu;
+    code = ((E - 112u) << 2) | (mant >> 21);
+    const uint32_t rem = mant & 0x1FFFFFu;
+    if (rem > 0x100000u || (rem == 0x100000u && (code & 1u))) code += 1u;
+    if (code > 0x7Bu) code = 0x7Bu;
+  }
+  return code | sign;
+}
+
+// FP32 -> symmetric 8-bit integer (two's-complement byte): round half to even, clamp to +-127.
+__device__ __forceinline__ uint32_t f32_to_int8(float s) {
+  float q = __builtin_rintf(s);
+  q = q > 127.f ? 127.f : (q < -127.f ? -127.f : q);
+  return (uint32_t)(int)q & 0xFFu;
+}
+
+// Block constant of a stored entry c (the 8-bit code, or for kDqNone the FP32 bits).
+template <int DQ>
+__device__ __forceinline__ float block_scale_fmt(uint32_t c, float c2s, float mu) {
+  if (DQ == kDqNone) return __uint_as_float(c);
+  const float v = DQ == kDqE4M3 ? e4m3_to_f32(c) : (DQ == kDqE5M2 ? e5m2_to_f32(c) : (float)(int8_t)(uint8_t)c);
+  return __fadd_rn(__fmul_rn(v, c2s), mu);
+}
+
 // ---------------------------------------------------------------- byte-permute LUT decode
 //
 // A 16-entry byte table t0..t3 (entry j at dword j/4, byte j%4) is looked up for the four

@@ -13,6 +13,9 @@ namespace qlora {
 
 void build_nf4_tables(Nf4Tables* t);
 const Nf4Tables& nf4_tables();
+// First-level codebooks: 0 NF4, 1 uniform INT4, 2 FP4 (E2M1 levels).
+void build_codebook_tables(int codebook, Nf4Tables* t);
+const Nf4Tables& codebook_tables(int codebook);
 
 // Start/stop events for one kernel launch when timing is enabled for its id (see
 // qlora_timing_*), else null.  Launch with hipExtLaunchKernelGGL(..., t.start, t.stop, 0,
@@ -27,21 +30,23 @@ struct LaunchTimer {
 hipError_t launch_quant_pass1(const void* W, bool w_bf16, uint32_t* codes, float* c1, unsigned long long* hist,
                               int* flag, int64_t n_words, const Nf4Tables& T, hipStream_t s);
 hipError_t launch_quant_pass2(const float* c1, float mu, uint8_t* code8, float* c2s, float* mu_out,
-                              int64_t n_blocks, hipStream_t s);
+                              int64_t n_blocks, int dq, hipStream_t s);
 hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t s);
+// dq: second-level format of the block constants (kDqE4M3 .. kDqNone; for kDqNone code8
+// holds FP32 constants and c2s, mu are not read).
 hipError_t launch_dequant(const uint32_t* codes, const uint8_t* code8, const float* c2s,
-                          const float* mu, uint16_t* out, int64_t n_words, const Nf4Tables& T,
+                          const float* mu, uint16_t* out, int64_t n_words, const Nf4Tables& T, int dq,
                           hipStream_t s);
 
 // w_hat^T [K, N] BF16 (transposed decode; the dX operand).
 hipError_t launch_dequant_t(const uint32_t* codes, const uint8_t* code8, const float* c2s,
-                            const float* mu, int64_t N, int64_t K, uint16_t* out, const Nf4Tables& T,
+                            const float* mu, int64_t N, int64_t K, uint16_t* out, const Nf4Tables& T, int dq,
                             hipStream_t s);
 
 // ---- merged export (merge.hip): out [N, K] BF16 = bf16(w_hat + s B A), B [N, r], A [r, K]
 hipError_t launch_merge(const uint32_t* codes, const uint8_t* code8, const float* c2s, const float* mu,
                         const uint16_t* A, const uint16_t* B, int64_t N, int64_t K, int32_t r, float s,
-                        uint16_t* out, const Nf4Tables& T, hipStream_t st);
+                        uint16_t* out, const Nf4Tables& T, int dq, hipStream_t st);
 
 // ---- adapter optimizer step (adamw.hip): scalars formed on the host in FP64, rounded once
 struct AdamWScalars {

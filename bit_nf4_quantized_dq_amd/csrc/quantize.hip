@@ -9,6 +9,8 @@
 //   "QLoRA -- Fine-Tuning a 65B Model on One GPU", "Double quantization"): the constants
 //   are centred on their mean mu and quantized to 8-bit floats in groups of 256 with one
 //   FP32 constant per group: c2s = fl32(max|c1 - mu| / 448), code8 = E4M3(fl32(d / c2s)).
+//   The comparison formats swap E4M3 for E5M2 (top 57344) or a symmetric 8-bit integer (top
+//   127); without double quantization pass 1 writes c1 straight into the constant buffer.
 //
 // Memory layout: W FP32 or BF16 [d_out*d_in] is read as 8-value words (one packed code word
 // each); a wavefront covers 8 blocks of W with 16-byte lane loads.  A BF16 checkpoint (the
@@ -71,8 +73,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_pass1(const void* __restrict
 #pragma unroll
     for (int i = 0; i < 8; ++i) c[i] = nf4_code(__fdiv_rn(v[i], mx), T);
   } else {
+    const uint32_t z = nf4_code(0.f, T);  // the level nearest 0, ties low (8 for NF4)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = 8u;
+    for (int i = 0; i < 8; ++i) c[i] = z;
   }
   uint32_t word = 0;
 #pragma unroll
@@ -98,6 +101,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_pass1(const void* __restrict
 }
 
 // One wavefront per group of 256 constants; lane l owns constants 4l..4l+3 of the group.
+// DQ selects the 8-bit format: E4M3 (top 448), E5M2 (top 57344) or INT8 (top 127).
+template <int DQ>
 __global__ __launch_bounds__(kThreads) void k_quant_pass2(const float* __restrict__ c1, float mu,
                                                           uint8_t* __restrict__ code8,
                                                           float* __restrict__ c2s,
@@ -119,10 +124,14 @@ __global__ __launch_bounds__(kThreads) void k_quant_pass2(const float* __restric
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  const float c2 = __fdiv_rn(m, 448.0f);
+  const float top = DQ == kDqE4M3 ? 448.0f : (DQ == kDqE5M2 ? 57344.0f : 127.0f);
+  const float c2 = __fdiv_rn(m, top);
   uint32_t q[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) q[j] = (c2 > 0.f) ? f32_to_e4m3(__fdiv_rn(d[j], c2)) : 0u;
+  for (int j = 0; j < 4; ++j) {
+    const float t = __fdiv_rn(d[j], c2);
+    q[j] = (c2 > 0.f) ? (DQ == kDqE4M3 ? f32_to_e4m3(t) : (DQ == kDqE5M2 ? f32_to_e5m2(t) : f32_to_int8(t))) : 0u;
+  }
   if (base + 3 < n_blocks && (base & 3) == 0) {
     *reinterpret_cast<uint32_t*>(code8 + base) = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
   } else {
@@ -155,12 +164,17 @@ hipError_t launch_quant_pass1(const void* W, bool w_bf16, uint32_t* codes, float
 }
 
 hipError_t launch_quant_pass2(const float* c1, float mu, uint8_t* code8, float* c2s, float* mu_out,
-                              int64_t n_blocks, hipStream_t s) {
+                              int64_t n_blocks, int dq, hipStream_t s) {
   const int64_t n_groups = (n_blocks + kBlock2 - 1) / kBlock2;
   const int64_t grid = (n_groups + 3) / 4;
   LaunchTimer t(1, s);
-  hipExtLaunchKernelGGL(k_quant_pass2, dim3((unsigned)grid), dim3(kThreads), 0, s, t.start, t.stop, 0, c1, mu, code8, c2s,
-                     mu_out, n_blocks);
+  auto go = [&](auto kern) {
+    hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, s, t.start, t.stop, 0, c1, mu, code8, c2s, mu_out,
+                          n_blocks);
+  };
+  if (dq == kDqE5M2) go(k_quant_pass2<kDqE5M2>);
+  else if (dq == kDqInt8) go(k_quant_pass2<kDqInt8>);
+  else go(k_quant_pass2<kDqE4M3>);
   return hipGetLastError();
 }
 

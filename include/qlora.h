@@ -46,24 +46,49 @@ enum qlora_status {
   QLORA_ERR_INVALID_ARG = -1, /* null pointer, M < 1, r outside [1, 128], alpha not finite */
   QLORA_ERR_BAD_SHAPE = -2,   /* d_in % 64 != 0, d_out % 16 != 0, d_in or d_out > 2^22,
                                  d_out * d_in > 2^32 (32-bit buffer offsets) */
-  QLORA_ERR_UNSUPPORTED = -3, /* block sizes other than (64, 256) */
+  QLORA_ERR_UNSUPPORTED = -3, /* block sizes other than (64, 256), unknown codebook or format */
   QLORA_ERR_NONFINITE = -4,   /* NaN or Inf in the weights given to qlora_quantize */
   QLORA_ERR_WORKSPACE = -5,   /* workspace pointer null or smaller than required */
   QLORA_ERR_HIP = -6          /* a HIP runtime call or kernel launch failed */
 };
 
+/* First-level codebooks: the 16 levels a 4-bit code indexes ("QLoRA: Quantize Base Weights
+ * to 4-Bit", Section 2 "1. 4-bit NormalFloat", compares NF4 with standard INT4 and FP4). */
+enum qlora_codebook {
+  QLORA_CB_NF4 = 0,  /* NormalFloat: normal-quantile levels, exact 0 and +-1 (the method) */
+  QLORA_CB_INT4 = 1, /* 16 evenly spaced levels -1 + 2i/15 (no zero level) */
+  QLORA_CB_FP4 = 2   /* E2M1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 over 6, both signs (15 levels) */
+};
+
+/* Second-level format of the block constants ("QLoRA: Quantize Base Weights to 4-Bit",
+ * Section 2 "2. Double Quantization"; the pages call the 8-bit format both a float and an
+ * integer, and give FP32 constants, 0.5 bits/param, as the case without it). */
+enum qlora_dq_format {
+  QLORA_DQ_E4M3 = 0, /* OCP FP8 E4M3, group constant max|d| / 448 (the method) */
+  QLORA_DQ_E5M2 = 1, /* OCP FP8 E5M2, group constant max|d| / 57344 */
+  QLORA_DQ_INT8 = 2, /* symmetric 8-bit integer, group constant max|d| / 127 */
+  QLORA_DQ_NONE = 3  /* no double quantization: one FP32 constant per block in code8 */
+};
+
 /* A quantized weight tensor.  The struct and the buffers it points to belong to the
- * caller.  Sizes come from qlora_quant_sizes.  After qlora_quantize fills it, it is
- * read-only to every other entry point.
+ * caller.  Sizes come from qlora_quant_sizes (or qlora_format_sizes for another second-level
+ * format).  After qlora_quantize fills it, it is read-only to every other entry point.
  *
  *   codes : device uint8[d_out * d_in / 2].  4-bit level indices, row-major; each aligned
  *           run of 8 weights e0..e7 is 4 bytes, byte i = e_i | (e_{i+4} << 4).
- *   code8 : device uint8[d_out * d_in / 64].  One OCP FP8 E4M3 bit pattern per block of
- *           64 consecutive weights (the double-quantized, mean-shifted block constant).
+ *   code8 : device uint8[d_out * d_in / 64].  One 8-bit code per block of 64 consecutive
+ *           weights (the double-quantized, mean-shifted block constant; E4M3 by default).
+ *           With QLORA_DQ_NONE: device float[d_out * d_in / 64], the constants themselves.
  *   c2s   : device float[ceil(n_blocks / 256)].  The FP32 second-level constant of each
- *           group of 256 consecutive blocks (flattened order).
- *   mu    : device float[1].  The mean of all first-level constants of the tensor.
- *   block1, block2 : must be 64 and 256. */
+ *           group of 256 consecutive blocks (flattened order).  Unused (may be NULL) with
+ *           QLORA_DQ_NONE.
+ *   mu    : device float[1].  The mean of all first-level constants of the tensor.  Unused
+ *           (may be NULL) with QLORA_DQ_NONE.
+ *   block1, block2 : must be 64 and 256.
+ *   codebook  : an enum qlora_codebook value; 0, the default, is NF4.
+ *   dq_format : an enum qlora_dq_format value; 0, the default, is E4M3.  The fused decode of the
+ *           weight-streaming and mid-size kernels reads E4M3 only; other formats are decoded
+ *           once per call into a BF16 copy at every token count (more workspace). */
 typedef struct qlora_nf4dq {
   uint8_t *codes;
   uint8_t *code8;
@@ -73,6 +98,8 @@ typedef struct qlora_nf4dq {
   int64_t d_in;
   int32_t block1;
   int32_t block2;
+  int32_t codebook;
+  int32_t dq_format;
 } qlora_nf4dq_t;
 
 /* Bytes of the three buffers of a [d_out, d_in] tensor (mu is always 4 bytes).
@@ -80,10 +107,18 @@ typedef struct qlora_nf4dq {
 int qlora_quant_sizes(int64_t d_out, int64_t d_in, size_t *codes_bytes, size_t *code8_bytes,
                       size_t *c2s_bytes);
 
-/* Workspace bytes needed by one call of `op` (QLORA_OP_*) at these sizes.  Host only. */
+/* The same for a given second-level format: with QLORA_DQ_NONE code8 holds 4 bytes per
+ * block and there is no c2s.  Host only.  Errors: as above, UNSUPPORTED (unknown format). */
+int qlora_format_sizes(int64_t d_out, int64_t d_in, int dq_format, size_t *codes_bytes,
+                       size_t *code8_bytes, size_t *c2s_bytes);
+
+/* Workspace bytes needed by one call of `op` (QLORA_OP_*) at these sizes, for E4M3
+ * constants (qlora_workspace_size) or the given second-level format.  Host only. */
 enum qlora_op { QLORA_OP_QUANTIZE = 0, QLORA_OP_FWD = 1, QLORA_OP_BWD = 2 };
 int qlora_workspace_size(int op, int64_t M, int64_t d_out, int64_t d_in, int32_t r,
                          size_t *ws_bytes);
+int qlora_workspace_size_fmt(int op, int64_t M, int64_t d_out, int64_t d_in, int32_t r,
+                             int dq_format, size_t *ws_bytes);
 
 /* The FP32 NF4 table the library uses (host memory, 16 floats), built from the
  * normal-quantile formula of "QLoRA: Quantize Base Weights to 4-Bit", Section 2
@@ -92,12 +127,18 @@ int qlora_workspace_size(int op, int64_t M, int64_t d_out, int64_t d_in, int32_t
  * One GPU", "NF4"). */
 int qlora_nf4_codebook(float out16[16]);
 
+/* The FP32 levels of any first-level codebook (QLORA_CB_*), host memory, 16 floats.
+ * Errors: INVALID_ARG (null output or unknown codebook). */
+int qlora_codebook(int codebook, float out16[16]);
+
 /* Quantize FP32 weights W (device, [d_out, d_in], d_in % 64 == 0) into *Wq, whose
  * buffers the caller allocated.  First level: c1 = max|w| per 64-block, code = nearest
- * level to fl32(w / c1), ties to the lower level, an all-zero block gets the zero level.
+ * level of Wq->codebook to fl32(w / c1), ties to the lower level; an all-zero block gets
+ * the level nearest 0 (the zero level of NF4).
  * Double quantization: mu = FP32 of the exact mean of all c1; d = fl32(c1 - mu); per group
  * of 256 blocks c2s = fl32(max|d| / 448) and code8 = E4M3(fl32(d / c2s)) rounded to
- * nearest, ties to even (0 when c2s == 0).
+ * nearest, ties to even (0 when c2s == 0).  Other second-level formats use 57344 and E5M2,
+ * or 127 and a round-half-even integer; QLORA_DQ_NONE stores c1 in code8 (mu not written).
  * ws: device, qlora_workspace_size(QLORA_OP_QUANTIZE) bytes.  host_mu: host float, may be
  * NULL.  SYNCHRONIZES `stream` once (to fold the exact mean on the host).
  * Errors: INVALID_ARG, BAD_SHAPE, UNSUPPORTED, NONFINITE (then Wq's contents are

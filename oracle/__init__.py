@@ -40,4 +40,10 @@ from .qlora_oracle import (  # noqa: F401
     merge,
     quantize_bf16,
     adamw_step,
+    CODEBOOKS,
+    DQ_FORMATS,
+    codebook,
+    e5m2_value,
+    e5m2_encode,
+    int8_encode,
 )

@@ -179,6 +179,81 @@ def e4m3_encode(s: np.ndarray) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------------------
+# Format variants: other 16-level codebooks and other second-level formats
+# --------------------------------------------------------------------------------------
+
+CODEBOOKS = ("nf4", "int4", "fp4")
+DQ_FORMATS = ("e4m3", "e5m2", "int8", "none")
+E5M2_MAX = 57344.0  # largest finite OCP FP8 E5M2 value (S.11110.11 = 1.75 * 2^15)
+INT8_MAX = 127.0
+
+
+def codebook(name: str = "nf4") -> np.ndarray:
+    """16 ascending FP32 levels of a first-level codebook (absmax-normalized to [-1, 1]).
+
+    nf4  : the NormalFloat levels (:func:`nf4_codebook`).
+    int4 : standard 4-bit integer quantization, 16 evenly spaced levels over the range
+           ([4-Bit] Sec. 2 "1. 4-bit NormalFloat": INT4 divides the range into equal steps;
+           reading: the 16 levels -1 + 2 i / 15, so both ends are exact and there is no 0).
+    fp4  : the magnitudes of a 4-bit float with 2 exponent and 1 mantissa bit (E2M1:
+           0, 0.5, 1, 1.5, 2, 3, 4, 6), both signs, scaled by 1/6 so the ends are +-1; +0 and
+           -0 are one level, so the 16th entry repeats +1 (it is never nearest first).
+    Each value is its float64 rounded once to FP32."""
+    if name == "nf4":
+        return nf4_codebook()
+    if name == "int4":
+        return np.array([np.float32((2.0 * i - 15.0) / 15.0) for i in range(16)], dtype=np.float32)
+    if name == "fp4":
+        mags = [6.0, 4.0, 3.0, 2.0, 1.5, 1.0, 0.5]
+        vals = [-m / 6.0 for m in mags] + [0.0] + [m / 6.0 for m in reversed(mags)] + [1.0]
+        return np.array([np.float32(v) for v in vals], dtype=np.float32)
+    raise ValueError(name)
+
+
+def e5m2_value(code) -> np.ndarray:
+    """Value of an OCP E5M2 bit pattern as float64: sign, 5 exponent bits (bias 15), 2
+    mantissa bits; exponent 0 is subnormal (m/4 * 2^-14); exponent 31 is Inf/NaN."""
+    b = np.asarray(code, dtype=np.int64)
+    sign = np.where((b >> 7) & 1, -1.0, 1.0)
+    e = (b >> 2) & 0x1F
+    m = b & 0x3
+    mag = np.where(e == 0, (m / 4.0) * 2.0**-14, (1.0 + m / 4.0) * np.exp2(e.astype(np.float64) - 15))
+    return np.where(e == 31, np.nan, sign * mag)
+
+
+_E5M2_POS_CODES = np.arange(0x00, 0x7C, dtype=np.int64)  # 0x00..0x7B: all finite non-negative
+_E5M2_POS_VALS = e5m2_value(_E5M2_POS_CODES)
+
+
+def e5m2_encode(s: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest finite E5M2 value, ties to the even code, beyond
+    57344 to 57344; the sign bit is the sign of s.  Brute force over the 124 finite
+    magnitudes, as :func:`e4m3_encode`."""
+    s = np.asarray(s, dtype=np.float32)
+    flat = s.reshape(-1).astype(np.float64)
+    neg = np.signbit(s.reshape(-1))
+    mag = np.abs(flat)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    for st in range(0, flat.size, 1 << 16):
+        a = mag[st : st + (1 << 16)]
+        dist = np.abs(a[:, None] - _E5M2_POS_VALS[None, :])
+        first = np.argmin(dist, axis=1)
+        dmin = dist[np.arange(a.size), first]
+        nxt = np.minimum(first + 1, _E5M2_POS_VALS.size - 1)
+        tie = (nxt != first) & (dist[np.arange(a.size), nxt] == dmin)
+        out[st : st + (1 << 16)] = np.where(tie & (first % 2 == 1), nxt, first).astype(np.uint8)
+    out = np.where(neg, out | 0x80, out).astype(np.uint8)
+    return out.reshape(s.shape)
+
+
+def int8_encode(s: np.ndarray) -> np.ndarray:
+    """Symmetric 8-bit integer code of float32 values: round half to even, clamp to
+    [-127, 127], stored as the two's-complement byte."""
+    q = np.clip(np.rint(np.asarray(s, dtype=np.float32).astype(np.float64)), -INT8_MAX, INT8_MAX)
+    return q.astype(np.int64).astype(np.int8).view(np.uint8)
+
+
+# --------------------------------------------------------------------------------------
 # BF16 rounding
 # --------------------------------------------------------------------------------------
 
@@ -200,7 +275,8 @@ def bf16_bits_to_f32(b) -> np.ndarray:
 # --------------------------------------------------------------------------------------
 
 
-def quantize(W: np.ndarray, blocks: np.ndarray | None = None) -> dict:
+def quantize(W: np.ndarray, blocks: np.ndarray | None = None, codebook_name: str = "nf4",
+             dq: str = "e4m3") -> dict:
     """Quantize an FP32 weight matrix W[d_out, d_in] (d_in % 64 == 0).
 
     `blocks` (optional boolean mask over the flattened 64-blocks) restricts which blocks
@@ -219,26 +295,44 @@ def quantize(W: np.ndarray, blocks: np.ndarray | None = None) -> dict:
          per group c2s = fl32(max|d| / 448) is the FP32 second-level constant, and
          code8 = E4M3_RNE(fl32(d / c2s)) (code8 = 0 when c2s == 0).
     Returns a dict of the stored buffers plus the transient c1 and the unpacked codes.
+
+    Format variants (the error study of the pages' comparisons: [4-Bit] Sec. 2 "1. 4-bit
+    NormalFloat" against INT4 and FP4; Sec. 2 "2. Double Quantization" and [Consumer] FAQ
+    for the 8-bit format of the constants, which the pages call both "8-bit floats" and
+    "8-bit integers"; [4-Bit] Sec. 2 for FP32 constants without double quantization):
+      codebook_name : "nf4" (default), "int4" or "fp4" (:func:`codebook`).  An all-zero
+                      block takes the code of the level nearest 0 (ties low): 8 for NF4.
+      dq            : "e4m3" (default), "e5m2" (c2s = max|d| / 57344), "int8" (c2s =
+                      max|d| / 127, round half to even), or "none": no mean, no second
+                      level; code8 then holds the FP32 c1 themselves.
     """
     W = np.asarray(W, dtype=np.float32)
     assert W.ndim == 2 and W.shape[1] % BLOCK1 == 0
     if not np.all(np.isfinite(W)):
         raise ValueError("non-finite weight")
     d_out, d_in = W.shape
-    table = nf4_codebook()
+    table = codebook(codebook_name)
     sel = None if blocks is None else np.asarray(blocks, dtype=bool).reshape(-1)
 
     blocks = W.reshape(-1, BLOCK1)
     c1 = np.max(np.abs(blocks), axis=1).astype(np.float32)
     n_blocks = c1.size
 
-    codes = np.full(blocks.shape, 8, dtype=np.uint8)
+    zero_code = int(nearest_level(np.zeros(1, np.float32), table)[0])
+    codes = np.full(blocks.shape, zero_code, dtype=np.uint8)
     nz = c1 > 0
     if sel is not None:
         codes[~sel] = 255
         nz = nz & sel
     rho = blocks[nz] / c1[nz][:, None]  # float32 / float32: one IEEE rounding
     codes[nz] = nearest_level(rho, table)
+
+    fmt = {"codebook": codebook_name, "dq": dq}
+    if dq == "none":
+        return {"d_out": d_out, "d_in": d_in, "codes": codes.reshape(d_out, d_in),
+                "packed": pack_codes(codes).reshape(d_out, d_in // 2) if sel is None else None,
+                "c1": c1, "mu": np.float32(0.0), "code8": c1.copy(), "c2s": np.zeros(0, np.float32), **fmt}
+    top, enc = {"e4m3": (E4M3_MAX, e4m3_encode), "e5m2": (E5M2_MAX, e5m2_encode), "int8": (INT8_MAX, int8_encode)}[dq]
 
     mu = np.float32(math.fsum(c1.astype(np.float64).tolist()) / n_blocks)
 
@@ -249,11 +343,12 @@ def quantize(W: np.ndarray, blocks: np.ndarray | None = None) -> dict:
     for g in range(n_groups):
         seg = d[g * BLOCK2 : (g + 1) * BLOCK2]
         m = np.max(np.abs(seg))
-        c2 = np.float32(m / np.float32(E4M3_MAX))
+        c2 = np.float32(m / np.float32(top))
         c2s[g] = c2
         if c2 > 0:
-            code8[g * BLOCK2 : (g + 1) * BLOCK2] = e4m3_encode((seg / c2).astype(np.float32))
+            code8[g * BLOCK2 : (g + 1) * BLOCK2] = enc((seg / c2).astype(np.float32))
     return {
+        **fmt,
         "d_out": d_out,
         "d_in": d_in,
         "codes": codes.reshape(d_out, d_in),
@@ -265,15 +360,24 @@ def quantize(W: np.ndarray, blocks: np.ndarray | None = None) -> dict:
     }
 
 
-def decode_scales(code8: np.ndarray, c2s: np.ndarray, mu) -> np.ndarray:
-    """Recovered first-level constants: c1_hat = fl32(fl32(E4M3(code8) * c2s) + mu).
+def decode_scales(code8: np.ndarray, c2s: np.ndarray, mu, dq: str = "e4m3") -> np.ndarray:
+    """Recovered first-level constants: c1_hat = fl32(fl32(v(code8) * c2s) + mu), v the value
+    of the 8-bit code (E4M3 by default, E5M2 or the signed integer); for dq = "none" the
+    stored FP32 constants themselves.
 
     Two separate FP32 roundings, undoing the mean shift and the second-level scaling of
     [4-Bit] Sec. 2 "2. Double Quantization" / [65B] "Double quantization"."""
+    if dq == "none":
+        return np.asarray(code8, dtype=np.float32).copy()
     code8 = np.asarray(code8, dtype=np.uint8)
     n = code8.size
     grp = np.arange(n) // BLOCK2
-    v = e4m3_value(code8).astype(np.float32)  # every finite E4M3 value is exact in FP32
+    if dq == "e4m3":
+        v = e4m3_value(code8).astype(np.float32)  # every finite E4M3 value is exact in FP32
+    elif dq == "e5m2":
+        v = e5m2_value(code8).astype(np.float32)
+    else:
+        v = code8.view(np.int8).astype(np.float32)
     prod = (v * np.asarray(c2s, dtype=np.float32)[grp]).astype(np.float32)
     return (prod + np.float32(mu)).astype(np.float32)
 
@@ -283,8 +387,8 @@ def dequantize_bf16_bits(q: dict) -> np.ndarray:
     w_hat = bf16(fl32(q[code] * c1_hat)) -- a lookup and a multiply ([65B] "Quantization
     in one paragraph"), rounded to the BF16 compute type ([4-Bit] Sec. 3).
     Blocks whose codes were not computed (code 255) decode to NaN."""
-    table = np.concatenate([nf4_codebook(), np.full(240, np.nan, np.float32)])
-    c1h = decode_scales(q["code8"], q["c2s"], q["mu"])
+    table = np.concatenate([codebook(q.get("codebook", "nf4")), np.full(240, np.nan, np.float32)])
+    c1h = decode_scales(q["code8"], q["c2s"], q["mu"], q.get("dq", "e4m3"))
     codes = q["codes"].reshape(-1, BLOCK1)
     vals = (table[codes] * c1h[:, None]).astype(np.float32)
     bits = bf16_round_bits(np.where(np.isnan(vals), 0, vals))
@@ -337,12 +441,15 @@ def lora_bwd(W_hat: np.ndarray, X: np.ndarray, dY: np.ndarray, A: np.ndarray, B:
 # --------------------------------------------------------------------------------------
 
 
-def quant_sizes(d_out: int, d_in: int) -> dict:
+def quant_sizes(d_out: int, d_in: int, dq: str = "e4m3") -> dict:
     """Bytes of each stored buffer: 4-bit codes, one 8-bit constant per 64 weights, one
-    FP32 second-level constant per 256 constants, and one FP32 mean per tensor."""
+    FP32 second-level constant per 256 constants, and one FP32 mean per tensor; without
+    double quantization one FP32 constant per 64 weights and nothing else."""
     n = d_out * d_in
     n_blocks = n // BLOCK1
     n_groups = -(-n_blocks // BLOCK2)
+    if dq == "none":
+        return {"codes": n // 2, "code8": 4 * n_blocks, "c2s": 0, "mu": 0}
     return {"codes": n // 2, "code8": n_blocks, "c2s": 4 * n_groups, "mu": 4}
 
 
@@ -394,11 +501,12 @@ def merge(q: dict, A: np.ndarray, B: np.ndarray, alpha: float, r: int):
     return bf16_round_f64_bits(exact), exact
 
 
-def quantize_bf16(W_bits: np.ndarray, blocks: np.ndarray | None = None) -> dict:
+def quantize_bf16(W_bits: np.ndarray, blocks: np.ndarray | None = None, codebook_name: str = "nf4",
+                  dq: str = "e4m3") -> dict:
     """Quantize a BF16 weight matrix (bit patterns).  Every BF16 value is exact in FP32,
     so this is :func:`quantize` of the widened values: the 16-bit checkpoint a model ships
     in is quantized as it stands ([4-Bit] Sec. 1: the frozen base lives in 16 bits)."""
-    return quantize(bf16_bits_to_f32(W_bits), blocks)
+    return quantize(bf16_bits_to_f32(W_bits), blocks, codebook_name, dq)
 
 
 # --------------------------------------------------------------------------------------

@@ -24,7 +24,7 @@ def L():
 def test_every_declared_symbol_is_exported(L):
     text = open(HEADER).read()
     names = sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text)))
-    assert len(names) == 14
+    assert len(names) == 17
     for n in names:
         assert hasattr(L, n), n
 
@@ -47,9 +47,9 @@ def test_bits_per_param_from_library_sizes():
     assert round(bpp, 3) == 4.127
 
 
-def _wq(d_out=256, d_in=256, b1=64, b2=256):
+def _wq(d_out=256, d_in=256, b1=64, b2=256, cb=0, dq=0, c2s=4096):
     dummy = ctypes.c_void_p(4096)  # never dereferenced: validation fails first
-    return B._Nf4dq(dummy, dummy, dummy, dummy, d_out, d_in, b1, b2)
+    return B._Nf4dq(dummy, dummy, ctypes.c_void_p(c2s) if c2s else None, dummy, d_out, d_in, b1, b2, cb, dq)
 
 
 def test_shape_and_argument_errors_before_launch(L):
@@ -82,6 +82,17 @@ def test_shape_and_argument_errors_before_launch(L):
     assert L.qlora_merge(ctypes.byref(_wq()), dummy, dummy, 8, 16.0, ctypes.c_void_p(4098), None) == -1
     assert L.qlora_merge(ctypes.byref(_wq(d_out=250)), dummy, dummy, 8, 16.0, dummy, None) == -2
     assert L.qlora_merge(ctypes.byref(_wq(b1=32)), dummy, dummy, 8, 16.0, dummy, None) == -3
+    # formats: unknown codebook or second-level format, missing c2s where it is needed
+    assert L.qlora_dequantize(ctypes.byref(_wq(cb=3)), dummy, None) == -3
+    assert L.qlora_dequantize(ctypes.byref(_wq(dq=4)), dummy, None) == -3
+    assert L.qlora_dequantize(ctypes.byref(_wq(dq=-1)), dummy, None) == -3
+    assert L.qlora_dequantize(ctypes.byref(_wq(dq=1, c2s=0)), dummy, None) == -1
+    assert L.qlora_merge(ctypes.byref(_wq(cb=7)), dummy, dummy, 8, 16.0, dummy, None) == -3
+    assert L.qlora_linear_fwd(ctypes.byref(_wq(dq=9)), dummy, 4, dummy, dummy, 8, 16.0, dummy, None, ws, 1 << 20, None) == -3
+    n = ctypes.c_size_t()
+    assert L.qlora_workspace_size_fmt(1, 4, 256, 256, 8, 7, ctypes.byref(n)) == -3
+    f16 = (ctypes.c_float * 16)()
+    assert L.qlora_codebook(3, f16) == -1 and L.qlora_codebook(0, None) == -1
     f = ctypes.c_float
     ok = dict(lr=f(1e-3), b1=f(0.9), b2=f(0.999), eps=f(1e-8), wd=f(0.0))
     def adamw(master=dummy, g=dummy, p=dummy, n=16, step=1, **kw):
@@ -107,3 +118,24 @@ def test_workspace_sizes_are_sane():
 def test_strerror_covers_every_status(L):
     for s in range(0, -7, -1):
         assert B._strerror(s) not in ("?", "unknown status")
+
+
+@pytest.mark.parametrize("name", ["nf4", "int4", "fp4"])
+def test_codebooks_equal_oracle_bit_for_bit(name):
+    lib_levels = np.array(B.codebook(name), dtype=np.float32)
+    assert np.array_equal(lib_levels.view(np.uint32), O.codebook(name).view(np.uint32))
+
+
+@pytest.mark.parametrize("dq", ["e4m3", "e5m2", "int8", "none"])
+def test_format_sizes_match_oracle(dq):
+    a, b, c = B.quant_sizes(1024, 4096, dq)
+    sz = O.quant_sizes(1024, 4096, dq)
+    assert (a, b, c) == (sz["codes"], sz["code8"], sz["c2s"])
+
+
+def test_workspace_grows_for_decode_once_formats():
+    """Only E4M3 constants are decoded inside the small-M kernels; other formats need the
+    BF16 weight copy in the workspace at every M."""
+    base = B.workspace_size(B.OP_FWD, 1, 4096, 4096, 16, "e4m3")
+    for dq in ("e5m2", "int8", "none"):
+        assert B.workspace_size(B.OP_FWD, 1, 4096, 4096, 16, dq) >= 2 * 4096 * 4096 > base

@@ -506,3 +506,101 @@ def test_adamw_pure_decay():
         th, m, v, _, _ = O.adamw_step(th, m, v, g, t, 0.01, 0.9, 0.999, 1e-8, 0.5)
     assert np.all(m == 0) and np.all(v == 0)
     assert np.allclose(th, th0.astype(np.float64) * (1 - 0.005) ** 3, rtol=1e-6)
+
+
+# ------------------------------------------------------------------ format variants
+
+def test_variant_codebooks_closed_forms():
+    """INT4: 16 evenly spaced levels -1 + 2i/15; FP4: the E2M1 magnitudes over 6, with the
+    duplicated top level never chosen first."""
+    q = O.codebook("int4").astype(np.float64)
+    exact = np.array([-1 + 2 * i / 15 for i in range(16)])
+    assert np.all(np.abs(q - exact) <= 2.0**-24) and q[0] == -1 and q[15] == 1 and not np.any(q == 0)
+    f = O.codebook("fp4").astype(np.float64)
+    e2m1 = sorted({s * m for s in (-1, 1) for m in (0, 0.5, 1, 1.5, 2, 3, 4, 6)})
+    assert np.all(np.abs(f[:15] * 6 - np.array(e2m1)) <= 6 * 2.0**-24) and f[15] == f[14] == 1
+    assert np.all(np.diff(f[:15]) > 0)
+    # nearest-level assignment never picks the duplicate
+    assert np.all(O.nearest_level(np.linspace(-1, 1, 4001, dtype=np.float32), O.codebook("fp4")) <= 14)
+
+
+def test_e5m2_matches_torch():
+    codes = np.arange(0, 0x7C)
+    assert np.array_equal(O.e5m2_value(codes).astype(np.float32),
+                          torch.from_numpy(codes.astype(np.uint8)).view(torch.float8_e5m2).float().numpy())
+    vals = O.e5m2_value(codes)
+    mids = 0.5 * (vals[:-1] + vals[1:])
+    pts = []
+    for m in np.concatenate([vals, mids]):
+        f = np.float32(m)
+        pts += [f, np.nextafter(f, np.float32(0)), np.nextafter(f, np.float32(1e9))]
+    pts = np.array(pts, np.float32)
+    pts = np.concatenate([pts, -pts, np.random.default_rng(41).uniform(-57344, 57344, 20000).astype(np.float32)])
+    pts = pts[np.abs(pts) <= 57344]
+    ref = torch.from_numpy(pts).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    assert np.array_equal(O.e5m2_encode(pts), ref)
+
+
+def test_int8_encode_rounding_by_hand():
+    s = np.array([0.5, 1.5, 2.5, -0.5, -1.5, 126.5, 127.0, -127.0, 3.49999976, -0.0], np.float32)
+    assert list(O.int8_encode(s).view(np.int8)) == [0, 2, 2, 0, -2, 126, 127, -127, 3, 0]
+
+
+@pytest.mark.parametrize("dq,rel", [("e4m3", 2.0**-4), ("e5m2", 2.0**-3), ("int8", 0.0), ("none", 0.0)])
+def test_variant_double_quant_error_bounds(dq, rel):
+    """|c1 - c1_hat| <= |d| * 2^-(m+1) + c2s * (half a step at the bottom of the format),
+    plus FP32 rounding; exact without double quantization.  INT8 steps are c2s wide."""
+    W = _randW(256, 1024, seed=42)
+    q = O.quantize(W, dq=dq)
+    c1 = q["c1"].astype(np.float64)
+    c1h = O.decode_scales(q["code8"], q["c2s"], q["mu"], dq).astype(np.float64)
+    if dq == "none":
+        assert np.array_equal(c1h, c1)
+        return
+    d = c1 - float(q["mu"])
+    c2s = q["c2s"].astype(np.float64)[np.arange(c1.size) // 256]
+    floor = {"e4m3": 2.0**-10, "e5m2": 2.0**-17, "int8": 0.5}[dq]
+    bound = np.abs(d) * rel + c2s * floor + 2.0**-22 * (np.abs(c1) + np.abs(d))
+    assert np.all(np.abs(c1h - c1) <= bound)
+
+
+def test_nf4_reconstructs_gaussian_weights_best():
+    """The pages' claim ([4-Bit] Sec. 2 "1. 4-bit NormalFloat"; [65B] "NF4"): at the same 4
+    bits, NF4 levels reconstruct normally distributed weights better than evenly spaced
+    INT4 or FP4 levels.  Checked with and without double quantization."""
+    W = _randW(512, 1024, seed=43)
+    for dq in ("e4m3", "none"):
+        mse = {cb: float(np.mean((O.dequantize_f64(O.quantize(W, codebook_name=cb, dq=dq)) - W.astype(np.float64)) ** 2))
+               for cb in O.CODEBOOKS}
+        assert mse["nf4"] < mse["int4"] and mse["nf4"] < mse["fp4"], (dq, mse)
+
+
+def test_variant_storage_bits():
+    """8-bit second-level formats keep the 4.127 bits/param; without double quantization the
+    constants cost 32/64 = 0.5 bits/param ([4-Bit] Sec. 2: 0.500 bits per parameter)."""
+    for dq in ("e4m3", "e5m2", "int8"):
+        sz = O.quant_sizes(4096, 4096, dq)
+        assert 8 * sum(sz.values()) / 4096**2 == pytest.approx(4.127, abs=5e-4)
+    sz = O.quant_sizes(4096, 4096, "none")
+    assert 8 * sum(sz.values()) / 4096**2 == 4.5
+
+
+def test_variant_zero_block_and_exact_special_case():
+    """An all-zero block takes the level nearest 0 (code 8 for NF4, 7 for FP4's zero and for
+    INT4, whose two middle levels tie); with power-of-two constants and every weight a level
+    times that constant, every format reproduces bf16(W) exactly without double
+    quantization."""
+    W = np.zeros((2, 64), np.float32)
+    assert np.all(O.quantize(W, codebook_name="int4", dq="none")["codes"] == 7)
+    assert np.all(O.quantize(W, codebook_name="fp4", dq="none")["codes"] == 7)
+    assert np.all(O.quantize(W)["codes"] == 8)
+    rng = np.random.default_rng(44)
+    for cb in O.CODEBOOKS:
+        t = O.codebook(cb)
+        k = rng.integers(0, 15, size=(16, 256))
+        k[:, ::64] = 0
+        W = (t[k] * np.float32(2.0**-6)).astype(np.float32)
+        q = O.quantize(W, codebook_name=cb, dq="none")
+        assert np.array_equal(t[q["codes"]], t[k])
+        exp = torch.from_numpy(W).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(O.dequantize_bf16_bits(q), exp)
