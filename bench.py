@@ -15,9 +15,12 @@ same linear (128 distinct quantized copies rotated so every call reads HBM), the
 rate, the merged-export rate (w_hat + s B A to BF16 over the same rotated copies), the
 AdamW step over the 41.9M adapter parameters of a Llama-3-8B-shaped model, an error study of
 the format variants (codebook x second-level format: bits/weight, reconstruction error,
-decode time), and the CPU oracle timed on a bounded sample of the same workload.
+decode time), the other two named workloads (all seven linears of a Llama-3-8B-shaped layer
+at M = 8192, fwd + bwd; a 70B-class model's 560 linears, ~35 GB of NF4+DQ resident, forward at
+M = 1 by graph replay and at M = 2048), and the CPU oracle timed on a bounded sample of the
+same workload.
 
-  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-extra]
   python bench.py --pmc-pass    # 2 steps, one merge, one AdamW step and a 256 MiB device
                                 # copy (the counter calibration), for counter runs
 """
@@ -80,6 +83,124 @@ def merge_bytes(N, K, r):
     return N * K // 2 + N * K // 64 + 4 * ((N * K // 64 + 255) // 256) + 4 + 2 * r * (N + K) + 2 * N * K
 
 
+def llama3_8b_layer(dev, steps=3, warmup=1):
+    """Llama-3-8B-shaped decoder layer: all seven linears (q, k, v, o, gate, up, down), LoRA
+    r = 16 on each, M = 8192 tokens; a step is the seven forwards then the seven backwards."""
+    import torch
+
+    import bit_nf4_quantized_dq_amd as Q
+    from bit_nf4_quantized_dq_amd import inputs as I
+
+    M, r, alpha = 8192, 16, 32.0
+    lin, flops, wsf, wsb = [], 0, 0, 0
+    for idx, shp in enumerate(I.LLAMA3_8B_LAYER):
+        N, K = shp.d_out, shp.d_in
+        W = I.weight(4, idx, N, K, 0.02, device=dev)
+        q = Q.quantize(W)
+        del W
+        t = dict(q=q, X=I.activations(4, idx, M, K, device=dev), dY=I.grad_out(4, idx, M, N, device=dev),
+                 A=I.lora_A(4, idx, r, K, device=dev), B=I.lora_B(4, idx, N, r, device=dev),
+                 Y=torch.empty(M, N, dtype=torch.bfloat16, device=dev), T=torch.empty(M, r, dtype=torch.bfloat16, device=dev),
+                 dX=torch.empty(M, K, dtype=torch.bfloat16, device=dev), dA=torch.empty(r, K, dtype=torch.bfloat16, device=dev),
+                 dB=torch.empty(N, r, dtype=torch.bfloat16, device=dev))
+        lin.append(t)
+        flops += step_flops(M, N, K, r)
+        wsf = max(wsf, Q.workspace_size(Q.OP_FWD, M, N, K, r))
+        wsb = max(wsb, Q.workspace_size(Q.OP_BWD, M, N, K, r))
+    ws_f = torch.empty(wsf, dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+    def step():
+        for t in lin:
+            Q.linear_fwd(t["q"], t["X"], t["A"], t["B"], alpha, Y=t["Y"], T_save=t["T"], ws=ws_f)
+        for t in reversed(lin):
+            Q.linear_bwd(t["q"], t["X"], t["dY"], t["A"], t["B"], alpha, T_saved=t["T"], dX=t["dX"], dA=t["dA"],
+                         dB=t["dB"], ws=ws_b)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / steps
+    return {"metric": "NF4+DQ decoder-layer linears fwd+bwd TFLOP/s (7 linears, M=8192, r=16)",
+            "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": round(ms, 3),
+            "step_tflop": round(flops / 1e12, 4), "steps": steps,
+            "roofline_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
+def seventy_b_model(dev, layers=80, passes=3):
+    """70B-class model: 80 layers x 7 linears (q, o 8192^2; k, v 1024x8192; gate, up
+    28672x8192; down 8192x28672), NF4+DQ resident on the GPU (~35 GB), LoRA r = 16 on every
+    linear.  M = 1: one forward through all linears, captured once in a HIP graph and replayed
+    (every call streams its own weights from HBM).  M = 2048: one eager forward pass."""
+    import torch
+
+    import bit_nf4_quantized_dq_amd as Q
+    from bit_nf4_quantized_dq_amd import inputs as I
+
+    r, alpha = 16, 32.0
+    lin, nbytes1, flops2048 = [], 0, 0
+    for layer in range(layers):
+        for idx, shp in enumerate(I.SEVENTY_B_LAYER):
+            N, K = shp.d_out, shp.d_in
+            W = I.weight(5, idx, N, K, 0.015, layer, device=dev)
+            q = Q.quantize(W)
+            del W
+            lin.append((q, I.lora_A(5, idx, r, K, layer, device=dev), I.lora_B(5, idx, N, r, layer, device=dev)))
+            nbytes1 += stream_bytes(1, N, K, r)
+            flops2048 += 2 * 2048 * N * K + 2 * 2048 * r * (N + K)
+    weights_gb = sum(q.nbytes() for q, _, _ in lin) / 1e9
+    shapes = {(s.d_out, s.d_in) for s in I.SEVENTY_B_LAYER}
+    out = {"weights_GB": round(weights_gb, 3), "linears": len(lin)}
+    for M in (1, 2048):
+        Xs = {K: I.activations(5, 99, M, K, device=dev) for _, K in shapes}
+        Ys = {N: torch.empty(M, N, dtype=torch.bfloat16, device=dev) for N, _ in shapes}
+        ws = torch.empty(max(Q.workspace_size(Q.OP_FWD, M, N, K, r) for N, K in shapes), dtype=torch.uint8, device=dev)
+
+        def fwd_pass():
+            for q, A, B in lin:
+                Q.linear_fwd(q, Xs[q.d_in], A, B, alpha, Y=Ys[q.d_out], ws=ws)
+
+        fwd_pass()
+        torch.cuda.synchronize()
+        if M == 1:
+            g = torch.cuda.CUDAGraph()
+            cap = torch.cuda.Stream()
+            cap.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(cap):
+                with torch.cuda.graph(g, stream=cap):
+                    fwd_pass()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(passes):
+                g.replay()
+            torch.cuda.synchronize()
+            ms = 1e3 * (time.perf_counter() - t0) / passes
+            out["M1"] = {"metric": "weight-stream GB/s at M=1 through all 560 linears (graph replay)",
+                         "value": round(nbytes1 / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "ms_per_pass": round(ms, 3),
+                         "bytes_per_pass": nbytes1, "frac_of_hbm_peak": round(nbytes1 / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            del g
+        else:
+            t0 = time.perf_counter()
+            for _ in range(passes):
+                fwd_pass()
+            torch.cuda.synchronize()
+            ms = 1e3 * (time.perf_counter() - t0) / passes
+            out["M2048"] = {"metric": "forward TFLOP/s at M=2048 through all 560 linears",
+                            "value": round(flops2048 / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                            "ms_per_pass": round(ms, 2), "tflop_per_pass": round(flops2048 / 1e12, 2),
+                            "roofline_frac": round(flops2048 / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del Xs, Ys, ws
+    del lin
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(N, K, r, alpha, target_s=15.0):
     """The oracle as it stands, on the host cores: dequantize + fwd + bwd on a token sample."""
     import numpy as np
@@ -128,6 +249,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the Llama-3-8B layer and 70B-class model workloads")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="run 2 steps, one merge, one AdamW step and a plain 256 MiB device copy (the counter "
                          "calibration), print nothing")
@@ -397,6 +520,12 @@ def main():
         "adamw_llama3_8b_adapters": adamw,
         "format_study_4096x4096": study,
     }
+    if not args.no_extra:
+        del q, W
+        torch.cuda.empty_cache()
+        out["llama3_8b_layer_M8192"] = llama3_8b_layer(dev)
+        torch.cuda.empty_cache()
+        out["model_70b_class"] = seventy_b_model(dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(N, K, r, alpha)
     print(json.dumps(out), flush=True)

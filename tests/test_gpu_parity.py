@@ -343,3 +343,45 @@ def test_weight_stream_graph_replay(gpu_lib):
             ye = linear_fwd(q, X, A, B, 32.0)
             torch.cuda.synchronize()
             assert torch.equal(ye.view(torch.int16), yg.view(torch.int16)), f"replay {rep}"
+
+
+@pytest.mark.parametrize("idx", [0, 2, 4, 6])
+def test_config5_70b_shapes_sampled(gpu_lib, idx):
+    """70B-class layer linears (layer 79 of the seed rule), forward at M = 1 (weight stream)
+    and M = 2048 (decoded copy + BF16 GEMM): encode/decode on sampled blocks, outputs on
+    sampled (token, feature) pairs."""
+    from bit_nf4_quantized_dq_amd import dequantize, linear_fwd, quantize
+
+    shp = I.SEVENTY_B_LAYER[idx]
+    N, K, r, alpha, layer = shp.d_out, shp.d_in, 16, 32.0, 79
+    print(f"70B {shp.name} {N}x{K}", flush=True)
+    W = I.weight(5, idx, N, K, 0.015, layer)
+    rng = np.random.default_rng(100 + idx)
+    n_s = np.sort(rng.choice(N, 32, replace=False))
+    kb_s = int(rng.integers(0, K // 64))
+    mask = np.zeros((N, K // 64), bool)
+    mask[n_s, :] = True
+    mask[:, kb_s] = True
+    oq = O.quantize(W.numpy(), blocks=mask)
+    q = quantize(W.cuda())
+    wq = dequantize(q)
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(q.code8), oq["code8"]) and np.array_equal(_np(q.c2s), oq["c2s"])
+    assert _np(q.mu)[0] == oq["mu"]
+    sel = np.repeat(mask, 64, axis=1)
+    ob = O.dequantize_bf16_bits(oq)
+    assert np.array_equal(_np(wq.view(torch.int16)).view(np.uint16)[sel], ob[sel])
+    del wq
+    what = O.bf16_bits_to_f32(ob[n_s]).astype(np.float64)
+    del ob, sel
+    A = I.lora_A(5, idx, r, K, layer)
+    Bm = I.lora_B(5, idx, N, r, layer)
+    Af, Bf = _f64(A), _f64(Bm)
+    for M in (1, 2048):
+        X = I.activations(5, idx, M, K, layer)
+        m_s = np.arange(M) if M == 1 else np.sort(rng.choice(M, 32, replace=False))
+        Y = linear_fwd(q, X.cuda(), A.cuda(), Bm.cuda(), alpha)
+        torch.cuda.synchronize()
+        Xf = _f64(X)[m_s]
+        Y_ref = Xf @ what.T + (alpha / r) * (Xf @ Af.T) @ Bf[n_s].T
+        assert normwise(_f64(Y)[np.ix_(m_s, n_s)], Y_ref) <= TOL, M
