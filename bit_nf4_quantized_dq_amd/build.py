@@ -19,7 +19,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libqlora_nf4.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["api.cpp", "codebook.cpp", "quantize.hip", "dequant.hip", "lora.hip", "gemv.hip", "gemm.hip", "gemm_nt.hip", "merge.hip", "adamw.hip"]
+SOURCES = ["api.cpp", "codebook.cpp", "quantize.hip", "dequant.hip", "lora.hip", "gemv.hip",
+    "gemv_stream.hip", "gemm.hip", "gemm_nt.hip", "merge.hip", "adamw.hip"]
 
 COMMON = [
     "-O3",

@@ -73,7 +73,7 @@ FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r, int dq) {
   size_t off = 0;
   w.tpart = off;
   if (M <= kGemvMaxM && !decode_once(M, dq)) {
-    const int32_t ks = gemv_ksplit(N, K);
+    const int32_t ks = gemv_stream_fits(N, K, M, r) ? gemv_stream_plan(N, K, M, r).ksplit : gemv_ksplit(N, K);
     off = align_up(off + sizeof(float) * ks * M * r, 256);
     w.ypart = off;
     off = align_up(off + sizeof(float) * ks * M * N, 256);
@@ -355,6 +355,9 @@ int qlora_linear_fwd(const qlora_nf4dq_t* Wq, const uint16_t* X, int64_t M, cons
   if (M <= kGemvMaxM && !decode_once(M, dq)) {
     if ((N + 63) / 64 > 65536) return QLORA_ERR_BAD_SHAPE;  // one arrival counter per 64 rows
     float* ypart = reinterpret_cast<float*>(base + L.ypart);
+    if (gemv_stream_fits(N, K, M, r))
+      return hip_status(launch_gemv_stream(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, X, M, A, B, r, s, Y, T_save,
+                                           ypart, tpart, tables_of(Wq), stream));
     return hip_status(launch_gemv_fwd(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, X, M, A, B, r, s, Y, T_save, ypart,
                                       tpart, tables_of(Wq), stream));
   }

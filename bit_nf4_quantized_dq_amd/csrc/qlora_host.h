@@ -80,6 +80,19 @@ hipError_t launch_gemv_fwd(const uint32_t* codes, const uint8_t* code8, const fl
                            const uint16_t* A, const uint16_t* B, int32_t r, float s, uint16_t* Y,
                            uint16_t* T_save, float* part, float* tpart, const Nf4Tables& T,
                            hipStream_t st);
+// The same forward for large weights (gemv_stream.hip): used when gemv_stream_fits(); its
+// reduction split comes from gemv_stream_plan() (same partial layout as above).
+struct GemvPlan {
+  int64_t groups;
+  int32_t ksplit, nbs, nchunk, xpitch;
+};
+GemvPlan gemv_stream_plan(int64_t N, int64_t K, int64_t M, int32_t r);
+bool gemv_stream_fits(int64_t N, int64_t K, int64_t M, int32_t r);
+hipError_t launch_gemv_stream(const uint32_t* codes, const uint8_t* code8, const float* c2s,
+                              const float* mu, int64_t N, int64_t K, const uint16_t* X, int64_t M,
+                              const uint16_t* A, const uint16_t* B, int32_t r, float s, uint16_t* Y,
+                              uint16_t* T_save, float* part, float* tpart, const Nf4Tables& T,
+                              hipStream_t st);
 
 // ---- fused dequant MFMA GEMMs (gemm.hip)
 // Y[M,N] = X[M,K] w_hat^T + L[M,r] B[N,r]^T, L = s*T (BF16, prescaled)

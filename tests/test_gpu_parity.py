@@ -302,6 +302,42 @@ def test_config4_llama3_8b_layer_sampled(gpu_lib, idx):
     assert normwise(_f64(T), T_ref) <= TOL
 
 
+# d_out * d_in >= 32M with d_in a multiple of 256: the large-weight stream kernel
+STREAM_CASES = [
+    # d_out, d_in, M, r
+    (8192, 4096, 1, 16),
+    (8192 + 160, 4096, 3, 40),  # a partial row group; r not a multiple of 8 (B read element-wise)
+    (4352, 8192, 16, 128),      # M = 16 and the largest rank
+    (12288, 4096, 2, 8),
+]
+
+
+@pytest.mark.parametrize("N,K,M,r", STREAM_CASES)
+def test_weight_stream_large_shapes(gpu_lib, N, K, M, r):
+    """Large weights at M <= 16: Y on sampled features (every row group boundary and the last
+    rows included) against the oracle on those rows; the saved T in full."""
+    from bit_nf4_quantized_dq_amd import linear_fwd, quantize
+
+    print(f"stream {N}x{K} M={M} r={r}", flush=True)
+    alpha = 2.0 * r
+    c = _case(9, N, K, M, r, 0.02, idx=40 + M)
+    rng = np.random.default_rng(N + K + M + r)
+    n_s = np.unique(np.concatenate([rng.choice(N, 40, replace=False), np.arange(0, N, 256)[:8], [255, 256, N - 1]]))
+    mask = np.zeros((N, K // 64), bool)
+    mask[n_s, :] = True
+    oq = O.quantize(c["W"].numpy(), blocks=mask)
+    what = O.bf16_bits_to_f32(O.dequantize_bf16_bits(oq)[n_s]).astype(np.float64)
+    q = quantize(c["W"].cuda())
+    T = torch.empty(M, r, dtype=torch.bfloat16, device="cuda")
+    Y = linear_fwd(q, c["X"].cuda(), c["A"].cuda(), c["B"].cuda(), alpha, T_save=T)
+    torch.cuda.synchronize()
+    Xf, Af, Bf = _f64(c["X"]), _f64(c["A"]), _f64(c["B"])
+    T_ref = Xf @ Af.T
+    Y_ref = Xf @ what.T + (alpha / r) * T_ref @ Bf[n_s].T
+    assert normwise(_f64(Y)[:, n_s], Y_ref) <= TOL
+    assert normwise(_f64(T), T_ref) <= TOL
+
+
 def test_weight_stream_graph_replay(gpu_lib):
     """The M <= 16 path captured in a HIP graph and replayed with new inputs in between:
     every replay equals an eager call on the same inputs (the split-K arrival counters
@@ -309,7 +345,7 @@ def test_weight_stream_graph_replay(gpu_lib):
     from bit_nf4_quantized_dq_amd import QuantizedWeight, linear_fwd, quantize, workspace_size, OP_FWD
 
     dev = torch.device("cuda")
-    shapes = [(1040, 4096, 1, 16), (272, 320, 16, 16), (4096, 4096, 16, 16)]
+    shapes = [(1040, 4096, 1, 16), (272, 320, 16, 16), (4096, 4096, 16, 16), (8192, 4096, 1, 16)]
     cases = []
     for i, (N, K, M, r) in enumerate(shapes):
         c = _case(9, N, K, M, r, 0.02, idx=10 + i)
