@@ -200,10 +200,12 @@ __global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L) {
   uint4 xv[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    const int i = u * kThreads + tid, m = i / pieces, pc = i % pieces;
-    const int64_t k = b0 * 64 + 8 * pc;
-    const bool ok = i < items && m < M && k < b1 * 64;
-    xv[u] = bload16(rx, ok ? (uint32_t)(((int64_t)m * K + k) * 2) : kOOB);
+    if (u * kThreads < items) {  // uniform: only the passes that hold pieces
+      const int i = u * kThreads + tid, m = i / pieces, pc = i % pieces;
+      const int64_t k = b0 * 64 + 8 * pc;
+      const bool ok = i < items && m < M && k < b1 * 64;
+      xv[u] = bload16(rx, ok ? (uint32_t)(((int64_t)m * K + k) * 2) : kOOB);
+    }
   }
   const uint32_t c2v = bload4(r2, tid < a.c2max ? (uint32_t)((g0 + tid) * 4) : kOOB);
 
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L) {
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int i = u * kThreads + tid, m = i / pieces, pc = i % pieces;
-    if (i < items) *reinterpret_cast<uint4*>(sR + m * a.xpitch + 16 * pc) = pair_order(xv[u]);
+    if (u * kThreads < items && i < items) *reinterpret_cast<uint4*>(sR + m * a.xpitch + 16 * pc) = pair_order(xv[u]);
   }
   if (tid < a.c2max) reinterpret_cast<float*>(sR + a.c2off)[tid] = __uint_as_float(c2v);
 #pragma unroll
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L) {
   for (int ci0 = 0; ci0 < a.nchunk; ci0 += kDepth) {
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
-      issue(ci0 + d + kDepth - 1, C[(d + kDepth - 1) % kDepth]);
+      if (kDepth > 1) issue(ci0 + d + kDepth - 1, C[(d + kDepth - 1) % kDepth]);
       if (ci0 + d < nreal) compute(ci0 + d, C[d]);
     }
   }
@@ -424,7 +426,8 @@ RegionUse region_use(int64_t nb_row, int64_t M, int64_t nbs, int64_t nchunk) {
   return u;
 }
 
-// Chunks in flight per wavefront: three where registers allow (r <= 32), else two.
+// Chunks in flight per wavefront: three where registers allow (r <= 32), else two.  Plans
+// whose ranges are single chunks run with one (no prefetch to issue).
 int stream_depth(int32_t r) { return r <= 32 ? 3 : 2; }
 
 }  // namespace
@@ -457,7 +460,7 @@ GemvPlan gemv_stream_plan(int64_t N, int64_t K, int64_t M, int32_t r) {
   }
   p.ksplit = (int32_t)best_ks;
   p.nbs = (int32_t)nbs_of(best_ks);
-  p.nchunk = (int32_t)chunks_of(p.nbs);
+  p.nchunk = p.nbs <= kCB ? 1 : (int32_t)chunks_of(p.nbs);
   p.xpitch = region_use(nb_row, M, p.nbs, p.nchunk).xpitch;
   return p;
 }
@@ -511,8 +514,13 @@ hipError_t launch_gemv_stream(const uint32_t* codes, const uint8_t* code8, const
   }
   dim3 grid((unsigned)p.groups, (unsigned)p.ksplit);
   LaunchTimer t(3, st);
-#define QLORA_GEMV_GO(RT16, NQ, D) \
-  hipExtLaunchKernelGGL((k_gemv_stream<RT16, NQ, D>), grid, dim3(kThreads), 0, st, t.start, t.stop, 0, a, L)
+#define QLORA_GEMV_GO(RT16, NQ, D)                                                                       \
+  do {                                                                                                   \
+    if (p.nchunk == 1)                                                                                   \
+      hipExtLaunchKernelGGL((k_gemv_stream<RT16, NQ, 1>), grid, dim3(kThreads), 0, st, t.start, t.stop, 0, a, L); \
+    else                                                                                                 \
+      hipExtLaunchKernelGGL((k_gemv_stream<RT16, NQ, D>), grid, dim3(kThreads), 0, st, t.start, t.stop, 0, a, L); \
+  } while (0)
   if (M == 1) {
     if (r <= 16) QLORA_GEMV_GO(1, 1, 3);
     else if (r <= 32) QLORA_GEMV_GO(2, 1, 3);
