@@ -21,8 +21,9 @@ M = 1 by graph replay and at M = 2048), and the CPU oracle timed on a bounded sa
 same workload.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-extra]
-  python bench.py --pmc-pass    # 2 steps, one merge, one AdamW step and a 256 MiB device
-                                # copy (the counter calibration), for counter runs
+  python bench.py --pmc-pass    # 2 steps, one merge, one AdamW step, two M = 1 calls on a
+                                # 28672x8192 weight and a 256 MiB device copy (the counter
+                                # calibration), for counter runs
 """
 
 from __future__ import annotations
@@ -44,14 +45,18 @@ PEAK_HBM_GBS = 8000.0
 # taken on: when that file's SHA-1 differs, the traffic is reported as null.
 COUNTER_TRAFFIC = {
     "gemm_nt": {"source": "bit_nf4_quantized_dq_amd/csrc/gemm_nt.hip",
-                "sha1": "55a5847c5dd297270656fa3947bbba1b45dd78ec",
-                "read_bytes": 303_434_547, "write_bytes": 33_554_432},
+                "sha1": "021ef9132d398a81639332f1eaf4b8987d540d5b",
+                "read_bytes": 303_442_624, "write_bytes": 33_554_432},
     "merge": {"source": "bit_nf4_quantized_dq_amd/csrc/merge.hip",
-              "sha1": "ed2a116b67d462d7e3501d8ca7652e1d8ca9ec4b",
-              "read_bytes": 11_907_993, "write_bytes": 33_554_688},
+              "sha1": "aa1649879396b227b61d065c057ec39a4962a28a",
+              "read_bytes": 11_908_864, "write_bytes": 33_554_688},
     "adamw": {"source": "bit_nf4_quantized_dq_amd/csrc/adamw.hip",
               "sha1": "513130524f3da5219d61f8dcabd1c76bb0828e6f",
-              "read_bytes": 587_279_872, "write_bytes": 587_202_560},
+              "read_bytes": 587_289_984, "write_bytes": 587_202_560},
+    # one M = 1 call on a 28672 x 8192 weight (the gate shape of the 70B-class model)
+    "gemv_stream": {"source": "bit_nf4_quantized_dq_amd/csrc/gemv_stream.hip",
+                    "sha1": "d9538abb192262e71f1f1da72ba17a277d416d2a",
+                    "read_bytes": 125_036_864, "write_bytes": 297_600},
 }
 
 
@@ -183,7 +188,9 @@ def seventy_b_model(dev, layers=80, passes=3):
             ms = 1e3 * (time.perf_counter() - t0) / passes
             out["M1"] = {"metric": "weight-stream GB/s at M=1 through all 560 linears (graph replay)",
                          "value": round(nbytes1 / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "ms_per_pass": round(ms, 3),
-                         "bytes_per_pass": nbytes1, "frac_of_hbm_peak": round(nbytes1 / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+                         "bytes_per_pass": nbytes1, "frac_of_hbm_peak": round(nbytes1 / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                         "gate_28672x8192_call": {"algorithmic_bytes": stream_bytes(1, 28672, 8192, r),
+                                                  "counter_bytes": counter_traffic("gemv_stream")}}
             del g
         else:
             t0 = time.perf_counter()
@@ -252,8 +259,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the Llama-3-8B layer and 70B-class model workloads")
     ap.add_argument("--pmc-pass", action="store_true",
-                    help="run 2 steps, one merge, one AdamW step and a plain 256 MiB device copy (the counter "
-                         "calibration), print nothing")
+                    help="run 2 steps, one merge, one AdamW step, two M = 1 calls on a 28672x8192 weight and a "
+                         "plain 256 MiB device copy (the counter calibration), print nothing")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
@@ -298,6 +305,15 @@ def main():
         Q.adamw_step(st[0], st[1], st[2], st[3], 1, 2e-4, weight_decay=0.01,
                      param=torch.empty(na, dtype=torch.bfloat16, device=dev))
         del st
+        # one large-weight stream call pair at M = 1 (a 28672 x 8192 gate-shaped linear)
+        Wg = I.weight(5, 4, 28672, 8192, 0.015, device=dev)
+        qg = Q.quantize(Wg)
+        del Wg
+        Xg = I.activations(5, 4, 1, 8192, device=dev)
+        Ag, Bg = I.lora_A(5, 4, r, 8192, device=dev), I.lora_B(5, 4, 28672, r, device=dev)
+        for _ in range(2):
+            Q.linear_fwd(qg, Xg, Ag, Bg, alpha)
+        del qg
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         src.fill_(1)
