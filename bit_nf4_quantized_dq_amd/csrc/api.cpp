@@ -179,9 +179,11 @@ LaunchTimer::LaunchTimer(int kernel_id, hipStream_t) {
   if (kernel_id < 0 || kernel_id >= QLORA_K_COUNT || !((T.mask >> kernel_id) & 1)) return;
   auto& v = T.ev[kernel_id];
   if (T.used[kernel_id] == v.size()) {
+    // timing-only events: no system-scope fence (an L2 write-back and invalidate) when they
+    // are recorded, so they neither stall the stream nor cool the caches of the next launch
     hipEvent_t a, b;
-    if (hipEventCreate(&a) != hipSuccess) return;
-    if (hipEventCreate(&b) != hipSuccess) {
+    if (hipEventCreateWithFlags(&a, hipEventDisableSystemFence) != hipSuccess) return;
+    if (hipEventCreateWithFlags(&b, hipEventDisableSystemFence) != hipSuccess) {
       (void)hipEventDestroy(a);
       return;
     }
