@@ -421,9 +421,10 @@ int qlora_linear_bwd(const qlora_nf4dq_t* Wq, const uint16_t* X, const uint16_t*
         hipSuccess)
       return QLORA_ERR_HIP;
   }
-  // dA = s G^T X [r, K]; dB = s dY^T T, stored [N, r] (own partials and arrival counters each)
-  if ((e = launch_lora_grad(g, X, M, r, K, s, 0, cpa, 0, dA, stream)) != hipSuccess) return QLORA_ERR_HIP;
-  if ((e = launch_lora_grad(T, dY, M, r, N, s, 1, cpb, 1, dB, stream)) != hipSuccess) return QLORA_ERR_HIP;
+  // dA = s G^T X [r, K] and dB = s dY^T T, stored [N, r], in one launch (own partials and
+  // arrival counters each)
+  if ((e = launch_lora_grad2(g, X, K, 0, cpa, dA, T, dY, N, 1, cpb, dB, M, r, s, stream)) != hipSuccess)
+    return QLORA_ERR_HIP;
   return QLORA_OK;
 }
 

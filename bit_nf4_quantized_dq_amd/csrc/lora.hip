@@ -175,22 +175,42 @@ constexpr int kGradWaves = kGradThreads / 64;
 constexpr int kGradCols = 64;      // columns per workgroup (4 tiles of 16)
 constexpr int kVTile = 32 * 32 + 64;  // bytes per staged [32][16] BF16 tile, padded (bank offset)
 
-// grid (ceil(C / 64), msplit).  JT = ceil(R / 16).  part: [msplit][R][C] FP32 (msplit > 1).
+// One gradient product out = scale * U^T V (or its transpose): U [M, R], V [M, C].
+struct GradArgs {
+  const uint16_t* U;
+  const uint16_t* V;
+  int64_t M;
+  int32_t R;
+  int64_t C;
+  int64_t mps;          // tokens per slice (a multiple of 32)
+  float scale;
+  int transposed;       // out is [C, R] instead of [R, C]
+  float* part;          // [msplit][R][C] FP32 (msplit > 1)
+  unsigned int* counters;
+  uint16_t* out;
+  int32_t msplit;
+};
+
+// The workgroup of column tile c_tile (64 columns) and token slice m_slice.  JT = ceil(R / 16).
 template <int JT, int D>
-__global__ __launch_bounds__(kGradThreads) void k_lora_grad(const uint16_t* __restrict__ U,
-                                                            const uint16_t* __restrict__ V, int64_t M,
-                                                            int32_t R, int64_t C, int64_t mps, float scale,
-                                                            int transposed, float* __restrict__ part,
-                                                            unsigned int* __restrict__ counters,
-                                                            uint16_t* __restrict__ out) {
+__device__ __forceinline__ void grad_body(const GradArgs& g, int64_t c_tile, int64_t m_slice) {
+  const uint16_t* __restrict__ U = g.U;
+  const uint16_t* __restrict__ V = g.V;
+  const int64_t M = g.M, C = g.C, mps = g.mps;
+  const int32_t R = g.R;
+  const float scale = g.scale;
+  const int transposed = g.transposed;
+  float* __restrict__ part = g.part;
+  unsigned int* __restrict__ counters = g.counters;
+  uint16_t* __restrict__ out = g.out;
   // per wavefront: 4 V tiles + JT U tiles of [32][16] BF16; reused for the cross-wave sums
   constexpr int kWaveBytes = (4 + JT) * kVTile;
   constexpr int kRedBytes = kGradWaves * JT * 4 * 64 * 16;
   __shared__ __attribute__((aligned(16))) char smem[kGradWaves * kWaveBytes > kRedBytes ? kGradWaves * kWaveBytes : kRedBytes];
   __shared__ bool s_last;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t c0 = (int64_t)blockIdx.x * kGradCols;
-  const int64_t mbeg = (int64_t)blockIdx.y * mps;
+  const int64_t c0 = c_tile * kGradCols;
+  const int64_t mbeg = m_slice * mps;
   const int64_t mend = (mbeg + mps < M) ? mbeg + mps : M;
   const rsrc_t rv = make_rsrc(V, M * C * 2);
   const rsrc_t ru = make_rsrc(U, M * (int64_t)R * 2);
@@ -267,7 +287,7 @@ __global__ __launch_bounds__(kGradThreads) void k_lora_grad(const uint16_t* __re
 #pragma unroll
     for (int q = 0; q < 4; ++q) red[((wave * JT + t) * 4 + q) * 64 + lane] = acc[t][q];
   __syncthreads();
-  const int32_t msplit = gridDim.y;
+  const int32_t msplit = g.msplit;
   // one (t, q, lane) item per thread pass: JT * 4 * 64 items
   for (int i = threadIdx.x; i < JT * 4 * 64; i += kGradThreads) {
     const int l = i & 63, q = (i >> 6) & 3, t = i >> 8;
@@ -286,7 +306,7 @@ __global__ __launch_bounds__(kGradThreads) void k_lora_grad(const uint16_t* __re
         if (transposed) out[c * R + j] = b16;
         else out[(int64_t)j * C + c] = b16;
       } else {
-        __hip_atomic_store(part + ((int64_t)blockIdx.y * R + j) * C + c, sum[v], __ATOMIC_RELAXED,
+        __hip_atomic_store(part + (m_slice * R + j) * C + c, sum[v], __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_SYSTEM);
       }
     }
@@ -297,7 +317,7 @@ __global__ __launch_bounds__(kGradThreads) void k_lora_grad(const uint16_t* __re
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned int inc = kCounterPeriod / (unsigned int)msplit;
-    const unsigned int old = __hip_atomic_fetch_add(&counters[blockIdx.x], inc, __ATOMIC_RELAXED,
+    const unsigned int old = __hip_atomic_fetch_add(&counters[c_tile], inc, __ATOMIC_RELAXED,
                                                     __HIP_MEMORY_SCOPE_AGENT);
     s_last = ((old + inc) % kCounterPeriod) == 0u;
   }
@@ -323,6 +343,21 @@ __global__ __launch_bounds__(kGradThreads) void k_lora_grad(const uint16_t* __re
     if (transposed) out[c * R + j] = b16;
     else out[(int64_t)j * C + c] = b16;
   }
+}
+
+// grid (ceil(C / 64), msplit)
+template <int JT, int D>
+__global__ __launch_bounds__(kGradThreads) void k_lora_grad(GradArgs g) {
+  grad_body<JT, D>(g, blockIdx.x, blockIdx.y);
+}
+
+// Two independent products in one launch (dA and dB of one backward), blockIdx.z selecting:
+// grid (max column tiles, max slices, 2); workgroups past a product's own grid return.
+template <int JT, int D>
+__global__ __launch_bounds__(kGradThreads) void k_lora_grad2(GradArgs g0, GradArgs g1) {
+  const GradArgs& g = blockIdx.z ? g1 : g0;
+  if ((int64_t)blockIdx.x * kGradCols >= g.C || (int32_t)blockIdx.y >= g.msplit) return;
+  grad_body<JT, D>(g, blockIdx.x, blockIdx.y);
 }
 
 // Device address of the arrival counters on the current device (looked up once per device).
@@ -365,26 +400,67 @@ hipError_t down_launch(const uint16_t* P, const uint16_t* Q, int64_t M, int32_t 
   return hipGetLastError();
 }
 
+// Gradient product arguments: msplit token slices of mps tokens, arrival counters of set
+// counter_set.
+GradArgs grad_args(const uint16_t* U, const uint16_t* V, int64_t M, int32_t R, int64_t C, float scale, int transposed,
+                   float* part, int counter_set, uint16_t* out, unsigned int* counters) {
+  GradArgs g;
+  g.U = U;
+  g.V = V;
+  g.M = M;
+  g.R = R;
+  g.C = C;
+  g.msplit = lora_grad_msplit(M, C);
+  g.mps = ((M + g.msplit - 1) / g.msplit + 31) / 32 * 32;
+  g.scale = scale;
+  g.transposed = transposed;
+  g.part = part;
+  g.counters = counters + 65536 * counter_set;
+  g.out = out;
+  return g;
+}
+
+// Loads of D token chunks are held at once: D is chosen from the chunks per wavefront.
 template <int JT>
-hipError_t grad_launch(const uint16_t* U, const uint16_t* V, int64_t M, int32_t R, int64_t C, int32_t msplit,
-                       int64_t mps, float scale, int transposed, float* part, int counter_set, uint16_t* out,
-                       hipStream_t s) {
-  dim3 grid((unsigned)((C + kGradCols - 1) / kGradCols), (unsigned)msplit);
-  unsigned int* counters = lora_counters();
-  if (!counters) return hipErrorInvalidSymbol;
-  counters += 65536 * counter_set;
+int grad_depth(int64_t mps) {
   constexpr int kMaxD = JT <= 2 ? 8 : (JT <= 4 ? 4 : 2);  // <= 192 VGPRs of loads
-  const int d = batch_depth((mps / 32 + kGradWaves - 1) / kGradWaves, kMaxD);
+  return batch_depth((mps / 32 + kGradWaves - 1) / kGradWaves, kMaxD);
+}
+
+template <int JT>
+hipError_t grad_launch(const GradArgs& g0, const GradArgs* g1, hipStream_t s) {
+  constexpr int kMaxD = JT <= 2 ? 8 : (JT <= 4 ? 4 : 2);
+  int d = grad_depth<JT>(g0.mps);
+  int64_t tiles = (g0.C + kGradCols - 1) / kGradCols;
+  int32_t ms = g0.msplit;
+  if (g1) {
+    const int d1 = grad_depth<JT>(g1->mps);
+    d = d1 < d ? d1 : d;
+    const int64_t t1 = (g1->C + kGradCols - 1) / kGradCols;
+    tiles = t1 > tiles ? t1 : tiles;
+    ms = g1->msplit > ms ? g1->msplit : ms;
+  }
   LaunchTimer t(7, s);
-  auto go = [&](auto kern) {
-    hipExtLaunchKernelGGL(kern, grid, dim3(kGradThreads), 0, s, t.start, t.stop, 0, U, V, M, R, C, mps, scale, transposed,
-                          part, counters, out);
+  auto go = [&](auto k1, auto k2) {
+    if (g1)
+      hipExtLaunchKernelGGL(k2, dim3((unsigned)tiles, (unsigned)ms, 2), dim3(kGradThreads), 0, s, t.start, t.stop, 0, g0,
+                            *g1);
+    else
+      hipExtLaunchKernelGGL(k1, dim3((unsigned)tiles, (unsigned)ms), dim3(kGradThreads), 0, s, t.start, t.stop, 0, g0);
   };
-  if (d >= 8 && kMaxD >= 8) go(k_lora_grad<JT, (kMaxD >= 8 ? 8 : 1)>);
-  else if (d >= 4 && kMaxD >= 4) go(k_lora_grad<JT, (kMaxD >= 4 ? 4 : 1)>);
-  else if (d >= 2) go(k_lora_grad<JT, 2>);
-  else go(k_lora_grad<JT, 1>);
+  if (d >= 8 && kMaxD >= 8) go(k_lora_grad<JT, (kMaxD >= 8 ? 8 : 1)>, k_lora_grad2<JT, (kMaxD >= 8 ? 8 : 1)>);
+  else if (d >= 4 && kMaxD >= 4) go(k_lora_grad<JT, (kMaxD >= 4 ? 4 : 1)>, k_lora_grad2<JT, (kMaxD >= 4 ? 4 : 1)>);
+  else if (d >= 2) go(k_lora_grad<JT, 2>, k_lora_grad2<JT, 2>);
+  else go(k_lora_grad<JT, 1>, k_lora_grad2<JT, 1>);
   return hipGetLastError();
+}
+
+hipError_t grad_dispatch(const GradArgs& g0, const GradArgs* g1, hipStream_t s) {
+  const int32_t R = g0.R;
+  if (R <= 16) return grad_launch<1>(g0, g1, s);
+  if (R <= 32) return grad_launch<2>(g0, g1, s);
+  if (R <= 64) return grad_launch<4>(g0, g1, s);
+  return grad_launch<8>(g0, g1, s);
 }
 
 }  // namespace
@@ -413,12 +489,20 @@ int32_t lora_grad_msplit(int64_t M, int64_t C) {
 
 hipError_t launch_lora_grad(const uint16_t* U, const uint16_t* V, int64_t M, int32_t R, int64_t C, float scale,
                             int transposed, float* part, int counter_set, uint16_t* out, hipStream_t s) {
-  const int32_t ms = lora_grad_msplit(M, C);
-  const int64_t mps = ((M + ms - 1) / ms + 31) / 32 * 32;
-  if (R <= 16) return grad_launch<1>(U, V, M, R, C, ms, mps, scale, transposed, part, counter_set, out, s);
-  if (R <= 32) return grad_launch<2>(U, V, M, R, C, ms, mps, scale, transposed, part, counter_set, out, s);
-  if (R <= 64) return grad_launch<4>(U, V, M, R, C, ms, mps, scale, transposed, part, counter_set, out, s);
-  return grad_launch<8>(U, V, M, R, C, ms, mps, scale, transposed, part, counter_set, out, s);
+  unsigned int* counters = lora_counters();
+  if (!counters) return hipErrorInvalidSymbol;
+  const GradArgs g = grad_args(U, V, M, R, C, scale, transposed, part, counter_set, out, counters);
+  return grad_dispatch(g, nullptr, s);
+}
+
+hipError_t launch_lora_grad2(const uint16_t* U0, const uint16_t* V0, int64_t C0, int transposed0, float* part0,
+                             uint16_t* out0, const uint16_t* U1, const uint16_t* V1, int64_t C1, int transposed1,
+                             float* part1, uint16_t* out1, int64_t M, int32_t R, float scale, hipStream_t s) {
+  unsigned int* counters = lora_counters();
+  if (!counters) return hipErrorInvalidSymbol;
+  const GradArgs g0 = grad_args(U0, V0, M, R, C0, scale, transposed0, part0, 0, out0, counters);
+  const GradArgs g1 = grad_args(U1, V1, M, R, C1, scale, transposed1, part1, 1, out1, counters);
+  return grad_dispatch(g0, &g1, s);
 }
 
 }  // namespace qlora

@@ -71,6 +71,10 @@ hipError_t launch_lora_down(const uint16_t* P, const uint16_t* Q, int q_transpos
 int32_t lora_grad_msplit(int64_t M, int64_t C);
 hipError_t launch_lora_grad(const uint16_t* U, const uint16_t* V, int64_t M, int32_t R, int64_t C, float scale,
                             int transposed, float* part, int counter_set, uint16_t* out, hipStream_t s);
+// Two such products in one launch (counter sets 0 and 1), e.g. dA and dB of one backward.
+hipError_t launch_lora_grad2(const uint16_t* U0, const uint16_t* V0, int64_t C0, int transposed0, float* part0,
+                             uint16_t* out0, const uint16_t* U1, const uint16_t* V1, int64_t C1, int transposed1,
+                             float* part1, uint16_t* out1, int64_t M, int32_t R, float scale, hipStream_t s);
 
 // ---- weight-streaming forward, M <= 16 (gemv.hip): one launch, split-K with FP32
 // partials part [ksplit][M][N] and tpart [ksplit][M][r] in the workspace.
