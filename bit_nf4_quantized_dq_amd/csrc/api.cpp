@@ -366,16 +366,23 @@ int qlora_linear_fwd(const qlora_nf4dq_t* Wq, const uint16_t* X, int64_t M, cons
   // T = X A^T: s T (BF16) feeds the adapter slices of the GEMM; T itself is saved if asked
   uint16_t* ls = reinterpret_cast<uint16_t*>(base + L.ls);
   hipError_t e;
-  if ((e = launch_lora_down(X, A, 0, M, r, K, s, ls, T_save, stream)) != hipSuccess) return QLORA_ERR_HIP;
   if (decode_once(M, dq)) {
     uint16_t* wcopy = reinterpret_cast<uint16_t*>(base + L.wcopy);
-    if ((e = launch_dequant(codes, Wq->code8, Wq->c2s, Wq->mu, wcopy, N * K / 8, tables_of(Wq), dq, stream)) !=
-        hipSuccess)
-      return QLORA_ERR_HIP;
+    if (dq == QLORA_DQ_E4M3) {  // T and the decoded copy in one launch
+      if ((e = launch_fwd_prologue(X, A, M, r, K, s, ls, T_save, codes, Wq->code8, Wq->c2s, Wq->mu, N, wcopy,
+                                   tables_of(Wq), stream)) != hipSuccess)
+        return QLORA_ERR_HIP;
+    } else {
+      if ((e = launch_lora_down(X, A, 0, M, r, K, s, ls, T_save, stream)) != hipSuccess) return QLORA_ERR_HIP;
+      if ((e = launch_dequant(codes, Wq->code8, Wq->c2s, Wq->mu, wcopy, N * K / 8, tables_of(Wq), dq, stream)) !=
+          hipSuccess)
+        return QLORA_ERR_HIP;
+    }
     // Y = X w_hat^T + (s T) B^T: A = w_hat [N, K], Wl = B [N, r] (f*r + j)
     e = launch_gemm_nt(wcopy, N, X, M, K, B, r, 1, ls, r, Y, QLORA_K_GEMM_FWD, stream);
     return hip_status(e);
   }
+  if ((e = launch_lora_down(X, A, 0, M, r, K, s, ls, T_save, stream)) != hipSuccess) return QLORA_ERR_HIP;
   e = launch_gemm_fwd(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, X, M, ls, B, r, Y, tables_of(Wq), stream);
   return hip_status(e);
 }
@@ -406,12 +413,20 @@ int qlora_linear_bwd(const qlora_nf4dq_t* Wq, const uint16_t* X, const uint16_t*
     if ((e = launch_lora_down(X, A, 0, M, r, K, 1.0f, t, nullptr, stream)) != hipSuccess) return QLORA_ERR_HIP;
     T = t;
   }
-  // G = dY B (B [N, r] is read as the transposed operand); s G and G in BF16
-  if ((e = launch_lora_down(dY, B, 1, M, r, N, s, lg, g, stream)) != hipSuccess) return QLORA_ERR_HIP;
-  // dX = dY w_hat + (s G) A
+  // G = dY B (B [N, r] is read as the transposed operand); s G and G in BF16.  dX = dY w_hat +
+  // (s G) A; with the decoded copy, G and the transposed decode share one launch (E4M3).
+  const bool fused = dX && decode_once(M, dq) && dq == QLORA_DQ_E4M3;
+  uint16_t* wcopy = reinterpret_cast<uint16_t*>(base + L.wcopy);
+  if (fused) {
+    if ((e = launch_bwd_prologue(dY, B, M, r, N, s, lg, g, codes, Wq->code8, Wq->c2s, Wq->mu, K, wcopy, tables_of(Wq),
+                                 stream)) != hipSuccess)
+      return QLORA_ERR_HIP;
+  } else if ((e = launch_lora_down(dY, B, 1, M, r, N, s, lg, g, stream)) != hipSuccess) {
+    return QLORA_ERR_HIP;
+  }
   if (dX && decode_once(M, dq)) {
-    uint16_t* wcopy = reinterpret_cast<uint16_t*>(base + L.wcopy);
-    if ((e = launch_dequant_t(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, wcopy, tables_of(Wq), dq, stream)) != hipSuccess)
+    if (!fused &&
+        (e = launch_dequant_t(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, wcopy, tables_of(Wq), dq, stream)) != hipSuccess)
       return QLORA_ERR_HIP;
     // A = w_hat^T [K, N], Wl(f, j) = A[j][f]: read in place from A [r, K] (f*1 + j*K)
     if ((e = launch_gemm_nt(wcopy, K, dY, M, N, A, 1, K, lg, r, dX, QLORA_K_GEMM_DX, stream)) != hipSuccess)

@@ -18,7 +18,7 @@
 // i/4, i/4 + 4, i/4 + 8, i/4 + 12.  If lane j addresses row k0 + j/4, columns 4 (j % 4) .. +3
 // of a tile with 16 columns, lane i therefore receives rows k0 .. k0+3 of column i, and two
 // such reads give the 8 consecutive reduction indices of an MFMA operand.
-#include "qlora_device.h"
+#include "decode_tiles.h"
 #include "qlora_host.h"
 
 namespace qlora {
@@ -52,20 +52,22 @@ __device__ __forceinline__ uint16_t to_bf16(float v) { return (uint16_t)(pack_bf
 constexpr int kDownThreads = 512;
 constexpr int kDownWaves = kDownThreads / 64;
 
-// grid: ceil(M / (16 MT)).  JT = ceil(R / 16) tiles of outputs, all held by every wavefront.
+// LDS of one down-projection workgroup: per wavefront, the QT staging of one slab (JT tiles
+// of 32 rows x 16 columns); reused for the cross-wavefront sums.
+template <int JT, int MT>
+constexpr int down_lds_bytes() {
+  return kDownWaves * JT * MT * 64 * 16 > kDownWaves * JT * 1024 ? kDownWaves * JT * MT * 64 * 16
+                                                                   : kDownWaves * JT * 1024;
+}
+
+// Workgroup wg of the down-projection: tokens 16 MT wg .. +16 MT.  JT = ceil(R / 16) tiles of
+// outputs, all held by every wavefront.
 template <int JT, int MT, bool QT, int D>
-__global__ __launch_bounds__(kDownThreads) void k_lora_down(const uint16_t* __restrict__ P,
-                                                            const uint16_t* __restrict__ Q, int64_t M,
-                                                            int32_t R, int64_t Kd, float scale,
-                                                            uint16_t* __restrict__ out_s,
-                                                            uint16_t* __restrict__ out_u) {
-  // per wavefront: QT staging of one slab (JT tiles of 32 rows x 16 columns); reused below
-  // for the cross-wavefront sums
-  __shared__ __attribute__((aligned(16))) char smem[kDownWaves * JT * MT * 64 * 16 > kDownWaves * JT * 1024
-                                                       ? kDownWaves * JT * MT * 64 * 16
-                                                       : kDownWaves * JT * 1024];
+__device__ __forceinline__ void down_body(const uint16_t* __restrict__ P, const uint16_t* __restrict__ Q, int64_t M,
+                                          int32_t R, int64_t Kd, float scale, uint16_t* __restrict__ out_s,
+                                          uint16_t* __restrict__ out_u, int64_t wg, char* smem) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t m0 = (int64_t)blockIdx.x * 16 * MT;
+  const int64_t m0 = wg * 16 * MT;
   const int kk = 8 * (lane >> 4);
   const rsrc_t rp = make_rsrc(P + m0 * Kd, (M - m0) * Kd * 2);
   const rsrc_t rq = make_rsrc(Q, (int64_t)R * Kd * 2);
@@ -167,6 +169,68 @@ __global__ __launch_bounds__(kDownThreads) void k_lora_down(const uint16_t* __re
       if (out_u) out_u[m * R + j] = to_bf16(sum[v]);
     }
   }
+}
+
+// grid: ceil(M / (16 MT))
+template <int JT, int MT, bool QT, int D>
+__global__ __launch_bounds__(kDownThreads) void k_lora_down(const uint16_t* __restrict__ P,
+                                                            const uint16_t* __restrict__ Q, int64_t M,
+                                                            int32_t R, int64_t Kd, float scale,
+                                                            uint16_t* __restrict__ out_s,
+                                                            uint16_t* __restrict__ out_u) {
+  __shared__ __attribute__((aligned(16))) char smem[down_lds_bytes<JT, MT>()];
+  down_body<JT, MT, QT, D>(P, Q, M, R, Kd, scale, out_s, out_u, blockIdx.x, smem);
+}
+
+// The step's two prologues pair a down-projection with a decode of the weight: the two are
+// independent and each bound by HBM, so one launch runs both.  The first n_down workgroups
+// project; the rest decode.
+struct DownArgs {
+  const uint16_t* P;
+  const uint16_t* Q;
+  int64_t M;
+  int32_t R;
+  int64_t Kd;
+  float scale;
+  uint16_t* out_s;
+  uint16_t* out_u;
+};
+struct DecodeArgs {
+  const uint32_t* codes;
+  const uint8_t* code8;
+  const float* c2s;
+  const float* mu;
+  uint16_t* out;
+  int64_t N, K;
+};
+
+// Forward: T = X A^T, and the decoded copy w_hat [N, K] (512 code words per workgroup).
+template <int JT, int MT, int D, int DQ>
+__global__ __launch_bounds__(kDownThreads) void k_fwd_prologue(DownArgs d, DecodeArgs e, int64_t n_down, Nf4Tables T) {
+  __shared__ __attribute__((aligned(16))) char smem[down_lds_bytes<JT, MT>()];
+  if ((int64_t)blockIdx.x < n_down) {
+    down_body<JT, MT, false, D>(d.P, d.Q, d.M, d.R, d.Kd, d.scale, d.out_s, d.out_u, blockIdx.x, smem);
+    return;
+  }
+  const int64_t g = ((int64_t)blockIdx.x - n_down) * kDownThreads + threadIdx.x;
+  if (g < e.N * e.K / 8) decode_word<DQ>(e.codes, e.code8, e.c2s, e.mu, reinterpret_cast<uint4*>(e.out), g, T);
+}
+
+// Backward: G = dY B, and the transposed decoded copy w_hat^T [K, N] (two 64 x 256 tiles per
+// workgroup, one per half).
+template <int JT, int MT, int D, int DQ>
+__global__ __launch_bounds__(kDownThreads) void k_bwd_prologue(DownArgs d, DecodeArgs e, int64_t n_down, Nf4Tables T) {
+  constexpr int kLds = down_lds_bytes<JT, MT>() > 2 * kTileLdsBytes ? down_lds_bytes<JT, MT>() : 2 * kTileLdsBytes;
+  __shared__ __attribute__((aligned(16))) char smem[kLds];
+  if ((int64_t)blockIdx.x < n_down) {
+    down_body<JT, MT, true, D>(d.P, d.Q, d.M, d.R, d.Kd, d.scale, d.out_s, d.out_u, blockIdx.x, smem);
+    return;
+  }
+  const int half = threadIdx.x >> 8;
+  const int64_t tiles_k = (e.K + kTK - 1) / kTK;
+  const int64_t tile = 2 * ((int64_t)blockIdx.x - n_down) + half;  // past the last tile: decodes nothing
+  decode_tile_t<DQ>(e.codes, e.code8, e.c2s, e.mu, e.out, e.N, e.K, T, tile % tiles_k, tile / tiles_k,
+                    threadIdx.x & 255, reinterpret_cast<uint32_t*>(smem + half * kTileLdsBytes));
 }
 
 // ---------------------------------------------------------------- gradients of A and B
@@ -421,6 +485,42 @@ GradArgs grad_args(const uint16_t* U, const uint16_t* V, int64_t M, int32_t R, i
 }
 
 // Loads of D token chunks are held at once: D is chosen from the chunks per wavefront.
+// The paired prologue launches (E4M3 constants).  Depth of the down-projection's loads as in
+// down_launch, at most 8 for the transposed operand (registers shared with the decode role).
+template <int JT, int MT, bool BWD>
+hipError_t prologue_launch(const DownArgs& dn, const DecodeArgs& de, const Nf4Tables& T, hipStream_t s) {
+  const int64_t n_down = (dn.M + 16 * MT - 1) / (16 * MT);
+  const int64_t n_dec = BWD ? (((de.K + kTK - 1) / kTK) * ((de.N + kTN - 1) / kTN) + 1) / 2
+                            : (de.N * de.K / 8 + kDownThreads - 1) / kDownThreads;
+  constexpr int kMaxD = BWD ? ((JT + MT <= 3) ? 8 : (JT + MT <= 6 ? 4 : 2))
+                            : ((JT + MT <= 2) ? 16 : (JT + MT <= 3 ? 8 : (JT + MT <= 6 ? 4 : 2)));
+  const int d = batch_depth(((dn.Kd + 31) / 32 + kDownWaves - 1) / kDownWaves, kMaxD);
+  LaunchTimer t(BWD ? 8 : 2, s);
+  auto go = [&](auto kern) {
+    hipExtLaunchKernelGGL(kern, dim3((unsigned)(n_down + n_dec)), dim3(kDownThreads), 0, s, t.start, t.stop, 0, dn, de,
+                          n_down, T);
+  };
+  if (BWD) {
+    if (d >= 8 && kMaxD >= 8) go(k_bwd_prologue<JT, MT, (kMaxD >= 8 ? 8 : 1), kDqE4M3>);
+    else if (d >= 4 && kMaxD >= 4) go(k_bwd_prologue<JT, MT, (kMaxD >= 4 ? 4 : 1), kDqE4M3>);
+    else go(k_bwd_prologue<JT, MT, 2, kDqE4M3>);
+  } else {
+    if (d >= 16 && kMaxD >= 16) go(k_fwd_prologue<JT, MT, (kMaxD >= 16 ? 16 : 1), kDqE4M3>);
+    else if (d >= 8 && kMaxD >= 8) go(k_fwd_prologue<JT, MT, (kMaxD >= 8 ? 8 : 1), kDqE4M3>);
+    else if (d >= 4 && kMaxD >= 4) go(k_fwd_prologue<JT, MT, (kMaxD >= 4 ? 4 : 1), kDqE4M3>);
+    else go(k_fwd_prologue<JT, MT, 2, kDqE4M3>);
+  }
+  return hipGetLastError();
+}
+
+template <bool BWD>
+hipError_t prologue_dispatch(const DownArgs& dn, const DecodeArgs& de, const Nf4Tables& T, hipStream_t s) {
+  if (dn.R <= 16) return prologue_launch<1, 1, BWD>(dn, de, T, s);
+  if (dn.R <= 32) return prologue_launch<2, 1, BWD>(dn, de, T, s);
+  if (dn.R <= 64) return prologue_launch<4, 2, BWD>(dn, de, T, s);
+  return prologue_launch<8, 2, BWD>(dn, de, T, s);
+}
+
 template <int JT>
 int grad_depth(int64_t mps) {
   constexpr int kMaxD = JT <= 2 ? 8 : (JT <= 4 ? 4 : 2);  // <= 192 VGPRs of loads
@@ -478,6 +578,24 @@ hipError_t launch_lora_down(const uint16_t* P, const uint16_t* Q, int q_transpos
   if (R <= 32) return down_launch<2, 1, false>(P, Q, M, R, Kd, scale, out_s, out_u, s);
   if (R <= 64) return down_launch<4, 2, false>(P, Q, M, R, Kd, scale, out_s, out_u, s);
   return down_launch<8, 2, false>(P, Q, M, R, Kd, scale, out_s, out_u, s);
+}
+
+hipError_t launch_fwd_prologue(const uint16_t* X, const uint16_t* A, int64_t M, int32_t R, int64_t K, float scale,
+                               uint16_t* t_s, uint16_t* t_u, const uint32_t* codes, const uint8_t* code8,
+                               const float* c2s, const float* mu, int64_t N, uint16_t* w_out, const Nf4Tables& T,
+                               hipStream_t s) {
+  const DownArgs dn{X, A, M, R, K, scale, t_s, t_u};
+  const DecodeArgs de{codes, code8, c2s, mu, w_out, N, K};
+  return prologue_dispatch<false>(dn, de, T, s);
+}
+
+hipError_t launch_bwd_prologue(const uint16_t* dY, const uint16_t* B, int64_t M, int32_t R, int64_t N, float scale,
+                               uint16_t* g_s, uint16_t* g_u, const uint32_t* codes, const uint8_t* code8,
+                               const float* c2s, const float* mu, int64_t K, uint16_t* wt_out, const Nf4Tables& T,
+                               hipStream_t s) {
+  const DownArgs dn{dY, B, M, R, N, scale, g_s, g_u};
+  const DecodeArgs de{codes, code8, c2s, mu, wt_out, N, K};
+  return prologue_dispatch<true>(dn, de, T, s);
 }
 
 int32_t lora_grad_msplit(int64_t M, int64_t C) {

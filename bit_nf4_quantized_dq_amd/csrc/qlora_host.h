@@ -71,6 +71,17 @@ hipError_t launch_lora_down(const uint16_t* P, const uint16_t* Q, int q_transpos
 int32_t lora_grad_msplit(int64_t M, int64_t C);
 hipError_t launch_lora_grad(const uint16_t* U, const uint16_t* V, int64_t M, int32_t R, int64_t C, float scale,
                             int transposed, float* part, int counter_set, uint16_t* out, hipStream_t s);
+// The step's prologues as one launch each (E4M3 constants): the down-projection T = X A^T
+// (t_s = scale T, t_u = T) with the decoded copy w_out = w_hat [N, K]; and G = dY B (g_s, g_u)
+// with the transposed decoded copy wt_out = w_hat^T [K, N].
+hipError_t launch_fwd_prologue(const uint16_t* X, const uint16_t* A, int64_t M, int32_t R, int64_t K, float scale,
+                               uint16_t* t_s, uint16_t* t_u, const uint32_t* codes, const uint8_t* code8,
+                               const float* c2s, const float* mu, int64_t N, uint16_t* w_out, const Nf4Tables& T,
+                               hipStream_t s);
+hipError_t launch_bwd_prologue(const uint16_t* dY, const uint16_t* B, int64_t M, int32_t R, int64_t N, float scale,
+                               uint16_t* g_s, uint16_t* g_u, const uint32_t* codes, const uint8_t* code8,
+                               const float* c2s, const float* mu, int64_t K, uint16_t* wt_out, const Nf4Tables& T,
+                               hipStream_t s);
 // Two such products in one launch (counter sets 0 and 1), e.g. dA and dB of one backward.
 hipError_t launch_lora_grad2(const uint16_t* U0, const uint16_t* V0, int64_t C0, int transposed0, float* part0,
                              uint16_t* out0, const uint16_t* U1, const uint16_t* V1, int64_t C1, int transposed1,
