@@ -147,7 +147,9 @@ def seventy_b_model(dev, layers=80, passes=3):
     """70B-class model: 80 layers x 7 linears (q, o 8192^2; k, v 1024x8192; gate, up
     28672x8192; down 8192x28672), NF4+DQ resident on the GPU (~35 GB), LoRA r = 16 on every
     linear.  M = 1: one forward through all linears, captured once in a HIP graph and replayed
-    (every call streams its own weights from HBM).  M = 2048: one eager forward pass."""
+    (every call streams its own weights from HBM), first one call per linear, then with the
+    linears that share an input (q, k, v and gate, up) as grouped launches.  M = 2048: one
+    eager forward pass."""
     import torch
 
     import bit_nf4_quantized_dq_amd as Q
@@ -169,36 +171,58 @@ def seventy_b_model(dev, layers=80, passes=3):
     out = {"weights_GB": round(weights_gb, 3), "linears": len(lin)}
     for M in (1, 2048):
         Xs = {K: I.activations(5, 99, M, K, device=dev) for _, K in shapes}
-        Ys = {N: torch.empty(M, N, dtype=torch.bfloat16, device=dev) for N, _ in shapes}
-        ws = torch.empty(max(Q.workspace_size(Q.OP_FWD, M, N, K, r) for N, K in shapes), dtype=torch.uint8, device=dev)
+        Ys = [torch.empty(M, s.d_out, dtype=torch.bfloat16, device=dev) for s in I.SEVENTY_B_LAYER]
+        need = max(Q.workspace_size(Q.OP_FWD, M, N, K, r) for N, K in shapes)
+        groups = [[0, 1, 2], [3], [4, 5], [6]]  # q, k, v | o | gate, up | down: each group reads one input
+        for grp_ in groups:
+            if len(grp_) > 1:
+                need = max(need, Q.workspace_size_multi([lin[i][0] for i in grp_], M, r))
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
 
         def fwd_pass():
-            for q, A, B in lin:
-                Q.linear_fwd(q, Xs[q.d_in], A, B, alpha, Y=Ys[q.d_out], ws=ws)
+            for i, (q, A, B) in enumerate(lin):
+                Q.linear_fwd(q, Xs[q.d_in], A, B, alpha, Y=Ys[i % 7], ws=ws)
+
+        def fwd_pass_grouped():
+            for layer in range(layers):
+                base = 7 * layer
+                for grp_ in groups:
+                    if len(grp_) == 1:
+                        q, A, B = lin[base + grp_[0]]
+                        Q.linear_fwd(q, Xs[q.d_in], A, B, alpha, Y=Ys[grp_[0]], ws=ws)
+                    else:
+                        qs = [lin[base + i][0] for i in grp_]
+                        Q.linear_fwd_multi(qs, Xs[qs[0].d_in], [lin[base + i][1] for i in grp_],
+                                           [lin[base + i][2] for i in grp_], alpha, Ys=[Ys[i] for i in grp_], ws=ws)
 
         fwd_pass()
         torch.cuda.synchronize()
         if M == 1:
-            g = torch.cuda.CUDAGraph()
-            cap = torch.cuda.Stream()
-            cap.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(cap):
-                with torch.cuda.graph(g, stream=cap):
-                    fwd_pass()
+            fwd_pass_grouped()
             torch.cuda.synchronize()
-            g.replay()
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for _ in range(passes):
+            for key, fn, what in (("M1", fwd_pass, "one launch per linear"),
+                                  ("M1_grouped", fwd_pass_grouped, "q/k/v and gate/up as grouped launches")):
+                g = torch.cuda.CUDAGraph()
+                cap = torch.cuda.Stream()
+                cap.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(cap):
+                    with torch.cuda.graph(g, stream=cap):
+                        fn()
+                torch.cuda.synchronize()
                 g.replay()
-            torch.cuda.synchronize()
-            ms = 1e3 * (time.perf_counter() - t0) / passes
-            out["M1"] = {"metric": "weight-stream GB/s at M=1 through all 560 linears (graph replay)",
-                         "value": round(nbytes1 / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "ms_per_pass": round(ms, 3),
-                         "bytes_per_pass": nbytes1, "frac_of_hbm_peak": round(nbytes1 / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                         "gate_28672x8192_call": {"algorithmic_bytes": stream_bytes(1, 28672, 8192, r),
-                                                  "counter_bytes": counter_traffic("gemv_stream")}}
-            del g
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(passes):
+                    g.replay()
+                torch.cuda.synchronize()
+                ms = 1e3 * (time.perf_counter() - t0) / passes
+                out[key] = {"metric": f"weight-stream GB/s at M=1 through all 560 linears, {what} (graph replay)",
+                            "value": round(nbytes1 / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "ms_per_pass": round(ms, 3),
+                            "bytes_per_pass": nbytes1,
+                            "frac_of_hbm_peak": round(nbytes1 / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+                del g
+            out["M1"]["gate_28672x8192_call"] = {"algorithmic_bytes": stream_bytes(1, 28672, 8192, r),
+                                                 "counter_bytes": counter_traffic("gemv_stream")}
         else:
             t0 = time.perf_counter()
             for _ in range(passes):

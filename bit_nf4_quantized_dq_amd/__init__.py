@@ -20,6 +20,8 @@ from ._binding import (  # noqa: F401
     adamw_step,
     dequantize,
     linear_fwd,
+    linear_fwd_multi,
+    workspace_size_multi,
     linear_bwd,
     e4m3_encode,
     quant_sizes,

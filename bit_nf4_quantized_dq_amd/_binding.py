@@ -79,6 +79,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         "qlora_merge": (P(_Nf4dq), vp, vp, i32, ctypes.c_float, vp, vp),
         "qlora_linear_fwd": (P(_Nf4dq), vp, i64, vp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp),
         "qlora_linear_bwd": (P(_Nf4dq), vp, vp, i64, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp),
+        "qlora_workspace_size_multi": (ctypes.c_int, P(P(_Nf4dq)), i64, i32, P(sz)),
+        "qlora_linear_fwd_multi": (ctypes.c_int, P(P(_Nf4dq)), vp, i64, P(vp), P(vp), i32, ctypes.c_float, P(vp),
+                                   P(vp), vp, sz, vp),
         "qlora_adamw_step": (vp, vp, vp, vp, vp, i64, i64, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                              ctypes.c_float, ctypes.c_float, vp),
         "qlora_e4m3_encode": (vp, vp, i64, vp),
@@ -285,6 +288,49 @@ def linear_fwd(q: QuantizedWeight, X: torch.Tensor, A: torch.Tensor, B: torch.Te
                                            float(alpha), Y.data_ptr(), _ptr(T_save), ws.data_ptr(), ws.numel(),
                                            _stream(X)), "linear_fwd")
     return Y
+
+
+def _struct_array(qs):
+    """Host array of pointers to descriptor structs (the structs are kept alive with it)."""
+    structs = [q.struct() for q in qs]
+    arr = (ctypes.POINTER(_Nf4dq) * len(qs))(*[ctypes.pointer(x) for x in structs])
+    return arr, structs
+
+
+def workspace_size_multi(qs, M: int, r: int) -> int:
+    arr, _keep = _struct_array(qs)
+    n = ctypes.c_size_t()
+    _check(load_library().qlora_workspace_size_multi(len(qs), arr, M, r, ctypes.byref(n)), "workspace_size_multi")
+    return n.value
+
+
+def linear_fwd_multi(qs, X: torch.Tensor, As, Bs, alpha: float, Ys=None, T_saves=None,
+                     ws: torch.Tensor | None = None):
+    """Forward of up to 4 linears that read the same X (e.g. q, k, v): returns the list of Y[i]."""
+    qs = list(qs)
+    _dev(X, torch.bfloat16, "X")
+    for i in range(len(qs)):
+        _dev(As[i], torch.bfloat16, f"A[{i}]")
+        _dev(Bs[i], torch.bfloat16, f"B[{i}]")
+    M, r = X.shape[0], As[0].shape[0]
+    Ys = list(Ys) if Ys is not None else [torch.empty(M, q.d_out, dtype=torch.bfloat16, device=X.device) for q in qs]
+    for i, y in enumerate(Ys):
+        _dev(y, torch.bfloat16, f"Y[{i}]")
+    need = workspace_size_multi(qs, M, r)
+    ws = ws if ws is not None else _WS.get(need, X.device, "fwd")
+    arr, _keep = _struct_array(qs)
+    n = len(qs)
+    VP = ctypes.c_void_p * n
+    a_ptrs, b_ptrs, y_ptrs = VP(*[a.data_ptr() for a in As]), VP(*[b.data_ptr() for b in Bs]), VP(*[y.data_ptr() for y in Ys])
+    t_ptrs = None
+    if T_saves is not None:
+        for t in T_saves:
+            if t is not None:
+                _dev(t, torch.bfloat16, "T_save")
+        t_ptrs = VP(*[_ptr(t) for t in T_saves])
+    _check(load_library().qlora_linear_fwd_multi(n, arr, X.data_ptr(), M, a_ptrs, b_ptrs, r, float(alpha), y_ptrs,
+                                                 t_ptrs, ws.data_ptr(), ws.numel(), _stream(X)), "linear_fwd_multi")
+    return Ys
 
 
 def linear_bwd(q: QuantizedWeight, X: torch.Tensor, dY: torch.Tensor, A: torch.Tensor, B: torch.Tensor,

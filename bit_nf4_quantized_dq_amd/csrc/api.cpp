@@ -115,6 +115,44 @@ BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r, int dq) {
   return w;
 }
 
+// Grouped forward (qlora_linear_fwd_multi): one weight-streaming launch over linears that
+// share X, else one qlora_linear_fwd per linear in the same workspace.
+struct GroupWs {
+  bool one_launch;
+  size_t tpart, ypart, total;
+};
+GroupWs group_ws(int count, const qlora_nf4dq_t* const* Wq, int64_t M, int32_t r) {
+  GroupWs w{};
+  int64_t N[kStreamMaxGroup];
+  const int64_t K = Wq[0]->d_in;
+  bool one = count >= 2 && M <= kGemvMaxM;
+  for (int i = 0; i < count; ++i) {
+    N[i] = Wq[i]->d_out;
+    one = one && Wq[i]->dq_format == QLORA_DQ_E4M3 && Wq[i]->codebook == Wq[0]->codebook;
+    w.total = std::max(w.total, fwd_ws(M, N[i], K, r, Wq[i]->dq_format).total);
+  }
+  w.one_launch = one && gemv_stream_group_fits(count, N, K, M, r);
+  if (w.one_launch) {
+    int64_t Nt = 0;
+    for (int i = 0; i < count; ++i) Nt += N[i];
+    const int32_t ks = gemv_stream_plan(Nt, K, M, r).ksplit;
+    w.tpart = 0;
+    w.ypart = align_up(sizeof(float) * count * ks * M * r, 256);
+    w.total = std::max(w.total, align_up(w.ypart + sizeof(float) * ks * M * Nt, 256));
+  }
+  return w;
+}
+
+int check_group(int count, const qlora_nf4dq_t* const* Wq) {
+  if (count < 1 || count > kStreamMaxGroup || !Wq) return QLORA_ERR_INVALID_ARG;
+  for (int i = 0; i < count; ++i) {
+    int st = check_wq(Wq[i]);
+    if (st) return st;
+    if (Wq[i]->d_in != Wq[0]->d_in) return QLORA_ERR_BAD_SHAPE;
+  }
+  return QLORA_OK;
+}
+
 size_t quant_ws(int64_t d_out, int64_t d_in) {
   const int64_t nb = d_out * d_in / 64;
   return align_up(sizeof(float) * nb, 256) + 256 * sizeof(unsigned long long) + 256;
@@ -385,6 +423,45 @@ int qlora_linear_fwd(const qlora_nf4dq_t* Wq, const uint16_t* X, int64_t M, cons
   if ((e = launch_lora_down(X, A, 0, M, r, K, s, ls, T_save, stream)) != hipSuccess) return QLORA_ERR_HIP;
   e = launch_gemm_fwd(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, X, M, ls, B, r, Y, tables_of(Wq), stream);
   return hip_status(e);
+}
+
+int qlora_workspace_size_multi(int count, const qlora_nf4dq_t* const* Wq, int64_t M, int32_t r, size_t* ws_bytes) {
+  if (!ws_bytes) return QLORA_ERR_INVALID_ARG;
+  int st = check_group(count, Wq);
+  if (st) return st;
+  if ((st = check_lora(M, r, 1.0f))) return st;
+  *ws_bytes = group_ws(count, Wq, M, r).total;
+  return QLORA_OK;
+}
+
+int qlora_linear_fwd_multi(int count, const qlora_nf4dq_t* const* Wq, const uint16_t* X, int64_t M,
+                           const uint16_t* const* A, const uint16_t* const* B, int32_t r, float alpha,
+                           uint16_t* const* Y, uint16_t* const* T_save, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  int st = check_group(count, Wq);
+  if (st) return st;
+  if ((st = check_lora(M, r, alpha))) return st;
+  if (!X || !A || !B || !Y || !aligned16(X)) return QLORA_ERR_INVALID_ARG;
+  for (int i = 0; i < count; ++i)
+    if (!A[i] || !B[i] || !Y[i] || !aligned16(A[i]) || !aligned16(Y[i])) return QLORA_ERR_INVALID_ARG;
+  const GroupWs L = group_ws(count, Wq, M, r);
+  if (!ws || ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
+  if (!L.one_launch) {
+    for (int i = 0; i < count; ++i) {
+      st = qlora_linear_fwd(Wq[i], X, M, A[i], B[i], r, alpha, Y[i], T_save ? T_save[i] : nullptr, ws, ws_bytes,
+                            stream);
+      if (st) return st;
+    }
+    return QLORA_OK;
+  }
+  StreamLinear lins[kStreamMaxGroup];
+  for (int i = 0; i < count; ++i)
+    lins[i] = StreamLinear{reinterpret_cast<const uint32_t*>(Wq[i]->codes), Wq[i]->code8, Wq[i]->c2s, Wq[i]->mu,
+                           Wq[i]->d_out, A[i], B[i], Y[i], T_save ? T_save[i] : nullptr};
+  char* base = static_cast<char*>(ws);
+  return hip_status(launch_gemv_stream_group(count, lins, Wq[0]->d_in, X, M, r, alpha / (float)r,
+                                             reinterpret_cast<float*>(base + L.ypart),
+                                             reinterpret_cast<float*>(base + L.tpart), tables_of(Wq[0]), stream));
 }
 
 int qlora_linear_bwd(const qlora_nf4dq_t* Wq, const uint16_t* X, const uint16_t* dY, int64_t M, const uint16_t* A,

@@ -29,6 +29,12 @@
 // chunk, for every 16-rank tile), applies B to it for its rows, and adds that to its partial
 // output.
 //
+// Grouped launch.  Linears that read the same activations (the q, k and v projections of a
+// decoder layer, or its gate and up projections) can run as one launch: their row groups
+// are numbered one after the other, each workgroup first finds the linear its row group
+// belongs to, and from there on works as in a single launch.  One launch pays the start-up
+// and the split-K hand-off once for the whole group instead of once per linear.
+//
 // Split-K reduction.  With ksplit > 1 each workgroup writes an FP32 partial; the last
 // workgroup of a row group to finish (a device-scope counter; that workgroup resets it to
 // zero) sums the partials in a fixed order and writes BF16 Y (and T for the backward).  The
@@ -111,6 +117,26 @@ struct StreamArgs {
   int32_t c2max;   // scales staged per workgroup
 };
 
+// Per-linear operands of a grouped launch (count <= kMaxLin linears of d_out a multiple of
+// kRows, sharing d_in, M, r and the codebook).  Row group g of the launch belongs to linear i
+// for gstart[i] <= g < gstart[i + 1].
+constexpr int kMaxLin = 4;
+struct StreamGroup {
+  const uint8_t* codes[kMaxLin];
+  const uint8_t* code8[kMaxLin];
+  const float* c2s[kMaxLin];
+  const float* mu[kMaxLin];
+  const uint16_t* A[kMaxLin];
+  const uint16_t* B[kMaxLin];
+  uint16_t* Y[kMaxLin];
+  uint16_t* T_save[kMaxLin];
+  int32_t gstart[kMaxLin + 1];
+  int32_t count;
+};
+struct NoGroup {};
+template <bool MULTI> struct GroupArg { typedef NoGroup type; };
+template <> struct GroupArg<true> { typedef StreamGroup type; };
+
 struct Smem {
   uint8_t lut[kLutBytes];  // first, so that its LDS address is 0
   uint8_t region[kRegion];
@@ -128,8 +154,8 @@ struct Chunk {
 // RT16: 16-wide rank tiles (r <= 16 RT16).  NQ: accumulator registers kept (1 for M = 1,
 // where only row 0 of the 32x32 product is live; 8 for M <= 16).  K is a multiple of 256, so
 // a chunk's four E4M3 bytes form one aligned word and share one second-level scale.
-template <int RT16, int NQ, int kDepth>
-__global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L) {
+template <int RT16, int NQ, int kDepth, bool MULTI>
+__global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L, typename GroupArg<MULTI>::type G) {
   __shared__ Smem sm;
   const uint8_t* const sLut = sm.lut;
   uint8_t* const sR = sm.region;
@@ -137,23 +163,51 @@ __global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5, l16 = lane & 15, g = lane >> 4;
-  const int64_t N = a.N, K = a.K;
+  // Nt, pgrp: rows and row group of the launch (partials, counters); N, grp: of the linear
+  const int64_t Nt = a.N, K = a.K;
   const int M = a.M;
   const int64_t nb_row = K / kBlock1;
-  const int64_t grp = blockIdx.x;
+  const int64_t pgrp = blockIdx.x;
   const int ks = blockIdx.y;
+  int64_t N = Nt, grp = pgrp;
+  float* tpart = a.tpart;
+  const uint8_t* w_codes = a.codes;
+  const uint8_t* w_code8 = a.code8;
+  const float* w_c2s = a.c2s;
+  const float* w_mu = a.mu;
+  const uint16_t* l_A = a.A;
+  const uint16_t* l_B = a.B;
+  uint16_t* o_Y = a.Y;
+  uint16_t* o_T = a.T_save;
+  if constexpr (MULTI) {
+    int li = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxLin; ++i)
+      if (i < G.count && (int)blockIdx.x >= G.gstart[i]) li = i;
+    w_codes = G.codes[li];
+    w_code8 = G.code8[li];
+    w_c2s = G.c2s[li];
+    w_mu = G.mu[li];
+    l_A = G.A[li];
+    l_B = G.B[li];
+    o_Y = G.Y[li];
+    o_T = G.T_save[li];
+    N = (int64_t)(G.gstart[li + 1] - G.gstart[li]) * kRows;
+    grp = pgrp - G.gstart[li];
+    tpart += (int64_t)li * a.ksplit * M * a.r;
+  }
   const int64_t b0 = (int64_t)ks * a.nbs;
   const int64_t b1 = (b0 + a.nbs < nb_row) ? b0 + a.nbs : nb_row;
   const int64_t row0 = grp * kRows;
   const int64_t n = row0 + 32 * wave + l32;  // this lane's weight row
-  const float mu = a.mu[0];
+  const float mu = w_mu[0];
 
-  const rsrc_t rc = make_rsrc(a.codes, N * (K / 2));
-  const rsrc_t r8 = make_rsrc(a.code8, N * nb_row);
-  const rsrc_t r2 = make_rsrc(a.c2s, ((N * nb_row + 255) / 256) * 4);
+  const rsrc_t rc = make_rsrc(w_codes, N * (K / 2));
+  const rsrc_t r8 = make_rsrc(w_code8, N * nb_row);
+  const rsrc_t r2 = make_rsrc(w_c2s, ((N * nb_row + 255) / 256) * 4);
   const rsrc_t rx = make_rsrc(a.X, (int64_t)M * K * 2);
-  const rsrc_t ra = make_rsrc(a.A, (int64_t)a.r * K * 2);
-  const rsrc_t rb = make_rsrc(a.B, N * a.r * 2);
+  const rsrc_t ra = make_rsrc(l_A, (int64_t)a.r * K * 2);
+  const rsrc_t rb = make_rsrc(l_B, N * a.r * 2);
 
   const uint32_t code_row = n < N ? (uint32_t)(n * (K / 2)) + 16u * h : kOOB;
   // first second-level group touched by this workgroup
@@ -356,32 +410,33 @@ __global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int m = 8 * (q / 4) + 4 * h + (q % 4);
-      if (m < M && n < N) a.Y[(int64_t)m * N + n] = (uint16_t)(pack_bf16x2(acc[q], 0.f) & 0xFFFFu);
+      if (m < M && n < N) o_Y[(int64_t)m * N + n] = (uint16_t)(pack_bf16x2(acc[q], 0.f) & 0xFFFFu);
     }
-    if (a.T_save && grp == 0) {
+    if (o_T && grp == 0) {
       for (int i = tid; i < M * a.r; i += kThreads)
-        a.T_save[i] = (uint16_t)(pack_bf16x2(sT[i / a.r][i % a.r], 0.f) & 0xFFFFu);
+        o_T[i] = (uint16_t)(pack_bf16x2(sT[i / a.r][i % a.r], 0.f) & 0xFFFFu);
     }
     return;
   }
+  const int64_t pn = pgrp * kRows + 32 * wave + l32;  // this lane's column of the launch's partials
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const int m = 8 * (q / 4) + 4 * h + (q % 4);
     if (m < M && n < N)
-      __hip_atomic_store(a.part + ((int64_t)ks * M + m) * N + n, acc[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      __hip_atomic_store(a.part + ((int64_t)ks * M + m) * Nt + pn, acc[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
   if (grp == 0) {
     for (int i = tid; i < M * a.r; i += kThreads)
-      __hip_atomic_store(a.tpart + (int64_t)ks * M * a.r + i, sT[i / a.r][i % a.r], __ATOMIC_RELAXED,
+      __hip_atomic_store(tpart + (int64_t)ks * M * a.r + i, sT[i / a.r][i % a.r], __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_SYSTEM);
   }
   // every partial store of this workgroup has completed before its counter increment
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
-    const unsigned int old = __hip_atomic_fetch_add(&g_stream_counters[grp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned int old = __hip_atomic_fetch_add(&g_stream_counters[pgrp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sm.last = (old + 1u == (unsigned int)a.ksplit) ? 1u : 0u;
-    if (sm.last) __hip_atomic_store(&g_stream_counters[grp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (sm.last) __hip_atomic_store(&g_stream_counters[pgrp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   if (!sm.last) return;
@@ -400,12 +455,14 @@ __global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L) {
   };
   const int64_t nrows = (row0 + kRows <= N) ? kRows : N - row0;
   for (int64_t i = tid; i < (int64_t)M * nrows; i += kThreads) {
-    const int64_t m = i / nrows, nn = row0 + i % nrows;
-    a.Y[m * N + nn] = (uint16_t)(pack_bf16x2(sum_published(a.part + m * N + nn, a.ksplit, (int64_t)M * N), 0.f) & 0xFFFFu);
+    const int64_t m = i / nrows, nn = i % nrows;
+    o_Y[m * N + row0 + nn] =
+        (uint16_t)(pack_bf16x2(sum_published(a.part + m * Nt + pgrp * kRows + nn, a.ksplit, (int64_t)M * Nt), 0.f) &
+                   0xFFFFu);
   }
-  if (a.T_save && grp == 0) {
+  if (o_T && grp == 0) {
     for (int i = tid; i < M * a.r; i += kThreads)
-      a.T_save[i] = (uint16_t)(pack_bf16x2(sum_published(a.tpart + i, a.ksplit, (int64_t)M * a.r), 0.f) & 0xFFFFu);
+      o_T[i] = (uint16_t)(pack_bf16x2(sum_published(tpart + i, a.ksplit, (int64_t)M * a.r), 0.f) & 0xFFFFu);
   }
 }
 
@@ -470,31 +527,47 @@ bool gemv_stream_fits(int64_t N, int64_t K, int64_t M, int32_t r) {
   return gemv_stream_plan(N, K, M, r).ksplit >= 1;
 }
 
-hipError_t launch_gemv_stream(const uint32_t* codes, const uint8_t* code8, const float* c2s,
-                           const float* mu, int64_t N, int64_t K, const uint16_t* X, int64_t M,
-                           const uint16_t* A, const uint16_t* B, int32_t r, float s, uint16_t* Y,
-                           uint16_t* T_save, float* part, float* tpart, const Nf4Tables& T,
-                           hipStream_t st) {
-  if (M < 1 || M > 16 || r < 1 || r > kMaxR) return hipErrorInvalidValue;
-  const GemvPlan p = gemv_stream_plan(N, K, M, r);
+bool gemv_stream_group_fits(int count, const int64_t* N, int64_t K, int64_t M, int32_t r) {
+  if (count < 2 || count > kMaxLin) return false;
+  int64_t Nt = 0;
+  for (int i = 0; i < count; ++i) {
+    if (N[i] < 1 || N[i] % kRows != 0) return false;
+    Nt += N[i];
+  }
+  return Nt / kRows <= 65536 && gemv_stream_fits(Nt, K, M, r);
+}
+
+namespace {
+
+// One launch over `count` linears (count == 1: the single-linear kernel, without the group
+// table in its arguments).
+hipError_t stream_launch(int count, const StreamLinear* lins, int64_t K, const uint16_t* X, int64_t M, int32_t r,
+                         float s, float* part, float* tpart, const Nf4Tables& T, hipStream_t st) {
+  if (count < 1 || count > kMaxLin || M < 1 || M > 16 || r < 1 || r > kMaxR) return hipErrorInvalidValue;
+  int64_t Nt = 0;
+  for (int i = 0; i < count; ++i) {
+    if (count > 1 && lins[i].N % kRows != 0) return hipErrorInvalidValue;
+    Nt += lins[i].N;
+  }
+  const GemvPlan p = gemv_stream_plan(Nt, K, M, r);
   const int64_t nb_row = K / kBlock1;
   const RegionUse u = region_use(nb_row, M, p.nbs, p.nchunk);
   if (p.ksplit < 1 || u.total > kRegion || (M + 1) * p.nchunk * kCB * 8 > 8 * kThreads || u.c2max > kThreads ||
-      u.c8dw > kC8Loads * kThreads || nb_row % kCB != 0)
+      u.c8dw > kC8Loads * kThreads || nb_row % kCB != 0 || p.groups > 65536)
     return hipErrorInvalidValue;
   StreamArgs a;
-  a.codes = reinterpret_cast<const uint8_t*>(codes);
-  a.code8 = code8;
-  a.c2s = c2s;
-  a.mu = mu;
+  a.codes = reinterpret_cast<const uint8_t*>(lins[0].codes);
+  a.code8 = lins[0].code8;
+  a.c2s = lins[0].c2s;
+  a.mu = lins[0].mu;
   a.X = X;
-  a.A = A;
-  a.B = B;
-  a.Y = Y;
-  a.T_save = T_save;
+  a.A = lins[0].A;
+  a.B = lins[0].B;
+  a.Y = lins[0].Y;
+  a.T_save = lins[0].T_save;
   a.part = part;
   a.tpart = tpart;
-  a.N = N;
+  a.N = Nt;
   a.K = K;
   a.M = (int32_t)M;
   a.r = r;
@@ -512,14 +585,37 @@ hipError_t launch_gemv_stream(const uint32_t* codes, const uint8_t* code8, const
     L.lo[w] = T.lut_lo[w];
     L.hi[w] = T.lut_hi[w];
   }
+  StreamGroup G{};
+  NoGroup none;
+  G.count = count;
+  G.gstart[0] = 0;
+  for (int i = 0; i < count; ++i) {
+    G.codes[i] = reinterpret_cast<const uint8_t*>(lins[i].codes);
+    G.code8[i] = lins[i].code8;
+    G.c2s[i] = lins[i].c2s;
+    G.mu[i] = lins[i].mu;
+    G.A[i] = lins[i].A;
+    G.B[i] = lins[i].B;
+    G.Y[i] = lins[i].Y;
+    G.T_save[i] = lins[i].T_save;
+    G.gstart[i + 1] = G.gstart[i] + (int32_t)(lins[i].N / kRows);
+  }
+  for (int i = count + 1; i <= kMaxLin; ++i) G.gstart[i] = G.gstart[count];
   dim3 grid((unsigned)p.groups, (unsigned)p.ksplit);
   LaunchTimer t(3, st);
-#define QLORA_GEMV_GO(RT16, NQ, D)                                                                       \
-  do {                                                                                                   \
-    if (p.nchunk == 1)                                                                                   \
-      hipExtLaunchKernelGGL((k_gemv_stream<RT16, NQ, 1>), grid, dim3(kThreads), 0, st, t.start, t.stop, 0, a, L); \
-    else                                                                                                 \
-      hipExtLaunchKernelGGL((k_gemv_stream<RT16, NQ, D>), grid, dim3(kThreads), 0, st, t.start, t.stop, 0, a, L); \
+#define QLORA_GEMV_GO1(RT16, NQ, D)                                                                                  \
+  do {                                                                                                               \
+    if (count > 1)                                                                                                   \
+      hipExtLaunchKernelGGL((k_gemv_stream<RT16, NQ, D, true>), grid, dim3(kThreads), 0, st, t.start, t.stop, 0, a, \
+                            L, G);                                                                                   \
+    else                                                                                                             \
+      hipExtLaunchKernelGGL((k_gemv_stream<RT16, NQ, D, false>), grid, dim3(kThreads), 0, st, t.start, t.stop, 0, a, \
+                            L, none);                                                                                \
+  } while (0)
+#define QLORA_GEMV_GO(RT16, NQ, D)            \
+  do {                                        \
+    if (p.nchunk == 1) QLORA_GEMV_GO1(RT16, NQ, 1); \
+    else QLORA_GEMV_GO1(RT16, NQ, D);         \
   } while (0)
   if (M == 1) {
     if (r <= 16) QLORA_GEMV_GO(1, 1, 3);
@@ -533,7 +629,26 @@ hipError_t launch_gemv_stream(const uint32_t* codes, const uint8_t* code8, const
     else QLORA_GEMV_GO(8, 8, 2);
   }
 #undef QLORA_GEMV_GO
+#undef QLORA_GEMV_GO1
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv_stream(const uint32_t* codes, const uint8_t* code8, const float* c2s,
+                              const float* mu, int64_t N, int64_t K, const uint16_t* X, int64_t M,
+                              const uint16_t* A, const uint16_t* B, int32_t r, float s, uint16_t* Y,
+                              uint16_t* T_save, float* part, float* tpart, const Nf4Tables& T,
+                              hipStream_t st) {
+  const StreamLinear one{codes, code8, c2s, mu, N, A, B, Y, T_save};
+  return stream_launch(1, &one, K, X, M, r, s, part, tpart, T, st);
+}
+
+hipError_t launch_gemv_stream_group(int count, const StreamLinear* lins, int64_t K, const uint16_t* X, int64_t M,
+                                    int32_t r, float s, float* part, float* tpart, const Nf4Tables& T,
+                                    hipStream_t st) {
+  if (count < 2) return hipErrorInvalidValue;
+  return stream_launch(count, lins, K, X, M, r, s, part, tpart, T, st);
 }
 
 }  // namespace qlora

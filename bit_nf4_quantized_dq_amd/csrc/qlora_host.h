@@ -108,6 +108,25 @@ hipError_t launch_gemv_stream(const uint32_t* codes, const uint8_t* code8, const
                               const uint16_t* A, const uint16_t* B, int32_t r, float s, uint16_t* Y,
                               uint16_t* T_save, float* part, float* tpart, const Nf4Tables& T,
                               hipStream_t st);
+// Grouped form: count (2..4) linears that read the same X [M, K], each d_out a multiple of
+// 256, run as one launch.  Partials: part [ksplit][M][sum of d_out], tpart [count][ksplit][M][r],
+// with ksplit = gemv_stream_plan(sum of d_out, K, M, r).ksplit.
+struct StreamLinear {
+  const uint32_t* codes;
+  const uint8_t* code8;
+  const float* c2s;
+  const float* mu;
+  int64_t N;
+  const uint16_t* A;
+  const uint16_t* B;
+  uint16_t* Y;
+  uint16_t* T_save;
+};
+constexpr int kStreamMaxGroup = 4;
+bool gemv_stream_group_fits(int count, const int64_t* N, int64_t K, int64_t M, int32_t r);
+hipError_t launch_gemv_stream_group(int count, const StreamLinear* lins, int64_t K, const uint16_t* X, int64_t M,
+                                    int32_t r, float s, float* part, float* tpart, const Nf4Tables& T,
+                                    hipStream_t st);
 
 // ---- fused dequant MFMA GEMMs (gemm.hip)
 // Y[M,N] = X[M,K] w_hat^T + L[M,r] B[N,r]^T, L = s*T (BF16, prescaled)

@@ -189,6 +189,26 @@ int qlora_linear_fwd(const qlora_nf4dq_t *Wq, const uint16_t *X, int64_t M, cons
                      const uint16_t *B, int32_t r, float alpha, uint16_t *Y, uint16_t *T_save,
                      void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* The forward of several linears that read the same input, e.g. the q, k and v projections or
+ * the gate and up projections of a decoder layer: for i < count,
+ *   Y[i] = X w_hat_i^T + (alpha / r) (X A[i]^T) B[i]^T      (as qlora_linear_fwd)
+ *   Wq: host array of count (1..4) weight descriptors, all with the same d_in.
+ *   A, B, Y: host arrays of count device pointers (A[i] [r, d_in], B[i] [d_out_i, r], Y[i]
+ *            [M, d_out_i], BF16).  T_save: host array of count device pointers (each may be
+ *            NULL) or NULL.  X [M, d_in], r and alpha are shared.
+ *   ws: device workspace of qlora_workspace_size_multi() bytes.
+ * For M <= 16 with E4M3 constants, one codebook, every d_out a multiple of 256 and at least 32M
+ * weights in all, the linears run as one weight-streaming launch (start-up and split-K
+ * hand-off paid once for the group); otherwise this is count calls of qlora_linear_fwd in
+ * order, on the same workspace.  Results match qlora_linear_fwd within its rounding (the
+ * reduction split can differ).  Errors: as qlora_linear_fwd; BAD_SHAPE when d_in differs. */
+int qlora_workspace_size_multi(int count, const qlora_nf4dq_t *const *Wq, int64_t M, int32_t r,
+                               size_t *ws_bytes);
+int qlora_linear_fwd_multi(int count, const qlora_nf4dq_t *const *Wq, const uint16_t *X, int64_t M,
+                           const uint16_t *const *A, const uint16_t *const *B, int32_t r, float alpha,
+                           uint16_t *const *Y, uint16_t *const *T_save, void *ws, size_t ws_bytes,
+                           hipStream_t stream);
+
 /* Backward of qlora_linear_fwd.  With G = dY B:
  *   dX = dY w_hat + (alpha/r) G A      [M, d_in]   (may be NULL: not computed)
  *   dA = (alpha/r) G^T X               [r, d_in]

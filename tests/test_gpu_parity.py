@@ -306,7 +306,7 @@ def test_config4_llama3_8b_layer_sampled(gpu_lib, idx):
 STREAM_CASES = [
     # d_out, d_in, M, r
     (8192, 4096, 1, 16),
-    (8192 + 160, 4096, 3, 40),  # a partial row group; r not a multiple of 8 (B read element-wise)
+    (8192 + 160, 4096, 3, 40),  # a partial row group; B ranks past 32 read element by element
     (4352, 8192, 16, 128),      # M = 16 and the largest rank
     (12288, 4096, 2, 8),
 ]

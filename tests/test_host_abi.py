@@ -24,7 +24,7 @@ def L():
 def test_every_declared_symbol_is_exported(L):
     text = open(HEADER).read()
     names = sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text)))
-    assert len(names) == 17
+    assert len(names) == 19
     for n in names:
         assert hasattr(L, n), n
 
@@ -105,6 +105,60 @@ def test_shape_and_argument_errors_before_launch(L):
     assert adamw(p=ctypes.c_void_p(4098)) == -1
     assert adamw(lr=-1.0) == -1 and adamw(lr=float("nan")) == -1 and adamw(b1=1.0) == -1 and adamw(b2=-0.1) == -1
     assert adamw(eps=0.0) == -1 and adamw(wd=-0.5) == -1 and adamw(wd=float("inf")) == -1
+
+
+def test_grouped_forward_errors_before_launch(L):
+    """qlora_linear_fwd_multi / qlora_workspace_size_multi reject bad groups on the host."""
+    dummy = ctypes.c_void_p(4096)
+    ws = ctypes.c_void_p(8192)
+    P = ctypes.POINTER(B._Nf4dq)
+
+    def group(*wqs):
+        keep = list(wqs)
+        return (P * len(keep))(*[ctypes.pointer(w) for w in keep]), keep
+
+    VP = ctypes.c_void_p * 5
+    ptrs = VP(dummy, dummy, dummy, dummy, dummy)
+    n = ctypes.c_size_t()
+    ok, _k1 = group(_wq(), _wq(d_out=512))
+    assert L.qlora_workspace_size_multi(2, ok, 4, 8, ctypes.byref(n)) == 0 and n.value >= 256
+    assert L.qlora_workspace_size_multi(2, ok, 4, 8, None) == -1
+    assert L.qlora_workspace_size_multi(0, ok, 4, 8, ctypes.byref(n)) == -1
+    five, _k2 = group(*[_wq() for _ in range(5)])
+    assert L.qlora_workspace_size_multi(5, five, 4, 8, ctypes.byref(n)) == -1
+    assert L.qlora_linear_fwd_multi(5, five, dummy, 4, ptrs, ptrs, 8, 16.0, ptrs, None, ws, 1 << 20, None) == -1
+    mixed, _k3 = group(_wq(), _wq(d_in=512))
+    assert L.qlora_workspace_size_multi(2, mixed, 4, 8, ctypes.byref(n)) == -2
+    assert L.qlora_linear_fwd_multi(2, mixed, dummy, 4, ptrs, ptrs, 8, 16.0, ptrs, None, ws, 1 << 20, None) == -2
+    bad, _k4 = group(_wq(), _wq(b1=32))
+    assert L.qlora_linear_fwd_multi(2, bad, dummy, 4, ptrs, ptrs, 8, 16.0, ptrs, None, ws, 1 << 20, None) == -3
+    assert L.qlora_linear_fwd_multi(2, ok, None, 4, ptrs, ptrs, 8, 16.0, ptrs, None, ws, 1 << 20, None) == -1
+    assert L.qlora_linear_fwd_multi(2, ok, dummy, 4, None, ptrs, 8, 16.0, ptrs, None, ws, 1 << 20, None) == -1
+    holes = VP(dummy, None, dummy, dummy, dummy)
+    assert L.qlora_linear_fwd_multi(2, ok, dummy, 4, ptrs, ptrs, 8, 16.0, holes, None, ws, 1 << 20, None) == -1
+    assert L.qlora_linear_fwd_multi(2, ok, dummy, 4, ptrs, ptrs, 0, 16.0, ptrs, None, ws, 1 << 20, None) == -1
+    assert L.qlora_linear_fwd_multi(2, ok, dummy, 4, ptrs, ptrs, 8, 16.0, ptrs, None, ws, 16, None) == -5
+
+
+def test_grouped_workspace_covers_every_single_call():
+    """A group's workspace also holds each linear's own forward (the path taken when the
+    group does not run as one launch) and, for the one-launch case, the group's partials."""
+    from bit_nf4_quantized_dq_amd import QuantizedWeight
+    import torch
+
+    z = torch.zeros(16, dtype=torch.uint8)  # host buffers: only the sizes are read
+
+    def fake(d_out, d_in):
+        return QuantizedWeight(z, z, z.view(torch.float32), z.view(torch.float32)[:1], d_out, d_in)
+
+    for dims, M, r in [([8192, 1024, 1024], 1, 16), ([28672, 28672], 1, 16), ([4096, 4096], 16, 128),
+                       ([1008, 512], 4, 8), ([4096, 1024, 1024], 4096, 16)]:
+        qs = [fake(d, 8192 if dims[0] > 5000 else 4096) for d in dims]
+        need = B.workspace_size_multi(qs, M, r)
+        for q in qs:
+            assert need >= B.workspace_size(B.OP_FWD, M, q.d_out, q.d_in, r)
+        if M <= 16 and all(d % 256 == 0 for d in dims) and sum(dims) * qs[0].d_in >= (32 << 20):
+            assert need >= 4 * M * sum(dims)  # at least one split of FP32 partials
 
 
 def test_workspace_sizes_are_sane():
