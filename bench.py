@@ -59,8 +59,8 @@ COUNTER_TRAFFIC = {
               "read_bytes": 587_289_984, "write_bytes": 587_202_560},
     # one M = 1 call on a 28672 x 8192 weight (the gate shape of the 70B-class model)
     "gemv_stream": {"source": "bit_nf4_quantized_dq_amd/csrc/gemv_stream.hip",
-                    "sha1": "d9538abb192262e71f1f1da72ba17a277d416d2a",
-                    "read_bytes": 125_036_864, "write_bytes": 297_600},
+                    "sha1": "811d34250c8b0abc3a507f724811f74ec7698c9c",
+                    "read_bytes": 125_030_400, "write_bytes": 297_574},
 }
 
 
