@@ -243,10 +243,21 @@ __device__ __forceinline__ void store_tile(uint16_t* __restrict__ C, int64_t M, 
 }
 
 // Consecutive workgroups are dealt round-robin to the 8 XCDs (each with its own L2):
-// renumber so that one XCD gets a contiguous run of tiles in feature-fastest order.
+// renumber so that one XCD gets a contiguous run of tiles.  When the feature tiles divide
+// into columns of 4 that split the grid into 8 equal blocks (4 feature tiles x n/32 token
+// tiles), each XCD takes one block: at 16 x 16 tiles its L2 then sees 4 weight row blocks
+// and 8 token row blocks per reduction step instead of 16 and 2.  Otherwise it takes a run in
+// feature-fastest order.
 __device__ __forceinline__ void tile_xy(int64_t& tx, int64_t& ty) {
   const uint32_t gx = gridDim.x, n = gridDim.x * gridDim.y;
   uint32_t L = blockIdx.x + gx * blockIdx.y;
+  if ((n & 31) == 0 && gx % 4 == 0 && 32 % gx == 0) {
+    L = (L & 7) * (n >> 3) + (L >> 3);
+    const uint32_t per = n >> 3, xcd = L / per, w = L % per, cols = gx / 4;
+    tx = (xcd % cols) * 4 + (w % 4);
+    ty = (xcd / cols) * (per / 4) + w / 4;
+    return;
+  }
   if ((n & 7) == 0) L = (L & 7) * (n >> 3) + (L >> 3);
   tx = L % gx;
   ty = L / gx;
