@@ -25,6 +25,10 @@ constexpr int kThreads = 256;
 
 // W is FP32 (BF = false: two 16-byte loads per word) or BF16 (BF = true: one 16-byte load
 // per word, each value widened exactly to FP32).
+// Grid-stride over code words: a workgroup takes words w, w + stride, ... (stride = grid x
+// 256), so its LDS histogram gathers many blocks and the global histogram receives one
+// atomic per non-empty bin per workgroup.  The constants of a tensor share a few exponents,
+// so one atomic per block would pile onto the same few addresses.
 template <bool BF>
 __global__ __launch_bounds__(kThreads) void k_quant_pass1(const void* __restrict__ W,
                                                           uint32_t* __restrict__ codes,
@@ -36,63 +40,69 @@ __global__ __launch_bounds__(kThreads) void k_quant_pass1(const void* __restrict
   sh_hist[threadIdx.x] = 0ull;
   __syncthreads();
 
-  const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // one code word = 8 weights
-  const bool active = g < n_words;  // n_words is a multiple of 8, so whole blocks are active
-  float v[8];
-  if (active && BF) {
-    const uint4 a = static_cast<const uint4*>(W)[g];
-    const uint32_t p[4] = {a.x, a.y, a.z, a.w};
+  bool any_bad = false;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  // g0 is the same for every thread of the workgroup, so the 8-lane shuffles see whole blocks
+  for (int64_t g0 = (int64_t)blockIdx.x * kThreads; g0 < n_words; g0 += stride) {
+    const int64_t g = g0 + threadIdx.x;  // one code word = 8 weights
+    const bool active = g < n_words;     // n_words is a multiple of 8, so whole blocks are active
+    float v[8];
+    if (active && BF) {
+      const uint4 a = static_cast<const uint4*>(W)[g];
+      const uint32_t p[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = bf16lo_to_f32(p[i]);
-      v[2 * i + 1] = bf16hi_to_f32(p[i]);
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16lo_to_f32(p[i]);
+        v[2 * i + 1] = bf16hi_to_f32(p[i]);
+      }
+    } else if (active) {
+      const float4 a = static_cast<const float4*>(W)[2 * g];
+      const float4 b = static_cast<const float4*>(W)[2 * g + 1];
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = 0.f;
     }
-  } else if (active) {
-    const float4 a = static_cast<const float4*>(W)[2 * g];
-    const float4 b = static_cast<const float4*>(W)[2 * g + 1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  } else {
+    bool bad = false;
+    float mx = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = 0.f;
-  }
-  bool bad = false;
-  float mx = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    bad |= !__builtin_isfinite(v[i]);
-    mx = fmaxf(mx, fabsf(v[i]));
-  }
-  // absmax over the 8 lanes of one 64-weight block (lanes 8j..8j+7)
-  mx = fmaxf(mx, __shfl_xor(mx, 1));
-  mx = fmaxf(mx, __shfl_xor(mx, 2));
-  mx = fmaxf(mx, __shfl_xor(mx, 4));
-
-  uint32_t c[8];
-  if (mx > 0.f) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = nf4_code(__fdiv_rn(v[i], mx), T);
-  } else {
-    const uint32_t z = nf4_code(0.f, T);  // the level nearest 0, ties low (8 for NF4)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = z;
-  }
-  uint32_t word = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) word |= (c[i] | (c[i + 4] << 4)) << (8 * i);
-
-  if (active) {
-    codes[g] = word;
-    if ((threadIdx.x & 7) == 0 && !bad) {
-      c1_out[g >> 3] = mx;
-      const uint32_t bits = __float_as_uint(mx);
-      const uint32_t e = bits >> 23;  // mx >= 0
-      const uint32_t bin = e ? e : 1u;
-      const unsigned long long m = (unsigned long long)((bits & 0x7FFFFFu) | (e ? 0x800000u : 0u));
-      if (m) atomicAdd(&sh_hist[bin], m);
+    for (int i = 0; i < 8; ++i) {
+      bad |= !__builtin_isfinite(v[i]);
+      mx = fmaxf(mx, fabsf(v[i]));
     }
+    // absmax over the 8 lanes of one 64-weight block (lanes 8j..8j+7)
+    mx = fmaxf(mx, __shfl_xor(mx, 1));
+    mx = fmaxf(mx, __shfl_xor(mx, 2));
+    mx = fmaxf(mx, __shfl_xor(mx, 4));
+
+    uint32_t c[8];
+    if (mx > 0.f) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[i] = nf4_code(__fdiv_rn(v[i], mx), T);
+    } else {
+      const uint32_t z = nf4_code(0.f, T);  // the level nearest 0, ties low (8 for NF4)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[i] = z;
+    }
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) word |= (c[i] | (c[i + 4] << 4)) << (8 * i);
+
+    if (active) {
+      codes[g] = word;
+      if ((threadIdx.x & 7) == 0 && !bad) {
+        c1_out[g >> 3] = mx;
+        const uint32_t bits = __float_as_uint(mx);
+        const uint32_t e = bits >> 23;  // mx >= 0
+        const uint32_t bin = e ? e : 1u;
+        const unsigned long long m = (unsigned long long)((bits & 0x7FFFFFu) | (e ? 0x800000u : 0u));
+        if (m) atomicAdd(&sh_hist[bin], m);
+      }
+    }
+    any_bad |= bad && active;
   }
-  if (__any(bad && active)) {
+  if (__any(any_bad)) {
     if ((threadIdx.x & 63) == 0) atomicOr(flag, 1);
   }
   __syncthreads();
@@ -152,7 +162,8 @@ __global__ __launch_bounds__(kThreads) void k_e4m3_encode(const float* __restric
 
 hipError_t launch_quant_pass1(const void* W, bool w_bf16, uint32_t* codes, float* c1, unsigned long long* hist,
                               int* flag, int64_t n_words, const Nf4Tables& T, hipStream_t s) {
-  const int64_t grid = (n_words + kThreads - 1) / kThreads;
+  // 2048 workgroups of 256 threads fill the chip (8 per CU); larger tensors loop
+  const int64_t grid = std::min<int64_t>((n_words + kThreads - 1) / kThreads, 2048);
   LaunchTimer t(0, s);
   if (w_bf16)
     hipExtLaunchKernelGGL(k_quant_pass1<true>, dim3((unsigned)grid), dim3(kThreads), 0, s, t.start, t.stop, 0, W, codes,
