@@ -191,11 +191,22 @@ __device__ __forceinline__ void load_unscaled_lut(const Nf4Tables& T, Lut& L) {
 }
 
 // NF4 code of one ratio rho = w / c1 (c1 > 0): the number of thresholds below rho.
+// The thresholds ascend, so the count of those below rho is found by a 4-step binary
+// search: at step s the candidate threshold is thr[c + 2^(3-s) - 1] for the bits c found so
+// far, chosen among constants with selects.  Same result as counting all 15 (also for NaN:
+// every comparison is false).
 __device__ __forceinline__ uint32_t nf4_code(float rho, const Nf4Tables& T) {
-  uint32_t c = 0;
-#pragma unroll
-  for (int k = 0; k < 15; ++k) c += (rho > T.thr[k]) ? 1u : 0u;
-  return c;
+  const bool b3 = rho > T.thr[7];
+  const bool b2 = rho > (b3 ? T.thr[11] : T.thr[3]);
+  const float t1a = b2 ? T.thr[13] : T.thr[9], t1b = b2 ? T.thr[5] : T.thr[1];
+  const bool b1 = rho > (b3 ? t1a : t1b);
+  const uint32_t c3 = (b3 ? 8u : 0u) | (b2 ? 4u : 0u) | (b1 ? 2u : 0u);
+  // thr[c3] for c3 in {0, 2, ..., 14}
+  const float u0 = b1 ? T.thr[2] : T.thr[0], u1 = b1 ? T.thr[6] : T.thr[4];
+  const float u2 = b1 ? T.thr[10] : T.thr[8], u3 = b1 ? T.thr[14] : T.thr[12];
+  const float v0 = b2 ? u1 : u0, v1 = b2 ? u3 : u2;
+  const bool b0 = rho > (b3 ? v1 : v0);
+  return c3 | (b0 ? 1u : 0u);
 }
 
 // ---------------------------------------------------------------- buffer loads
