@@ -547,7 +547,19 @@ def main():
         Q.quantize(W, out=q)
     torch.cuda.synchronize()
     q_ms = 1e3 * (time.perf_counter() - t0) / nq
-    quant = {"ms": round(q_ms, 3), "input_GBs": round(4 * N * K / (q_ms * 1e-3) / 1e9, 1)}
+    # the kernels alone (the call also synchronizes once to fold the mean on the host)
+    Q.timing_enable(True, ["quant_pass1", "quant_pass2"])
+    for _ in range(nq):
+        Q.quantize(W, out=q)
+    p1_ms, p1_n = Q.timing_read("quant_pass1")
+    p2_ms, p2_n = Q.timing_read("quant_pass2")
+    Q.timing_enable(False)
+    p1_us = 1e3 * p1_ms / max(p1_n, 1)
+    p1_bytes = N * K * 4 + N * K // 2 + N * K // 16  # FP32 in; codes and FP32 block constants out
+    quant = {"ms": round(q_ms, 3), "input_GBs": round(4 * N * K / (q_ms * 1e-3) / 1e9, 1),
+             "pass1_us": round(p1_us, 2), "pass1_GBs": round(p1_bytes / p1_us / 1e3, 1),
+             "pass1_frac": round(p1_bytes / p1_us / 1e3 / PEAK_HBM_GBS, 4),
+             "pass2_us": round(1e3 * p2_ms / max(p2_n, 1), 2)}
 
     out = {
         "metric": METRIC,
