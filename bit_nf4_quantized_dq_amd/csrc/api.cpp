@@ -66,7 +66,8 @@ inline bool decode_once(int64_t M, int dq) { return M >= kNtMinM || dq != QLORA_
 
 // ---- workspace layouts
 struct FwdWs {
-  size_t tpart, ypart, ls, wcopy, total;
+  size_t tpart, ypart, ls, wcopy, gpart, total;
+  int32_t gsplit;  // reduction split of the decode-once GEMM (FP32 partials at gpart)
 };
 FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r, int dq) {
   FwdWs w{};
@@ -85,6 +86,11 @@ FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r, int dq) {
     if (decode_once(M, dq)) {
       w.wcopy = off;
       off = align_up(off + 2 * (size_t)N * K, 256);
+      w.gsplit = gemm_nt_ksplit(N, M, K);
+      if (w.gsplit > 1) {
+        w.gpart = off;
+        off = align_up(off + sizeof(float) * (size_t)w.gsplit * M * N, 256);
+      }
     }
   }
   w.total = std::max<size_t>(off, 256);
@@ -417,7 +423,8 @@ int qlora_linear_fwd(const qlora_nf4dq_t* Wq, const uint16_t* X, int64_t M, cons
         return QLORA_ERR_HIP;
     }
     // Y = X w_hat^T + (s T) B^T: A = w_hat [N, K], Wl = B [N, r] (f*r + j)
-    e = launch_gemm_nt(wcopy, N, X, M, K, B, r, 1, ls, r, Y, QLORA_K_GEMM_FWD, stream);
+    e = launch_gemm_nt(wcopy, N, X, M, K, B, r, 1, ls, r, Y, QLORA_K_GEMM_FWD, stream,
+                       L.gsplit > 1 ? reinterpret_cast<float*>(base + L.gpart) : nullptr, L.gsplit > 1 ? L.gsplit : 1);
     return hip_status(e);
   }
   if ((e = launch_lora_down(X, A, 0, M, r, K, s, ls, T_save, stream)) != hipSuccess) return QLORA_ERR_HIP;

@@ -23,6 +23,12 @@
 // from 64 banks, and the 16 rows x one chunk of an MFMA operand read then cover all 256
 // bytes exactly once; the ring writes (1 KB contiguous per load) are conflict-free anyway.  Out-of-range rows or
 // reduction columns read as zero (raw buffer loads), so no tail needs a branch in the loop.
+//
+// Split reduction.  A product with few tiles (at most 128, e.g. a 1024-row projection at
+// 2048 tokens: 32 tiles) would leave most CUs idle, so its reduction steps are dealt to
+// ksplit workgroups per tile (blockIdx.z).  Each writes its FP32 partial tile to the
+// workspace; k_sum_parts then adds the ksplit partials in a fixed order and rounds to BF16.
+// The adapter slices run in split 0 only.
 #include "qlora_device.h"
 #include "qlora_host.h"
 
@@ -79,13 +85,15 @@ struct Ring {
   uint32_t base[2];  // byte offset of the lane's chunk at reduction index 0; kOOB past the rows
   uint32_t col[2];   // the lane's first reduction index within a step
   uint32_t Kr;
+  uint32_t kbase;  // first reduction step of this workgroup's range
   int wave;
 
   __device__ __forceinline__ void init(const uint16_t* P, int64_t rows_total, int64_t row0, int64_t Kr_, int w,
-                                       int lane) {
+                                       int lane, uint32_t kb0) {
     const int64_t rows = rows_total - row0 < 256 ? rows_total - row0 : 256;
     r = make_rsrc(P + row0 * Kr_, rows * Kr_ * 2);
     Kr = (uint32_t)Kr_;
+    kbase = kb0;
     wave = w;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -96,7 +104,7 @@ struct Ring {
     }
   }
   __device__ __forceinline__ void issue1(uint4* slot, uint32_t kb, int j) const {
-    const uint32_t k0 = kb * BK;
+    const uint32_t k0 = (kbase + kb) * BK;
     const uint32_t off = (base[j] != kOOB && k0 + col[j] < Kr) ? base[j] + 2 * k0 : kOOB;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(slot + (2 * wave + j) * 64), 16, off, 0, 0, 0);
   }
@@ -242,6 +250,55 @@ __device__ __forceinline__ void store_tile(uint16_t* __restrict__ C, int64_t M, 
   }
 }
 
+// FP32 partial of a split: the wavefront's 128 features x 64 tokens go out in two passes of
+// 32 tokens (16 KB of its staging region: 32 rows of 512 bytes, 16-byte unit u of row m at
+// u ^ (m & 31)), read back 32 lanes per row so that each store writes two 512-byte row
+// segments.  Register 4q + v of tile (i, j) holds feature 32 i + 8 q + 4 h32 + v.
+__device__ __forceinline__ void store_part(float* __restrict__ P, int64_t M, int64_t F, int64_t f0, int64_t m0,
+                                           int wave, int lane, int l32, int h32, const Acc& acc) {
+  uint4* reg = epi_region(wave);
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int u = 8 * i + 2 * q + h32;
+        reg[l32 * 32 + (u ^ l32)] = make_uint4(__float_as_uint(acc[i][j][4 * q + 0]), __float_as_uint(acc[i][j][4 * q + 1]),
+                                               __float_as_uint(acc[i][j][4 * q + 2]), __float_as_uint(acc[i][j][4 * q + 3]));
+      }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // this wavefront's LDS writes are done (it reads only its own region)
+    const int c = lane & 31;
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int m = 2 * it + (lane >> 5);
+      const uint4 v = reg[m * 32 + (c ^ m)];
+      const int64_t gm = m0 + 32 * j + m, gf = f0 + 4 * c;
+      if (gm < M && gf < F) *reinterpret_cast<uint4*>(P + gm * F + gf) = v;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // reads done before the next pass rewrites the region
+  }
+}
+
+// C [M, F] = bf16(sum over s of P[s] [M, F]), the splits added in order s = 0, 1, ...; one
+// thread per 8 consecutive features (F % 16 == 0).
+__global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ P, int32_t ks, int64_t M, int64_t F,
+                                                   uint16_t* __restrict__ C) {
+  const int64_t n8 = M * F / 8;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride) {
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int32_t sp = 0; sp < ks; ++sp) {
+      const float4* src = reinterpret_cast<const float4*>(P + (int64_t)sp * M * F) + 2 * i;
+      const float4 x = src[0], y = src[1];
+      a[0] += x.x; a[1] += x.y; a[2] += x.z; a[3] += x.w;
+      a[4] += y.x; a[5] += y.y; a[6] += y.z; a[7] += y.w;
+    }
+    reinterpret_cast<uint4*>(C)[i] = make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                                                 pack_bf16x2(a[4], a[5]), pack_bf16x2(a[6], a[7]));
+  }
+}
+
 // Consecutive workgroups are dealt round-robin to the 8 XCDs (each with its own L2):
 // renumber so that one XCD gets a contiguous run of tiles.  When the feature tiles divide
 // into columns of 4 that split the grid into 8 equal blocks (4 feature tiles x n/32 token
@@ -306,22 +363,27 @@ __device__ __forceinline__ void nt_step(const Ring& ra, const Ring& rb, uint32_t
   }
 }
 
+template <bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(const uint16_t* __restrict__ A, int64_t F,
                                                          const uint16_t* __restrict__ B, int64_t M, int64_t Kr,
                                                          const uint16_t* __restrict__ wl, int64_t wl_fs,
                                                          int64_t wl_js, const uint16_t* __restrict__ Lm, int32_t r,
-                                                         uint16_t* __restrict__ C) {
+                                                         uint16_t* __restrict__ C, float* __restrict__ part,
+                                                         uint32_t kb_per) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h32 = lane >> 5;
   const int wf = (wave & 1) * 128, wmt = (wave >> 1) * 64;
   int64_t tx, ty;
   tile_xy(tx, ty);
   const int64_t f0 = tx * BF, m0 = ty * BMT;
-  const uint32_t nk = (uint32_t)((Kr + BK - 1) / BK);
+  const uint32_t nk_all = (uint32_t)((Kr + BK - 1) / BK);
+  // this workgroup's reduction steps: [kb0, kb0 + nk)
+  const uint32_t kb0 = SPLIT ? blockIdx.z * kb_per : 0u;
+  const uint32_t nk = SPLIT ? (kb0 + kb_per <= nk_all ? kb_per : (kb0 < nk_all ? nk_all - kb0 : 0u)) : nk_all;
 
   Ring ra, rb;
-  ra.init(A, F, f0, Kr, wave, lane);
-  rb.init(B, M, m0, Kr, wave, lane);
+  ra.init(A, F, f0, Kr, wave, lane, kb0);
+  rb.init(B, M, m0, Kr, wave, lane, kb0);
   // steps 0..2 in flight while the adapter slices run through slot 4
   ra.issue(abuf<0>(), 0);
   rb.issue(bbuf<0>(), 0);
@@ -338,7 +400,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(const uint16_t* __restr
   for (int i = 0; i < TI; ++i)
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = f32x16_t{};
-  adapter(wl, wl_fs, wl_js, F, Lm, M, r, f0, m0, tid, wf, wmt, l32, h32, acc);
+  if (!SPLIT || blockIdx.z == 0) adapter(wl, wl_fs, wl_js, F, Lm, M, r, f0, m0, tid, wf, wmt, l32, h32, acc);
   wait_vm<0>();
   lds_barrier();  // steps 0, 1 landed everywhere; the adapter's reads of slot 4 are done
 
@@ -370,17 +432,42 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(const uint16_t* __restr
   }
   mma(o1, acc);  // ks = 1 of the last step
   lds_barrier();  // every wavefront is done with the ring slots, which now stage the epilogue
-  store_tile(C, M, F, f0 + wf, m0 + wmt, wave, lane, l32, h32, acc);
+  if (SPLIT)
+    store_part(part + (int64_t)blockIdx.z * M * F, M, F, f0 + wf, m0 + wmt, wave, lane, l32, h32, acc);
+  else
+    store_tile(C, M, F, f0 + wf, m0 + wmt, wave, lane, l32, h32, acc);
 }
 
 }  // namespace
 
+int32_t gemm_nt_ksplit(int64_t F, int64_t M, int64_t Kr) {
+  const int64_t tiles = ((F + BF - 1) / BF) * ((M + BMT - 1) / BMT);
+  const int64_t nk = (Kr + BK - 1) / BK;
+  if (tiles > 128) return 1;
+  int64_t ks = 256 / tiles;
+  if (ks > nk / 16) ks = nk / 16;  // at least 16 reduction steps per split
+  return ks >= 2 ? (int32_t)ks : 1;
+}
+
 hipError_t launch_gemm_nt(const uint16_t* A, int64_t F, const uint16_t* B, int64_t M, int64_t Kr,
                           const uint16_t* wl, int64_t wl_fs, int64_t wl_js, const uint16_t* L, int32_t r,
-                          uint16_t* C, int kernel_id, hipStream_t st) {
-  dim3 grid((unsigned)((F + BF - 1) / BF), (unsigned)((M + BMT - 1) / BMT));
+                          uint16_t* C, int kernel_id, hipStream_t st, float* part, int32_t ksplit) {
+  const int64_t nk = (Kr + BK - 1) / BK;
+  if (ksplit > 1 && (!part || F % 16 != 0)) return hipErrorInvalidValue;
+  const uint32_t kb_per = ksplit > 1 ? (uint32_t)((nk + ksplit - 1) / ksplit) : (uint32_t)nk;
+  dim3 grid((unsigned)((F + BF - 1) / BF), (unsigned)((M + BMT - 1) / BMT), (unsigned)(ksplit > 1 ? ksplit : 1));
   LaunchTimer t(kernel_id, st);
-  hipExtLaunchKernelGGL(k_gemm_nt, grid, dim3(kThreads), 0, st, t.start, t.stop, 0, A, F, B, M, Kr, wl, wl_fs, wl_js, L, r, C);
+  if (ksplit > 1)
+    hipExtLaunchKernelGGL(k_gemm_nt<true>, grid, dim3(kThreads), 0, st, t.start, t.stop, 0, A, F, B, M, Kr, wl, wl_fs,
+                          wl_js, L, r, C, part, kb_per);
+  else
+    hipExtLaunchKernelGGL(k_gemm_nt<false>, grid, dim3(kThreads), 0, st, t.start, t.stop, 0, A, F, B, M, Kr, wl, wl_fs,
+                          wl_js, L, r, C, part, kb_per);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ksplit <= 1) return e;
+  const int64_t n8 = M * F / 8;
+  const int64_t blocks = std::min<int64_t>((n8 + 255) / 256, 2048);
+  hipLaunchKernelGGL(k_sum_parts, dim3((unsigned)blocks), dim3(256), 0, st, part, ksplit, M, F, C);
   return hipGetLastError();
 }
 

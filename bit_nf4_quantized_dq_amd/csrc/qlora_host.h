@@ -142,8 +142,11 @@ hipError_t launch_gemm_dx(const uint32_t* codes, const uint8_t* code8, const flo
 
 // ---- BF16 GEMM over a decoded weight copy (gemm_nt.hip):
 // C [M, F] = (A [F, Kr] B [M, Kr]^T)^T + L [M, r] Wl^T, Wl(f, j) at f*wl_fs + j*wl_js.
+// With ksplit > 1 (gemm_nt_ksplit(): products of at most 128 tiles), the reduction is split
+// over ksplit workgroups per tile; part is FP32 [ksplit][M][F] workspace and F % 16 == 0.
+int32_t gemm_nt_ksplit(int64_t F, int64_t M, int64_t Kr);
 hipError_t launch_gemm_nt(const uint16_t* A, int64_t F, const uint16_t* B, int64_t M, int64_t Kr,
                           const uint16_t* wl, int64_t wl_fs, int64_t wl_js, const uint16_t* L, int32_t r,
-                          uint16_t* C, int kernel_id, hipStream_t st);
+                          uint16_t* C, int kernel_id, hipStream_t st, float* part = nullptr, int32_t ksplit = 1);
 
 }  // namespace qlora

@@ -381,6 +381,36 @@ def test_weight_stream_graph_replay(gpu_lib):
             assert torch.equal(ye.view(torch.int16), yg.view(torch.int16)), f"replay {rep}"
 
 
+@pytest.mark.parametrize("N,K,M", [
+    (528, 2112, 1100),   # 3 x 5 tiles, ragged edges; 66 reduction steps over 4 splits (17, 17, 17, 15)
+    (1024, 8192, 2048),  # a k/v projection of the 70B-class model: 32 tiles, 8 splits
+])
+def test_split_reduction_gemm(gpu_lib, N, K, M):
+    """Forward at M >= 1024 through the decoded copy, on a product with few tiles, so the BF16
+    GEMM splits its reduction over several workgroups and sums the FP32 partials in a second
+    launch: every output against the oracle (the second shape on sampled rows)."""
+    from bit_nf4_quantized_dq_amd import linear_fwd, quantize
+
+    r, alpha = 16, 32.0
+    print(f"split gemm {N}x{K} M={M}", flush=True)
+    c = _case(13, N, K, M, r, 0.02, idx=N % 97)
+    rng = np.random.default_rng(N + K + M)
+    n_s = np.arange(N) if N * K <= (4 << 20) else np.sort(rng.choice(N, 48, replace=False))
+    mask = np.zeros((N, K // 64), bool)
+    mask[n_s, :] = True
+    oq = O.quantize(c["W"].numpy(), blocks=mask)
+    what = O.bf16_bits_to_f32(O.dequantize_bf16_bits(oq)[n_s]).astype(np.float64)
+    q = quantize(c["W"].cuda())
+    T = torch.empty(M, r, dtype=torch.bfloat16, device="cuda")
+    Y = linear_fwd(q, c["X"].cuda(), c["A"].cuda(), c["B"].cuda(), alpha, T_save=T)
+    torch.cuda.synchronize()
+    Xf, Af, Bf = _f64(c["X"]), _f64(c["A"]), _f64(c["B"])
+    T_ref = Xf @ Af.T
+    Y_ref = Xf @ what.T + (alpha / r) * T_ref @ Bf[n_s].T
+    assert normwise(_f64(Y)[:, n_s], Y_ref) <= TOL
+    assert normwise(_f64(T), T_ref) <= TOL
+
+
 @pytest.mark.parametrize("idx", [0, 2, 4, 6])
 def test_config5_70b_shapes_sampled(gpu_lib, idx):
     """70B-class layer linears (layer 79 of the seed rule), forward at M = 1 (weight stream)
