@@ -99,7 +99,12 @@ struct ChunkRegs {
   uint4 xv[kXItems];
 };
 
-template <int RT>  // 16-wide tiles of the adapter rank: r <= 16 * RT
+// ONE: the workgroup's range is exactly one full chunk (e.g. 4096x4096).  Then the adapter
+// part runs first, while the codes are still in flight: X, the A pieces and the B rows are
+// issued before the codes, so waiting for them (loads complete in issue order) does not wait
+// for the codes, and T, its cross-wavefront sum and the up-projection overlap the code
+// transfer.  The chunk loop below is the general path.
+template <int RT, bool ONE>  // RT: 16-wide tiles of the adapter rank, r <= 16 * RT
 __global__ __launch_bounds__(kThreads) void k_gemv_fused(GemvArgs a, Nf4Tables T) {
   __shared__ Stage S;
   __shared__ f32x4_t sred[kWaves][RT][64];
@@ -142,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_fused(GemvArgs a, Nf4Tables T
   // B rows of this workgroup for the adapter up-projection, prefetched with the first chunk
   __shared__ uint4 sB[kRows][kRStage / 8];
   uint4 bpre[kRStage / 8];
-  {
+  if (!ONE) {
     const rsrc_t rb = make_rsrc(a.B, N * a.r * 2);
     const bool pre = (a.r % 8) == 0 && a.r <= kRStage;
 #pragma unroll
@@ -188,119 +193,91 @@ __global__ __launch_bounds__(kThreads) void k_gemv_fused(GemvArgs a, Nf4Tables T
     }
   };
 
-  ChunkRegs R;
-  issue(b0, R);
-  if (tid < kRows) {
+  if constexpr (ONE) {
+    static_assert(kChunk == kWaves && kTiles == 1, "one adapter block and one row tile per wavefront");
+    const int nb = (int)(b1 - b0);
+    const int u = wave;
+    // X pieces of the chunk, then this wavefront's A pieces, then the B rows, then the codes
+    uint4 xv[kXItems];
 #pragma unroll
-    for (int q = 0; q < kRStage / 8; ++q) sB[tid][q] = bpre[q];
-  }
-  for (int64_t c0 = b0; c0 < b1; c0 += kChunk) {
-    const int nb = (b1 - c0 < kChunk) ? (int)(b1 - c0) : kChunk;
-    // adapter down-projection inputs of this chunk: wavefront w takes blocks u = w (mod kWaves);
-    // for r <= 32 they are issued here, with the chunk, for larger r when the block comes up
-    constexpr int kTA = RT <= 2 ? (kChunk + kWaves - 1) / kWaves : 1;
-    uint4 av[kTA][RT][2];
-    auto load_a = [&](int u, uint4 (&dst)[RT][2]) {
-#pragma unroll
-      for (int j = 0; j < RT; ++j) {
-        const bool ok = u < nb && 16 * j + l16 < a.r;
-        const uint32_t ao = (uint32_t)((((int64_t)(16 * j + l16)) * K + 64 * (c0 + u) + 16 * g) * 2);
-        dst[j][0] = bload16(ra, ok ? ao : kOOB);
-        dst[j][1] = bload16(ra, ok ? ao + 16 : kOOB);
-      }
-    };
-    if (RT <= 2) {
-#pragma unroll
-      for (int q = 0; q < kTA; ++q) load_a(kWaves * q + wave, av[q]);
+    for (int p = 0; p < kXItems; ++p) {
+      const int i = tid + kThreads * p, xm = i / (8 * kChunk), col = i % (8 * kChunk);
+      const int64_t k = 64 * (b0 + col / 8) + 8 * (col % 8);
+      xv[p] = bload16(rx, b0 + col / 8 < b1 ? (uint32_t)((xm * K + k) * 2) : kOOB);
     }
-    __syncthreads();  // the previous chunk's LDS reads are done
-    stage(R);
+    uint4 av[RT][2];
+#pragma unroll
+    for (int j = 0; j < RT; ++j) {
+      const bool ok = u < nb && 16 * j + l16 < a.r;
+      const uint32_t ao = (uint32_t)((((int64_t)(16 * j + l16)) * K + 64 * (b0 + u) + 16 * g) * 2);
+      av[j][0] = bload16(ra, ok ? ao : kOOB);
+      av[j][1] = bload16(ra, ok ? ao + 16 : kOOB);
+    }
+    {
+      const rsrc_t rb = make_rsrc(a.B, N * a.r * 2);
+      const bool pre = (a.r % 8) == 0 && a.r <= kRStage;
+#pragma unroll
+      for (int q = 0; q < kRStage / 8; ++q)
+        bpre[q] = bload16(rb, (pre && 8 * q < a.r && tid < kRows) ? (uint32_t)(((row0 + tid) * a.r + 8 * q) * 2) : kOOB);
+    }
+    uint4 cv[kStageBlocks][2];
+    uint32_t c8[kStageBlocks], c2[kStageBlocks];
+#pragma unroll
+    for (int v = 0; v < kStageBlocks; ++v) {
+      const int ub = sb0 + v;
+      const bool ok = ub < nb;
+      const uint32_t off = my_code_off + (uint32_t)((b0 + ub) * 32);
+      cv[v][0] = bload16(rc, ok ? off : kOOB);
+      cv[v][1] = bload16(rc, ok ? off + 16 : kOOB);
+      const uint32_t bi = my_blk + (uint32_t)(b0 + ub);
+      c8[v] = bload1(r8, ok ? bi : kOOB);
+      c2[v] = bload4(r2, ok ? (bi >> 8) * 4 : kOOB);
+    }
+    // adapter part while the codes travel
+#pragma unroll
+    for (int p = 0; p < kXItems; ++p) {
+      const int i = tid + kThreads * p;
+      S.x[i / (8 * kChunk)][i % (8 * kChunk)] = xv[p];
+    }
+    if (tid < kRows) {
+#pragma unroll
+      for (int q = 0; q < kRStage / 8; ++q) sB[tid][q] = bpre[q];
+    }
     __syncthreads();
-    if (c0 + kChunk < b1) issue(c0 + kChunk, R);  // next chunk in flight during this one's math
-
-    // ---- adapter down-projection share of this wavefront: blocks u = wave (mod kWaves)
-    if (RT <= 2) {
-#pragma unroll
-      for (int q = 0; q < kTA; ++q) {
-        const int u = kWaves * q + wave;
-        if (u < nb) {
-          const bf16x8_t xa = as_bf16x8(S.x[l16][8 * u + 2 * g]);
-          const bf16x8_t xb = as_bf16x8(S.x[l16][8 * u + 2 * g + 1]);
-#pragma unroll
-          for (int j = 0; j < RT; ++j) {
-            tacc[j] = mfma16x16x32(xa, as_bf16x8(av[q][j][0]), tacc[j]);
-            tacc[j] = mfma16x16x32(xb, as_bf16x8(av[q][j][1]), tacc[j]);
-          }
-        }
-      }
-    } else {
-      for (int u = wave; u < nb; u += kWaves) {
-        load_a(u, av[0]);
-        const bf16x8_t xa = as_bf16x8(S.x[l16][8 * u + 2 * g]);
-        const bf16x8_t xb = as_bf16x8(S.x[l16][8 * u + 2 * g + 1]);
-#pragma unroll
-        for (int j = 0; j < RT; ++j) {
-          tacc[j] = mfma16x16x32(xa, as_bf16x8(av[0][j][0]), tacc[j]);
-          tacc[j] = mfma16x16x32(xb, as_bf16x8(av[0][j][1]), tacc[j]);
-        }
-      }
-    }
-    // ---- MFMA over the staged chunk
-    // blocks past the slice (u >= nb) hold zero activations, so they add exact zeros
-#pragma unroll
-    for (int u = 0; u < kChunk; ++u) {
+    if (u < nb) {
       const bf16x8_t xa = as_bf16x8(S.x[l16][8 * u + 2 * g]);
       const bf16x8_t xb = as_bf16x8(S.x[l16][8 * u + 2 * g + 1]);
 #pragma unroll
-      for (int t = 0; t < kTiles; ++t) {
-        const int row = wave * 16 * kTiles + 16 * t + l16;
-        const uint2 cw = S.codes[row][4 * u + g];
-        uint32_t w0[4], w1[4];
-        decode8(cw.x, L, w0);
-        decode8(cw.y, L, w1);
-        f32x4_t p = mfma16x16x32(xa, as_bf16x8(w0), z);
-        p = mfma16x16x32(xb, as_bf16x8(w1), p);
-        const float c = S.scale[row][u];
-        acc[t][0] = fmaf(c, p[0], acc[t][0]);
-        acc[t][1] = fmaf(c, p[1], acc[t][1]);
-        acc[t][2] = fmaf(c, p[2], acc[t][2]);
-        acc[t][3] = fmaf(c, p[3], acc[t][3]);
+      for (int j = 0; j < RT; ++j) {
+        tacc[j] = mfma16x16x32(xa, as_bf16x8(av[j][0]), tacc[j]);
+        tacc[j] = mfma16x16x32(xb, as_bf16x8(av[j][1]), tacc[j]);
       }
     }
-  }
-
-  // ---- T over this k-range: sum the wavefronts' shares -> sT[m][j]
 #pragma unroll
-  for (int j = 0; j < RT; ++j) sred[wave][j][lane] = tacc[j];
-  __syncthreads();
-  for (int i = tid; i < 16 * 16 * RT; i += kThreads) {
-    const int j16 = i / 256, rem = i % 256, ln = rem / 4, v = rem % 4;  // D[m = 4*(ln>>4)+v][j = ln & 15]
-    float s = sred[0][j16][ln][v];
-    for (int w = 1; w < kWaves; ++w) s += sred[w][j16][ln][v];
-    sT[4 * (ln >> 4) + v][16 * j16 + (ln & 15)] = s;
-  }
-  __syncthreads();
-
-  // ---- adapter up-projection of this partial T: acc[t][m][n] += s * sum_j T[m][j] B[n][j]
-  const bool b_staged = (a.r % 8) == 0 && a.r <= kRStage;
-  const rsrc_t rb = make_rsrc(a.B, N * a.r * 2);
-  for (int32_t j0 = 0; j0 < a.r; j0 += 32) {
-    const int32_t jj = j0 + 8 * g;
-    uint32_t tv[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float lo = (jj + 2 * q < a.r) ? a.s * sT[l16][jj + 2 * q] : 0.f;
-      const float hi = (jj + 2 * q + 1 < a.r) ? a.s * sT[l16][jj + 2 * q + 1] : 0.f;
-      tv[q] = pack_bf16x2(lo, hi);
+    for (int j = 0; j < RT; ++j) sred[wave][j][lane] = tacc[j];
+    __syncthreads();
+    for (int i = tid; i < 16 * 16 * RT; i += kThreads) {
+      const int j16 = i / 256, rem = i % 256, ln = rem / 4, v = rem % 4;  // D[m = 4*(ln>>4)+v][j = ln & 15]
+      float s = sred[0][j16][ln][v];
+      for (int w = 1; w < kWaves; ++w) s += sred[w][j16][ln][v];
+      sT[4 * (ln >> 4) + v][16 * j16 + (ln & 15)] = s;
     }
-    const bf16x8_t ta = as_bf16x8(tv);
+    __syncthreads();
+    for (int32_t j0 = 0; j0 < a.r; j0 += 32) {  // r <= 32 here, so B comes from LDS or element loads
+      const int32_t jj = j0 + 8 * g;
+      uint32_t tv[4];
 #pragma unroll
-    for (int t = 0; t < kTiles; ++t) {
-      const int rl = wave * 16 * kTiles + 16 * t + l16;
+      for (int q = 0; q < 4; ++q) {
+        const float lo = (jj + 2 * q < a.r) ? a.s * sT[l16][jj + 2 * q] : 0.f;
+        const float hi = (jj + 2 * q + 1 < a.r) ? a.s * sT[l16][jj + 2 * q + 1] : 0.f;
+        tv[q] = pack_bf16x2(lo, hi);
+      }
+      const int rl = wave * 16 + l16;
       uint4 bw;
-      if (b_staged) {
+      if ((a.r % 8) == 0) {
         bw = (jj < a.r) ? sB[rl][jj / 8] : make_uint4(0, 0, 0, 0);
       } else {
+        const rsrc_t rb = make_rsrc(a.B, N * a.r * 2);
         const int64_t n = row0 + rl;
         uint32_t e[8];
 #pragma unroll
@@ -309,9 +286,163 @@ __global__ __launch_bounds__(kThreads) void k_gemv_fused(GemvArgs a, Nf4Tables T
         bw = make_uint4((e[0] & 0xFFFFu) | (e[1] << 16), (e[2] & 0xFFFFu) | (e[3] << 16),
                         (e[4] & 0xFFFFu) | (e[5] << 16), (e[6] & 0xFFFFu) | (e[7] << 16));
       }
-      acc[t] = mfma16x16x32(ta, as_bf16x8(bw), acc[t]);
+      acc[0] = mfma16x16x32(as_bf16x8(tv), as_bf16x8(bw), acc[0]);
     }
-  }
+    // the codes: stage, then the chunk's MFMAs on top of the adapter term
+#pragma unroll
+    for (int v = 0; v < kStageBlocks; ++v) {
+      const int ub = sb0 + v;
+      S.codes[srow][4 * ub + 0] = make_uint2(cv[v][0].x, cv[v][0].y);
+      S.codes[srow][4 * ub + 1] = make_uint2(cv[v][0].z, cv[v][0].w);
+      S.codes[srow][4 * ub + 2] = make_uint2(cv[v][1].x, cv[v][1].y);
+      S.codes[srow][4 * ub + 3] = make_uint2(cv[v][1].z, cv[v][1].w);
+      S.scale[srow][ub] = block_scale(c8[v], __uint_as_float(c2[v]), mu);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ub = 0; ub < kChunk; ++ub) {
+      const bf16x8_t xa = as_bf16x8(S.x[l16][8 * ub + 2 * g]);
+      const bf16x8_t xb = as_bf16x8(S.x[l16][8 * ub + 2 * g + 1]);
+      const int row = wave * 16 + l16;
+      const uint2 cw = S.codes[row][4 * ub + g];
+      uint32_t w0[4], w1[4];
+      decode8(cw.x, L, w0);
+      decode8(cw.y, L, w1);
+      f32x4_t p = mfma16x16x32(xa, as_bf16x8(w0), z);
+      p = mfma16x16x32(xb, as_bf16x8(w1), p);
+      const float c = S.scale[row][ub];
+      acc[0][0] = fmaf(c, p[0], acc[0][0]);
+      acc[0][1] = fmaf(c, p[1], acc[0][1]);
+      acc[0][2] = fmaf(c, p[2], acc[0][2]);
+      acc[0][3] = fmaf(c, p[3], acc[0][3]);
+    }
+  } else {
+    ChunkRegs R;
+    issue(b0, R);
+    if (tid < kRows) {
+#pragma unroll
+      for (int q = 0; q < kRStage / 8; ++q) sB[tid][q] = bpre[q];
+    }
+    for (int64_t c0 = b0; c0 < b1; c0 += kChunk) {
+      const int nb = (b1 - c0 < kChunk) ? (int)(b1 - c0) : kChunk;
+      // adapter down-projection inputs of this chunk: wavefront w takes blocks u = w (mod kWaves);
+      // for r <= 32 they are issued here, with the chunk, for larger r when the block comes up
+      constexpr int kTA = RT <= 2 ? (kChunk + kWaves - 1) / kWaves : 1;
+      uint4 av[kTA][RT][2];
+      auto load_a = [&](int u, uint4 (&dst)[RT][2]) {
+#pragma unroll
+        for (int j = 0; j < RT; ++j) {
+          const bool ok = u < nb && 16 * j + l16 < a.r;
+          const uint32_t ao = (uint32_t)((((int64_t)(16 * j + l16)) * K + 64 * (c0 + u) + 16 * g) * 2);
+          dst[j][0] = bload16(ra, ok ? ao : kOOB);
+          dst[j][1] = bload16(ra, ok ? ao + 16 : kOOB);
+        }
+      };
+      if (RT <= 2) {
+#pragma unroll
+        for (int q = 0; q < kTA; ++q) load_a(kWaves * q + wave, av[q]);
+      }
+      __syncthreads();  // the previous chunk's LDS reads are done
+      stage(R);
+      __syncthreads();
+      if (c0 + kChunk < b1) issue(c0 + kChunk, R);  // next chunk in flight during this one's math
+
+      // ---- adapter down-projection share of this wavefront: blocks u = wave (mod kWaves)
+      if (RT <= 2) {
+#pragma unroll
+        for (int q = 0; q < kTA; ++q) {
+          const int u = kWaves * q + wave;
+          if (u < nb) {
+            const bf16x8_t xa = as_bf16x8(S.x[l16][8 * u + 2 * g]);
+            const bf16x8_t xb = as_bf16x8(S.x[l16][8 * u + 2 * g + 1]);
+#pragma unroll
+            for (int j = 0; j < RT; ++j) {
+              tacc[j] = mfma16x16x32(xa, as_bf16x8(av[q][j][0]), tacc[j]);
+              tacc[j] = mfma16x16x32(xb, as_bf16x8(av[q][j][1]), tacc[j]);
+            }
+          }
+        }
+      } else {
+        for (int u = wave; u < nb; u += kWaves) {
+          load_a(u, av[0]);
+          const bf16x8_t xa = as_bf16x8(S.x[l16][8 * u + 2 * g]);
+          const bf16x8_t xb = as_bf16x8(S.x[l16][8 * u + 2 * g + 1]);
+#pragma unroll
+          for (int j = 0; j < RT; ++j) {
+            tacc[j] = mfma16x16x32(xa, as_bf16x8(av[0][j][0]), tacc[j]);
+            tacc[j] = mfma16x16x32(xb, as_bf16x8(av[0][j][1]), tacc[j]);
+          }
+        }
+      }
+      // ---- MFMA over the staged chunk
+      // blocks past the slice (u >= nb) hold zero activations, so they add exact zeros
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) {
+        const bf16x8_t xa = as_bf16x8(S.x[l16][8 * u + 2 * g]);
+        const bf16x8_t xb = as_bf16x8(S.x[l16][8 * u + 2 * g + 1]);
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) {
+          const int row = wave * 16 * kTiles + 16 * t + l16;
+          const uint2 cw = S.codes[row][4 * u + g];
+          uint32_t w0[4], w1[4];
+          decode8(cw.x, L, w0);
+          decode8(cw.y, L, w1);
+          f32x4_t p = mfma16x16x32(xa, as_bf16x8(w0), z);
+          p = mfma16x16x32(xb, as_bf16x8(w1), p);
+          const float c = S.scale[row][u];
+          acc[t][0] = fmaf(c, p[0], acc[t][0]);
+          acc[t][1] = fmaf(c, p[1], acc[t][1]);
+          acc[t][2] = fmaf(c, p[2], acc[t][2]);
+          acc[t][3] = fmaf(c, p[3], acc[t][3]);
+        }
+      }
+    }
+
+    // ---- T over this k-range: sum the wavefronts' shares -> sT[m][j]
+#pragma unroll
+    for (int j = 0; j < RT; ++j) sred[wave][j][lane] = tacc[j];
+    __syncthreads();
+    for (int i = tid; i < 16 * 16 * RT; i += kThreads) {
+      const int j16 = i / 256, rem = i % 256, ln = rem / 4, v = rem % 4;  // D[m = 4*(ln>>4)+v][j = ln & 15]
+      float s = sred[0][j16][ln][v];
+      for (int w = 1; w < kWaves; ++w) s += sred[w][j16][ln][v];
+      sT[4 * (ln >> 4) + v][16 * j16 + (ln & 15)] = s;
+    }
+    __syncthreads();
+
+    // ---- adapter up-projection of this partial T: acc[t][m][n] += s * sum_j T[m][j] B[n][j]
+    const bool b_staged = (a.r % 8) == 0 && a.r <= kRStage;
+    const rsrc_t rb = make_rsrc(a.B, N * a.r * 2);
+    for (int32_t j0 = 0; j0 < a.r; j0 += 32) {
+      const int32_t jj = j0 + 8 * g;
+      uint32_t tv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float lo = (jj + 2 * q < a.r) ? a.s * sT[l16][jj + 2 * q] : 0.f;
+        const float hi = (jj + 2 * q + 1 < a.r) ? a.s * sT[l16][jj + 2 * q + 1] : 0.f;
+        tv[q] = pack_bf16x2(lo, hi);
+      }
+      const bf16x8_t ta = as_bf16x8(tv);
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t) {
+        const int rl = wave * 16 * kTiles + 16 * t + l16;
+        uint4 bw;
+        if (b_staged) {
+          bw = (jj < a.r) ? sB[rl][jj / 8] : make_uint4(0, 0, 0, 0);
+        } else {
+          const int64_t n = row0 + rl;
+          uint32_t e[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            e[q] = __builtin_amdgcn_raw_buffer_load_b16(rb, (jj + q < a.r) ? (int)((n * a.r + jj + q) * 2) : (int)kOOB, 0, 0);
+          bw = make_uint4((e[0] & 0xFFFFu) | (e[1] << 16), (e[2] & 0xFFFFu) | (e[3] << 16),
+                          (e[4] & 0xFFFFu) | (e[5] << 16), (e[6] & 0xFFFFu) | (e[7] << 16));
+        }
+        acc[t] = mfma16x16x32(ta, as_bf16x8(bw), acc[t]);
+      }
+    }
+
+  }  // general path
 
   // ---- output: D[m][n] -- lane holds rows m = 4g + v of column n
   if (a.ksplit == 1) {
@@ -404,10 +535,16 @@ hipError_t launch_gemv_fwd(const uint32_t* codes, const uint8_t* code8, const fl
   a.nbs = (int32_t)((nb_row + a.ksplit - 1) / a.ksplit);
   dim3 grid((unsigned)gemv_groups(N), (unsigned)a.ksplit);
   LaunchTimer t(3, st);
-  if (r <= 16) hipExtLaunchKernelGGL(k_gemv_fused<1>, grid, dim3(kThreads), 0, st, t.start, t.stop, 0, a, T);
-  else if (r <= 32) hipExtLaunchKernelGGL(k_gemv_fused<2>, grid, dim3(kThreads), 0, st, t.start, t.stop, 0, a, T);
-  else if (r <= 64) hipExtLaunchKernelGGL(k_gemv_fused<4>, grid, dim3(kThreads), 0, st, t.start, t.stop, 0, a, T);
-  else hipExtLaunchKernelGGL(k_gemv_fused<8>, grid, dim3(kThreads), 0, st, t.start, t.stop, 0, a, T);
+  // A full single chunk per workgroup: adapter part first, under the code transfer.  With
+  // fewer blocks the codes land almost at once and the reordering only adds latency, so those
+  // keep the chunk loop.
+  const bool one = a.nbs == kChunk;
+  if (r <= 16 && one) hipExtLaunchKernelGGL((k_gemv_fused<1, true>), grid, dim3(kThreads), 0, st, t.start, t.stop, 0, a, T);
+  else if (r <= 16) hipExtLaunchKernelGGL((k_gemv_fused<1, false>), grid, dim3(kThreads), 0, st, t.start, t.stop, 0, a, T);
+  else if (r <= 32 && one) hipExtLaunchKernelGGL((k_gemv_fused<2, true>), grid, dim3(kThreads), 0, st, t.start, t.stop, 0, a, T);
+  else if (r <= 32) hipExtLaunchKernelGGL((k_gemv_fused<2, false>), grid, dim3(kThreads), 0, st, t.start, t.stop, 0, a, T);
+  else if (r <= 64) hipExtLaunchKernelGGL((k_gemv_fused<4, false>), grid, dim3(kThreads), 0, st, t.start, t.stop, 0, a, T);
+  else hipExtLaunchKernelGGL((k_gemv_fused<8, false>), grid, dim3(kThreads), 0, st, t.start, t.stop, 0, a, T);
   return hipGetLastError();
 }
 

@@ -303,6 +303,28 @@ def test_config4_llama3_8b_layer_sampled(gpu_lib, idx):
 
 
 # d_out * d_in >= 32M with d_in a multiple of 256: the large-weight stream kernel
+@pytest.mark.parametrize("M,r", [(1, 8), (7, 24), (16, 32), (3, 16)])
+def test_weight_stream_full_chunk_adapter_first(gpu_lib, M, r):
+    """4096x4096 at M <= 16 splits d_in into 8 ranges of one full chunk, where the adapter part
+    runs before the weight codes are staged: Y and T in full against the oracle."""
+    from bit_nf4_quantized_dq_amd import linear_fwd, quantize
+
+    N = K = 4096
+    alpha = 2.0 * r
+    print(f"full-chunk 4096x4096 M={M} r={r}", flush=True)
+    c = _case(14, N, K, M, r, 0.02, idx=M + r)
+    oq = O.quantize(c["W"].numpy())
+    what = O.bf16_bits_to_f32(O.dequantize_bf16_bits(oq)).astype(np.float64)
+    q = quantize(c["W"].cuda())
+    T = torch.empty(M, r, dtype=torch.bfloat16, device="cuda")
+    Y = linear_fwd(q, c["X"].cuda(), c["A"].cuda(), c["B"].cuda(), alpha, T_save=T)
+    torch.cuda.synchronize()
+    Xf, Af, Bf = _f64(c["X"]), _f64(c["A"]), _f64(c["B"])
+    T_ref = Xf @ Af.T
+    assert normwise(_f64(Y), Xf @ what.T + (alpha / r) * T_ref @ Bf.T) <= TOL
+    assert normwise(_f64(T), T_ref) <= TOL
+
+
 STREAM_CASES = [
     # d_out, d_in, M, r
     (8192, 4096, 1, 16),
