@@ -21,6 +21,9 @@ from ._binding import (  # noqa: F401
     dequantize,
     linear_fwd,
     linear_fwd_multi,
+    mlp_fwd,
+    mlp_bwd,
+    mlp_workspace_size,
     workspace_size_multi,
     linear_bwd,
     e4m3_encode,

@@ -82,6 +82,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         "qlora_workspace_size_multi": (ctypes.c_int, P(P(_Nf4dq)), i64, i32, P(sz)),
         "qlora_linear_fwd_multi": (ctypes.c_int, P(P(_Nf4dq)), vp, i64, P(vp), P(vp), i32, ctypes.c_float, P(vp),
                                    P(vp), vp, sz, vp),
+        "qlora_mlp_workspace_size": (ctypes.c_int, i64, P(_Nf4dq), P(_Nf4dq), P(_Nf4dq), i32, P(sz)),
+        "qlora_mlp_fwd": (P(_Nf4dq), P(_Nf4dq), P(_Nf4dq), vp, i64, P(vp), P(vp), i32, ctypes.c_float, vp, vp, vp,
+                          vp, sz, vp),
+        "qlora_mlp_bwd": (P(_Nf4dq), P(_Nf4dq), P(_Nf4dq), vp, vp, i64, P(vp), P(vp), i32, ctypes.c_float, vp, vp,
+                          vp, P(vp), P(vp), vp, sz, vp),
         "qlora_adamw_step": (vp, vp, vp, vp, vp, i64, i64, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                              ctypes.c_float, ctypes.c_float, vp),
         "qlora_e4m3_encode": (vp, vp, i64, vp),
@@ -331,6 +336,64 @@ def linear_fwd_multi(qs, X: torch.Tensor, As, Bs, alpha: float, Ys=None, T_saves
     _check(load_library().qlora_linear_fwd_multi(n, arr, X.data_ptr(), M, a_ptrs, b_ptrs, r, float(alpha), y_ptrs,
                                                  t_ptrs, ws.data_ptr(), ws.numel(), _stream(X)), "linear_fwd_multi")
     return Ys
+
+
+def mlp_workspace_size(op: int, M: int, qg: QuantizedWeight, qu: QuantizedWeight, qd: QuantizedWeight,
+                       r: int) -> int:
+    n = ctypes.c_size_t()
+    sg, su, sd = qg.struct(), qu.struct(), qd.struct()
+    _check(load_library().qlora_mlp_workspace_size(op, M, ctypes.byref(sg), ctypes.byref(su), ctypes.byref(sd), r,
+                                                   ctypes.byref(n)), "mlp_workspace_size")
+    return n.value
+
+
+def _ptrs(ts):
+    return (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+
+
+def mlp_fwd(qs, X: torch.Tensor, As, Bs, alpha: float, Y: torch.Tensor | None = None,
+            G_save: torch.Tensor | None = None, U_save: torch.Tensor | None = None,
+            ws: torch.Tensor | None = None) -> torch.Tensor:
+    """MLP block Y = down(silu(gate(X)) * up(X)); qs, As, Bs in the order gate, up, down."""
+    qg, qu, qd = qs
+    _dev(X, torch.bfloat16, "X")
+    for i in range(3):
+        _dev(As[i], torch.bfloat16, f"A[{i}]")
+        _dev(Bs[i], torch.bfloat16, f"B[{i}]")
+    M, r = X.shape[0], As[0].shape[0]
+    Y = Y if Y is not None else torch.empty(M, qd.d_out, dtype=torch.bfloat16, device=X.device)
+    _dev(Y, torch.bfloat16, "Y")
+    for t, n in ((G_save, "G_save"), (U_save, "U_save")):
+        if t is not None:
+            _dev(t, torch.bfloat16, n)
+    need = mlp_workspace_size(OP_FWD, M, qg, qu, qd, r)
+    ws = ws if ws is not None else _WS.get(need, X.device, "fwd")
+    sg, su, sd = qg.struct(), qu.struct(), qd.struct()
+    _check(load_library().qlora_mlp_fwd(ctypes.byref(sg), ctypes.byref(su), ctypes.byref(sd), X.data_ptr(), M,
+                                        _ptrs(As), _ptrs(Bs), r, float(alpha), Y.data_ptr(), _ptr(G_save),
+                                        _ptr(U_save), ws.data_ptr(), ws.numel(), _stream(X)), "mlp_fwd")
+    return Y
+
+
+def mlp_bwd(qs, X: torch.Tensor, dY: torch.Tensor, As, Bs, alpha: float, G_saved: torch.Tensor | None = None,
+            U_saved: torch.Tensor | None = None, dX: torch.Tensor | None = None, ws: torch.Tensor | None = None):
+    """Backward of mlp_fwd: returns (dX, [dA_gate, dA_up, dA_down], [dB_gate, dB_up, dB_down])."""
+    qg, qu, qd = qs
+    for t, n in ((X, "X"), (dY, "dY")):
+        _dev(t, torch.bfloat16, n)
+    M, r = X.shape[0], As[0].shape[0]
+    dev = X.device
+    dX = dX if dX is not None else torch.empty(M, qg.d_in, dtype=torch.bfloat16, device=dev)
+    dAs = [torch.empty(r, q.d_in, dtype=torch.bfloat16, device=dev) for q in qs]
+    dBs = [torch.empty(q.d_out, r, dtype=torch.bfloat16, device=dev) for q in qs]
+    need = mlp_workspace_size(OP_BWD, M, qg, qu, qd, r)
+    ws = ws if ws is not None else _WS.get(need, dev, "bwd")
+    sg, su, sd = qg.struct(), qu.struct(), qd.struct()
+    _check(load_library().qlora_mlp_bwd(ctypes.byref(sg), ctypes.byref(su), ctypes.byref(sd), X.data_ptr(),
+                                        dY.data_ptr(), M, _ptrs(As), _ptrs(Bs), r, float(alpha), _ptr(G_saved),
+                                        _ptr(U_saved), dX.data_ptr(), _ptrs(dAs), _ptrs(dBs), ws.data_ptr(),
+                                        ws.numel(), _stream(X)), "mlp_bwd")
+    return dX, dAs, dBs
 
 
 def linear_bwd(q: QuantizedWeight, X: torch.Tensor, dY: torch.Tensor, A: torch.Tensor, B: torch.Tensor,

@@ -159,6 +159,52 @@ int check_group(int count, const qlora_nf4dq_t* const* Wq) {
   return QLORA_OK;
 }
 
+// MLP block (qlora_mlp_fwd / qlora_mlp_bwd): the BF16 activations of the block, then one
+// region large enough for any of the block's linear calls.
+struct MlpWs {
+  size_t g, u, h, dh, dg, du, dxu, lin, lin_bytes, total;
+};
+int check_mlp(const qlora_nf4dq_t* Wg, const qlora_nf4dq_t* Wu, const qlora_nf4dq_t* Wd) {
+  int st;
+  if ((st = check_wq(Wg)) || (st = check_wq(Wu)) || (st = check_wq(Wd))) return st;
+  if (Wg->d_in != Wu->d_in || Wg->d_out != Wu->d_out || Wd->d_out != Wg->d_in || Wd->d_in != Wg->d_out)
+    return QLORA_ERR_BAD_SHAPE;
+  return QLORA_OK;
+}
+MlpWs mlp_ws(bool bwd, int64_t M, const qlora_nf4dq_t* Wg, const qlora_nf4dq_t* Wu, const qlora_nf4dq_t* Wd,
+             int32_t r) {
+  MlpWs w{};
+  const int64_t d = Wg->d_in, f = Wg->d_out;
+  const size_t act = align_up(2 * (size_t)M * f, 256);
+  size_t off = 0;
+  w.g = off;
+  off += act;
+  w.u = off;
+  off += act;
+  w.h = off;
+  off += act;
+  if (bwd) {
+    w.dh = off;
+    off += act;
+    w.dg = off;
+    off += act;
+    w.du = off;
+    off += act;
+    w.dxu = off;
+    off += align_up(2 * (size_t)M * d, 256);
+  }
+  const qlora_nf4dq_t* gu[2] = {Wg, Wu};
+  size_t lin = std::max(group_ws(2, gu, M, r).total, fwd_ws(M, d, f, r, Wd->dq_format).total);
+  if (bwd) {
+    lin = std::max({lin, bwd_ws(M, f, d, r, Wg->dq_format).total, bwd_ws(M, f, d, r, Wu->dq_format).total,
+                    bwd_ws(M, d, f, r, Wd->dq_format).total});
+  }
+  w.lin = off;
+  w.lin_bytes = lin;
+  w.total = off + align_up(lin, 256);
+  return w;
+}
+
 size_t quant_ws(int64_t d_out, int64_t d_in) {
   const int64_t nb = d_out * d_in / 64;
   return align_up(sizeof(float) * nb, 256) + 256 * sizeof(unsigned long long) + 256;
@@ -469,6 +515,76 @@ int qlora_linear_fwd_multi(int count, const qlora_nf4dq_t* const* Wq, const uint
   return hip_status(launch_gemv_stream_group(count, lins, Wq[0]->d_in, X, M, r, alpha / (float)r,
                                              reinterpret_cast<float*>(base + L.ypart),
                                              reinterpret_cast<float*>(base + L.tpart), tables_of(Wq[0]), stream));
+}
+
+int qlora_mlp_workspace_size(int op, int64_t M, const qlora_nf4dq_t* Wg, const qlora_nf4dq_t* Wu,
+                             const qlora_nf4dq_t* Wd, int32_t r, size_t* ws_bytes) {
+  if (!ws_bytes || (op != QLORA_OP_FWD && op != QLORA_OP_BWD)) return QLORA_ERR_INVALID_ARG;
+  int st = check_mlp(Wg, Wu, Wd);
+  if (st || (st = check_lora(M, r, 1.0f))) return st;
+  *ws_bytes = mlp_ws(op == QLORA_OP_BWD, M, Wg, Wu, Wd, r).total;
+  return QLORA_OK;
+}
+
+int qlora_mlp_fwd(const qlora_nf4dq_t* Wg, const qlora_nf4dq_t* Wu, const qlora_nf4dq_t* Wd, const uint16_t* X,
+                  int64_t M, const uint16_t* const* A, const uint16_t* const* B, int32_t r, float alpha, uint16_t* Y,
+                  uint16_t* G_save, uint16_t* U_save, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_mlp(Wg, Wu, Wd);
+  if (st || (st = check_lora(M, r, alpha))) return st;
+  if (!X || !A || !B || !Y) return QLORA_ERR_INVALID_ARG;
+  if ((G_save && !aligned16(G_save)) || (U_save && !aligned16(U_save))) return QLORA_ERR_INVALID_ARG;
+  const MlpWs L = mlp_ws(false, M, Wg, Wu, Wd, r);
+  if (!ws || ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  uint16_t* G = G_save ? G_save : reinterpret_cast<uint16_t*>(base + L.g);
+  uint16_t* U = U_save ? U_save : reinterpret_cast<uint16_t*>(base + L.u);
+  uint16_t* H = reinterpret_cast<uint16_t*>(base + L.h);
+  void* lin = base + L.lin;
+  const qlora_nf4dq_t* gu[2] = {Wg, Wu};
+  uint16_t* GU[2] = {G, U};
+  // gate and up read the same X: one grouped call (one weight-streaming launch at M <= 16)
+  if ((st = qlora_linear_fwd_multi(2, gu, X, M, A, B, r, alpha, GU, nullptr, lin, L.lin_bytes, stream))) return st;
+  if (launch_swiglu_fwd(G, U, H, M * Wg->d_out, stream) != hipSuccess) return QLORA_ERR_HIP;
+  return qlora_linear_fwd(Wd, H, M, A[2], B[2], r, alpha, Y, nullptr, lin, L.lin_bytes, stream);
+}
+
+int qlora_mlp_bwd(const qlora_nf4dq_t* Wg, const qlora_nf4dq_t* Wu, const qlora_nf4dq_t* Wd, const uint16_t* X,
+                  const uint16_t* dY, int64_t M, const uint16_t* const* A, const uint16_t* const* B, int32_t r,
+                  float alpha, const uint16_t* G_saved, const uint16_t* U_saved, uint16_t* dX, uint16_t* const* dA,
+                  uint16_t* const* dB, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_mlp(Wg, Wu, Wd);
+  if (st || (st = check_lora(M, r, alpha))) return st;
+  if (!X || !dY || !A || !B || !dX || !dA || !dB || !aligned16(dX)) return QLORA_ERR_INVALID_ARG;
+  if ((G_saved == nullptr) != (U_saved == nullptr)) return QLORA_ERR_INVALID_ARG;
+  if (G_saved && (!aligned16(G_saved) || !aligned16(U_saved))) return QLORA_ERR_INVALID_ARG;
+  const MlpWs L = mlp_ws(true, M, Wg, Wu, Wd, r);
+  if (!ws || ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  const int64_t f = Wg->d_out, d = Wg->d_in;
+  void* lin = base + L.lin;
+  const uint16_t* G = G_saved;
+  const uint16_t* U = U_saved;
+  if (!G) {  // recompute the block's inner activations (gradient checkpointing)
+    uint16_t* GU[2] = {reinterpret_cast<uint16_t*>(base + L.g), reinterpret_cast<uint16_t*>(base + L.u)};
+    const qlora_nf4dq_t* gu[2] = {Wg, Wu};
+    if ((st = qlora_linear_fwd_multi(2, gu, X, M, A, B, r, alpha, GU, nullptr, lin, L.lin_bytes, stream))) return st;
+    G = GU[0];
+    U = GU[1];
+  }
+  uint16_t* H = reinterpret_cast<uint16_t*>(base + L.h);
+  uint16_t* dH = reinterpret_cast<uint16_t*>(base + L.dh);
+  uint16_t* dG = reinterpret_cast<uint16_t*>(base + L.dg);
+  uint16_t* dU = reinterpret_cast<uint16_t*>(base + L.du);
+  uint16_t* dXu = reinterpret_cast<uint16_t*>(base + L.dxu);
+  if (launch_swiglu_fwd(G, U, H, M * f, stream) != hipSuccess) return QLORA_ERR_HIP;
+  if ((st = qlora_linear_bwd(Wd, H, dY, M, A[2], B[2], r, alpha, nullptr, dH, dA[2], dB[2], lin, L.lin_bytes, stream)))
+    return st;
+  if (launch_swiglu_bwd(dH, G, U, dG, dU, M * f, stream) != hipSuccess) return QLORA_ERR_HIP;
+  if ((st = qlora_linear_bwd(Wg, X, dG, M, A[0], B[0], r, alpha, nullptr, dX, dA[0], dB[0], lin, L.lin_bytes, stream)))
+    return st;
+  if ((st = qlora_linear_bwd(Wu, X, dU, M, A[1], B[1], r, alpha, nullptr, dXu, dA[1], dB[1], lin, L.lin_bytes, stream)))
+    return st;
+  return hip_status(launch_add_bf16(dX, dXu, dX, M * d, stream));
 }
 
 int qlora_linear_bwd(const qlora_nf4dq_t* Wq, const uint16_t* X, const uint16_t* dY, int64_t M, const uint16_t* A,

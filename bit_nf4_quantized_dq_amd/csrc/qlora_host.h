@@ -149,4 +149,10 @@ hipError_t launch_gemm_nt(const uint16_t* A, int64_t F, const uint16_t* B, int64
                           const uint16_t* wl, int64_t wl_fs, int64_t wl_js, const uint16_t* L, int32_t r,
                           uint16_t* C, int kernel_id, hipStream_t st, float* part = nullptr, int32_t ksplit = 1);
 
+// ---- element-wise steps of the MLP block (mlp.hip); n values, n % 8 == 0, 16-byte aligned
+hipError_t launch_swiglu_fwd(const uint16_t* G, const uint16_t* U, uint16_t* H, int64_t n, hipStream_t st);
+hipError_t launch_swiglu_bwd(const uint16_t* dH, const uint16_t* G, const uint16_t* U, uint16_t* dG, uint16_t* dU,
+                             int64_t n, hipStream_t st);
+hipError_t launch_add_bf16(const uint16_t* a, const uint16_t* b, uint16_t* c, int64_t n, hipStream_t st);
+
 }  // namespace qlora

@@ -209,6 +209,36 @@ int qlora_linear_fwd_multi(int count, const qlora_nf4dq_t *const *Wq, const uint
                            uint16_t *const *Y, uint16_t *const *T_save, void *ws, size_t ws_bytes,
                            hipStream_t stream);
 
+/* The MLP block of a decoder layer with all three projections stored NF4 + DQ and adapted
+ * ("QLoRA -- Fine-Tuning a 65B Model on One GPU", "Seeing it in code": adapters on every
+ * linear, gate_proj / up_proj / down_proj among them; gradient checkpointing on, as "QLoRA
+ * fine-tuning on consumer GPUs", "In production", also asks).  The pages name the three
+ * projections but not the activation between them; the one those names denote is used:
+ *   G = gate(X), U = up(X)          (qlora_linear_fwd each; one grouped call)
+ *   H = bf16(silu(G) * U),  silu(g) = g / (1 + e^-g)   (FP32 from the BF16 G, U)
+ *   Y = down(H)
+ *   Wg, Wu: [f, d]; Wd: [d, f]; X [M, d], Y [M, d]: device BF16.
+ *   A, B: host arrays of 3 device pointers in the order gate, up, down (A[i] [r, d_in_i],
+ *         B[i] [d_out_i, r]); r and alpha shared.
+ *   G_save, U_save: device BF16 [M, f] that receive G and U for the backward, or NULL.
+ *   ws: device workspace of qlora_mlp_workspace_size(QLORA_OP_FWD or QLORA_OP_BWD) bytes.
+ * The backward takes dY [M, d] and returns dX [M, d] (the sum of the input gradients through
+ * gate and up, added in FP32 and rounded once more), and dA[i], dB[i] (host arrays of 3
+ * device pointers, gate, up, down), as qlora_linear_bwd does per projection.  With
+ * G_saved = U_saved = NULL it recomputes G and U from X (checkpointing); H is always
+ * recomputed.  Errors: as qlora_linear_fwd / bwd; BAD_SHAPE when the shapes do not chain. */
+int qlora_mlp_workspace_size(int op, int64_t M, const qlora_nf4dq_t *Wg, const qlora_nf4dq_t *Wu,
+                             const qlora_nf4dq_t *Wd, int32_t r, size_t *ws_bytes);
+int qlora_mlp_fwd(const qlora_nf4dq_t *Wg, const qlora_nf4dq_t *Wu, const qlora_nf4dq_t *Wd,
+                  const uint16_t *X, int64_t M, const uint16_t *const *A, const uint16_t *const *B,
+                  int32_t r, float alpha, uint16_t *Y, uint16_t *G_save, uint16_t *U_save, void *ws,
+                  size_t ws_bytes, hipStream_t stream);
+int qlora_mlp_bwd(const qlora_nf4dq_t *Wg, const qlora_nf4dq_t *Wu, const qlora_nf4dq_t *Wd,
+                  const uint16_t *X, const uint16_t *dY, int64_t M, const uint16_t *const *A,
+                  const uint16_t *const *B, int32_t r, float alpha, const uint16_t *G_saved,
+                  const uint16_t *U_saved, uint16_t *dX, uint16_t *const *dA, uint16_t *const *dB,
+                  void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Backward of qlora_linear_fwd.  With G = dY B:
  *   dX = dY w_hat + (alpha/r) G A      [M, d_in]   (may be NULL: not computed)
  *   dA = (alpha/r) G^T X               [r, d_in]

@@ -46,4 +46,7 @@ from .qlora_oracle import (  # noqa: F401
     e5m2_value,
     e5m2_encode,
     int8_encode,
+    silu,
+    mlp_fwd,
+    mlp_bwd,
 )

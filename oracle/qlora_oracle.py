@@ -546,3 +546,48 @@ def adamw_step(master: np.ndarray, m: np.ndarray, v: np.ndarray, grad_bits: np.n
     th = th - lr * mhat / (np.sqrt(vhat) + eps)
     th32 = th.astype(np.float32)
     return th32, m1.astype(np.float32), v1.astype(np.float32), bf16_round_bits(th32), th
+
+
+# --------------------------------------------------------------------------------------
+# MLP block of a decoder layer: gate, up and down projections, all quantized and adapted
+# --------------------------------------------------------------------------------------
+
+
+def silu(g: np.ndarray) -> np.ndarray:
+    """silu(g) = g * sigmoid(g) = g / (1 + e^-g), float64.
+
+    Reading: [65B] "Seeing it in code" puts adapters on gate_proj, up_proj and down_proj, but
+    no page states the activation between them; the gated one those names denote is taken,
+    H = silu(gate(X)) * up(X), Y = down(H)."""
+    g = np.asarray(g, dtype=np.float64)
+    return g / (1.0 + np.exp(-g))
+
+
+def mlp_fwd(Wg_hat, Wu_hat, Wd_hat, X, As, Bs, alpha: float, r: int):
+    """Forward of the MLP block, each projection a frozen quantized linear with its adapter
+    (:func:`lora_fwd`): G = gate(X), U = up(X), H = silu(G) * U, Y = down(H).
+    Wg_hat, Wu_hat [f, d]; Wd_hat [d, f]; X [M, d]; As, Bs in the order gate, up, down.
+    Every step exact in float64.  Returns (Y, G, U, H)."""
+    G, _ = lora_fwd(Wg_hat, X, As[0], Bs[0], alpha, r)
+    U, _ = lora_fwd(Wu_hat, X, As[1], Bs[1], alpha, r)
+    H = silu(G) * U
+    Y, _ = lora_fwd(Wd_hat, H, As[2], Bs[2], alpha, r)
+    return Y, G, U, H
+
+
+def mlp_bwd(Wg_hat, Wu_hat, Wd_hat, X, dY, As, Bs, alpha: float, r: int):
+    """Backward of :func:`mlp_fwd` by the chain rule, the inner activations recomputed from X
+    (the gradient checkpointing of [65B] "Seeing it in code"):
+      dH = input gradient of down;  with s = sigmoid(G),
+      dG = dH * U * s * (1 + G (1 - s)),   dU = dH * G * s;
+      dX = (input gradient of gate for dG) + (input gradient of up for dU);
+    each projection's adapter gradients as :func:`lora_bwd` gives them.
+    Returns (dX, [dA_gate, dA_up, dA_down], [dB_gate, dB_up, dB_down])."""
+    _, G, U, H = mlp_fwd(Wg_hat, Wu_hat, Wd_hat, X, As, Bs, alpha, r)
+    dH, dA_d, dB_d = lora_bwd(Wd_hat, H, dY, As[2], Bs[2], alpha, r)
+    s = 1.0 / (1.0 + np.exp(-G))
+    dG = dH * U * s * (1.0 + G * (1.0 - s))
+    dU = dH * G * s
+    dX_g, dA_g, dB_g = lora_bwd(Wg_hat, X, dG, As[0], Bs[0], alpha, r)
+    dX_u, dA_u, dB_u = lora_bwd(Wu_hat, X, dU, As[1], Bs[1], alpha, r)
+    return dX_g + dX_u, [dA_g, dA_u, dA_d], [dB_g, dB_u, dB_d]

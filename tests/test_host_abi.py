@@ -24,7 +24,7 @@ def L():
 def test_every_declared_symbol_is_exported(L):
     text = open(HEADER).read()
     names = sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text)))
-    assert len(names) == 19
+    assert len(names) == 22
     for n in names:
         assert hasattr(L, n), n
 
@@ -138,6 +138,34 @@ def test_grouped_forward_errors_before_launch(L):
     assert L.qlora_linear_fwd_multi(2, ok, dummy, 4, ptrs, ptrs, 8, 16.0, holes, None, ws, 1 << 20, None) == -1
     assert L.qlora_linear_fwd_multi(2, ok, dummy, 4, ptrs, ptrs, 0, 16.0, ptrs, None, ws, 1 << 20, None) == -1
     assert L.qlora_linear_fwd_multi(2, ok, dummy, 4, ptrs, ptrs, 8, 16.0, ptrs, None, ws, 16, None) == -5
+
+
+def test_mlp_block_errors_before_launch(L):
+    """qlora_mlp_* reject shapes that do not chain and missing buffers on the host."""
+    dummy = ctypes.c_void_p(4096)
+    ws = ctypes.c_void_p(8192)
+    VP = ctypes.c_void_p * 3
+    ptrs = VP(dummy, dummy, dummy)
+    g, u, d = _wq(d_out=512, d_in=256), _wq(d_out=512, d_in=256), _wq(d_out=256, d_in=512)
+    n = ctypes.c_size_t()
+    assert L.qlora_mlp_workspace_size(1, 64, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), 8, ctypes.byref(n)) == 0
+    fwd_need = n.value
+    assert L.qlora_mlp_workspace_size(2, 64, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), 8, ctypes.byref(n)) == 0
+    assert n.value > fwd_need >= 3 * 2 * 64 * 512
+    assert L.qlora_mlp_workspace_size(3, 64, ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), 8, ctypes.byref(n)) == -1
+    bad_d = _wq(d_out=256, d_in=256)  # down must take d_in = f = 512
+    assert L.qlora_mlp_workspace_size(1, 64, ctypes.byref(g), ctypes.byref(u), ctypes.byref(bad_d), 8, ctypes.byref(n)) == -2
+    assert L.qlora_mlp_fwd(ctypes.byref(g), ctypes.byref(u), ctypes.byref(bad_d), dummy, 64, ptrs, ptrs, 8, 16.0, dummy,
+                           None, None, ws, 1 << 30, None) == -2
+    assert L.qlora_mlp_fwd(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), None, 64, ptrs, ptrs, 8, 16.0, dummy,
+                           None, None, ws, 1 << 30, None) == -1
+    assert L.qlora_mlp_fwd(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), dummy, 64, ptrs, ptrs, 8, 16.0, dummy,
+                           None, None, ws, 16, None) == -5
+    # G and U saved together or not at all
+    assert L.qlora_mlp_bwd(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), dummy, dummy, 64, ptrs, ptrs, 8, 16.0,
+                           dummy, None, dummy, ptrs, ptrs, ws, 1 << 30, None) == -1
+    assert L.qlora_mlp_bwd(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), dummy, dummy, 64, ptrs, ptrs, 8, 16.0,
+                           None, None, dummy, ptrs, ptrs, ws, 16, None) == -5
 
 
 def test_grouped_workspace_covers_every_single_call():

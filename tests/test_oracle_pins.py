@@ -604,3 +604,98 @@ def test_variant_zero_block_and_exact_special_case():
         assert np.array_equal(t[q["codes"]], t[k])
         exp = torch.from_numpy(W).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
         assert np.array_equal(O.dequantize_bf16_bits(q), exp)
+
+
+# ---------------------------------------------------------------- MLP block
+
+
+def test_silu_closed_forms():
+    """silu(0) = 0, slope 1/2 at 0, silu(x) - silu(-x) = x, silu -> x for large x and -> 0 for
+    very negative x, and the value at 1 is 1 / (1 + 1/e)."""
+    x = np.linspace(-30.0, 30.0, 241)
+    assert O.silu(0.0) == 0.0
+    assert np.allclose(O.silu(x) - O.silu(-x), x, rtol=0, atol=1e-12)
+    h = 1e-6
+    assert (O.silu(h) - O.silu(-h)) / (2 * h) == pytest.approx(0.5, rel=1e-9)
+    assert O.silu(40.0) == pytest.approx(40.0, rel=1e-15)
+    assert abs(O.silu(-40.0)) < 1e-15
+    assert O.silu(1.0) == pytest.approx(1.0 / (1.0 + math.exp(-1.0)), rel=1e-15)
+    assert np.allclose(O.silu(x), torch.nn.functional.silu(torch.tensor(x)).numpy(), rtol=1e-14, atol=1e-14)
+
+
+def _mlp_case(M=3, d=8, f=16, r=2, seed=21):
+    rng = np.random.default_rng(seed)
+    Wg = rng.standard_normal((f, d)) * 0.3
+    Wu = rng.standard_normal((f, d)) * 0.3
+    Wd = rng.standard_normal((d, f)) * 0.3
+    X = rng.standard_normal((M, d))
+    As = [rng.standard_normal((r, d)) * 0.3, rng.standard_normal((r, d)) * 0.3, rng.standard_normal((r, f)) * 0.3]
+    Bs = [rng.standard_normal((f, r)) * 0.2, rng.standard_normal((f, r)) * 0.2, rng.standard_normal((d, r)) * 0.2]
+    dY = rng.standard_normal((M, d))
+    return Wg, Wu, Wd, X, As, Bs, dY
+
+
+def test_mlp_bwd_matches_finite_differences():
+    """Every gradient of the MLP block against central differences of the scalar loss
+    sum(dY * Y): a dropped term, a wrong sign or a swapped operand in the chain fails."""
+    Wg, Wu, Wd, X, As, Bs, dY = _mlp_case()
+    alpha, r = 6.0, 2
+
+    def loss(X_, As_, Bs_):
+        return float(np.sum(O.mlp_fwd(Wg, Wu, Wd, X_, As_, Bs_, alpha, r)[0] * dY))
+
+    dX, dAs, dBs = O.mlp_bwd(Wg, Wu, Wd, X, dY, As, Bs, alpha, r)
+    eps = 1e-6
+    targets = [("X", None, X, dX)] + [("A", i, As[i], dAs[i]) for i in range(3)] + [("B", i, Bs[i], dBs[i]) for i in range(3)]
+    for kind, i, arr, grad in targets:
+        for idx in [(0, 0), (arr.shape[0] - 1, arr.shape[1] - 1), (arr.shape[0] // 2, 1)]:
+            def perturbed(delta):
+                a = arr.copy()
+                a[idx] += delta
+                Xp = a if kind == "X" else X
+                Ap = [a if (kind == "A" and j == i) else As[j] for j in range(3)]
+                Bp = [a if (kind == "B" and j == i) else Bs[j] for j in range(3)]
+                return loss(Xp, Ap, Bp)
+            fd = (perturbed(eps) - perturbed(-eps)) / (2 * eps)
+            assert fd == pytest.approx(grad[idx], rel=1e-5, abs=1e-8), (kind, i, idx)
+
+
+def test_mlp_matches_torch_autograd():
+    """The same block written with torch's own silu and autograd gives the same outputs and
+    gradients."""
+    Wg, Wu, Wd, X, As, Bs, dY = _mlp_case(M=4, d=16, f=24, r=3, seed=5)
+    alpha, r = 9.0, 3
+    Y, G, U, H = O.mlp_fwd(Wg, Wu, Wd, X, As, Bs, alpha, r)
+    dX, dAs, dBs = O.mlp_bwd(Wg, Wu, Wd, X, dY, As, Bs, alpha, r)
+    F = torch.nn.functional
+    tX = torch.tensor(X, requires_grad=True)
+    tA = [torch.tensor(a, requires_grad=True) for a in As]
+    tB = [torch.tensor(b, requires_grad=True) for b in Bs]
+    s = alpha / r
+
+    def lin(W, x, A, B):
+        return F.linear(x, torch.tensor(W)) + s * F.linear(F.linear(x, A), B)
+
+    tY = lin(Wd, F.silu(lin(Wg, tX, tA[0], tB[0])) * lin(Wu, tX, tA[1], tB[1]), tA[2], tB[2])
+    tY.backward(torch.tensor(dY))
+    assert np.allclose(Y, tY.detach().numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(dX, tX.grad.numpy(), rtol=1e-11, atol=1e-12)
+    for i in range(3):
+        assert np.allclose(dAs[i], tA[i].grad.numpy(), rtol=1e-11, atol=1e-12)
+        assert np.allclose(dBs[i], tB[i].grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_mlp_special_cases():
+    """With the up projection zero (weights and B), U = 0, so H = 0 and Y = 0, and no gradient
+    reaches the gate's adapter; with the gate projection zero, G = 0 and H = silu(0) U = 0."""
+    Wg, Wu, Wd, X, As, Bs, dY = _mlp_case(seed=3)
+    alpha, r = 4.0, 2
+    Bz = [Bs[0], np.zeros_like(Bs[1]), Bs[2]]
+    Y, G, U, H = O.mlp_fwd(Wg, np.zeros_like(Wu), Wd, X, As, Bz, alpha, r)
+    assert np.all(U == 0) and np.all(H == 0) and np.all(Y == 0)
+    dX, dAs, dBs = O.mlp_bwd(Wg, np.zeros_like(Wu), Wd, X, dY, As, Bz, alpha, r)
+    assert np.all(dAs[0] == 0) and np.all(dBs[0] == 0)
+    Bg = [np.zeros_like(Bs[0]), Bs[1], Bs[2]]
+    _, G0, _, H0 = O.mlp_fwd(np.zeros_like(Wg), Wu, Wd, X, As, Bg, alpha, r)
+    assert np.all(G0 == 0) and np.all(H0 == 0)
+
