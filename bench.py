@@ -18,8 +18,10 @@ AdamW step over the 41.9M adapter parameters of a Llama-3-8B-shaped model, an er
 the format variants (codebook x second-level format: bits/weight, reconstruction error,
 decode time), the other two named workloads (all seven linears of a Llama-3-8B-shaped layer
 at M = 8192, fwd + bwd; a 70B-class model's 560 linears, ~35 GB of NF4+DQ resident, forward at
-M = 1 by graph replay and at M = 2048), and the CPU oracle timed on a bounded sample of the
-same workload.
+M = 1 by graph replay, one launch per linear and with q/k/v and gate/up grouped, and at
+M = 2048), the Llama-3-8B-shaped MLP block chained through its activation (fwd + bwd, with
+saved or recomputed activations), and the CPU oracle timed on a bounded sample of the same
+workload.
 
   python bench.py [--gpus 1] [--steps 100] [--warmup 100] [--no-cpu-baseline] [--no-extra]
 
@@ -141,6 +143,58 @@ def llama3_8b_layer(dev, steps=5, warmup=3):
             "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": round(ms, 3),
             "step_tflop": round(flops / 1e12, 4), "steps": steps,
             "roofline_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
+def llama3_8b_mlp(dev, steps=5, warmup=3):
+    """Llama-3-8B-shaped MLP block (gate and up 14336x4096, down 4096x14336, NF4+DQ, LoRA
+    r = 16 on each) at M = 8192 tokens: one forward, then the backward through the block,
+    with the forward's G and U kept (saved) or recomputed from X (checkpointing).  The rate
+    counts the three linears' forward and backward FLOPs; the recompute's two extra
+    projections are reported separately."""
+    import torch
+
+    import bit_nf4_quantized_dq_amd as Q
+    from bit_nf4_quantized_dq_amd import inputs as I
+
+    M, r, alpha, d, f = 8192, 16, 32.0, 4096, 14336
+    shapes = [(f, d), (f, d), (d, f)]
+    qs, As, Bs = [], [], []
+    for i, (N, K) in enumerate(shapes):
+        W = I.weight(6, 40 + i, N, K, 0.02, device=dev)
+        qs.append(Q.quantize(W))
+        del W
+        As.append(I.lora_A(6, 40 + i, r, K, device=dev))
+        Bs.append(I.lora_B(6, 40 + i, N, r, device=dev))
+    X = I.activations(6, 49, M, d, device=dev)
+    dY = I.grad_out(6, 49, M, d, device=dev)
+    Y = torch.empty(M, d, dtype=torch.bfloat16, device=dev)
+    dX = torch.empty(M, d, dtype=torch.bfloat16, device=dev)
+    G = torch.empty(M, f, dtype=torch.bfloat16, device=dev)
+    U = torch.empty(M, f, dtype=torch.bfloat16, device=dev)
+    ws_f = torch.empty(Q.mlp_workspace_size(Q.OP_FWD, M, *qs, r), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(Q.mlp_workspace_size(Q.OP_BWD, M, *qs, r), dtype=torch.uint8, device=dev)
+    flops = sum(step_flops(M, N, K, r) for N, K in shapes)
+    out = {"metric": "NF4+DQ MLP block fwd+bwd TFLOP/s (gate/up 14336x4096, down 4096x14336, M=8192, r=16)",
+           "unit": "TFLOP/s", "step_tflop": round(flops / 1e12, 4), "steps": steps}
+    for key, saved in (("saved", True), ("recompute", False)):
+        def step():
+            Q.mlp_fwd(qs, X, As, Bs, alpha, Y=Y, G_save=G if saved else None, U_save=U if saved else None, ws=ws_f)
+            Q.mlp_bwd(qs, X, dY, As, Bs, alpha, G_saved=G if saved else None, U_saved=U if saved else None, dX=dX,
+                      ws=ws_b)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        ms = 1e3 * (time.perf_counter() - t0) / steps
+        out[key] = {"value": round(flops / (ms * 1e-3) / 1e12, 2), "ms_per_step": round(ms, 3),
+                    "roofline_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del qs, As, Bs, X, dY, Y, dX, G, U, ws_f, ws_b
+    torch.cuda.empty_cache()
+    return out
 
 
 def seventy_b_model(dev, layers=80, passes=3):
@@ -588,6 +642,7 @@ def main():
         del q, W
         torch.cuda.empty_cache()
         out["llama3_8b_layer_M8192"] = llama3_8b_layer(dev)
+        out["llama3_8b_mlp_block_M8192"] = llama3_8b_mlp(dev)
         torch.cuda.empty_cache()
         out["model_70b_class"] = seventy_b_model(dev)
     if not args.no_cpu_baseline:
