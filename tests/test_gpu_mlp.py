@@ -95,3 +95,40 @@ def test_mlp_recompute_equals_saved(gpu_lib):
     assert torch.equal(a[0], b[0])
     for i in range(3):
         assert torch.equal(a[1][i], b[1][i]) and torch.equal(a[2][i], b[2][i])
+
+
+def test_mlp_block_decode_groups_gate_and_up(gpu_lib):
+    """At decode size (M <= 16) with gate + up holding 32M weights or more, the forward runs
+    gate and up as one grouped weight-streaming launch: the block's output, G and U against
+    the oracle, and the backward at the same size, within the block tolerance."""
+    from bit_nf4_quantized_dq_amd import mlp_bwd, mlp_fwd, quantize, timing_enable, timing_read
+
+    d, f, M, r = 2048, 8192, 2, 16
+    alpha = 32.0
+    print(f"mlp decode d={d} f={f} M={M}", flush=True)
+    Ws, As, Bs, X, dY = _block(17, d, f, M, r)
+    qs = [quantize(W.cuda()) for W in Ws]
+    What = [O.bf16_bits_to_f32(O.dequantize_bf16_bits(O.quantize(W.numpy()))).astype(np.float64) for W in Ws]
+    Ad, Bd = [a.cuda() for a in As], [b.cuda() for b in Bs]
+    G = torch.empty(M, f, dtype=torch.bfloat16, device="cuda")
+    U = torch.empty(M, f, dtype=torch.bfloat16, device="cuda")
+    timing_enable(True, ["gemv_fwd"])
+    try:
+        timing_read("gemv_fwd")
+        Y = mlp_fwd(qs, X.cuda(), Ad, Bd, alpha, G_save=G, U_save=U)
+        torch.cuda.synchronize()
+        _, launches = timing_read("gemv_fwd")
+    finally:
+        timing_enable(False)
+    assert launches == 2, "gate + up grouped, then down"
+    dX, dAs, dBs = mlp_bwd(qs, X.cuda(), dY.cuda(), Ad, Bd, alpha, G_saved=G, U_saved=U)
+    torch.cuda.synchronize()
+    Af, Bf, Xf, dYf = [_f64(a) for a in As], [_f64(b) for b in Bs], _f64(X), _f64(dY)
+    Y_ref, G_ref, U_ref, _ = O.mlp_fwd(What[0], What[1], What[2], Xf, Af, Bf, alpha, r)
+    dX_ref, dA_ref, dB_ref = O.mlp_bwd(What[0], What[1], What[2], Xf, dYf, Af, Bf, alpha, r)
+    assert normwise(_f64(G), G_ref) <= TOL and normwise(_f64(U), U_ref) <= TOL
+    assert normwise(_f64(Y), Y_ref) <= TOL_BLOCK
+    assert normwise(_f64(dX), dX_ref) <= TOL_BLOCK
+    for i in range(3):
+        assert normwise(_f64(dAs[i]), dA_ref[i]) <= TOL_BLOCK, f"dA[{i}]"
+        assert normwise(_f64(dBs[i]), dB_ref[i]) <= TOL_BLOCK, f"dB[{i}]"
