@@ -509,8 +509,14 @@ def main():
         "value": round(sb / (us_call * 1e-6) / 1e9, 1), "unit": "GB/s", "us_per_call": round(us_call, 2),
         "us_per_call_eager_python": round(us_eager, 2),
         "bytes_per_call": sb,
-        "gemv_kernel": {"avg_us": round(gemv_us, 2), "achieved_GBs": round(sb / (gemv_us * 1e-6) / 1e9, 1),
-                        "peak_GBs": PEAK_HBM_GBS, "frac": round(sb / (gemv_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
+        # the kernel's roofline from the graph replay (back-to-back calls; the launch gaps,
+        # under 0.3 us in a kernel trace, are included, so this bounds the kernel time from
+        # above).  Per-launch events add about 2 us to every launch they bracket, so their
+        # figure is kept only for reference.
+        "gemv_kernel": {"avg_us": round(us_call, 2), "achieved_GBs": round(sb / (us_call * 1e-6) / 1e9, 1),
+                        "peak_GBs": PEAK_HBM_GBS, "frac": round(sb / (us_call * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                        "method": "graph replay, launch gaps included",
+                        "avg_us_per_launch_events": round(gemv_us, 2)},
     }
     del graph
 
