@@ -1,7 +1,7 @@
 // Element-wise steps of the MLP block whose three projections (gate, up, down) are all
 // NF4 + LoRA linears ("QLoRA -- Fine-Tuning a 65B Model on One GPU", "Seeing it in code":
 // adapters on every linear, gate_proj, up_proj and down_proj among them; gradient
-// checkpointing on, as "QLoRA fine-tuning on consumer GPUs", "In production", also asks).
+// checkpointing on, as "QLoRA: Quantize Base Weights to 4-Bit", "In production", also asks).
 // The pages name the projections but not the activation between them; the one the names
 // denote is the SiLU-gated product
 //   H = silu(G) * U,  silu(g) = g * sigmoid(g),  G = gate(X), U = up(X),  Y = down(H)

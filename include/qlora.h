@@ -211,8 +211,8 @@ int qlora_linear_fwd_multi(int count, const qlora_nf4dq_t *const *Wq, const uint
 
 /* The MLP block of a decoder layer with all three projections stored NF4 + DQ and adapted
  * ("QLoRA -- Fine-Tuning a 65B Model on One GPU", "Seeing it in code": adapters on every
- * linear, gate_proj / up_proj / down_proj among them; gradient checkpointing on, as "QLoRA
- * fine-tuning on consumer GPUs", "In production", also asks).  The pages name the three
+ * linear, gate_proj / up_proj / down_proj among them; gradient checkpointing on, as "QLoRA:
+ * Quantize Base Weights to 4-Bit", "In production", also asks).  The pages name the three
  * projections but not the activation between them; the one those names denote is used:
  *   G = gate(X), U = up(X)          (qlora_linear_fwd each; one grouped call)
  *   H = bf16(silu(G) * U),  silu(g) = g / (1 + e^-g)   (FP32 from the BF16 G, U)

@@ -12,7 +12,8 @@ Sources (cited by page title and section):
            update", "Quantization in one paragraph", "NF4: sixteen levels shaped like the
            weights", "Double quantization: the constants are not free", "Where the
            gradients actually go".
-  [Consumer] "QLoRA fine-tuning on consumer GPUs" -- FAQ on double quantization.
+  [Consumer] "What is 4-bit NormalFloat (NF4) quantization and why is it
+           information-theoretically optimal?" -- FAQ on double quantization.
 """
 
 from __future__ import annotations
