@@ -168,6 +168,10 @@ FB_CASES = [
     (9, 272, 320, 1100, 16, 32.0),  # ragged M and N; the dX reduction (over N) ends mid-step
     (9, 528, 192, 1025, 40, 80.0),  # two adapter slices, r not a multiple of 8
     (9, 64, 2048, 1024, 128, 256.0),  # four adapter slices, one feature tile
+    # rank 1 (the smallest adapter) on each path
+    (9, 272, 320, 4, 1, 2.0),
+    (9, 272, 320, 300, 1, 2.0),
+    (9, 272, 320, 1100, 1, 2.0),
 ]
 
 
