@@ -116,6 +116,7 @@ def test_grouped_stream_is_deterministic_and_replays(gpu_lib):
     ([1008, 512], 1024, 4, 8),        # d_out not a multiple of 256: single calls
     ([4096, 1024, 1024], 4096, 64, 16),  # M > 16: single calls of the fused GEMM
     ([2048, 2048], 4096, 1, 16),      # 16M weights in all: below the streaming threshold
+    ([8192], 4096, 1, 16),            # a group of one: the single call
 ])
 def test_grouped_fallback_equals_single_calls(gpu_lib, dims, K, M, r):
     from bit_nf4_quantized_dq_amd import linear_fwd, linear_fwd_multi, quantize
