@@ -214,7 +214,7 @@ int qlora_linear_fwd_multi(int count, const qlora_nf4dq_t *const *Wq, const uint
  * linear, gate_proj / up_proj / down_proj among them; gradient checkpointing on, as "QLoRA:
  * Quantize Base Weights to 4-Bit", "In production", also asks).  The pages name the three
  * projections but not the activation between them; the one those names denote is used:
- *   G = gate(X), U = up(X)          (qlora_linear_fwd each; one grouped call)
+ *   G = gate(X), U = up(X)          (one qlora_linear_fwd_multi call: a single launch at M <= 16)
  *   H = bf16(silu(G) * U),  silu(g) = g / (1 + e^-g)   (FP32 from the BF16 G, U)
  *   Y = down(H)
  *   Wg, Wu: [f, d]; Wd: [d, f]; X [M, d], Y [M, d]: device BF16.
