@@ -19,6 +19,7 @@ Sources (cited by page title and section):
 from __future__ import annotations
 
 import math
+from fractions import Fraction
 
 import mpmath
 import numpy as np
@@ -97,18 +98,30 @@ def nf4_codebook() -> np.ndarray:
 
 def nearest_level(rho: np.ndarray, table: np.ndarray) -> np.ndarray:
     """Index of the NF4 level nearest to each rho ([65B] "Quantization in one paragraph":
-    store the index of the level nearest to x/c).  Brute force over all 16 levels, FP64
-    distances; ties go to the lower index (reading: the pages do not say)."""
+    store the index of the level nearest to x/c).  Brute force over all 16 levels; ties go
+    to the lower index (reading: the pages do not say).
+
+    Distances are taken in FP64.  Rounding is monotonic, so an FP64 distance can make two
+    distinct distances equal but never reverse their order; every FP64 tie is therefore
+    settled again with exact rational distances (rho and the levels are binary fractions).
+    A false tie happens when a tiny rho sits next to a midpoint at 0 (the INT4 table)."""
     rho = np.asarray(rho, dtype=np.float32).astype(np.float64)
     t = table.astype(np.float64)
     out = np.empty(rho.shape, dtype=np.uint8)
     flat_in = rho.reshape(-1)
     flat_out = out.reshape(-1)
     chunk = 1 << 20
+    exact_t = [Fraction(float(v)) for v in t]
     for s in range(0, flat_in.size, chunk):
         r = flat_in[s : s + chunk]
         dist = np.abs(r[:, None] - t[None, :])
-        flat_out[s : s + chunk] = np.argmin(dist, axis=1)  # first minimum = lowest index
+        best = np.argmin(dist, axis=1)  # first minimum = lowest index
+        tied = np.nonzero(np.sum(dist == dist[np.arange(r.size), best][:, None], axis=1) > 1)[0]
+        for i in tied:
+            x = Fraction(float(r[i]))
+            d = [abs(x - v) for v in exact_t]
+            best[i] = d.index(min(d))
+        flat_out[s : s + chunk] = best
     return out
 
 

@@ -99,6 +99,31 @@ def test_nearest_level_tie_goes_low():
             assert O.nearest_level(np.array([m], np.float32), O.nf4_codebook())[0] == k
 
 
+@pytest.mark.parametrize("name", ["nf4", "int4", "fp4"])
+def test_nearest_level_matches_midpoint_count_at_every_boundary(name):
+    """Every codebook, at every midpoint's FP32 neighbours (two each side) and at the tiny
+    values next to 0, inside [-1, 1]: the nearest level is the count of exact midpoints strictly below rho.
+    The INT4 table has its midpoint at 0, where FP64 distances to the two levels tie for a
+    subnormal rho; the sign of rho alone decides it (0 itself is a true tie, so it goes low)."""
+    q = O.codebook(name).astype(np.float64)
+    mids = 0.5 * (q[:-1] + q[1:])
+    pts = [np.float32(0.0), np.float32(-0.0)]
+    for m in np.concatenate([mids, [0.0]]):
+        lo = hi = np.float32(m)
+        pts.append(lo)
+        for _ in range(2):
+            lo, hi = np.nextafter(lo, np.float32(-2)), np.nextafter(hi, np.float32(2))
+            pts += [lo, hi]
+    rho = np.array(pts, dtype=np.float32)
+    rho = rho[np.abs(rho) <= 1]  # |w / absmax| never exceeds 1
+    ours = O.nearest_level(rho, O.codebook(name))
+    theirs = np.searchsorted(mids, rho.astype(np.float64), side="left")
+    assert np.array_equal(ours, theirs.astype(np.uint8))
+    if name == "int4":
+        tiny = np.array([1e-45, -1e-45, 0.0], np.float32)
+        assert O.nearest_level(tiny, O.codebook(name)).tolist() == [8, 7, 7]
+
+
 # ------------------------------------------------------------------ packing
 
 def test_pack_roundtrip_and_layout():
