@@ -121,8 +121,8 @@ def llama3_8b_layer(dev, steps=5, warmup=3):
         flops += step_flops(M, N, K, r)
         wsf = max(wsf, Q.workspace_size(Q.OP_FWD, M, N, K, r))
         wsb = max(wsb, Q.workspace_size(Q.OP_BWD, M, N, K, r))
-    ws_f = torch.empty(wsf, dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    ws_f = Q.new_workspace(wsf, dev)
+    ws_b = Q.new_workspace(wsb, dev)
 
     def step():
         for t in lin:
@@ -171,8 +171,8 @@ def llama3_8b_mlp(dev, steps=5, warmup=3):
     dX = torch.empty(M, d, dtype=torch.bfloat16, device=dev)
     G = torch.empty(M, f, dtype=torch.bfloat16, device=dev)
     U = torch.empty(M, f, dtype=torch.bfloat16, device=dev)
-    ws_f = torch.empty(Q.mlp_workspace_size(Q.OP_FWD, M, *qs, r), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(Q.mlp_workspace_size(Q.OP_BWD, M, *qs, r), dtype=torch.uint8, device=dev)
+    ws_f = Q.new_workspace(Q.mlp_workspace_size(Q.OP_FWD, M, *qs, r), dev)
+    ws_b = Q.new_workspace(Q.mlp_workspace_size(Q.OP_BWD, M, *qs, r), dev)
     flops = sum(step_flops(M, N, K, r) for N, K in shapes)
     out = {"metric": "NF4+DQ MLP block fwd+bwd TFLOP/s (gate/up 14336x4096, down 4096x14336, M=8192, r=16)",
            "unit": "TFLOP/s", "step_tflop": round(flops / 1e12, 4), "steps": steps}
@@ -231,7 +231,7 @@ def seventy_b_model(dev, layers=80, passes=3):
         for grp_ in groups:
             if len(grp_) > 1:
                 need = max(need, Q.workspace_size_multi([lin[i][0] for i in grp_], M, r))
-        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        ws = Q.new_workspace(need, dev)
 
         def fwd_pass():
             for i, (q, A, B) in enumerate(lin):
@@ -372,8 +372,8 @@ def main():
     dX = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
     dA = torch.empty(r, K, dtype=torch.bfloat16, device=dev)
     dB = torch.empty(N, r, dtype=torch.bfloat16, device=dev)
-    ws_f = torch.empty(Q.workspace_size(Q.OP_FWD, M, N, K, r), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(Q.workspace_size(Q.OP_BWD, M, N, K, r), dtype=torch.uint8, device=dev)
+    ws_f = Q.new_workspace(Q.workspace_size(Q.OP_FWD, M, N, K, r), dev)
+    ws_b = Q.new_workspace(Q.workspace_size(Q.OP_BWD, M, N, K, r), dev)
 
     def step():
         Q.linear_fwd(q, X, A, B, alpha, Y=Y, T_save=T, ws=ws_f)
@@ -466,7 +466,7 @@ def main():
     del Ws
     X1 = c["X"][:1].to(dev).contiguous()
     Y1 = torch.empty(1, N, dtype=torch.bfloat16, device=dev)
-    ws1 = torch.empty(Q.workspace_size(Q.OP_FWD, 1, N, K, r), dtype=torch.uint8, device=dev)
+    ws1 = Q.new_workspace(Q.workspace_size(Q.OP_FWD, 1, N, K, r), dev)
     for cp in copies[:8]:
         Q.linear_fwd(cp, X1, A, B, alpha, Y=Y1, ws=ws1)
     torch.cuda.synchronize()

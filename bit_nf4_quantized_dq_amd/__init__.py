@@ -29,6 +29,8 @@ from ._binding import (  # noqa: F401
     e4m3_encode,
     quant_sizes,
     workspace_size,
+    new_workspace,
+    workspace_init,
     timing_enable,
     timing_read,
     KERNEL_IDS,

@@ -6,6 +6,7 @@ from __future__ import annotations
 
 import ctypes
 import dataclasses
+import functools
 import os
 
 import torch
@@ -70,6 +71,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         "qlora_quant_sizes": (i64, i64, P(sz), P(sz), P(sz)),
         "qlora_workspace_size": (ctypes.c_int, i64, i64, i64, i32, P(sz)),
         "qlora_workspace_size_fmt": (ctypes.c_int, i64, i64, i64, i32, ctypes.c_int, P(sz)),
+        "qlora_workspace_init": (vp, sz, vp),
         "qlora_format_sizes": (i64, i64, ctypes.c_int, P(sz), P(sz), P(sz)),
         "qlora_nf4_codebook": (P(ctypes.c_float),),
         "qlora_codebook": (ctypes.c_int, P(ctypes.c_float)),
@@ -132,11 +134,63 @@ def _ptr(t: torch.Tensor | None) -> int | None:
     return None if t is None else t.data_ptr()
 
 
-def _dev(t: torch.Tensor, dtype, name: str) -> None:
-    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
-        raise ValueError(f"{name}: need a contiguous {dtype} CUDA tensor, got {t.dtype} on {t.device}")
+def _dev(t: torch.Tensor, dtype, name: str, shape=None, device=None) -> None:
+    """Check one tensor before its pointer crosses the C ABI (see _validate)."""
+    _validate([(t, dtype, name, shape)], device)
 
 
+def _validate(specs, device=None) -> None:
+    """Check tensors before their pointers cross the C ABI, which cannot see sizes: each spec
+    (tensor, dtype, name, shape or None) must be a contiguous tensor of that dtype and shape;
+    then each must be a CUDA tensor on `device` (when given).  All shapes and dtypes are
+    checked before any placement, so a wrong size is reported as such wherever it lives."""
+    for t, dtype, name, shape in specs:
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name}: need a torch tensor, got {type(t).__name__}")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name}: need shape {tuple(shape)}, got {tuple(t.shape)}")
+        if t.dtype != dtype or not t.is_contiguous():
+            raise ValueError(f"{name}: need a contiguous {dtype} tensor, got {t.dtype}")
+    for t, dtype, name, shape in specs:
+        if not t.is_cuda:
+            raise ValueError(f"{name}: need a CUDA tensor, got one on {t.device}")
+        if device is not None and t.device != device:
+            raise ValueError(f"{name}: on {t.device}, the other operands are on {device}")
+
+
+def _weight_specs(q: "QuantizedWeight", prefix: str = "weight"):
+    """Specs of the quantized weight's buffers: the sizes its shape and format need."""
+    nc, n8, n2 = quant_sizes(q.d_out, q.d_in, q.dq)
+    specs = [(q.codes, torch.uint8, f"{prefix}.codes", (nc,)), (q.code8, torch.uint8, f"{prefix}.code8", (n8,))]
+    if q.dq != "none":
+        specs += [(q.c2s, torch.float32, f"{prefix}.c2s", (n2 // 4,)), (q.mu, torch.float32, f"{prefix}.mu", (1,))]
+    return specs
+
+
+def _check_weight(q: "QuantizedWeight", device=None) -> None:
+    _validate(_weight_specs(q), device)
+
+
+def _check_ws(ws: torch.Tensor, device) -> None:
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or not ws.is_contiguous() or ws.dtype != torch.uint8:
+        raise ValueError("ws: need a contiguous uint8 CUDA tensor")
+    if ws.device != device:
+        raise ValueError(f"ws: on {ws.device}, the operands are on {device}")
+
+
+def _rank(A: torch.Tensor, name: str = "A") -> int:
+    if not isinstance(A, torch.Tensor) or A.dim() != 2:
+        raise ValueError(f"{name}: need a 2-D [r, d_in] tensor")
+    return A.shape[0]
+
+
+def _tokens(X: torch.Tensor, name: str = "X") -> int:
+    if not isinstance(X, torch.Tensor) or X.dim() != 2:
+        raise ValueError(f"{name}: need a 2-D [M, d] tensor")
+    return X.shape[0]
+
+
+@functools.lru_cache(maxsize=1024)
 def quant_sizes(d_out: int, d_in: int, dq: str = "e4m3") -> tuple[int, int, int]:
     a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
     _check(load_library().qlora_format_sizes(d_out, d_in, DQ_FORMATS[dq], ctypes.byref(a), ctypes.byref(b),
@@ -144,6 +198,7 @@ def quant_sizes(d_out: int, d_in: int, dq: str = "e4m3") -> tuple[int, int, int]
     return a.value, b.value, c.value
 
 
+@functools.lru_cache(maxsize=4096)
 def workspace_size(op: int, M: int, d_out: int, d_in: int, r: int, dq: str = "e4m3") -> int:
     n = ctypes.c_size_t()
     _check(load_library().qlora_workspace_size_fmt(op, M, d_out, d_in, r, DQ_FORMATS[dq], ctypes.byref(n)),
@@ -203,17 +258,33 @@ class QuantizedWeight:
         return self.codes.numel() + self.code8.numel() + extra
 
 
+def new_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A workspace of `nbytes` bytes ready for its first use: zero-filled, so its counter
+    head (the first QLORA_WS_COUNTER_BYTES bytes) starts at zero, as every call leaves it."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def workspace_init(ws: torch.Tensor) -> torch.Tensor:
+    """Zero the counter head of a workspace that was not allocated zero-filled."""
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or not ws.is_contiguous() or ws.dtype != torch.uint8:
+        raise ValueError("ws: need a contiguous uint8 CUDA tensor")
+    _check(load_library().qlora_workspace_init(ws.data_ptr(), ws.numel(), _stream(ws)), "workspace_init")
+    return ws
+
+
 class _Workspace:
-    """Per-device scratch buffers grown on demand (allocated through torch)."""
+    """Scratch buffers grown on demand, one per (device, stream, kind): calls on different
+    streams never share one, so they may overlap (calls that share a workspace must not)."""
 
     def __init__(self):
         self._bufs: dict = {}
 
     def get(self, nbytes: int, device: torch.device, key: str = "ws") -> torch.Tensor:
-        k = (device.index if device.index is not None else torch.cuda.current_device(), key)
+        idx = device.index if device.index is not None else torch.cuda.current_device()
+        k = (idx, torch.cuda.current_stream(idx).cuda_stream, key)
         buf = self._bufs.get(k)
         if buf is None or buf.numel() < nbytes:
-            buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+            buf = new_workspace(nbytes, torch.device("cuda", idx))
             self._bufs[k] = buf
         return buf
 
@@ -225,41 +296,44 @@ def quantize(W: torch.Tensor, out: QuantizedWeight | None = None, ws: torch.Tens
              codebook: str = "nf4", dq: str = "e4m3") -> QuantizedWeight:
     """Quantize an FP32 [d_out, d_in] CUDA tensor (synchronizes the current stream once).
     The format comes from `out` when given, else from `codebook` and `dq`."""
-    _dev(W, torch.float32, "W")
+    return _quantize(W, torch.float32, "qlora_quantize", out, ws, codebook, dq)
+
+
+def _quantize(W, dtype, fn, out, ws, codebook, dq):
+    if not isinstance(W, torch.Tensor) or W.dim() != 2:
+        raise ValueError("W: need a 2-D [d_out, d_in] tensor")
     d_out, d_in = W.shape
+    if out is not None and (out.d_out, out.d_in) != (d_out, d_in):
+        raise ValueError(f"out: a {out.d_out}x{out.d_in} weight cannot hold a {d_out}x{d_in} tensor")
+    _dev(W, dtype, "W")
     q = out if out is not None else QuantizedWeight.empty(d_out, d_in, W.device, codebook, dq)
+    _check_weight(q, W.device)
     need = workspace_size(OP_QUANTIZE, 1, d_out, d_in, 1)
     ws = ws if ws is not None else _WS.get(need, W.device, "quant")
+    _check_ws(ws, W.device)
     mu = ctypes.c_float()
     s = q.struct()
-    _check(load_library().qlora_quantize(W.data_ptr(), ctypes.byref(s), ctypes.byref(mu), ws.data_ptr(), ws.numel(),
-                                         _stream(W)), "quantize")
+    _check(getattr(load_library(), fn)(W.data_ptr(), ctypes.byref(s), ctypes.byref(mu), ws.data_ptr(), ws.numel(),
+                                       _stream(W)), fn[len("qlora_"):])
     return q
 
 
 def quantize_bf16(W: torch.Tensor, out: QuantizedWeight | None = None, ws: torch.Tensor | None = None,
                   codebook: str = "nf4", dq: str = "e4m3") -> QuantizedWeight:
     """Quantize a BF16 [d_out, d_in] CUDA tensor (its exact FP32 values; synchronizes once)."""
-    _dev(W, torch.bfloat16, "W")
-    d_out, d_in = W.shape
-    q = out if out is not None else QuantizedWeight.empty(d_out, d_in, W.device, codebook, dq)
-    need = workspace_size(OP_QUANTIZE, 1, d_out, d_in, 1)
-    ws = ws if ws is not None else _WS.get(need, W.device, "quant")
-    mu = ctypes.c_float()
-    s = q.struct()
-    _check(load_library().qlora_quantize_bf16(W.data_ptr(), ctypes.byref(s), ctypes.byref(mu), ws.data_ptr(),
-                                              ws.numel(), _stream(W)), "quantize_bf16")
-    return q
+    return _quantize(W, torch.bfloat16, "qlora_quantize_bf16", out, ws, codebook, dq)
 
 
 def merge(q: QuantizedWeight, A: torch.Tensor, B: torch.Tensor, alpha: float,
           out: torch.Tensor | None = None) -> torch.Tensor:
     """Merged BF16 [d_out, d_in] weight bf16(w_hat + (alpha/r) B A) for export."""
-    for t, n in ((A, "A"), (B, "B")):
-        _dev(t, torch.bfloat16, n)
-    r = A.shape[0]
-    out = out if out is not None else torch.empty(q.d_out, q.d_in, dtype=torch.bfloat16, device=A.device)
-    _dev(out, torch.bfloat16, "out")
+    r = _rank(A)
+    dev = A.device
+    specs = _weight_specs(q) + [(A, torch.bfloat16, "A", (r, q.d_in)), (B, torch.bfloat16, "B", (q.d_out, r))]
+    if out is not None:
+        specs.append((out, torch.bfloat16, "out", (q.d_out, q.d_in)))
+    _validate(specs, dev)
+    out = out if out is not None else torch.empty(q.d_out, q.d_in, dtype=torch.bfloat16, device=dev)
     s = q.struct()
     _check(load_library().qlora_merge(ctypes.byref(s), A.data_ptr(), B.data_ptr(), r, float(alpha), out.data_ptr(),
                                       _stream(out)), "merge")
@@ -268,8 +342,12 @@ def merge(q: QuantizedWeight, A: torch.Tensor, B: torch.Tensor, alpha: float,
 
 def dequantize(q: QuantizedWeight, out: torch.Tensor | None = None) -> torch.Tensor:
     """BF16 [d_out, d_in] w_hat, bit-exact."""
-    out = out if out is not None else torch.empty(q.d_out, q.d_in, dtype=torch.bfloat16, device=q.codes.device)
-    _dev(out, torch.bfloat16, "out")
+    dev = q.codes.device
+    specs = _weight_specs(q)
+    if out is not None:
+        specs.append((out, torch.bfloat16, "out", (q.d_out, q.d_in)))
+    _validate(specs, dev)
+    out = out if out is not None else torch.empty(q.d_out, q.d_in, dtype=torch.bfloat16, device=dev)
     s = q.struct()
     _check(load_library().qlora_dequantize(ctypes.byref(s), out.data_ptr(), _stream(out)), "dequantize")
     return out
@@ -279,15 +357,18 @@ def linear_fwd(q: QuantizedWeight, X: torch.Tensor, A: torch.Tensor, B: torch.Te
                Y: torch.Tensor | None = None, T_save: torch.Tensor | None = None,
                ws: torch.Tensor | None = None) -> torch.Tensor:
     """Y = X w_hat^T + (alpha/r) (X A^T) B^T.  X [M, d_in], A [r, d_in], B [d_out, r] BF16."""
-    for t, n in ((X, "X"), (A, "A"), (B, "B")):
-        _dev(t, torch.bfloat16, n)
-    M, r = X.shape[0], A.shape[0]
-    Y = Y if Y is not None else torch.empty(M, q.d_out, dtype=torch.bfloat16, device=X.device)
-    _dev(Y, torch.bfloat16, "Y")
+    M, r, dev = _tokens(X), _rank(A), X.device
+    specs = _weight_specs(q) + [(X, torch.bfloat16, "X", (M, q.d_in)), (A, torch.bfloat16, "A", (r, q.d_in)),
+                                (B, torch.bfloat16, "B", (q.d_out, r))]
+    if Y is not None:
+        specs.append((Y, torch.bfloat16, "Y", (M, q.d_out)))
     if T_save is not None:
-        _dev(T_save, torch.bfloat16, "T_save")
+        specs.append((T_save, torch.bfloat16, "T_save", (M, r)))
+    _validate(specs, dev)
+    Y = Y if Y is not None else torch.empty(M, q.d_out, dtype=torch.bfloat16, device=dev)
     need = workspace_size(OP_FWD, M, q.d_out, q.d_in, r, q.dq)
-    ws = ws if ws is not None else _WS.get(need, X.device, "fwd")
+    ws = ws if ws is not None else _WS.get(need, dev, "fwd")
+    _check_ws(ws, dev)
     s = q.struct()
     _check(load_library().qlora_linear_fwd(ctypes.byref(s), X.data_ptr(), M, A.data_ptr(), B.data_ptr(), r,
                                            float(alpha), Y.data_ptr(), _ptr(T_save), ws.data_ptr(), ws.numel(),
@@ -313,25 +394,29 @@ def linear_fwd_multi(qs, X: torch.Tensor, As, Bs, alpha: float, Ys=None, T_saves
                      ws: torch.Tensor | None = None):
     """Forward of up to 4 linears that read the same X (e.g. q, k, v): returns the list of Y[i]."""
     qs = list(qs)
-    _dev(X, torch.bfloat16, "X")
-    for i in range(len(qs)):
-        _dev(As[i], torch.bfloat16, f"A[{i}]")
-        _dev(Bs[i], torch.bfloat16, f"B[{i}]")
-    M, r = X.shape[0], As[0].shape[0]
-    Ys = list(Ys) if Ys is not None else [torch.empty(M, q.d_out, dtype=torch.bfloat16, device=X.device) for q in qs]
-    for i, y in enumerate(Ys):
-        _dev(y, torch.bfloat16, f"Y[{i}]")
-    need = workspace_size_multi(qs, M, r)
-    ws = ws if ws is not None else _WS.get(need, X.device, "fwd")
-    arr, _keep = _struct_array(qs)
     n = len(qs)
+    if n < 1 or len(As) != n or len(Bs) != n or (Ys is not None and len(Ys) != n) or \
+            (T_saves is not None and len(T_saves) != n):
+        raise ValueError("linear_fwd_multi: need one A, B (and Y, T_save when given) per weight")
+    M, r, dev = _tokens(X), _rank(As[0], "A[0]"), X.device
+    specs = [(X, torch.bfloat16, "X", (M, qs[0].d_in))]
+    for i, q in enumerate(qs):
+        specs += _weight_specs(q, f"weight[{i}]") + [(As[i], torch.bfloat16, f"A[{i}]", (r, q.d_in)),
+                                                     (Bs[i], torch.bfloat16, f"B[{i}]", (q.d_out, r))]
+        if Ys is not None:
+            specs.append((Ys[i], torch.bfloat16, f"Y[{i}]", (M, q.d_out)))
+        if T_saves is not None and T_saves[i] is not None:
+            specs.append((T_saves[i], torch.bfloat16, f"T_save[{i}]", (M, r)))
+    _validate(specs, dev)
+    Ys = list(Ys) if Ys is not None else [torch.empty(M, q.d_out, dtype=torch.bfloat16, device=dev) for q in qs]
+    need = workspace_size_multi(qs, M, r)
+    ws = ws if ws is not None else _WS.get(need, dev, "fwd")
+    _check_ws(ws, dev)
+    arr, _keep = _struct_array(qs)
     VP = ctypes.c_void_p * n
     a_ptrs, b_ptrs, y_ptrs = VP(*[a.data_ptr() for a in As]), VP(*[b.data_ptr() for b in Bs]), VP(*[y.data_ptr() for y in Ys])
     t_ptrs = None
     if T_saves is not None:
-        for t in T_saves:
-            if t is not None:
-                _dev(t, torch.bfloat16, "T_save")
         t_ptrs = VP(*[_ptr(t) for t in T_saves])
     _check(load_library().qlora_linear_fwd_multi(n, arr, X.data_ptr(), M, a_ptrs, b_ptrs, r, float(alpha), y_ptrs,
                                                  t_ptrs, ws.data_ptr(), ws.numel(), _stream(X)), "linear_fwd_multi")
@@ -351,23 +436,34 @@ def _ptrs(ts):
     return (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
 
 
+def _mlp_specs(qs, As, Bs, r):
+    if len(qs) != 3 or len(As) != 3 or len(Bs) != 3:
+        raise ValueError("MLP block: need the three weights and adapters gate, up, down")
+    specs = []
+    for i, q in enumerate(qs):
+        specs += _weight_specs(q, f"weight[{i}]") + [(As[i], torch.bfloat16, f"A[{i}]", (r, q.d_in)),
+                                                     (Bs[i], torch.bfloat16, f"B[{i}]", (q.d_out, r))]
+    return specs
+
+
 def mlp_fwd(qs, X: torch.Tensor, As, Bs, alpha: float, Y: torch.Tensor | None = None,
             G_save: torch.Tensor | None = None, U_save: torch.Tensor | None = None,
             ws: torch.Tensor | None = None) -> torch.Tensor:
     """MLP block Y = down(silu(gate(X)) * up(X)); qs, As, Bs in the order gate, up, down."""
     qg, qu, qd = qs
-    _dev(X, torch.bfloat16, "X")
-    for i in range(3):
-        _dev(As[i], torch.bfloat16, f"A[{i}]")
-        _dev(Bs[i], torch.bfloat16, f"B[{i}]")
-    M, r = X.shape[0], As[0].shape[0]
-    Y = Y if Y is not None else torch.empty(M, qd.d_out, dtype=torch.bfloat16, device=X.device)
-    _dev(Y, torch.bfloat16, "Y")
+    M, r, dev = _tokens(X), _rank(As[0], "A[0]"), X.device
+    d, f = qg.d_in, qg.d_out
+    specs = _mlp_specs(qs, As, Bs, r) + [(X, torch.bfloat16, "X", (M, d))]
+    if Y is not None:
+        specs.append((Y, torch.bfloat16, "Y", (M, qd.d_out)))
     for t, n in ((G_save, "G_save"), (U_save, "U_save")):
         if t is not None:
-            _dev(t, torch.bfloat16, n)
+            specs.append((t, torch.bfloat16, n, (M, f)))
+    _validate(specs, dev)
+    Y = Y if Y is not None else torch.empty(M, qd.d_out, dtype=torch.bfloat16, device=dev)
     need = mlp_workspace_size(OP_FWD, M, qg, qu, qd, r)
-    ws = ws if ws is not None else _WS.get(need, X.device, "fwd")
+    ws = ws if ws is not None else _WS.get(need, dev, "fwd")
+    _check_ws(ws, dev)
     sg, su, sd = qg.struct(), qu.struct(), qd.struct()
     _check(load_library().qlora_mlp_fwd(ctypes.byref(sg), ctypes.byref(su), ctypes.byref(sd), X.data_ptr(), M,
                                         _ptrs(As), _ptrs(Bs), r, float(alpha), Y.data_ptr(), _ptr(G_save),
@@ -379,15 +475,21 @@ def mlp_bwd(qs, X: torch.Tensor, dY: torch.Tensor, As, Bs, alpha: float, G_saved
             U_saved: torch.Tensor | None = None, dX: torch.Tensor | None = None, ws: torch.Tensor | None = None):
     """Backward of mlp_fwd: returns (dX, [dA_gate, dA_up, dA_down], [dB_gate, dB_up, dB_down])."""
     qg, qu, qd = qs
-    for t, n in ((X, "X"), (dY, "dY")):
-        _dev(t, torch.bfloat16, n)
-    M, r = X.shape[0], As[0].shape[0]
-    dev = X.device
-    dX = dX if dX is not None else torch.empty(M, qg.d_in, dtype=torch.bfloat16, device=dev)
+    M, r, dev = _tokens(X), _rank(As[0], "A[0]"), X.device
+    d, f = qg.d_in, qg.d_out
+    if (G_saved is None) != (U_saved is None):
+        raise ValueError("mlp_bwd: give both G_saved and U_saved, or neither")
+    specs = _mlp_specs(qs, As, Bs, r) + [(X, torch.bfloat16, "X", (M, d)), (dY, torch.bfloat16, "dY", (M, qd.d_out))]
+    for t, n in ((G_saved, "G_saved"), (U_saved, "U_saved"), (dX, "dX")):
+        if t is not None:
+            specs.append((t, torch.bfloat16, n, (M, d if n == "dX" else f)))
+    _validate(specs, dev)
+    dX = dX if dX is not None else torch.empty(M, d, dtype=torch.bfloat16, device=dev)
     dAs = [torch.empty(r, q.d_in, dtype=torch.bfloat16, device=dev) for q in qs]
     dBs = [torch.empty(q.d_out, r, dtype=torch.bfloat16, device=dev) for q in qs]
     need = mlp_workspace_size(OP_BWD, M, qg, qu, qd, r)
     ws = ws if ws is not None else _WS.get(need, dev, "bwd")
+    _check_ws(ws, dev)
     sg, su, sd = qg.struct(), qu.struct(), qd.struct()
     _check(load_library().qlora_mlp_bwd(ctypes.byref(sg), ctypes.byref(su), ctypes.byref(sd), X.data_ptr(),
                                         dY.data_ptr(), M, _ptrs(As), _ptrs(Bs), r, float(alpha), _ptr(G_saved),
@@ -401,16 +503,21 @@ def linear_bwd(q: QuantizedWeight, X: torch.Tensor, dY: torch.Tensor, A: torch.T
                dX: torch.Tensor | None = None, dA: torch.Tensor | None = None, dB: torch.Tensor | None = None,
                ws: torch.Tensor | None = None):
     """Returns (dX or None, dA, dB), all BF16."""
-    for t, n in ((X, "X"), (dY, "dY"), (A, "A"), (B, "B")):
-        _dev(t, torch.bfloat16, n)
-    M, r = X.shape[0], A.shape[0]
-    dev = X.device
+    M, r, dev = _tokens(X), _rank(A), X.device
+    specs = _weight_specs(q) + [(X, torch.bfloat16, "X", (M, q.d_in)), (dY, torch.bfloat16, "dY", (M, q.d_out)),
+                                (A, torch.bfloat16, "A", (r, q.d_in)), (B, torch.bfloat16, "B", (q.d_out, r))]
+    for t, n, shp in ((T_saved, "T_saved", (M, r)), (dX if need_dX else None, "dX", (M, q.d_in)),
+                      (dA, "dA", (r, q.d_in)), (dB, "dB", (q.d_out, r))):
+        if t is not None:
+            specs.append((t, torch.bfloat16, n, shp))
+    _validate(specs, dev)
     if need_dX and dX is None:
         dX = torch.empty(M, q.d_in, dtype=torch.bfloat16, device=dev)
     dA = dA if dA is not None else torch.empty(r, q.d_in, dtype=torch.bfloat16, device=dev)
     dB = dB if dB is not None else torch.empty(q.d_out, r, dtype=torch.bfloat16, device=dev)
     need = workspace_size(OP_BWD, M, q.d_out, q.d_in, r, q.dq)
     ws = ws if ws is not None else _WS.get(need, dev, "bwd")
+    _check_ws(ws, dev)
     s = q.struct()
     _check(load_library().qlora_linear_bwd(ctypes.byref(s), X.data_ptr(), dY.data_ptr(), M, A.data_ptr(),
                                            B.data_ptr(), r, float(alpha), _ptr(T_saved),

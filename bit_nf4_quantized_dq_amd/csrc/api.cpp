@@ -44,8 +44,15 @@ int check_wq(const qlora_nf4dq_t* Wq) {
   return QLORA_OK;
 }
 
+// The caller's workspace: present and large enough (WORKSPACE), 16-byte aligned (INVALID_ARG).
+int check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (!ws || ws_bytes < need) return QLORA_ERR_WORKSPACE;
+  return aligned16(ws) ? QLORA_OK : QLORA_ERR_INVALID_ARG;
+}
+
 int check_lora(int64_t M, int32_t r, float alpha) {
-  if (M < 1 || M > (int64_t(1) << 24)) return QLORA_ERR_INVALID_ARG;
+  // M < 2^24 keeps every [M, r] operand (r <= 128) below the 4 GiB reach of a buffer descriptor
+  if (M < 1 || M >= (int64_t(1) << 24)) return QLORA_ERR_INVALID_ARG;
   if (r < 1 || r > 128) return QLORA_ERR_INVALID_ARG;
   if (!std::isfinite(alpha)) return QLORA_ERR_INVALID_ARG;
   return QLORA_OK;
@@ -65,13 +72,22 @@ constexpr int64_t kNtMinM = 1024;
 inline bool decode_once(int64_t M, int dq) { return M >= kNtMinM || dq != QLORA_DQ_E4M3; }
 
 // ---- workspace layouts
+// Every workspace starts with the arrival counters of the split reductions: one 32-bit word
+// per row group of an M <= 16 forward, or per 64-column tile of dA and of dB in a backward
+// (dB's after dA's).  The head has one fixed size, so calls of any kind and shape can share a
+// workspace without one call's partials landing on another's counters.  It must be zero
+// before the first use; every call leaves it zero.
+constexpr size_t kHead = QLORA_WS_COUNTER_BYTES;
+constexpr int64_t kHeadWords = (int64_t)(kHead / sizeof(unsigned int));
+inline unsigned int* head_counters(void* ws) { return static_cast<unsigned int*>(ws); }
+
 struct FwdWs {
   size_t tpart, ypart, ls, wcopy, gpart, total;
   int32_t gsplit;  // reduction split of the decode-once GEMM (FP32 partials at gpart)
 };
 FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r, int dq) {
   FwdWs w{};
-  size_t off = 0;
+  size_t off = kHead;
   w.tpart = off;
   if (M <= kGemvMaxM && !decode_once(M, dq)) {
     const int32_t ks = gemv_stream_fits(N, K, M, r) ? gemv_stream_plan(N, K, M, r).ksplit : gemv_ksplit(N, K);
@@ -102,7 +118,7 @@ struct BwdWs {
 };
 BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int32_t r, int dq) {
   BwdWs w{};
-  size_t off = 0;
+  size_t off = kHead;
   w.t = off;
   off = align_up(off + 2 * M * r, 256);
   w.g = off;
@@ -142,8 +158,8 @@ GroupWs group_ws(int count, const qlora_nf4dq_t* const* Wq, int64_t M, int32_t r
     int64_t Nt = 0;
     for (int i = 0; i < count; ++i) Nt += N[i];
     const int32_t ks = gemv_stream_plan(Nt, K, M, r).ksplit;
-    w.tpart = 0;
-    w.ypart = align_up(sizeof(float) * count * ks * M * r, 256);
+    w.tpart = kHead;
+    w.ypart = align_up(kHead + sizeof(float) * count * ks * M * r, 256);
     w.total = std::max(w.total, align_up(w.ypart + sizeof(float) * ks * M * Nt, 256));
   }
   return w;
@@ -171,12 +187,30 @@ int check_mlp(const qlora_nf4dq_t* Wg, const qlora_nf4dq_t* Wu, const qlora_nf4d
     return QLORA_ERR_BAD_SHAPE;
   return QLORA_OK;
 }
+// The three adapters of the MLP block (gate, up, down) and, for the backward, their gradient
+// outputs: every pointer present and A (16-byte loads) aligned, checked before any launch.
+int check_adapters(const uint16_t* const* A, const uint16_t* const* B, uint16_t* const* dA, uint16_t* const* dB) {
+  for (int i = 0; i < 3; ++i) {
+    if (!A[i] || !B[i] || !aligned16(A[i])) return QLORA_ERR_INVALID_ARG;
+    if (dA && (!dA[i] || !dB[i])) return QLORA_ERR_INVALID_ARG;
+  }
+  return QLORA_OK;
+}
 MlpWs mlp_ws(bool bwd, int64_t M, const qlora_nf4dq_t* Wg, const qlora_nf4dq_t* Wu, const qlora_nf4dq_t* Wd,
              int32_t r) {
   MlpWs w{};
   const int64_t d = Wg->d_in, f = Wg->d_out;
   const size_t act = align_up(2 * (size_t)M * f, 256);
-  size_t off = 0;
+  // the linear calls' region comes first, so their counter head is the block's own head
+  const qlora_nf4dq_t* gu[2] = {Wg, Wu};
+  size_t lin = std::max(group_ws(2, gu, M, r).total, fwd_ws(M, d, f, r, Wd->dq_format).total);
+  if (bwd) {
+    lin = std::max({lin, bwd_ws(M, f, d, r, Wg->dq_format).total, bwd_ws(M, f, d, r, Wu->dq_format).total,
+                    bwd_ws(M, d, f, r, Wd->dq_format).total});
+  }
+  w.lin = 0;
+  w.lin_bytes = align_up(lin, 256);
+  size_t off = w.lin_bytes;
   w.g = off;
   off += act;
   w.u = off;
@@ -193,21 +227,15 @@ MlpWs mlp_ws(bool bwd, int64_t M, const qlora_nf4dq_t* Wg, const qlora_nf4dq_t* 
     w.dxu = off;
     off += align_up(2 * (size_t)M * d, 256);
   }
-  const qlora_nf4dq_t* gu[2] = {Wg, Wu};
-  size_t lin = std::max(group_ws(2, gu, M, r).total, fwd_ws(M, d, f, r, Wd->dq_format).total);
-  if (bwd) {
-    lin = std::max({lin, bwd_ws(M, f, d, r, Wg->dq_format).total, bwd_ws(M, f, d, r, Wu->dq_format).total,
-                    bwd_ws(M, d, f, r, Wd->dq_format).total});
-  }
-  w.lin = off;
-  w.lin_bytes = lin;
-  w.total = off + align_up(lin, 256);
+  w.total = off;
   return w;
 }
 
+// The quantize workspace keeps the counter head untouched too, so one buffer can serve
+// every entry point.
 size_t quant_ws(int64_t d_out, int64_t d_in) {
   const int64_t nb = d_out * d_in / 64;
-  return align_up(sizeof(float) * nb, 256) + 256 * sizeof(unsigned long long) + 256;
+  return kHead + align_up(sizeof(float) * nb, 256) + 256 * sizeof(unsigned long long) + 256;
 }
 
 // ---- exact mean: value = sum_e S_e * 2^(e-150) (e >= 1), folded in a big integer and
@@ -332,6 +360,12 @@ int qlora_workspace_size_fmt(int op, int64_t M, int64_t d_out, int64_t d_in, int
   return QLORA_OK;
 }
 
+int qlora_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ws || !aligned16(ws)) return QLORA_ERR_INVALID_ARG;
+  if (ws_bytes < kHead) return QLORA_ERR_WORKSPACE;
+  return hip_status(launch_zero_words(head_counters(ws), kHeadWords, stream));
+}
+
 int qlora_format_sizes(int64_t d_out, int64_t d_in, int dq_format, size_t* codes_bytes, size_t* code8_bytes,
                        size_t* c2s_bytes) {
   if (dq_format < QLORA_DQ_E4M3 || dq_format > QLORA_DQ_NONE) return QLORA_ERR_UNSUPPORTED;
@@ -365,8 +399,8 @@ int quantize_impl(const void* W, bool w_bf16, const qlora_nf4dq_t* Wq, float* ho
   if (st) return st;
   if (!W || !aligned16(W)) return QLORA_ERR_INVALID_ARG;
   const int64_t n = Wq->d_out * Wq->d_in, nb = n / 64;
-  if (!ws || ws_bytes < quant_ws(Wq->d_out, Wq->d_in)) return QLORA_ERR_WORKSPACE;
-  char* base = static_cast<char*>(ws);
+  if ((st = check_ws(ws, ws_bytes, quant_ws(Wq->d_out, Wq->d_in)))) return st;
+  char* base = static_cast<char*>(ws) + kHead;
   float* c1 = reinterpret_cast<float*>(base);
   auto* hist = reinterpret_cast<unsigned long long*>(base + align_up(sizeof(float) * nb, 256));
   int* flag = reinterpret_cast<int*>(hist + 256);
@@ -439,19 +473,21 @@ int qlora_linear_fwd(const qlora_nf4dq_t* Wq, const uint16_t* X, int64_t M, cons
   const int64_t N = Wq->d_out, K = Wq->d_in;
   const int dq = Wq->dq_format;
   const FwdWs L = fwd_ws(M, N, K, r, dq);
-  if (!ws || ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
+  if ((st = check_ws(ws, ws_bytes, L.total))) return st;
   char* base = static_cast<char*>(ws);
   const float s = alpha / (float)r;
   const uint32_t* codes = reinterpret_cast<const uint32_t*>(Wq->codes);
   float* tpart = reinterpret_cast<float*>(base + L.tpart);
   if (M <= kGemvMaxM && !decode_once(M, dq)) {
-    if ((N + 63) / 64 > 65536) return QLORA_ERR_BAD_SHAPE;  // one arrival counter per 64 rows
     float* ypart = reinterpret_cast<float*>(base + L.ypart);
-    if (gemv_stream_fits(N, K, M, r))
+    const bool big = gemv_stream_fits(N, K, M, r);
+    // one arrival counter per row group of the launch, in the workspace head
+    if ((big ? gemv_stream_plan(N, K, M, r).groups : gemv_groups(N)) > kHeadWords) return QLORA_ERR_BAD_SHAPE;
+    if (big)
       return hip_status(launch_gemv_stream(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, X, M, A, B, r, s, Y, T_save,
-                                           ypart, tpart, tables_of(Wq), stream));
+                                           ypart, tpart, head_counters(ws), tables_of(Wq), stream));
     return hip_status(launch_gemv_fwd(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, X, M, A, B, r, s, Y, T_save, ypart,
-                                      tpart, tables_of(Wq), stream));
+                                      tpart, head_counters(ws), tables_of(Wq), stream));
   }
   // T = X A^T: s T (BF16) feeds the adapter slices of the GEMM; T itself is saved if asked
   uint16_t* ls = reinterpret_cast<uint16_t*>(base + L.ls);
@@ -498,7 +534,7 @@ int qlora_linear_fwd_multi(int count, const qlora_nf4dq_t* const* Wq, const uint
   for (int i = 0; i < count; ++i)
     if (!A[i] || !B[i] || !Y[i] || !aligned16(A[i]) || !aligned16(Y[i])) return QLORA_ERR_INVALID_ARG;
   const GroupWs L = group_ws(count, Wq, M, r);
-  if (!ws || ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
+  if ((st = check_ws(ws, ws_bytes, L.total))) return st;
   if (!L.one_launch) {
     for (int i = 0; i < count; ++i) {
       st = qlora_linear_fwd(Wq[i], X, M, A[i], B[i], r, alpha, Y[i], T_save ? T_save[i] : nullptr, ws, ws_bytes,
@@ -514,7 +550,8 @@ int qlora_linear_fwd_multi(int count, const qlora_nf4dq_t* const* Wq, const uint
   char* base = static_cast<char*>(ws);
   return hip_status(launch_gemv_stream_group(count, lins, Wq[0]->d_in, X, M, r, alpha / (float)r,
                                              reinterpret_cast<float*>(base + L.ypart),
-                                             reinterpret_cast<float*>(base + L.tpart), tables_of(Wq[0]), stream));
+                                             reinterpret_cast<float*>(base + L.tpart), head_counters(ws),
+                                             tables_of(Wq[0]), stream));
 }
 
 int qlora_mlp_workspace_size(int op, int64_t M, const qlora_nf4dq_t* Wg, const qlora_nf4dq_t* Wu,
@@ -531,10 +568,11 @@ int qlora_mlp_fwd(const qlora_nf4dq_t* Wg, const qlora_nf4dq_t* Wu, const qlora_
                   uint16_t* G_save, uint16_t* U_save, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_mlp(Wg, Wu, Wd);
   if (st || (st = check_lora(M, r, alpha))) return st;
-  if (!X || !A || !B || !Y) return QLORA_ERR_INVALID_ARG;
+  if (!X || !A || !B || !Y || !aligned16(X) || !aligned16(Y)) return QLORA_ERR_INVALID_ARG;
+  if ((st = check_adapters(A, B, nullptr, nullptr))) return st;
   if ((G_save && !aligned16(G_save)) || (U_save && !aligned16(U_save))) return QLORA_ERR_INVALID_ARG;
   const MlpWs L = mlp_ws(false, M, Wg, Wu, Wd, r);
-  if (!ws || ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
+  if ((st = check_ws(ws, ws_bytes, L.total))) return st;
   char* base = static_cast<char*>(ws);
   uint16_t* G = G_save ? G_save : reinterpret_cast<uint16_t*>(base + L.g);
   uint16_t* U = U_save ? U_save : reinterpret_cast<uint16_t*>(base + L.u);
@@ -554,11 +592,13 @@ int qlora_mlp_bwd(const qlora_nf4dq_t* Wg, const qlora_nf4dq_t* Wu, const qlora_
                   uint16_t* const* dB, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_mlp(Wg, Wu, Wd);
   if (st || (st = check_lora(M, r, alpha))) return st;
-  if (!X || !dY || !A || !B || !dX || !dA || !dB || !aligned16(dX)) return QLORA_ERR_INVALID_ARG;
+  if (!X || !dY || !A || !B || !dX || !dA || !dB) return QLORA_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(dY) || !aligned16(dX)) return QLORA_ERR_INVALID_ARG;
+  if ((st = check_adapters(A, B, dA, dB))) return st;
   if ((G_saved == nullptr) != (U_saved == nullptr)) return QLORA_ERR_INVALID_ARG;
   if (G_saved && (!aligned16(G_saved) || !aligned16(U_saved))) return QLORA_ERR_INVALID_ARG;
   const MlpWs L = mlp_ws(true, M, Wg, Wu, Wd, r);
-  if (!ws || ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
+  if ((st = check_ws(ws, ws_bytes, L.total))) return st;
   char* base = static_cast<char*>(ws);
   const int64_t f = Wg->d_out, d = Wg->d_in;
   void* lin = base + L.lin;
@@ -598,7 +638,7 @@ int qlora_linear_bwd(const qlora_nf4dq_t* Wq, const uint16_t* X, const uint16_t*
   const int64_t N = Wq->d_out, K = Wq->d_in;
   const int dq = Wq->dq_format;
   const BwdWs L = bwd_ws(M, N, K, r, dq);
-  if (!ws || ws_bytes < L.total) return QLORA_ERR_WORKSPACE;
+  if ((st = check_ws(ws, ws_bytes, L.total))) return st;
   char* base = static_cast<char*>(ws);
   const float s = alpha / (float)r;
   uint16_t* t = reinterpret_cast<uint16_t*>(base + L.t);
@@ -638,7 +678,10 @@ int qlora_linear_bwd(const qlora_nf4dq_t* Wq, const uint16_t* X, const uint16_t*
   }
   // dA = s G^T X [r, K] and dB = s dY^T T, stored [N, r], in one launch (own partials and
   // arrival counters each)
-  if ((e = launch_lora_grad2(g, X, K, 0, cpa, dA, T, dY, N, 1, cpb, dB, M, r, s, stream)) != hipSuccess)
+  // (counters: dA's column tiles, then dB's, in the workspace head)
+  unsigned int* cnt_a = head_counters(ws);
+  unsigned int* cnt_b = cnt_a + (K + 63) / 64;
+  if ((e = launch_lora_grad2(g, X, K, 0, cpa, cnt_a, dA, T, dY, N, 1, cpb, cnt_b, dB, M, r, s, stream)) != hipSuccess)
     return QLORA_ERR_HIP;
   return QLORA_OK;
 }

@@ -5,7 +5,7 @@
 // and 4 bits leave less to read).  Each weight is decoded once, on chip, from its 4-bit code
 // ("QLoRA: Quantize Base Weights to 4-Bit", Section 3) and multiplied on the MFMA units.
 //
-// Work split.  A workgroup owns 128 weight rows (4 wavefronts x 2 MFMA column tiles of 16
+// Work split.  A workgroup owns 128 weight rows (8 wavefronts x one MFMA column tile of 16
 // rows) and one of `ksplit` ranges of 64-weight blocks, walked in chunks of kChunk blocks.
 // Per chunk, every thread first issues all of its global loads (part of one weight row's
 // codes and block constants, a slice of X) into registers, then writes them to LDS; the MFMA
@@ -22,19 +22,16 @@
 // 128 rows, and adds that to its partial output.
 //
 // Split-K reduction.  With ksplit > 1 each workgroup writes an FP32 partial; the last
-// workgroup of a row group to finish (a device-scope counter that each workgroup advances by
-// 65536/ksplit, so it is always a multiple of 65536 between calls) sums the partials in a
-// fixed order and writes BF16 Y (and T for the backward).  The counters live in this file as
-// zero-initialized device data; calls with M <= 16 on one device must therefore not overlap.
-// The partials travel through memory with system-scope (cache-bypassing) stores and loads:
+// workgroup of a row group to finish (a device-scope arrival counter, one per row group, in
+// the caller's workspace; that workgroup resets it to zero) sums the partials in a fixed
+// order and writes BF16 Y (and T for the backward).  Calls that share a workspace must not
+// overlap; calls with separate workspaces may.  The partials travel through memory with system-scope (cache-bypassing) stores and loads:
 // the writer waits for its stores to complete before advancing the counter, so the reader
 // needs no cache write-back fence.
 #include "qlora_device.h"
 #include "qlora_host.h"
 
 namespace qlora {
-
-__device__ unsigned int g_gemv_counters[65536];
 
 namespace {
 
@@ -45,7 +42,7 @@ constexpr int kRows = kWaves * 16 * kTiles;  // rows per workgroup
 constexpr int kChunk = 8;               // blocks staged per pass (all loads of a pass in flight at once)
 constexpr int kXItems = 16 * kChunk * 8 / kThreads;  // 16-byte pieces of X staged per thread per pass
 constexpr int kStageBlocks = kChunk * kRows / kThreads;  // blocks of one row staged per thread
-constexpr uint32_t kCounterPeriod = 65536;
+constexpr int32_t kMaxSplit = 65536;
 constexpr int kSumU = 16;               // partials loaded together in the split-K sum
 
 struct GemvArgs {
@@ -64,6 +61,7 @@ struct GemvArgs {
   uint16_t* T_save;
   float* part;   // [ksplit][M][N]
   float* tpart;  // [ksplit][M][r]
+  unsigned int* counters;  // [row groups], zero between calls
   int32_t ksplit;
   int32_t nbs;   // blocks per split
 };
@@ -477,9 +475,9 @@ __global__ __launch_bounds__(kThreads) void k_gemv_fused(GemvArgs a, Nf4Tables T
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
-    const unsigned int inc = kCounterPeriod / (unsigned int)a.ksplit;
-    const unsigned int old = __hip_atomic_fetch_add(&g_gemv_counters[grp], inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = ((old + inc) % kCounterPeriod) == 0u;
+    const unsigned int old = __hip_atomic_fetch_add(&a.counters[grp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (old + 1u == (unsigned int)a.ksplit) ? 1u : 0u;
+    if (s_last) __hip_atomic_store(&a.counters[grp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   if (!s_last) return;
@@ -502,7 +500,7 @@ int32_t gemv_ksplit(int64_t N, int64_t K) {
   const int64_t nb_row = K / kBlock1;
   const int64_t want = (256 + groups - 1) / groups;
   int32_t ks = 1;
-  while (ks < want && ks * 2 <= nb_row && ks < (int32_t)kCounterPeriod) ks *= 2;
+  while (ks < want && ks * 2 <= nb_row && ks < kMaxSplit) ks *= 2;
   return ks;
 }
 
@@ -511,8 +509,8 @@ int64_t gemv_groups(int64_t N) { return (N + kRows - 1) / kRows; }
 hipError_t launch_gemv_fwd(const uint32_t* codes, const uint8_t* code8, const float* c2s,
                            const float* mu, int64_t N, int64_t K, const uint16_t* X, int64_t M,
                            const uint16_t* A, const uint16_t* B, int32_t r, float s, uint16_t* Y,
-                           uint16_t* T_save, float* part, float* tpart, const Nf4Tables& T,
-                           hipStream_t st) {
+                           uint16_t* T_save, float* part, float* tpart, unsigned int* counters,
+                           const Nf4Tables& T, hipStream_t st) {
   GemvArgs a;
   a.codes = reinterpret_cast<const uint8_t*>(codes);
   a.code8 = code8;
@@ -530,6 +528,7 @@ hipError_t launch_gemv_fwd(const uint32_t* codes, const uint8_t* code8, const fl
   a.T_save = T_save;
   a.part = part;
   a.tpart = tpart;
+  a.counters = counters;
   a.ksplit = gemv_ksplit(N, K);
   const int64_t nb_row = K / kBlock1;
   a.nbs = (int32_t)((nb_row + a.ksplit - 1) / a.ksplit);

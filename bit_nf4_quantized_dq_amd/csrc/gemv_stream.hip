@@ -36,18 +36,16 @@
 // and the split-K hand-off once for the whole group instead of once per linear.
 //
 // Split-K reduction.  With ksplit > 1 each workgroup writes an FP32 partial; the last
-// workgroup of a row group to finish (a device-scope counter; that workgroup resets it to
-// zero) sums the partials in a fixed order and writes BF16 Y (and T for the backward).  The
-// counters live in this file as zero-initialized device data; calls with M <= 16 on one
-// device must therefore not overlap.  The partials travel through memory with system-scope
+// workgroup of a row group to finish (a device-scope arrival counter per row group of the
+// launch, in the caller's workspace; that workgroup resets it to zero) sums the partials in
+// a fixed order and writes BF16 Y (and T for the backward).  Calls that share a workspace
+// must not overlap; calls with separate workspaces may.  The partials travel through memory with system-scope
 // (cache-bypassing) stores and loads: the writer waits for its stores to complete before
 // advancing the counter, so the reader needs no cache write-back fence.
 #include "qlora_device.h"
 #include "qlora_host.h"
 
 namespace qlora {
-
-__device__ unsigned int g_stream_counters[65536];
 
 namespace {
 
@@ -104,6 +102,7 @@ struct StreamArgs {
   uint16_t* T_save;
   float* part;   // [ksplit][M][N]
   float* tpart;  // [ksplit][M][r]
+  unsigned int* counters;  // [row groups of the launch], zero between calls
   int64_t N, K;
   int32_t M, r;
   float s;
@@ -434,9 +433,9 @@ __global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L, t
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
-    const unsigned int old = __hip_atomic_fetch_add(&g_stream_counters[pgrp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned int old = __hip_atomic_fetch_add(&a.counters[pgrp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sm.last = (old + 1u == (unsigned int)a.ksplit) ? 1u : 0u;
-    if (sm.last) __hip_atomic_store(&g_stream_counters[pgrp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (sm.last) __hip_atomic_store(&a.counters[pgrp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   if (!sm.last) return;
@@ -542,7 +541,8 @@ namespace {
 // One launch over `count` linears (count == 1: the single-linear kernel, without the group
 // table in its arguments).
 hipError_t stream_launch(int count, const StreamLinear* lins, int64_t K, const uint16_t* X, int64_t M, int32_t r,
-                         float s, float* part, float* tpart, const Nf4Tables& T, hipStream_t st) {
+                         float s, float* part, float* tpart, unsigned int* counters, const Nf4Tables& T,
+                         hipStream_t st) {
   if (count < 1 || count > kMaxLin || M < 1 || M > 16 || r < 1 || r > kMaxR) return hipErrorInvalidValue;
   int64_t Nt = 0;
   for (int i = 0; i < count; ++i) {
@@ -567,6 +567,7 @@ hipError_t stream_launch(int count, const StreamLinear* lins, int64_t K, const u
   a.T_save = lins[0].T_save;
   a.part = part;
   a.tpart = tpart;
+  a.counters = counters;
   a.N = Nt;
   a.K = K;
   a.M = (int32_t)M;
@@ -638,17 +639,17 @@ hipError_t stream_launch(int count, const StreamLinear* lins, int64_t K, const u
 hipError_t launch_gemv_stream(const uint32_t* codes, const uint8_t* code8, const float* c2s,
                               const float* mu, int64_t N, int64_t K, const uint16_t* X, int64_t M,
                               const uint16_t* A, const uint16_t* B, int32_t r, float s, uint16_t* Y,
-                              uint16_t* T_save, float* part, float* tpart, const Nf4Tables& T,
-                              hipStream_t st) {
+                              uint16_t* T_save, float* part, float* tpart, unsigned int* counters,
+                              const Nf4Tables& T, hipStream_t st) {
   const StreamLinear one{codes, code8, c2s, mu, N, A, B, Y, T_save};
-  return stream_launch(1, &one, K, X, M, r, s, part, tpart, T, st);
+  return stream_launch(1, &one, K, X, M, r, s, part, tpart, counters, T, st);
 }
 
 hipError_t launch_gemv_stream_group(int count, const StreamLinear* lins, int64_t K, const uint16_t* X, int64_t M,
-                                    int32_t r, float s, float* part, float* tpart, const Nf4Tables& T,
-                                    hipStream_t st) {
+                                    int32_t r, float s, float* part, float* tpart, unsigned int* counters,
+                                    const Nf4Tables& T, hipStream_t st) {
   if (count < 2) return hipErrorInvalidValue;
-  return stream_launch(count, lins, K, X, M, r, s, part, tpart, T, st);
+  return stream_launch(count, lins, K, X, M, r, s, part, tpart, counters, T, st);
 }
 
 }  // namespace qlora

@@ -10,7 +10,8 @@
 // grad : out(j, c) = scale * sum_m U[m][j] V[m][c]            (dA = s G^T X, dB = s dY^T T)
 //        One workgroup owns 64 columns c and a slice of the tokens; the slices' FP32 sums
 //        are combined in a fixed order by the last workgroup of the column tile to finish
-//        (arrival counters in one of two sets, so two launches may run concurrently).
+//        (arrival counters in the caller's workspace, one per column tile, reset to zero by
+//        that workgroup; products with their own counters may run concurrently).
 //
 // Both use MFMA 16x16x32 BF16.  Operands whose reduction index is strided in memory (Q as
 // [Kd, R], U and V) are staged in LDS row-major and read with ds_read_b64_tr_b16: within
@@ -23,15 +24,12 @@
 
 namespace qlora {
 
-__device__ unsigned int g_lora_counters[2 * 65536];
-
 namespace {
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 constexpr int kSumU = 16;                 // partials loaded together before they are added
-constexpr uint32_t kCounterPeriod = 65536;
 
 // 8 consecutive rows k0 + 8 (lane >> 4) .. +7 of column (lane & 15) of an LDS tile with 16
 // columns and a row pitch of `pitch` bytes (rows k0 .. k0 + 31).
@@ -272,12 +270,12 @@ __device__ __forceinline__ void grad_body(const GradArgs& g, int64_t c_tile, int
   constexpr int kRedBytes = kGradWaves * JT * 4 * 64 * 16;
   __shared__ __attribute__((aligned(16))) char smem[kGradWaves * kWaveBytes > kRedBytes ? kGradWaves * kWaveBytes : kRedBytes];
   __shared__ bool s_last;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wavefront index is uniform: keep it in a scalar register so the per-chunk buffer
+  // descriptors below stay scalar
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t c0 = c_tile * kGradCols;
   const int64_t mbeg = m_slice * mps;
   const int64_t mend = (mbeg + mps < M) ? mbeg + mps : M;
-  const rsrc_t rv = make_rsrc(V, M * C * 2);
-  const rsrc_t ru = make_rsrc(U, M * (int64_t)R * 2);
   char* vt = smem + wave * kWaveBytes;  // 4 V tiles, then JT U tiles
   char* ut = vt + 4 * kVTile;
   f32x4_t acc[JT][4];
@@ -295,23 +293,28 @@ __device__ __forceinline__ void grad_body(const GradArgs& g, int64_t c_tile, int
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int64_t mc = mc0 + (int64_t)32 * kGradWaves * d;
+      // descriptors based at the chunk's first token: in-chunk offsets stay below 32 rows,
+      // whatever M * C is (rows at or past mend read as zero)
+      const int64_t live = mend - mc;
+      const rsrc_t rv = make_rsrc(V + mc * C, live * C * 2);
+      const rsrc_t ru = make_rsrc(U + mc * R, live * (int64_t)R * 2);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t m = mc + 8 * i + (lane >> 3);
+        const int64_t ml = 8 * i + (lane >> 3);
         const int64_t c = c0 + 8 * (lane & 7);
-        vv[d][i] = bload16(rv, (m < mend && c < C) ? (uint32_t)((m * C + c) * 2) : kOOB);
+        vv[d][i] = bload16(rv, (ml < live && c < C) ? (uint32_t)((ml * C + c) * 2) : kOOB);
       }
-      const int64_t m = mc + (lane >> 1);
+      const int64_t ml = lane >> 1;
 #pragma unroll
       for (int t = 0; t < JT; ++t) {
         const int j = 16 * t + 8 * (lane & 1);
         if (uvec) {
-          uw[d][t] = bload16(ru, (m < mend && j < R) ? (uint32_t)((m * R + j) * 2) : kOOB);
+          uw[d][t] = bload16(ru, (ml < live && j < R) ? (uint32_t)((ml * R + j) * 2) : kOOB);
         } else {
           uint32_t e[8];
 #pragma unroll
           for (int q = 0; q < 8; ++q)
-            e[q] = __builtin_amdgcn_raw_buffer_load_b16(ru, (m < mend && j + q < R) ? (int)((m * R + j + q) * 2) : (int)kOOB, 0, 0);
+            e[q] = __builtin_amdgcn_raw_buffer_load_b16(ru, (ml < live && j + q < R) ? (int)((ml * R + j + q) * 2) : (int)kOOB, 0, 0);
           uw[d][t] = make_uint4((e[0] & 0xFFFFu) | (e[1] << 16), (e[2] & 0xFFFFu) | (e[3] << 16),
                                 (e[4] & 0xFFFFu) | (e[5] << 16), (e[6] & 0xFFFFu) | (e[7] << 16));
         }
@@ -380,10 +383,9 @@ __device__ __forceinline__ void grad_body(const GradArgs& g, int64_t c_tile, int
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned int inc = kCounterPeriod / (unsigned int)msplit;
-    const unsigned int old = __hip_atomic_fetch_add(&counters[c_tile], inc, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-    s_last = ((old + inc) % kCounterPeriod) == 0u;
+    const unsigned int old = __hip_atomic_fetch_add(&counters[c_tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = old + 1u == (unsigned int)msplit;
+    if (s_last) __hip_atomic_store(&counters[c_tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   if (!s_last) return;
@@ -424,19 +426,6 @@ __global__ __launch_bounds__(kGradThreads) void k_lora_grad2(GradArgs g0, GradAr
   grad_body<JT, D>(g, blockIdx.x, blockIdx.y);
 }
 
-// Device address of the arrival counters on the current device (looked up once per device).
-unsigned int* lora_counters() {
-  static unsigned int* addr[64] = {nullptr};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  if (!addr[dev]) {
-    void* p = nullptr;
-    if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_lora_counters)) != hipSuccess) return nullptr;
-    addr[dev] = static_cast<unsigned int*>(p);
-  }
-  return addr[dev];
-}
-
 // Batch depth: slabs (or token chunks) per pass, at most the wavefront's share and at most
 // kMaxD (the register budget of the loads held at once).
 inline int batch_depth(int64_t per_wave, int max_d) {
@@ -464,10 +453,10 @@ hipError_t down_launch(const uint16_t* P, const uint16_t* Q, int64_t M, int32_t 
   return hipGetLastError();
 }
 
-// Gradient product arguments: msplit token slices of mps tokens, arrival counters of set
-// counter_set.
+// Gradient product arguments: msplit token slices of mps tokens; one arrival counter per
+// column tile at `counters`.
 GradArgs grad_args(const uint16_t* U, const uint16_t* V, int64_t M, int32_t R, int64_t C, float scale, int transposed,
-                   float* part, int counter_set, uint16_t* out, unsigned int* counters) {
+                   float* part, unsigned int* counters, uint16_t* out) {
   GradArgs g;
   g.U = U;
   g.V = V;
@@ -479,7 +468,7 @@ GradArgs grad_args(const uint16_t* U, const uint16_t* V, int64_t M, int32_t R, i
   g.scale = scale;
   g.transposed = transposed;
   g.part = part;
-  g.counters = counters + 65536 * counter_set;
+  g.counters = counters;
   g.out = out;
   return g;
 }
@@ -606,20 +595,17 @@ int32_t lora_grad_msplit(int64_t M, int64_t C) {
 }
 
 hipError_t launch_lora_grad(const uint16_t* U, const uint16_t* V, int64_t M, int32_t R, int64_t C, float scale,
-                            int transposed, float* part, int counter_set, uint16_t* out, hipStream_t s) {
-  unsigned int* counters = lora_counters();
-  if (!counters) return hipErrorInvalidSymbol;
-  const GradArgs g = grad_args(U, V, M, R, C, scale, transposed, part, counter_set, out, counters);
+                            int transposed, float* part, unsigned int* counters, uint16_t* out, hipStream_t s) {
+  const GradArgs g = grad_args(U, V, M, R, C, scale, transposed, part, counters, out);
   return grad_dispatch(g, nullptr, s);
 }
 
 hipError_t launch_lora_grad2(const uint16_t* U0, const uint16_t* V0, int64_t C0, int transposed0, float* part0,
-                             uint16_t* out0, const uint16_t* U1, const uint16_t* V1, int64_t C1, int transposed1,
-                             float* part1, uint16_t* out1, int64_t M, int32_t R, float scale, hipStream_t s) {
-  unsigned int* counters = lora_counters();
-  if (!counters) return hipErrorInvalidSymbol;
-  const GradArgs g0 = grad_args(U0, V0, M, R, C0, scale, transposed0, part0, 0, out0, counters);
-  const GradArgs g1 = grad_args(U1, V1, M, R, C1, scale, transposed1, part1, 1, out1, counters);
+                             unsigned int* counters0, uint16_t* out0, const uint16_t* U1, const uint16_t* V1,
+                             int64_t C1, int transposed1, float* part1, unsigned int* counters1, uint16_t* out1,
+                             int64_t M, int32_t R, float scale, hipStream_t s) {
+  const GradArgs g0 = grad_args(U0, V0, M, R, C0, scale, transposed0, part0, counters0, out0);
+  const GradArgs g1 = grad_args(U1, V1, M, R, C1, scale, transposed1, part1, counters1, out1);
   return grad_dispatch(g0, &g1, s);
 }
 

@@ -11,6 +11,8 @@
 // rounded once (RNE).  The two input gradients of the block (through gate and through up)
 // are added by k_add_bf16.  All three kernels are HBM-bound: one thread per 8 consecutive
 // values, 16-byte loads and stores, grid-stride.
+#include <algorithm>
+
 #include "qlora_device.h"
 #include "qlora_host.h"
 
@@ -83,7 +85,20 @@ unsigned grid_for(int64_t n8) {
   return (unsigned)(blocks < 4096 ? (blocks > 0 ? blocks : 1) : 4096);
 }
 
+__global__ __launch_bounds__(kThreads) void k_zero_words(unsigned int* __restrict__ p, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) p[i] = 0u;
+}
+
 }  // namespace
+
+// The counter head of a workspace (qlora_workspace_init): a fill kernel rather than a memset,
+// so that it may sit in a captured graph.
+hipError_t launch_zero_words(unsigned int* p, int64_t n, hipStream_t st) {
+  const int64_t blocks = std::min<int64_t>((n + kThreads - 1) / kThreads, 1024);
+  hipLaunchKernelGGL(k_zero_words, dim3((unsigned)std::max<int64_t>(blocks, 1)), dim3(kThreads), 0, st, p, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_swiglu_fwd(const uint16_t* G, const uint16_t* U, uint16_t* H, int64_t n, hipStream_t st) {
   if (n % 8 != 0) return hipErrorInvalidValue;

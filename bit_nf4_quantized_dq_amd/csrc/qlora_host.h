@@ -66,11 +66,11 @@ hipError_t launch_adamw(float* master, float* m, float* v, const uint16_t* grad,
 hipError_t launch_lora_down(const uint16_t* P, const uint16_t* Q, int q_transposed, int64_t M, int32_t R, int64_t Kd,
                             float scale, uint16_t* out_s, uint16_t* out_u, hipStream_t s);
 // out(j, c) = bf16(scale * sum_m U[m][j] V[m][c]); U [M, R], V [M, C]; out [R, C], or
-// [C, R] when transposed.  part: FP32 [lora_grad_msplit(M, C)][R][C] scratch; counter_set
-// (0 or 1) selects the arrival counters, so two launches with different sets may overlap.
+// [C, R] when transposed.  part: FP32 [lora_grad_msplit(M, C)][R][C] scratch; counters: one
+// arrival counter per 64-column tile, zero before the call and left zero after it.
 int32_t lora_grad_msplit(int64_t M, int64_t C);
 hipError_t launch_lora_grad(const uint16_t* U, const uint16_t* V, int64_t M, int32_t R, int64_t C, float scale,
-                            int transposed, float* part, int counter_set, uint16_t* out, hipStream_t s);
+                            int transposed, float* part, unsigned int* counters, uint16_t* out, hipStream_t s);
 // The step's prologues as one launch each (E4M3 constants): the down-projection T = X A^T
 // (t_s = scale T, t_u = T) with the decoded copy w_out = w_hat [N, K]; and G = dY B (g_s, g_u)
 // with the transposed decoded copy wt_out = w_hat^T [K, N].
@@ -82,19 +82,23 @@ hipError_t launch_bwd_prologue(const uint16_t* dY, const uint16_t* B, int64_t M,
                                uint16_t* g_s, uint16_t* g_u, const uint32_t* codes, const uint8_t* code8,
                                const float* c2s, const float* mu, int64_t K, uint16_t* wt_out, const Nf4Tables& T,
                                hipStream_t s);
-// Two such products in one launch (counter sets 0 and 1), e.g. dA and dB of one backward.
+// Two such products in one launch (each with its own partials and counters), e.g. dA and dB
+// of one backward.
 hipError_t launch_lora_grad2(const uint16_t* U0, const uint16_t* V0, int64_t C0, int transposed0, float* part0,
-                             uint16_t* out0, const uint16_t* U1, const uint16_t* V1, int64_t C1, int transposed1,
-                             float* part1, uint16_t* out1, int64_t M, int32_t R, float scale, hipStream_t s);
+                             unsigned int* counters0, uint16_t* out0, const uint16_t* U1, const uint16_t* V1,
+                             int64_t C1, int transposed1, float* part1, unsigned int* counters1, uint16_t* out1,
+                             int64_t M, int32_t R, float scale, hipStream_t s);
 
 // ---- weight-streaming forward, M <= 16 (gemv.hip): one launch, split-K with FP32
-// partials part [ksplit][M][N] and tpart [ksplit][M][r] in the workspace.
+// partials part [ksplit][M][N] and tpart [ksplit][M][r] in the workspace, and one arrival
+// counter per row group (gemv_groups), zero before the call and left zero after it.
 int32_t gemv_ksplit(int64_t N, int64_t K);
+int64_t gemv_groups(int64_t N);
 hipError_t launch_gemv_fwd(const uint32_t* codes, const uint8_t* code8, const float* c2s,
                            const float* mu, int64_t N, int64_t K, const uint16_t* X, int64_t M,
                            const uint16_t* A, const uint16_t* B, int32_t r, float s, uint16_t* Y,
-                           uint16_t* T_save, float* part, float* tpart, const Nf4Tables& T,
-                           hipStream_t st);
+                           uint16_t* T_save, float* part, float* tpart, unsigned int* counters,
+                           const Nf4Tables& T, hipStream_t st);
 // The same forward for large weights (gemv_stream.hip): used when gemv_stream_fits(); its
 // reduction split comes from gemv_stream_plan() (same partial layout as above).
 struct GemvPlan {
@@ -106,11 +110,12 @@ bool gemv_stream_fits(int64_t N, int64_t K, int64_t M, int32_t r);
 hipError_t launch_gemv_stream(const uint32_t* codes, const uint8_t* code8, const float* c2s,
                               const float* mu, int64_t N, int64_t K, const uint16_t* X, int64_t M,
                               const uint16_t* A, const uint16_t* B, int32_t r, float s, uint16_t* Y,
-                              uint16_t* T_save, float* part, float* tpart, const Nf4Tables& T,
-                              hipStream_t st);
+                              uint16_t* T_save, float* part, float* tpart, unsigned int* counters,
+                              const Nf4Tables& T, hipStream_t st);
 // Grouped form: count (2..4) linears that read the same X [M, K], each d_out a multiple of
 // 256, run as one launch.  Partials: part [ksplit][M][sum of d_out], tpart [count][ksplit][M][r],
-// with ksplit = gemv_stream_plan(sum of d_out, K, M, r).ksplit.
+// with ksplit = gemv_stream_plan(sum of d_out, K, M, r).ksplit, and one arrival counter per
+// row group of the launch (gemv_stream_plan(...).groups).
 struct StreamLinear {
   const uint32_t* codes;
   const uint8_t* code8;
@@ -125,8 +130,8 @@ struct StreamLinear {
 constexpr int kStreamMaxGroup = 4;
 bool gemv_stream_group_fits(int count, const int64_t* N, int64_t K, int64_t M, int32_t r);
 hipError_t launch_gemv_stream_group(int count, const StreamLinear* lins, int64_t K, const uint16_t* X, int64_t M,
-                                    int32_t r, float s, float* part, float* tpart, const Nf4Tables& T,
-                                    hipStream_t st);
+                                    int32_t r, float s, float* part, float* tpart, unsigned int* counters,
+                                    const Nf4Tables& T, hipStream_t st);
 
 // ---- fused dequant MFMA GEMMs (gemm.hip)
 // Y[M,N] = X[M,K] w_hat^T + L[M,r] B[N,r]^T, L = s*T (BF16, prescaled)
@@ -154,5 +159,7 @@ hipError_t launch_swiglu_fwd(const uint16_t* G, const uint16_t* U, uint16_t* H, 
 hipError_t launch_swiglu_bwd(const uint16_t* dH, const uint16_t* G, const uint16_t* U, uint16_t* dG, uint16_t* dU,
                              int64_t n, hipStream_t st);
 hipError_t launch_add_bf16(const uint16_t* a, const uint16_t* b, uint16_t* c, int64_t n, hipStream_t st);
+// n 32-bit zeros at p (the workspace's counter head)
+hipError_t launch_zero_words(unsigned int* p, int64_t n, hipStream_t st);
 
 }  // namespace qlora

@@ -27,7 +27,15 @@
  *     Arguments are validated before any launch; on an error nothing is launched.
  *     Work is enqueued on the caller's stream `stream` (0 = null stream).  Except where
  *     stated, calls do not synchronize, so device-side faults surface on the stream.
- *   - Calls that share a workspace must not overlap in time.
+ *   - Workspaces.  The first QLORA_WS_COUNTER_BYTES bytes of every workspace hold the
+ *     arrival counters of the split reductions (the last workgroup to finish a row group or
+ *     column tile adds the partial results in a fixed order).  They must be zero before the
+ *     workspace is first used: allocate it zero-filled, or call qlora_workspace_init once.
+ *     Every call leaves them zero again, so one workspace serves any sequence of calls of
+ *     any kind and shape, and calls captured in a HIP graph can be replayed.
+ *   - Concurrency.  Calls that share a workspace must not overlap in time (e.g. run on two
+ *     streams at once).  The library keeps no device state of its own, so calls with
+ *     separate workspaces may overlap, on one device or several.
  */
 #ifndef QLORA_NF4_H
 #define QLORA_NF4_H
@@ -41,9 +49,14 @@
 extern "C" {
 #endif
 
+/* Bytes of arrival counters at the head of every workspace (512 KiB: one 32-bit word per
+ * 64-column tile of dA and of dB, each dimension at most 2^22). */
+#define QLORA_WS_COUNTER_BYTES ((size_t)524288)
+
 enum qlora_status {
   QLORA_OK = 0,
-  QLORA_ERR_INVALID_ARG = -1, /* null pointer, M < 1, r outside [1, 128], alpha not finite */
+  QLORA_ERR_INVALID_ARG = -1, /* null or misaligned pointer, M outside [1, 2^24), r outside
+                                 [1, 128], alpha not finite */
   QLORA_ERR_BAD_SHAPE = -2,   /* d_in % 64 != 0, d_out % 16 != 0, d_in or d_out > 2^22,
                                  d_out * d_in > 2^32 (32-bit buffer offsets) */
   QLORA_ERR_UNSUPPORTED = -3, /* block sizes other than (64, 256), unknown codebook or format */
@@ -102,7 +115,11 @@ typedef struct qlora_nf4dq {
   int32_t dq_format;
 } qlora_nf4dq_t;
 
-/* Bytes of the three buffers of a [d_out, d_in] tensor (mu is always 4 bytes).
+/* Bytes of the three buffers of a [d_out, d_in] tensor (mu is always 4 bytes): 4 bits per
+ * weight, one 8-bit constant per block of 64 and one FP32 constant per group of 256 blocks,
+ * the 0.5 + 0.127 bits of overhead worked out on "QLoRA: Quantize Base Weights to 4-Bit",
+ * Section 2 "2. Double Quantization" (and "QLoRA -- Fine-Tuning a 65B Model on One GPU",
+ * "Double quantization: the constants are not free").
  * Host only.  Errors: INVALID_ARG (null outputs), BAD_SHAPE. */
 int qlora_quant_sizes(int64_t d_out, int64_t d_in, size_t *codes_bytes, size_t *code8_bytes,
                       size_t *c2s_bytes);
@@ -113,12 +130,21 @@ int qlora_format_sizes(int64_t d_out, int64_t d_in, int dq_format, size_t *codes
                        size_t *code8_bytes, size_t *c2s_bytes);
 
 /* Workspace bytes needed by one call of `op` (QLORA_OP_*) at these sizes, for E4M3
- * constants (qlora_workspace_size) or the given second-level format.  Host only. */
+ * constants (qlora_workspace_size) or the given second-level format.  The count includes the
+ * QLORA_WS_COUNTER_BYTES head.  Host only.
+ * Errors: INVALID_ARG (null output, unknown op, M or r out of range), BAD_SHAPE, UNSUPPORTED. */
 enum qlora_op { QLORA_OP_QUANTIZE = 0, QLORA_OP_FWD = 1, QLORA_OP_BWD = 2 };
 int qlora_workspace_size(int op, int64_t M, int64_t d_out, int64_t d_in, int32_t r,
                          size_t *ws_bytes);
 int qlora_workspace_size_fmt(int op, int64_t M, int64_t d_out, int64_t d_in, int32_t r,
                              int dq_format, size_t *ws_bytes);
+
+/* Zero the counter head of a workspace (device memory of ws_bytes >= QLORA_WS_COUNTER_BYTES
+ * bytes) on `stream`, so it is ready for its first use; the rest is left as it is.  Needed
+ * once per workspace unless it was allocated zero-filled.  Uses a fill kernel, not a memset,
+ * so it may also be captured in a HIP graph.  No synchronization.
+ * Errors: INVALID_ARG (null pointer), WORKSPACE (ws_bytes too small), HIP. */
+int qlora_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* The FP32 NF4 table the library uses (host memory, 16 floats), built from the
  * normal-quantile formula of "QLoRA: Quantize Base Weights to 4-Bit", Section 2
@@ -132,7 +158,10 @@ int qlora_nf4_codebook(float out16[16]);
 int qlora_codebook(int codebook, float out16[16]);
 
 /* Quantize FP32 weights W (device, [d_out, d_in], d_in % 64 == 0) into *Wq, whose
- * buffers the caller allocated.  First level: c1 = max|w| per 64-block, code = nearest
+ * buffers the caller allocated ("QLoRA -- Fine-Tuning a 65B Model on One GPU", "Quantization
+ * in one paragraph" for the absmax blocks and the nearest level, "NF4" for the table;
+ * "QLoRA: Quantize Base Weights to 4-Bit", Section 2 "2. Double Quantization" for the
+ * second level).  First level: c1 = max|w| per 64-block, code = nearest
  * level of Wq->codebook to fl32(w / c1), ties to the lower level; an all-zero block gets
  * the level nearest 0 (the zero level of NF4).
  * Double quantization: mu = FP32 of the exact mean of all c1; d = fl32(c1 - mu); per group
@@ -158,7 +187,11 @@ int qlora_quantize_bf16(const uint16_t *W, const qlora_nf4dq_t *Wq, float *host_
 
 /* Dequantize to BF16 (device uint16[d_out, d_in]), bit-exact:
  *   c1_hat = fl32(fl32(E4M3(code8) * c2s) + mu),  w_hat = bf16_rne(fl32(q[code] * c1_hat)).
- * For export and tests; the linear entry points decode on chip instead.
+ * A lookup times the recovered block constant ("QLoRA -- Fine-Tuning a 65B Model on One
+ * GPU", "Quantization in one paragraph"), after undoing the second level ("QLoRA: Quantize
+ * Base Weights to 4-Bit", Section 2 "2. Double Quantization"), rounded to the BF16 compute
+ * type (same page, Section 3).  For export and tests; the linear entry points decode as part
+ * of their own kernels.
  * Errors: INVALID_ARG, BAD_SHAPE, UNSUPPORTED, HIP. */
 int qlora_dequantize(const qlora_nf4dq_t *Wq, uint16_t *W_bf16, hipStream_t stream);
 
@@ -183,7 +216,10 @@ int qlora_merge(const qlora_nf4dq_t *Wq, const uint16_t *A, const uint16_t *B, i
  *   Y [M, d_out]: device BF16 output (overwritten).
  *   T_save [M, r]: device BF16, receives bf16(T) for the backward; may be NULL.
  *   ws: device workspace of qlora_workspace_size(QLORA_OP_FWD) bytes.
- * M <= 16 runs a weight-streaming kernel; larger M runs the fused dequant MFMA GEMM.
+ * M <= 16 runs one weight-streaming launch that decodes the 4-bit codes on chip; 16 < M <
+ * 1024 runs the fused GEMM that decodes each weight tile on chip; M >= 1024 (and any M for
+ * second-level formats other than E4M3) first decodes the weight once into a BF16 copy in the
+ * workspace (2 d_out d_in bytes), then runs a plain BF16 MFMA GEMM over it.
  * Errors: INVALID_ARG, BAD_SHAPE, UNSUPPORTED, WORKSPACE, HIP. */
 int qlora_linear_fwd(const qlora_nf4dq_t *Wq, const uint16_t *X, int64_t M, const uint16_t *A,
                      const uint16_t *B, int32_t r, float alpha, uint16_t *Y, uint16_t *T_save,
@@ -239,13 +275,17 @@ int qlora_mlp_bwd(const qlora_nf4dq_t *Wg, const qlora_nf4dq_t *Wu, const qlora_
                   const uint16_t *U_saved, uint16_t *dX, uint16_t *const *dA, uint16_t *const *dB,
                   void *ws, size_t ws_bytes, hipStream_t stream);
 
-/* Backward of qlora_linear_fwd.  With G = dY B:
+/* Backward of qlora_linear_fwd ("QLoRA -- Fine-Tuning a 65B Model on One GPU", "Where the
+ * gradients actually go": the input gradient flows through the dequantized weights, only A
+ * and B receive gradients, the 4-bit tensor is never written).  With G = dY B:
  *   dX = dY w_hat + (alpha/r) G A      [M, d_in]   (may be NULL: not computed)
  *   dA = (alpha/r) G^T X               [r, d_in]
  *   dB = (alpha/r) dY^T T, T = X A^T   [d_out, r]
  * dY [M, d_out], X, A, B: device BF16 inputs.  T_saved: device BF16 [M, r] from the
  * forward, or NULL to recompute it.  Outputs are device BF16 and overwritten (not
- * accumulated).  The quantized weights are only read.
+ * accumulated).  The quantized weights are only read.  dX runs as the forward does: the
+ * fused transposed-tile GEMM below 1024 tokens, else the transposed BF16 copy in the
+ * workspace and the plain BF16 GEMM.
  * Errors: INVALID_ARG, BAD_SHAPE, UNSUPPORTED, WORKSPACE, HIP. */
 int qlora_linear_bwd(const qlora_nf4dq_t *Wq, const uint16_t *X, const uint16_t *dY, int64_t M,
                      const uint16_t *A, const uint16_t *B, int32_t r, float alpha,

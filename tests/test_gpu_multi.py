@@ -79,14 +79,14 @@ def test_grouped_stream_matches_oracle(gpu_lib, dims, K, M, r):
 def test_grouped_stream_is_deterministic_and_replays(gpu_lib):
     """Two eager calls and three HIP-graph replays (new inputs copied in between) give the
     same bits: the group's arrival counters reset themselves."""
-    from bit_nf4_quantized_dq_amd import linear_fwd_multi, quantize, workspace_size_multi
+    from bit_nf4_quantized_dq_amd import linear_fwd_multi, new_workspace, quantize, workspace_size_multi
 
     dims, K, M, r = [8192, 1024, 1024], 4096, 1, 16
     X, Ws, As, Bs = _group(11, dims, K, M, r)
     qs = [quantize(W.cuda()) for W in Ws]
     Xd, Ad, Bd = X.cuda(), [a.cuda() for a in As], [b.cuda() for b in Bs]
     Ys = [torch.empty(M, N, dtype=torch.bfloat16, device="cuda") for N in dims]
-    ws = torch.empty(workspace_size_multi(qs, M, r), dtype=torch.uint8, device="cuda")
+    ws = new_workspace(workspace_size_multi(qs, M, r), "cuda")
     first = [y.clone() for y in linear_fwd_multi(qs, Xd, Ad, Bd, 32.0, Ys=Ys, ws=ws)]
     linear_fwd_multi(qs, Xd, Ad, Bd, 32.0, Ys=Ys, ws=ws)
     torch.cuda.synchronize()

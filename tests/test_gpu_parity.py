@@ -368,7 +368,7 @@ def test_weight_stream_graph_replay(gpu_lib):
     """The M <= 16 path captured in a HIP graph and replayed with new inputs in between:
     every replay equals an eager call on the same inputs (the split-K arrival counters
     carry no per-call host state)."""
-    from bit_nf4_quantized_dq_amd import QuantizedWeight, linear_fwd, quantize, workspace_size, OP_FWD
+    from bit_nf4_quantized_dq_amd import QuantizedWeight, linear_fwd, new_workspace, quantize, workspace_size, OP_FWD
 
     dev = torch.device("cuda")
     shapes = [(1040, 4096, 1, 16), (272, 320, 16, 16), (4096, 4096, 16, 16), (8192, 4096, 1, 16)]
@@ -379,7 +379,7 @@ def test_weight_stream_graph_replay(gpu_lib):
         X = c["X"].to(dev)
         A, B = c["A"].to(dev), c["B"].to(dev)
         Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-        ws = torch.empty(workspace_size(OP_FWD, M, N, K, r), dtype=torch.uint8, device=dev)
+        ws = new_workspace(workspace_size(OP_FWD, M, N, K, r), dev)
         cases.append((q, X, A, B, Y, ws))
     for q, X, A, B, Y, ws in cases:  # warm-up outside the capture
         linear_fwd(q, X, A, B, 32.0, Y=Y, ws=ws)

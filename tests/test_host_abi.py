@@ -24,7 +24,7 @@ def L():
 def test_every_declared_symbol_is_exported(L):
     text = open(HEADER).read()
     names = sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text)))
-    assert len(names) == 22
+    assert len(names) == 23
     for n in names:
         assert hasattr(L, n), n
 
@@ -59,6 +59,13 @@ def test_shape_and_argument_errors_before_launch(L):
     assert L.qlora_linear_fwd(ctypes.byref(_wq(d_out=250)), dummy, 4, dummy, dummy, 8, 16.0, dummy, None, ws, 1 << 20, None) == -2
     assert L.qlora_linear_fwd(ctypes.byref(_wq(b1=32)), dummy, 4, dummy, dummy, 8, 16.0, dummy, None, ws, 1 << 20, None) == -3
     assert L.qlora_linear_fwd(ctypes.byref(_wq()), dummy, 0, dummy, dummy, 8, 16.0, dummy, None, ws, 1 << 20, None) == -1
+    # M below 2^24: [M, r] operands stay within the 4 GiB reach of a buffer descriptor
+    assert L.qlora_linear_fwd(ctypes.byref(_wq()), dummy, 1 << 24, dummy, dummy, 8, 16.0, dummy, None, ws, 1 << 40, None) == -1
+    assert L.qlora_linear_bwd(ctypes.byref(_wq()), dummy, dummy, 1 << 24, dummy, dummy, 8, 16.0, None, dummy, dummy, dummy,
+                              ws, 1 << 40, None) == -1
+    # the workspace: misaligned is an argument error, too small a workspace error
+    assert L.qlora_linear_fwd(ctypes.byref(_wq()), dummy, 4, dummy, dummy, 8, 16.0, dummy, None, ctypes.c_void_p(8200),
+                              1 << 20, None) == -1
     assert L.qlora_linear_fwd(ctypes.byref(_wq()), dummy, 4, dummy, dummy, 0, 16.0, dummy, None, ws, 1 << 20, None) == -1
     assert L.qlora_linear_fwd(ctypes.byref(_wq()), dummy, 4, dummy, dummy, 129, 16.0, dummy, None, ws, 1 << 20, None) == -1
     assert L.qlora_linear_fwd(ctypes.byref(_wq()), dummy, 4, dummy, dummy, 8, float("nan"), dummy, None, ws, 1 << 20, None) == -1
@@ -105,6 +112,18 @@ def test_shape_and_argument_errors_before_launch(L):
     assert adamw(p=ctypes.c_void_p(4098)) == -1
     assert adamw(lr=-1.0) == -1 and adamw(lr=float("nan")) == -1 and adamw(b1=1.0) == -1 and adamw(b2=-0.1) == -1
     assert adamw(eps=0.0) == -1 and adamw(wd=-0.5) == -1 and adamw(wd=float("inf")) == -1
+
+
+def test_workspace_head_and_init_errors(L):
+    """Every workspace starts with the counter head: sizes include it, the init call checks
+    its arguments before any launch."""
+    head = 524288
+    n = ctypes.c_size_t()
+    for op in (0, 1, 2):
+        assert L.qlora_workspace_size(op, 4, 256, 256, 8, ctypes.byref(n)) == 0 and n.value > head
+    assert L.qlora_workspace_init(None, 1 << 20, None) == -1
+    assert L.qlora_workspace_init(ctypes.c_void_p(8200), 1 << 20, None) == -1
+    assert L.qlora_workspace_init(ctypes.c_void_p(8192), head - 1, None) == -5
 
 
 def test_grouped_forward_errors_before_launch(L):
@@ -161,6 +180,20 @@ def test_mlp_block_errors_before_launch(L):
                            None, None, ws, 1 << 30, None) == -1
     assert L.qlora_mlp_fwd(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), dummy, 64, ptrs, ptrs, 8, 16.0, dummy,
                            None, None, ws, 16, None) == -5
+    # every adapter pointer is checked before the first launch: a missing or misaligned A[2]
+    # (the down projection's, used last) and a missing dA[1] fail up front
+    late = VP(dummy, dummy, None)
+    assert L.qlora_mlp_fwd(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), dummy, 64, late, ptrs, 8, 16.0, dummy,
+                           None, None, ws, 1 << 30, None) == -1
+    odd = VP(dummy, dummy, ctypes.c_void_p(4098))
+    assert L.qlora_mlp_fwd(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), dummy, 64, odd, ptrs, 8, 16.0, dummy,
+                           None, None, ws, 1 << 30, None) == -1
+    assert L.qlora_mlp_fwd(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), dummy, 64, ptrs, ptrs, 8, 16.0,
+                           ctypes.c_void_p(4098), None, None, ws, 1 << 30, None) == -1  # Y misaligned
+    assert L.qlora_mlp_bwd(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), dummy, dummy, 64, ptrs, ptrs, 8, 16.0,
+                           None, None, dummy, ptrs, VP(dummy, None, dummy), ws, 1 << 30, None) == -1
+    assert L.qlora_mlp_bwd(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), dummy, ctypes.c_void_p(4098), 64, ptrs,
+                           ptrs, 8, 16.0, None, None, dummy, ptrs, ptrs, ws, 1 << 30, None) == -1  # dY misaligned
     # G and U saved together or not at all
     assert L.qlora_mlp_bwd(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), dummy, dummy, 64, ptrs, ptrs, 8, 16.0,
                            dummy, None, dummy, ptrs, ptrs, ws, 1 << 30, None) == -1
@@ -221,3 +254,78 @@ def test_workspace_grows_for_decode_once_formats():
     base = B.workspace_size(B.OP_FWD, 1, 4096, 4096, 16, "e4m3")
     for dq in ("e5m2", "int8", "none"):
         assert B.workspace_size(B.OP_FWD, 1, 4096, 4096, 16, dq) >= 2 * 4096 * 4096 > base
+
+
+# ------------------------------------------------------------------ binding checks (no GPU)
+
+
+def _cpu_weight(d_out=256, d_in=256):
+    import torch
+
+    from bit_nf4_quantized_dq_amd import QuantizedWeight
+
+    nc, n8, n2 = B.quant_sizes(d_out, d_in)
+    return QuantizedWeight(torch.zeros(nc, dtype=torch.uint8), torch.zeros(n8, dtype=torch.uint8),
+                           torch.zeros(n2 // 4), torch.zeros(1), d_out, d_in)
+
+
+def test_binding_rejects_mis_shaped_operands_before_any_call():
+    """The C ABI sees raw pointers only, so the binding checks every tensor's shape against the
+    weight, M and r first: a wrong shape is reported by name (CPU tensors: every shape and
+    dtype is checked before the device), and right shapes get as far as the device check."""
+    import torch
+
+    bf = torch.bfloat16
+    q = _cpu_weight(256, 512)
+    M, r = 4, 8
+    X, A, Bm = torch.zeros(M, 512, dtype=bf), torch.zeros(r, 512, dtype=bf), torch.zeros(256, r, dtype=bf)
+    dY = torch.zeros(M, 256, dtype=bf)
+    cases = [
+        (lambda: B.linear_fwd(q, torch.zeros(M, 256, dtype=bf), A, Bm, 16.0), "X"),
+        (lambda: B.linear_fwd(q, X, torch.zeros(r, 256, dtype=bf), Bm, 16.0), "A"),
+        (lambda: B.linear_fwd(q, X, A, torch.zeros(512, r, dtype=bf), 16.0), "B"),
+        (lambda: B.linear_fwd(q, X, A, torch.zeros(256, r + 1, dtype=bf), 16.0), "B"),
+        (lambda: B.linear_fwd(q, X, A, Bm, 16.0, Y=torch.zeros(M, 512, dtype=bf)), "Y"),
+        (lambda: B.linear_fwd(q, X, A, Bm, 16.0, T_save=torch.zeros(M, r + 1, dtype=bf)), "T_save"),
+        (lambda: B.linear_fwd(q, X.float(), A, Bm, 16.0), "X"),
+        (lambda: B.linear_bwd(q, X, torch.zeros(M, 512, dtype=bf), A, Bm, 16.0), "dY"),
+        (lambda: B.linear_bwd(q, X, dY, A, Bm, 16.0, T_saved=torch.zeros(M + 1, r, dtype=bf)), "T_saved"),
+        (lambda: B.linear_bwd(q, X, dY, A, Bm, 16.0, dX=torch.zeros(M, 256, dtype=bf)), "dX"),
+        (lambda: B.linear_bwd(q, X, dY, A, Bm, 16.0, dA=torch.zeros(r, 256, dtype=bf)), "dA"),
+        (lambda: B.linear_bwd(q, X, dY, A, Bm, 16.0, dB=torch.zeros(r, 256, dtype=bf)), "dB"),
+        (lambda: B.merge(q, A, Bm, 16.0, out=torch.zeros(512, 256, dtype=bf)), "out"),
+        (lambda: B.dequantize(q, out=torch.zeros(256, 256, dtype=bf)), "out"),
+        (lambda: B.linear_fwd(_cpu_weight(256, 512).__class__(q.codes[:-1], q.code8, q.c2s, q.mu, 256, 512), X, A, Bm,
+                              16.0), "weight.codes"),
+        (lambda: B.linear_fwd_multi([q, q], X, [A, A], [Bm, torch.zeros(256, r - 1, dtype=bf)], 16.0), "B[1]"),
+        (lambda: B.linear_fwd_multi([q, q], X, [A], [Bm, Bm], 16.0), "one A"),
+    ]
+    for fn, name in cases:
+        with pytest.raises(ValueError, match=re.escape(name)):
+            fn()
+    # correctly shaped host tensors pass the shape checks and stop at the device check
+    with pytest.raises(ValueError, match="CUDA"):
+        B.linear_fwd(q, X, A, Bm, 16.0)
+    with pytest.raises(ValueError, match="CUDA"):
+        B.linear_bwd(q, X, dY, A, Bm, 16.0)
+
+
+def test_binding_rejects_mis_shaped_mlp_operands():
+    import torch
+
+    bf = torch.bfloat16
+    d, f, M, r = 256, 512, 4, 8
+    qs = [_cpu_weight(f, d), _cpu_weight(f, d), _cpu_weight(d, f)]
+    As = [torch.zeros(r, d, dtype=bf), torch.zeros(r, d, dtype=bf), torch.zeros(r, f, dtype=bf)]
+    Bs = [torch.zeros(f, r, dtype=bf), torch.zeros(f, r, dtype=bf), torch.zeros(d, r, dtype=bf)]
+    X, dY = torch.zeros(M, d, dtype=bf), torch.zeros(M, d, dtype=bf)
+    with pytest.raises(ValueError, match=re.escape("A[2]")):
+        B.mlp_fwd(qs, X, As[:2] + [torch.zeros(r, d, dtype=bf)], Bs, 16.0)
+    with pytest.raises(ValueError, match="G_save"):
+        B.mlp_fwd(qs, X, As, Bs, 16.0, G_save=torch.zeros(M, d, dtype=bf))
+    with pytest.raises(ValueError, match="U_saved"):
+        B.mlp_bwd(qs, X, dY, As, Bs, 16.0, G_saved=torch.zeros(M, f, dtype=bf), U_saved=torch.zeros(M, f))
+    with pytest.raises(ValueError, match="both"):
+        B.mlp_bwd(qs, X, dY, As, Bs, 16.0, G_saved=torch.zeros(M, f, dtype=bf))
+    with pytest.raises(ValueError, match="CUDA"):
+        B.mlp_bwd(qs, X, dY, As, Bs, 16.0)
