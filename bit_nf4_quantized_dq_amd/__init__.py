@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     adamw_step,
     dequantize,
     linear_fwd,
+    linear_fwd_noalloc,
     linear_fwd_multi,
     mlp_fwd,
     mlp_bwd,

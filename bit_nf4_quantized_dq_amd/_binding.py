@@ -80,6 +80,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
         "qlora_dequantize": (P(_Nf4dq), vp, vp),
         "qlora_merge": (P(_Nf4dq), vp, vp, i32, ctypes.c_float, vp, vp),
         "qlora_linear_fwd": (P(_Nf4dq), vp, i64, vp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp),
+        "qlora_linear_fwd_noalloc": (P(_Nf4dq), vp, i64, vp, vp, i32, ctypes.c_float, vp, vp, vp),
         "qlora_linear_bwd": (P(_Nf4dq), vp, vp, i64, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp),
         "qlora_workspace_size_multi": (ctypes.c_int, P(P(_Nf4dq)), i64, i32, P(sz)),
         "qlora_linear_fwd_multi": (ctypes.c_int, P(P(_Nf4dq)), vp, i64, P(vp), P(vp), i32, ctypes.c_float, P(vp),
@@ -373,6 +374,24 @@ def linear_fwd(q: QuantizedWeight, X: torch.Tensor, A: torch.Tensor, B: torch.Te
     _check(load_library().qlora_linear_fwd(ctypes.byref(s), X.data_ptr(), M, A.data_ptr(), B.data_ptr(), r,
                                            float(alpha), Y.data_ptr(), _ptr(T_save), ws.data_ptr(), ws.numel(),
                                            _stream(X)), "linear_fwd")
+    return Y
+
+
+def linear_fwd_noalloc(q: QuantizedWeight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor, alpha: float,
+                       Y: torch.Tensor, T_save: torch.Tensor | None = None) -> torch.Tensor:
+    """linear_fwd on the library's fixed per-device scratch: no workspace, and no allocation
+    anywhere in the call (Y must be given).  Refused (status -7) when the call needs more than
+    QLORA_NOALLOC_SCRATCH_BYTES; calls that overlap on one device race."""
+    M, r, dev = _tokens(X), _rank(A), X.device
+    specs = _weight_specs(q) + [(X, torch.bfloat16, "X", (M, q.d_in)), (A, torch.bfloat16, "A", (r, q.d_in)),
+                                (B, torch.bfloat16, "B", (q.d_out, r)), (Y, torch.bfloat16, "Y", (M, q.d_out))]
+    if T_save is not None:
+        specs.append((T_save, torch.bfloat16, "T_save", (M, r)))
+    _validate(specs, dev)
+    s = q.struct()
+    _check(load_library().qlora_linear_fwd_noalloc(ctypes.byref(s), X.data_ptr(), M, A.data_ptr(), B.data_ptr(), r,
+                                                   float(alpha), Y.data_ptr(), _ptr(T_save), _stream(X)),
+           "linear_fwd_noalloc")
     return Y
 
 

@@ -291,7 +291,15 @@ TimingState& timing() {
 
 namespace qlora {
 
+namespace {
+thread_local int t_timing_off = 0;
+}  // namespace
+
+TimingOff::TimingOff() { ++t_timing_off; }
+TimingOff::~TimingOff() { --t_timing_off; }
+
 LaunchTimer::LaunchTimer(int kernel_id, hipStream_t) {
+  if (t_timing_off) return;
   TimingState& T = timing();
   std::lock_guard<std::mutex> lk(T.mu);
   if (kernel_id < 0 || kernel_id >= QLORA_K_COUNT || !((T.mask >> kernel_id) & 1)) return;
@@ -314,6 +322,71 @@ LaunchTimer::LaunchTimer(int kernel_id, hipStream_t) {
 
 }  // namespace qlora
 
+namespace qlora {
+
+int fwd_validate(const qlora_nf4dq_t* Wq, const uint16_t* X, int64_t M, const uint16_t* A, const uint16_t* B,
+                 int32_t r, float alpha, const uint16_t* Y) {
+  int st = check_wq(Wq);
+  if (st) return st;
+  if ((st = check_lora(M, r, alpha))) return st;
+  if (!X || !A || !B || !Y || !aligned16(X) || !aligned16(A) || !aligned16(Y)) return QLORA_ERR_INVALID_ARG;
+  if (M <= kGemvMaxM && !decode_once(M, Wq->dq_format)) {
+    const int64_t N = Wq->d_out, K = Wq->d_in;
+    // one arrival counter per row group of the launch, in the workspace head
+    if ((gemv_stream_fits(N, K, M, r) ? gemv_stream_plan(N, K, M, r).groups : gemv_groups(N)) > kHeadWords)
+      return QLORA_ERR_BAD_SHAPE;
+  }
+  return QLORA_OK;
+}
+
+size_t fwd_workspace_bytes(int64_t M, int64_t d_out, int64_t d_in, int32_t r, int dq) {
+  return fwd_ws(M, d_out, d_in, r, dq).total;
+}
+
+int fwd_enqueue(const qlora_nf4dq_t* Wq, const uint16_t* X, int64_t M, const uint16_t* A, const uint16_t* B,
+                int32_t r, float alpha, uint16_t* Y, uint16_t* T_save, void* ws, hipStream_t stream) {
+  const int64_t N = Wq->d_out, K = Wq->d_in;
+  const int dq = Wq->dq_format;
+  const FwdWs L = fwd_ws(M, N, K, r, dq);
+  char* base = static_cast<char*>(ws);
+  const float s = alpha / (float)r;
+  const uint32_t* codes = reinterpret_cast<const uint32_t*>(Wq->codes);
+  float* tpart = reinterpret_cast<float*>(base + L.tpart);
+  if (M <= kGemvMaxM && !decode_once(M, dq)) {
+    float* ypart = reinterpret_cast<float*>(base + L.ypart);
+    if (gemv_stream_fits(N, K, M, r))
+      return hip_status(launch_gemv_stream(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, X, M, A, B, r, s, Y, T_save,
+                                           ypart, tpart, head_counters(ws), tables_of(Wq), stream));
+    return hip_status(launch_gemv_fwd(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, X, M, A, B, r, s, Y, T_save, ypart,
+                                      tpart, head_counters(ws), tables_of(Wq), stream));
+  }
+  // T = X A^T: s T (BF16) feeds the adapter slices of the GEMM; T itself is saved if asked
+  uint16_t* ls = reinterpret_cast<uint16_t*>(base + L.ls);
+  hipError_t e;
+  if (decode_once(M, dq)) {
+    uint16_t* wcopy = reinterpret_cast<uint16_t*>(base + L.wcopy);
+    if (dq == QLORA_DQ_E4M3) {  // T and the decoded copy in one launch
+      if ((e = launch_fwd_prologue(X, A, M, r, K, s, ls, T_save, codes, Wq->code8, Wq->c2s, Wq->mu, N, wcopy,
+                                   tables_of(Wq), stream)) != hipSuccess)
+        return QLORA_ERR_HIP;
+    } else {
+      if ((e = launch_lora_down(X, A, 0, M, r, K, s, ls, T_save, stream)) != hipSuccess) return QLORA_ERR_HIP;
+      if ((e = launch_dequant(codes, Wq->code8, Wq->c2s, Wq->mu, wcopy, N * K / 8, tables_of(Wq), dq, stream)) !=
+          hipSuccess)
+        return QLORA_ERR_HIP;
+    }
+    // Y = X w_hat^T + (s T) B^T: A = w_hat [N, K], Wl = B [N, r] (f*r + j)
+    e = launch_gemm_nt(wcopy, N, X, M, K, B, r, 1, ls, r, Y, QLORA_K_GEMM_FWD, stream,
+                       L.gsplit > 1 ? reinterpret_cast<float*>(base + L.gpart) : nullptr, L.gsplit > 1 ? L.gsplit : 1);
+    return hip_status(e);
+  }
+  if ((e = launch_lora_down(X, A, 0, M, r, K, s, ls, T_save, stream)) != hipSuccess) return QLORA_ERR_HIP;
+  e = launch_gemm_fwd(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, X, M, ls, B, r, Y, tables_of(Wq), stream);
+  return hip_status(e);
+}
+
+}  // namespace qlora
+
 extern "C" {
 
 const char* qlora_strerror(int status) {
@@ -325,6 +398,7 @@ const char* qlora_strerror(int status) {
     case QLORA_ERR_NONFINITE: return "non-finite weight";
     case QLORA_ERR_WORKSPACE: return "workspace too small";
     case QLORA_ERR_HIP: return "HIP runtime error";
+    case QLORA_ERR_SCRATCH: return "needs more than the fixed scratch of the no-allocation forward";
     default: return "unknown status";
   }
 }
@@ -466,52 +540,10 @@ int qlora_merge(const qlora_nf4dq_t* Wq, const uint16_t* A, const uint16_t* B, i
 int qlora_linear_fwd(const qlora_nf4dq_t* Wq, const uint16_t* X, int64_t M, const uint16_t* A, const uint16_t* B,
                      int32_t r, float alpha, uint16_t* Y, uint16_t* T_save, void* ws, size_t ws_bytes,
                      hipStream_t stream) {
-  int st = check_wq(Wq);
+  int st = qlora::fwd_validate(Wq, X, M, A, B, r, alpha, Y);
   if (st) return st;
-  if ((st = check_lora(M, r, alpha))) return st;
-  if (!X || !A || !B || !Y || !aligned16(X) || !aligned16(A) || !aligned16(Y)) return QLORA_ERR_INVALID_ARG;
-  const int64_t N = Wq->d_out, K = Wq->d_in;
-  const int dq = Wq->dq_format;
-  const FwdWs L = fwd_ws(M, N, K, r, dq);
-  if ((st = check_ws(ws, ws_bytes, L.total))) return st;
-  char* base = static_cast<char*>(ws);
-  const float s = alpha / (float)r;
-  const uint32_t* codes = reinterpret_cast<const uint32_t*>(Wq->codes);
-  float* tpart = reinterpret_cast<float*>(base + L.tpart);
-  if (M <= kGemvMaxM && !decode_once(M, dq)) {
-    float* ypart = reinterpret_cast<float*>(base + L.ypart);
-    const bool big = gemv_stream_fits(N, K, M, r);
-    // one arrival counter per row group of the launch, in the workspace head
-    if ((big ? gemv_stream_plan(N, K, M, r).groups : gemv_groups(N)) > kHeadWords) return QLORA_ERR_BAD_SHAPE;
-    if (big)
-      return hip_status(launch_gemv_stream(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, X, M, A, B, r, s, Y, T_save,
-                                           ypart, tpart, head_counters(ws), tables_of(Wq), stream));
-    return hip_status(launch_gemv_fwd(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, X, M, A, B, r, s, Y, T_save, ypart,
-                                      tpart, head_counters(ws), tables_of(Wq), stream));
-  }
-  // T = X A^T: s T (BF16) feeds the adapter slices of the GEMM; T itself is saved if asked
-  uint16_t* ls = reinterpret_cast<uint16_t*>(base + L.ls);
-  hipError_t e;
-  if (decode_once(M, dq)) {
-    uint16_t* wcopy = reinterpret_cast<uint16_t*>(base + L.wcopy);
-    if (dq == QLORA_DQ_E4M3) {  // T and the decoded copy in one launch
-      if ((e = launch_fwd_prologue(X, A, M, r, K, s, ls, T_save, codes, Wq->code8, Wq->c2s, Wq->mu, N, wcopy,
-                                   tables_of(Wq), stream)) != hipSuccess)
-        return QLORA_ERR_HIP;
-    } else {
-      if ((e = launch_lora_down(X, A, 0, M, r, K, s, ls, T_save, stream)) != hipSuccess) return QLORA_ERR_HIP;
-      if ((e = launch_dequant(codes, Wq->code8, Wq->c2s, Wq->mu, wcopy, N * K / 8, tables_of(Wq), dq, stream)) !=
-          hipSuccess)
-        return QLORA_ERR_HIP;
-    }
-    // Y = X w_hat^T + (s T) B^T: A = w_hat [N, K], Wl = B [N, r] (f*r + j)
-    e = launch_gemm_nt(wcopy, N, X, M, K, B, r, 1, ls, r, Y, QLORA_K_GEMM_FWD, stream,
-                       L.gsplit > 1 ? reinterpret_cast<float*>(base + L.gpart) : nullptr, L.gsplit > 1 ? L.gsplit : 1);
-    return hip_status(e);
-  }
-  if ((e = launch_lora_down(X, A, 0, M, r, K, s, ls, T_save, stream)) != hipSuccess) return QLORA_ERR_HIP;
-  e = launch_gemm_fwd(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, X, M, ls, B, r, Y, tables_of(Wq), stream);
-  return hip_status(e);
+  if ((st = check_ws(ws, ws_bytes, fwd_ws(M, Wq->d_out, Wq->d_in, r, Wq->dq_format).total))) return st;
+  return qlora::fwd_enqueue(Wq, X, M, A, B, r, alpha, Y, T_save, ws, stream);
 }
 
 int qlora_workspace_size_multi(int count, const qlora_nf4dq_t* const* Wq, int64_t M, int32_t r, size_t* ws_bytes) {

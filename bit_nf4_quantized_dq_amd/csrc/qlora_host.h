@@ -7,6 +7,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "qlora.h"
 #include "qlora_tables.h"
 
 namespace qlora {
@@ -25,6 +26,20 @@ struct LaunchTimer {
   hipEvent_t start = nullptr;
   hipEvent_t stop = nullptr;
 };
+// While one of these lives on a thread, launches made by that thread carry no timing events
+// (creating them allocates): the entry point that allocates nothing holds one.
+struct TimingOff {
+  TimingOff();
+  ~TimingOff();
+};
+
+// ---- the forward entry point in two steps (api.cpp): every argument check, then the
+// launches on a workspace of at least fwd_workspace_bytes() whose counter head is zero.
+int fwd_validate(const qlora_nf4dq_t* Wq, const uint16_t* X, int64_t M, const uint16_t* A, const uint16_t* B,
+                 int32_t r, float alpha, const uint16_t* Y);
+size_t fwd_workspace_bytes(int64_t M, int64_t d_out, int64_t d_in, int32_t r, int dq);
+int fwd_enqueue(const qlora_nf4dq_t* Wq, const uint16_t* X, int64_t M, const uint16_t* A, const uint16_t* B,
+                int32_t r, float alpha, uint16_t* Y, uint16_t* T_save, void* ws, hipStream_t stream);
 
 // ---- quantize / dequantize (quantize.hip, dequant.hip)
 hipError_t launch_quant_pass1(const void* W, bool w_bf16, uint32_t* codes, float* c1, unsigned long long* hist,

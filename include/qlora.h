@@ -53,6 +53,9 @@ extern "C" {
  * 64-column tile of dA and of dB, each dimension at most 2^22). */
 #define QLORA_WS_COUNTER_BYTES ((size_t)524288)
 
+/* Bytes of the fixed per-device scratch of qlora_linear_fwd_noalloc (16 MiB). */
+#define QLORA_NOALLOC_SCRATCH_BYTES ((size_t)16777216)
+
 enum qlora_status {
   QLORA_OK = 0,
   QLORA_ERR_INVALID_ARG = -1, /* null or misaligned pointer, M outside [1, 2^24), r outside
@@ -62,7 +65,9 @@ enum qlora_status {
   QLORA_ERR_UNSUPPORTED = -3, /* block sizes other than (64, 256), unknown codebook or format */
   QLORA_ERR_NONFINITE = -4,   /* NaN or Inf in the weights given to qlora_quantize */
   QLORA_ERR_WORKSPACE = -5,   /* workspace pointer null or smaller than required */
-  QLORA_ERR_HIP = -6          /* a HIP runtime call or kernel launch failed */
+  QLORA_ERR_HIP = -6,         /* a HIP runtime call or kernel launch failed */
+  QLORA_ERR_SCRATCH = -7      /* the call needs more than the fixed scratch of the no-allocation
+                                 entry point */
 };
 
 /* First-level codebooks: the 16 levels a 4-bit code indexes ("QLoRA: Quantize Base Weights
@@ -224,6 +229,26 @@ int qlora_merge(const qlora_nf4dq_t *Wq, const uint16_t *A, const uint16_t *B, i
 int qlora_linear_fwd(const qlora_nf4dq_t *Wq, const uint16_t *X, int64_t M, const uint16_t *A,
                      const uint16_t *B, int32_t r, float alpha, uint16_t *Y, uint16_t *T_save,
                      void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* qlora_linear_fwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  Same arguments, results and
+ * errors as qlora_linear_fwd, minus the workspace: the call uses a fixed array of
+ * QLORA_NOALLOC_SCRATCH_BYTES that the library holds on each device until the process ends,
+ * and calls no hipMalloc, hipFree or other allocating routine (diagnostic timing events are
+ * not recorded for its launches).
+ *   Limit: calls whose workspace need (qlora_workspace_size_fmt, QLORA_OP_FWD) exceeds that
+ *   size return QLORA_ERR_SCRATCH before any launch.  That admits every M < 1024 at the
+ *   workload shapes (at most 12 MiB, 8192 x 28672 at M = 16); M >= 1024 needs the decoded
+ *   weight copy and is refused except for small weights.
+ *   Set-up: the first call on a device (with that device current) looks the array up and
+ *   zeroes its counter head on `stream`; make that first call outside graph capture.
+ *   Concurrency: every call on a device shares that device's array, which keeps the last
+ *   call's contents (the counter head is left zero), so calls that overlap on one device
+ *   race; serialize them (one stream, or events).
+ * Errors: as qlora_linear_fwd, SCRATCH instead of WORKSPACE. */
+int qlora_linear_fwd_noalloc(const qlora_nf4dq_t *Wq, const uint16_t *X, int64_t M,
+                             const uint16_t *A, const uint16_t *B, int32_t r, float alpha,
+                             uint16_t *Y, uint16_t *T_save, hipStream_t stream);
 
 /* The forward of several linears that read the same input, e.g. the q, k and v projections or
  * the gate and up projections of a decoder layer: for i < count,

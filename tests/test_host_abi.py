@@ -24,7 +24,7 @@ def L():
 def test_every_declared_symbol_is_exported(L):
     text = open(HEADER).read()
     names = sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text)))
-    assert len(names) == 23
+    assert len(names) == 24
     for n in names:
         assert hasattr(L, n), n
 
@@ -124,6 +124,19 @@ def test_workspace_head_and_init_errors(L):
     assert L.qlora_workspace_init(None, 1 << 20, None) == -1
     assert L.qlora_workspace_init(ctypes.c_void_p(8200), 1 << 20, None) == -1
     assert L.qlora_workspace_init(ctypes.c_void_p(8192), head - 1, None) == -5
+
+
+def test_noalloc_forward_errors_before_launch(L):
+    """The forward on the fixed scratch validates as qlora_linear_fwd does, and refuses a call
+    that needs more than its scratch (here the decoded 4096 x 4096 copy at M = 4096) with its
+    own status, before any launch or device lookup."""
+    dummy = ctypes.c_void_p(4096)
+    assert L.qlora_linear_fwd_noalloc(ctypes.byref(_wq(d_in=100)), dummy, 4, dummy, dummy, 8, 16.0, dummy, None, None) == -2
+    assert L.qlora_linear_fwd_noalloc(ctypes.byref(_wq()), dummy, 0, dummy, dummy, 8, 16.0, dummy, None, None) == -1
+    assert L.qlora_linear_fwd_noalloc(ctypes.byref(_wq()), None, 4, dummy, dummy, 8, 16.0, dummy, None, None) == -1
+    assert L.qlora_linear_fwd_noalloc(None, dummy, 4, dummy, dummy, 8, 16.0, dummy, None, None) == -1
+    big = _wq(d_out=4096, d_in=4096)
+    assert L.qlora_linear_fwd_noalloc(ctypes.byref(big), dummy, 4096, dummy, dummy, 16, 32.0, dummy, None, None) == -7
 
 
 def test_grouped_forward_errors_before_launch(L):
@@ -231,7 +244,7 @@ def test_workspace_sizes_are_sane():
 
 
 def test_strerror_covers_every_status(L):
-    for s in range(0, -7, -1):
+    for s in range(0, -8, -1):
         assert B._strerror(s) not in ("?", "unknown status")
 
 
