@@ -67,6 +67,42 @@ COUNTER_TRAFFIC = {
 
 
 EVENT_STEPS = 4  # timed steps whose GEMM launches carry HIP events
+WINDOWS = 20     # timed windows (step boundaries with events) for the median step time
+
+
+class HipEvents:
+    """Timing-only HIP events (no system-scope fence on record, so no L2 write-back around
+    them) from the HIP runtime this process already runs (the one torch loaded)."""
+
+    def __init__(self, n):
+        import ctypes
+
+        path = next((ln.split()[-1] for ln in open("/proc/self/maps") if "libamdhip64.so" in ln), None)
+        if path is None:
+            raise RuntimeError("HIP runtime not loaded")
+        self.L = ctypes.CDLL(path)
+        self.ct = ctypes
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.L.hipEventCreateWithFlags(ctypes.byref(e), ctypes.c_uint(0x20000000)) != 0:  # DisableSystemFence
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.ev.append(e)
+
+    def record(self, i, stream_ptr):
+        if self.L.hipEventRecord(self.ev[i], self.ct.c_void_p(stream_ptr)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, i, j):
+        f = self.ct.c_float()
+        self.L.hipEventSynchronize(self.ev[j])
+        if self.L.hipEventElapsedTime(self.ct.byref(f), self.ev[i], self.ev[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return f.value
+
+    def close(self):
+        for e in self.ev:
+            self.L.hipEventDestroy(e)
 
 
 def counter_traffic(kernel):
@@ -293,20 +329,95 @@ def seventy_b_model(dev, layers=80, passes=3):
     return out
 
 
-def cpu_baseline(N, K, r, alpha, target_s=15.0):
-    """The oracle as it stands, on the host cores: dequantize + fwd + bwd on a token sample."""
-    import numpy as np
+def weight_stream(copies, X_all, A, B, alpha, N, K, r, M, dev, replays=20):
+    """Forward of one linear at M tokens over rotated quantized copies (every call reads its
+    weight from HBM): the calls back to back, captured once in a HIP graph, replayed
+    `replays` times; median and spread of the per-call time over the replays, plus per-launch
+    event durations of an eager pass for reference."""
     import torch
+
+    import bit_nf4_quantized_dq_amd as Q
+
+    X1 = X_all[:M].to(dev).contiguous()
+    Y1 = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    ws1 = Q.new_workspace(Q.workspace_size(Q.OP_FWD, M, N, K, r), dev)
+    for cp in copies[:8]:
+        Q.linear_fwd(cp, X1, A, B, alpha, Y=Y1, ws=ws1)
+    torch.cuda.synchronize()
+    # (a) kernel durations from HIP events, eager launches
+    Q.timing_enable(True)
+    for cp in copies:
+        Q.linear_fwd(cp, X1, A, B, alpha, Y=Y1, ws=ws1)
+    torch.cuda.synchronize()
+    gv_ms, gv_n = Q.timing_read("gemv_fwd")
+    Q.timing_enable(False)
+    # (b) whole calls back to back, captured once in a HIP graph and replayed
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for cp in copies:
+                Q.linear_fwd(cp, X1, A, B, alpha, Y=Y1, ws=ws1)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    per_call = []
+    for _ in range(replays):
+        t0 = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        per_call.append(1e6 * (time.perf_counter() - t0) / len(copies))
+    per_call.sort()
+    us_call = per_call[len(per_call) // 2]
+    # (c) eager Python calls, for reference
+    t0 = time.perf_counter()
+    for cp in copies:
+        Q.linear_fwd(cp, X1, A, B, alpha, Y=Y1, ws=ws1)
+    torch.cuda.synchronize()
+    us_eager = 1e6 * (time.perf_counter() - t0) / len(copies)
+    del graph
+    sb = stream_bytes(M, N, K, r)
+    gemv_us = 1e3 * gv_ms / max(gv_n, 1)
+    return {
+        "metric": f"weight-stream GB/s at M={M} ({N}x{K}, r={r}, {len(copies)} rotated copies, HIP-graph replay)",
+        "value": round(sb / (us_call * 1e-6) / 1e9, 1), "unit": "GB/s", "us_per_call": round(us_call, 2),
+        "us_per_call_min": round(per_call[0], 2), "us_per_call_max": round(per_call[-1], 2), "replays": replays,
+        "us_per_call_eager_python": round(us_eager, 2),
+        "bytes_per_call": sb,
+        # the kernel's roofline from the graph replay (back-to-back calls; the gaps between
+        # launches are included, so this bounds the kernel time from above).  Per-launch events
+        # add about 2 us to every launch they bracket, so their figure is kept for reference.
+        "gemv_kernel": {"avg_us": round(us_call, 2), "achieved_GBs": round(sb / (us_call * 1e-6) / 1e9, 1),
+                        "peak_GBs": PEAK_HBM_GBS, "frac": round(sb / (us_call * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                        "method": f"graph replay of {len(copies)} calls, median of {replays} replays, "
+                                  "launch gaps included",
+                        "avg_us_per_launch_events": round(gemv_us, 2)},
+    }
+
+
+def host_info():
+    """CPU model, logical CPUs and RAM of the host that runs the oracle."""
+    model, ram = "unknown", None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
+        with open("/proc/meminfo") as f:
+            kb = next((int(ln.split()[1]) for ln in f if ln.startswith("MemTotal")), None)
+            ram = None if kb is None else round(kb / 2**20, 1)
+    except OSError:
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "ram_GiB": ram}
+
+
+def cpu_baseline(N, K, r, alpha, target_s=15.0):
+    """The oracle as it stands, on the host cores: dequantize + fwd + bwd on a token sample,
+    with the BLAS threads it uses by default, and once more on one thread."""
+    import numpy as np
 
     import oracle as O
     from bit_nf4_quantized_dq_amd import inputs as I
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = os.cpu_count() or 1
     c = I.linear_case(3, 0, N, K, 4096, r, 0.02)
     oq = O.quantize(c["W"].numpy())
     Ms = 256
@@ -314,17 +425,30 @@ def cpu_baseline(N, K, r, alpha, target_s=15.0):
     dY = c["dY"][:Ms].float().numpy().astype(np.float64)
     A = c["A"].float().numpy().astype(np.float64)
     B = c["B"].float().numpy().astype(np.float64)
-    t0 = time.perf_counter()
-    n = 0
-    while True:
-        what = O.dequantize_f64(oq)
-        O.lora_fwd(what, X, A, B, alpha, r)
-        O.lora_bwd(what, X, dY, A, B, alpha, r)
-        n += 1
-        if time.perf_counter() - t0 > target_s / 2 or n >= 8:
-            break
-    dt = (time.perf_counter() - t0) / n
-    del torch
+
+    def run(budget_s, max_n):
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            what = O.dequantize_f64(oq)
+            O.lora_fwd(what, X, A, B, alpha, r)
+            O.lora_bwd(what, X, dY, A, B, alpha, r)
+            n += 1
+            if time.perf_counter() - t0 > budget_s or n >= max_n:
+                return n, (time.perf_counter() - t0) / n
+
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        threadpool_limits, threads = None, os.cpu_count() or 1
+    n, dt = run(target_s / 2, 8)
+    single = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1, user_api="blas"):
+            n1, dt1 = run(target_s / 2, 2)
+        single = {"value": step_flops(Ms, N, K, r) / dt1 / 1e12, "s_per_step": round(dt1, 3), "steps": n1}
     return {
         "value": step_flops(Ms, N, K, r) / dt / 1e12,
         "unit": "TFLOP/s",
@@ -332,6 +456,8 @@ def cpu_baseline(N, K, r, alpha, target_s=15.0):
         "kind": "oracle",
         "sample": f"{n} oracle step(s) (dequantize + FP64 fwd + bwd) at M={Ms} tokens of the {N}x{K} r={r} linear; "
                   f"{dt:.2f} s per step",
+        "single_thread": single,
+        "host": {**host_info(), "blas_threads": int(threads)},
     }
 
 
@@ -416,14 +542,24 @@ def main():
     # stream about 5 us of command processing, so the other steps run without them.
     gemms = ("gemm_fwd", "gemm_dx")
     ev_from = max(0, args.steps - EVENT_STEPS)
+    # window boundaries: about WINDOWS windows of whole steps, one timing-only event each
+    per_win = max(1, args.steps // WINDOWS)
+    bounds = list(range(0, args.steps, per_win))[:WINDOWS] + [args.steps]
+    wev = HipEvents(len(bounds))
+    sptr = torch.cuda.current_stream().cuda_stream
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         if i == ev_from:
             Q.timing_enable(True, kernels=gemms)
+        if i in bounds:
+            wev.record(bounds.index(i), sptr)
         step()
+    wev.record(len(bounds) - 1, sptr)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    win_ms = sorted(wev.ms(k, k + 1) / (bounds[k + 1] - bounds[k]) for k in range(len(bounds) - 1))
+    wev.close()
     gemm_us = {}
     for name in gemms:
         ms, n = Q.timing_read(name)
@@ -432,6 +568,11 @@ def main():
     ms_per_step = 1e3 * (t1 - t0) / args.steps
     flops = step_flops(M, N, K, r)
     value = flops / (ms_per_step * 1e-3) / 1e12
+    win_med = win_ms[len(win_ms) // 2]
+    windows = {"windows": len(win_ms), "steps_per_window": per_win, "ms_per_step_median": round(win_med, 4),
+               "ms_per_step_min": round(win_ms[0], 4), "ms_per_step_max": round(win_ms[-1], 4),
+               "tflops_at_median": round(flops / (win_med * 1e-3) / 1e12, 2),
+               "method": "timing-only HIP events at window boundaries inside the timed steps"}
 
     # separate pass with events on every launch: per-kernel breakdown (slower step)
     inst_steps = min(args.steps, 20)
@@ -456,69 +597,15 @@ def main():
                 "algorithmic_flops_per_launch": kflops[dom], "avg_us": round(gemm_us[dom], 2),
                 "other_gemm_avg_us": {k: round(v, 2) for k, v in gemm_us.items() if k != dom}}
 
-    # ---- M = 1 weight stream over 128 distinct copies (>= 1.1 GB, beyond the 256 MB cache)
+    # ---- weight stream at M = 1 and M = 16 over 128 distinct copies (>= 1.1 GB, beyond the
+    # 256 MB cache)
     ncopy = 128
-    Ws = [Q.quantize(W) for _ in range(1)]
-    base = Ws[0]
-    copies = []
-    for _ in range(ncopy):
-        copies.append(Q.QuantizedWeight(base.codes.clone(), base.code8.clone(), base.c2s.clone(), base.mu.clone(), N, K))
-    del Ws
-    X1 = c["X"][:1].to(dev).contiguous()
-    Y1 = torch.empty(1, N, dtype=torch.bfloat16, device=dev)
-    ws1 = Q.new_workspace(Q.workspace_size(Q.OP_FWD, 1, N, K, r), dev)
-    for cp in copies[:8]:
-        Q.linear_fwd(cp, X1, A, B, alpha, Y=Y1, ws=ws1)
-    torch.cuda.synchronize()
-    # (a) kernel durations from HIP events, eager launches
-    Q.timing_enable(True)
-    for cp in copies:
-        Q.linear_fwd(cp, X1, A, B, alpha, Y=Y1, ws=ws1)
-    torch.cuda.synchronize()
-    gv_ms, gv_n = Q.timing_read("gemv_fwd")
-    Q.timing_enable(False)
-    # (b) whole calls back to back, captured once in a HIP graph and replayed
-    graph = torch.cuda.CUDAGraph()
-    cap = torch.cuda.Stream()
-    cap.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(cap):
-        with torch.cuda.graph(graph, stream=cap):
-            for cp in copies:
-                Q.linear_fwd(cp, X1, A, B, alpha, Y=Y1, ws=ws1)
-    torch.cuda.synchronize()
-    graph.replay()
-    torch.cuda.synchronize()
-    rounds = 8
-    t0 = time.perf_counter()
-    for _ in range(rounds):
-        graph.replay()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    calls = rounds * ncopy
-    us_call = 1e6 * (t1 - t0) / calls
-    # (c) eager Python calls, for reference
-    t0 = time.perf_counter()
-    for cp in copies:
-        Q.linear_fwd(cp, X1, A, B, alpha, Y=Y1, ws=ws1)
-    torch.cuda.synchronize()
-    us_eager = 1e6 * (time.perf_counter() - t0) / ncopy
-    sb = stream_bytes(1, N, K, r)
-    gemv_us = 1e3 * gv_ms / max(gv_n, 1)
-    stream = {
-        "metric": "weight-stream GB/s at M=1 (4096x4096, r=16, 128 rotated copies, HIP-graph replay)",
-        "value": round(sb / (us_call * 1e-6) / 1e9, 1), "unit": "GB/s", "us_per_call": round(us_call, 2),
-        "us_per_call_eager_python": round(us_eager, 2),
-        "bytes_per_call": sb,
-        # the kernel's roofline from the graph replay (back-to-back calls; the launch gaps,
-        # under 0.3 us in a kernel trace, are included, so this bounds the kernel time from
-        # above).  Per-launch events add about 2 us to every launch they bracket, so their
-        # figure is kept only for reference.
-        "gemv_kernel": {"avg_us": round(us_call, 2), "achieved_GBs": round(sb / (us_call * 1e-6) / 1e9, 1),
-                        "peak_GBs": PEAK_HBM_GBS, "frac": round(sb / (us_call * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-                        "method": "graph replay, launch gaps included",
-                        "avg_us_per_launch_events": round(gemv_us, 2)},
-    }
-    del graph
+    base = Q.quantize(W)
+    copies = [Q.QuantizedWeight(base.codes.clone(), base.code8.clone(), base.c2s.clone(), base.mu.clone(), N, K)
+              for _ in range(ncopy)]
+    del base
+    stream = weight_stream(copies, c["X"], A, B, alpha, N, K, r, 1, dev)
+    stream16 = weight_stream(copies, c["X"], A, B, alpha, N, K, r, 16, dev)
 
     # ---- merged export bf16(w_hat + s B A): the same rotated copies, 8 rotated outputs
     # (8 x 32 MiB, beyond the 256 MB cache)
@@ -649,6 +736,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "timed_windows": windows,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -659,6 +747,7 @@ def main():
         "roofline": roofline,
         "kernels_instrumented_pass": {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in per_kernel.items()},
         "weight_stream_M1": stream,
+        "weight_stream_M16": stream16,
         "quantize_4096x4096": quant,
         "merge_4096x4096": merge,
         "adamw_llama3_8b_adapters": adamw,

@@ -20,7 +20,7 @@ LIB_NAME = "libqlora_nf4.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
 SOURCES = ["api.cpp", "codebook.cpp", "quantize.hip", "dequant.hip", "lora.hip", "gemv.hip",
-    "gemv_stream.hip", "gemm.hip", "gemm_nt.hip", "merge.hip", "adamw.hip", "mlp.hip", "noalloc.hip"]
+    "gemv_stream.hip", "gemm.hip", "gemm_nt.hip", "merge.hip", "adamw.hip", "mlp.hip", "noalloc.hip", "gemv_rows.hip"]
 
 COMMON = [
     "-O3",

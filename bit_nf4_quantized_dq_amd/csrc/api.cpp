@@ -71,6 +71,12 @@ constexpr int64_t kGemvMaxM = 16;
 constexpr int64_t kNtMinM = 1024;
 inline bool decode_once(int64_t M, int dq) { return M >= kNtMinM || dq != QLORA_DQ_E4M3; }
 
+// The M <= 16 forward: the large-weight stream when it applies, else whole rows per
+// workgroup when the shape allows, else the split-reduction kernel.
+inline bool rows_path(int64_t N, int64_t K, int64_t M, int32_t r) {
+  return !gemv_stream_fits(N, K, M, r) && gemv_rows_fits(N, K, M, r);
+}
+
 // ---- workspace layouts
 // Every workspace starts with the arrival counters of the split reductions: one 32-bit word
 // per row group of an M <= 16 forward, or per 64-column tile of dA and of dB in a backward
@@ -89,7 +95,9 @@ FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, int32_t r, int dq) {
   FwdWs w{};
   size_t off = kHead;
   w.tpart = off;
-  if (M <= kGemvMaxM && !decode_once(M, dq)) {
+  if (M <= kGemvMaxM && !decode_once(M, dq) && rows_path(N, K, M, r)) {
+    w.ypart = w.ls = off;  // whole rows per workgroup: only the counter head
+  } else if (M <= kGemvMaxM && !decode_once(M, dq)) {
     const int32_t ks = gemv_stream_fits(N, K, M, r) ? gemv_stream_plan(N, K, M, r).ksplit : gemv_ksplit(N, K);
     off = align_up(off + sizeof(float) * ks * M * r, 256);
     w.ypart = off;
@@ -354,6 +362,9 @@ int fwd_enqueue(const qlora_nf4dq_t* Wq, const uint16_t* X, int64_t M, const uin
   float* tpart = reinterpret_cast<float*>(base + L.tpart);
   if (M <= kGemvMaxM && !decode_once(M, dq)) {
     float* ypart = reinterpret_cast<float*>(base + L.ypart);
+    if (rows_path(N, K, M, r))
+      return hip_status(launch_gemv_rows(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, X, M, A, B, r, s, Y, T_save, ws,
+                                         tables_of(Wq), stream));
     if (gemv_stream_fits(N, K, M, r))
       return hip_status(launch_gemv_stream(codes, Wq->code8, Wq->c2s, Wq->mu, N, K, X, M, A, B, r, s, Y, T_save,
                                            ypart, tpart, head_counters(ws), tables_of(Wq), stream));

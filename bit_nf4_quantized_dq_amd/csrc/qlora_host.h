@@ -114,6 +114,14 @@ hipError_t launch_gemv_fwd(const uint32_t* codes, const uint8_t* code8, const fl
                            const uint16_t* A, const uint16_t* B, int32_t r, float s, uint16_t* Y,
                            uint16_t* T_save, float* part, float* tpart, unsigned int* counters,
                            const Nf4Tables& T, hipStream_t st);
+// The same forward with whole rows per workgroup (gemv_rows.hip): used when gemv_rows_fits()
+// and the large-weight stream below does not apply.  Its only workspace is the counter head
+// (`head`, QLORA_WS_COUNTER_BYTES, zero before the call and left zero).
+bool gemv_rows_fits(int64_t N, int64_t K, int64_t M, int32_t r);
+hipError_t launch_gemv_rows(const uint32_t* codes, const uint8_t* code8, const float* c2s, const float* mu,
+                            int64_t N, int64_t K, const uint16_t* X, int64_t M, const uint16_t* A,
+                            const uint16_t* B, int32_t r, float s, uint16_t* Y, uint16_t* T_save, void* head,
+                            const Nf4Tables& T, hipStream_t st);
 // The same forward for large weights (gemv_stream.hip): used when gemv_stream_fits(); its
 // reduction split comes from gemv_stream_plan() (same partial layout as above).
 struct GemvPlan {

@@ -329,6 +329,47 @@ def test_weight_stream_full_chunk_adapter_first(gpu_lib, M, r):
     assert normwise(_f64(T), T_ref) <= TOL
 
 
+ROWS_CASES = [
+    # d_out, d_in, M, r: whole rows per workgroup (M <= 4, at least 4096 rows, d_in 2048 or 4096)
+    (4096, 2048, 3, 8),    # the shorter reduction
+    (6144, 4096, 2, 64),   # 384 row groups, 64 T workgroups
+    (4096, 4096, 1, 40),   # a rank that ends inside a 32-wide step
+    (5120, 4096, 4, 24),
+    (4096, 4096, 4, 16),
+]
+
+
+@pytest.mark.parametrize("N,K,M,r", ROWS_CASES)
+def test_weight_stream_whole_rows(gpu_lib, N, K, M, r):
+    """M <= 16 with whole rows per workgroup and T handed over through the workspace head:
+    Y and T in full against the oracle, over three calls on one workspace (the handed-over
+    words are cleared by each call)."""
+    from bit_nf4_quantized_dq_amd import OP_FWD, linear_fwd, new_workspace, quantize, workspace_size
+
+    print(f"rows {N}x{K} M={M} r={r}", flush=True)
+    alpha = 2.0 * r
+    c = _case(18, N, K, M, r, 0.02, idx=M + r)
+    oq = O.quantize(c["W"].numpy())
+    what = O.bf16_bits_to_f32(O.dequantize_bf16_bits(oq)).astype(np.float64)
+    q = quantize(c["W"].cuda())
+    ws = new_workspace(workspace_size(OP_FWD, M, N, K, r), "cuda")
+    X, A, Bm = c["X"].cuda(), c["A"].cuda(), c["B"].cuda()
+    Xf, Af, Bf = _f64(c["X"]), _f64(c["A"]), _f64(c["B"])
+    T_ref = Xf @ Af.T
+    Y_ref = Xf @ what.T + (alpha / r) * T_ref @ Bf.T
+    first = None
+    for call in range(3):
+        T = torch.empty(M, r, dtype=torch.bfloat16, device="cuda")
+        Y = linear_fwd(q, X, A, Bm, alpha, T_save=T, ws=ws)
+        torch.cuda.synchronize()
+        assert normwise(_f64(Y), Y_ref) <= TOL, call
+        assert normwise(_f64(T), T_ref) <= TOL, call
+        if first is None:
+            first = Y.clone()
+        assert torch.equal(Y.view(torch.int16), first.view(torch.int16)), call
+    assert int(ws[:524288].view(torch.int32).abs().sum()) == 0, "the counter head is left zero"
+
+
 STREAM_CASES = [
     # d_out, d_in, M, r
     (8192, 4096, 1, 16),
