@@ -246,6 +246,22 @@ size_t quant_ws(int64_t d_out, int64_t d_in) {
   return kHead + align_up(sizeof(float) * nb, 256) + 256 * sizeof(unsigned long long) + 256;
 }
 
+// ---- kernel timing
+struct TimingState {
+  std::mutex mu;
+  unsigned mask = 0;  // bit i: kernel id i is timed
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[QLORA_K_COUNT];
+  size_t used[QLORA_K_COUNT] = {0};
+};
+TimingState& timing() {
+  static TimingState t;
+  return t;
+}
+
+}  // namespace
+
+namespace qlora {
+
 // ---- exact mean: value = sum_e S_e * 2^(e-150) (e >= 1), folded in a big integer and
 // rounded once to double (nearest, ties to even).
 double exact_sum_to_double(const unsigned long long hist[256]) {
@@ -282,22 +298,6 @@ double exact_sum_to_double(const unsigned long long hist[256]) {
   if (guard && (sticky || (mant & 1))) mant += 1;  // may carry to 2^53: still exact in double
   return std::ldexp((double)mant, lsb_pos - 149);
 }
-
-// ---- kernel timing
-struct TimingState {
-  std::mutex mu;
-  unsigned mask = 0;  // bit i: kernel id i is timed
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[QLORA_K_COUNT];
-  size_t used[QLORA_K_COUNT] = {0};
-};
-TimingState& timing() {
-  static TimingState t;
-  return t;
-}
-
-}  // namespace
-
-namespace qlora {
 
 namespace {
 thread_local int t_timing_off = 0;

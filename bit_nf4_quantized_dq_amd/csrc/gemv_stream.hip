@@ -515,6 +515,7 @@ GemvPlan gemv_stream_plan(int64_t N, int64_t K, int64_t M, int32_t r) {
     }
   }
   p.ksplit = (int32_t)best_ks;
+  if (best_ks == 0) return p;  // no split fits the staging limits: the shape is not streamed
   p.nbs = (int32_t)nbs_of(best_ks);
   p.nchunk = p.nbs <= kCB ? 1 : (int32_t)chunks_of(p.nbs);
   p.xpitch = region_use(nb_row, M, p.nbs, p.nchunk).xpitch;

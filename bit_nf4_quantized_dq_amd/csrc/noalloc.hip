@@ -7,6 +7,8 @@
 // FP32 partials and the BF16 adapter intermediate of the call.  Calls whose workspace need
 // exceeds its size are refused before anything is launched.  Every call on a device shares
 // that device's array, so calls that overlap on one device (two streams at once) race.
+#include <hip/hip_runtime.h>
+
 #include <mutex>
 
 #include "qlora_host.h"

@@ -10,6 +10,7 @@
 //   c1_hat = fl32(fl32(E4M3(code8) * c2s) + mu);   w_hat = bf16(fl32(q[code] * c1_hat)).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

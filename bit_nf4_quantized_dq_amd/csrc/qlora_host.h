@@ -3,7 +3,6 @@
 #pragma once
 
 #include <hip/hip_runtime_api.h>
-#include <hip/hip_ext.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -17,6 +16,13 @@ const Nf4Tables& nf4_tables();
 // First-level codebooks: 0 NF4, 1 uniform INT4, 2 FP4 (E2M1 levels).
 void build_codebook_tables(int codebook, Nf4Tables* t);
 const Nf4Tables& codebook_tables(int codebook);
+
+// sum over e = 1..255 of hist[e] * 2^(e - 150), computed exactly and rounded once to double
+// (nearest, ties to even).  Bin e of the first quantize pass holds the integer sum of the
+// significands (implicit bit included) of the block constants whose biased FP32 exponent is
+// e; subnormal constants go to bin 1 with their fraction bits, which gives them the same
+// weight 2^-149 per unit.
+double exact_sum_to_double(const unsigned long long hist[256]);
 
 // Start/stop events for one kernel launch when timing is enabled for its id (see
 // qlora_timing_*), else null.  Launch with hipExtLaunchKernelGGL(..., t.start, t.stop, 0,

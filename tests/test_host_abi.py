@@ -243,6 +243,16 @@ def test_workspace_sizes_are_sane():
     assert B.workspace_size(B.OP_QUANTIZE, 1, 4096, 4096, 1) >= 4096 * 4096 // 64 * 4
 
 
+def test_weight_stream_plan_without_a_fitting_split():
+    """A shape at the edge of the limits for which no split of the weight stream fits its
+    staging limits (1024 rows of 2^22 weights): the plan reports none, and the other path
+    serves it (the plan once divided by the empty split count)."""
+    for M in (1, 4, 16):
+        for r in (8, 64, 128):
+            assert B.workspace_size(B.OP_FWD, M, 1024, 1 << 22, r) > 0
+            assert B.workspace_size(B.OP_FWD, M, 1 << 22, 1024, r) > 0
+
+
 def test_strerror_covers_every_status(L):
     for s in range(0, -8, -1):
         assert B._strerror(s) not in ("?", "unknown status")
