@@ -27,7 +27,8 @@ workload.
 
 The default warm-up (about 30 ms of steps) lets the clock under sustained MFMA load settle:
 on a fresh box the first ~60 steps run up to 13% slower than the rest.
-  python bench.py --pmc-pass    # 2 steps, one merge, one AdamW step, two M = 1 calls on a
+  python bench.py --pmc-pass    # 2 steps, one merge, one AdamW step, two M = 1 and two
+                                # M = 16 calls on the step's weight, two M = 1 calls on a
                                 # 28672x8192 weight and a 256 MiB device copy (the counter
                                 # calibration), for counter runs
 """
@@ -45,25 +46,81 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 
 
-# HBM bytes per launch from two rocprofv3 counter passes of `bench.py --pmc-pass`
-# (FETCH_SIZE scaled by 2.0 and WRITE_SIZE by 1.0, the factors that make a plain 256 MiB
-# device copy read and write 256 MiB).  A figure holds only for the kernel source it was
-# taken on: when that file's SHA-1 differs, the traffic is reported as null.
-COUNTER_TRAFFIC = {
+# Counters per launch from four rocprofv3 passes of `bench.py --pmc-pass` (FETCH_SIZE;
+# WRITE_SIZE; SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_MFMA, SQ_INSTS_VALU, SQ_INSTS_LDS and others;
+# SQ_LDS_BANK_CONFLICT, SQ_INSTS_SALU and others).  HBM bytes are FETCH_SIZE scaled by 2.0 and
+# WRITE_SIZE by 1.0, the factors that make a plain 256 MiB device copy read and write 256 MiB.
+# SQ_* counts are summed over the whole chip.  A record holds only for the kernel source it
+# was taken on: when that file's SHA-1 differs, its figures are reported as null.
+COUNTERS = {
     "gemm_nt": {"source": "bit_nf4_quantized_dq_amd/csrc/gemm_nt.hip",
                 "sha1": "97131bf4dd7659cfe4e89f3f5274c999b3e6af69",
-                "read_bytes": 202_387_866, "write_bytes": 33_554_432},
+                "read_bytes": 202_388_608, "write_bytes": 33_554_432,
+                "mfma_insts": 4_243_456, "mfma_busy_cycles": 135_790_592, "valu_insts": 11_699_456,
+                "lds_insts": 3_244_032, "lds_bank_conflict_cycles": 65_536, "salu_insts": 6_105_600},
     "merge": {"source": "bit_nf4_quantized_dq_amd/csrc/merge.hip",
               "sha1": "aa1649879396b227b61d065c057ec39a4962a28a",
-              "read_bytes": 11_908_864, "write_bytes": 33_554_688},
+              "read_bytes": 11_912_832, "write_bytes": 33_554_944},
     "adamw": {"source": "bit_nf4_quantized_dq_amd/csrc/adamw.hip",
               "sha1": "513130524f3da5219d61f8dcabd1c76bb0828e6f",
-              "read_bytes": 587_289_984, "write_bytes": 587_202_560},
+              "read_bytes": 587_332_608, "write_bytes": 587_202_560},
+    # the 4096 x 4096 weight at M = 1 (whole-row stream) and at M = 16 (split-K stream)
+    "gemv_rows": {"source": "bit_nf4_quantized_dq_amd/csrc/gemv_rows.hip",
+                  "sha1": "90e057c10df734c17c9123101ef90e743f36e7e1",
+                  "read_bytes": 9_203_008, "write_bytes": 270_336, "weights": 4096 * 4096,
+                  "mfma_insts": 35_072, "valu_insts": 724_080, "lds_insts": 188_928, "lds_bank_conflict_cycles": 0},
+    "gemv_fused": {"source": "bit_nf4_quantized_dq_amd/csrc/gemv.hip",
+                   "sha1": "977c367891ded57ee601fb265121bce9fa8f787f",
+                   "read_bytes": 13_196_288, "write_bytes": 2_245_632, "weights": 4096 * 4096,
+                   "mfma_insts": 38_912, "valu_insts": 1_661_728, "lds_insts": 100_640,
+                   "lds_bank_conflict_cycles": 219_200},
     # one M = 1 call on a 28672 x 8192 weight (the gate shape of the 70B-class model)
     "gemv_stream": {"source": "bit_nf4_quantized_dq_amd/csrc/gemv_stream.hip",
-                    "sha1": "811d34250c8b0abc3a507f724811f74ec7698c9c",
-                    "read_bytes": 125_030_400, "write_bytes": 297_574},
+                    "sha1": "111ed5118cece5a11f25608c6d9732d1a18e5e83",
+                    "read_bytes": 125_032_256, "write_bytes": 297_600, "weights": 28672 * 8192,
+                    "mfma_insts": 489_216, "valu_insts": 7_018_118, "lds_insts": 2_475_426,
+                    "lds_bank_conflict_cycles": 403_200},
 }
+SIMDS = 256 * 4  # MFMA pipes on the chip
+
+
+def _counter_record(kernel):
+    import hashlib
+
+    rec = COUNTERS[kernel]
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), rec["source"])
+    try:
+        with open(path, "rb") as f:
+            if hashlib.sha1(f.read()).hexdigest() != rec["sha1"]:
+                return None
+    except OSError:
+        return None
+    return rec
+
+
+def counter_traffic(kernel):
+    rec = _counter_record(kernel)
+    return None if rec is None else rec["read_bytes"] + rec["write_bytes"]
+
+
+def counter_figures(kernel, avg_us=None):
+    """The pinned counters of one launch, with what follows from them: VALU lane-ops per
+    weight (wave instructions x 64 lanes, MFMA included: an upper bound, as masked-off lanes
+    count) and, given the launch time, the fraction of it the MFMA pipes were busy at the
+    published 2.4 GHz clock."""
+    rec = _counter_record(kernel)
+    if rec is None:
+        return None
+    out = {k: v for k, v in rec.items() if k not in ("source", "sha1")}
+    if "weights" in rec:
+        out["valu_lane_ops_per_weight"] = round(64 * rec["valu_insts"] / rec["weights"], 3)
+        out["valu_lane_ops_per_weight_excl_mfma"] = round(64 * (rec["valu_insts"] - rec["mfma_insts"]) / rec["weights"], 3)
+    if "mfma_busy_cycles" in rec:
+        out["mfma_busy_cycles_per_simd"] = rec["mfma_busy_cycles"] // SIMDS
+        out["mfma_cycles_per_inst"] = round(rec["mfma_busy_cycles"] / rec["mfma_insts"], 2)
+        if avg_us:
+            out["mfma_busy_frac_at_2p4GHz"] = round(rec["mfma_busy_cycles"] / SIMDS / (avg_us * 2400.0), 4)
+    return out
 
 
 EVENT_STEPS = 4  # timed steps whose GEMM launches carry HIP events
@@ -103,20 +160,6 @@ class HipEvents:
     def close(self):
         for e in self.ev:
             self.L.hipEventDestroy(e)
-
-
-def counter_traffic(kernel):
-    import hashlib
-
-    rec = COUNTER_TRAFFIC[kernel]
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), rec["source"])
-    try:
-        with open(path, "rb") as f:
-            if hashlib.sha1(f.read()).hexdigest() != rec["sha1"]:
-                return None
-    except OSError:
-        return None
-    return rec["read_bytes"] + rec["write_bytes"]
 
 
 def step_flops(M, N, K, r):
@@ -312,7 +355,8 @@ def seventy_b_model(dev, layers=80, passes=3):
                             "frac_of_hbm_peak": round(nbytes1 / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
                 del g
             out["M1"]["gate_28672x8192_call"] = {"algorithmic_bytes": stream_bytes(1, 28672, 8192, r),
-                                                 "counter_bytes": counter_traffic("gemv_stream")}
+                                                 "counter_bytes": counter_traffic("gemv_stream"),
+                                                 "counters": counter_figures("gemv_stream")}
         else:
             t0 = time.perf_counter()
             for _ in range(passes):
@@ -329,7 +373,7 @@ def seventy_b_model(dev, layers=80, passes=3):
     return out
 
 
-def weight_stream(copies, X_all, A, B, alpha, N, K, r, M, dev, replays=20):
+def weight_stream(copies, X_all, A, B, alpha, N, K, r, M, dev, kernel, replays=20):
     """Forward of one linear at M tokens over rotated quantized copies (every call reads its
     weight from HBM): the calls back to back, captured once in a HIP graph, replayed
     `replays` times; median and spread of the per-call time over the replays, plus per-launch
@@ -392,7 +436,9 @@ def weight_stream(copies, X_all, A, B, alpha, N, K, r, M, dev, replays=20):
                         "peak_GBs": PEAK_HBM_GBS, "frac": round(sb / (us_call * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                         "method": f"graph replay of {len(copies)} calls, median of {replays} replays, "
                                   "launch gaps included",
-                        "avg_us_per_launch_events": round(gemv_us, 2)},
+                        "avg_us_per_launch_events": round(gemv_us, 2),
+                        "kernel": f"k_{kernel}", "traffic": counter_traffic(kernel),
+                        "counters": counter_figures(kernel)},
     }
 
 
@@ -470,8 +516,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the Llama-3-8B layer and 70B-class model workloads")
     ap.add_argument("--pmc-pass", action="store_true",
-                    help="run 2 steps, one merge, one AdamW step, two M = 1 calls on a 28672x8192 weight and a "
-                         "plain 256 MiB device copy (the counter calibration), print nothing")
+                    help="run 2 steps, one merge, one AdamW step, two M = 1 and two M = 16 calls on the step's "
+                         "weight, two M = 1 calls on a 28672x8192 weight and a plain 256 MiB device copy (the "
+                         "counter calibration), print nothing")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
@@ -516,6 +563,10 @@ def main():
         Q.adamw_step(st[0], st[1], st[2], st[3], 1, 2e-4, weight_decay=0.01,
                      param=torch.empty(na, dtype=torch.bfloat16, device=dev))
         del st
+        # the step's own 4096 x 4096 weight at M = 1 and M = 16 (two calls each)
+        for m in (1, 16):
+            for _ in range(2):
+                Q.linear_fwd(q, X[:m], A, B, alpha)
         # one large-weight stream call pair at M = 1 (a 28672 x 8192 gate-shaped linear)
         Wg = I.weight(5, 4, 28672, 8192, 0.015, device=dev)
         qg = Q.quantize(Wg)
@@ -595,7 +646,8 @@ def main():
                 "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": counter_traffic("gemm_nt"),
                 "traffic_algorithmic_bytes": 2 * (N * K + M * K + M * r + N * r) + 2 * M * N,
                 "algorithmic_flops_per_launch": kflops[dom], "avg_us": round(gemm_us[dom], 2),
-                "other_gemm_avg_us": {k: round(v, 2) for k, v in gemm_us.items() if k != dom}}
+                "other_gemm_avg_us": {k: round(v, 2) for k, v in gemm_us.items() if k != dom},
+                "counters": counter_figures("gemm_nt", gemm_us[dom])}
 
     # ---- weight stream at M = 1 and M = 16 over 128 distinct copies (>= 1.1 GB, beyond the
     # 256 MB cache)
@@ -604,8 +656,8 @@ def main():
     copies = [Q.QuantizedWeight(base.codes.clone(), base.code8.clone(), base.c2s.clone(), base.mu.clone(), N, K)
               for _ in range(ncopy)]
     del base
-    stream = weight_stream(copies, c["X"], A, B, alpha, N, K, r, 1, dev)
-    stream16 = weight_stream(copies, c["X"], A, B, alpha, N, K, r, 16, dev)
+    stream = weight_stream(copies, c["X"], A, B, alpha, N, K, r, 1, dev, "gemv_rows")
+    stream16 = weight_stream(copies, c["X"], A, B, alpha, N, K, r, 16, dev, "gemv_fused")
 
     # ---- merged export bf16(w_hat + s B A): the same rotated copies, 8 rotated outputs
     # (8 x 32 MiB, beyond the 256 MB cache)
