@@ -54,10 +54,10 @@ PEAK_HBM_GBS = 8000.0
 # was taken on: when that file's SHA-1 differs, its figures are reported as null.
 COUNTERS = {
     "gemm_nt": {"source": "bit_nf4_quantized_dq_amd/csrc/gemm_nt.hip",
-                "sha1": "97131bf4dd7659cfe4e89f3f5274c999b3e6af69",
-                "read_bytes": 202_388_608, "write_bytes": 33_554_432,
-                "mfma_insts": 4_243_456, "mfma_busy_cycles": 135_790_592, "valu_insts": 11_699_456,
-                "lds_insts": 3_244_032, "lds_bank_conflict_cycles": 65_536, "salu_insts": 6_105_600},
+                "sha1": "51cc3417a957207fd566e5a261d842db78495348",
+                "read_bytes": 202_372_192, "write_bytes": 33_554_432,
+                "mfma_insts": 4_243_456, "mfma_busy_cycles": 135_790_592, "valu_insts": 9_571_584,
+                "lds_insts": 3_244_032, "lds_bank_conflict_cycles": 65_536, "salu_insts": 3_396_096},
     "merge": {"source": "bit_nf4_quantized_dq_amd/csrc/merge.hip",
               "sha1": "aa1649879396b227b61d065c057ec39a4962a28a",
               "read_bytes": 11_912_832, "write_bytes": 33_554_944},
@@ -65,15 +65,15 @@ COUNTERS = {
               "sha1": "513130524f3da5219d61f8dcabd1c76bb0828e6f",
               "read_bytes": 587_332_608, "write_bytes": 587_202_560},
     # the 4096 x 4096 weight at M = 1 (whole-row stream) and at M = 16 (split-K stream)
-    "gemv_rows": {"source": "bit_nf4_quantized_dq_amd/csrc/gemv_rows.hip",
-                  "sha1": "90e057c10df734c17c9123101ef90e743f36e7e1",
-                  "read_bytes": 9_203_008, "write_bytes": 270_336, "weights": 4096 * 4096,
-                  "mfma_insts": 35_072, "valu_insts": 724_080, "lds_insts": 188_928, "lds_bank_conflict_cycles": 0},
-    "gemv_fused": {"source": "bit_nf4_quantized_dq_amd/csrc/gemv.hip",
-                   "sha1": "977c367891ded57ee601fb265121bce9fa8f787f",
-                   "read_bytes": 13_196_288, "write_bytes": 2_245_632, "weights": 4096 * 4096,
-                   "mfma_insts": 38_912, "valu_insts": 1_661_728, "lds_insts": 100_640,
-                   "lds_bank_conflict_cycles": 219_200},
+    "gemv_rows_M1": {"source": "bit_nf4_quantized_dq_amd/csrc/gemv_rows.hip",
+                     "sha1": "90e057c10df734c17c9123101ef90e743f36e7e1",
+                     "read_bytes": 9_203_008, "write_bytes": 270_336, "weights": 4096 * 4096,
+                     "mfma_insts": 35_072, "valu_insts": 724_080, "lds_insts": 188_928, "lds_bank_conflict_cycles": 0},
+    "gemv_fused_M16": {"source": "bit_nf4_quantized_dq_amd/csrc/gemv.hip",
+                       "sha1": "977c367891ded57ee601fb265121bce9fa8f787f",
+                       "read_bytes": 13_196_288, "write_bytes": 2_245_632, "weights": 4096 * 4096,
+                       "mfma_insts": 38_912, "valu_insts": 1_661_728, "lds_insts": 100_640,
+                       "lds_bank_conflict_cycles": 219_200},
     # one M = 1 call on a 28672 x 8192 weight (the gate shape of the 70B-class model)
     "gemv_stream": {"source": "bit_nf4_quantized_dq_amd/csrc/gemv_stream.hip",
                     "sha1": "111ed5118cece5a11f25608c6d9732d1a18e5e83",
@@ -99,6 +99,8 @@ def _counter_record(kernel):
 
 
 def counter_traffic(kernel):
+    if kernel not in COUNTERS:
+        return None
     rec = _counter_record(kernel)
     return None if rec is None else rec["read_bytes"] + rec["write_bytes"]
 
@@ -108,7 +110,7 @@ def counter_figures(kernel, avg_us=None):
     weight (wave instructions x 64 lanes, MFMA included: an upper bound, as masked-off lanes
     count) and, given the launch time, the fraction of it the MFMA pipes were busy at the
     published 2.4 GHz clock."""
-    rec = _counter_record(kernel)
+    rec = _counter_record(kernel) if kernel in COUNTERS else None
     if rec is None:
         return None
     out = {k: v for k, v in rec.items() if k not in ("source", "sha1")}
@@ -437,7 +439,7 @@ def weight_stream(copies, X_all, A, B, alpha, N, K, r, M, dev, kernel, replays=2
                         "method": f"graph replay of {len(copies)} calls, median of {replays} replays, "
                                   "launch gaps included",
                         "avg_us_per_launch_events": round(gemv_us, 2),
-                        "kernel": f"k_{kernel}", "traffic": counter_traffic(kernel),
+                        "kernel": "k_" + kernel.split("_M")[0], "traffic": counter_traffic(kernel),
                         "counters": counter_figures(kernel)},
     }
 
@@ -656,8 +658,8 @@ def main():
     copies = [Q.QuantizedWeight(base.codes.clone(), base.code8.clone(), base.c2s.clone(), base.mu.clone(), N, K)
               for _ in range(ncopy)]
     del base
-    stream = weight_stream(copies, c["X"], A, B, alpha, N, K, r, 1, dev, "gemv_rows")
-    stream16 = weight_stream(copies, c["X"], A, B, alpha, N, K, r, 16, dev, "gemv_fused")
+    stream = weight_stream(copies, c["X"], A, B, alpha, N, K, r, 1, dev, "gemv_rows_M1")
+    stream16 = weight_stream(copies, c["X"], A, B, alpha, N, K, r, 16, dev, "gemv_fused_M16")
 
     # ---- merged export bf16(w_hat + s B A): the same rotated copies, 8 rotated outputs
     # (8 x 32 MiB, beyond the 256 MB cache)

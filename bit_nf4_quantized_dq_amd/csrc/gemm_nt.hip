@@ -324,7 +324,10 @@ __device__ __forceinline__ void tile_xy(int64_t& tx, int64_t& ty) {
 // barrier after step 2t+1 publishes the slots of steps 2t+2 and 2t+3 and retires those of
 // steps up to 2t+1, so within a pair the wavefronts of a SIMD may drift apart and fill each
 // other's gaps on the matrix pipe.  Step kb issues the loads of step kb+3 into the slot of
-// step kb-2, which every wavefront finished reading before the last barrier.
+// step kb-2, which every wavefront finished reading before the last barrier.  The last three
+// steps issue them too, for steps past the range: those read zeros (or the next split's
+// columns) into slots that are never read again, and the epilogue waits for them.  A branch
+// around each load cost more than the loads (about 2% of the launch).
 //
 // The second half (ks = 1) of the previous step's MFMAs is deferred: its operands are in
 // `o1`, so those MFMAs run while this step's operand reads are in flight.  The four ring
@@ -334,31 +337,28 @@ __device__ __forceinline__ void tile_xy(int64_t& tx, int64_t& ty) {
 template <int S, bool ODD>
 __device__ __forceinline__ void nt_step(const Ring& ra, const Ring& rb, uint32_t kb, uint32_t nk, int wf, int wmt,
                                         int l32, int h32, Ops& o1, Acc& acc) {
-  const bool ld = kb + 3 < nk;
   uint4* const na = abuf<(S + 3) % kRing>();
   uint4* const nb = bbuf<(S + 3) % kRing>();
   Ops o0;
   read_ops(abuf<S>(), bbuf<S>(), 0, wf, wmt, l32, h32, o0);
   mma_half(o1, 0, acc);  // ks = 1 of step kb - 1
   __builtin_amdgcn_sched_barrier(0);
-  if (ld) ra.issue1(na, kb + 3, 0);
+  ra.issue1(na, kb + 3, 0);
   __builtin_amdgcn_sched_barrier(0);
   mma_half(o1, 1, acc);
   __builtin_amdgcn_sched_barrier(0);
-  if (ld) ra.issue1(na, kb + 3, 1);
+  ra.issue1(na, kb + 3, 1);
   __builtin_amdgcn_sched_barrier(0);
   read_ops(abuf<S>(), bbuf<S>(), 1, wf, wmt, l32, h32, o1);
   mma_half(o0, 0, acc);
   __builtin_amdgcn_sched_barrier(0);
-  if (ld) rb.issue1(nb, kb + 3, 0);
+  rb.issue1(nb, kb + 3, 0);
   __builtin_amdgcn_sched_barrier(0);
   mma_half(o0, 1, acc);
   __builtin_amdgcn_sched_barrier(0);
-  if (ld) rb.issue1(nb, kb + 3, 1);
+  rb.issue1(nb, kb + 3, 1);
   if (ODD) {
-    // this wavefront's loads of steps kb+1 and kb+2 are complete (only kb+3's may be pending)
-    if (ld) wait_vm<4>();
-    else wait_vm<0>();
+    wait_vm<4>();  // this wavefront's loads of steps kb+1 and kb+2 are complete (kb+3's may be pending)
     lds_barrier();
   }
 }
@@ -431,6 +431,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(const uint16_t* __restr
     nt_step<4, true>(ra, rb, kb + 9, nk, wf, wmt, l32, h32, o1, acc);
   }
   mma(o1, acc);  // ks = 1 of the last step
+  wait_vm<0>();   // the loads issued past the range have landed
   lds_barrier();  // every wavefront is done with the ring slots, which now stage the epilogue
   if (SPLIT)
     store_part(part + (int64_t)blockIdx.z * M * F, M, F, f0 + wf, m0 + wmt, wave, lane, l32, h32, acc);

@@ -336,6 +336,7 @@ ROWS_CASES = [
     (4096, 4096, 1, 40),   # a rank that ends inside a 32-wide step
     (5120, 4096, 4, 24),
     (4096, 4096, 4, 16),
+    (4096, 2048, 4, 128),  # rank 128 (the largest): the handed-over words fill the 512 KiB head
 ]
 
 
@@ -368,6 +369,34 @@ def test_weight_stream_whole_rows(gpu_lib, N, K, M, r):
             first = Y.clone()
         assert torch.equal(Y.view(torch.int16), first.view(torch.int16)), call
     assert int(ws[:524288].view(torch.int32).abs().sum()) == 0, "the counter head is left zero"
+
+
+def test_weight_stream_whole_rows_token_independence(gpu_lib):
+    """Each token's output of the whole-row kernel depends on that token alone: a 4-token
+    call equals 4 one-token calls, and a 3-token call equals a 2-token call plus a 1-token
+    call, bit for bit, Y and T."""
+    from bit_nf4_quantized_dq_amd import linear_fwd, quantize
+
+    N, K, r = 4096, 4096, 16
+    c = _case(19, N, K, 4, r, 0.02, idx=3)
+    q = quantize(c["W"].cuda())
+    X, A, Bm = c["X"].cuda(), c["A"].cuda(), c["B"].cuda()
+
+    def fwd(rows):
+        T = torch.empty(rows.shape[0], r, dtype=torch.bfloat16, device="cuda")
+        Y = linear_fwd(q, rows.contiguous(), A, Bm, 32.0, T_save=T)
+        return Y.clone(), T.clone()
+
+    Y4, T4 = fwd(X)
+    parts = [fwd(X[m:m + 1]) for m in range(4)]
+    Y3, T3 = fwd(X[:3])
+    Y2, T2 = fwd(X[:2])
+    torch.cuda.synchronize()
+    bits = lambda t: t.view(torch.int16)
+    assert torch.equal(bits(Y4), bits(torch.cat([p[0] for p in parts])))
+    assert torch.equal(bits(T4), bits(torch.cat([p[1] for p in parts])))
+    assert torch.equal(bits(Y3), bits(torch.cat([Y2, parts[2][0]])))
+    assert torch.equal(bits(T3), bits(torch.cat([T2, parts[2][1]])))
 
 
 STREAM_CASES = [
