@@ -48,6 +48,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // Two rings of five 16 KB slots (160 KB, all of a CU's LDS).
 constexpr int kRing = 5;
+// A row offset past every tile (tiles are below 2^31 bytes and step offsets below 2^24), so
+// a missing row reads zeros however the scalar step offset adds to it.
+constexpr uint32_t kFarRow = 0xF0000000u;
 __shared__ uint4 s_a0[kSlot], s_a1[kSlot], s_a2[kSlot], s_a3[kSlot], s_a4[kSlot];
 __shared__ uint4 s_b0[kSlot], s_b1[kSlot], s_b2[kSlot], s_b3[kSlot], s_b4[kSlot];
 
@@ -82,35 +85,48 @@ __device__ __forceinline__ void lds_barrier() {
 // swizzle maps there.
 struct Ring {
   rsrc_t r;
-  uint32_t base[2];  // byte offset of the lane's chunk at reduction index 0; kOOB past the rows
+  uint32_t base[2];  // byte offset of the lane's chunk at reduction index 0; past the rows,
+                     // kFarRow (whole steps) or kOOB
   uint32_t col[2];   // the lane's first reduction index within a step
   uint32_t Kr;
   uint32_t kbase;  // first reduction step of this workgroup's range
+  uint32_t kmax;   // last reduction step of the whole product
   int wave;
 
+  template <bool FULLK>
   __device__ __forceinline__ void init(const uint16_t* P, int64_t rows_total, int64_t row0, int64_t Kr_, int w,
                                        int lane, uint32_t kb0) {
     const int64_t rows = rows_total - row0 < 256 ? rows_total - row0 : 256;
     r = make_rsrc(P + row0 * Kr_, rows * Kr_ * 2);
     Kr = (uint32_t)Kr_;
     kbase = kb0;
+    kmax = (uint32_t)((Kr_ + BK - 1) / BK) - 1u;
     wave = w;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int row = 16 * (2 * w + j) + (lane >> 2);
       const int lc = (lane & 3) ^ ((row >> 2) & 3);
       col[j] = 8 * lc;
-      base[j] = row < rows ? (uint32_t)(row * Kr_ * 2 + 16 * lc) : kOOB;
+      base[j] = row < rows ? (uint32_t)(row * Kr_ * 2 + 16 * lc) : (FULLK ? kFarRow : kOOB);
     }
   }
+  template <bool FULLK>
   __device__ __forceinline__ void issue1(uint4* slot, uint32_t kb, int j) const {
-    const uint32_t k0 = (kbase + kb) * BK;
-    const uint32_t off = (base[j] != kOOB && k0 + col[j] < Kr) ? base[j] + 2 * k0 : kOOB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(slot + (2 * wave + j) * 64), 16, off, 0, 0, 0);
+    if (FULLK) {
+      // whole steps only: the row offset stays in the lane's register and the step's column
+      // offset goes in the scalar offset; steps past the product reload its last step
+      const uint32_t kk = kbase + kb < kmax ? kbase + kb : kmax;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(slot + (2 * wave + j) * 64), 16, base[j], kk * (2 * BK), 0, 0);
+    } else {
+      const uint32_t k0 = (kbase + kb) * BK;
+      const uint32_t off = (base[j] != kOOB && k0 + col[j] < Kr) ? base[j] + 2 * k0 : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(slot + (2 * wave + j) * 64), 16, off, 0, 0, 0);
+    }
   }
+  template <bool FULLK>
   __device__ __forceinline__ void issue(uint4* slot, uint32_t kb) const {
-    issue1(slot, kb, 0);
-    issue1(slot, kb, 1);
+    issue1<FULLK>(slot, kb, 0);
+    issue1<FULLK>(slot, kb, 1);
   }
 };
 
@@ -334,7 +350,7 @@ __device__ __forceinline__ void tile_xy(int64_t& tx, int64_t& ty) {
 // loads are issued one at a time between groups of four MFMAs: a CU's address unit takes
 // one 1 KB load per ~16 clocks, and a burst at the top of the step would stall every
 // wavefront's (in-order) issue behind it.
-template <int S, bool ODD>
+template <int S, bool ODD, bool FULLK>
 __device__ __forceinline__ void nt_step(const Ring& ra, const Ring& rb, uint32_t kb, uint32_t nk, int wf, int wmt,
                                         int l32, int h32, Ops& o1, Acc& acc) {
   uint4* const na = abuf<(S + 3) % kRing>();
@@ -343,34 +359,34 @@ __device__ __forceinline__ void nt_step(const Ring& ra, const Ring& rb, uint32_t
   read_ops(abuf<S>(), bbuf<S>(), 0, wf, wmt, l32, h32, o0);
   mma_half(o1, 0, acc);  // ks = 1 of step kb - 1
   __builtin_amdgcn_sched_barrier(0);
-  ra.issue1(na, kb + 3, 0);
+  ra.issue1<FULLK>(na, kb + 3, 0);
   __builtin_amdgcn_sched_barrier(0);
   mma_half(o1, 1, acc);
   __builtin_amdgcn_sched_barrier(0);
-  ra.issue1(na, kb + 3, 1);
+  ra.issue1<FULLK>(na, kb + 3, 1);
   __builtin_amdgcn_sched_barrier(0);
   read_ops(abuf<S>(), bbuf<S>(), 1, wf, wmt, l32, h32, o1);
   mma_half(o0, 0, acc);
   __builtin_amdgcn_sched_barrier(0);
-  rb.issue1(nb, kb + 3, 0);
+  rb.issue1<FULLK>(nb, kb + 3, 0);
   __builtin_amdgcn_sched_barrier(0);
   mma_half(o0, 1, acc);
   __builtin_amdgcn_sched_barrier(0);
-  rb.issue1(nb, kb + 3, 1);
+  rb.issue1<FULLK>(nb, kb + 3, 1);
   if (ODD) {
     wait_vm<4>();  // this wavefront's loads of steps kb+1 and kb+2 are complete (kb+3's may be pending)
     lds_barrier();
   }
 }
 
-template <bool SPLIT>
+template <bool SPLIT, bool FULLK>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(const uint16_t* __restrict__ A, int64_t F,
                                                          const uint16_t* __restrict__ B, int64_t M, int64_t Kr,
                                                          const uint16_t* __restrict__ wl, int64_t wl_fs,
                                                          int64_t wl_js, const uint16_t* __restrict__ Lm, int32_t r,
                                                          uint16_t* __restrict__ C, float* __restrict__ part,
                                                          uint32_t kb_per) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, h32 = lane >> 5;
   const int wf = (wave & 1) * 128, wmt = (wave >> 1) * 64;
   int64_t tx, ty;
@@ -382,18 +398,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(const uint16_t* __restr
   const uint32_t nk = SPLIT ? (kb0 + kb_per <= nk_all ? kb_per : (kb0 < nk_all ? nk_all - kb0 : 0u)) : nk_all;
 
   Ring ra, rb;
-  ra.init(A, F, f0, Kr, wave, lane, kb0);
-  rb.init(B, M, m0, Kr, wave, lane, kb0);
+  ra.init<FULLK>(A, F, f0, Kr, wave, lane, kb0);
+  rb.init<FULLK>(B, M, m0, Kr, wave, lane, kb0);
   // steps 0..2 in flight while the adapter slices run through slot 4
-  ra.issue(abuf<0>(), 0);
-  rb.issue(bbuf<0>(), 0);
+  ra.issue<FULLK>(abuf<0>(), 0);
+  rb.issue<FULLK>(bbuf<0>(), 0);
   if (nk > 1) {
-    ra.issue(abuf<1>(), 1);
-    rb.issue(bbuf<1>(), 1);
+    ra.issue<FULLK>(abuf<1>(), 1);
+    rb.issue<FULLK>(bbuf<1>(), 1);
   }
   if (nk > 2) {
-    ra.issue(abuf<2>(), 2);
-    rb.issue(bbuf<2>(), 2);
+    ra.issue<FULLK>(abuf<2>(), 2);
+    rb.issue<FULLK>(bbuf<2>(), 2);
   }
   Acc acc;
 #pragma unroll
@@ -410,25 +426,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(const uint16_t* __restr
 #pragma unroll
   for (int j = 0; j < TJ; ++j) o1.b[j] = bf16x8_t{};
   for (uint32_t kb = 0; kb < nk; kb += 10) {
-    nt_step<0, false>(ra, rb, kb + 0, nk, wf, wmt, l32, h32, o1, acc);
+    nt_step<0, false, FULLK>(ra, rb, kb + 0, nk, wf, wmt, l32, h32, o1, acc);
     if (kb + 1 >= nk) break;
-    nt_step<1, true>(ra, rb, kb + 1, nk, wf, wmt, l32, h32, o1, acc);
+    nt_step<1, true, FULLK>(ra, rb, kb + 1, nk, wf, wmt, l32, h32, o1, acc);
     if (kb + 2 >= nk) break;
-    nt_step<2, false>(ra, rb, kb + 2, nk, wf, wmt, l32, h32, o1, acc);
+    nt_step<2, false, FULLK>(ra, rb, kb + 2, nk, wf, wmt, l32, h32, o1, acc);
     if (kb + 3 >= nk) break;
-    nt_step<3, true>(ra, rb, kb + 3, nk, wf, wmt, l32, h32, o1, acc);
+    nt_step<3, true, FULLK>(ra, rb, kb + 3, nk, wf, wmt, l32, h32, o1, acc);
     if (kb + 4 >= nk) break;
-    nt_step<4, false>(ra, rb, kb + 4, nk, wf, wmt, l32, h32, o1, acc);
+    nt_step<4, false, FULLK>(ra, rb, kb + 4, nk, wf, wmt, l32, h32, o1, acc);
     if (kb + 5 >= nk) break;
-    nt_step<0, true>(ra, rb, kb + 5, nk, wf, wmt, l32, h32, o1, acc);
+    nt_step<0, true, FULLK>(ra, rb, kb + 5, nk, wf, wmt, l32, h32, o1, acc);
     if (kb + 6 >= nk) break;
-    nt_step<1, false>(ra, rb, kb + 6, nk, wf, wmt, l32, h32, o1, acc);
+    nt_step<1, false, FULLK>(ra, rb, kb + 6, nk, wf, wmt, l32, h32, o1, acc);
     if (kb + 7 >= nk) break;
-    nt_step<2, true>(ra, rb, kb + 7, nk, wf, wmt, l32, h32, o1, acc);
+    nt_step<2, true, FULLK>(ra, rb, kb + 7, nk, wf, wmt, l32, h32, o1, acc);
     if (kb + 8 >= nk) break;
-    nt_step<3, false>(ra, rb, kb + 8, nk, wf, wmt, l32, h32, o1, acc);
+    nt_step<3, false, FULLK>(ra, rb, kb + 8, nk, wf, wmt, l32, h32, o1, acc);
     if (kb + 9 >= nk) break;
-    nt_step<4, true>(ra, rb, kb + 9, nk, wf, wmt, l32, h32, o1, acc);
+    nt_step<4, true, FULLK>(ra, rb, kb + 9, nk, wf, wmt, l32, h32, o1, acc);
   }
   mma(o1, acc);  // ks = 1 of the last step
   wait_vm<0>();   // the loads issued past the range have landed
@@ -458,12 +474,17 @@ hipError_t launch_gemm_nt(const uint16_t* A, int64_t F, const uint16_t* B, int64
   const uint32_t kb_per = ksplit > 1 ? (uint32_t)((nk + ksplit - 1) / ksplit) : (uint32_t)nk;
   dim3 grid((unsigned)((F + BF - 1) / BF), (unsigned)((M + BMT - 1) / BMT), (unsigned)(ksplit > 1 ? ksplit : 1));
   LaunchTimer t(kernel_id, st);
-  if (ksplit > 1)
-    hipExtLaunchKernelGGL(k_gemm_nt<true>, grid, dim3(kThreads), 0, st, t.start, t.stop, 0, A, F, B, M, Kr, wl, wl_fs,
-                          wl_js, L, r, C, part, kb_per);
+  const bool fullk = Kr % BK == 0;
+#define GEMM_ARGS A, F, B, M, Kr, wl, wl_fs, wl_js, L, r, C, part, kb_per
+  if (ksplit > 1 && fullk)
+    hipExtLaunchKernelGGL(k_gemm_nt<true, true>, grid, dim3(kThreads), 0, st, t.start, t.stop, 0, GEMM_ARGS);
+  else if (ksplit > 1)
+    hipExtLaunchKernelGGL(k_gemm_nt<true, false>, grid, dim3(kThreads), 0, st, t.start, t.stop, 0, GEMM_ARGS);
+  else if (fullk)
+    hipExtLaunchKernelGGL(k_gemm_nt<false, true>, grid, dim3(kThreads), 0, st, t.start, t.stop, 0, GEMM_ARGS);
   else
-    hipExtLaunchKernelGGL(k_gemm_nt<false>, grid, dim3(kThreads), 0, st, t.start, t.stop, 0, A, F, B, M, Kr, wl, wl_fs,
-                          wl_js, L, r, C, part, kb_per);
+    hipExtLaunchKernelGGL(k_gemm_nt<false, false>, grid, dim3(kThreads), 0, st, t.start, t.stop, 0, GEMM_ARGS);
+#undef GEMM_ARGS
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || ksplit <= 1) return e;
   const int64_t n8 = M * F / 8;
