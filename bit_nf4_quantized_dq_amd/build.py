@@ -45,12 +45,53 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# Private (scratch) memory per lane that a kernel may use; every other kernel must use none.
+# A kernel that starts spilling registers runs many times slower (a fused reduction split once
+# went from 6.9 to 11 ms per 8B-shaped layer step that way), so the build refuses it.
+SCRATCH_ALLOWANCE = {
+    "k_gemm_dx": 8,  # one spilled register in the fused mid-size dX kernel
+}
+
+
+def _kernel_resources(stderr: str) -> list[tuple[str, int, int]]:
+    """(kernel name, VGPRs, scratch bytes per lane) from the compiler's resource remarks."""
+    out, name, vgpr = [], None, 0
+    for line in stderr.splitlines():
+        if "remark:" not in line:
+            continue
+        text = line.split("remark:", 1)[1].split("[-Rpass", 1)[0].strip()
+        if text.startswith("Function Name:"):
+            name = text.split(":", 1)[1].strip()
+        elif text.startswith("VGPRs:") and name:
+            vgpr = int(text.split(":", 1)[1])
+        elif text.startswith("ScratchSize") and name:
+            out.append((name, vgpr, int(text.split(":", 1)[1])))
+            name = None
+    return out
+
+
+def _short(mangled: str) -> str:
+    """The kernel's own name inside an Itanium-mangled symbol: a decimal length, then the name
+    (the digits before it may also end the anonymous namespace's tag, so each split of them
+    is tried, shortest length first)."""
+    import re
+
+    for m in re.finditer(r"(\d+)k_", mangled):
+        digits, start = m.group(1), m.end(1)
+        for i in range(len(digits) - 1, -1, -1):
+            n = int(digits[i:])
+            name = mangled[start:start + n]
+            if len(name) == n and re.fullmatch(r"k_[a-z0-9_]+", name):
+                return name
+    return mangled
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
     path = os.path.join(CSRC, src)
     cmd = [_hipcc(), *COMMON]
     if src.endswith(".hip"):
-        cmd += ["-x", "hip", *DEVICE]
+        cmd += ["-x", "hip", *DEVICE, "-Rpass-analysis=kernel-resource-usage"]
     else:
         cmd += ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include"]  # host-only units
     cmd += ["-c", path, "-o", obj]
@@ -59,6 +100,14 @@ def _compile(src: str, verbose: bool) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {src}\n{r.stdout}\n{r.stderr}")
+    if src.endswith(".hip"):
+        res = _kernel_resources(r.stderr)
+        with open(os.path.splitext(obj)[0] + ".resources.txt", "w") as f:
+            for name, vgpr, scratch in res:
+                f.write(f"{name} vgpr={vgpr} scratch={scratch}\n")
+        bad = [(n, sc) for n, _, sc in res if sc > SCRATCH_ALLOWANCE.get(_short(n), 0)]
+        if bad:
+            raise RuntimeError(f"{src}: kernels use scratch memory (spilled registers): {bad}")
     return obj
 
 

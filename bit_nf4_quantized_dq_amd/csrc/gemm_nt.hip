@@ -155,15 +155,13 @@ __device__ __forceinline__ void mma_half(const Ops& o, int h, Acc& acc) {
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = mfma32(o.a[i], o.b[j], acc[i][j]);
 }
-// One 32-wide step; `second` false when reduction indices 16..31 of the step are all past
-// the end (they would add exact zeros).
 __device__ __forceinline__ void mma_step(const uint4* __restrict__ sa, const uint4* __restrict__ sb, int wf,
-                                         int wmt, int l32, int h32, Acc& acc, bool second) {
+                                         int wmt, int l32, int h32, Acc& acc) {
   Ops o0, o1;
   read_ops(sa, sb, 0, wf, wmt, l32, h32, o0);
-  if (second) read_ops(sa, sb, 1, wf, wmt, l32, h32, o1);
+  read_ops(sa, sb, 1, wf, wmt, l32, h32, o1);
   mma(o0, acc);
-  if (second) mma(o1, acc);
+  mma(o1, acc);
 }
 
 // Adapter slices of 32: acc[f][m] += sum_j Wl(f, j) * L[m][j] for j < r, Wl(f, j) at
@@ -217,7 +215,7 @@ __device__ __forceinline__ void adapter(const uint16_t* __restrict__ wl, int64_t
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) dst[swz(row, c)] = c4[c];
     lds_barrier();
-    mma_step(abuf<4>(), bbuf<4>(), wf, wmt, l32, h32, acc, j0 + BK / 2 < r);
+    mma_step(abuf<4>(), bbuf<4>(), wf, wmt, l32, h32, acc);
   }
 }
 
@@ -357,15 +355,13 @@ __device__ __forceinline__ void nt_step(const Ring& ra, const Ring& rb, uint32_t
                                         int l32, int h32, Ops& o1, Acc& acc) {
   uint4* const na = abuf<(S + 3) % kRing>();
   uint4* const nb = bbuf<(S + 3) % kRing>();
-  // ks = 1 of step kb - 1 (none before step 0)
-  const bool prev = !(S == 0 && !ODD) || kb != 0;
   Ops o0;
   read_ops(abuf<S>(), bbuf<S>(), 0, wf, wmt, l32, h32, o0);
-  if (prev) mma_half(o1, 0, acc);
+  mma_half(o1, 0, acc);  // ks = 1 of step kb - 1
   __builtin_amdgcn_sched_barrier(0);
   ra.issue1<FULLK>(na, kb + 3, 0);
   __builtin_amdgcn_sched_barrier(0);
-  if (prev) mma_half(o1, 1, acc);
+  mma_half(o1, 1, acc);
   __builtin_amdgcn_sched_barrier(0);
   ra.issue1<FULLK>(na, kb + 3, 1);
   __builtin_amdgcn_sched_barrier(0);
@@ -424,7 +420,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nt(const uint16_t* __restr
   wait_vm<0>();
   lds_barrier();  // steps 0, 1 landed everywhere; the adapter's reads of slot 4 are done
 
-  Ops o1;  // deferred second half of the previous step (unused before step 0)
+  Ops o1;  // deferred second half of the previous step: none before step 0
 #pragma unroll
   for (int i = 0; i < TI; ++i) o1.a[i] = bf16x8_t{};
 #pragma unroll

@@ -35,6 +35,14 @@ namespace qlora {
 
 namespace {
 
+// Workgroup barrier that waits for this wavefront's LDS accesses only (lgkmcnt), so global
+// loads in flight stay in flight across it.  Every barrier here orders LDS traffic between
+// the wavefronts; none orders global memory.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
+
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kTiles = 1;               // column tiles (16 rows) per wavefront
@@ -241,7 +249,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_fused(GemvArgs a, Nf4Tables T
 #pragma unroll
       for (int q = 0; q < kRStage / 8; ++q) sB[tid][q] = bpre[q];
     }
-    __syncthreads();
+    lds_barrier();
     if (u < nb) {
       const bf16x8_t xa = as_bf16x8(S.x[l16][8 * u + 2 * g]);
       const bf16x8_t xb = as_bf16x8(S.x[l16][8 * u + 2 * g + 1]);
@@ -253,14 +261,14 @@ __global__ __launch_bounds__(kThreads) void k_gemv_fused(GemvArgs a, Nf4Tables T
     }
 #pragma unroll
     for (int j = 0; j < RT; ++j) sred[wave][j][lane] = tacc[j];
-    __syncthreads();
+    lds_barrier();
     for (int i = tid; i < 16 * 16 * RT; i += kThreads) {
       const int j16 = i / 256, rem = i % 256, ln = rem / 4, v = rem % 4;  // D[m = 4*(ln>>4)+v][j = ln & 15]
       float s = sred[0][j16][ln][v];
       for (int w = 1; w < kWaves; ++w) s += sred[w][j16][ln][v];
       sT[4 * (ln >> 4) + v][16 * j16 + (ln & 15)] = s;
     }
-    __syncthreads();
+    lds_barrier();
     for (int32_t j0 = 0; j0 < a.r; j0 += 32) {  // r <= 32 here, so B comes from LDS or element loads
       const int32_t jj = j0 + 8 * g;
       uint32_t tv[4];
@@ -296,7 +304,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_fused(GemvArgs a, Nf4Tables T
       S.codes[srow][4 * ub + 3] = make_uint2(cv[v][1].z, cv[v][1].w);
       S.scale[srow][ub] = block_scale(c8[v], __uint_as_float(c2[v]), mu);
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int ub = 0; ub < kChunk; ++ub) {
       const bf16x8_t xa = as_bf16x8(S.x[l16][8 * ub + 2 * g]);
@@ -340,9 +348,9 @@ __global__ __launch_bounds__(kThreads) void k_gemv_fused(GemvArgs a, Nf4Tables T
 #pragma unroll
         for (int q = 0; q < kTA; ++q) load_a(kWaves * q + wave, av[q]);
       }
-      __syncthreads();  // the previous chunk's LDS reads are done
+      lds_barrier();  // the previous chunk's LDS reads are done
       stage(R);
-      __syncthreads();
+      lds_barrier();
       if (c0 + kChunk < b1) issue(c0 + kChunk, R);  // next chunk in flight during this one's math
 
       // ---- adapter down-projection share of this wavefront: blocks u = wave (mod kWaves)
@@ -399,14 +407,14 @@ __global__ __launch_bounds__(kThreads) void k_gemv_fused(GemvArgs a, Nf4Tables T
     // ---- T over this k-range: sum the wavefronts' shares -> sT[m][j]
 #pragma unroll
     for (int j = 0; j < RT; ++j) sred[wave][j][lane] = tacc[j];
-    __syncthreads();
+    lds_barrier();
     for (int i = tid; i < 16 * 16 * RT; i += kThreads) {
       const int j16 = i / 256, rem = i % 256, ln = rem / 4, v = rem % 4;  // D[m = 4*(ln>>4)+v][j = ln & 15]
       float s = sred[0][j16][ln][v];
       for (int w = 1; w < kWaves; ++w) s += sred[w][j16][ln][v];
       sT[4 * (ln >> 4) + v][16 * j16 + (ln & 15)] = s;
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- adapter up-projection of this partial T: acc[t][m][n] += s * sum_j T[m][j] B[n][j]
     const bool b_staged = (a.r % 8) == 0 && a.r <= kRStage;

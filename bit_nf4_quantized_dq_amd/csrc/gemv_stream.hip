@@ -61,6 +61,14 @@ constexpr int kRegion = 87 * 1024;       // activations, block constants, scales
 constexpr int kC8Loads = 24;             // staged block-constant dwords per thread, at most
 constexpr int kSumU = 16;                // partials loaded together in the split-K sum
 
+// Workgroup barrier that waits for this wavefront's LDS accesses only (lgkmcnt), so global
+// loads in flight stay in flight across it.  Every barrier here orders LDS traffic between
+// the wavefronts; none orders global memory.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -293,7 +301,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L, t
     const int d = u * kThreads + tid;
     if (u * kThreads < dwords && d < dwords) reinterpret_cast<uint32_t*>(sR + a.c8off)[d] = c8v[u];
   }
-  __syncthreads();
+  lds_barrier();
 
   const uint32_t lane4 = (uint32_t)lane * 4u;
   // activation rows of this lane (rows >= M read the zero row): 32x32 operand and 16x16 operand
@@ -358,12 +366,12 @@ __global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L, t
   }
 
   // ---- T over this range: sum the wavefronts' parts
-  __syncthreads();  // every wavefront is done with the staged region
+  lds_barrier();  // every wavefront is done with the staged region
   float* sred = reinterpret_cast<float*>(sR);  // [kWaves][RT16][64][4]
 #pragma unroll
   for (int k = 0; k < RT16; ++k)
     *reinterpret_cast<f32x4_t*>(sred + ((wave * RT16 + k) * 64 + lane) * 4) = tacc[k];
-  __syncthreads();
+  lds_barrier();
   for (int i = tid; i < M * a.r; i += kThreads) {
     const int m = i / a.r, j = i % a.r;
     const int k = j / 16, ln = (j % 16) + 16 * (m / 4), v = m % 4;  // D[m = 4 (lane >> 4) + v][j = lane & 15]
@@ -371,7 +379,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L, t
     for (int w = 0; w < kWaves; ++w) sum += sred[((w * RT16 + k) * 64 + ln) * 4 + v];
     sT[m][j] = sum;
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- adapter up-projection of this partial T: rows n of this wavefront
   {
