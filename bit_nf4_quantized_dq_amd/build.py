@@ -73,7 +73,8 @@ def _kernel_resources(stderr: str) -> list[tuple[str, int, int]]:
 def _short(mangled: str) -> str:
     """The kernel's own name inside an Itanium-mangled symbol: a decimal length, then the name
     (the digits before it may also end the anonymous namespace's tag, so each split of them
-    is tried, shortest length first)."""
+    is tried; the name is the one that ends where the nested name or its template arguments
+    begin)."""
     import re
 
     for m in re.finditer(r"(\d+)k_", mangled):
@@ -81,7 +82,8 @@ def _short(mangled: str) -> str:
         for i in range(len(digits) - 1, -1, -1):
             n = int(digits[i:])
             name = mangled[start:start + n]
-            if len(name) == n and re.fullmatch(r"k_[a-z0-9_]+", name):
+            after = mangled[start + n:start + n + 1]
+            if len(name) == n and re.fullmatch(r"k_[a-z0-9_]+", name) and after in ("E", "I"):
                 return name
     return mangled
 
