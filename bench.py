@@ -28,8 +28,9 @@ workload.
 The default warm-up (about 30 ms of steps) lets the clock under sustained MFMA load settle:
 on a fresh box the first ~60 steps run up to 13% slower than the rest.
   python bench.py --pmc-pass    # 2 steps, one merge, one AdamW step, two M = 1 and two
-                                # M = 16 calls on the step's weight, two M = 1 calls on a
-                                # 28672x8192 weight and a 256 MiB device copy (the counter
+                                # M = 16 calls on the step's weight, two M = 1 calls and one
+                                # M = 2048 call on a 28672x8192 weight, one M = 2048 call on a
+                                # 1024x8192 weight and a 256 MiB device copy (the counter
                                 # calibration), for counter runs
 """
 
@@ -577,7 +578,16 @@ def main():
         Ag, Bg = I.lora_A(5, 4, r, 8192, device=dev), I.lora_B(5, 4, 28672, r, device=dev)
         for _ in range(2):
             Q.linear_fwd(qg, Xg, Ag, Bg, alpha)
+        # the decode-once path at M = 2048 on the same weight, and on a 1024 x 8192 one (the k
+        # and v shape of the 70B-class model, whose product takes the split reduction)
+        X2k = I.activations(5, 5, 2048, 8192, device=dev)
+        Q.linear_fwd(qg, X2k, Ag, Bg, alpha)
         del qg
+        Wk = I.weight(5, 6, 1024, 8192, 0.015, device=dev)
+        qk = Q.quantize(Wk)
+        del Wk
+        Q.linear_fwd(qk, X2k, Ag, I.lora_B(5, 6, 1024, r, device=dev), alpha)
+        del qk, X2k
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         src.fill_(1)

@@ -316,19 +316,39 @@ __global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ P, 
 }
 
 // Consecutive workgroups are dealt round-robin to the 8 XCDs (each with its own L2):
-// renumber so that one XCD gets a contiguous run of tiles.  When the feature tiles divide
-// into columns of 4 that split the grid into 8 equal blocks (4 feature tiles x n/32 token
-// tiles), each XCD takes one block: at 16 x 16 tiles its L2 then sees 4 weight row blocks
-// and 8 token row blocks per reduction step instead of 16 and 2.  Otherwise it takes a run in
-// feature-fastest order.
+// renumber so that one XCD gets a compact block of tiles.
+// - When the feature tiles divide into columns of 4 that split the grid into 8 equal blocks
+//   (4 feature tiles x n/32 token tiles; up to 32 feature tiles), each XCD takes one block:
+//   at 16 x 16 tiles its L2 then sees 4 weight row blocks and 8 token row blocks per
+//   reduction step instead of 16 and 2.
+// - Wider products (feature tiles a multiple of 8, more than 32 of them) give each XCD its
+//   own gx/8 feature columns over all token tiles, walked in bands of bw columns (the largest
+//   divisor of gx/8 up to 8), columns fastest: each weight row block then goes to one XCD
+//   only, and the 32 workgroups an XCD runs at once cover about bw columns x 32/bw token
+//   tiles.  Taking runs in feature-fastest order instead sent every weight row block to all
+//   8 XCDs (28672 x 8192 at M = 2048: 4.97 GB fetched from beyond the L2s per launch).
+// - Otherwise each XCD takes a run in feature-fastest order.
 __device__ __forceinline__ void tile_xy(int64_t& tx, int64_t& ty) {
-  const uint32_t gx = gridDim.x, n = gridDim.x * gridDim.y;
+  const uint32_t gx = gridDim.x, gy = gridDim.y, n = gridDim.x * gridDim.y;
   uint32_t L = blockIdx.x + gx * blockIdx.y;
   if ((n & 31) == 0 && gx % 4 == 0 && 32 % gx == 0) {
     L = (L & 7) * (n >> 3) + (L >> 3);
     const uint32_t per = n >> 3, xcd = L / per, w = L % per, cols = gx / 4;
     tx = (xcd % cols) * 4 + (w % 4);
     ty = (xcd / cols) * (per / 4) + w / 4;
+    return;
+  }
+  if (gx % 8 == 0) {
+    const uint32_t xcd = L & 7, idx = L >> 3, cx = gx >> 3;
+    uint32_t bw = 1;
+    for (uint32_t d = 8; d > 1; --d)
+      if (cx % d == 0) {
+        bw = d;
+        break;
+      }
+    const uint32_t band = idx / (bw * gy), r = idx % (bw * gy);
+    tx = xcd * cx + band * bw + r % bw;
+    ty = r / bw;
     return;
   }
   if ((n & 7) == 0) L = (L & 7) * (n >> 3) + (L >> 3);
