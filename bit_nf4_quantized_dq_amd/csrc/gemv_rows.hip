@@ -23,12 +23,14 @@
 // accumulator.  Tokens past M read row M - 1, whose products land in output rows that are
 // never written.  The eight wavefronts' sums meet in LDS in a fixed order.
 //
-// Adapter.  T = X A^T needs the whole reduction, so workgroup j < r first forms column j of T
-// (MFMA with row j of A, parked in LDS beside X, as the only operand column; the codes are in
-// flight meanwhile) and writes bf16(s T[m][j]) with a tag into a private block of words of
-// every workgroup, in the workspace head.  Each workgroup, after its rows, reads its M x r
-// words until all carry the tag, clears them, applies (s T) B^T for its rows on MFMA and
-// writes Y.  Each word block is read and cleared by its one owner, so the head is zero again
+// Adapter.  T = X A^T needs the whole reduction, so workgroup j < r forms column j of T first:
+// each wavefront takes the dot product of its X slices with its slice of row j of A in
+// registers (8 products per lane, then a fixed-order sum across the lanes) and parks it in LDS
+// before the barrier that publishes the X slices, so T[m][j] is complete right after that
+// barrier, while the codes are still in flight.  The workgroup then writes bf16(s T[m][j])
+// with a tag into a private block of words of every workgroup, in the workspace head.  Each
+// workgroup, after its rows, reads its M x r words until all carry the tag, applies (s T) B^T
+// for its rows on MFMA, writes Y and then clears the words.  Each word block is read and cleared by its one owner, so the head is zero again
 // after every call and a stale T is never taken for a new one, with no counter shared between
 // workgroups.  Workgroups 0 .. r-1 are dispatched first and write T before they wait on
 // anything, so no reader waits on a workgroup that has not started.
@@ -66,9 +68,9 @@ struct RowsArgs {
 template <int NBW>
 struct RowsLds {
   uint32_t pair[256 * 64];
-  uint4 x[kWaves][kMaxM + 1][8 * NBW];  // X rows 0..M-1 of the slice, then row c of A (T)
+  uint4 x[kWaves][kMaxM][8 * NBW];  // X rows 0..M-1 of the slice
   f32x4_t red[kWaves][64];
-  float t[16];
+  float tp[kWaves][kMaxM];  // per wavefront: its slice's part of T[m][c] (workgroup c < r)
 };
 
 // Workgroup barrier that waits for this wavefront's LDS accesses only, so global loads in
@@ -86,6 +88,26 @@ __device__ __forceinline__ uint32_t byte_of(uint2 w, int i) {
 __device__ __forceinline__ uint4 nibble_order(uint4 v) {
   return make_uint4(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u), __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
                     __builtin_amdgcn_perm(v.w, v.y, 0x05040100u), __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
+}
+
+// Sum over the 64 lanes in a fixed order, the same in every lane (all 64 lanes must be active):
+// within each row of 16 lanes
+// by DPP (lane pairs, then quads, half rows and rows, each step adding the mirrored partner,
+// so both partners form the same sum), then the four row sums in order.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_partner(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_partner<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_partner<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_partner<0x141>(v);  // row_half_mirror
+  v += dpp_partner<0x140>(v);  // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return ((r0 + r1) + r2) + r3;
 }
 
 // BF16 bits of the levels named by the four index bytes of idx (values 0..15), one per
@@ -176,11 +198,29 @@ __global__ __launch_bounds__(kThreads) void k_gemv_rows(RowsArgs a, Lut L) {
 #pragma unroll
   for (int b = 0; b < NBW; ++b) cr[b] = bload8(rc, (uint32_t)(l16 * (K / 2) + 32 * (b0 + b) + 8 * g));
 
-  // ---- while the codes travel: the byte-pair table, the X (and A) slices
+  // ---- while the codes travel: the byte-pair table, the X slices and this wavefront's part
+  // of column c of T (zero outside the producers, whose A slice is read out of range)
   build_pairs(L, S.pair, wave, lane);
 #pragma unroll
-  for (int m = 0; m < kMaxM + 1; ++m)
-    if ((m < M || (m == kMaxM && producer)) && lane < 8 * NBW) S.x[wave][m == kMaxM ? M : m][lane] = nibble_order(xv[m]);
+  for (int m = 0; m < kMaxM; ++m)
+    if (m < M && lane < 8 * NBW) S.x[wave][m][lane] = nibble_order(xv[m]);
+  {
+    const uint32_t av[4] = {xv[kMaxM].x, xv[kMaxM].y, xv[kMaxM].z, xv[kMaxM].w};
+#pragma unroll
+    for (int m = 0; m < kMaxM; ++m) {
+      const uint32_t xw[4] = {xv[m].x, xv[m].y, xv[m].z, xv[m].w};
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        d = fmaf(bf16lo_to_f32(xw[e]), bf16lo_to_f32(av[e]), d);
+        d = fmaf(bf16hi_to_f32(xw[e]), bf16hi_to_f32(av[e]), d);
+      }
+      if (m < M) {  // uniform: every lane takes part in the sum
+        const float t = wave_sum(d);
+        if (lane == 0) S.tp[wave][m] = t;
+      }
+    }
+  }
   lds_barrier();
 
   // every X operand of the wavefront's blocks into registers at once (one LDS wait)
@@ -192,40 +232,17 @@ __global__ __launch_bounds__(kThreads) void k_gemv_rows(RowsArgs a, Lut L) {
     for (int s = 0; s < 2; ++s) xo[b][s] = S.x[wave][mx][8 * b + 2 * g + s];
   const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
 
-  // ---- workgroup c < r: column c of T into every workgroup's words
+  // ---- workgroup c < r: column c of T (the wavefronts' parts in a fixed order) into every
+  // workgroup's words
   if (producer) {
-    uint4 ao[NBW][2];  // row c of A as operand column 0 (lanes with l16 == 0), read at once
-#pragma unroll
-    for (int b = 0; b < NBW; ++b)
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const uint4 v = S.x[wave][M][8 * b + 2 * g + s];
-        ao[b][s] = l16 == 0 ? v : make_uint4(0, 0, 0, 0);
-      }
-    f32x4_t t = z;
-#pragma unroll
-    for (int b = 0; b < NBW; ++b)
-#pragma unroll
-      for (int s = 0; s < 2; ++s) t = mfma16x16x32(as_bf16x8(xo[b][s]), as_bf16x8(ao[b][s]), t);
-    S.red[wave][lane] = t;
-    lds_barrier();
-    if (wave == 0 && l16 == 0) {  // lanes 0, 16, 32, 48 hold T[m = 4 g + v][c]
-      f32x4_t sum = S.red[0][lane];
-      for (int w = 1; w < kWaves; ++w) {
-        const f32x4_t v = S.red[w][lane];
-        sum[0] += v[0]; sum[1] += v[1]; sum[2] += v[2]; sum[3] += v[3];
-      }
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int mm = 4 * g + v;
-        S.t[mm] = sum[v];
-        if (mm < M && a.T_save) a.T_save[mm * r + c] = (uint16_t)(pack_bf16x2(sum[v], 0.f) & 0xFFFFu);
-      }
-    }
-    lds_barrier();
     const int nwg = (int)gridDim.x;
     for (int i = tid; i < nwg * M; i += kThreads) {  // word (workgroup i / M, token i % M)
-      const uint32_t w = kTag | (pack_bf16x2(a.s * S.t[i % M], 0.f) & 0xFFFFu);
+      const int m = i % M;
+      float t = S.tp[0][m];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) t += S.tp[w][m];
+      if (i < M && a.T_save) a.T_save[m * r + c] = (uint16_t)(pack_bf16x2(t, 0.f) & 0xFFFFu);
+      const uint32_t w = kTag | (pack_bf16x2(a.s * t, 0.f) & 0xFFFFu);
       __hip_atomic_store(a.words + (int64_t)i * r + c, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
   }
@@ -252,15 +269,20 @@ __global__ __launch_bounds__(kThreads) void k_gemv_rows(RowsArgs a, Lut L) {
     acc[3] = fmaf(cb, p[3], acc[3]);
   }
   S.red[wave][lane] = acc;
-  // wavefront 0 issues its first read of the T words before the barrier (they were written
-  // long before, so the read is usually the only one)
+  // wavefront 0 issues its first read of the T words (they were written long before, so the
+  // read is usually the only one) and the B rows of the first rank step before the barrier,
+  // so that both travel while the other wavefronts finish
   uint32_t* mine = a.words + (int64_t)c * M * r;
-  uint32_t tw[8];
+  const rsrc_t rb = make_rsrc(a.B, N * r * 2);
+  uint32_t tw[8], e[8];  // e: B[n][8 g .. 8 g + 7], element loads (B carries no alignment promise)
   if (wave == 0) {
     const bool live0 = l16 < M && 8 * g < r;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       tw[i] = live0 ? __hip_atomic_load(mine + l16 * r + 8 * g + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) : kTag;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      e[i] = __builtin_amdgcn_raw_buffer_load_b16(rb, 8 * g < r ? (int)((n * r + 8 * g + i) * 2) : (int)kOOB, 0, 0);
   }
   lds_barrier();
   if (wave != 0) return;
@@ -271,15 +293,15 @@ __global__ __launch_bounds__(kThreads) void k_gemv_rows(RowsArgs a, Lut L) {
     const f32x4_t v = S.red[w][lane];
     y[0] += v[0]; y[1] += v[1]; y[2] += v[2]; y[3] += v[3];
   }
-  const rsrc_t rb = make_rsrc(a.B, N * r * 2);
   for (int q0 = 0; q0 < r; q0 += 32) {
     // A operand: bf16(s T[m][q0 + 8 g .. +7]) from this workgroup's words; B operand: B[n][same]
     const int j0 = q0 + 8 * g;
     const bool live = l16 < M && j0 < r;  // r % 8 == 0: a live lane's 8 ranks all exist
-    uint32_t e[8];  // B[n][j0 .. j0 + 7], element loads (B carries no alignment promise)
+    if (q0) {  // later rank steps: B rows loaded here (the first step's came with its words)
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      e[i] = __builtin_amdgcn_raw_buffer_load_b16(rb, j0 < r ? (int)((n * r + j0 + i) * 2) : (int)kOOB, 0, 0);
+      for (int i = 0; i < 8; ++i)
+        e[i] = __builtin_amdgcn_raw_buffer_load_b16(rb, j0 < r ? (int)((n * r + j0 + i) * 2) : (int)kOOB, 0, 0);
+    }
     bool ready = false;
     // bounded wait (about 2^20 polls): should the words never arrive, the outputs become NaN
     // instead of the wavefront spinning forever.  The first step's first read was issued above.
@@ -298,10 +320,6 @@ __global__ __launch_bounds__(kThreads) void k_gemv_rows(RowsArgs a, Lut L) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) tw[i] = kTag | 0x7FC0u;
     }
-    if (live) {  // read: clear for the next call
-#pragma unroll
-      for (int i = 0; i < 8; ++i) __hip_atomic_store(mine + l16 * r + j0 + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    }
     uint32_t tv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) tv[i] = live ? ((tw[2 * i] & 0xFFFFu) | (tw[2 * i + 1] << 16)) : 0u;
@@ -313,6 +331,15 @@ __global__ __launch_bounds__(kThreads) void k_gemv_rows(RowsArgs a, Lut L) {
   for (int v = 0; v < 4; ++v) {
     const int mm = 4 * g + v;
     if (mm < M) a.Y[mm * N + n] = (uint16_t)(pack_bf16x2(y[v], 0.f) & 0xFFFFu);
+  }
+  // the words read, cleared for the next call: after the stores of Y, which then wait for
+  // nothing but the loads they use
+  for (int q0 = 0; q0 < r; q0 += 32) {
+    const int j0 = q0 + 8 * g;
+    if (l16 < M && j0 < r) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) __hip_atomic_store(mine + l16 * r + j0 + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
   }
 }
 
