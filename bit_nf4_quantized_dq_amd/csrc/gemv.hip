@@ -90,6 +90,35 @@ __device__ __forceinline__ float sum_published(const float* p, int32_t n, int64_
   return s;
 }
 
+// The same fixed-order sum for up to kSumOut outputs of one thread at once (output i0 + o
+// kThreads, o < kSumOut, of `total`; output i is Y[i / nrows][row0 + i % nrows] of a row-major
+// [M][N] partial), all of their loads issued before any is summed.
+constexpr int kSumOut = 4;
+constexpr int kSumOutU = 8;  // partials per output loaded together there
+__device__ __forceinline__ void sum_published_n(const float* part, int64_t i0, int64_t total, int64_t nrows,
+                                                int64_t row0, int64_t N, int32_t n, int64_t stride,
+                                                float (&sum)[kSumOut]) {
+#pragma unroll
+  for (int o = 0; o < kSumOut; ++o) sum[o] = 0.f;
+  for (int32_t k0 = 0; k0 < n; k0 += kSumOutU) {
+    float v[kSumOut][kSumOutU];
+#pragma unroll
+    for (int o = 0; o < kSumOut; ++o) {
+      const int64_t i = i0 + (int64_t)o * kThreads;
+      const float* p = part + (i / nrows) * N + row0 + i % nrows;
+#pragma unroll
+      for (int u = 0; u < kSumOutU; ++u)
+        v[o][u] = (i < total && k0 + u < n)
+                      ? __hip_atomic_load(p + (int64_t)(k0 + u) * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)
+                      : 0.f;
+    }
+#pragma unroll
+    for (int o = 0; o < kSumOut; ++o)
+#pragma unroll
+      for (int u = 0; u < kSumOutU; ++u) sum[o] += v[o][u];
+  }
+}
+
 // Rows are padded so the 16 lanes that read 16 consecutive rows hit distinct LDS banks.
 struct Stage {
   uint2 codes[kRows][kChunk * 4 + 1];  // row, (block, 8-byte part g) at 4 * block + g
@@ -489,11 +518,17 @@ __global__ __launch_bounds__(kThreads) void k_gemv_fused(GemvArgs a, Nf4Tables T
   }
   __syncthreads();
   if (!s_last) return;
-  // last workgroup of this row group: fixed-order sum of the partials
+  // last workgroup of this row group: fixed-order sum of the partials, the loads of up to
+  // kSumOut outputs per thread in flight together
   const int64_t nrows = (row0 + kRows <= N) ? kRows : N - row0;
-  for (int64_t i = tid; i < M * nrows; i += kThreads) {
-    const int64_t m = i / nrows, n = row0 + i % nrows;
-    a.Y[m * N + n] = (uint16_t)(pack_bf16x2(sum_published(a.part + m * N + n, a.ksplit, M * N), 0.f) & 0xFFFFu);
+  for (int64_t i0 = tid; i0 < M * nrows; i0 += (int64_t)kThreads * kSumOut) {
+    float sum[kSumOut];
+    sum_published_n(a.part, i0, M * nrows, nrows, row0, N, a.ksplit, M * N, sum);
+#pragma unroll
+    for (int o = 0; o < kSumOut; ++o) {
+      const int64_t i = i0 + (int64_t)o * kThreads;
+      if (i < M * nrows) a.Y[(i / nrows) * N + row0 + i % nrows] = (uint16_t)(pack_bf16x2(sum[o], 0.f) & 0xFFFFu);
+    }
   }
   if (a.T_save && grp == 0) {
     for (int i = tid; i < M * a.r; i += kThreads)
