@@ -518,16 +518,24 @@ __global__ __launch_bounds__(kThreads) void k_gemv_fused(GemvArgs a, Nf4Tables T
   }
   __syncthreads();
   if (!s_last) return;
-  // last workgroup of this row group: fixed-order sum of the partials, the loads of up to
-  // kSumOut outputs per thread in flight together
+  // last workgroup of this row group: fixed-order sum of the partials.  With one output per
+  // thread, kSumU partials per round trip; with more, the loads of up to kSumOut outputs per
+  // thread in flight together.
   const int64_t nrows = (row0 + kRows <= N) ? kRows : N - row0;
-  for (int64_t i0 = tid; i0 < M * nrows; i0 += (int64_t)kThreads * kSumOut) {
-    float sum[kSumOut];
-    sum_published_n(a.part, i0, M * nrows, nrows, row0, N, a.ksplit, M * N, sum);
+  if (M * nrows <= kThreads) {
+    if (tid < M * nrows) {
+      const int64_t m = tid / nrows, n = row0 + tid % nrows;
+      a.Y[m * N + n] = (uint16_t)(pack_bf16x2(sum_published(a.part + m * N + n, a.ksplit, M * N), 0.f) & 0xFFFFu);
+    }
+  } else {
+    for (int64_t i0 = tid; i0 < M * nrows; i0 += (int64_t)kThreads * kSumOut) {
+      float sum[kSumOut];
+      sum_published_n(a.part, i0, M * nrows, nrows, row0, N, a.ksplit, M * N, sum);
 #pragma unroll
-    for (int o = 0; o < kSumOut; ++o) {
-      const int64_t i = i0 + (int64_t)o * kThreads;
-      if (i < M * nrows) a.Y[(i / nrows) * N + row0 + i % nrows] = (uint16_t)(pack_bf16x2(sum[o], 0.f) & 0xFFFFu);
+      for (int o = 0; o < kSumOut; ++o) {
+        const int64_t i = i0 + (int64_t)o * kThreads;
+        if (i < M * nrows) a.Y[(i / nrows) * N + row0 + i % nrows] = (uint16_t)(pack_bf16x2(sum[o], 0.f) & 0xFFFFu);
+      }
     }
   }
   if (a.T_save && grp == 0) {
