@@ -55,32 +55,51 @@ PEAK_HBM_GBS = 8000.0
 # was taken on: when that file's SHA-1 differs, its figures are reported as null.
 COUNTERS = {
     "gemm_nt": {"source": "bit_nf4_quantized_dq_amd/csrc/gemm_nt.hip",
-                "sha1": "dfb9fc24b92bb37b4f3c7137c2e1e9860f3d4101",
-                "read_bytes": 202_336_000, "write_bytes": 33_554_432,
+                "sha1": "5ce5dbfd0aa38821b99f12d226e7a0e43790f4b7",
+                "read_bytes": 202_359_398, "write_bytes": 33_554_432,
                 "mfma_insts": 4_243_456, "mfma_busy_cycles": 135_790_592, "valu_insts": 5_626_368,
                 "lds_insts": 3_244_032, "lds_bank_conflict_cycles": 65_536, "salu_insts": 3_279_616},
+    # the step's HBM-bound launches (4096 x 4096, M = 4096, r = 16)
+    "fwd_prologue": {"source": "bit_nf4_quantized_dq_amd/csrc/lora.hip",
+                     "sha1": "f932c0af8724c12de8611188a66347f95693d0b8",
+                     "read_bytes": 43_637_146, "write_bytes": 33_816_576},
+    "bwd_prologue": {"source": "bit_nf4_quantized_dq_amd/csrc/lora.hip",
+                     "sha1": "f932c0af8724c12de8611188a66347f95693d0b8",
+                     "read_bytes": 45_298_278, "write_bytes": 33_816_576},
+    "lora_grad2": {"source": "bit_nf4_quantized_dq_amd/csrc/lora.hip",
+                   "sha1": "f932c0af8724c12de8611188a66347f95693d0b8",
+                   "read_bytes": 71_523_738, "write_bytes": 2_379_776},
     "merge": {"source": "bit_nf4_quantized_dq_amd/csrc/merge.hip",
               "sha1": "aa1649879396b227b61d065c057ec39a4962a28a",
-              "read_bytes": 11_912_832, "write_bytes": 33_554_944},
+              "read_bytes": 11_910_758, "write_bytes": 33_554_534},
     "adamw": {"source": "bit_nf4_quantized_dq_amd/csrc/adamw.hip",
               "sha1": "513130524f3da5219d61f8dcabd1c76bb0828e6f",
-              "read_bytes": 587_332_608, "write_bytes": 587_202_560},
+              "read_bytes": 587_329_946, "write_bytes": 587_202_560},
     # the 4096 x 4096 weight at M = 1 (whole-row stream) and at M = 16 (split-K stream)
     "gemv_rows_M1": {"source": "bit_nf4_quantized_dq_amd/csrc/gemv_rows.hip",
-                     "sha1": "90e057c10df734c17c9123101ef90e743f36e7e1",
-                     "read_bytes": 9_203_008, "write_bytes": 270_336, "weights": 4096 * 4096,
-                     "mfma_insts": 35_072, "valu_insts": 724_080, "lds_insts": 188_928, "lds_bank_conflict_cycles": 0},
+                     "sha1": "d13d57026c543be9968ababe8348c5f1ea3aa3ef",
+                     "read_bytes": 9_187_533, "write_bytes": 270_336, "weights": 4096 * 4096,
+                     "mfma_insts": 33_024, "valu_insts": 832_736, "lds_insts": 188_672, "lds_bank_conflict_cycles": 0},
     "gemv_fused_M16": {"source": "bit_nf4_quantized_dq_amd/csrc/gemv.hip",
-                       "sha1": "977c367891ded57ee601fb265121bce9fa8f787f",
-                       "read_bytes": 13_196_288, "write_bytes": 2_245_632, "weights": 4096 * 4096,
-                       "mfma_insts": 38_912, "valu_insts": 1_661_728, "lds_insts": 100_640,
+                       "sha1": "d6d0d81ba9fe6a63badad67570d594860f6598f4",
+                       "read_bytes": 13_297_254, "write_bytes": 2_245_632, "weights": 4096 * 4096,
+                       "mfma_insts": 38_912, "valu_insts": 1_601_056, "lds_insts": 100_640,
                        "lds_bank_conflict_cycles": 219_200},
     # one M = 1 call on a 28672 x 8192 weight (the gate shape of the 70B-class model)
     "gemv_stream": {"source": "bit_nf4_quantized_dq_amd/csrc/gemv_stream.hip",
-                    "sha1": "111ed5118cece5a11f25608c6d9732d1a18e5e83",
-                    "read_bytes": 125_032_256, "write_bytes": 297_600, "weights": 28672 * 8192,
+                    "sha1": "9cf575627acc88e2475edeb976f48a2f6d8b2da9",
+                    "read_bytes": 125_027_123, "write_bytes": 297_574, "weights": 28672 * 8192,
                     "mfma_insts": 489_216, "valu_insts": 7_018_118, "lds_insts": 2_475_426,
                     "lds_bank_conflict_cycles": 403_200},
+    # the decode-once forward at M = 2048 on the same 28672 x 8192 weight: the decode (with
+    # T = X A^T) and the BF16 GEMM
+    "fwd_prologue_gate_M2048": {"source": "bit_nf4_quantized_dq_amd/csrc/lora.hip",
+                                "sha1": "f932c0af8724c12de8611188a66347f95693d0b8",
+                                "read_bytes": 160_976_077, "write_bytes": 469_827_584},
+    "gemm_nt_gate_M2048": {"source": "bit_nf4_quantized_dq_amd/csrc/gemm_nt.hip",
+                           "sha1": "5ce5dbfd0aa38821b99f12d226e7a0e43790f4b7",
+                           "read_bytes": 2_001_885_389, "write_bytes": 117_440_512,
+                           "mfma_insts": 29_532_160, "mfma_busy_cycles": 945_029_120},
 }
 SIMDS = 256 * 4  # MFMA pipes on the chip
 
@@ -369,7 +388,14 @@ def seventy_b_model(dev, layers=80, passes=3):
             out["M2048"] = {"metric": "forward TFLOP/s at M=2048 through all 560 linears",
                             "value": round(flops2048 / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
                             "ms_per_pass": round(ms, 2), "tflop_per_pass": round(flops2048 / 1e12, 2),
-                            "roofline_frac": round(flops2048 / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+                            "roofline_frac": round(flops2048 / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                            # counted traffic of the gate projection's two launches (decode with
+                            # T, then the BF16 GEMM over 2048 x 8192 and the decoded 28672 x 8192)
+                            "gate_28672x8192": {
+                                "prologue_traffic": counter_traffic("fwd_prologue_gate_M2048"),
+                                "gemm_traffic": counter_traffic("gemm_nt_gate_M2048"),
+                                "gemm_operand_bytes": 2 * (28672 * 8192 + 2048 * 8192) + 2 * 2048 * 28672,
+                                "gemm_counters": counter_figures("gemm_nt_gate_M2048")}}
         del Xs, Ys, ws
     del lin
     torch.cuda.empty_cache()
@@ -644,10 +670,16 @@ def main():
         step()
     torch.cuda.synchronize()
     per_kernel = {}
+    # launches of the step whose HBM traffic was counted (the paired prologues and dA + dB)
+    counted = {"dequant": "fwd_prologue", "dequant_t": "bwd_prologue", "lora_grad": "lora_grad2"}
     for name in Q.KERNEL_IDS:
         ms, n = Q.timing_read(name)
         if n:
             per_kernel[name] = {"avg_us": 1e3 * ms / n, "launches_per_step": n / inst_steps}
+            tb = counter_traffic(counted[name]) if name in counted else None
+            if tb:
+                per_kernel[name]["traffic"] = tb
+                per_kernel[name]["traffic_GBs"] = tb / (1e3 * ms / n) / 1e3
     Q.timing_enable(False)
 
     # dominant kernel roofline (algorithmic FLOPs per launch / avg launch time in the timed region)
