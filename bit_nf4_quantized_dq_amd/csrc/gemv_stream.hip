@@ -12,7 +12,9 @@
 // LDS what every wavefront shares: the activations of the range, the E4M3 block constants and
 // second-level scales of its rows, and the byte-pair decode table.  The 4-bit codes never
 // touch LDS: each wavefront streams its own rows straight into registers, kDepth chunks of
-// kCB blocks in flight, with no barrier in the loop.
+// kCB blocks in flight, with no barrier in the loop.  Without a reduction split, row group g
+// walks its chunks starting at chunk g (mod their count), so that the workgroups do not all
+// read the same column offset at once.
 //
 // MFMA mapping (v_mfma_f32_32x32x16_bf16).  Lane (n = lane & 31, h = lane >> 5) loads the 16
 // bytes [16 h, 16 h + 16) of block b of weight row n: 32 weights, four code words.  Step s
@@ -220,8 +222,16 @@ __global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L, t
   // first second-level group touched by this workgroup
   const int64_t g0 = (row0 * nb_row + b0) >> 8;
 
+  // chunks holding blocks of this range; the rest of nchunk only pads the unrolled loop.
+  // Without a reduction split every workgroup walks the whole row, and all of them would read
+  // the same reduction offset (their codes at the same column, the same A rows) at the same
+  // time; so workgroup `grp` starts at its chunk grp mod nreal and wraps around (a fixed
+  // order per row group, the same in a grouped launch).
+  const int nreal = (int)(((b1 > b0 ? b1 - b0 : 0) + kCB - 1) / kCB);
+  const int rot = (a.ksplit == 1 && nreal > 0) ? (int)(grp % nreal) : 0;
+  auto chunk_of = [&](int ci) { return ci < nreal ? (ci + rot) % nreal : ci; };
   auto issue = [&](int ci, Chunk<RT16>& C) {
-    const int64_t bc = b0 + (int64_t)ci * kCB;
+    const int64_t bc = b0 + (int64_t)chunk_of(ci) * kCB;
 #pragma unroll
     for (int i = 0; i < kCB; ++i) {
       const bool ok = bc + i < b1 && code_row != kOOB;
@@ -317,7 +327,8 @@ __global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L, t
 #pragma unroll
   for (int k = 0; k < RT16; ++k) tacc[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int ci, const Chunk<RT16>& Cc) {
+  auto compute = [&](int step, const Chunk<RT16>& Cc) {
+    const int ci = chunk_of(step);
     const int64_t bc = b0 + (int64_t)ci * kCB;
     const uint8_t* xc = xrow + ci * kCB * 128;
     float cs[kCB];
@@ -355,8 +366,6 @@ __global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L, t
     for (int k = 0; k < RT16; ++k) tacc[k] = mfma16x16x32(xt, as_bf16x8(pair_order(Cc.av[k])), tacc[k]);
   };
 
-  // chunks holding blocks of this range; the rest of nchunk only pads the unrolled loop
-  const int nreal = (int)(((b1 > b0 ? b1 - b0 : 0) + kCB - 1) / kCB);
   for (int ci0 = 0; ci0 < a.nchunk; ci0 += kDepth) {
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
