@@ -62,6 +62,8 @@ constexpr int kMaxR = 128;
 constexpr int kRegion = 87 * 1024;       // activations, block constants, scales (then the T sums)
 constexpr int kC8Loads = 24;             // staged block-constant dwords per thread, at most
 constexpr int kSumU = 16;                // partials loaded together in the split-K sum
+constexpr uint32_t kTag = 0x10000u;      // marks a handed-over word (tag | bf16)
+constexpr int kMaxHandP = 8;             // reduction pieces of 4096 per producer lane (K <= 32768)
 
 // Workgroup barrier that waits for this wavefront's LDS accesses only (lgkmcnt), so global
 // loads in flight stay in flight across it.  Every barrier here orders LDS traffic between
@@ -113,6 +115,8 @@ struct StreamArgs {
   float* part;   // [ksplit][M][N]
   float* tpart;  // [ksplit][M][r]
   unsigned int* counters;  // [row groups of the launch], zero between calls
+  uint32_t* words;         // handed-over T: [row groups of the launch][r] (tag | bf16(s T)), zero between calls
+  int32_t nprod;           // workgroups that also form a column of T (the first ones dispatched)
   int64_t N, K;
   int32_t M, r;
   float s;
@@ -150,6 +154,7 @@ struct Smem {
   uint8_t lut[kLutBytes];  // first, so that its LDS address is 0
   uint8_t region[kRegion];
   float t[16][kMaxR + 4];
+  float tp[kWaves];  // a T producer's per-wavefront parts
   unsigned int last;
 };
 
@@ -163,7 +168,16 @@ struct Chunk {
 // RT16: 16-wide rank tiles (r <= 16 RT16).  NQ: accumulator registers kept (1 for M = 1,
 // where only row 0 of the 32x32 product is live; 8 for M <= 16).  K is a multiple of 256, so
 // a chunk's four E4M3 bytes form one aligned word and share one second-level scale.
-template <int RT16, int NQ, int kDepth, bool MULTI>
+// HAND (M = 1 only): T is not formed in the loop.  The first count r workgroups in dispatch
+// order each also form one column j of T = x A^T of one linear over the whole reduction
+// (8 products per lane and piece of 4096, a fixed-order DPP sum per wavefront, then the
+// wavefronts in order) while their first chunks land, and write bf16(s T) with a tag into
+// the word block of every row group of that linear in the workspace head.  Row groups take
+// the adapter term in split 0 only: after the loop, each wavefront reads its row group's
+// words (bounded wait), applies them to B on MFMA and adds the result; the words are cleared
+// after the outputs.  Producers wait on nothing before they publish and are dispatched
+// first, so no reader waits on a workgroup that has not started.
+template <int RT16, int NQ, int kDepth, bool MULTI, bool HAND>
 __global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L, typename GroupArg<MULTI>::type G) {
   __shared__ Smem sm;
   const uint8_t* const sLut = sm.lut;
@@ -205,6 +219,23 @@ __global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L, t
     grp = pgrp - G.gstart[li];
     tpart += (int64_t)li * a.ksplit * M * a.r;
   }
+  // T producer role (HAND): column pj of linear pli
+  const int64_t lin = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;  // dispatch order
+  const bool producer = HAND && lin < a.nprod;
+  const int pj = producer ? (int)(lin % a.r) : 0, pli = producer ? (int)(lin / a.r) : 0;
+  const rsrc_t rx = make_rsrc(a.X, (int64_t)M * K * 2);
+  uint4 hx[HAND ? kMaxHandP : 1], ha[HAND ? kMaxHandP : 1];
+  if (HAND && producer) {
+    const uint16_t* pA = a.A;
+    if constexpr (MULTI) pA = G.A[pli];
+    const rsrc_t rpa = make_rsrc(pA + (int64_t)pj * K, K * 2);
+#pragma unroll
+    for (int p = 0; p < (HAND ? kMaxHandP : 1); ++p) {
+      const int64_t k = 4096 * p + 8 * (64 * wave + lane);
+      hx[p] = bload16(rx, k < K ? (uint32_t)(k * 2) : kOOB);
+      ha[p] = bload16(rpa, k < K ? (uint32_t)(k * 2) : kOOB);
+    }
+  }
   const int64_t b0 = (int64_t)ks * a.nbs;
   const int64_t b1 = (b0 + a.nbs < nb_row) ? b0 + a.nbs : nb_row;
   const int64_t row0 = grp * kRows;
@@ -214,7 +245,6 @@ __global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L, t
   const rsrc_t rc = make_rsrc(w_codes, N * (K / 2));
   const rsrc_t r8 = make_rsrc(w_code8, N * nb_row);
   const rsrc_t r2 = make_rsrc(w_c2s, ((N * nb_row + 255) / 256) * 4);
-  const rsrc_t rx = make_rsrc(a.X, (int64_t)M * K * 2);
   const rsrc_t ra = make_rsrc(l_A, (int64_t)a.r * K * 2);
   const rsrc_t rb = make_rsrc(l_B, N * a.r * 2);
 
@@ -238,11 +268,13 @@ __global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L, t
       C.cw[i] = bload16(rc, ok ? code_row + (uint32_t)((bc + i) * 32) : kOOB);
     }
     // adapter: rows 16 k + l16, reduction indices 64 bc + 32 wave + 8 g .. + 8
+    if constexpr (!HAND) {
 #pragma unroll
-    for (int k = 0; k < RT16; ++k) {
-      const int j = 16 * k + l16;
-      const bool ok = bc < b1 && j < a.r;
-      C.av[k] = bload16(ra, ok ? (uint32_t)(((int64_t)j * K + bc * 64 + 32 * wave + 8 * g) * 2) : kOOB);
+      for (int k = 0; k < RT16; ++k) {
+        const int j = 16 * k + l16;
+        const bool ok = bc < b1 && j < a.r;
+        C.av[k] = bload16(ra, ok ? (uint32_t)(((int64_t)j * K + bc * 64 + 32 * wave + 8 * g) * 2) : kOOB);
+      }
     }
   };
 
@@ -311,7 +343,37 @@ __global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L, t
     const int d = u * kThreads + tid;
     if (u * kThreads < dwords && d < dwords) reinterpret_cast<uint32_t*>(sR + a.c8off)[d] = c8v[u];
   }
+  if (HAND && producer) {  // this wavefront's part of T[0][pj]
+    float d = 0.f;
+#pragma unroll
+    for (int p = 0; p < (HAND ? kMaxHandP : 1); ++p) {
+      const uint32_t xw[4] = {hx[p].x, hx[p].y, hx[p].z, hx[p].w}, aw[4] = {ha[p].x, ha[p].y, ha[p].z, ha[p].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        d = fmaf(bf16lo_to_f32(xw[e]), bf16lo_to_f32(aw[e]), d);
+        d = fmaf(bf16hi_to_f32(xw[e]), bf16hi_to_f32(aw[e]), d);
+      }
+    }
+    const float t = wave_sum(d);
+    if (lane == 0) sm.tp[wave] = t;
+  }
   lds_barrier();
+  if (HAND && producer) {  // publish column pj to every row group of linear pli
+    float t = sm.tp[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) t += sm.tp[w];
+    uint16_t* pT = a.T_save;
+    int gb = 0, ge = (int)gridDim.x;
+    if constexpr (MULTI) {
+      pT = G.T_save[pli];
+      gb = G.gstart[pli];
+      ge = G.gstart[pli + 1];
+    }
+    if (tid == 0 && pT) pT[pj] = (uint16_t)(pack_bf16x2(t, 0.f) & 0xFFFFu);
+    const uint32_t word = kTag | (pack_bf16x2(a.s * t, 0.f) & 0xFFFFu);
+    for (int q = gb + tid; q < ge; q += kThreads)
+      __hip_atomic_store(a.words + (int64_t)q * a.r + pj, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
 
   const uint32_t lane4 = (uint32_t)lane * 4u;
   // activation rows of this lane (rows >= M read the zero row): 32x32 operand and 16x16 operand
@@ -361,9 +423,11 @@ __global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L, t
       }
     }
     // adapter: this wavefront's 32-index step of the chunk, every rank tile
-    const bf16x8_t xt = as_bf16x8(*reinterpret_cast<const uint4*>(xrow16 + ci * kCB * 128));
+    if constexpr (!HAND) {
+      const bf16x8_t xt = as_bf16x8(*reinterpret_cast<const uint4*>(xrow16 + ci * kCB * 128));
 #pragma unroll
-    for (int k = 0; k < RT16; ++k) tacc[k] = mfma16x16x32(xt, as_bf16x8(pair_order(Cc.av[k])), tacc[k]);
+      for (int k = 0; k < RT16; ++k) tacc[k] = mfma16x16x32(xt, as_bf16x8(pair_order(Cc.av[k])), tacc[k]);
+    }
   };
 
   for (int ci0 = 0; ci0 < a.nchunk; ci0 += kDepth) {
@@ -374,35 +438,63 @@ __global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L, t
     }
   }
 
-  // ---- T over this range: sum the wavefronts' parts
-  lds_barrier();  // every wavefront is done with the staged region
-  float* sred = reinterpret_cast<float*>(sR);  // [kWaves][RT16][64][4]
+  // ---- T over this range: sum the wavefronts' parts (without HAND)
+  if constexpr (!HAND) {
+    lds_barrier();  // every wavefront is done with the staged region
+    float* sred = reinterpret_cast<float*>(sR);  // [kWaves][RT16][64][4]
 #pragma unroll
-  for (int k = 0; k < RT16; ++k)
-    *reinterpret_cast<f32x4_t*>(sred + ((wave * RT16 + k) * 64 + lane) * 4) = tacc[k];
-  lds_barrier();
-  for (int i = tid; i < M * a.r; i += kThreads) {
-    const int m = i / a.r, j = i % a.r;
-    const int k = j / 16, ln = (j % 16) + 16 * (m / 4), v = m % 4;  // D[m = 4 (lane >> 4) + v][j = lane & 15]
-    float sum = 0.f;
-    for (int w = 0; w < kWaves; ++w) sum += sred[((w * RT16 + k) * 64 + ln) * 4 + v];
-    sT[m][j] = sum;
+    for (int k = 0; k < RT16; ++k)
+      *reinterpret_cast<f32x4_t*>(sred + ((wave * RT16 + k) * 64 + lane) * 4) = tacc[k];
+    lds_barrier();
+    for (int i = tid; i < M * a.r; i += kThreads) {
+      const int m = i / a.r, j = i % a.r;
+      const int k = j / 16, ln = (j % 16) + 16 * (m / 4), v = m % 4;  // D[m = 4 (lane >> 4) + v][j = lane & 15]
+      float sum = 0.f;
+      for (int w = 0; w < kWaves; ++w) sum += sred[((w * RT16 + k) * 64 + ln) * 4 + v];
+      sT[m][j] = sum;
+    }
+    lds_barrier();
   }
-  lds_barrier();
 
-  // ---- adapter up-projection of this partial T: rows n of this wavefront
-  {
+  // ---- adapter up-projection: rows n of this wavefront, with this range's T, or (HAND) with
+  // the handed-over T in split 0 only
+  uint32_t* const mine = HAND ? a.words + pgrp * a.r : nullptr;  // this row group's words
+  if (!HAND || ks == 0) {
     f32x16_t up = {};
 #pragma unroll
     for (int u = 0; u < kMaxR / 16; ++u) {
       if (16 * u >= a.r) break;
       const int j0 = 16 * u + 8 * h;
       uint32_t tv[4];
+      if constexpr (HAND) {
+        // bounded wait (about 2^20 polls): should the words never arrive, the outputs become
+        // NaN instead of the wavefront spinning forever
+        const bool live = l32 == 0;  // token row 0 of the A operand
+        uint32_t tw[8];
+        bool ready = false;
+        for (int it = 0; !ready && it < (1 << 20); ++it) {
+          if (it) __builtin_amdgcn_s_sleep(2);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float lo = (l32 < M && j0 + 2 * e < a.r) ? a.s * sT[l32][j0 + 2 * e] : 0.f;
-        const float hi = (l32 < M && j0 + 2 * e + 1 < a.r) ? a.s * sT[l32][j0 + 2 * e + 1] : 0.f;
-        tv[e] = pack_bf16x2(lo, hi);
+          for (int i = 0; i < 8; ++i)
+            tw[i] = (live && j0 + i < a.r) ? __hip_atomic_load(mine + j0 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)
+                                           : kTag;
+          ready = true;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) ready = ready && (tw[i] & 0xFFFF0000u) == kTag;
+        }
+        if (!ready) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) tw[i] = kTag | 0x7FC0u;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tv[e] = live ? ((tw[2 * e] & 0xFFFFu) | (tw[2 * e + 1] << 16)) : 0u;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float lo = (l32 < M && j0 + 2 * e < a.r) ? a.s * sT[l32][j0 + 2 * e] : 0.f;
+          const float hi = (l32 < M && j0 + 2 * e + 1 < a.r) ? a.s * sT[l32][j0 + 2 * e + 1] : 0.f;
+          tv[e] = pack_bf16x2(lo, hi);
+        }
       }
       uint4 bw;
       if (u < 2 && (a.r % 8) == 0) {
@@ -428,9 +520,14 @@ __global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L, t
       const int m = 8 * (q / 4) + 4 * h + (q % 4);
       if (m < M && n < N) o_Y[(int64_t)m * N + n] = (uint16_t)(pack_bf16x2(acc[q], 0.f) & 0xFFFFu);
     }
-    if (o_T && grp == 0) {
+    if (!HAND && o_T && grp == 0) {
       for (int i = tid; i < M * a.r; i += kThreads)
         o_T[i] = (uint16_t)(pack_bf16x2(sT[i / a.r][i % a.r], 0.f) & 0xFFFFu);
+    }
+    if (HAND) {  // every wavefront has read the words: clear them for the next call
+      lds_barrier();
+      for (int i = tid; i < a.r; i += kThreads)
+        __hip_atomic_store(mine + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
     return;
   }
@@ -441,7 +538,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L, t
     if (m < M && n < N)
       __hip_atomic_store(a.part + ((int64_t)ks * M + m) * Nt + pn, acc[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
-  if (grp == 0) {
+  if (!HAND && grp == 0) {
     for (int i = tid; i < M * a.r; i += kThreads)
       __hip_atomic_store(tpart + (int64_t)ks * M * a.r + i, sT[i / a.r][i % a.r], __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_SYSTEM);
@@ -449,6 +546,10 @@ __global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L, t
   // every partial store of this workgroup has completed before its counter increment
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if (HAND && ks == 0) {  // every wavefront has read the words: clear them for the next call
+    for (int i = tid; i < a.r; i += kThreads)
+      __hip_atomic_store(mine + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
   if (tid == 0) {
     const unsigned int old = __hip_atomic_fetch_add(&a.counters[pgrp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sm.last = (old + 1u == (unsigned int)a.ksplit) ? 1u : 0u;
@@ -476,7 +577,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L, t
         (uint16_t)(pack_bf16x2(sum_published(a.part + m * Nt + pgrp * kRows + nn, a.ksplit, (int64_t)M * Nt), 0.f) &
                    0xFFFFu);
   }
-  if (o_T && grp == 0) {
+  if (!HAND && o_T && grp == 0) {
     for (int i = tid; i < M * a.r; i += kThreads)
       o_T[i] = (uint16_t)(pack_bf16x2(sum_published(tpart + i, a.ksplit, (int64_t)M * a.r), 0.f) & 0xFFFFu);
   }
@@ -586,6 +687,13 @@ hipError_t stream_launch(int count, const StreamLinear* lins, int64_t K, const u
   a.part = part;
   a.tpart = tpart;
   a.counters = counters;
+  // T handed over through words (M = 1): the words follow the counters in the head, and the
+  // producers are row workgroups too, so there must be at least count r of those
+  const int64_t woff = (p.groups + 63) / 64 * 64;
+  const bool hand = M == 1 && K <= 4096 * kMaxHandP && (int64_t)count * r <= p.groups * p.ksplit &&
+                    (size_t)(woff + p.groups * r) * 4 <= QLORA_WS_COUNTER_BYTES;
+  a.words = hand ? reinterpret_cast<uint32_t*>(counters + woff) : nullptr;
+  a.nprod = hand ? count * r : 0;
   a.N = Nt;
   a.K = K;
   a.M = (int32_t)M;
@@ -625,18 +733,31 @@ hipError_t stream_launch(int count, const StreamLinear* lins, int64_t K, const u
 #define QLORA_GEMV_GO1(RT16, NQ, D)                                                                                  \
   do {                                                                                                               \
     if (count > 1)                                                                                                   \
-      hipExtLaunchKernelGGL((k_gemv_stream<RT16, NQ, D, true>), grid, dim3(kThreads), 0, st, t.start, t.stop, 0, a, \
-                            L, G);                                                                                   \
+      hipExtLaunchKernelGGL((k_gemv_stream<RT16, NQ, D, true, false>), grid, dim3(kThreads), 0, st, t.start, t.stop, \
+                            0, a, L, G);                                                                             \
     else                                                                                                             \
-      hipExtLaunchKernelGGL((k_gemv_stream<RT16, NQ, D, false>), grid, dim3(kThreads), 0, st, t.start, t.stop, 0, a, \
-                            L, none);                                                                                \
+      hipExtLaunchKernelGGL((k_gemv_stream<RT16, NQ, D, false, false>), grid, dim3(kThreads), 0, st, t.start,       \
+                            t.stop, 0, a, L, none);                                                                  \
+  } while (0)
+#define QLORA_GEMV_HAND1(D)                                                                                          \
+  do {                                                                                                               \
+    if (count > 1)                                                                                                   \
+      hipExtLaunchKernelGGL((k_gemv_stream<1, 1, D, true, true>), grid, dim3(kThreads), 0, st, t.start, t.stop, 0, \
+                            a, L, G);                                                                                \
+    else                                                                                                             \
+      hipExtLaunchKernelGGL((k_gemv_stream<1, 1, D, false, true>), grid, dim3(kThreads), 0, st, t.start, t.stop, 0, \
+                            a, L, none);                                                                             \
   } while (0)
 #define QLORA_GEMV_GO(RT16, NQ, D)            \
   do {                                        \
     if (p.nchunk == 1) QLORA_GEMV_GO1(RT16, NQ, 1); \
     else QLORA_GEMV_GO1(RT16, NQ, D);         \
   } while (0)
-  if (M == 1) {
+  if (hand) {
+    if (p.nchunk == 1) QLORA_GEMV_HAND1(1);
+    else if (stream_depth(r) == 3) QLORA_GEMV_HAND1(3);
+    else QLORA_GEMV_HAND1(2);
+  } else if (M == 1) {
     if (r <= 16) QLORA_GEMV_GO(1, 1, 3);
     else if (r <= 32) QLORA_GEMV_GO(2, 1, 3);
     else if (r <= 64) QLORA_GEMV_GO(4, 1, 2);
@@ -649,6 +770,7 @@ hipError_t stream_launch(int count, const StreamLinear* lins, int64_t K, const u
   }
 #undef QLORA_GEMV_GO
 #undef QLORA_GEMV_GO1
+#undef QLORA_GEMV_HAND1
   return hipGetLastError();
 }
 

@@ -251,4 +251,26 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
   return __builtin_bit_cast(bf16x8_t, t);
 }
 
+// ---------------------------------------------------------------- wavefront sums
+
+// Sum over the 64 lanes in a fixed order, the same in every lane (all 64 lanes must be active):
+// within each row of 16 lanes by DPP (lane pairs, then quads, half rows and rows, each step
+// adding the mirrored partner, so both partners form the same sum), then the four row sums
+// in order.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_partner(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_partner<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_partner<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_partner<0x141>(v);  // row_half_mirror
+  v += dpp_partner<0x140>(v);  // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return ((r0 + r1) + r2) + r3;
+}
+
 }  // namespace qlora
