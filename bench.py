@@ -77,20 +77,20 @@ COUNTERS = {
               "read_bytes": 587_329_946, "write_bytes": 587_202_560},
     # the 4096 x 4096 weight at M = 1 (whole-row stream) and at M = 16 (split-K stream)
     "gemv_rows_M1": {"source": "bit_nf4_quantized_dq_amd/csrc/gemv_rows.hip",
-                     "sha1": "d13d57026c543be9968ababe8348c5f1ea3aa3ef",
-                     "read_bytes": 9_187_533, "write_bytes": 270_336, "weights": 4096 * 4096,
-                     "mfma_insts": 33_024, "valu_insts": 832_736, "lds_insts": 188_672, "lds_bank_conflict_cycles": 0},
+                     "sha1": "d0b0ff5f0796809dd74d5b7176d0c2c9adad137c",
+                     "read_bytes": 9_184_256, "write_bytes": 270_336, "weights": 4096 * 4096,
+                     "mfma_insts": 33_024, "valu_insts": 832_064, "lds_insts": 188_672, "lds_bank_conflict_cycles": 0},
     "gemv_fused_M16": {"source": "bit_nf4_quantized_dq_amd/csrc/gemv.hip",
-                       "sha1": "d6d0d81ba9fe6a63badad67570d594860f6598f4",
-                       "read_bytes": 13_297_254, "write_bytes": 2_245_632, "weights": 4096 * 4096,
-                       "mfma_insts": 38_912, "valu_insts": 1_601_056, "lds_insts": 100_640,
+                       "sha1": "8ae5ee9e6ebbb3916e42c137a627953fc195b350",
+                       "read_bytes": 13_308_314, "write_bytes": 2_245_632, "weights": 4096 * 4096,
+                       "mfma_insts": 38_912, "valu_insts": 1_603_616, "lds_insts": 100_640,
                        "lds_bank_conflict_cycles": 219_200},
     # one M = 1 call on a 28672 x 8192 weight (the gate shape of the 70B-class model)
     "gemv_stream": {"source": "bit_nf4_quantized_dq_amd/csrc/gemv_stream.hip",
-                    "sha1": "9cf575627acc88e2475edeb976f48a2f6d8b2da9",
-                    "read_bytes": 125_027_123, "write_bytes": 297_574, "weights": 28672 * 8192,
-                    "mfma_insts": 489_216, "valu_insts": 7_018_118, "lds_insts": 2_475_426,
-                    "lds_bank_conflict_cycles": 403_200},
+                    "sha1": "d0a4a7ee7035829efd0fc480da987ea97d69655c",
+                    "read_bytes": 123_232_256, "write_bytes": 361_984, "weights": 28672 * 8192,
+                    "mfma_insts": 459_648, "valu_insts": 6_172_000, "lds_insts": 2_429_888,
+                    "lds_bank_conflict_cycles": 344_064},
     # the decode-once forward at M = 2048 on the same 28672 x 8192 weight: the decode (with
     # T = X A^T) and the BF16 GEMM
     "fwd_prologue_gate_M2048": {"source": "bit_nf4_quantized_dq_amd/csrc/lora.hip",

@@ -405,6 +405,8 @@ STREAM_CASES = [
     (8192 + 160, 4096, 3, 40),  # a partial row group; B ranks past 32 read element by element
     (4352, 8192, 16, 128),      # M = 16 and the largest rank
     (12288, 4096, 2, 8),
+    (8192, 4096, 1, 40),        # M = 1: T handed over by producer workgroups, B rows read by element
+    (1024, 40960, 1, 16),       # M = 1 with a reduction past 32768: T formed in the loop
 ]
 
 
