@@ -88,12 +88,19 @@ def _short(mangled: str) -> str:
     return mangled
 
 
+# Extra device flags per source: the whole-row stream takes its first 16 argument dwords
+# preloaded into SGPRs (its first loads then need no argument fetch).
+EXTRA_DEVICE = {
+    "gemv_rows.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"],
+}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
     path = os.path.join(CSRC, src)
     cmd = [_hipcc(), *COMMON]
     if src.endswith(".hip"):
-        cmd += ["-x", "hip", *DEVICE, "-Rpass-analysis=kernel-resource-usage"]
+        cmd += ["-x", "hip", *DEVICE, *EXTRA_DEVICE.get(src, []), "-Rpass-analysis=kernel-resource-usage"]
     else:
         cmd += ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include"]  # host-only units
     cmd += ["-c", path, "-o", obj]

@@ -136,8 +136,38 @@ __device__ __forceinline__ bf16x8_t lookup8(const uint32_t* pair, uint32_t u, ui
   return as_bf16x8(w);
 }
 
+// The operands the loads need come first, as scalars: the leading argument dwords (14 here)
+// are preloaded into SGPRs (a by-value struct would not be), so the loads issue without
+// waiting for the argument block.  mu (loaded after the codes) and the rest follow.
+struct RowsRest {
+  const uint16_t* B;
+  uint16_t* Y;
+  uint16_t* T_save;
+  uint32_t* words;
+  float s;
+};
+
 template <int NBW>  // blocks of 64 weights per wavefront: K = 64 * 8 * NBW
-__global__ __launch_bounds__(kThreads) void k_gemv_rows(RowsArgs a, Lut L) {
+__global__ __launch_bounds__(kThreads) void k_gemv_rows(const uint16_t* X, const uint16_t* A, const uint8_t* code8,
+                                                        const float* c2s, const uint8_t* codes, int32_t N32,
+                                                        int32_t K32, int32_t M32, int32_t r32, const float* mu_p,
+                                                        RowsRest rest, Lut L) {
+  RowsArgs a;
+  a.codes = codes;
+  a.code8 = code8;
+  a.c2s = c2s;
+  a.mu = mu_p;
+  a.N = N32;
+  a.K = K32;
+  a.X = X;
+  a.A = A;
+  a.B = rest.B;
+  a.Y = rest.Y;
+  a.T_save = rest.T_save;
+  a.words = rest.words;
+  a.M = M32;
+  a.r = r32;
+  a.s = rest.s;
   __shared__ RowsLds<NBW> S;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -172,11 +202,11 @@ __global__ __launch_bounds__(kThreads) void k_gemv_rows(RowsArgs a, Lut L) {
   else c8w = make_uint2(bload4(r8, (uint32_t)blk0), 0u);
   const float c2a = __uint_as_float(bload4(r2, (uint32_t)((blk0 >> 8) * 4)));
   const float c2b = __uint_as_float(bload4(r2, (uint32_t)(((blk0 + NBW - 1) >> 8) * 4)));
-  const float mu = __uint_as_float(bload4(make_rsrc(a.mu, 4), 0u));  // before the codes, like the constants
   const rsrc_t rc = make_rsrc(a.codes + row0 * (K / 2), kRows * (K / 2));
   uint2 cr[NBW];
 #pragma unroll
   for (int b = 0; b < NBW; ++b) cr[b] = bload8(rc, (uint32_t)(l16 * (K / 2) + 32 * (b0 + b) + 8 * g));
+  const float mu = __uint_as_float(bload4(make_rsrc(a.mu, 4), 0u));  // used with the codes
 
   // ---- while the codes travel: the byte-pair table, the X slices and this wavefront's part
   // of column c of T (zero outside the producers, whose A slice is read out of range)
@@ -358,9 +388,14 @@ hipError_t launch_gemv_rows(const uint32_t* codes, const uint8_t* code8, const f
     L.hi[w] = T.lut_hi[w];
   }
   const dim3 grid((unsigned)(N / kRows));
+  const RowsRest rest{a.B, a.Y, a.T_save, a.words, a.s};
   LaunchTimer t(3, st);
-  if (K == 4096) hipExtLaunchKernelGGL(k_gemv_rows<8>, grid, dim3(kThreads), 0, st, t.start, t.stop, 0, a, L);
-  else hipExtLaunchKernelGGL(k_gemv_rows<4>, grid, dim3(kThreads), 0, st, t.start, t.stop, 0, a, L);
+  if (K == 4096)
+    hipExtLaunchKernelGGL(k_gemv_rows<8>, grid, dim3(kThreads), 0, st, t.start, t.stop, 0, a.X, a.A, a.code8, a.c2s,
+                          a.codes, (int32_t)N, (int32_t)K, a.M, a.r, a.mu, rest, L);
+  else
+    hipExtLaunchKernelGGL(k_gemv_rows<4>, grid, dim3(kThreads), 0, st, t.start, t.stop, 0, a.X, a.A, a.code8, a.c2s,
+                          a.codes, (int32_t)N, (int32_t)K, a.M, a.r, a.mu, rest, L);
   return hipGetLastError();
 }
 
