@@ -15,6 +15,8 @@
 // Memory layout: W FP32 or BF16 [d_out*d_in] is read as 8-value words (one packed code word
 // each); a wavefront covers 8 blocks of W with 16-byte lane loads.  A BF16 checkpoint (the
 // 16-bit form a model ships in, and the merged export) is quantized as its exact FP32 values.
+#include <cmath>
+
 #include "qlora_device.h"
 #include "qlora_host.h"
 
@@ -23,21 +25,58 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// The pass is bound by its VALU work (a wave64 instruction takes 4 cycles of a 16-lane SIMD),
+// so the two per-weight steps are written for few instructions, with the same results:
+//
+// - The ratio rho = fl32(w / c1).  The correctly rounded division is a 10-instruction
+//   sequence per weight.  The block's 64 weights share c1, so each lane takes y = fl32(1 / c1)
+//   once (correctly rounded) and then, per weight, q = fl32(w y) followed by two corrections
+//   q <- fl32(q + fl32(w - c1 q) y), each a fused multiply-add rounded once: five instructions.
+//   After the first correction q is within one ulp of w / c1, and Markstein's theorem (a
+//   reciprocal within half an ulp and a quotient within one ulp give an exact remainder and a
+//   correctly rounded corrected quotient) makes the second one exactly fl32(w / c1).  The
+//   theorem needs no underflow or overflow on the way, which holds for 2^-40 <= c1 <= 2^100:
+//   y stays normal, a remainder is a multiple of ulp(q) ulp(c1) >= 2^-149 once |q| >= 2^-60,
+//   and a smaller |q| lies below every threshold's magnitude (at least 2^-50, checked on the
+//   host), where any q in that range has the code of 0.  Other blocks (and codebooks with a
+//   threshold that close to 0) keep the correctly rounded division.
+// - The code, the number of the 15 ascending thresholds below rho, by the same 4-step binary
+//   search as everywhere else, with the thresholds of steps 2-4 read from LDS at an address
+//   that the steps update (3 instructions a step) instead of picked among constants.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_max(float v) {
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false)));
+}
+__device__ __forceinline__ float lds_f32(const float* base, uint32_t byte_off) {
+  return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+// thr: the 15 thresholds in LDS; t7 = thr[7].  Step s reads thr at byte offset a = 4 (c + 2^(3-s) - 1)
+// for the bits c found so far, so a moves by +-2^(4-s) bytes with each decision.
+__device__ __forceinline__ uint32_t code_lds(float rho, const float* thr, float t7) {
+  uint32_t a = rho > t7 ? 44u : 12u;  // thr[11] or thr[3]
+  a += rho > lds_f32(thr, a) ? 8u : (uint32_t)-8;
+  a += rho > lds_f32(thr, a) ? 4u : (uint32_t)-4;
+  return (a >> 2) + (rho > lds_f32(thr, a) ? 1u : 0u);
+}
+
 // W is FP32 (BF = false: two 16-byte loads per word) or BF16 (BF = true: one 16-byte load
 // per word, each value widened exactly to FP32).
 // Grid-stride over code words: a workgroup takes words w, w + stride, ... (stride = grid x
 // 256), so its LDS histogram gathers many blocks and the global histogram receives one
 // atomic per non-empty bin per workgroup.  The constants of a tensor share a few exponents,
 // so one atomic per block would pile onto the same few addresses.
+// fast: the codebook allows the reciprocal form (every threshold finite, |t| >= 2^-50).
 template <bool BF>
 __global__ __launch_bounds__(kThreads) void k_quant_pass1(const void* __restrict__ W,
                                                           uint32_t* __restrict__ codes,
                                                           float* __restrict__ c1_out,
                                                           unsigned long long* __restrict__ hist,
                                                           int* __restrict__ flag, int64_t n_words,
-                                                          Nf4Tables T) {
+                                                          Nf4Tables T, int32_t fast) {
   __shared__ unsigned long long sh_hist[256];
+  __shared__ float s_thr[16];
   sh_hist[threadIdx.x] = 0ull;
+  if (threadIdx.x < 15) s_thr[threadIdx.x] = T.thr[threadIdx.x];
   __syncthreads();
 
   bool any_bad = false;
@@ -71,13 +110,22 @@ __global__ __launch_bounds__(kThreads) void k_quant_pass1(const void* __restrict
       bad |= !__builtin_isfinite(v[i]);
       mx = fmaxf(mx, fabsf(v[i]));
     }
-    // absmax over the 8 lanes of one 64-weight block (lanes 8j..8j+7)
-    mx = fmaxf(mx, __shfl_xor(mx, 1));
-    mx = fmaxf(mx, __shfl_xor(mx, 2));
-    mx = fmaxf(mx, __shfl_xor(mx, 4));
+    // absmax over the 8 lanes of one 64-weight block (lanes 8j..8j+7, a half row)
+    mx = dpp_max<0xB1>(mx);   // quad_perm [1, 0, 3, 2]
+    mx = dpp_max<0x4E>(mx);   // quad_perm [2, 3, 0, 1]
+    mx = dpp_max<0x141>(mx);  // row_half_mirror
 
     uint32_t c[8];
-    if (mx > 0.f) {
+    if (fast && mx >= 0x1p-40f && mx <= 0x1p100f) {
+      const float y = __fdiv_rn(1.f, mx);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float q = v[i] * y;
+        q = __builtin_fmaf(__builtin_fmaf(-q, mx, v[i]), y, q);
+        q = __builtin_fmaf(__builtin_fmaf(-q, mx, v[i]), y, q);
+        c[i] = code_lds(q, s_thr, T.thr[7]);
+      }
+    } else if (mx > 0.f) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) c[i] = nf4_code(__fdiv_rn(v[i], mx), T);
     } else {
@@ -164,13 +212,16 @@ hipError_t launch_quant_pass1(const void* W, bool w_bf16, uint32_t* codes, float
                               int* flag, int64_t n_words, const Nf4Tables& T, hipStream_t s) {
   // 2048 workgroups of 256 threads fill the chip (8 per CU); larger tensors loop
   const int64_t grid = std::min<int64_t>((n_words + kThreads - 1) / kThreads, 2048);
+  int32_t fast = 1;  // every threshold finite and at least 2^-50 away from 0
+  for (int k = 0; k < 15; ++k)
+    if (!(std::fabs(T.thr[k]) >= 0x1p-50f && std::fabs(T.thr[k]) <= 0x1p100f)) fast = 0;
   LaunchTimer t(0, s);
   if (w_bf16)
     hipExtLaunchKernelGGL(k_quant_pass1<true>, dim3((unsigned)grid), dim3(kThreads), 0, s, t.start, t.stop, 0, W, codes,
-                          c1, hist, flag, n_words, T);
+                          c1, hist, flag, n_words, T, fast);
   else
     hipExtLaunchKernelGGL(k_quant_pass1<false>, dim3((unsigned)grid), dim3(kThreads), 0, s, t.start, t.stop, 0, W,
-                          codes, c1, hist, flag, n_words, T);
+                          codes, c1, hist, flag, n_words, T, fast);
   return hipGetLastError();
 }
 

@@ -113,6 +113,46 @@ def test_nearest_level_at_decision_boundaries(gpu_lib, cb):
     assert np.array_equal(_np(w.view(torch.int16)).view(np.uint16), O.dequantize_bf16_bits(oq))
 
 
+def test_nearest_level_at_decision_boundaries_many_scales(gpu_lib):
+    """rho = fl32(w / c1) for many block constants c1: each block holds +-c1 and the FP32
+    values fl32(c1 p) and one ulp either side of it for the decision points p, so that the
+    rounded quotient lands on and around every boundary.  The constants span 2^-40 .. 2^100
+    (the range where the device forms the quotient from a reciprocal, exactly) and the FP32
+    values just outside it at both ends (the correctly rounded division)."""
+    from bit_nf4_quantized_dq_amd import quantize
+
+    table = O.nf4_codebook()
+    pts = _decision_points(table)
+    rng = np.random.default_rng(11)
+    scales = [np.float32(m * 2.0**e) for m, e in zip(rng.uniform(1, 2, 48), rng.integers(-39, 99, 48))]
+    scales += [np.float32(s) for s in rng.uniform(0.005, 0.2, 12)]
+    lo, hi = np.float32(2.0**-40), np.float32(2.0**100)
+    scales += [lo, np.nextafter(lo, np.float32(0)), np.nextafter(lo, np.float32(np.inf)),
+               hi, np.nextafter(hi, np.float32(np.inf)), np.nextafter(hi, np.float32(0))]
+    blocks = []
+    for sc in scales:
+        w = (pts.astype(np.float32) * sc).astype(np.float32)
+        w = np.concatenate([np.nextafter(w, np.float32(-np.inf)), w, np.nextafter(w, np.float32(np.inf))])
+        w = np.clip(w, -sc, sc).astype(np.float32)
+        nb = -(-w.size // 63)
+        body = np.resize(w, (nb, 63))
+        b = np.empty((nb, 64), np.float32)
+        b[:, 1:] = body
+        b[:, 0] = np.where(np.arange(nb) % 2 == 0, sc, -sc)
+        blocks.append(b)
+    B = np.concatenate(blocks, axis=0)
+    B = np.resize(B, (-(-B.shape[0] // 64) * 64, 64))  # whole rows of 256, rows a multiple of 16
+    W = B.reshape(-1, 256)
+    oq = O.quantize(W)
+    q = quantize(torch.from_numpy(W).cuda())
+    torch.cuda.synchronize()
+    got = _np(q.codes).reshape(-1)
+    exp = oq["packed"].reshape(-1)
+    bad = np.nonzero(got != exp)[0]
+    assert bad.size == 0, f"{bad.size} code bytes differ, first at byte {bad[:4]}"
+    assert np.array_equal(_np(q.code8), oq["code8"])
+
+
 def test_nearest_level_at_decision_boundaries_bf16_input(gpu_lib):
     """BF16 weights: the BF16 values next to each NF4 midpoint (a BF16 rho has 8 significant
     bits, so the boundary is straddled by its two BF16 neighbours)."""
