@@ -243,7 +243,7 @@ MlpWs mlp_ws(bool bwd, int64_t M, const qlora_nf4dq_t* Wg, const qlora_nf4dq_t* 
 // every entry point.
 size_t quant_ws(int64_t d_out, int64_t d_in) {
   const int64_t nb = d_out * d_in / 64;
-  return kHead + align_up(sizeof(float) * nb, 256) + 256 * sizeof(unsigned long long) + 256;
+  return kHead + align_up(sizeof(float) * nb, 256) + kHistCopies * 256 * sizeof(unsigned long long) + 256;
 }
 
 // ---- kernel timing
@@ -488,8 +488,8 @@ int quantize_impl(const void* W, bool w_bf16, const qlora_nf4dq_t* Wq, float* ho
   char* base = static_cast<char*>(ws) + kHead;
   float* c1 = reinterpret_cast<float*>(base);
   auto* hist = reinterpret_cast<unsigned long long*>(base + align_up(sizeof(float) * nb, 256));
-  int* flag = reinterpret_cast<int*>(hist + 256);
-  hipError_t e = hipMemsetAsync(hist, 0, 256 * sizeof(unsigned long long) + 256, stream);
+  int* flag = reinterpret_cast<int*>(hist + kHistCopies * 256);
+  hipError_t e = hipMemsetAsync(hist, 0, kHistCopies * 256 * sizeof(unsigned long long) + 256, stream);
   if (e != hipSuccess) return QLORA_ERR_HIP;
   const bool no_dq = Wq->dq_format == QLORA_DQ_NONE;  // then c1 itself is the stored constant
   e = launch_quant_pass1(W, w_bf16, reinterpret_cast<uint32_t*>(Wq->codes), no_dq ? reinterpret_cast<float*>(Wq->code8) : c1,

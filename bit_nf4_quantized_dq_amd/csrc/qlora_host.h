@@ -48,6 +48,11 @@ int fwd_enqueue(const qlora_nf4dq_t* Wq, const uint16_t* X, int64_t M, const uin
                 int32_t r, float alpha, uint16_t* Y, uint16_t* T_save, void* ws, hipStream_t stream);
 
 // ---- quantize / dequantize (quantize.hip, dequant.hip)
+// Pass 1 spreads its exponent sums over kHistCopies zeroed copies of the 256 bins (workgroup
+// w adds into copy w % kHistCopies), then adds the copies into copy 0: hist holds
+// kHistCopies * 256 counters.  One copy for all workgroups serialized thousands of 64-bit
+// atomics on a few addresses (about 20 us per call).
+constexpr int kHistCopies = 64;
 hipError_t launch_quant_pass1(const void* W, bool w_bf16, uint32_t* codes, float* c1, unsigned long long* hist,
                               int* flag, int64_t n_words, const Nf4Tables& T, hipStream_t s);
 hipError_t launch_quant_pass2(const float* c1, float mu, uint8_t* code8, float* c2s, float* mu_out,

@@ -155,7 +155,15 @@ __global__ __launch_bounds__(kThreads) void k_quant_pass1(const void* __restrict
   }
   __syncthreads();
   const unsigned long long h = sh_hist[threadIdx.x];
-  if (h) atomicAdd(&hist[threadIdx.x], h);
+  if (h) atomicAdd(&hist[(blockIdx.x % kHistCopies) * 256 + threadIdx.x], h);
+}
+
+// Copy 0 of the exponent sums += copies 1 .. kHistCopies - 1 (integer adds: exact, and the
+// order does not matter).  One workgroup, one bin per thread.
+__global__ __launch_bounds__(kThreads) void k_hist_fold(unsigned long long* __restrict__ hist) {
+  unsigned long long s = 0;
+  for (int c = 0; c < kHistCopies; ++c) s += hist[c * 256 + threadIdx.x];
+  hist[threadIdx.x] = s;
 }
 
 // One wavefront per group of 256 constants; lane l owns constants 4l..4l+3 of the group.
@@ -222,6 +230,9 @@ hipError_t launch_quant_pass1(const void* W, bool w_bf16, uint32_t* codes, float
   else
     hipExtLaunchKernelGGL(k_quant_pass1<false>, dim3((unsigned)grid), dim3(kThreads), 0, s, t.start, t.stop, 0, W,
                           codes, c1, hist, flag, n_words, T, fast);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_hist_fold, dim3(1), dim3(kThreads), 0, s, hist);
   return hipGetLastError();
 }
 
