@@ -21,14 +21,18 @@ __device__ __forceinline__ float stored_c1(const uint8_t* __restrict__ code8, co
 }
 
 // Code word g (8 weights) decoded into out[g] (4 dwords of BF16 pairs, element order).
+// The code word is loaded first, as a raw buffer load: the constant's decode holds a branch,
+// and a plain load placed after it waited for the constant's round trip before it issued.
 template <int DQ>
 __device__ __forceinline__ void decode_word(const uint32_t* __restrict__ codes, const uint8_t* __restrict__ code8,
                                             const float* __restrict__ c2s, const float* __restrict__ mu,
                                             uint4* __restrict__ out, int64_t g, const Nf4Tables& T) {
+  // codes hold at most 2^31 bytes (at most 2^32 weights), so the byte offset fits 32 bits
+  const uint32_t cw = bload4(make_rsrc(codes, (int64_t)0xFFFFFFFF), (uint32_t)(4 * g));
   Lut L;
   build_scaled_lut(T, stored_c1<DQ>(code8, c2s, mu, g >> 3), L);
   uint32_t w[4];
-  decode8(codes[g], L, w);
+  decode8(cw, L, w);
   out[g] = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
@@ -54,10 +58,12 @@ __device__ __forceinline__ void decode_tile_t(const uint32_t* __restrict__ codes
   uint32_t o[32];
   if (n < N && kb < nb_row) {
     const int64_t blk = n * nb_row + kb;
+    // the block's codes first (as in decode_word: raw buffer loads, issued before the
+    // constant's decode and its branch)
+    const rsrc_t rc = make_rsrc(codes, (int64_t)0xFFFFFFFF);
+    const uint4 w0 = bload16(rc, (uint32_t)(32 * blk)), w1 = bload16(rc, (uint32_t)(32 * blk + 16));
     Lut L;
     build_scaled_lut(T, stored_c1<DQ>(code8, c2s, mu, blk), L);
-    const uint4* wp = reinterpret_cast<const uint4*>(codes + blk * 8);
-    const uint4 w0 = wp[0], w1 = wp[1];
     const uint32_t words[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
     for (int c = 0; c < 8; ++c) decode8(words[c], L, &o[4 * c]);
