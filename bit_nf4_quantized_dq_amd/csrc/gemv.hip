@@ -90,6 +90,14 @@ __device__ __forceinline__ float sum_published(const float* p, int32_t n, int64_
   return s;
 }
 
+// Token and row of output i (< M nrows <= 16 kRows) of a row group with nrows rows: 32-bit,
+// and shifts for a whole group (a 64-bit division is a long instruction sequence, and these
+// sit in the launch's critical tail).
+__device__ __forceinline__ void split_out(int i, int nrows, int& m, int& nn) {
+  m = nrows == kRows ? (int)((unsigned)i / (unsigned)kRows) : (int)((unsigned)i / (unsigned)nrows);
+  nn = i - m * nrows;
+}
+
 // The same fixed-order sum for up to kSumOut outputs of one thread at once (output i0 + o
 // kThreads, o < kSumOut, of `total`; output i is Y[i / nrows][row0 + i % nrows] of a row-major
 // [M][N] partial), all of their loads issued before any is summed.
@@ -105,7 +113,9 @@ __device__ __forceinline__ void sum_published_n(const float* part, int64_t i0, i
 #pragma unroll
     for (int o = 0; o < kSumOut; ++o) {
       const int64_t i = i0 + (int64_t)o * kThreads;
-      const float* p = part + (i / nrows) * N + row0 + i % nrows;
+      int m, nn;
+      split_out((int)i, (int)nrows, m, nn);
+      const float* p = part + (int64_t)m * N + row0 + nn;
 #pragma unroll
       for (int u = 0; u < kSumOutU; ++u)
         v[o][u] = (i < total && k0 + u < n)
@@ -524,7 +534,9 @@ __global__ __launch_bounds__(kThreads) void k_gemv_fused(GemvArgs a, Nf4Tables T
   const int64_t nrows = (row0 + kRows <= N) ? kRows : N - row0;
   if (M * nrows <= kThreads) {
     if (tid < M * nrows) {
-      const int64_t m = tid / nrows, n = row0 + tid % nrows;
+      int m, nn;
+      split_out(tid, (int)nrows, m, nn);
+      const int64_t n = row0 + nn;
       a.Y[m * N + n] = (uint16_t)(pack_bf16x2(sum_published(a.part + m * N + n, a.ksplit, M * N), 0.f) & 0xFFFFu);
     }
   } else {
@@ -534,7 +546,9 @@ __global__ __launch_bounds__(kThreads) void k_gemv_fused(GemvArgs a, Nf4Tables T
 #pragma unroll
       for (int o = 0; o < kSumOut; ++o) {
         const int64_t i = i0 + (int64_t)o * kThreads;
-        if (i < M * nrows) a.Y[(i / nrows) * N + row0 + i % nrows] = (uint16_t)(pack_bf16x2(sum[o], 0.f) & 0xFFFFu);
+        int m, nn;
+        split_out((int)i, (int)nrows, m, nn);
+        if (i < M * nrows) a.Y[(int64_t)m * N + row0 + nn] = (uint16_t)(pack_bf16x2(sum[o], 0.f) & 0xFFFFu);
       }
     }
   }

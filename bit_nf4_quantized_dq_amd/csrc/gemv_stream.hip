@@ -259,7 +259,8 @@ __global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L, t
   // order per row group, the same in a grouped launch).
   const int nreal = (int)(((b1 > b0 ? b1 - b0 : 0) + kCB - 1) / kCB);
   const int rot = (a.ksplit == 1 && nreal > 0) ? (int)(grp % nreal) : 0;
-  auto chunk_of = [&](int ci) { return ci < nreal ? (ci + rot) % nreal : ci; };
+  // (ci + rot) mod nreal without a division: both terms are below nreal
+  auto chunk_of = [&](int ci) { return ci < nreal ? (ci + rot >= nreal ? ci + rot - nreal : ci + rot) : ci; };
   auto issue = [&](int ci, Chunk<RT16>& C) {
     const int64_t bc = b0 + (int64_t)chunk_of(ci) * kCB;
 #pragma unroll
@@ -284,30 +285,62 @@ __global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L, t
   Chunk<RT16> C[kDepth];
   issue(0, C[0]);
   // block constants of the range: dword d of the staged [kRows][c8pitch] block is row d / c8w,
-  // bytes 4 (d % c8w) .. + 3 of the row's range (the last dword of a row is padding)
+  // bytes 4 (d % c8w) .. + 3 of the row's range (the last dword of a row is padding).  The
+  // row and column of d = u kThreads + tid advance by the quotient and remainder of kThreads
+  // / c8w from pass to pass (one division per thread, not one per pass: an integer division
+  // is a few dozen instructions, and they delayed the issue of every later load).
   const int c8w = a.c8pitch / 4;
   const int dwords = kRows * c8w;
+  const int c8q = kThreads / c8w, c8r = kThreads - c8q * c8w;
   uint32_t c8v[kC8Loads];
+  {
+    // 32-bit operands (rows below 2^22, the range below 2^26 blocks) and no short-circuit,
+    // so that the test and the offset are selects, not branches
+    const int rows_left = (int)(N - row0), span = (int)(b1 - b0);
+    const uint32_t c8base = (uint32_t)(row0 * nb_row + b0), nbr = (uint32_t)nb_row;
+    int row = tid / c8w, cd = tid - (tid / c8w) * c8w;
 #pragma unroll
-  for (int u = 0; u < kC8Loads; ++u) {
-    if (u * kThreads < dwords) {  // uniform: only the passes that hold staged dwords
-      const int d = u * kThreads + tid, row = d / c8w, cd = d % c8w;
-      const bool ok = d < dwords && row0 + row < N && 4 * cd < b1 - b0;
-      c8v[u] = bload4(r8, ok ? (uint32_t)((row0 + row) * nb_row + b0 + 4 * cd) : kOOB);
+    for (int u = 0; u < kC8Loads; ++u) {
+      if (u * kThreads < dwords) {  // uniform: only the passes that hold staged dwords
+        const int d = u * kThreads + tid;
+        const bool ok = (d < dwords) & (row < rows_left) & (4 * cd < span);
+        c8v[u] = bload4(r8, ok ? c8base + (uint32_t)row * nbr + 4u * (uint32_t)cd : kOOB);
+      }
+      row += c8q;
+      cd += c8r;
+      if (cd >= c8w) {
+        cd -= c8w;
+        ++row;
+      }
     }
   }
   // activations of this range, pair-ordered: rows 0..M-1 then a zero row.  (M + 1) rows of
   // nchunk * kCB * 128 bytes are at most 4096 pieces of 16 bytes: one batch of 8 per thread.
+  // Item i = u kThreads + tid is piece i % pieces of row i / pieces, advanced per pass as above;
+  // xo[u] keeps its LDS offset for the staging writes.
   const int pieces = a.nchunk * kCB * 8;
   const int items = (M + 1) * pieces;
+  const int xq = kThreads / pieces, xr = kThreads - xq * pieces;
   uint4 xv[8];
+  int xo[8];
+  {
+    const int kspan = (int)(64 * (b1 - b0));  // reduction indices of the range
+    const uint32_t xbase = (uint32_t)(b0 * 128), xrow = (uint32_t)(2 * K);
+    int m = tid / pieces, pc = tid - (tid / pieces) * pieces;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    if (u * kThreads < items) {  // uniform: only the passes that hold pieces
-      const int i = u * kThreads + tid, m = i / pieces, pc = i % pieces;
-      const int64_t k = b0 * 64 + 8 * pc;
-      const bool ok = i < items && m < M && k < b1 * 64;
-      xv[u] = bload16(rx, ok ? (uint32_t)(((int64_t)m * K + k) * 2) : kOOB);
+    for (int u = 0; u < 8; ++u) {
+      xo[u] = m * a.xpitch + 16 * pc;
+      if (u * kThreads < items) {  // uniform: only the passes that hold pieces
+        const int i = u * kThreads + tid;
+        const bool ok = (i < items) & (m < M) & (8 * pc < kspan);
+        xv[u] = bload16(rx, ok ? (uint32_t)m * xrow + xbase + 16u * (uint32_t)pc : kOOB);
+      }
+      m += xq;
+      pc += xr;
+      if (pc >= pieces) {
+        pc -= pieces;
+        ++m;
+      }
     }
   }
   const uint32_t c2v = bload4(r2, tid < a.c2max ? (uint32_t)((g0 + tid) * 4) : kOOB);
@@ -334,8 +367,8 @@ __global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L, t
   }
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    const int i = u * kThreads + tid, m = i / pieces, pc = i % pieces;
-    if (u * kThreads < items && i < items) *reinterpret_cast<uint4*>(sR + m * a.xpitch + 16 * pc) = pair_order(xv[u]);
+    const int i = u * kThreads + tid;
+    if (u * kThreads < items && i < items) *reinterpret_cast<uint4*>(sR + xo[u]) = pair_order(xv[u]);
   }
   if (tid < a.c2max) reinterpret_cast<float*>(sR + a.c2off)[tid] = __uint_as_float(c2v);
 #pragma unroll
@@ -572,7 +605,10 @@ __global__ __launch_bounds__(kThreads) void k_gemv_stream(StreamArgs a, Lut L, t
   };
   const int64_t nrows = (row0 + kRows <= N) ? kRows : N - row0;
   for (int64_t i = tid; i < (int64_t)M * nrows; i += kThreads) {
-    const int64_t m = i / nrows, nn = i % nrows;
+    // 32-bit, by a shift for a whole group (a 64-bit division is a long sequence, in the tail)
+    const int nr = (int)nrows, ii = (int)i;
+    const int m = nr == kRows ? (int)((unsigned)ii / (unsigned)kRows) : (int)((unsigned)ii / (unsigned)nr);
+    const int nn = ii - m * nr;
     o_Y[m * N + row0 + nn] =
         (uint16_t)(pack_bf16x2(sum_published(a.part + m * Nt + pgrp * kRows + nn, a.ksplit, (int64_t)M * Nt), 0.f) &
                    0xFFFFu);

@@ -225,9 +225,12 @@ __global__ __launch_bounds__(kDownThreads) void k_bwd_prologue(DownArgs d, Decod
     return;
   }
   const int half = threadIdx.x >> 8;
-  const int64_t tiles_k = (e.K + kTK - 1) / kTK;
-  const int64_t tile = 2 * ((int64_t)blockIdx.x - n_down) + half;  // past the last tile: decodes nothing
-  decode_tile_t<DQ>(e.codes, e.code8, e.c2s, e.mu, e.out, e.N, e.K, T, tile % tiles_k, tile / tiles_k,
+  // 32-bit tile arithmetic (fewer than 2^31 tiles): a 64-bit division here delayed the
+  // decode's first loads
+  const uint32_t tiles_k = (uint32_t)((e.K + kTK - 1) / kTK);
+  const uint32_t tile = 2u * (uint32_t)((int64_t)blockIdx.x - n_down) + (uint32_t)half;  // past the last tile: decodes nothing
+  const uint32_t tn = tile / tiles_k;
+  decode_tile_t<DQ>(e.codes, e.code8, e.c2s, e.mu, e.out, e.N, e.K, T, (int64_t)(tile - tn * tiles_k), (int64_t)tn,
                     threadIdx.x & 255, reinterpret_cast<uint32_t*>(smem + half * kTileLdsBytes));
 }
 
@@ -392,8 +395,11 @@ __device__ __forceinline__ void grad_body(const GradArgs& g, int64_t c_tile, int
   // last workgroup of this column tile: fixed-order sum of the slices
   const int64_t ncol = (c0 + kGradCols <= C) ? kGradCols : C - c0;
   for (int64_t i = threadIdx.x; i < (int64_t)R * ncol; i += kGradThreads) {
-    const int32_t j = (int32_t)(i / ncol);
-    const int64_t c = c0 + i % ncol;
+    // 32-bit (R ncol <= 128 kGradCols), a shift for a whole tile: a 64-bit division is a long
+    // sequence, and this runs in the launch's tail
+    const int ii = (int)i, nc = (int)ncol;
+    const int32_t j = nc == kGradCols ? (int32_t)((unsigned)ii / (unsigned)kGradCols) : (int32_t)((unsigned)ii / (unsigned)nc);
+    const int64_t c = c0 + (ii - j * nc);
     const float* p = part + (int64_t)j * C + c;
     float s = 0.f;
     for (int32_t k0 = 0; k0 < msplit; k0 += kSumU) {
