@@ -61,14 +61,14 @@ COUNTERS = {
                 "lds_insts": 3_244_032, "lds_bank_conflict_cycles": 65_536, "salu_insts": 3_279_616},
     # the step's HBM-bound launches (4096 x 4096, M = 4096, r = 16)
     "fwd_prologue": {"source": "bit_nf4_quantized_dq_amd/csrc/lora.hip",
-                     "sha1": "f932c0af8724c12de8611188a66347f95693d0b8",
-                     "read_bytes": 43_637_146, "write_bytes": 33_816_576},
+                     "sha1": "5e5a44a0e5cd2afd08cb9dc3f4982b79edec5458",
+                     "read_bytes": 43_637_568, "write_bytes": 33_816_576},
     "bwd_prologue": {"source": "bit_nf4_quantized_dq_amd/csrc/lora.hip",
-                     "sha1": "f932c0af8724c12de8611188a66347f95693d0b8",
-                     "read_bytes": 45_298_278, "write_bytes": 33_816_576},
+                     "sha1": "5e5a44a0e5cd2afd08cb9dc3f4982b79edec5458",
+                     "read_bytes": 45_275_136, "write_bytes": 33_816_576},
     "lora_grad2": {"source": "bit_nf4_quantized_dq_amd/csrc/lora.hip",
-                   "sha1": "f932c0af8724c12de8611188a66347f95693d0b8",
-                   "read_bytes": 71_523_738, "write_bytes": 2_379_776},
+                   "sha1": "5e5a44a0e5cd2afd08cb9dc3f4982b79edec5458",
+                   "read_bytes": 71_514_688, "write_bytes": 2_379_776},
     "merge": {"source": "bit_nf4_quantized_dq_amd/csrc/merge.hip",
               "sha1": "aa1649879396b227b61d065c057ec39a4962a28a",
               "read_bytes": 11_910_758, "write_bytes": 33_554_534},
@@ -81,21 +81,21 @@ COUNTERS = {
                      "read_bytes": 9_203_392, "write_bytes": 270_336, "weights": 4096 * 4096,
                      "mfma_insts": 33_024, "valu_insts": 826_768, "lds_insts": 188_672, "lds_bank_conflict_cycles": 0},
     "gemv_fused_M16": {"source": "bit_nf4_quantized_dq_amd/csrc/gemv.hip",
-                       "sha1": "8ae5ee9e6ebbb3916e42c137a627953fc195b350",
-                       "read_bytes": 13_308_314, "write_bytes": 2_245_632, "weights": 4096 * 4096,
-                       "mfma_insts": 38_912, "valu_insts": 1_603_616, "lds_insts": 100_640,
+                       "sha1": "722bc599e5742326b6648d9d31c04341b0eaa8f2",
+                       "read_bytes": 13_233_664, "write_bytes": 2_245_632, "weights": 4096 * 4096,
+                       "mfma_insts": 38_912, "valu_insts": 1_597_728, "lds_insts": 100_640,
                        "lds_bank_conflict_cycles": 219_200},
     # one M = 1 call on a 28672 x 8192 weight (the gate shape of the 70B-class model)
     "gemv_stream": {"source": "bit_nf4_quantized_dq_amd/csrc/gemv_stream.hip",
-                    "sha1": "d0a4a7ee7035829efd0fc480da987ea97d69655c",
-                    "read_bytes": 123_232_256, "write_bytes": 361_984, "weights": 28672 * 8192,
-                    "mfma_insts": 459_648, "valu_insts": 6_172_000, "lds_insts": 2_429_888,
+                    "sha1": "582116b2f7d814e3398559b0f16316fbc13952b6",
+                    "read_bytes": 123_147_008, "write_bytes": 361_984, "weights": 28672 * 8192,
+                    "mfma_insts": 459_648, "valu_insts": 6_625_632, "lds_insts": 2_429_888,
                     "lds_bank_conflict_cycles": 344_064},
     # the decode-once forward at M = 2048 on the same 28672 x 8192 weight: the decode (with
     # T = X A^T) and the BF16 GEMM
     "fwd_prologue_gate_M2048": {"source": "bit_nf4_quantized_dq_amd/csrc/lora.hip",
-                                "sha1": "f932c0af8724c12de8611188a66347f95693d0b8",
-                                "read_bytes": 160_976_077, "write_bytes": 469_827_584},
+                                "sha1": "5e5a44a0e5cd2afd08cb9dc3f4982b79edec5458",
+                                "read_bytes": 160_989_696, "write_bytes": 469_827_584},
     "gemm_nt_gate_M2048": {"source": "bit_nf4_quantized_dq_amd/csrc/gemm_nt.hip",
                            "sha1": "5ce5dbfd0aa38821b99f12d226e7a0e43790f4b7",
                            "read_bytes": 2_001_885_389, "write_bytes": 117_440_512,
