@@ -20,20 +20,38 @@ __device__ __forceinline__ float stored_c1(const uint8_t* __restrict__ code8, co
   return block_scale_fmt<DQ>(code8[blk], c2s[blk >> 8], mu[0]);
 }
 
-// Code word g (8 weights) decoded into out[g] (4 dwords of BF16 pairs, element order).
-// The code word is loaded first, as a raw buffer load: the constant's decode holds a branch,
-// and a plain load placed after it waited for the constant's round trip before it issued.
-template <int DQ>
-__device__ __forceinline__ void decode_word(const uint32_t* __restrict__ codes, const uint8_t* __restrict__ code8,
-                                            const float* __restrict__ c2s, const float* __restrict__ mu,
-                                            uint4* __restrict__ out, int64_t g, const Nf4Tables& T) {
-  // codes hold at most 2^31 bytes (at most 2^32 weights), so the byte offset fits 32 bits
-  const uint32_t cw = bload4(make_rsrc(codes, (int64_t)0xFFFFFFFF), (uint32_t)(4 * g));
-  Lut L;
-  build_scaled_lut(T, stored_c1<DQ>(code8, c2s, mu, g >> 3), L);
-  uint32_t w[4];
-  decode8(cw, L, w);
-  out[g] = make_uint4(w[0], w[1], w[2], w[3]);
+// Code words (blk kDecWords + i) NT + t, i < kDecWords, decoded by thread t of workgroup blk
+// (NT threads) into out[word] (4 dwords of BF16 pairs, element order).  The code words are
+// loaded first, as raw buffer loads (the constant's decode holds a branch, and a plain load
+// placed after it waited for the constant's round trip before it issued), and all of a
+// thread's loads go out before its first decode: with one word per thread the decode ran as
+// thousands of small workgroups that overlapped poorly with the launch it shares a grid with.
+constexpr int kDecWords = 8;
+template <int DQ, int NT>
+__device__ __forceinline__ void decode_words(const uint32_t* __restrict__ codes, const uint8_t* __restrict__ code8,
+                                             const float* __restrict__ c2s, const float* __restrict__ mu,
+                                             uint4* __restrict__ out, int64_t blk, int t, int64_t n_words,
+                                             const Nf4Tables& T) {
+  const rsrc_t rc = make_rsrc(codes, (int64_t)0xFFFFFFFF);
+  uint32_t cw[kDecWords];
+  float c1[kDecWords];
+  int64_t g[kDecWords];
+#pragma unroll
+  for (int i = 0; i < kDecWords; ++i) {
+    g[i] = (blk * kDecWords + i) * NT + t;
+    const bool ok = g[i] < n_words;
+    cw[i] = bload4(rc, ok ? (uint32_t)(4 * g[i]) : kOOB);
+    c1[i] = stored_c1<DQ>(code8, c2s, mu, ok ? g[i] >> 3 : 0);
+  }
+#pragma unroll
+  for (int i = 0; i < kDecWords; ++i) {
+    if (g[i] >= n_words) continue;
+    Lut L;
+    build_scaled_lut(T, c1[i], L);
+    uint32_t w[4];
+    decode8(cw[i], L, w);
+    out[g[i]] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
 }
 
 // Transposed copy w_hat^T [K, N] (the operand layout of the dX product, whose reduction runs
@@ -58,8 +76,8 @@ __device__ __forceinline__ void decode_tile_t(const uint32_t* __restrict__ codes
   uint32_t o[32];
   if (n < N && kb < nb_row) {
     const int64_t blk = n * nb_row + kb;
-    // the block's codes first (as in decode_word: raw buffer loads, issued before the
-    // constant's decode and its branch)
+    // the block's codes first (raw buffer loads, issued before the constant's decode and its
+    // branch, as in decode_words)
     const rsrc_t rc = make_rsrc(codes, (int64_t)0xFFFFFFFF);
     const uint4 w0 = bload16(rc, (uint32_t)(32 * blk)), w1 = bload16(rc, (uint32_t)(32 * blk + 16));
     Lut L;

@@ -9,7 +9,7 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// One thread per 8-weight code word.
+// kDecWords 8-weight code words per thread.
 template <int DQ>
 __global__ __launch_bounds__(kThreads) void k_dequant(const uint32_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ code8,
@@ -17,9 +17,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint32_t* __restrict
                                                       const float* __restrict__ mu,
                                                       uint4* __restrict__ out, int64_t n_words,
                                                       Nf4Tables T) {
-  const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (g >= n_words) return;
-  decode_word<DQ>(codes, code8, c2s, mu, out, g, T);
+  decode_words<DQ, kThreads>(codes, code8, c2s, mu, out, blockIdx.x, threadIdx.x, n_words, T);
 }
 
 // The transposed copy w_hat^T [K, N]: one 64 x 256 tile per workgroup (decode_tile_t).
@@ -54,7 +52,7 @@ hipError_t launch_dequant_t(const uint32_t* codes, const uint8_t* code8, const f
 hipError_t launch_dequant(const uint32_t* codes, const uint8_t* code8, const float* c2s,
                           const float* mu, uint16_t* out, int64_t n_words, const Nf4Tables& T, int dq,
                           hipStream_t s) {
-  const int64_t grid = (n_words + kThreads - 1) / kThreads;
+  const int64_t grid = (n_words + kThreads * kDecWords - 1) / (kThreads * kDecWords);
   LaunchTimer t(2, s);
   auto go = [&](auto kern) {
     hipExtLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, s, t.start, t.stop, 0, codes, code8, c2s, mu,

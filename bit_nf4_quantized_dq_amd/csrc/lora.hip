@@ -202,7 +202,8 @@ struct DecodeArgs {
   int64_t N, K;
 };
 
-// Forward: T = X A^T, and the decoded copy w_hat [N, K] (512 code words per workgroup).
+// Forward: T = X A^T, and the decoded copy w_hat [N, K] (kDecWords x 256 code words per
+// workgroup).
 template <int JT, int MT, int D, int DQ>
 __global__ __launch_bounds__(kDownThreads) void k_fwd_prologue(DownArgs d, DecodeArgs e, int64_t n_down, Nf4Tables T) {
   __shared__ __attribute__((aligned(16))) char smem[down_lds_bytes<JT, MT>()];
@@ -210,8 +211,8 @@ __global__ __launch_bounds__(kDownThreads) void k_fwd_prologue(DownArgs d, Decod
     down_body<JT, MT, false, D>(d.P, d.Q, d.M, d.R, d.Kd, d.scale, d.out_s, d.out_u, blockIdx.x, smem);
     return;
   }
-  const int64_t g = ((int64_t)blockIdx.x - n_down) * kDownThreads + threadIdx.x;
-  if (g < e.N * e.K / 8) decode_word<DQ>(e.codes, e.code8, e.c2s, e.mu, reinterpret_cast<uint4*>(e.out), g, T);
+  decode_words<DQ, kDownThreads>(e.codes, e.code8, e.c2s, e.mu, reinterpret_cast<uint4*>(e.out), (int64_t)blockIdx.x - n_down,
+                   threadIdx.x, e.N * e.K / 8, T);
 }
 
 // Backward: G = dY B, and the transposed decoded copy w_hat^T [K, N] (two 64 x 256 tiles per
@@ -486,7 +487,7 @@ template <int JT, int MT, bool BWD>
 hipError_t prologue_launch(const DownArgs& dn, const DecodeArgs& de, const Nf4Tables& T, hipStream_t s) {
   const int64_t n_down = (dn.M + 16 * MT - 1) / (16 * MT);
   const int64_t n_dec = BWD ? (((de.K + kTK - 1) / kTK) * ((de.N + kTN - 1) / kTN) + 1) / 2
-                            : (de.N * de.K / 8 + kDownThreads - 1) / kDownThreads;
+                            : (de.N * de.K / 8 + kDownThreads * kDecWords - 1) / (kDownThreads * kDecWords);
   constexpr int kMaxD = BWD ? ((JT + MT <= 3) ? 8 : (JT + MT <= 6 ? 4 : 2))
                             : ((JT + MT <= 2) ? 16 : (JT + MT <= 3 ? 8 : (JT + MT <= 6 ? 4 : 2)));
   const int d = batch_depth(((dn.Kd + 31) / 32 + kDownWaves - 1) / kDownWaves, kMaxD);
