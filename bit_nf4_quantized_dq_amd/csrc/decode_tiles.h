@@ -55,58 +55,45 @@ __device__ __forceinline__ void decode_words(const uint32_t* __restrict__ codes,
 }
 
 // Transposed copy w_hat^T [K, N] (the operand layout of the dX product, whose reduction runs
-// over N), one 64 (n) x 256 (k) tile per 256 threads: thread t decodes one 64-weight block of
-// row n0 + (t & 63) with the per-block scaled table into LDS, then the tile is written
-// transposed, each item a pair of rows k, k+1 times 8 consecutive n (two 16-byte stores).
-// The LDS tile is [64][129] dwords (a dword = two k-neighbours), so the decode writes (one
-// dword column across 64 rows) and the transposed reads (8 rows 8c+i across lanes c) both
-// spread over distinct banks.  Contains a workgroup barrier: every thread of the workgroup
-// must call it.  Tiles past the weight decode zeros and store nothing.
-constexpr int kTN = 64, kTK = 256, kTPitch = kTK / 2 + 1;
-constexpr int kTileLdsBytes = kTN * kTPitch * 4;
-
-template <int DQ>
-__device__ __forceinline__ void decode_tile_t(const uint32_t* __restrict__ codes, const uint8_t* __restrict__ code8,
-                                              const float* __restrict__ c2s, const float* __restrict__ mu,
-                                              uint16_t* __restrict__ out, int64_t N, int64_t K, const Nf4Tables& T,
-                                              int64_t tile_k, int64_t tile_n, int t, uint32_t* tile) {
-  const int64_t n0 = tile_n * kTN, k0 = tile_k * kTK;
-  const int nl = t & 63, b = t >> 6;
-  const int64_t n = n0 + nl, kb = k0 / 64 + b, nb_row = K / 64;
-  uint32_t o[32];
-  if (n < N && kb < nb_row) {
-    const int64_t blk = n * nb_row + kb;
-    // the block's codes first (raw buffer loads, issued before the constant's decode and its
-    // branch, as in decode_words)
-    const rsrc_t rc = make_rsrc(codes, (int64_t)0xFFFFFFFF);
-    const uint4 w0 = bload16(rc, (uint32_t)(32 * blk)), w1 = bload16(rc, (uint32_t)(32 * blk + 16));
-    Lut L;
-    build_scaled_lut(T, stored_c1<DQ>(code8, c2s, mu, blk), L);
-    const uint32_t words[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+// over N), without LDS: lane l of wavefront w of workgroup (gn, gk) decodes block
+// kb = gk (NT / 64) + w of rows n = 128 gn + 2 l and n + 1 (the per-block scaled table, one
+// per row), and for each of the block's 64 reduction indices k stores the dword
+// (w_hat[n][k], w_hat[n + 1][k]) at row k of the output: the 64 lanes of a wavefront write
+// 256 contiguous bytes of that row.  (A tile transposed through LDS needed 66 KB per
+// workgroup, which held the launch that pairs it with G = dY B to two workgroups per CU.)
+// N is even, so a row pair is whole.  Blocks past the weight store nothing.
+constexpr int kTRows = 128;  // rows per workgroup (two per lane)
+template <int DQ, int NT>
+__device__ __forceinline__ void decode_pairs_t(const uint32_t* __restrict__ codes, const uint8_t* __restrict__ code8,
+                                               const float* __restrict__ c2s, const float* __restrict__ mu,
+                                               uint16_t* __restrict__ out, int64_t N, int64_t K, const Nf4Tables& T,
+                                               int64_t gn, int64_t gk, int t) {
+  const int lane = t & 63, w = t >> 6;
+  const int64_t n = gn * kTRows + 2 * lane, nb_row = K / 64, kb = gk * (NT / 64) + w;
+  if (n >= N || kb >= nb_row) return;
+  const int64_t blk0 = n * nb_row + kb, blk1 = blk0 + nb_row;
+  // the codes first (raw buffer loads, issued before the constants' decode and its branch,
+  // as in decode_words)
+  const rsrc_t rc = make_rsrc(codes, (int64_t)0xFFFFFFFF);
+  const uint4 a0 = bload16(rc, (uint32_t)(32 * blk0)), a1 = bload16(rc, (uint32_t)(32 * blk0 + 16));
+  const uint4 b0 = bload16(rc, (uint32_t)(32 * blk1)), b1 = bload16(rc, (uint32_t)(32 * blk1 + 16));
+  Lut La, Lb;
+  build_scaled_lut(T, stored_c1<DQ>(code8, c2s, mu, blk0), La);
+  build_scaled_lut(T, stored_c1<DQ>(code8, c2s, mu, blk1), Lb);
+  const uint32_t wa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+  const uint32_t wb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+  uint32_t* const o = reinterpret_cast<uint32_t*>(out) + (kb * 64 * N + n) / 2;  // row k = 64 kb, column n
 #pragma unroll
-    for (int c = 0; c < 8; ++c) decode8(words[c], L, &o[4 * c]);
-  } else {
+  for (int c = 0; c < 8; ++c) {
+    uint32_t da[4], db[4];  // dword j: elements 8c + 2j (low half) and 8c + 2j + 1 (high half)
+    decode8(wa[c], La, da);
+    decode8(wb[c], Lb, db);
 #pragma unroll
-    for (int j = 0; j < 32; ++j) o[j] = 0u;
-  }
-#pragma unroll
-  for (int j = 0; j < 32; ++j) tile[nl * kTPitch + 32 * b + j] = o[j];
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int item = t + 256 * q;
-    const int c = item & 7, p = item >> 3;  // n-chunk c (8 values), k pair p
-    const int64_t k = k0 + 2 * p, nn = n0 + 8 * c;
-    if (k >= K || nn >= N) continue;
-    uint32_t d[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) d[i] = tile[(8 * c + i) * kTPitch + p];
-    const uint4 even = make_uint4((d[0] & 0xFFFFu) | (d[1] << 16), (d[2] & 0xFFFFu) | (d[3] << 16),
-                                  (d[4] & 0xFFFFu) | (d[5] << 16), (d[6] & 0xFFFFu) | (d[7] << 16));
-    const uint4 odd = make_uint4((d[0] >> 16) | (d[1] & 0xFFFF0000u), (d[2] >> 16) | (d[3] & 0xFFFF0000u),
-                                 (d[4] >> 16) | (d[5] & 0xFFFF0000u), (d[6] >> 16) | (d[7] & 0xFFFF0000u));
-    *reinterpret_cast<uint4*>(out + k * N + nn) = even;
-    *reinterpret_cast<uint4*>(out + (k + 1) * N + nn) = odd;
+    for (int j = 0; j < 4; ++j) {
+      const int64_t k = 8 * c + 2 * j;  // within the block
+      o[(k * N) / 2] = __builtin_amdgcn_perm(db[j], da[j], 0x05040100u);        // (n, n + 1) at k
+      o[((k + 1) * N) / 2] = __builtin_amdgcn_perm(db[j], da[j], 0x07060302u);  // (n, n + 1) at k + 1
+    }
   }
 }
 

@@ -20,7 +20,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint32_t* __restrict
   decode_words<DQ, kThreads>(codes, code8, c2s, mu, out, blockIdx.x, threadIdx.x, n_words, T);
 }
 
-// The transposed copy w_hat^T [K, N]: one 64 x 256 tile per workgroup (decode_tile_t).
+// The transposed copy w_hat^T [K, N]: 128 rows x 4 blocks per workgroup (decode_pairs_t).
 template <int DQ>
 __global__ __launch_bounds__(kThreads) void k_dequant_t(const uint32_t* __restrict__ codes,
                                                         const uint8_t* __restrict__ code8,
@@ -28,8 +28,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant_t(const uint32_t* __restri
                                                         const float* __restrict__ mu,
                                                         uint16_t* __restrict__ out, int64_t N, int64_t K,
                                                         Nf4Tables T) {
-  __shared__ uint32_t tile[kTN * kTPitch];
-  decode_tile_t<DQ>(codes, code8, c2s, mu, out, N, K, T, blockIdx.x, blockIdx.y, threadIdx.x, tile);
+  decode_pairs_t<DQ, kThreads>(codes, code8, c2s, mu, out, N, K, T, blockIdx.y, blockIdx.x, threadIdx.x);
 }
 
 }  // namespace
@@ -37,7 +36,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant_t(const uint32_t* __restri
 hipError_t launch_dequant_t(const uint32_t* codes, const uint8_t* code8, const float* c2s,
                             const float* mu, int64_t N, int64_t K, uint16_t* out, const Nf4Tables& T, int dq,
                             hipStream_t s) {
-  dim3 grid((unsigned)((K + kTK - 1) / kTK), (unsigned)((N + kTN - 1) / kTN));
+  dim3 grid((unsigned)((K / 64 + kThreads / 64 - 1) / (kThreads / 64)), (unsigned)((N + kTRows - 1) / kTRows));
   LaunchTimer t(8, s);
   auto go = [&](auto kern) {
     hipExtLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, t.start, t.stop, 0, codes, code8, c2s, mu, out, N, K, T);

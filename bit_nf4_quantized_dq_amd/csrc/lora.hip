@@ -215,24 +215,23 @@ __global__ __launch_bounds__(kDownThreads) void k_fwd_prologue(DownArgs d, Decod
                    threadIdx.x, e.N * e.K / 8, T);
 }
 
-// Backward: G = dY B, and the transposed decoded copy w_hat^T [K, N] (two 64 x 256 tiles per
-// workgroup, one per half).
+// Backward: G = dY B, and the transposed decoded copy w_hat^T [K, N] (128 rows x 8 blocks per
+// workgroup, decode_pairs_t; no LDS, so the decode takes none from the G role's workgroups).
 template <int JT, int MT, int D, int DQ>
 __global__ __launch_bounds__(kDownThreads) void k_bwd_prologue(DownArgs d, DecodeArgs e, int64_t n_down, Nf4Tables T) {
-  constexpr int kLds = down_lds_bytes<JT, MT>() > 2 * kTileLdsBytes ? down_lds_bytes<JT, MT>() : 2 * kTileLdsBytes;
-  __shared__ __attribute__((aligned(16))) char smem[kLds];
+  __shared__ __attribute__((aligned(16))) char smem[down_lds_bytes<JT, MT>()];
   if ((int64_t)blockIdx.x < n_down) {
     down_body<JT, MT, true, D>(d.P, d.Q, d.M, d.R, d.Kd, d.scale, d.out_s, d.out_u, blockIdx.x, smem);
     return;
   }
-  const int half = threadIdx.x >> 8;
-  // 32-bit tile arithmetic (fewer than 2^31 tiles): a 64-bit division here delayed the
+  // 32-bit group arithmetic (fewer than 2^31 groups): a 64-bit division here delayed the
   // decode's first loads
-  const uint32_t tiles_k = (uint32_t)((e.K + kTK - 1) / kTK);
-  const uint32_t tile = 2u * (uint32_t)((int64_t)blockIdx.x - n_down) + (uint32_t)half;  // past the last tile: decodes nothing
-  const uint32_t tn = tile / tiles_k;
-  decode_tile_t<DQ>(e.codes, e.code8, e.c2s, e.mu, e.out, e.N, e.K, T, (int64_t)(tile - tn * tiles_k), (int64_t)tn,
-                    threadIdx.x & 255, reinterpret_cast<uint32_t*>(smem + half * kTileLdsBytes));
+  constexpr int kBlocks = kDownThreads / 64;  // k blocks per workgroup
+  const uint32_t groups_k = (uint32_t)((e.K / 64 + kBlocks - 1) / kBlocks);
+  const uint32_t grp = (uint32_t)((int64_t)blockIdx.x - n_down);
+  const uint32_t gn = grp / groups_k;
+  decode_pairs_t<DQ, kDownThreads>(e.codes, e.code8, e.c2s, e.mu, e.out, e.N, e.K, T, (int64_t)gn,
+                                   (int64_t)(grp - gn * groups_k), threadIdx.x);
 }
 
 // ---------------------------------------------------------------- gradients of A and B
@@ -486,7 +485,7 @@ GradArgs grad_args(const uint16_t* U, const uint16_t* V, int64_t M, int32_t R, i
 template <int JT, int MT, bool BWD>
 hipError_t prologue_launch(const DownArgs& dn, const DecodeArgs& de, const Nf4Tables& T, hipStream_t s) {
   const int64_t n_down = (dn.M + 16 * MT - 1) / (16 * MT);
-  const int64_t n_dec = BWD ? (((de.K + kTK - 1) / kTK) * ((de.N + kTN - 1) / kTN) + 1) / 2
+  const int64_t n_dec = BWD ? ((de.K / 64 + kDownThreads / 64 - 1) / (kDownThreads / 64)) * ((de.N + kTRows - 1) / kTRows)
                             : (de.N * de.K / 8 + kDownThreads * kDecWords - 1) / (kDownThreads * kDecWords);
   constexpr int kMaxD = BWD ? ((JT + MT <= 3) ? 8 : (JT + MT <= 6 ? 4 : 2))
                             : ((JT + MT <= 2) ? 16 : (JT + MT <= 3 ? 8 : (JT + MT <= 6 ? 4 : 2)));
