@@ -61,14 +61,14 @@ COUNTERS = {
                 "lds_insts": 3_244_032, "lds_bank_conflict_cycles": 65_536, "salu_insts": 3_279_616},
     # the step's HBM-bound launches (4096 x 4096, M = 4096, r = 16)
     "fwd_prologue": {"source": "bit_nf4_quantized_dq_amd/csrc/lora.hip",
-                     "sha1": "193db98fce30510436fd6b0e9566782f5d9b2b94",
-                     "read_bytes": 43_487_552, "write_bytes": 33_816_576},
+                     "sha1": "0b8df2d485634ad8f60dc2dba058b04007f6deeb",
+                     "read_bytes": 43_486_144, "write_bytes": 33_816_576},
     "bwd_prologue": {"source": "bit_nf4_quantized_dq_amd/csrc/lora.hip",
-                     "sha1": "193db98fce30510436fd6b0e9566782f5d9b2b94",
-                     "read_bytes": 45_275_136, "write_bytes": 33_816_576},
+                     "sha1": "0b8df2d485634ad8f60dc2dba058b04007f6deeb",
+                     "read_bytes": 45_822_208, "write_bytes": 33_816_576},
     "lora_grad2": {"source": "bit_nf4_quantized_dq_amd/csrc/lora.hip",
-                   "sha1": "193db98fce30510436fd6b0e9566782f5d9b2b94",
-                   "read_bytes": 71_514_624, "write_bytes": 2_379_776},
+                   "sha1": "0b8df2d485634ad8f60dc2dba058b04007f6deeb",
+                   "read_bytes": 71_515_008, "write_bytes": 2_379_776},
     "merge": {"source": "bit_nf4_quantized_dq_amd/csrc/merge.hip",
               "sha1": "aa1649879396b227b61d065c057ec39a4962a28a",
               "read_bytes": 11_910_758, "write_bytes": 33_554_534},
@@ -94,8 +94,8 @@ COUNTERS = {
     # the decode-once forward at M = 2048 on the same 28672 x 8192 weight: the decode (with
     # T = X A^T) and the BF16 GEMM
     "fwd_prologue_gate_M2048": {"source": "bit_nf4_quantized_dq_amd/csrc/lora.hip",
-                                "sha1": "193db98fce30510436fd6b0e9566782f5d9b2b94",
-                                "read_bytes": 157_597_312, "write_bytes": 469_827_584},
+                                "sha1": "0b8df2d485634ad8f60dc2dba058b04007f6deeb",
+                                "read_bytes": 157_554_176, "write_bytes": 469_827_584},
     "gemm_nt_gate_M2048": {"source": "bit_nf4_quantized_dq_amd/csrc/gemm_nt.hip",
                            "sha1": "5ce5dbfd0aa38821b99f12d226e7a0e43790f4b7",
                            "read_bytes": 2_001_885_389, "write_bytes": 117_440_512,
